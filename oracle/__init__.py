@@ -1,0 +1,154 @@
+"""Plain fp64 CPU oracle for the RNN-T loss (forward and backward).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The product path
+(``rnn_transducer_loss_amd``) never imports it, and the two share no code:
+the only thing both sides use is the seeded input generator in
+``workloads.py``, which holds none of the method's arithmetic.
+
+The arithmetic lives in ``rnnt_oracle.c`` (fp64, row-major loops over the
+lattice).  This module only builds/loads it and marshals numpy arrays.
+Semantics follow the rnnt-loss-ascend README (parameter table and usage
+example): ``blank`` in [-V, V-1] with negative values counted from the end,
+``clamp <= 0`` disables clipping, and ``reduction`` is one of none / mean
+(batch mean) / sum.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "rnnt_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+_lock = threading.Lock()
+
+ORACLE_OK = 0
+ORACLE_BAD_ARGS = 1
+ORACLE_BAD_TARGET = 2
+ORACLE_NO_MEMORY = 3
+
+
+def build(force: bool = True) -> str:
+    """Compile rnnt_oracle.c into liboracle.so with gcc (plain -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                build(force=False)
+            lib = ctypes.CDLL(_LIB_PATH)
+            dp = ctypes.POINTER(ctypes.c_double)
+            lib.rnnt_oracle_sample.argtypes = [
+                dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                ctypes.c_int, ctypes.c_int, ctypes.c_double, dp, dp, dp, dp, dp]
+            lib.rnnt_oracle_sample.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def normalize_blank(blank: int, V: int) -> int:
+    """Blank in [-V, V-1]; a negative value counts from the end (-1 -> V-1)."""
+    if blank < -V or blank > V - 1:
+        raise ValueError(f"blank {blank} outside [-{V}, {V - 1}]")
+    return blank + V if blank < 0 else blank
+
+
+class SampleResult:
+    __slots__ = ("loss", "loss_alpha", "grad", "alpha", "beta")
+
+    def __init__(self, loss, loss_alpha, grad, alpha, beta):
+        self.loss = loss
+        self.loss_alpha = loss_alpha
+        self.grad = grad
+        self.alpha = alpha
+        self.beta = beta
+
+
+def sample(x, T: int, U: int, y, blank: int, fused: bool = True, clamp: float = -1.0,
+           want_grad: bool = True, want_tables: bool = False) -> SampleResult:
+    """Loss (and optionally gradient / alpha / beta tables) of one sample.
+
+    ``x`` holds the sample's T*(U+1) rows of V values (any float dtype; values
+    are converted exactly to fp64).  ``blank`` must already be in [0, V).
+    The loss is the beta-path value -beta(0,0); ``loss_alpha`` is the
+    alpha-path value kept for the cross-check.
+    """
+    lib = _load()
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    V = x.shape[1]
+    if x.shape[0] != T * (U + 1):
+        raise ValueError("row count does not match T*(U+1)")
+    yy = np.ascontiguousarray(np.asarray(y[:U], dtype=np.int32)) if U > 0 else np.zeros(1, np.int32)
+    grad = np.empty((T * (U + 1), V), np.float64) if want_grad else None
+    al = np.empty((T, U + 1), np.float64) if want_tables else None
+    be = np.empty((T, U + 1), np.float64) if want_tables else None
+    la = ctypes.c_double()
+    lb = ctypes.c_double()
+    rc = lib.rnnt_oracle_sample(_ptr(x), T, U, V, yy.ctypes.data_as(ctypes.POINTER(ctypes.c_int)),
+                                int(blank), int(bool(fused)), float(clamp), _ptr(grad), _ptr(al), _ptr(be),
+                                ctypes.byref(la), ctypes.byref(lb))
+    if rc == ORACLE_BAD_TARGET:
+        raise ValueError("target label equal to blank or outside [0, V)")
+    if rc != ORACLE_OK:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return SampleResult(lb.value, la.value, grad, al, be)
+
+
+def batch(logits, targets, logit_lengths, target_lengths, blank: int = -1, clamp: float = -1.0,
+          reduction: str = "mean", fused: bool = True, want_grad: bool = True):
+    """Whole-batch oracle over the packed (sum_i T_i*(U_i+1), V) layout.
+
+    Returns ``(loss_per_sample, reduced_loss, grad_per_sample, grad_reduced)``.
+    ``grad_per_sample`` is d loss_i / d logits for each sample's own rows
+    (clamped, unscaled); ``grad_reduced`` is the gradient of the reduced loss
+    with a unit upstream gradient: the same rows scaled by 1/B for mean and 1
+    for sum and none.  Both are None when ``want_grad`` is False.
+    """
+    logits = np.asarray(logits)
+    N, V = logits.shape
+    B = len(logit_lengths)
+    b = normalize_blank(int(blank), V)
+    Ts = [int(v) for v in logit_lengths]
+    Us = [int(v) for v in target_lengths]
+    rows = [Ts[i] * (Us[i] + 1) for i in range(B)]
+    if sum(rows) != N:
+        raise ValueError("sum of T_i*(U_i+1) does not equal logits.shape[0]")
+    if reduction not in ("none", "mean", "sum"):
+        raise ValueError(f"unknown reduction {reduction!r}")
+    losses = np.empty(B, np.float64)
+    grad = np.empty((N, V), np.float64) if want_grad else None
+    off = 0
+    for i in range(B):
+        res = sample(logits[off:off + rows[i]], Ts[i], Us[i], np.asarray(targets[i]), b, fused, clamp,
+                     want_grad=want_grad)
+        losses[i] = res.loss
+        if want_grad:
+            grad[off:off + rows[i]] = res.grad
+        off += rows[i]
+    if reduction == "none":
+        reduced, scale = losses.copy(), 1.0
+    elif reduction == "sum":
+        reduced, scale = losses.sum(), 1.0
+    else:
+        reduced, scale = losses.sum() / B, 1.0 / B
+    grad_reduced = grad * scale if want_grad else None
+    return losses, reduced, grad, grad_reduced

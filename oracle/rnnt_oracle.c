@@ -1,0 +1,191 @@
+/*
+ * rnnt_oracle.c -- plain fp64 CPU oracle for the RNN-T loss and its gradient.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library and
+ * its Python binding) may include, link or call this file.  Only the tests,
+ * the smoke check and the bench's CPU-baseline leg use it.  It shares no code,
+ * header, table or helper with the HIP implementation.
+ *
+ * What it computes, and where the pages define it:
+ *
+ *  - Alignment lattice (warp-transducer build post, section 1.1: the loss sums
+ *    over every legal alignment path on a 2-D T x (U+1) grid; at each node the
+ *    model either emits a vocabulary symbol or emits blank).  A path starts at
+ *    node (0,0).  Blank at (t,u) moves to (t+1,u); the next label y_{u+1} at
+ *    (t,u) moves to (t,u+1).  The path ends by emitting blank at (T-1,U).
+ *    P(y|x) is the sum over paths of the product of the emitted symbols'
+ *    probabilities and loss = -log P(y|x).
+ *
+ *  - Row layout (rnnt-loss-ascend README, "Main features" and the parameter
+ *    table): the joiner logits of sample i are packed as T*(U+1) rows of V
+ *    classes.  Rows are t-major inside a sample: row t*(U+1)+u is node (t,u).
+ *
+ *  - log_softmax over V at every node when fused_log_softmax is set; the raw
+ *    inputs are used as log-probabilities otherwise (README parameter table).
+ *
+ *  - Log-space forward/backward variables (README "Value", section 3: both
+ *    recursions run in the log domain; the alpha-path and beta-path losses are
+ *    computed independently and cross-checked).
+ *
+ *  - Gradient (README "Value", section 2, the fused gradient formula).  Here it
+ *    is obtained by the chain rule written out: first the derivative of the
+ *    loss with respect to each log-probability the lattice uses (minus the
+ *    posterior probability that the alignment takes that edge), then, when
+ *    log_softmax is fused, the log_softmax Jacobian
+ *        dL/dx_k = dL/dlp_k - softmax_k * sum_j dL/dlp_j.
+ *
+ *  - Clamp (README "Operator features": for clamp > 0 every gradient element
+ *    is clipped to [-clamp, clamp]; clamp <= 0 disables it).
+ *
+ * The loops run row-major over (t,u), never along anti-diagonals, so the
+ * oracle has no structure in common with the GPU kernels.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARGS 1
+#define ORACLE_BAD_TARGET 2
+#define ORACLE_NO_MEMORY 3
+
+/* log(exp(a) + exp(b)) with -inf handled: log(0 + 0) = -inf. */
+static double log_add(double a, double b)
+{
+    if (a == -INFINITY) return b;
+    if (b == -INFINITY) return a;
+    if (a > b) return a + log1p(exp(b - a));
+    return b + log1p(exp(a - b));
+}
+
+/* log-sum-exp of one row of V values, shifted by the row maximum. */
+static double row_logsumexp(const double *x, int V)
+{
+    double m = -INFINITY;
+    for (int k = 0; k < V; ++k)
+        if (x[k] > m) m = x[k];
+    if (m == -INFINITY) return -INFINITY;
+    double s = 0.0;
+    for (int k = 0; k < V; ++k) s += exp(x[k] - m);
+    return m + log(s);
+}
+
+/*
+ * One sample.
+ *   x        (T*(U+1)) x V row-major fp64 inputs (logits, or log-probs when
+ *            fused == 0).
+ *   y        U target labels; each must lie in [0,V) and differ from blank.
+ *   blank    already normalised to [0,V).
+ *   grad     optional (T*(U+1)) x V output: d loss / d x, clamped if clamp>0.
+ *   alpha, beta  optional T*(U+1) outputs of the log forward / backward
+ *            variables (beta(t,u) includes the emissions at (t,u) onwards,
+ *            so beta(0,0) = log P(y|x)).
+ *   loss_alpha, loss_beta  -log P(y|x) from each recursion.
+ * Returns ORACLE_OK or an error code.
+ */
+int rnnt_oracle_sample(const double *x, int T, int U, int V, const int *y,
+                       int blank, int fused, double clamp, double *grad,
+                       double *alpha_out, double *beta_out,
+                       double *loss_alpha, double *loss_beta)
+{
+    if (T < 1 || U < 0 || V < 1 || blank < 0 || blank >= V) return ORACLE_BAD_ARGS;
+    for (int u = 0; u < U; ++u)
+        if (y[u] < 0 || y[u] >= V || y[u] == blank) return ORACLE_BAD_TARGET;
+
+    const int U1 = U + 1;
+    const long cells = (long)T * U1;
+    double *lse = malloc(sizeof(double) * cells);   /* per-node log normaliser */
+    double *lpb = malloc(sizeof(double) * cells);   /* log P(blank | t,u) */
+    double *lpy = malloc(sizeof(double) * cells);   /* log P(y_{u+1} | t,u), u < U */
+    double *al = malloc(sizeof(double) * cells);
+    double *be = malloc(sizeof(double) * cells);
+    if (!lse || !lpb || !lpy || !al || !be) {
+        free(lse); free(lpb); free(lpy); free(al); free(be);
+        return ORACLE_NO_MEMORY;
+    }
+
+    /* Step 1: per-node normaliser and the two log-probs the lattice uses. */
+    for (int t = 0; t < T; ++t) {
+        for (int u = 0; u <= U; ++u) {
+            long c = (long)t * U1 + u;
+            const double *row = x + c * V;
+            lse[c] = fused ? row_logsumexp(row, V) : 0.0;
+            lpb[c] = row[blank] - lse[c];
+            lpy[c] = (u < U) ? row[y[u]] - lse[c] : -INFINITY;
+        }
+    }
+
+    /* Step 2: forward variable, alpha(t,u) = log of the summed probability
+     * of all partial paths from (0,0) that arrive at (t,u). */
+    for (int t = 0; t < T; ++t) {
+        for (int u = 0; u <= U; ++u) {
+            long c = (long)t * U1 + u;
+            if (t == 0 && u == 0) { al[c] = 0.0; continue; }
+            double from_blank = (t > 0) ? al[c - U1] + lpb[c - U1] : -INFINITY;
+            double from_label = (u > 0) ? al[c - 1] + lpy[c - 1] : -INFINITY;
+            al[c] = log_add(from_blank, from_label);
+        }
+    }
+    const long last = (long)(T - 1) * U1 + U;
+    double logz_alpha = al[last] + lpb[last];
+
+    /* Step 3: backward variable, beta(t,u) = log of the summed probability
+     * of all path suffixes from (t,u), the final blank included. */
+    for (int t = T - 1; t >= 0; --t) {
+        for (int u = U; u >= 0; --u) {
+            long c = (long)t * U1 + u;
+            if (c == last) { be[c] = lpb[c]; continue; }
+            double via_blank = (t < T - 1) ? be[c + U1] + lpb[c] : -INFINITY;
+            double via_label = (u < U) ? be[c + 1] + lpy[c] : -INFINITY;
+            be[c] = log_add(via_blank, via_label);
+        }
+    }
+    double logz_beta = be[0];
+
+    if (loss_alpha) *loss_alpha = -logz_alpha;
+    if (loss_beta) *loss_beta = -logz_beta;
+    if (alpha_out) memcpy(alpha_out, al, sizeof(double) * cells);
+    if (beta_out) memcpy(beta_out, be, sizeof(double) * cells);
+
+    /* Step 4: gradient by the chain rule. */
+    if (grad) {
+        const double logz = logz_beta;
+        for (int t = 0; t < T; ++t) {
+            for (int u = 0; u <= U; ++u) {
+                long c = (long)t * U1 + u;
+                double *g = grad + c * V;
+                const double *row = x + c * V;
+                /* d loss / d lp(blank) and d loss / d lp(y_{u+1}) at this node:
+                 * minus the posterior probability of taking that edge. */
+                double d_blank = 0.0, d_label = 0.0;
+                if (logz != -INFINITY) {
+                    if (t < T - 1)
+                        d_blank = -exp(al[c] + lpb[c] + be[c + U1] - logz);
+                    else if (u == U)
+                        d_blank = -exp(al[c] + lpb[c] - logz);
+                    if (u < U)
+                        d_label = -exp(al[c] + lpy[c] + be[c + 1] - logz);
+                }
+                for (int k = 0; k < V; ++k) g[k] = 0.0;
+                g[blank] += d_blank;
+                if (u < U) g[y[u]] += d_label;
+                if (fused) {
+                    double sum_d = d_blank + d_label;
+                    for (int k = 0; k < V; ++k) {
+                        double p = (lse[c] == -INFINITY) ? 0.0 : exp(row[k] - lse[c]);
+                        g[k] -= p * sum_d;
+                    }
+                }
+                if (clamp > 0.0) {
+                    for (int k = 0; k < V; ++k) {
+                        if (g[k] > clamp) g[k] = clamp;
+                        if (g[k] < -clamp) g[k] = -clamp;
+                    }
+                }
+            }
+        }
+    }
+
+    free(lse); free(lpb); free(lpy); free(al); free(be);
+    return ORACLE_OK;
+}

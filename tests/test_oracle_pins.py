@@ -1,0 +1,295 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+None of these checks retypes the oracle's recursion.  Each compares it with
+an independent fact:
+
+* brute-force enumeration of every alignment path (definition of the loss as
+  a sum over alignments: warp-transducer build post, section 1.1);
+* the all-zero-logit closed forms for the loss and, derived from path
+  counting, for the whole gradient;
+* invariants: alpha-path loss == beta-path loss (rnnt-loss-ascend README,
+  "Value" section 3, dual-loss cross-check), fused-gradient rows sum to zero,
+  each anti-diagonal carries total occupancy one, the non-fused gradient
+  sums to -(T+U);
+* the chain rule linking the fused and non-fused gradients via a library
+  log_softmax; shift invariance of the fused path;
+* central finite differences of the loss;
+* single-path special cases (U = 0 and T = 1);
+* clamp and reduction semantics of the README parameter table / usage example.
+"""
+import math
+
+import numpy as np
+import pytest
+from scipy.special import log_softmax as sp_log_softmax
+
+import oracle
+from oracle import bruteforce
+
+
+def _rand_case(rng, T, U, V, blank, std=1.0):
+    x = rng.normal(0.0, std, size=(T * (U + 1), V))
+    ids = [k for k in range(V) if k != blank]
+    y = rng.choice(ids, size=U) if U > 0 else np.zeros(0, np.int64)
+    return x, y
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("T,U", [(1, 0), (1, 1), (1, 3), (2, 0), (2, 1), (3, 2), (4, 3), (5, 2), (2, 5), (6, 4)])
+def test_bruteforce_small_lattices(T, U, fused):
+    rng = np.random.default_rng(100 * T + U + (7 if fused else 0))
+    V, blank = 5, 2
+    x, y = _rand_case(rng, T, U, V, blank)
+    if not fused:
+        x = sp_log_softmax(x, axis=1) + rng.normal(0, 0.1, size=x.shape)  # log-probs, not exactly normalised
+    bf_loss, bf_grad = bruteforce.sample(x, T, U, y, blank, fused)
+    r = oracle.sample(x, T, U, y, blank, fused)
+    assert abs(r.loss - bf_loss) <= 1e-12 * max(1.0, abs(bf_loss))
+    assert abs(r.loss_alpha - bf_loss) <= 1e-12 * max(1.0, abs(bf_loss))
+    np.testing.assert_allclose(r.grad, bf_grad, atol=1e-12, rtol=0)
+
+
+def test_bruteforce_tiny_workload():
+    """Both samples of the tiny workload shape (T=[12,9], U=[4,3], V=16): 1365 and 165 paths."""
+    rng = np.random.default_rng(11)
+    V, blank = 16, 15
+    for T, U in [(12, 4), (9, 3)]:
+        x, y = _rand_case(rng, T, U, V, blank)
+        assert bruteforce.count_paths(T, U) == {(12, 4): 1365, (9, 3): 165}[(T, U)]
+        bf_loss, bf_grad = bruteforce.sample(x, T, U, y, blank, True)
+        r = oracle.sample(x, T, U, y, blank, True)
+        assert abs(r.loss - bf_loss) <= 1e-11 * abs(bf_loss)
+        np.testing.assert_allclose(r.grad, bf_grad, atol=1e-12, rtol=0)
+
+
+def _log_comb(n, k):
+    return math.lgamma(n + 1) - math.lgamma(k + 1) - math.lgamma(n - k + 1)
+
+
+@pytest.mark.parametrize("T,U,V", [(1, 0, 3), (1, 5, 7), (12, 4, 16), (9, 3, 16), (50, 10, 29), (300, 80, 1024),
+                                   (600, 150, 4096)])
+def test_zero_logits_loss_closed_form(T, U, V):
+    """All-zero logits: every path has probability V^-(T+U), there are C(T-1+U, U) of them."""
+    x = np.zeros((T * (U + 1), V))
+    y = np.arange(U) % (V - 1)
+    r = oracle.sample(x, T, U, y, V - 1, True, want_grad=False)
+    expect = -_log_comb(T - 1 + U, U) + (T + U) * math.log(V)
+    assert abs(r.loss - expect) <= 1e-12 * max(1.0, abs(expect))
+
+
+@pytest.mark.parametrize("T,U,V,blank", [(1, 0, 4, 0), (3, 2, 5, 4), (7, 3, 6, 0), (12, 4, 16, 15), (20, 9, 11, 5)])
+def test_zero_logits_gradient_closed_form(T, U, V, blank):
+    """All-zero logits: occupancy and edge flows are ratios of path counts.
+
+    occ(t,u)    = C(t+u,u) C(T-1-t+U-u, U-u) / C(T-1+U, U)
+    flow_b(t,u) = C(t+u,u) C(T-2-t+U-u, U-u) / C(T-1+U, U)    (t < T-1); occ at (T-1,U); 0 at t=T-1, u<U
+    flow_y(t,u) = C(t+u,u) C(T-1-t+U-u-1, U-u-1) / C(T-1+U, U)  (u < U)
+    grad_k      = occ/V - [k=blank] flow_b - [k=y_{u+1}] flow_y
+    """
+    rng = np.random.default_rng(T * 31 + U)
+    ids = [k for k in range(V) if k != blank]
+    y = rng.choice(ids, size=U) if U else np.zeros(0, np.int64)
+    x = np.zeros((T * (U + 1), V))
+    r = oracle.sample(x, T, U, y, blank, True)
+    C = math.comb
+    total = C(T - 1 + U, U)
+    expect = np.zeros_like(x)
+    for t in range(T):
+        for u in range(U + 1):
+            row = t * (U + 1) + u
+            occ = C(t + u, u) * C(T - 1 - t + U - u, U - u) / total
+            if t < T - 1:
+                fb = C(t + u, u) * C(T - 2 - t + U - u, U - u) / total
+            elif u == U:
+                fb = occ
+            else:
+                fb = 0.0
+            fy = C(t + u, u) * C(T - 1 - t + U - u - 1, U - u - 1) / total if u < U else 0.0
+            expect[row, :] = occ / V
+            expect[row, blank] -= fb
+            if u < U:
+                expect[row, y[u]] -= fy
+    np.testing.assert_allclose(r.grad, expect, atol=1e-14, rtol=0)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_alpha_beta_agree_and_occupancy(seed):
+    rng = np.random.default_rng(seed)
+    T, U, V, blank = 60 + 20 * seed, 15 + 5 * seed, 37, 0
+    x, y = _rand_case(rng, T, U, V, blank, std=2.0)
+    r = oracle.sample(x, T, U, y, blank, True, want_tables=True)
+    assert abs(r.loss - r.loss_alpha) <= 1e-12 * abs(r.loss)
+    logz = r.beta[0, 0]
+    assert abs(-logz - r.loss) == 0.0
+    occ = np.exp(r.alpha + r.beta - logz)
+    for n in range(T + U):
+        s = sum(occ[t, n - t] for t in range(max(0, n - U), min(T - 1, n) + 1))
+        assert abs(s - 1.0) < 1e-11, (n, s)
+    # Each fused gradient row sums to zero (softmax probabilities sum to one).
+    assert np.abs(r.grad.sum(axis=1)).max() < 1e-13
+
+
+def test_nonfused_gradient_counts_emissions():
+    rng = np.random.default_rng(5)
+    T, U, V, blank = 40, 12, 20, 19
+    x, y = _rand_case(rng, T, U, V, blank)
+    lp = sp_log_softmax(x, axis=1)
+    r = oracle.sample(lp, T, U, y, blank, False)
+    # Every path makes exactly T blank and U label emissions.
+    assert abs(r.grad.sum() + (T + U)) < 1e-10
+    assert abs(r.grad[:, blank].sum() + T) < 1e-10
+    nnz = (r.grad != 0).sum(axis=1)
+    assert nnz.max() <= 2
+
+
+def test_fused_equals_chain_rule_of_nonfused():
+    rng = np.random.default_rng(6)
+    T, U, V, blank = 25, 7, 13, 3
+    x, y = _rand_case(rng, T, U, V, blank, std=1.5)
+    lp = sp_log_softmax(x, axis=1)
+    rf = oracle.sample(x, T, U, y, blank, True)
+    rn = oracle.sample(lp, T, U, y, blank, False)
+    assert abs(rf.loss - rn.loss) <= 1e-12 * abs(rf.loss)
+    p = np.exp(lp)
+    expect = rn.grad - p * rn.grad.sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(rf.grad, expect, atol=1e-13, rtol=0)
+
+
+def test_fused_shift_invariance():
+    rng = np.random.default_rng(7)
+    T, U, V, blank = 15, 6, 9, 8
+    x, y = _rand_case(rng, T, U, V, blank)
+    shift = rng.normal(0, 5.0, size=(x.shape[0], 1))
+    a = oracle.sample(x, T, U, y, blank, True)
+    b = oracle.sample(x + shift, T, U, y, blank, True)
+    assert abs(a.loss - b.loss) <= 1e-12 * abs(a.loss)
+    np.testing.assert_allclose(a.grad, b.grad, atol=1e-13, rtol=0)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_central_finite_differences(fused):
+    rng = np.random.default_rng(8 + fused)
+    T, U, V, blank = 6, 4, 7, 0
+    x, y = _rand_case(rng, T, U, V, blank)
+    if not fused:
+        x = sp_log_softmax(x, axis=1)
+    g = oracle.sample(x, T, U, y, blank, fused).grad
+    eps = 1e-6
+    for _ in range(40):
+        r = rng.integers(0, x.shape[0])
+        k = rng.integers(0, V)
+        xp = x.copy(); xp[r, k] += eps
+        xm = x.copy(); xm[r, k] -= eps
+        fd = (oracle.sample(xp, T, U, y, blank, fused, want_grad=False).loss
+              - oracle.sample(xm, T, U, y, blank, fused, want_grad=False).loss) / (2 * eps)
+        assert abs(fd - g[r, k]) < 1e-8, (r, k, fd, g[r, k])
+
+
+def test_central_finite_differences_char_sized():
+    """Random elements of a character-vocabulary-sized sample (T=70, U=20, V=29)."""
+    rng = np.random.default_rng(9)
+    T, U, V, blank = 70, 20, 29, 0
+    x, y = _rand_case(rng, T, U, V, blank)
+    g = oracle.sample(x, T, U, y, blank, True).grad
+    eps = 1e-6
+    for _ in range(12):
+        r = rng.integers(0, x.shape[0])
+        k = rng.integers(0, V)
+        xp = x.copy(); xp[r, k] += eps
+        xm = x.copy(); xm[r, k] -= eps
+        fd = (oracle.sample(xp, T, U, y, blank, True, want_grad=False).loss
+              - oracle.sample(xm, T, U, y, blank, True, want_grad=False).loss) / (2 * eps)
+        assert abs(fd - g[r, k]) < 1e-7, (r, k, fd, g[r, k])
+
+
+def test_single_path_special_cases():
+    rng = np.random.default_rng(10)
+    V, blank = 11, 4
+    # U = 0: the only path emits blank at every frame.
+    T = 9
+    x, _ = _rand_case(rng, T, 0, V, blank)
+    lp = sp_log_softmax(x, axis=1)
+    r = oracle.sample(x, T, 0, [], blank, True)
+    assert abs(r.loss + lp[:, blank].sum()) < 1e-12
+    # T = 1: the only path emits all labels at t=0, then one blank.
+    U = 6
+    x, y = _rand_case(rng, 1, U, V, blank)
+    lp = sp_log_softmax(x, axis=1)
+    expect = -sum(lp[u, y[u]] for u in range(U)) - lp[U, blank]
+    r = oracle.sample(x, 1, U, y, blank, True)
+    assert abs(r.loss - expect) < 1e-12
+
+
+def test_clamp_semantics():
+    rng = np.random.default_rng(12)
+    T, U, V, blank = 20, 5, 6, 5
+    x, y = _rand_case(rng, T, U, V, blank, std=3.0)
+    g = oracle.sample(x, T, U, y, blank, True).grad
+    for c in (0.02, 0.1, 0.3):
+        gc = oracle.sample(x, T, U, y, blank, True, clamp=c).grad
+        np.testing.assert_array_equal(gc, np.clip(g, -c, c))
+    for off in (0.0, -1.0):
+        np.testing.assert_array_equal(oracle.sample(x, T, U, y, blank, True, clamp=off).grad, g)
+
+
+def test_batch_reductions_and_permutation():
+    rng = np.random.default_rng(13)
+    V = 8
+    Ts, Us = [4, 6, 3], [2, 1, 0]
+    xs, ys = [], np.zeros((3, 2), np.int32)
+    for i, (T, U) in enumerate(zip(Ts, Us)):
+        x, y = _rand_case(rng, T, U, V, V - 1)
+        xs.append(x)
+        ys[i, :U] = y
+    logits = np.concatenate(xs)
+    loss, red, g, gr = oracle.batch(logits, ys, Ts, Us, blank=-1, reduction="mean")
+    assert abs(red - loss.mean()) < 1e-14
+    np.testing.assert_allclose(gr, g / 3, rtol=0, atol=1e-15)
+    _, red_s, _, gr_s = oracle.batch(logits, ys, Ts, Us, blank=-1, reduction="sum")
+    assert abs(red_s - loss.sum()) < 1e-13
+    np.testing.assert_array_equal(gr_s, g)
+    perm = [2, 0, 1]
+    logits_p = np.concatenate([xs[i] for i in perm])
+    loss_p, _, g_p, _ = oracle.batch(logits_p, ys[perm], [Ts[i] for i in perm], [Us[i] for i in perm],
+                                     blank=V - 1, reduction="none")
+    np.testing.assert_array_equal(loss_p, loss[perm])
+    off = np.concatenate([[0], np.cumsum([T * (U + 1) for T, U in zip(Ts, Us)])])
+    np.testing.assert_array_equal(g_p, np.concatenate([g[off[i]:off[i + 1]] for i in perm]))
+
+
+def test_blank_normalisation_and_bad_targets():
+    assert oracle.normalize_blank(-1, 10) == 9
+    assert oracle.normalize_blank(-10, 10) == 0
+    assert oracle.normalize_blank(9, 10) == 9
+    with pytest.raises(ValueError):
+        oracle.normalize_blank(10, 10)
+    with pytest.raises(ValueError):
+        oracle.normalize_blank(-11, 10)
+    x = np.zeros((3 * 2, 5))
+    with pytest.raises(ValueError):
+        oracle.sample(x, 3, 1, [4], 4)   # label equal to blank
+    with pytest.raises(ValueError):
+        oracle.sample(x, 3, 1, [5], 4)   # label outside [0, V)
+
+
+def test_golden_readme_example():
+    """The README usage-example layout (24 packed rows, V=8), values stored by tests/golden/make_golden.py."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "readme_example.json")
+    with open(path) as f:
+        gd = json.load(f)
+    logits = np.array(gd["logits"])
+    assert logits.shape == (24, 8)
+    for case in gd["cases"]:
+        loss, red, g, gr = oracle.batch(logits, np.array(gd["targets"], np.int32), gd["logit_lengths"],
+                                        gd["target_lengths"], blank=gd["blank"], reduction=case["reduction"])
+        np.testing.assert_allclose(np.atleast_1d(red), case["loss"], rtol=1e-13, atol=0)
+        np.testing.assert_allclose(gr, np.array(case["grad"]), rtol=0, atol=1e-15)
+        # Independent recomputation of each sample by path enumeration.
+        off = 0
+        for i, (T, U) in enumerate(zip(gd["logit_lengths"], gd["target_lengths"])):
+            rows = T * (U + 1)
+            bl, _ = bruteforce.sample(logits[off:off + rows], T, U, gd["targets"][i], 7, True)
+            assert abs(bl - case["loss_per_sample"][i]) < 1e-12
+            off += rows
