@@ -55,6 +55,13 @@ def _load():
                 dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
                 ctypes.c_int, ctypes.c_int, ctypes.c_double, dp, dp, dp, dp, dp]
             lib.rnnt_oracle_sample.restype = ctypes.c_int
+            lib.rnnt_oracle_sample_ex.argtypes = [
+                ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                ctypes.POINTER(ctypes.c_int64), ctypes.c_long, dp, dp, dp, dp, dp]
+            lib.rnnt_oracle_sample_ex.restype = ctypes.c_int
+            lib.rnnt_oracle_half_to_double.argtypes = [ctypes.c_uint16]
+            lib.rnnt_oracle_half_to_double.restype = ctypes.c_double
             _lib = lib
     return _lib
 
@@ -83,29 +90,51 @@ class SampleResult:
         self.beta = beta
 
 
+_DT = {np.dtype(np.float64): 0, np.dtype(np.float32): 1, np.dtype(np.float16): 2}
+
+
+def half_to_double(h: int) -> float:
+    """The oracle's own exact binary16 -> binary64 conversion (pinned against numpy)."""
+    return _load().rnnt_oracle_half_to_double(int(h))
+
+
 def sample(x, T: int, U: int, y, blank: int, fused: bool = True, clamp: float = -1.0,
-           want_grad: bool = True, want_tables: bool = False) -> SampleResult:
+           want_grad: bool = True, want_tables: bool = False, rows=None) -> SampleResult:
     """Loss (and optionally gradient / alpha / beta tables) of one sample.
 
-    ``x`` holds the sample's T*(U+1) rows of V values (any float dtype; values
-    are converted exactly to fp64).  ``blank`` must already be in [0, V).
-    The loss is the beta-path value -beta(0,0); ``loss_alpha`` is the
-    alpha-path value kept for the cross-check.
+    ``x`` holds the sample's T*(U+1) rows of V values as float64, float32 or
+    float16; the C code converts each value exactly to fp64 as it reads it.
+    ``blank`` must already be in [0, V).  ``rows`` (sample-local row indices)
+    restricts the gradient to those rows, returned in that order; by default
+    every row.  The loss is the beta-path value -beta(0,0); ``loss_alpha`` is
+    the alpha-path value kept for the cross-check.
     """
     lib = _load()
-    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    x = np.asarray(x)
+    if x.dtype not in _DT:
+        x = x.astype(np.float64)
+    x = np.ascontiguousarray(x)
     V = x.shape[1]
     if x.shape[0] != T * (U + 1):
         raise ValueError("row count does not match T*(U+1)")
     yy = np.ascontiguousarray(np.asarray(y[:U], dtype=np.int32)) if U > 0 else np.zeros(1, np.int32)
-    grad = np.empty((T * (U + 1), V), np.float64) if want_grad else None
+    if rows is None:
+        rr, nr = None, -1
+        n_out = T * (U + 1)
+    else:
+        rr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nr = len(rr)
+        n_out = nr
+    grad = np.empty((n_out, V), np.float64) if want_grad else None
     al = np.empty((T, U + 1), np.float64) if want_tables else None
     be = np.empty((T, U + 1), np.float64) if want_tables else None
     la = ctypes.c_double()
     lb = ctypes.c_double()
-    rc = lib.rnnt_oracle_sample(_ptr(x), T, U, V, yy.ctypes.data_as(ctypes.POINTER(ctypes.c_int)),
-                                int(blank), int(bool(fused)), float(clamp), _ptr(grad), _ptr(al), _ptr(be),
-                                ctypes.byref(la), ctypes.byref(lb))
+    rc = lib.rnnt_oracle_sample_ex(
+        x.ctypes.data_as(ctypes.c_void_p), _DT[x.dtype], T, U, V, yy.ctypes.data_as(ctypes.POINTER(ctypes.c_int)),
+        int(blank), int(bool(fused)), float(clamp),
+        rr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)) if rr is not None else None, nr,
+        _ptr(grad), _ptr(al), _ptr(be), ctypes.byref(la), ctypes.byref(lb))
     if rc == ORACLE_BAD_TARGET:
         raise ValueError("target label equal to blank or outside [0, V)")
     if rc != ORACLE_OK:

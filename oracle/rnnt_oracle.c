@@ -41,6 +41,7 @@
  * oracle has no structure in common with the GPU kernels.
  */
 #include <math.h>
+#include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -48,6 +49,34 @@
 #define ORACLE_BAD_ARGS 1
 #define ORACLE_BAD_TARGET 2
 #define ORACLE_NO_MEMORY 3
+
+#define ORACLE_F64 0
+#define ORACLE_F32 1
+#define ORACLE_F16 2
+
+/* IEEE 754 binary16 -> binary64, exact (every half is a double). */
+static double half_to_double(uint16_t h)
+{
+    const int sign = (h >> 15) & 1;
+    const int expo = (h >> 10) & 0x1f;
+    const int mant = h & 0x3ff;
+    double v;
+    if (expo == 0) v = ldexp((double)mant, -24);                 /* zero / subnormal */
+    else if (expo == 31) v = mant ? NAN : INFINITY;              /* inf / nan */
+    else v = ldexp((double)(mant | 0x400), expo - 25);           /* normal */
+    return sign ? -v : v;
+}
+
+/* Element k of row r of the sample's input, converted exactly to fp64. */
+static double elem(const void *x, int dtype, long r, int V, int k)
+{
+    const long i = r * (long)V + k;
+    if (dtype == ORACLE_F32) return (double)((const float *)x)[i];
+    if (dtype == ORACLE_F16) return half_to_double(((const uint16_t *)x)[i]);
+    return ((const double *)x)[i];
+}
+
+double rnnt_oracle_half_to_double(uint16_t h) { return half_to_double(h); }
 
 /* log(exp(a) + exp(b)) with -inf handled: log(0 + 0) = -inf. */
 static double log_add(double a, double b)
@@ -59,36 +88,42 @@ static double log_add(double a, double b)
 }
 
 /* log-sum-exp of one row of V values, shifted by the row maximum. */
-static double row_logsumexp(const double *x, int V)
+static double row_logsumexp(const void *x, int dtype, long r, int V)
 {
     double m = -INFINITY;
-    for (int k = 0; k < V; ++k)
-        if (x[k] > m) m = x[k];
+    for (int k = 0; k < V; ++k) {
+        double v = elem(x, dtype, r, V, k);
+        if (v > m) m = v;
+    }
     if (m == -INFINITY) return -INFINITY;
     double s = 0.0;
-    for (int k = 0; k < V; ++k) s += exp(x[k] - m);
+    for (int k = 0; k < V; ++k) s += exp(elem(x, dtype, r, V, k) - m);
     return m + log(s);
 }
 
 /*
  * One sample.
- *   x        (T*(U+1)) x V row-major fp64 inputs (logits, or log-probs when
- *            fused == 0).
+ *   x        T*(U+1) rows of V values, row-major, of type dtype (ORACLE_F64,
+ *            _F32 or _F16); logits, or log-probs when fused == 0.  Values are
+ *            converted exactly to fp64 as they are read.
  *   y        U target labels; each must lie in [0,V) and differ from blank.
  *   blank    already normalised to [0,V).
- *   grad     optional (T*(U+1)) x V output: d loss / d x, clamped if clamp>0.
+ *   grad_rows, n_grad_rows   sample-local rows whose gradient is wanted
+ *            (NULL with n_grad_rows < 0 means every row, in order).
+ *   grad     optional n x V output (n = rows requested): d loss / d x of
+ *            those rows, clamped if clamp > 0.
  *   alpha, beta  optional T*(U+1) outputs of the log forward / backward
  *            variables (beta(t,u) includes the emissions at (t,u) onwards,
  *            so beta(0,0) = log P(y|x)).
  *   loss_alpha, loss_beta  -log P(y|x) from each recursion.
  * Returns ORACLE_OK or an error code.
  */
-int rnnt_oracle_sample(const double *x, int T, int U, int V, const int *y,
-                       int blank, int fused, double clamp, double *grad,
-                       double *alpha_out, double *beta_out,
-                       double *loss_alpha, double *loss_beta)
+int rnnt_oracle_sample_ex(const void *x, int dtype, int T, int U, int V, const int *y, int blank, int fused,
+                          double clamp, const int64_t *grad_rows, long n_grad_rows, double *grad,
+                          double *alpha_out, double *beta_out, double *loss_alpha, double *loss_beta)
 {
     if (T < 1 || U < 0 || V < 1 || blank < 0 || blank >= V) return ORACLE_BAD_ARGS;
+    if (dtype != ORACLE_F64 && dtype != ORACLE_F32 && dtype != ORACLE_F16) return ORACLE_BAD_ARGS;
     for (int u = 0; u < U; ++u)
         if (y[u] < 0 || y[u] >= V || y[u] == blank) return ORACLE_BAD_TARGET;
 
@@ -108,10 +143,9 @@ int rnnt_oracle_sample(const double *x, int T, int U, int V, const int *y,
     for (int t = 0; t < T; ++t) {
         for (int u = 0; u <= U; ++u) {
             long c = (long)t * U1 + u;
-            const double *row = x + c * V;
-            lse[c] = fused ? row_logsumexp(row, V) : 0.0;
-            lpb[c] = row[blank] - lse[c];
-            lpy[c] = (u < U) ? row[y[u]] - lse[c] : -INFINITY;
+            lse[c] = fused ? row_logsumexp(x, dtype, c, V) : 0.0;
+            lpb[c] = elem(x, dtype, c, V, blank) - lse[c];
+            lpy[c] = (u < U) ? elem(x, dtype, c, V, y[u]) - lse[c] : -INFINITY;
         }
     }
 
@@ -147,40 +181,43 @@ int rnnt_oracle_sample(const double *x, int T, int U, int V, const int *y,
     if (alpha_out) memcpy(alpha_out, al, sizeof(double) * cells);
     if (beta_out) memcpy(beta_out, be, sizeof(double) * cells);
 
-    /* Step 4: gradient by the chain rule. */
+    /* Step 4: gradient of the requested rows, by the chain rule. */
     if (grad) {
         const double logz = logz_beta;
-        for (int t = 0; t < T; ++t) {
-            for (int u = 0; u <= U; ++u) {
-                long c = (long)t * U1 + u;
-                double *g = grad + c * V;
-                const double *row = x + c * V;
-                /* d loss / d lp(blank) and d loss / d lp(y_{u+1}) at this node:
-                 * minus the posterior probability of taking that edge. */
-                double d_blank = 0.0, d_label = 0.0;
-                if (logz != -INFINITY) {
-                    if (t < T - 1)
-                        d_blank = -exp(al[c] + lpb[c] + be[c + U1] - logz);
-                    else if (u == U)
-                        d_blank = -exp(al[c] + lpb[c] - logz);
-                    if (u < U)
-                        d_label = -exp(al[c] + lpy[c] + be[c + 1] - logz);
+        const long n = (grad_rows == NULL || n_grad_rows < 0) ? cells : n_grad_rows;
+        for (long i = 0; i < n; ++i) {
+            long c = (grad_rows == NULL || n_grad_rows < 0) ? i : (long)grad_rows[i];
+            double *g = grad + i * V;
+            if (c < 0 || c >= cells) {
+                for (int k = 0; k < V; ++k) g[k] = NAN;
+                continue;
+            }
+            int t = (int)(c / U1), u = (int)(c % U1);
+            /* d loss / d lp(blank) and d loss / d lp(y_{u+1}) at this node:
+             * minus the posterior probability of taking that edge. */
+            double d_blank = 0.0, d_label = 0.0;
+            if (logz != -INFINITY) {
+                if (t < T - 1)
+                    d_blank = -exp(al[c] + lpb[c] + be[c + U1] - logz);
+                else if (u == U)
+                    d_blank = -exp(al[c] + lpb[c] - logz);
+                if (u < U)
+                    d_label = -exp(al[c] + lpy[c] + be[c + 1] - logz);
+            }
+            for (int k = 0; k < V; ++k) g[k] = 0.0;
+            g[blank] += d_blank;
+            if (u < U) g[y[u]] += d_label;
+            if (fused) {
+                double sum_d = d_blank + d_label;
+                for (int k = 0; k < V; ++k) {
+                    double p = (lse[c] == -INFINITY) ? 0.0 : exp(elem(x, dtype, c, V, k) - lse[c]);
+                    g[k] -= p * sum_d;
                 }
-                for (int k = 0; k < V; ++k) g[k] = 0.0;
-                g[blank] += d_blank;
-                if (u < U) g[y[u]] += d_label;
-                if (fused) {
-                    double sum_d = d_blank + d_label;
-                    for (int k = 0; k < V; ++k) {
-                        double p = (lse[c] == -INFINITY) ? 0.0 : exp(row[k] - lse[c]);
-                        g[k] -= p * sum_d;
-                    }
-                }
-                if (clamp > 0.0) {
-                    for (int k = 0; k < V; ++k) {
-                        if (g[k] > clamp) g[k] = clamp;
-                        if (g[k] < -clamp) g[k] = -clamp;
-                    }
+            }
+            if (clamp > 0.0) {
+                for (int k = 0; k < V; ++k) {
+                    if (g[k] > clamp) g[k] = clamp;
+                    if (g[k] < -clamp) g[k] = -clamp;
                 }
             }
         }
@@ -188,4 +225,12 @@ int rnnt_oracle_sample(const double *x, int T, int U, int V, const int *y,
 
     free(lse); free(lpb); free(lpy); free(al); free(be);
     return ORACLE_OK;
+}
+
+/* fp64 input, gradient of every row (the form the pins use). */
+int rnnt_oracle_sample(const double *x, int T, int U, int V, const int *y, int blank, int fused, double clamp,
+                       double *grad, double *alpha_out, double *beta_out, double *loss_alpha, double *loss_beta)
+{
+    return rnnt_oracle_sample_ex(x, ORACLE_F64, T, U, V, y, blank, fused, clamp, NULL, -1, grad, alpha_out,
+                                 beta_out, loss_alpha, loss_beta);
 }

@@ -293,3 +293,28 @@ def test_golden_readme_example():
             bl, _ = bruteforce.sample(logits[off:off + rows], T, U, gd["targets"][i], 7, True)
             assert abs(bl - case["loss_per_sample"][i]) < 1e-12
             off += rows
+
+
+def test_half_conversion_exact_for_every_half():
+    """The oracle reads fp16 inputs through its own binary16 decoder: all 65536 encodings."""
+    bits = np.arange(65536, dtype=np.uint16)
+    expect = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.half_to_double(int(b)) for b in bits])
+    same = (got == expect) | (np.isnan(got) & np.isnan(expect))
+    assert same.all()
+
+
+def test_native_dtypes_and_row_subsets():
+    """fp32 / fp16 inputs are read exactly; a row subset of the gradient equals those rows of the full one."""
+    rng = np.random.default_rng(14)
+    T, U, V, blank = 9, 4, 24, 0
+    x, y = _rand_case(rng, T, U, V, blank, std=2.0)
+    for dt in (np.float32, np.float16):
+        xd = x.astype(dt)
+        a = oracle.sample(xd, T, U, y, blank, True)
+        b = oracle.sample(xd.astype(np.float64), T, U, y, blank, True)
+        assert a.loss == b.loss
+        np.testing.assert_array_equal(a.grad, b.grad)
+        rows = [7, 0, T * (U + 1) - 1, 3]
+        c = oracle.sample(xd, T, U, y, blank, True, rows=rows)
+        np.testing.assert_array_equal(c.grad, a.grad[rows])
