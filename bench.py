@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Throughput of the fused RNN-T loss (forward + backward) on one MI355X.
+
+One step is one ``rnnt_loss_fused`` call over one seeded synthetic batch: the
+host schedule upload, the row-statistics pass, the alpha/beta recursions, the
+gradient pass and the loss reduction -- every step of the hot path.  Inputs,
+outputs and workspace are resident in HBM before the timed region starts.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload bpe]
+
+Prints one JSON line.  ``value`` is packed logits elements per second
+(N*V per step / time per step); the line also carries the effective HBM
+bandwidth of the whole step, the roofline of the dominant kernel (its
+algorithmic bytes per launch over its average launch time, measured with
+HIP events on the library's stream) and the fp64 CPU oracle timed on a
+bounded sample of the same batch on this host's cores.
+
+``--copy-calibration`` instead runs a plain device-to-device copy of known
+size, so that rocprofv3's FETCH_SIZE / WRITE_SIZE can be scaled to bytes.
+"""
+import argparse
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "packed logits elements/s (fwd+bwd) & effective HBM GB/s vs peak, 1 MI355X"
+PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E, AMD published peak
+KERNEL_SOURCE = os.path.join(ROOT, "rnn_transducer_loss_amd", "csrc", "rnnt_kernels.hip")
+KERNEL_SYMBOLS = {"rowstats": "k_rowstats", "alpha_beta": "k_alpha_beta", "grad": "k_grad", "reduce": "k_reduce"}
+
+
+def esize(dtype) -> int:
+    import torch
+    return 2 if dtype == torch.float16 else 4
+
+
+def algorithmic_bytes(w) -> dict:
+    """Bytes each pass must move at minimum, and the whole path's ideal.
+
+    Fused: the path reads the logits once and writes the gradient once
+    (N*V*(s_in + s_out)); non-fused: the gradient is written once and two
+    values per row are gathered.  Targets, lengths and losses are added.
+    """
+    s = esize(w.dtype)
+    NV = w.N * w.V
+    aux = w.targets.size * 4 + w.B * 4 * 3
+    if w.fused:
+        path = NV * (s + s) + aux
+        rowstats = NV * s
+        grad = NV * (s + s)
+    else:
+        path = NV * s + 2 * w.N * s + aux
+        rowstats = 2 * w.N * s
+        grad = NV * s
+    return {"path": path, "rowstats": rowstats, "grad": grad}
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def committed_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it matches this kernel source."""
+    want = kernel_source_hash()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        text = open(path).read()
+        for block in re.findall(r"```json\n(.*?)\n```", text, flags=re.S):
+            try:
+                d = json.loads(block)
+            except ValueError:
+                continue
+            if (d.get("kind") == "pmc_traffic" and d.get("kernel") == kernel and d.get("workload") == workload
+                    and d.get("source_sha256_16") == want):
+                return d.get("traffic_bytes_per_launch")
+    return None
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """The fp64 oracle on this host's cores over a bounded set of the batch's samples."""
+    import concurrent.futures as cf
+    import numpy as np
+    import oracle
+
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        avail = os.cpu_count() or 1
+    threads = max(1, min(16, avail))
+    b = w.blank + w.V if w.blank < 0 else w.blank
+    rows = (w.logit_lengths.astype(np.int64) * (w.target_lengths + 1))
+    # batch order, skipping samples whose fp64 gradient would exceed 1 GiB per thread
+    cand = [i for i in range(w.B) if rows[i] * w.V * 8 <= (1 << 30)]
+    host = {}
+
+    def one(i):
+        r = oracle.sample(host[i], int(w.logit_lengths[i]), int(w.target_lengths[i]), w.targets[i], b, w.fused,
+                          w.clamp, want_grad=True)
+        return int(rows[i]) * w.V, r.loss
+
+    done_elems, done_samples = 0, 0
+    elapsed = 0.0
+    with cf.ThreadPoolExecutor(threads) as ex:
+        k = 0
+        while k < len(cand) and elapsed < budget_s:
+            wave = cand[k:k + threads]
+            k += len(wave)
+            for i in wave:
+                host[i] = w.logits[w.rows(i)].cpu().numpy()
+            t0 = time.perf_counter()
+            for n, _ in ex.map(one, wave):
+                done_elems += n
+            elapsed += time.perf_counter() - t0
+            done_samples += len(wave)
+            for i in wave:
+                host.pop(i, None)
+    if done_samples == 0:
+        return None
+    return {"value": done_elems / elapsed, "unit": "elements/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done_samples} of {w.B} samples of the {w.name} batch ({done_elems} packed elements), "
+                      f"loss and full gradient, fp64, one sample per thread, {elapsed:.2f} s wall"}
+
+
+def copy_calibration(steps: int):
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        b.copy_(a)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms_per_copy": ms,
+                      "GBps_read_plus_write": 2 * n / ms / 1e6}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="bpe", choices=["tiny", "char", "bpe", "half", "skewed"])
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the loss is computed per sample and its batch is one GPU's share; "
+              "run it with --gpus 1 (a multi-GPU run would shard samples with no exchange).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
+
+    import rnn_transducer_loss_amd as rl
+    import workloads
+
+    print(f"bench: drawing workload {args.workload}", file=sys.stderr, flush=True)
+    w = workloads.make(args.workload, seed=args.seed, device="cuda")
+    tg = torch.from_numpy(w.targets).cuda()
+    T, U = w.logit_lengths, w.target_lengths
+    dev = w.logits.device
+    loss = torch.empty(w.B, dtype=torch.float32, device=dev)
+    red = torch.empty(1, dtype=torch.float32, device=dev)
+    grad = torch.empty_like(w.logits)
+    ws = torch.empty(rl.workspace_bytes(w.logits, T, U), dtype=torch.uint8, device=dev)
+
+    def step():
+        rl.rnnt_loss_fused(w.logits, tg, T, U, blank=w.blank, clamp=w.clamp, reduction=w.reduction,
+                           fused_log_softmax=w.fused, grad=grad, workspace=ws, loss=loss, loss_reduced=red)
+
+    print(f"bench: N={w.N} V={w.V} B={w.B}; warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    flags = rl.device_flags(ws)
+    torch.cuda.synchronize()
+
+    # whole-step timing: K steps bracketed by synchronisation on both sides
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3 / args.steps
+    ms = e0.elapsed_time(e1) / args.steps
+    print(f"bench: {ms:.4f} ms/step (host wall {wall_ms:.4f})", file=sys.stderr, flush=True)
+
+    # per-kernel timing: events around each launch, on the library's stream
+    rl._lib.timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = rl._lib.timing_read()
+    rl._lib.timing_enable(False)
+    per_kernel = {k: (v[0] / v[1] if v[1] else None) for k, v in kt.items()}
+
+    ab = algorithmic_bytes(w)
+    dominant = max((k for k in per_kernel if per_kernel[k] is not None), key=lambda k: per_kernel[k])
+    dom_bytes = ab.get(dominant)
+    roofline = None
+    if dom_bytes is not None:
+        ach = dom_bytes / (per_kernel[dominant] * 1e-3) / 1e9
+        traffic = committed_traffic(KERNEL_SYMBOLS[dominant], w.name)
+        roofline = {"bound": "hbm", "kernel": KERNEL_SYMBOLS[dominant], "achieved": round(ach, 1),
+                    "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4),
+                    "traffic": traffic, "algorithmic_bytes_per_launch": dom_bytes,
+                    "avg_launch_ms": round(per_kernel[dominant], 5)}
+
+    eff = ab["path"] / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w)
+
+    out = {
+        "metric": METRIC,
+        "value": w.N * w.V / (ms * 1e-3),
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "V": w.V, "rows": w.N, "elements": w.N * w.V,
+                   "io_dtype": "fp16" if esize(w.dtype) == 2 else "fp32", "fused_log_softmax": w.fused,
+                   "reduction": w.reduction, "clamp": w.clamp, "T_max": int(T.max()), "U_max": int(U.max()),
+                   "recursion_dtype": "f64"},
+        "effective_GBps": round(eff, 1),
+        "effective_frac_of_peak": round(eff / PEAK_HBM_GBPS, 4),
+        "algorithmic_bytes_per_step": ab["path"],
+        "kernel_ms": {k: (round(v, 5) if v is not None else None) for k, v in per_kernel.items()},
+        "host_wall_ms_per_step": round(wall_ms, 4),
+        "device_flags": flags,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

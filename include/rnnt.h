@@ -1,0 +1,202 @@
+/*
+ * rnnt.h -- C ABI of librnnt, a fused RNN-T (transducer) loss, forward and
+ * backward, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (rnnt-loss-ascend README: "Main features", the parameter
+ * table, "Constraints" and "Architecture"):
+ *
+ *   Each sample i has T_i encoder frames and U_i target labels y_1..y_{U_i}.
+ *   Its joiner logits cover the T_i x (U_i+1) lattice and are packed, without
+ *   padding, as T_i*(U_i+1) consecutive rows of V classes; samples follow each
+ *   other in batch order, so the whole input is a (N, V) row-major matrix with
+ *   N = sum_i T_i*(U_i+1).  Inside a sample, rows are t-major: row
+ *   t*(U_i+1) + u is lattice node (t,u).
+ *
+ *   With fused_log_softmax set, a log_softmax over V is applied at every node;
+ *   otherwise the inputs are taken as log-probabilities as they are.  The
+ *   loss of a sample is -log of the total probability of all alignments from
+ *   node (0,0) that emit blank to advance t and emit y_{u+1} to advance u, and
+ *   end by emitting blank at (T_i-1, U_i) (warp-transducer build post,
+ *   section 1.1; README "Value" section 2 gives the gradient of it).  The
+ *   forward (alpha) and backward (beta) log-space recursions are both run and
+ *   their two losses cross-checked (README "Value" section 3).
+ *
+ *   The gradient is with respect to the packed input (logits, or the given
+ *   log-probabilities when fused_log_softmax is 0).  With clamp > 0 every
+ *   gradient element of a sample is clipped to [-clamp, clamp] before the
+ *   reduction scale is applied (README "Operator features"); clamp <= 0
+ *   disables clipping.  Reduction none / mean / sum follows the README usage
+ *   example (mean is over the batch dimension).
+ *
+ * Conventions for every entry point:
+ *   - "host" pointers are read by the CPU during the call and may be reused
+ *     as soon as it returns; "device" pointers are HIP device memory.
+ *   - The caller owns every buffer.  The library performs no device memory
+ *     allocation.  It keeps a small reusable pinned host staging ring per
+ *     device for uploading the per-call schedule.
+ *   - All device work is enqueued on `stream` (a hipStream_t; NULL means the
+ *     default stream); calls return before it completes.
+ *   - Host-detectable argument errors return a non-zero rnnt_status before
+ *     anything is enqueued; outputs are then untouched.  Problems only the
+ *     device can see set bits in a status word kept in the workspace (see
+ *     rnnt_loss_fused_check).  No entry point aborts or throws.
+ */
+#ifndef RNNT_H_
+#define RNNT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *rnnt_stream_t; /* a hipStream_t */
+
+/* Element type of logits and grad (README parameter table: float32 / float16). */
+typedef enum { RNNT_F32 = 0, RNNT_F16 = 1 } rnnt_dtype;
+
+/* Reduction of the per-sample losses (README usage example). */
+typedef enum { RNNT_REDUCTION_NONE = 0, RNNT_REDUCTION_MEAN = 1, RNNT_REDUCTION_SUM = 2 } rnnt_reduction;
+
+typedef enum {
+    RNNT_SUCCESS = 0,
+    RNNT_INVALID_VALUE = 1,       /* an argument violates the constraints below */
+    RNNT_WORKSPACE_TOO_SMALL = 2, /* workspace_bytes below what _workspace_size reported */
+    RNNT_MEMOPS_FAILED = 3,       /* a HIP copy or host staging allocation failed */
+    RNNT_EXECUTION_FAILED = 4     /* a kernel launch failed */
+} rnnt_status;
+
+/* Bits of the device status word (read back by rnnt_loss_fused_check). */
+enum {
+    RNNT_DEV_LOSS_MISMATCH = 1u, /* |L_alpha - L_beta| > 1e-4 * max(1, |L_beta|) for some sample */
+    RNNT_DEV_BAD_TARGET = 2u     /* a label y_u lies outside [0, V) or equals blank */
+};
+
+/*
+ * Bytes of device workspace rnnt_loss_fused needs for this batch.
+ *
+ *   B                 number of samples, >= 1.
+ *   V                 classes per row (blank included), >= 1.
+ *   N                 rows of the packed logits; must equal sum_i T_i*(U_i+1).
+ *   dtype             RNNT_F32 or RNNT_F16.
+ *   logit_lengths     host int32[B]: T_i >= 1.
+ *   target_lengths    host int32[B]: 0 <= U_i <= 1023 (U_i+1 is the lattice
+ *                     width; the alpha/beta kernel keeps a whole anti-diagonal
+ *                     of up to 1024 nodes in one wavefront's registers).
+ *   workspace_bytes   out: required size; the caller allocates it (any
+ *                     alignment of 256 bytes or more) and passes it back.
+ * Runs every host-side check of rnnt_loss_fused that does not need the
+ * other pointers, so invalid lengths fail here first.  Touches no GPU.
+ */
+rnnt_status rnnt_loss_fused_workspace_size(int32_t B, int32_t V, int64_t N, rnnt_dtype dtype,
+                                           const int32_t *logit_lengths, const int32_t *target_lengths,
+                                           size_t *workspace_bytes);
+
+/*
+ * Fused loss and gradient (README "Architecture": one call produces both).
+ *
+ *   logits            device (N, V) row-major, dtype; the packed layout above.
+ *   targets           device int32 (B, S) row-major; row i holds y_1..y_{U_i}
+ *                     in its first U_i entries; the rest is never read.  May
+ *                     be NULL only when every U_i is 0.
+ *   S                 row stride of targets, >= max_i U_i.
+ *   logit_lengths, target_lengths   host int32[B], as for _workspace_size.
+ *   blank             in [-V, V-1]; a negative value counts from the end
+ *                     (-1 is V-1, -V is 0).
+ *   clamp             > 0 clips each per-sample gradient element to
+ *                     [-clamp, clamp]; <= 0 disables clipping.
+ *   fused_log_softmax non-zero: apply log_softmax over V at each node.
+ *   reduction         RNNT_REDUCTION_NONE / _MEAN / _SUM.
+ *   loss              device float[B]: per-sample loss -log P(y|x) (beta
+ *                     path), always fp32 whatever dtype is.
+ *   loss_reduced      device float[1] or NULL: sum (SUM) or sum/B (MEAN) of
+ *                     loss; ignored for NONE.
+ *   grad              device (N, V) of dtype, or NULL to skip the gradient.
+ *                     Receives d(reduced loss)/d(logits) for a unit upstream
+ *                     gradient: the clamped per-sample gradient, times 1/B
+ *                     for MEAN.  Every element is written; no zero fill is
+ *                     needed.  grad may equal logits exactly (in place);
+ *                     any other overlap is RNNT_INVALID_VALUE.
+ *   workspace         device, workspace_bytes >= the _workspace_size value.
+ *   stream            hipStream_t for all device work.
+ * Returns RNNT_INVALID_VALUE for a NULL required pointer, bad dtype or
+ * reduction, V < 1, B < 1, blank out of range, T_i < 1, U_i < 0, U_i > 1023, U_i > S,
+ * sum_i T_i*(U_i+1) != N or partial overlap of grad and logits;
+ * RNNT_WORKSPACE_TOO_SMALL; RNNT_MEMOPS_FAILED; RNNT_EXECUTION_FAILED.
+ * Invalid label values are only visible on the device: they set
+ * RNNT_DEV_BAD_TARGET, and a label outside [0, V) makes its sample's
+ * alignment impossible (loss +inf, gradient 0 for that sample).
+ */
+rnnt_status rnnt_loss_fused(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V,
+                            const int32_t *targets, int32_t S,
+                            const int32_t *logit_lengths, const int32_t *target_lengths, int32_t B,
+                            int64_t blank, float clamp, int fused_log_softmax, rnnt_reduction reduction,
+                            float *loss, float *loss_reduced, void *grad,
+                            void *workspace, size_t workspace_bytes, rnnt_stream_t stream);
+
+/*
+ * Multiply the gradient written by rnnt_loss_fused by an upstream gradient
+ * kept in device memory (the backward step of the reduction, README
+ * "Architecture": reduction is handled above the kernel).
+ *
+ *   grad, dtype, N, V, logit_lengths, target_lengths, B   as passed to the
+ *                 rnnt_loss_fused call that wrote grad.
+ *   scale         device float[1] (per_sample = 0) or float[B] (per_sample =
+ *                 1, for reduction NONE: the rows of sample i are scaled by
+ *                 scale[i]).
+ *   workspace     the workspace of that call, not reused by another call on
+ *                 a different batch in between (its schedule tables are read).
+ * Rows whose factor is exactly 1 are left untouched, so a unit upstream
+ * gradient costs no memory traffic.  Returns RNNT_INVALID_VALUE for NULL
+ * pointers or inconsistent sizes.
+ */
+rnnt_status rnnt_grad_scale(void *grad, rnnt_dtype dtype, int64_t N, int32_t V, const int32_t *logit_lengths,
+                            const int32_t *target_lengths, int32_t B, const float *scale, int per_sample,
+                            const void *workspace, size_t workspace_bytes, rnnt_stream_t stream);
+
+/*
+ * Synchronises `stream`, then copies into *dev_flags the device status word
+ * (RNNT_DEV_* bits) of the most recent rnnt_loss_fused call that used
+ * `workspace`; every rnnt_loss_fused call clears it when it starts.
+ */
+rnnt_status rnnt_loss_fused_check(void *workspace, rnnt_stream_t stream, uint32_t *dev_flags);
+
+/* Static English description of a status code. */
+const char *rnnt_status_string(rnnt_status s);
+
+/*
+ * Host-side schedule of a batch, for inspection and tests; touches no GPU.
+ * Fills up to `cap` entries of each array:
+ *   sample_order  int32[B]: samples by decreasing lattice area T*(U+1)
+ *                 (ties: larger T+U first, then lower index) -- the order in
+ *                 which the alpha/beta work of each sample is started.
+ *   chunk_sample, chunk_row_begin, chunk_row_count   int32[n_chunks]: the
+ *                 row chunks of the row passes, in issue order; each chunk
+ *                 lies inside one sample; rows are sample-local.
+ *   n_chunks      out: total number of chunks (may exceed cap).
+ * Returns RNNT_INVALID_VALUE under the same length checks as _workspace_size.
+ */
+rnnt_status rnnt_plan_describe(int32_t B, int32_t V, rnnt_dtype dtype,
+                               const int32_t *logit_lengths, const int32_t *target_lengths,
+                               int32_t cap, int32_t *sample_order, int32_t *chunk_sample,
+                               int32_t *chunk_row_begin, int32_t *chunk_row_count, int32_t *n_chunks);
+
+/*
+ * Per-kernel timing for measurement.  While enabled, every rnnt_loss_fused
+ * call brackets each of its kernels with HIP events on its own stream.
+ * rnnt_timing_read synchronises on the recorded events and returns, for
+ * each kernel, the summed device milliseconds and the number of launches
+ * since timing was enabled (index 0 rowstats / gather, 1 alpha_beta,
+ * 2 grad, 3 reduce); ms and launches are arrays of 4, either may be NULL.
+ * rnnt_timing_enable(0) stops recording and discards what was recorded.
+ * Not for concurrent use from several threads.
+ */
+rnnt_status rnnt_timing_enable(int on);
+rnnt_status rnnt_timing_read(double *ms, int32_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RNNT_H_ */

@@ -1,0 +1,445 @@
+// Host side of librnnt: argument validation, the longest-first schedule, the
+// workspace layout, the schedule upload and the kernel launch sequence behind
+// the C ABI declared in include/rnnt.h.
+//
+// The two-phase interface (query the workspace size, then run with a caller
+// allocated workspace) and the host-side placement of samples by decreasing
+// lattice area follow the rnnt-loss-ascend README ("Architecture": the aclnn
+// layer's workspace query and the host's largest-task-first / least-loaded
+// balancing; "Operator features": samples sorted by T x U area).
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <numeric>
+#include <vector>
+
+#include "rnnt_internal.h"
+
+namespace rnnt {
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+    std::vector<SampleDesc> desc;
+    std::vector<int32_t> order;
+    std::vector<ChunkDesc> chunks;
+    WorkspaceLayout lay{};
+    int max_U1 = 1;
+};
+
+rnnt_status check_lengths(int32_t B, int32_t V, const int32_t *T, const int32_t *U) {
+    if (B < 1 || V < 1 || !T || !U) return RNNT_INVALID_VALUE;
+    for (int32_t i = 0; i < B; ++i) {
+        if (T[i] < 1 || U[i] < 0) return RNNT_INVALID_VALUE;
+        if (U[i] + 1 > kMaxU1) return RNNT_INVALID_VALUE;
+    }
+    return RNNT_SUCCESS;
+}
+
+// Samples by decreasing cost: lattice area T*(U+1) (the README's balancing
+// key), then the length T+U of the recursion's critical path, then index.
+std::vector<int32_t> lpt_order(int32_t B, const int32_t *T, const int32_t *U) {
+    std::vector<int32_t> ord(B);
+    std::iota(ord.begin(), ord.end(), 0);
+    std::stable_sort(ord.begin(), ord.end(), [&](int32_t a, int32_t b) {
+        const int64_t aa = (int64_t)T[a] * (U[a] + 1), ab = (int64_t)T[b] * (U[b] + 1);
+        if (aa != ab) return aa > ab;
+        const int64_t la = (int64_t)T[a] + U[a], lb = (int64_t)T[b] + U[b];
+        if (la != lb) return la > lb;
+        return a < b;
+    });
+    return ord;
+}
+
+// Rows per chunk: about 256 KiB of logits per workgroup, but at least ~1024
+// chunks when the batch is small, rounded to a multiple of 64 rows (the most
+// rows any row geometry's workgroup takes per iteration), so the chunk table
+// does not depend on the geometry.
+int32_t rows_per_chunk(int64_t N, int32_t V, int esize) {
+    const int64_t row_bytes = (int64_t)V * esize;
+    const int64_t by_bytes = std::max<int64_t>(1, (256 * 1024) / std::max<int64_t>(1, row_bytes));
+    const int64_t by_count = std::max<int64_t>(1, (N + 1023) / 1024);
+    int64_t r = std::min(by_bytes, by_count);
+    r = (r + 63) / 64 * 64;
+    return (int32_t)std::min<int64_t>(r, 1 << 16);
+}
+
+rnnt_status build_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t *T, const int32_t *U,
+                       Plan &p) {
+    rnnt_status st = check_lengths(B, V, T, U);
+    if (st != RNNT_SUCCESS) return st;
+    p.desc.resize(B);
+    int64_t row = 0, slot = 0;
+    p.max_U1 = 1;
+    for (int32_t i = 0; i < B; ++i) {
+        SampleDesc &d = p.desc[i];
+        d.row_off = row;
+        d.slot_off = slot;
+        d.T = T[i];
+        d.U = U[i];
+        d.index = i;
+        d.pad = 0;
+        row += (int64_t)T[i] * (U[i] + 1);
+        slot += ((int64_t)T[i] + U[i]) * (U[i] + 1);
+        p.max_U1 = std::max(p.max_U1, U[i] + 1);
+    }
+    if (N >= 0 && row != N) return RNNT_INVALID_VALUE;
+    if (row >= ((int64_t)1 << 62) / std::max(1, V)) return RNNT_INVALID_VALUE;
+    p.order = lpt_order(B, T, U);
+    const int32_t rpc = rows_per_chunk(row, V, esize);
+    p.chunks.clear();
+    for (int32_t k = 0; k < B; ++k) {
+        const int32_t i = p.order[k];
+        const int64_t rows = (int64_t)T[i] * (U[i] + 1);
+        if (rows > INT32_MAX) return RNNT_INVALID_VALUE;
+        for (int64_t r0 = 0; r0 < rows; r0 += rpc) {
+            ChunkDesc c;
+            c.sample = i;
+            c.row_begin = (int32_t)r0;
+            c.row_count = (int32_t)std::min<int64_t>(rpc, rows - r0);
+            c.pad = 0;
+            p.chunks.push_back(c);
+        }
+    }
+    if (p.chunks.size() > (size_t)INT32_MAX) return RNNT_INVALID_VALUE;
+    WorkspaceLayout &L = p.lay;
+    size_t off = 0;
+    L.status = off; off = align_up(off + 64);
+    L.desc = off;   off = align_up(off + sizeof(SampleDesc) * B);
+    L.order = off;  off = align_up(off + sizeof(int32_t) * B);
+    L.chunks = off; off = align_up(off + sizeof(ChunkDesc) * p.chunks.size());
+    L.den = off;    off = align_up(off + sizeof(float) * (size_t)row);
+    L.lpb = off;    off = align_up(off + sizeof(float) * (size_t)slot);
+    L.lpy = off;    off = align_up(off + sizeof(float) * (size_t)slot);
+    L.alpha = off;  off = align_up(off + sizeof(double) * (size_t)slot);
+    L.beta = off;   off = align_up(off + sizeof(double) * (size_t)slot);
+    L.total = off;
+    L.n_slots = slot;
+    L.n_chunks = (int32_t)p.chunks.size();
+    L.rows_per_chunk = rpc;
+    return RNNT_SUCCESS;
+}
+
+int esize_of(rnnt_dtype dt) { return dt == RNNT_F32 ? 4 : (dt == RNNT_F16 ? 2 : 0); }
+
+// ------------------------------------------------------------ upload staging
+// A small ring of pinned host buffers per device.  Each upload copies the
+// schedule into the next slot, enqueues an asynchronous copy on the caller's
+// stream and records an event; a slot is reused only after its event has
+// completed, so the caller's host memory is never referenced after return.
+struct StagingSlot {
+    void *host = nullptr;
+    size_t cap = 0;
+    hipEvent_t ev = nullptr;
+    bool pending = false;
+};
+struct StagingRing {
+    StagingSlot slot[8];
+    int next = 0;
+};
+std::mutex g_mu;
+std::map<int, StagingRing> g_rings;
+
+rnnt_status upload(void *dst, const std::vector<uint8_t> &src, hipStream_t stream) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return RNNT_MEMOPS_FAILED;
+    std::lock_guard<std::mutex> lk(g_mu);
+    StagingRing &ring = g_rings[dev];
+    StagingSlot &s = ring.slot[ring.next];
+    ring.next = (ring.next + 1) % 8;
+    if (s.pending) {
+        if (hipEventSynchronize(s.ev) != hipSuccess) return RNNT_MEMOPS_FAILED;
+        s.pending = false;
+    }
+    if (!s.ev && hipEventCreateWithFlags(&s.ev, hipEventDisableTiming) != hipSuccess) return RNNT_MEMOPS_FAILED;
+    if (s.cap < src.size()) {
+        if (s.host) (void)hipHostFree(s.host);
+        s.host = nullptr;
+        s.cap = 0;
+        const size_t want = std::max<size_t>(src.size() + src.size() / 2, 64 * 1024);
+        if (hipHostMalloc(&s.host, want, hipHostMallocDefault) != hipSuccess) return RNNT_MEMOPS_FAILED;
+        s.cap = want;
+    }
+    std::memcpy(s.host, src.data(), src.size());
+    if (hipMemcpyAsync(dst, s.host, src.size(), hipMemcpyHostToDevice, stream) != hipSuccess)
+        return RNNT_MEMOPS_FAILED;
+    if (hipEventRecord(s.ev, stream) != hipSuccess) return RNNT_MEMOPS_FAILED;
+    s.pending = true;
+    return RNNT_SUCCESS;
+}
+
+// The header, descriptors, order and chunks are contiguous at the start of
+// the workspace and go up in one copy (the status word is cleared with it).
+std::vector<uint8_t> pack_plan(const Plan &p) {
+    std::vector<uint8_t> buf(p.lay.den, 0);
+    std::memcpy(buf.data() + p.lay.desc, p.desc.data(), sizeof(SampleDesc) * p.desc.size());
+    std::memcpy(buf.data() + p.lay.order, p.order.data(), sizeof(int32_t) * p.order.size());
+    std::memcpy(buf.data() + p.lay.chunks, p.chunks.data(), sizeof(ChunkDesc) * p.chunks.size());
+    return buf;
+}
+
+bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+// The schedule depends only on (B, V, dtype, lengths); the last one built is
+// reused when a call repeats them, as training steps and the upstream
+// gradient pass do.
+struct PlanEntry {
+    std::vector<int32_t> key;
+    Plan plan;
+    std::vector<uint8_t> packed;
+};
+std::mutex g_plan_mu;
+std::shared_ptr<const PlanEntry> g_plan_cache;
+
+std::vector<int32_t> plan_key(int32_t B, int32_t V, int esize, const int32_t *T, const int32_t *U) {
+    std::vector<int32_t> k;
+    k.reserve(3 + 2 * (size_t)B);
+    k.push_back(B);
+    k.push_back(V);
+    k.push_back(esize);
+    k.insert(k.end(), T, T + B);
+    k.insert(k.end(), U, U + B);
+    return k;
+}
+
+rnnt_status get_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t *T, const int32_t *U,
+                     std::shared_ptr<const PlanEntry> &out) {
+    rnnt_status st = check_lengths(B, V, T, U);
+    if (st != RNNT_SUCCESS) return st;
+    std::vector<int32_t> key = plan_key(B, V, esize, T, U);
+    {
+        std::lock_guard<std::mutex> lk(g_plan_mu);
+        if (g_plan_cache && g_plan_cache->key == key) out = g_plan_cache;
+        else out.reset();
+    }
+    if (!out) {
+        auto e = std::make_shared<PlanEntry>();
+        st = build_plan(B, V, -1, esize, T, U, e->plan);
+        if (st != RNNT_SUCCESS) return st;
+        e->key = std::move(key);
+        e->packed = pack_plan(e->plan);
+        std::lock_guard<std::mutex> lk(g_plan_mu);
+        g_plan_cache = e;
+        out = e;
+    }
+    int64_t rows = 0;
+    for (int32_t i = 0; i < B; ++i) rows += (int64_t)T[i] * (U[i] + 1);
+    if (N >= 0 && rows != N) return RNNT_INVALID_VALUE;
+    return RNNT_SUCCESS;
+}
+
+// ------------------------------------------------------------- kernel timing
+constexpr int kTimedKernels = 4;
+struct TimingState {
+    bool on = false;
+    std::vector<hipEvent_t> pool;                       // reusable events
+    std::vector<std::pair<int, std::pair<hipEvent_t, hipEvent_t>>> recs;  // (kernel, (start, stop))
+    size_t used = 0;
+};
+std::mutex g_time_mu;
+TimingState g_time;
+
+hipEvent_t timing_event() {
+    if (g_time.used == g_time.pool.size()) {
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        g_time.pool.push_back(e);
+    }
+    return g_time.pool[g_time.used++];
+}
+
+// Launches `fn` on `stream`, bracketed by timing events when timing is on.
+template <typename F> hipError_t timed(int kernel, hipStream_t stream, F &&fn) {
+    std::unique_lock<std::mutex> lk(g_time_mu);
+    if (!g_time.on) {
+        lk.unlock();
+        return fn();
+    }
+    hipEvent_t a = timing_event(), b = timing_event();
+    if (a) (void)hipEventRecord(a, stream);
+    const hipError_t err = fn();
+    if (b) (void)hipEventRecord(b, stream);
+    if (a && b) g_time.recs.push_back({kernel, {a, b}});
+    return err;
+}
+
+}  // namespace
+}  // namespace rnnt
+
+using namespace rnnt;
+
+extern "C" {
+
+const char *rnnt_status_string(rnnt_status s) {
+    switch (s) {
+    case RNNT_SUCCESS: return "success";
+    case RNNT_INVALID_VALUE: return "invalid argument value";
+    case RNNT_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case RNNT_MEMOPS_FAILED: return "HIP memory operation failed";
+    case RNNT_EXECUTION_FAILED: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+rnnt_status rnnt_loss_fused_workspace_size(int32_t B, int32_t V, int64_t N, rnnt_dtype dtype,
+                                           const int32_t *logit_lengths, const int32_t *target_lengths,
+                                           size_t *workspace_bytes) {
+    const int es = esize_of(dtype);
+    if (!es || !workspace_bytes || N < 0) return RNNT_INVALID_VALUE;
+    std::shared_ptr<const PlanEntry> e;
+    rnnt_status st = get_plan(B, V, N, es, logit_lengths, target_lengths, e);
+    if (st != RNNT_SUCCESS) return st;
+    *workspace_bytes = e->plan.lay.total;
+    return RNNT_SUCCESS;
+}
+
+rnnt_status rnnt_plan_describe(int32_t B, int32_t V, rnnt_dtype dtype, const int32_t *logit_lengths,
+                               const int32_t *target_lengths, int32_t cap, int32_t *sample_order,
+                               int32_t *chunk_sample, int32_t *chunk_row_begin, int32_t *chunk_row_count,
+                               int32_t *n_chunks) {
+    const int es = esize_of(dtype);
+    if (!es || cap < 0) return RNNT_INVALID_VALUE;
+    Plan p;
+    rnnt_status st = build_plan(B, V, -1, es, logit_lengths, target_lengths, p);
+    if (st != RNNT_SUCCESS) return st;
+    if (sample_order)
+        for (int32_t k = 0; k < B && k < cap; ++k) sample_order[k] = p.order[k];
+    const int32_t nc = (int32_t)p.chunks.size();
+    for (int32_t k = 0; k < nc && k < cap; ++k) {
+        if (chunk_sample) chunk_sample[k] = p.chunks[k].sample;
+        if (chunk_row_begin) chunk_row_begin[k] = p.chunks[k].row_begin;
+        if (chunk_row_count) chunk_row_count[k] = p.chunks[k].row_count;
+    }
+    if (n_chunks) *n_chunks = nc;
+    return RNNT_SUCCESS;
+}
+
+rnnt_status rnnt_loss_fused(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V, const int32_t *targets,
+                            int32_t S, const int32_t *logit_lengths, const int32_t *target_lengths, int32_t B,
+                            int64_t blank, float clamp, int fused_log_softmax, rnnt_reduction reduction,
+                            float *loss, float *loss_reduced, void *grad, void *workspace, size_t workspace_bytes,
+                            rnnt_stream_t stream_) {
+    const int es = esize_of(dtype);
+    if (!es || N < 0 || V < 1 || B < 1) return RNNT_INVALID_VALUE;
+    if (reduction != RNNT_REDUCTION_NONE && reduction != RNNT_REDUCTION_MEAN && reduction != RNNT_REDUCTION_SUM)
+        return RNNT_INVALID_VALUE;
+    if (blank < -(int64_t)V || blank > (int64_t)V - 1) return RNNT_INVALID_VALUE;
+    if (!logit_lengths || !target_lengths || !loss || !workspace) return RNNT_INVALID_VALUE;
+    if (N > 0 && !logits) return RNNT_INVALID_VALUE;
+    int32_t maxU = 0;
+    for (int32_t i = 0; i < B; ++i) maxU = std::max(maxU, target_lengths[i]);
+    if (maxU > 0 && (!targets || S < maxU)) return RNNT_INVALID_VALUE;
+    if (S < 0) return RNNT_INVALID_VALUE;
+    const size_t bytes = (size_t)N * (size_t)V * (size_t)es;
+    if (grad && grad != logits && bytes > 0 && ranges_overlap(grad, bytes, logits, bytes)) return RNNT_INVALID_VALUE;
+    const bool aligned16 = ((int64_t)V * es) % 16 == 0 && ((uintptr_t)logits % 16 == 0) &&
+                           (!grad || (uintptr_t)grad % 16 == 0);
+    std::shared_ptr<const PlanEntry> e;
+    rnnt_status st = get_plan(B, V, N, es, logit_lengths, target_lengths, e);
+    if (st != RNNT_SUCCESS) return st;
+    const Plan &plan = e->plan;
+    if (workspace_bytes < plan.lay.total) return RNNT_WORKSPACE_TOO_SMALL;
+    if ((uintptr_t)workspace % kAlign != 0) return RNNT_INVALID_VALUE;
+
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    st = upload(workspace, e->packed, stream);
+    if (st != RNNT_SUCCESS) return st;
+
+    LaunchArgs a{};
+    a.logits = logits;
+    a.grad = grad;
+    a.esize = es;
+    a.N = N;
+    a.V = V;
+    a.B = B;
+    a.S = S;
+    a.blank = (int)(blank < 0 ? blank + V : blank);
+    a.fused = fused_log_softmax ? 1 : 0;
+    a.clamp = clamp;
+    a.grad_scale = reduction == RNNT_REDUCTION_MEAN ? 1.0f / (float)B : 1.0f;
+    a.targets = targets;
+    a.loss = loss;
+    a.loss_reduced = loss_reduced;
+    a.reduction = reduction;
+    a.ws = static_cast<uint8_t *>(workspace);
+    a.lay = plan.lay;
+    a.geom = row_geometry(V, es, aligned16);
+    a.max_U1 = plan.max_U1;
+    a.aligned16 = aligned16;
+
+    if (plan.lay.n_chunks > 0 && timed(0, stream, [&] { return launch_rowstats(a, stream); }) != hipSuccess)
+        return RNNT_EXECUTION_FAILED;
+    if (timed(1, stream, [&] { return launch_alpha_beta(a, stream); }) != hipSuccess) return RNNT_EXECUTION_FAILED;
+    if (grad && plan.lay.n_chunks > 0 && timed(2, stream, [&] { return launch_grad(a, stream); }) != hipSuccess)
+        return RNNT_EXECUTION_FAILED;
+    if (reduction != RNNT_REDUCTION_NONE && loss_reduced &&
+        timed(3, stream, [&] { return launch_reduce(a, stream); }) != hipSuccess)
+        return RNNT_EXECUTION_FAILED;
+    return RNNT_SUCCESS;
+}
+
+rnnt_status rnnt_grad_scale(void *grad, rnnt_dtype dtype, int64_t N, int32_t V, const int32_t *logit_lengths,
+                            const int32_t *target_lengths, int32_t B, const float *scale, int per_sample,
+                            const void *workspace, size_t workspace_bytes, rnnt_stream_t stream_) {
+    const int es = esize_of(dtype);
+    if (!es || !grad || !scale || !workspace || V < 1 || B < 1 || N < 0) return RNNT_INVALID_VALUE;
+    std::shared_ptr<const PlanEntry> e;
+    rnnt_status st = get_plan(B, V, N, es, logit_lengths, target_lengths, e);
+    if (st != RNNT_SUCCESS) return st;
+    const Plan &p = e->plan;
+    if (workspace_bytes < p.lay.total) return RNNT_WORKSPACE_TOO_SMALL;
+    if (p.lay.n_chunks == 0) return RNNT_SUCCESS;
+    const bool aligned16 = ((int64_t)V * es) % 16 == 0 && (uintptr_t)grad % 16 == 0;
+    if (launch_grad_scale(grad, es, V, scale, per_sample, static_cast<const uint8_t *>(workspace), p.lay,
+                          row_geometry(V, es, aligned16), aligned16, static_cast<hipStream_t>(stream_)) != hipSuccess)
+        return RNNT_EXECUTION_FAILED;
+    return RNNT_SUCCESS;
+}
+
+rnnt_status rnnt_timing_enable(int on) {
+    std::lock_guard<std::mutex> lk(g_time_mu);
+    g_time.on = on != 0;
+    g_time.recs.clear();
+    g_time.used = 0;
+    return RNNT_SUCCESS;
+}
+
+rnnt_status rnnt_timing_read(double *ms, int32_t *launches) {
+    std::lock_guard<std::mutex> lk(g_time_mu);
+    double acc[kTimedKernels] = {0, 0, 0, 0};
+    int32_t cnt[kTimedKernels] = {0, 0, 0, 0};
+    for (auto &r : g_time.recs) {
+        if (hipEventSynchronize(r.second.second) != hipSuccess) return RNNT_MEMOPS_FAILED;
+        float t = 0.f;
+        if (hipEventElapsedTime(&t, r.second.first, r.second.second) != hipSuccess) return RNNT_MEMOPS_FAILED;
+        acc[r.first] += t;
+        cnt[r.first] += 1;
+    }
+    for (int k = 0; k < kTimedKernels; ++k) {
+        if (ms) ms[k] = acc[k];
+        if (launches) launches[k] = cnt[k];
+    }
+    return RNNT_SUCCESS;
+}
+
+rnnt_status rnnt_loss_fused_check(void *workspace, rnnt_stream_t stream_, uint32_t *dev_flags) {
+    if (!workspace || !dev_flags) return RNNT_INVALID_VALUE;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    uint32_t v = 0;
+    if (hipMemcpyAsync(&v, workspace, sizeof(v), hipMemcpyDeviceToHost, stream) != hipSuccess)
+        return RNNT_MEMOPS_FAILED;
+    if (hipStreamSynchronize(stream) != hipSuccess) return RNNT_MEMOPS_FAILED;
+    *dev_flags = v;
+    return RNNT_SUCCESS;
+}
+
+}  // extern "C"

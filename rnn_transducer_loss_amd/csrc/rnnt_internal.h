@@ -1,0 +1,96 @@
+// Internal declarations shared by the librnnt host code (rnnt_api.cpp) and
+// its gfx950 kernels (rnnt_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "rnnt.h"
+
+namespace rnnt {
+
+// One sample of the packed batch.  Rows are t-major: packed row
+// row_off + t*(U+1) + u is lattice node (t,u).  The per-node scalars of the
+// recursions live in a skewed layout, one slot per (anti-diagonal n = t+u, u):
+// slot_off + n*(U+1) + u, n in [0, T+U), so every anti-diagonal is contiguous.
+struct SampleDesc {
+    int64_t row_off;
+    int64_t slot_off;
+    int32_t T;
+    int32_t U;
+    int32_t index;  // position of the sample in the batch (targets row)
+    int32_t pad;
+};
+
+// A run of rows of one sample processed by one workgroup of the row passes.
+struct ChunkDesc {
+    int32_t sample;
+    int32_t row_begin;  // sample-local first row
+    int32_t row_count;
+    int32_t pad;
+};
+
+// Byte offsets of the workspace regions (each 256-byte aligned).
+struct WorkspaceLayout {
+    size_t status;   // uint32 status word + reserved header
+    size_t desc;     // SampleDesc[B]
+    size_t order;    // int32[B], samples by decreasing cost
+    size_t chunks;   // ChunkDesc[n_chunks]
+    size_t den;      // float[N], per-row log-sum-exp (fused only)
+    size_t lpb;      // float[S], log P(blank) per slot
+    size_t lpy;      // float[S], log P(next label) per slot
+    size_t alpha;    // double[S]
+    size_t beta;     // double[S]
+    size_t total;
+    int64_t n_slots;
+    int32_t n_chunks;
+    int32_t rows_per_chunk;
+};
+
+// Row-pass geometry chosen from V and the element size.
+struct RowGeom {
+    int lanes_per_row;  // G: 1..64 lanes cooperate on one row (power of two)
+    int vec;            // elements per vector access (1 when rows are not 16-byte aligned)
+    int rows_per_block_iter;
+};
+
+RowGeom row_geometry(int V, int esize, bool aligned16);
+
+// Kernel launchers (defined in rnnt_kernels.hip).  All enqueue on `stream`
+// and return the launch status.
+struct LaunchArgs {
+    const void *logits;
+    void *grad;
+    int esize;           // 4 (fp32) or 2 (fp16)
+    int64_t N;
+    int V;
+    int B;
+    int S;               // targets row stride
+    int blank;           // normalised
+    int fused;
+    float clamp;         // <= 0: off
+    float grad_scale;    // 1 or 1/B
+    const int32_t *targets;
+    float *loss;
+    float *loss_reduced;
+    int reduction;
+    uint8_t *ws;
+    WorkspaceLayout lay;
+    RowGeom geom;
+    int max_U1;          // max_i (U_i + 1)
+    bool aligned16;
+};
+
+hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream);
+hipError_t launch_alpha_beta(const LaunchArgs &a, hipStream_t stream);
+hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream);
+hipError_t launch_reduce(const LaunchArgs &a, hipStream_t stream);
+hipError_t launch_grad_scale(void *grad, int esize, int V, const float *scale, int per_sample,
+                             const uint8_t *ws, const WorkspaceLayout &lay, const RowGeom &geom,
+                             bool aligned16, hipStream_t stream);
+
+// Largest lattice width (U+1) the alpha/beta kernel supports.
+constexpr int kMaxU1 = 1024;
+
+}  // namespace rnnt

@@ -1,0 +1,158 @@
+"""PyTorch front end of librnnt: ``rnnt_loss`` with autograd, and a low-level call.
+
+Signature and semantics follow the rnnt-loss-ascend README (parameter table,
+usage example): ``rnnt_loss(logits, targets, logit_lengths, target_lengths,
+blank=-1, clamp=-1.0, reduction="mean", fused_log_softmax=True)`` on packed
+``(sum_i T_i*(U_i+1), V)`` logits; ``loss.backward()`` fills ``logits.grad``.
+
+This module only marshals arguments.  The loss, the gradient, the reduction
+and the backward scaling all run in librnnt's kernels on the current HIP
+stream; PyTorch provides the device buffers.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.float32: _lib.RNNT_F32, torch.float16: _lib.RNNT_F16}
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt not in _DTYPES:
+        raise ValueError(f"logits must be float32 or float16, got {dt}")
+    return _DTYPES[dt]
+
+
+def _prepare(logits: torch.Tensor, targets: torch.Tensor):
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 2:
+        raise ValueError("logits must be a 2-D (sum_i T_i*(U_i+1), V) tensor")
+    if logits.device.type != "cuda":
+        raise ValueError("logits must be on a GPU device")
+    if not logits.is_contiguous():
+        raise ValueError("logits must be contiguous")
+    if targets.dim() == 1:
+        targets = targets.unsqueeze(0)
+    if targets.dim() != 2:
+        raise ValueError("targets must be a 2-D (B, S) tensor")
+    tg = targets.to(device=logits.device, dtype=torch.int32).contiguous()
+    return tg
+
+
+def workspace_bytes(logits: torch.Tensor, logit_lengths, target_lengths) -> int:
+    T = _lib.host_i32(logit_lengths)
+    U = _lib.host_i32(target_lengths)
+    return _lib.workspace_size(len(T), logits.shape[1], logits.shape[0], _dtype_code(logits.dtype), T, U)
+
+
+def rnnt_loss_fused(logits: torch.Tensor, targets: torch.Tensor, logit_lengths, target_lengths, blank: int = -1,
+                    clamp: float = -1.0, reduction: str = "mean", fused_log_softmax: bool = True,
+                    compute_grad: bool = True, grad: Optional[torch.Tensor] = None, inplace: bool = False,
+                    workspace: Optional[torch.Tensor] = None, loss: Optional[torch.Tensor] = None,
+                    loss_reduced: Optional[torch.Tensor] = None):
+    """One librnnt call.  Returns ``(loss, loss_reduced, grad, workspace)``.
+
+    ``loss`` is the fp32 per-sample loss (B,), ``loss_reduced`` a (1,) fp32
+    tensor for mean/sum (None for none).  ``grad`` is d(reduced loss)/d(logits)
+    for a unit upstream gradient (clamped per sample, times 1/B for mean), in
+    the logits dtype; with ``inplace=True`` it is written over ``logits``.
+    Buffers may be passed in to avoid allocation (the bench does).
+    """
+    tg = _prepare(logits, targets)
+    T = _lib.host_i32(logit_lengths)
+    U = _lib.host_i32(target_lengths)
+    B = len(T)
+    if len(U) != B:
+        raise ValueError("logit_lengths and target_lengths must have the same length")
+    dev = logits.device
+    code = _dtype_code(logits.dtype)
+    N, V = logits.shape
+    need = _lib.workspace_size(B, V, N, code, T, U)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if loss is None:
+        loss = torch.empty(B, dtype=torch.float32, device=dev)
+    if reduction != "none" and loss_reduced is None:
+        loss_reduced = torch.empty(1, dtype=torch.float32, device=dev)
+    if compute_grad:
+        if inplace:
+            grad = logits
+        elif grad is None:
+            grad = torch.empty_like(logits)
+        elif grad.shape != logits.shape or grad.dtype != logits.dtype or not grad.is_contiguous():
+            raise ValueError("grad must match logits in shape and dtype and be contiguous")
+    else:
+        grad = None
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        _lib.loss_fused(logits.data_ptr(), code, N, V, tg.data_ptr() if tg.numel() else 0, tg.shape[1], T, U, blank,
+                        clamp, fused_log_softmax, reduction, loss.data_ptr(),
+                        loss_reduced.data_ptr() if reduction != "none" else 0,
+                        grad.data_ptr() if grad is not None else 0, workspace.data_ptr(), workspace.numel(), stream)
+    return loss, (loss_reduced if reduction != "none" else None), grad, workspace
+
+
+def device_flags(workspace: torch.Tensor) -> int:
+    """RNNT_DEV_* bits of the last call on ``workspace`` (synchronises the current stream)."""
+    with torch.cuda.device(workspace.device):
+        return _lib.device_flags(workspace.data_ptr(), torch.cuda.current_stream(workspace.device).cuda_stream)
+
+
+class _RNNTLossFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, logits, targets, logit_lengths, target_lengths, blank, clamp, reduction, fused_log_softmax):
+        T = _lib.host_i32(logit_lengths)
+        U = _lib.host_i32(target_lengths)
+        loss, loss_red, grad, ws = rnnt_loss_fused(logits, targets, T, U, blank, clamp, reduction, fused_log_softmax,
+                                                   compute_grad=logits.requires_grad)
+        ctx.meta = (T, U, reduction, logits.shape, logits.dtype)
+        ctx.used = False
+        if grad is not None:
+            ctx.save_for_backward(grad, ws)
+        return loss if reduction == "none" else loss_red.reshape(())
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        T, U, reduction, shape, dtype = ctx.meta
+        if not ctx.saved_tensors:
+            return (None,) * 8
+        if ctx.used:
+            raise RuntimeError("rnnt_loss backward was already run for this forward call")
+        ctx.used = True
+        grad, ws = ctx.saved_tensors
+        scale = grad_out.detach().to(device=grad.device, dtype=torch.float32).contiguous().reshape(-1)
+        with torch.cuda.device(grad.device):
+            _lib.grad_scale(grad.data_ptr(), _dtype_code(dtype), shape[0], shape[1], T, U, scale.data_ptr(),
+                            reduction == "none", ws.data_ptr(), ws.numel(),
+                            torch.cuda.current_stream(grad.device).cuda_stream)
+        return grad, None, None, None, None, None, None, None
+
+
+def rnnt_loss(logits: torch.Tensor, targets: torch.Tensor, logit_lengths, target_lengths, blank: int = -1,
+              clamp: float = -1.0, reduction: str = "mean", fused_log_softmax: bool = True) -> torch.Tensor:
+    """RNN-T loss over packed logits; differentiable with respect to ``logits``.
+
+    ``blank`` in [-V, V-1] (negative counts from the end), ``clamp > 0`` clips
+    each gradient element to [-clamp, clamp], ``reduction`` is none (per
+    sample, fp32 (B,)), mean (over the batch) or sum.  With
+    ``fused_log_softmax=False`` the inputs are taken as log-probabilities.
+    """
+    if reduction not in ("none", "mean", "sum"):
+        raise ValueError(f"reduction must be none, mean or sum, got {reduction!r}")
+    return _RNNTLossFunction.apply(logits, targets, logit_lengths, target_lengths, int(blank), float(clamp),
+                                   reduction, bool(fused_log_softmax))
+
+
+class RNNTLoss(torch.nn.Module):
+    """Module form of :func:`rnnt_loss` with the attributes fixed at construction."""
+
+    def __init__(self, blank: int = -1, clamp: float = -1.0, reduction: str = "mean",
+                 fused_log_softmax: bool = True):
+        super().__init__()
+        self.blank, self.clamp, self.reduction, self.fused_log_softmax = blank, clamp, reduction, fused_log_softmax
+
+    def forward(self, logits, targets, logit_lengths, target_lengths):
+        return rnnt_loss(logits, targets, logit_lengths, target_lengths, self.blank, self.clamp, self.reduction,
+                         self.fused_log_softmax)

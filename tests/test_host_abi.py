@@ -1,0 +1,147 @@
+"""CPU-only checks of librnnt's C ABI: symbols, host validation and the schedule.
+
+No compute call is made (there is no GPU here): rnnt_loss_fused_workspace_size
+and rnnt_plan_describe touch no device, and argument errors are rejected by
+rnnt_loss_fused before anything is enqueued.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from rnn_transducer_loss_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"\b(rnnt_\w+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    declared = _declared_functions()
+    assert set(_lib.EXPORTS) <= set(declared)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert _lib.status_string(0) == "success"
+    assert "invalid" in _lib.status_string(1)
+    assert _lib.status_string(99) == "unknown status"
+
+
+def _ws(T, U, V=16, dtype=_lib.RNNT_F32, N=None):
+    T = np.asarray(T, np.int32)
+    U = np.asarray(U, np.int32)
+    if N is None:
+        N = int((T.astype(np.int64) * (U + 1)).sum())
+    return _lib.workspace_size(len(T), V, N, dtype, T, U)
+
+
+def test_workspace_size_grows_with_the_batch():
+    a = _ws([12, 9], [4, 3])
+    b = _ws([12, 9, 30], [4, 3, 7])
+    assert 0 < a < b
+    # per-node aux: 4 B den per row + 24 B per skewed slot, plus tables.
+    T, U = 300, 70
+    rows, slots = T * (U + 1), (T + U) * (U + 1)
+    assert _ws([T], [U], V=1024) >= 4 * rows + 24 * slots
+
+
+@pytest.mark.parametrize("T,U,N", [([0, 3], [1, 1], None), ([3, 3], [-1, 1], None), ([4], [2], 11),
+                                   ([4], [1023], None), ([2], [1024], None)])
+def test_workspace_size_rejects_bad_lengths(T, U, N):
+    if U == [1023]:
+        assert _ws(T, U) > 0      # widest lattice the kernels support
+        return
+    with pytest.raises(ValueError):
+        _ws(T, U, N=N)
+
+
+def test_workspace_size_rejects_bad_dtype_and_sizes():
+    T = np.array([3], np.int32)
+    U = np.array([1], np.int32)
+    with pytest.raises(ValueError):
+        _lib.workspace_size(1, 8, 6, 7, T, U)
+    with pytest.raises(ValueError):
+        _lib.workspace_size(1, 0, 6, 0, T, U)
+    with pytest.raises(ValueError):
+        _lib.workspace_size(0, 8, 0, 0, T[:0], U[:0])
+
+
+def _call_fused(**over):
+    """rnnt_loss_fused with fake (never dereferenced) device pointers; only host checks can run."""
+    T = np.array([4, 6], np.int32)
+    U = np.array([2, 1], np.int32)
+    args = dict(logits_ptr=0x100000, dtype_code=0, N=24, V=8, targets_ptr=0x200000, S=2, logit_lengths=T,
+                target_lengths=U, blank=-1, clamp=-1.0, fused=True, reduction="mean", loss_ptr=0x300000,
+                loss_reduced_ptr=0x400000, grad_ptr=0x500000, ws_ptr=0x600000, ws_bytes=1 << 20, stream=0)
+    args.update(over)
+    _lib.loss_fused(**args)
+
+
+@pytest.mark.parametrize("over", [
+    dict(blank=8), dict(blank=-9), dict(N=25), dict(S=1), dict(targets_ptr=0), dict(loss_ptr=0),
+    dict(ws_ptr=0), dict(logits_ptr=0), dict(dtype_code=3), dict(V=0),
+    dict(grad_ptr=0x100000 + 64),                # partial overlap with logits
+    dict(ws_bytes=64),                           # workspace too small
+    dict(ws_ptr=0x600010),                       # workspace not 256-byte aligned
+    dict(logit_lengths=np.array([4, 0], np.int32)),
+    dict(target_lengths=np.array([2, -1], np.int32)),
+])
+def test_fused_call_rejects_invalid_arguments_before_any_launch(over):
+    with pytest.raises(ValueError):
+        _call_fused(**over)
+
+
+def test_reduction_names_are_checked():
+    with pytest.raises(ValueError):
+        _call_fused(reduction="avg")
+
+
+@pytest.mark.parametrize("V,dtype", [(16, _lib.RNNT_F32), (29, _lib.RNNT_F32), (1024, _lib.RNNT_F32),
+                                     (4096, _lib.RNNT_F16), (2048, _lib.RNNT_F16)])
+def test_schedule_is_longest_first_and_covers_every_row_once(V, dtype):
+    rng = np.random.default_rng(V)
+    B = 37
+    T = rng.integers(1, 200, size=B).astype(np.int32)
+    U = rng.integers(0, 60, size=B).astype(np.int32)
+    T[5], U[5] = T[6], U[6]                       # a tie in area
+    order, chunks = _lib.plan_describe(V, dtype, T, U)
+    area = T.astype(np.int64) * (U + 1)
+    assert sorted(order.tolist()) == list(range(B))
+    for a, b in zip(order[:-1], order[1:]):
+        key_a = (area[a], T[a] + U[a], -a)
+        key_b = (area[b], T[b] + U[b], -b)
+        assert key_a > key_b
+    # chunks: samples appear in schedule order, each row of each sample exactly once
+    seen = {i: np.zeros(area[i], np.int32) for i in range(B)}
+    pos = {int(s): k for k, s in enumerate(order)}
+    last = -1
+    for s, b0, n in chunks:
+        assert pos[int(s)] >= last
+        last = pos[int(s)]
+        assert n > 0 and 0 <= b0 and b0 + n <= area[s]
+        seen[int(s)][b0:b0 + n] += 1
+    for i in range(B):
+        assert (seen[i] == 1).all()
+
+
+def test_schedule_chunk_sizes_follow_row_bytes():
+    T = np.array([400] * 8, np.int32)
+    U = np.array([100] * 8, np.int32)
+    _, c32 = _lib.plan_describe(1024, _lib.RNNT_F32, T, U)
+    _, c16 = _lib.plan_describe(4096, _lib.RNNT_F16, T, U)
+    # about 256 KiB of logits per chunk, in multiples of 64 rows
+    assert c32[0, 2] == 64 and c16[0, 2] == 64
+    assert (c32[:, 2] % 64 == 0).sum() >= len(c32) - 8

@@ -1,0 +1,331 @@
+"""GPU parity of librnnt against the fp64 oracle (run on an MI355X).
+
+Every case draws seeded inputs with ``workloads``, runs the HIP path through
+the C ABI (via the ctypes binding) and compares element by element with the
+oracle on the same inputs:
+
+    fp32 inputs: loss relative error <= 1e-5, gradient absolute error <= 1e-5
+    fp16 inputs: loss relative error <= 2e-3, gradient absolute error <= 3e-3
+                 (the oracle reads the fp16-rounded inputs exactly)
+
+The per-sample gradient (the library's output divided by the reduction scale)
+is held to the gate, which is stricter than comparing the scaled output.
+At the full workload sizes the oracle computes every sample's loss and the
+gradient of selected rows (the first and last rows of every sample, and
+random rows); properties that hold at any size are checked on the whole
+output.
+"""
+import concurrent.futures as cf
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: (1e-5, 1e-5), torch.float16: (2e-3, 3e-3)}
+
+
+@pytest.fixture(scope="module")
+def rl():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rnn_transducer_loss_amd as rl
+    rl._lib.load()
+    return rl
+
+
+def _threads():
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:  # pragma: no cover
+        return 4
+
+
+def _blank(w):
+    return w.blank + w.V if w.blank < 0 else w.blank
+
+
+def _np_rows(t: torch.Tensor) -> np.ndarray:
+    a = t.detach().cpu()
+    if a.dtype == torch.float16:
+        return a.numpy()
+    return a.numpy()
+
+
+def run(rl, w, reduction=None, inplace=False, compute_grad=True, clamp=None):
+    reduction = w.reduction if reduction is None else reduction
+    clamp = w.clamp if clamp is None else clamp
+    logits = w.logits.clone() if inplace else w.logits
+    tg = torch.from_numpy(w.targets).to("cuda")
+    loss, red, grad, ws = rl.rnnt_loss_fused(logits, tg, w.logit_lengths, w.target_lengths, blank=w.blank,
+                                             clamp=clamp, reduction=reduction, fused_log_softmax=w.fused,
+                                             compute_grad=compute_grad, inplace=inplace)
+    flags = rl.device_flags(ws)
+    torch.cuda.synchronize()
+    return loss, red, grad, flags
+
+
+def check_against_oracle(w, loss, grad, reduction, clamp=None, grad_rows="all", samples=None, seed=0):
+    """Compare per-sample loss (all samples) and gradients of selected rows with the oracle."""
+    clamp = w.clamp if clamp is None else clamp
+    ltol, gtol = TOL[w.dtype]
+    B = w.B
+    b = _blank(w)
+    scale = 1.0 / B if reduction == "mean" else 1.0
+    loss_h = loss.detach().cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(seed)
+    samples = range(B) if samples is None else samples
+    want_grad = set(samples) if grad is not None else set()
+
+    def one(i):
+        sl = w.rows(i)
+        x = _np_rows(w.logits[sl])
+        T, U = int(w.logit_lengths[i]), int(w.target_lengths[i])
+        n = T * (U + 1)
+        rows = None
+        if i in want_grad and grad_rows != "all":
+            pick = set([0, 1, U, n - 1, n - 2, max(0, n - U - 1)])
+            pick |= set(rng.integers(0, n, size=min(n, grad_rows)).tolist())
+            rows = np.array(sorted(r for r in pick if 0 <= r < n), np.int64)
+        r = oracle.sample(x, T, U, w.targets[i], b, w.fused, clamp, want_grad=(i in want_grad), rows=rows)
+        return i, r, rows
+
+    errs_loss, errs_grad = [], []
+    with cf.ThreadPoolExecutor(_threads()) as ex:
+        for i, r, rows in ex.map(one, range(B)):
+            ref = r.loss
+            rel = abs(loss_h[i] - ref) / max(1.0, abs(ref))
+            errs_loss.append(rel)
+            assert rel <= ltol, f"sample {i}: loss {loss_h[i]} vs oracle {ref} (rel {rel:.3g})"
+            assert abs(r.loss_alpha - r.loss) <= 1e-9 * max(1.0, abs(r.loss))
+            if r.grad is not None:
+                sl = w.rows(i)
+                g = grad[sl] if rows is None else grad[sl][torch.from_numpy(rows).to(grad.device)]
+                g = g.detach().double().cpu().numpy() / scale
+                err = np.abs(g - r.grad).max()
+                errs_grad.append(err)
+                assert err <= gtol, f"sample {i}: grad max abs err {err:.3g}"
+    return max(errs_loss), (max(errs_grad) if errs_grad else 0.0)
+
+
+def _reduced_ok(w, loss, red, reduction):
+    if reduction == "none":
+        assert red is None
+        return
+    s = loss.double().sum().item()
+    expect = s / w.B if reduction == "mean" else s
+    assert abs(red.item() - expect) <= 1e-6 * max(1.0, abs(expect))
+
+
+# ------------------------------------------------------------- named workloads
+@pytest.mark.parametrize("reduction", ["none", "mean", "sum"])
+def test_tiny_workload(rl, reduction):
+    w = workloads.make("tiny", device="cuda")
+    assert w.N == 96 and w.logits.shape == (96, 16)
+    loss, red, grad, flags = run(rl, w, reduction=reduction)
+    assert flags == 0
+    check_against_oracle(w, loss, grad, reduction)
+    _reduced_ok(w, loss, red, reduction)
+
+
+@pytest.mark.parametrize("seed", [2, 101, 102, 103])
+def test_char_workload(rl, seed):
+    w = workloads.make("char", seed=seed, device="cuda")
+    loss, red, grad, flags = run(rl, w)
+    assert flags == 0
+    check_against_oracle(w, loss, grad, w.reduction)
+    _reduced_ok(w, loss, red, w.reduction)
+
+
+def test_bpe_workload_full_size(rl):
+    w = workloads.make("bpe", device="cuda")
+    loss, red, grad, flags = run(rl, w)
+    assert flags == 0
+    order = np.argsort(w.logit_lengths.astype(np.int64) * (w.target_lengths + 1))
+    picks = [int(order[0]), int(order[-1]), int(order[len(order) // 2])]
+    check_against_oracle(w, loss, grad, w.reduction, grad_rows="all", samples=picks)
+    _reduced_ok(w, loss, red, w.reduction)
+    # any-size property: each fused gradient row sums to zero (fp32 rounding only)
+    rs = grad.double().sum(dim=1).abs().max().item()
+    assert rs < 1e-6
+
+
+def test_half_workload_full_size(rl):
+    w = workloads.make("half", device="cuda")
+    loss, red, grad, flags = run(rl, w)
+    assert flags == 0
+    order = np.argsort(w.logit_lengths.astype(np.int64) * (w.target_lengths + 1))
+    picks = [int(order[0]), int(order[-1])]
+    check_against_oracle(w, loss, grad, w.reduction, grad_rows=3000, samples=picks)
+    _reduced_ok(w, loss, red, w.reduction)
+    assert torch.isfinite(grad).all()
+
+
+def test_skewed_workload_full_size(rl):
+    w = workloads.make("skewed", device="cuda")
+    loss, red, grad, flags = run(rl, w)
+    assert flags == 0
+    order = np.argsort(w.logit_lengths.astype(np.int64) * (w.target_lengths + 1))
+    picks = [int(order[0]), int(order[-1]), int(order[len(order) // 2])]
+    check_against_oracle(w, loss, grad, w.reduction, grad_rows=4000, samples=picks)
+    _reduced_ok(w, loss, red, w.reduction)
+    # non-fused: at most two non-zeros per row; per sample the entries sum to -(T+U)
+    nnz = (grad != 0).sum(dim=1)
+    assert int(nnz.max().item()) <= 2
+    big = int(order[-1])
+    s = grad[w.rows(big)].double().sum().item()
+    T, U = int(w.logit_lengths[big]), int(w.target_lengths[big])
+    assert abs(s + (T + U)) <= 3e-3 * (T + U)
+
+
+# ------------------------------------------------------------------ edge cases
+def _custom(Ts, Us, V, **kw):
+    return workloads.make_custom(Ts, Us, V, device="cuda", **kw)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16])
+def test_single_path_and_degenerate_lattices(rl, dtype):
+    # U = 0 (all-blank lattice), T = 1 (single path), 1x1, and ordinary samples mixed
+    w = _custom([7, 1, 1, 5, 33], [0, 6, 0, 3, 0], 19, dtype=dtype, std=2.0, blank=4, reduction="sum", seed=11)
+    loss, red, grad, flags = run(rl, w)
+    assert flags == 0
+    check_against_oracle(w, loss, grad, "sum")
+
+
+@pytest.mark.parametrize("V", [1, 2, 3, 5, 31, 64, 65, 100, 257, 1000, 1023, 2049])
+def test_vocab_sizes(rl, V):
+    # V = 1 only admits U = 0; odd V exercises the scalar (unvectorised) row path
+    Us = [0, 0] if V == 1 else [3, min(9, 5)]
+    w = _custom([6, 11], Us, V, std=1.5, blank=-1, reduction="mean", seed=V)
+    loss, red, grad, flags = run(rl, w)
+    assert flags == 0
+    check_against_oracle(w, loss, grad, "mean")
+
+
+@pytest.mark.parametrize("U", [63, 64, 127, 128, 255, 256, 511, 512, 700, 1023])
+def test_lattice_widths_across_register_tiles(rl, U):
+    # U+1 crosses each multiple of 64 nodes the alpha/beta wavefront holds per lane
+    w = _custom([3, 40], [U, min(U, 20)], 8, std=1.0, blank=0, reduction="none", seed=U)
+    loss, red, grad, flags = run(rl, w)
+    assert flags == 0
+    check_against_oracle(w, loss, grad, "none")
+
+
+def test_ragged_batch_many_samples(rl):
+    rng = np.random.default_rng(77)
+    B = 150
+    Ts = rng.integers(1, 90, size=B).tolist()
+    Us = rng.integers(0, 40, size=B).tolist()
+    w = _custom(Ts, Us, 40, std=2.0, blank=-40, reduction="mean", seed=77)
+    loss, red, grad, flags = run(rl, w)
+    assert flags == 0
+    check_against_oracle(w, loss, grad, "mean")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16])
+@pytest.mark.parametrize("clamp", [0.02, 0.1, 0.3])
+def test_clamp(rl, dtype, clamp):
+    w = _custom([30, 17], [8, 5], 12, dtype=dtype, std=3.0, blank=-1, reduction="mean", seed=5)
+    loss, red, grad, flags = run(rl, w, clamp=clamp)
+    check_against_oracle(w, loss, grad, "mean", clamp=clamp)
+    assert grad.abs().max().item() <= clamp / w.B * (1 + 1e-3)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16])
+def test_nonfused_inputs(rl, dtype):
+    w = _custom([25, 40, 9], [6, 12, 0], 50, dtype=dtype, std=1.5, blank=0, fused=False, prenormalise=True,
+                reduction="sum", seed=9)
+    loss, red, grad, flags = run(rl, w)
+    check_against_oracle(w, loss, grad, "sum")
+
+
+def test_inplace_gradient_over_logits(rl):
+    w = _custom([40, 20], [10, 7], 256, std=2.0, blank=-1, reduction="none", seed=3)
+    ref_loss, _, ref_grad, _ = run(rl, w)
+    loss, _, grad, _ = run(rl, w, inplace=True)
+    assert torch.equal(loss, ref_loss)
+    assert torch.equal(grad, ref_grad)
+
+
+def test_score_only(rl):
+    w = _custom([40, 20], [10, 7], 64, std=2.0, blank=-1, reduction="sum", seed=4)
+    loss, red, grad, flags = run(rl, w, compute_grad=False)
+    assert grad is None
+    ref, _, _, _ = run(rl, w)
+    assert torch.equal(loss, ref)
+
+
+def test_unaligned_logits_pointer(rl):
+    # logits starting 4 bytes past a 16-byte boundary force the scalar access path
+    w = _custom([20, 13], [5, 9], 32, std=2.0, blank=3, reduction="mean", seed=6)
+    buf = torch.empty(w.logits.numel() + 1, dtype=w.logits.dtype, device="cuda")
+    buf[1:].copy_(w.logits.reshape(-1))
+    w.logits = buf[1:].view(w.N, w.V)
+    assert w.logits.data_ptr() % 16 != 0
+    loss, red, grad, flags = run(rl, w)
+    check_against_oracle(w, loss, grad, "mean")
+
+
+def test_deterministic_bitwise(rl):
+    w = workloads.make("char", seed=7, device="cuda")
+    a = run(rl, w)
+    b = run(rl, w)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+
+
+def test_bad_targets_are_flagged(rl):
+    w = _custom([6, 5], [3, 2], 10, std=1.0, blank=-1, reduction="none", seed=8)
+    tg = w.targets.copy()
+    tg[0, 1] = 9          # equals blank (V-1)
+    tg[1, 0] = 12         # outside [0, V)
+    w.targets = tg
+    loss, red, grad, flags = run(rl, w)
+    assert flags & 2
+    assert math.isinf(loss[1].item()) and loss[1].item() > 0
+    assert grad[w.rows(1)].abs().max().item() == 0.0
+    assert math.isfinite(loss[0].item())
+
+
+# ------------------------------------------------------------------- autograd
+@pytest.mark.parametrize("reduction", ["none", "mean", "sum"])
+def test_autograd_backward(rl, reduction):
+    w = _custom([30, 22, 15], [7, 4, 9], 48, std=2.0, blank=-1, reduction=reduction, seed=21)
+    x = w.logits.clone().requires_grad_(True)
+    tg = torch.from_numpy(w.targets).cuda()
+    Tl = torch.from_numpy(w.logit_lengths).cuda()
+    Ul = torch.from_numpy(w.target_lengths).cuda()
+    out = rl.rnnt_loss(x, tg, Tl, Ul, blank=-1, reduction=reduction)
+    if reduction == "none":
+        weights = torch.tensor([0.5, 2.0, -1.0], device="cuda")
+        (out * weights).sum().backward()
+    else:
+        (out * 3.5).backward()
+    # oracle: per-sample gradient times the upstream factor of each sample
+    _, _, gref, _ = oracle.batch(x.detach().cpu().numpy(), w.targets, w.logit_lengths, w.target_lengths,
+                                 blank=-1, reduction="none")
+    if reduction == "none":
+        fac = np.repeat([0.5, 2.0, -1.0], [w.rows(i).stop - w.rows(i).start for i in range(3)])[:, None]
+    else:
+        fac = 3.5 / w.B if reduction == "mean" else 3.5
+    err = np.abs(x.grad.double().cpu().numpy() - gref * fac).max()
+    assert err <= 1e-5 * (3.5 if reduction != "none" else 2.0)
+
+
+def test_readme_example_golden(rl):
+    """The README usage layout (24 rows, V=8) against the stored oracle values."""
+    import json
+    gd = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "readme_example.json")))
+    logits = torch.tensor(gd["logits"], dtype=torch.float32, device="cuda")
+    tg = torch.tensor(gd["targets"], dtype=torch.int32, device="cuda")
+    for case in gd["cases"]:
+        loss, red, grad, _ = rl.rnnt_loss_fused(logits, tg, gd["logit_lengths"], gd["target_lengths"], blank=-1,
+                                                reduction=case["reduction"])
+        out = (loss if case["reduction"] == "none" else red).double().cpu().numpy()
+        np.testing.assert_allclose(out, case["loss"], rtol=1e-5, atol=0)
+        np.testing.assert_allclose(grad.double().cpu().numpy(), np.array(case["grad"]), rtol=0, atol=1e-5)
