@@ -75,18 +75,20 @@ rnnt_status build_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t
     rnnt_status st = check_lengths(B, V, T, U);
     if (st != RNNT_SUCCESS) return st;
     p.desc.resize(B);
-    int64_t row = 0, slot = 0;
+    int64_t row = 0, slot = 0, diag = 0;
     p.max_U1 = 1;
     for (int32_t i = 0; i < B; ++i) {
         SampleDesc &d = p.desc[i];
         d.row_off = row;
         d.slot_off = slot;
+        d.diag_off = diag;
         d.T = T[i];
         d.U = U[i];
         d.index = i;
         d.pad = 0;
         row += (int64_t)T[i] * (U[i] + 1);
         slot += ((int64_t)T[i] + U[i]) * (U[i] + 1);
+        diag += (int64_t)T[i] + U[i];
         p.max_U1 = std::max(p.max_U1, U[i] + 1);
     }
     if (N >= 0 && row != N) return RNNT_INVALID_VALUE;
@@ -110,17 +112,23 @@ rnnt_status build_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t
     if (p.chunks.size() > (size_t)INT32_MAX) return RNNT_INVALID_VALUE;
     WorkspaceLayout &L = p.lay;
     size_t off = 0;
-    L.status = off; off = align_up(off + 64);
+    L.status = 0;
+    off = 256;
+    L.mode = off;   off = align_up(off + sizeof(int32_t) * B);
     L.desc = off;   off = align_up(off + sizeof(SampleDesc) * B);
     L.order = off;  off = align_up(off + sizeof(int32_t) * B);
     L.chunks = off; off = align_up(off + sizeof(ChunkDesc) * p.chunks.size());
-    L.den = off;    off = align_up(off + sizeof(float) * (size_t)row);
-    L.lpb = off;    off = align_up(off + sizeof(float) * (size_t)slot);
-    L.lpy = off;    off = align_up(off + sizeof(float) * (size_t)slot);
+    L.rec = off;    off = align_up(off + sizeof(RowRec) * (size_t)row);
+    L.lp = off;     off = align_up(off + 2 * sizeof(float) * (size_t)slot);
+    L.prob = off;   off = align_up(off + 2 * sizeof(float) * (size_t)slot);
     L.alpha = off;  off = align_up(off + sizeof(double) * (size_t)slot);
     L.beta = off;   off = align_up(off + sizeof(double) * (size_t)slot);
+    L.ealpha = off; off = align_up(off + sizeof(int32_t) * (size_t)diag);
+    L.ebeta = off;  off = align_up(off + sizeof(int32_t) * (size_t)diag);
+    L.log2z = off;  off = align_up(off + sizeof(double) * (size_t)B);
     L.total = off;
     L.n_slots = slot;
+    L.n_diags = diag;
     L.n_chunks = (int32_t)p.chunks.size();
     L.rows_per_chunk = rpc;
     return RNNT_SUCCESS;
@@ -177,7 +185,7 @@ rnnt_status upload(void *dst, const std::vector<uint8_t> &src, hipStream_t strea
 // The header, descriptors, order and chunks are contiguous at the start of
 // the workspace and go up in one copy (the status word is cleared with it).
 std::vector<uint8_t> pack_plan(const Plan &p) {
-    std::vector<uint8_t> buf(p.lay.den, 0);
+    std::vector<uint8_t> buf(p.lay.rec, 0);
     std::memcpy(buf.data() + p.lay.desc, p.desc.data(), sizeof(SampleDesc) * p.desc.size());
     std::memcpy(buf.data() + p.lay.order, p.order.data(), sizeof(int32_t) * p.order.size());
     std::memcpy(buf.data() + p.lay.chunks, p.chunks.data(), sizeof(ChunkDesc) * p.chunks.size());

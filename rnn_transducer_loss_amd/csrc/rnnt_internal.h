@@ -14,9 +14,12 @@ namespace rnnt {
 // row_off + t*(U+1) + u is lattice node (t,u).  The per-node scalars of the
 // recursions live in a skewed layout, one slot per (anti-diagonal n = t+u, u):
 // slot_off + n*(U+1) + u, n in [0, T+U), so every anti-diagonal is contiguous.
+// Per-diagonal values (the recursions' power-of-two exponents) are at
+// diag_off + n.
 struct SampleDesc {
     int64_t row_off;
     int64_t slot_off;
+    int64_t diag_off;
     int32_t T;
     int32_t U;
     int32_t index;  // position of the sample in the batch (targets row)
@@ -31,19 +34,35 @@ struct ChunkDesc {
     int32_t pad;
 };
 
-// Byte offsets of the workspace regions (each 256-byte aligned).
+// Per packed row, written by the row-statistics pass for the gradient pass:
+// the row's log-sum-exp (0 for log-prob inputs), its blank and label input
+// values, and its label (-1 at u = U or when out of range).
+struct RowRec {
+    float den;
+    float xb;
+    float xy;
+    int32_t y;
+};
+
+// Byte offsets of the workspace regions (each 256-byte aligned).  Everything
+// before `rec` is written by the per-call upload.
 struct WorkspaceLayout {
-    size_t status;   // uint32 status word + reserved header
-    size_t desc;     // SampleDesc[B]
-    size_t order;    // int32[B], samples by decreasing cost
-    size_t chunks;   // ChunkDesc[n_chunks]
-    size_t den;      // float[N], per-row log-sum-exp (fused only)
-    size_t lpb;      // float[S], log P(blank) per slot
-    size_t lpy;      // float[S], log P(next label) per slot
-    size_t alpha;    // double[S]
-    size_t beta;     // double[S]
+    size_t status;      // uint32 status word
+    size_t mode;        // int32[B]: 1 = log-domain recursion (set by rowstats)
+    size_t desc;        // SampleDesc[B]
+    size_t order;       // int32[B], samples by decreasing cost
+    size_t chunks;      // ChunkDesc[n_chunks]
+    size_t rec;         // RowRec[N]
+    size_t lp;          // float2[S]: {log P(blank), log P(next label)} per slot
+    size_t prob;        // float2[S]: the same as probabilities
+    size_t alpha;       // double[S]
+    size_t beta;        // double[S]
+    size_t ealpha;      // int32[D]: per-diagonal exponent of alpha
+    size_t ebeta;       // int32[D]
+    size_t log2z;       // double[B]: log2 P(y|x) (beta path)
     size_t total;
     int64_t n_slots;
+    int64_t n_diags;
     int32_t n_chunks;
     int32_t rows_per_chunk;
 };
@@ -53,6 +72,8 @@ struct RowGeom {
     int lanes_per_row;  // G: 1..64 lanes cooperate on one row (power of two)
     int vec;            // elements per vector access (1 when rows are not 16-byte aligned)
     int rows_per_block_iter;
+    int wide_nv;        // > 0: one row per wave, wide_nv vectors per lane
+    bool wide_full;     // V is exactly 64 * wide_nv vectors (no tail lanes)
 };
 
 RowGeom row_geometry(int V, int esize, bool aligned16);

@@ -1,22 +1,32 @@
 // gfx950 kernels of librnnt: the fused RNN-T loss, forward and backward.
 //
 // Pass structure (rnnt-loss-ascend README, "Architecture", kernel steps 1-5):
-//   rowstats   step 1   per packed row: log-sum-exp over V (fused) and the two
-//                       log-probs the lattice uses, log P(blank) and
-//                       log P(y_{u+1}), written into the skewed per-node arrays.
-//   alpha_beta steps 2-4 one workgroup per sample; wave 0 runs the forward
-//                       (alpha) recursion and wave 1 the backward (beta)
-//                       recursion, each one anti-diagonal per step (README
-//                       "Operator features": every node of an anti-diagonal
-//                       has its inputs ready), fp64 log-space accumulators;
-//                       the two losses are cross-checked.
-//   grad       step 5   per packed row: the fused gradient (README "Value"
-//                       section 2), clamp, reduction scale, one write of grad.
-//   reduce              none / mean / sum of the per-sample losses.
+//   rowstats    step 1    per packed row: log-sum-exp over V (fused) and the
+//                         two log-probs the lattice uses, log P(blank) and
+//                         log P(y_{u+1}), stored per node in a skewed layout
+//                         (one contiguous run per anti-diagonal) both as fp32
+//                         log-probs and as fp32 probabilities.
+//   alpha_beta  steps 2-4 one workgroup per sample; wave 0 runs the forward
+//                         (alpha) recursion and wave 1 the backward (beta)
+//                         recursion, one anti-diagonal per step (README
+//                         "Operator features": every node of an anti-diagonal
+//                         has its inputs ready); the two losses are
+//                         cross-checked.
+//   grad        step 5    per packed row: the fused gradient (README "Value"
+//                         section 2), clamp, reduction scale, one write.
+//   reduce                none / mean / sum of the per-sample losses.
 //
-// Nothing here is a dense contraction, so no MFMA: the row passes are bound by
-// HBM bandwidth (coalesced 16-byte accesses, wave-shuffle reductions) and the
-// recursion by the latency of its T+U dependent steps.
+// The recursions run in a scaled probability domain: node values are fp64
+// mantissas with one power-of-two exponent per anti-diagonal, renormalised
+// exactly (by a power of two) every four diagonals.  A step is then one add
+// and two multiplies per node instead of a log-sum-exp.  A sample whose
+// log-probs leave [-80, 80] (so that an fp32 probability could underflow)
+// is flagged by rowstats and takes a log-domain variant of the same sweep.
+//
+// Nothing here is a dense contraction, so no MFMA: the row passes are bound
+// by HBM bandwidth (coalesced 16-byte accesses, one row per wave with the next
+// row's loads in flight, DPP wave reductions) and the recursion by the latency
+// of its T+U dependent steps.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -30,129 +40,324 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr double kLog2eD = 1.4426950408889634074;
+constexpr double kLn2D = 0.69314718055994530942;
 constexpr double kNegInfD = -__builtin_inf();
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kProbRange = 80.f;  // |log-prob| bound of the probability-domain sweep
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
-// ---------------------------------------------------------------- element I/O
+// log2 of a non-negative fp64 value: exponent exactly, mantissa in fp32.
+__device__ __forceinline__ double log2_d(double x) {
+    const int e = __builtin_amdgcn_frexp_exp(x);
+    const float m = (float)__builtin_amdgcn_frexp_mant(x);
+    return (double)e + (double)log2_fast(m);
+}
+
+// exp(lp) in fp32 for |lp| <= kProbRange, with the exponent split off
+// (Cody-Waite) so the rounding of lp * log2(e) does not enter the result.
+__device__ __forceinline__ float prob_of(float lp) {
+    constexpr float kHi = 1.44269502162933349609375f;  // fp32 nearest to log2(e)
+    constexpr float kLo = 1.925963033500011079e-8f;     // log2(e) - kHi
+    const float k = rintf(lp * kLog2e);
+    const float f = fmaf(lp, kHi, -k) + lp * kLo;
+    const float p = __builtin_amdgcn_ldexpf(exp2_fast(f), (int)k);
+    return (lp == kNegInf) ? 0.f : p;
+}
+
+// ------------------------------------------------------------ element I/O
 template <typename T> struct Elem;
 template <> struct Elem<float> {
-    static constexpr int kVec = 4;  // 16 bytes
     __device__ static float load1(const float *p) { return *p; }
     __device__ static void store1(float *p, float v) { *p = v; }
-    __device__ static void loadv(const float *p, float *out) {
-        const float4 v = *reinterpret_cast<const float4 *>(p);
-        out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+    template <bool NT> __device__ static void loadv(const float *p, float *out) {
+        typedef float f4 __attribute__((ext_vector_type(4)));
+        f4 v;
+        if constexpr (NT) v = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(p));
+        else v = *reinterpret_cast<const f4 *>(p);
+        out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
     }
-    __device__ static void storev(float *p, const float *in) {
-        *reinterpret_cast<float4 *>(p) = make_float4(in[0], in[1], in[2], in[3]);
+    template <bool NT> __device__ static void storev(float *p, const float *in) {
+        typedef float f4 __attribute__((ext_vector_type(4)));
+        f4 v = {in[0], in[1], in[2], in[3]};
+        if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<f4 *>(p));
+        else *reinterpret_cast<f4 *>(p) = v;
     }
 };
 template <> struct Elem<_Float16> {
-    static constexpr int kVec = 8;  // 16 bytes
     __device__ static float load1(const _Float16 *p) { return (float)*p; }
     __device__ static void store1(_Float16 *p, float v) { *p = (_Float16)v; }
-    __device__ static void loadv(const _Float16 *p, float *out) {
+    template <bool NT> __device__ static void loadv(const _Float16 *p, float *out) {
         typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-        const h8 v = *reinterpret_cast<const h8 *>(p);
+        h8 v;
+        if constexpr (NT) v = __builtin_nontemporal_load(reinterpret_cast<const h8 *>(p));
+        else v = *reinterpret_cast<const h8 *>(p);
 #pragma unroll
         for (int i = 0; i < 8; ++i) out[i] = (float)v[i];
     }
-    __device__ static void storev(_Float16 *p, const float *in) {
+    template <bool NT> __device__ static void storev(_Float16 *p, const float *in) {
         typedef _Float16 h8 __attribute__((ext_vector_type(8)));
         h8 v;
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = (_Float16)in[i];
-        *reinterpret_cast<h8 *>(p) = v;
+        if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<h8 *>(p));
+        else *reinterpret_cast<h8 *>(p) = v;
     }
 };
 
-template <typename T, int VEC> __device__ __forceinline__ void load_n(const T *p, float *out) {
+template <typename T, int VEC, bool NT = false> __device__ __forceinline__ void load_n(const T *p, float *out) {
     if constexpr (VEC == 1) out[0] = Elem<T>::load1(p);
-    else Elem<T>::loadv(p, out);
+    else Elem<T>::template loadv<NT>(p, out);
 }
-template <typename T, int VEC> __device__ __forceinline__ void store_n(T *p, const float *in) {
+template <typename T, int VEC, bool NT = false> __device__ __forceinline__ void store_n(T *p, const float *in) {
     if constexpr (VEC == 1) Elem<T>::store1(p, in[0]);
-    else Elem<T>::storev(p, in);
+    else Elem<T>::template storev<NT>(p, in);
 }
 
-// Combine two (max, sum of exp(x - max)) partial states.
-__device__ __forceinline__ void lse_merge(float &m, float &s, float mo, float so) {
-    const float mn = fmaxf(m, mo);
-    const float mr = (mn == kNegInf) ? 0.f : mn;
-    s = s * exp2_fast((m - mr) * kLog2e) + so * exp2_fast((mo - mr) * kLog2e);
-    m = mn;
+// A 16-byte vector kept as loaded (4 fp32 or 8 fp16, in the element type's
+// own vector type), converted to fp32 element by element on use.
+template <typename T> struct Raw;
+template <> struct Raw<float> {
+    static constexpr int kVec = 4;
+    typedef float vec __attribute__((ext_vector_type(4)));
+    __device__ static float get(const vec &r, int e) { return r[e]; }
+    __device__ static vec put(const float *v) {
+        vec r = {v[0], v[1], v[2], v[3]};
+        return r;
+    }
+};
+template <> struct Raw<_Float16> {
+    static constexpr int kVec = 8;
+    typedef _Float16 vec __attribute__((ext_vector_type(8)));
+    __device__ static float get(const vec &r, int e) { return (float)r[e]; }
+    __device__ static vec put(const float *v) {
+        vec r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = (_Float16)v[e];
+        return r;
+    }
+};
+template <typename T, bool NT> __device__ __forceinline__ typename Raw<T>::vec load_raw(const T *p) {
+    using V = typename Raw<T>::vec;
+    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const V *>(p));
+    else return *reinterpret_cast<const V *>(p);
+}
+template <typename T, bool NT> __device__ __forceinline__ void store_raw(T *p, typename Raw<T>::vec v) {
+    using V = typename Raw<T>::vec;
+    if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<V *>(p));
+    else *reinterpret_cast<V *>(p) = v;
 }
 
-// log(exp(a) + exp(b)) in fp64 with the correction term in fp32: the argument
-// of exp is <= 0 and log1p's argument is in [0, 1], so fp32 costs at most a
-// few 1e-8 absolute per step while the fp64 accumulator keeps the large part.
-__device__ __forceinline__ double log_add(double a, double b) {
-    const double mx = fmax(a, b);
-    const double mn = fmin(a, b);
-    const float e = exp2_fast((float)(mn - mx) * kLog2e);
-    const float l = log2_fast(1.0f + e) * kLn2;
-    return (mn == kNegInfD) ? mx : mx + (double)l;
+// ------------------------------------------------------- wave reductions
+// DPP within rows of 16 lanes (quad permutes, row rotates), then row
+// broadcasts 15 and 31; the wave result lands in lane 63.
+template <int CTRL, int ROWMASK> __device__ __forceinline__ int dpp_i(int old, int v) {
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWMASK, 0xf, false);
+}
+template <int CTRL, int ROWMASK> __device__ __forceinline__ float dpp_f(float old, float v) {
+    return __int_as_float(dpp_i<CTRL, ROWMASK>(__float_as_int(old), __float_as_int(v)));
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+    v = fmaxf(v, dpp_f<0xb1, 0xf>(v, v));
+    v = fmaxf(v, dpp_f<0x4e, 0xf>(v, v));
+    v = fmaxf(v, dpp_f<0x124, 0xf>(v, v));
+    v = fmaxf(v, dpp_f<0x128, 0xf>(v, v));
+    v = fmaxf(v, dpp_f<0x142, 0xa>(v, v));
+    v = fmaxf(v, dpp_f<0x143, 0xc>(v, v));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+    v += dpp_f<0xb1, 0xf>(0.f, v);
+    v += dpp_f<0x4e, 0xf>(0.f, v);
+    v += dpp_f<0x124, 0xf>(0.f, v);
+    v += dpp_f<0x128, 0xf>(0.f, v);
+    v += dpp_f<0x142, 0xa>(0.f, v);
+    v += dpp_f<0x143, 0xc>(0.f, v);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+    v = max(v, dpp_i<0xb1, 0xf>(v, v));
+    v = max(v, dpp_i<0x4e, 0xf>(v, v));
+    v = max(v, dpp_i<0x124, 0xf>(v, v));
+    v = max(v, dpp_i<0x128, 0xf>(v, v));
+    v = max(v, dpp_i<0x142, 0xa>(v, v));
+    v = max(v, dpp_i<0x143, 0xc>(v, v));
+    return __builtin_amdgcn_readlane(v, 63);
 }
 
-// -------------------------------------------------------------- row geometry
-// Each row is handled by G consecutive lanes; a wave handles 64/G rows at a
-// time and a 256-thread workgroup 4*64/G rows.  Element k of a row goes to
-// lane (k / VEC) % G, so every access instruction of a group is contiguous.
-template <typename T, int VEC, int G, typename F>
-__device__ __forceinline__ void for_rows(const ChunkDesc &c, F &&body) {
-    constexpr int RPW = 64 / G;
+// fp64 lane shifts across the wave: lane l receives lane l-1 (up) or l+1
+// (down); the lane at the wave edge receives `edge`.
+__device__ __forceinline__ double shift_up(double x, double edge) {
+    const int lo = __builtin_amdgcn_update_dpp(__double2loint(edge), __double2loint(x), 0x138, 0xf, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(__double2hiint(edge), __double2hiint(x), 0x138, 0xf, 0xf, false);
+    return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double shift_down(double x, double edge) {
+    const int lo = __builtin_amdgcn_update_dpp(__double2loint(edge), __double2loint(x), 0x130, 0xf, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(__double2hiint(edge), __double2hiint(x), 0x130, 0xf, 0xf, false);
+    return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double read_lane_d(double x, int lane) {
+    const int lo = __builtin_amdgcn_readlane(__double2loint(x), lane);
+    const int hi = __builtin_amdgcn_readlane(__double2hiint(x), lane);
+    return __hiloint2double(hi, lo);
+}
+
+// ---------------------------------------------------- row statistics output
+// Writes what the recursions and the gradient need about node (t,u):
+//   rec  (row order)  {log-sum-exp of the row (fused) or 0, the blank input
+//                      value, the label input value, the label (-1 if none)},
+//   lp   (skewed)     {log P(blank), log P(y_{u+1})},
+//   prob (skewed)     the same as fp32 probabilities.
+// The blank edge leaving t = T-1 below u = U leaves the lattice and the label
+// edge at u = U does not exist, so both are stored as impossible.
+__device__ __forceinline__ void emit_node(const SampleDesc &d, int t, int u, int64_t row, float dn, float xb,
+                                          float xy, int y, float lpb, float lpy, RowRec *__restrict__ rec,
+                                          float2 *__restrict__ lp, float2 *__restrict__ prob,
+                                          int *__restrict__ mode) {
+    if (t == d.T - 1 && u < d.U) lpb = kNegInf;
+    if (u == d.U) lpy = kNegInf;
+    rec[row] = RowRec{dn, xb, xy, y};
+    const int U1 = d.U + 1;
+    const int64_t slot = d.slot_off + (int64_t)(t + u) * U1 + u;
+    lp[slot] = make_float2(lpb, lpy);
+    prob[slot] = make_float2(prob_of(lpb), prob_of(lpy));
+    const bool wide = (lpb != kNegInf && fabsf(lpb) > kProbRange) || (lpy != kNegInf && fabsf(lpy) > kProbRange);
+    if (wide) atomicOr(&mode[d.index], 1);
+}
+
+// The skewed layout has slots (n,u) with t = n-u outside [0, T): the upper
+// triangle n < u and the lower triangle n >= T + u.  The row (0,u) clears
+// column u of the first and the row (T-1,u) column u of the second, so the
+// recursions can read every slot of a diagonal without masks.
+__device__ __forceinline__ void fill_outside(const SampleDesc &d, int t, int u, int lane, int nl,
+                                             float2 *__restrict__ lp, float2 *__restrict__ prob) {
+    const int U1 = d.U + 1;
+    const float2 nlp = make_float2(kNegInf, kNegInf);
+    const float2 np = make_float2(0.f, 0.f);
+    if (t == 0)
+        for (int n = lane; n < u; n += nl) {
+            const int64_t s = d.slot_off + (int64_t)n * U1 + u;
+            lp[s] = nlp;
+            prob[s] = np;
+        }
+    if (t == d.T - 1)
+        for (int n = d.T + u + lane; n < d.T + d.U; n += nl) {
+            const int64_t s = d.slot_off + (int64_t)n * U1 + u;
+            lp[s] = nlp;
+            prob[s] = np;
+        }
+}
+
+__device__ __forceinline__ int read_label(const SampleDesc &d, int u, int V, int blank,
+                                          const int32_t *__restrict__ targets, int S, uint32_t *status) {
+    if (u >= d.U) return -1;
+    const int y = targets[(int64_t)d.index * S + u];
+    const bool in_range = (y >= 0) && (y < V);
+    if (!in_range || y == blank) atomicOr(status, (uint32_t)RNNT_DEV_BAD_TARGET);
+    return in_range ? y : -1;
+}
+
+// --------------------------------------------- K1 rowstats, one row per wave
+// Lane l holds elements (i*64 + l)*VEC .. +VEC-1 of a row, i < NV; the loads
+// of the wave's next row are issued before the current row is reduced.
+template <typename T, int NV, bool FULL>
+__global__ __launch_bounds__(256) void k_rowstats_wide(const T *__restrict__ logits, int V, int blank,
+                                                       const SampleDesc *__restrict__ desc,
+                                                       const ChunkDesc *__restrict__ chunks,
+                                                       const int32_t *__restrict__ targets, int S,
+                                                       RowRec *__restrict__ rec, float2 *__restrict__ lp,
+                                                       float2 *__restrict__ prob, int *__restrict__ mode,
+                                                       uint32_t *status) {
+    constexpr int VEC = Raw<T>::kVec;
+    const ChunkDesc c = chunks[blockIdx.x];
+    const SampleDesc d = desc[c.sample];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int grp = lane / G;
-    for (int base = wave * RPW; base < c.row_count; base += 4 * RPW) {
-        const int r = base + grp;
-        body(r < c.row_count, c.row_begin + (r < c.row_count ? r : 0));
+    // wave-uniform, so per-row scalars travel through scalar loads and do not
+    // share the vector memory counter with the row prefetch
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nvec = V / VEC;
+    const int U1 = d.U + 1;
+    typename Raw<T>::vec xa[NV], xb[NV];
+    auto load_row = [&](int lr, typename Raw<T>::vec (&x)[NV]) {
+        const T *p = logits + (d.row_off + lr) * (int64_t)V;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int vi = i * 64 + lane;
+            if (FULL || vi < nvec) x[i] = load_raw<T, false>(p + (int64_t)vi * VEC);
+        }
+    };
+    int r = wave;
+    if (r < c.row_count) load_row(c.row_begin + r, xa);
+    for (; r < c.row_count; r += 4) {
+        const int lr = c.row_begin + r;
+        const int t = lr / U1;
+        const int u = lr - t * U1;
+        const int64_t row = d.row_off + lr;
+        const T *p = logits + row * (int64_t)V;
+        const int y = read_label(d, u, V, blank, targets, S, status);
+        const float hb = Elem<T>::load1(p + blank);
+        const float hy = (y >= 0) ? Elem<T>::load1(p + y) : 0.f;
+        // unconditional (the last row is re-read at the end of the chunk), so
+        // the wait counts for the current row never include these loads
+        load_row(c.row_begin + min(r + 4, c.row_count - 1), xb);
+        float m = kNegInf;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            if (FULL || i * 64 + lane < nvec)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) m = fmaxf(m, Raw<T>::get(xa[i], e));
+        m = wave_max_f(m);
+        const float mr = (m == kNegInf) ? 0.f : m;
+        const float nm = -mr * kLog2e;
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            if (FULL || i * 64 + lane < nvec)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) s += exp2_fast(fmaf(Raw<T>::get(xa[i], e), kLog2e, nm));
+        s = wave_sum_f(s);
+        const float dn = (m == kNegInf) ? kNegInf : m + log2_fast(s) * kLn2;
+        if (lane == 0) {
+            const bool dead = (dn == kNegInf);
+            const float lpb = dead ? kNegInf : hb - dn;
+            const float lpy = (dead || y < 0) ? kNegInf : hy - dn;
+            emit_node(d, t, u, row, dn, hb, hy, y, lpb, lpy, rec, lp, prob, mode);
+        }
+        if (t == 0 || t == d.T - 1) fill_outside(d, t, u, lane, 64, lp, prob);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) xa[i] = xb[i];
     }
 }
 
-// ------------------------------------------------------------- K1: rowstats
+// --------------------------------- K1 rowstats, G < 64 lanes per row (small V)
 template <typename T, int VEC, int G>
-__global__ __launch_bounds__(256) void k_rowstats(const T *__restrict__ logits, int V, int blank,
-                                                  const SampleDesc *__restrict__ desc,
-                                                  const ChunkDesc *__restrict__ chunks,
-                                                  const int32_t *__restrict__ targets, int S,
-                                                  float *__restrict__ den, float *__restrict__ lpb,
-                                                  float *__restrict__ lpy, uint32_t *status) {
+__global__ __launch_bounds__(256) void k_rowstats_narrow(const T *__restrict__ logits, int V, int blank,
+                                                         const SampleDesc *__restrict__ desc,
+                                                         const ChunkDesc *__restrict__ chunks,
+                                                         const int32_t *__restrict__ targets, int S,
+                                                         RowRec *__restrict__ rec, float2 *__restrict__ lp,
+                                                         float2 *__restrict__ prob, int *__restrict__ mode,
+                                                         uint32_t *status) {
+    constexpr int RPW = 64 / G;
     const ChunkDesc c = chunks[blockIdx.x];
     const SampleDesc d = desc[c.sample];
     const int U1 = d.U + 1;
-    const int sub = (threadIdx.x & 63) & (G - 1);
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int sub = lane & (G - 1);
+    const int grp = lane / G;
     const int nvec = V / VEC;
-    for_rows<T, VEC, G>(c, [&](bool active, int lr) {
+    for (int base = wave * RPW; base < c.row_count; base += 4 * RPW) {
+        const int r = base + grp;
+        const bool active = r < c.row_count;
+        const int lr = c.row_begin + (active ? r : 0);
         const int64_t row = d.row_off + lr;
         const T *p = logits + row * (int64_t)V;
         float m = kNegInf, s = 0.f;
         if (active) {
-            int i = sub;
-            for (; i + 3 * G < nvec; i += 4 * G) {
-                float x[4][VEC];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) load_n<T, VEC>(p + (int64_t)(i + q * G) * VEC, x[q]);
-                float vm = x[0][0];
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) vm = fmaxf(vm, x[q][e]);
-                const float mn = fmaxf(m, vm);
-                const float mr = (mn == kNegInf) ? 0.f : mn;
-                const float nm = -mr * kLog2e;
-                float acc = s * exp2_fast((m - mr) * kLog2e);
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) acc += exp2_fast(fmaf(x[q][e], kLog2e, nm));
-                s = acc;
-                m = mn;
-            }
-            for (; i < nvec; i += G) {
+            for (int i = sub; i < nvec; i += G) {
                 float x[VEC];
                 load_n<T, VEC>(p + (int64_t)i * VEC, x);
                 float vm = x[0];
@@ -172,26 +377,26 @@ __global__ __launch_bounds__(256) void k_rowstats(const T *__restrict__ logits, 
         for (int off = G / 2; off > 0; off >>= 1) {
             const float mo = __shfl_xor(m, off, 64);
             const float so = __shfl_xor(s, off, 64);
-            lse_merge(m, s, mo, so);
+            const float mn = fmaxf(m, mo);
+            const float mr = (mn == kNegInf) ? 0.f : mn;
+            s = s * exp2_fast((m - mr) * kLog2e) + so * exp2_fast((mo - mr) * kLog2e);
+            m = mn;
         }
-        if (active && sub == 0) {
-            const int t = lr / U1;
-            const int u = lr - t * U1;
+        if (!active) continue;
+        const int t = lr / U1;
+        const int u = lr - t * U1;
+        if (sub == 0) {
             const float dn = (m == kNegInf) ? kNegInf : m + log2_fast(s) * kLn2;
-            den[row] = dn;
-            const int64_t slot = d.slot_off + (int64_t)(t + u) * U1 + u;
+            const int y = read_label(d, u, V, blank, targets, S, status);
             const bool dead = (dn == kNegInf);
-            lpb[slot] = dead ? kNegInf : Elem<T>::load1(p + blank) - dn;
-            float ly = kNegInf;
-            if (u < d.U) {
-                const int y = targets[(int64_t)d.index * S + u];
-                const bool in_range = (y >= 0) && (y < V);
-                if (!in_range || y == blank) atomicOr(status, (uint32_t)RNNT_DEV_BAD_TARGET);
-                if (in_range && !dead) ly = Elem<T>::load1(p + y) - dn;
-            }
-            lpy[slot] = ly;
+            const float hb = Elem<T>::load1(p + blank);
+            const float hy = (y >= 0) ? Elem<T>::load1(p + y) : 0.f;
+            const float lpb = dead ? kNegInf : hb - dn;
+            const float lpy = (dead || y < 0) ? kNegInf : hy - dn;
+            emit_node(d, t, u, row, dn, hb, hy, y, lpb, lpy, rec, lp, prob, mode);
         }
-    });
+        if (t == 0 || t == d.T - 1) fill_outside(d, t, u, sub, G, lp, prob);
+    }
 }
 
 // Non-fused inputs are already log-probabilities: gather the two values only.
@@ -200,7 +405,8 @@ __global__ __launch_bounds__(256) void k_gather(const T *__restrict__ logits, in
                                                 const SampleDesc *__restrict__ desc,
                                                 const ChunkDesc *__restrict__ chunks,
                                                 const int32_t *__restrict__ targets, int S,
-                                                float *__restrict__ lpb, float *__restrict__ lpy,
+                                                RowRec *__restrict__ rec, float2 *__restrict__ lp,
+                                                float2 *__restrict__ prob, int *__restrict__ mode,
                                                 uint32_t *status) {
     const ChunkDesc c = chunks[blockIdx.x];
     const SampleDesc d = desc[c.sample];
@@ -209,167 +415,235 @@ __global__ __launch_bounds__(256) void k_gather(const T *__restrict__ logits, in
         const int lr = c.row_begin + r;
         const int t = lr / U1;
         const int u = lr - t * U1;
-        const T *p = logits + (d.row_off + lr) * (int64_t)V;
-        const int64_t slot = d.slot_off + (int64_t)(t + u) * U1 + u;
-        lpb[slot] = Elem<T>::load1(p + blank);
-        float ly = kNegInf;
-        if (u < d.U) {
-            const int y = targets[(int64_t)d.index * S + u];
-            const bool in_range = (y >= 0) && (y < V);
-            if (!in_range || y == blank) atomicOr(status, (uint32_t)RNNT_DEV_BAD_TARGET);
-            if (in_range) ly = Elem<T>::load1(p + y);
-        }
-        lpy[slot] = ly;
+        const int64_t row = d.row_off + lr;
+        const T *p = logits + row * (int64_t)V;
+        const int y = read_label(d, u, V, blank, targets, S, status);
+        const float lpb = Elem<T>::load1(p + blank);
+        const float lpy = (y < 0) ? kNegInf : Elem<T>::load1(p + y);
+        emit_node(d, t, u, row, 0.f, lpb, lpy, y, lpb, lpy, rec, lp, prob, mode);
+        if (t == 0 || t == d.T - 1) fill_outside(d, t, u, 0, 1, lp, prob);
     }
 }
 
 // ----------------------------------------------------- K2: alpha/beta sweeps
-// Lane l of the wave owns lattice columns u = l + 64*j, j < C.  Anti-diagonal
-// n = t+u holds the nodes whose predecessors all lie on diagonal n-1, so one
-// step per diagonal advances every node of it at once.  The per-slot
-// log-probs of the next PF diagonals are kept in flight in a register ring.
-template <int C>
-__device__ __forceinline__ void load_diag(const float *__restrict__ lpb, const float *__restrict__ lpy, int n,
-                                          int nd, int U1, int lane, float *rb, float *ry) {
+// Lane l owns lattice columns u = l + 64*j, j < C.  Lanes past the lattice
+// width read column U instead: their values start at zero (-inf in the log
+// domain) and only ever receive zero, because the label edge leaving column U
+// is stored as impossible.  The node inputs of PF diagonals are loaded one
+// block ahead; each block's outputs are stored after it, so a wait for a
+// block's loads never waits for the previous block's stores.
+//
+// Probability domain: node value = mantissa * 2^E[n].  Forward step:
+//   a(n,u) = a(n-1,u) * pb(n-1,u) + a(n-1,u-1) * py(n-1,u-1)
+// kept as the two messages leaving diagonal n-1.  Backward step:
+//   b(n,u) = b(n+1,u) * pb(n,u) + b(n+1,u+1) * py(n,u).
+// Every fourth diagonal is rescaled by 2^-e so its largest value is in
+// [1, 2): |log-prob| <= 80 bounds the drift over four steps by 2^+-470.
+//
+// Log domain (fallback): the same recursions in log2 units with
+// log2(2^a + 2^b) in place of the sum and log2-prob addition in place of the
+// product; E[n] = 0.
+struct ProbDomain {
+    static constexpr bool kLog = false;
+    __device__ static double zero() { return 0.0; }
+    __device__ static double one() { return 1.0; }
+    __device__ static double combine(double a, double b) { return a + b; }
+    __device__ static double edge(double a, float w) { return a * (double)w; }
+};
+struct LogDomain {
+    static constexpr bool kLog = true;
+    __device__ static double zero() { return kNegInfD; }
+    __device__ static double one() { return 0.0; }
+    __device__ static double combine(double a, double b) {
+        const double mx = fmax(a, b);
+        const double mn = fmin(a, b);
+        const float l = log2_fast(1.0f + exp2_fast((float)(mn - mx)));
+        return (mn == kNegInfD) ? mx : mx + (double)l;
+    }
+    __device__ static double edge(double a, float lpv) { return a + (double)lpv * kLog2eD; }
+};
+
+template <int C> __device__ __forceinline__ int renorm(double (&a)[C]) {
+    int eb = 0;
 #pragma unroll
-    for (int j = 0; j < C; ++j) {
-        const int u = lane + 64 * j;
-        const bool ok = (n >= 0) && (n < nd) && (u < U1);
-        const int64_t s = ok ? (int64_t)n * U1 + u : 0;
-        rb[j] = ok ? lpb[s] : 0.f;
-        ry[j] = ok ? lpy[s] : 0.f;
+    for (int j = 0; j < C; ++j) eb = max(eb, (__double2hiint(a[j]) >> 20) & 0x7ff);
+    eb = wave_max_i(eb);
+    const int sh = eb - 1023;
+#pragma unroll
+    for (int j = 0; j < C; ++j) a[j] = __builtin_amdgcn_ldexp(a[j], -sh);
+    return sh;
+}
+
+template <int C, int PF> struct Ring {
+    float2 v[PF][C];
+};
+
+// Diagonals n0, n0+step, ... (clamped into [0, nd)) of a sample's slots.
+template <int C, int PF>
+__device__ __forceinline__ void load_block(Ring<C, PF> &r, const float2 *__restrict__ w, int U, int n0, int step,
+                                           int nd) {
+    const int lane = threadIdx.x & 63;
+    const int U1 = U + 1;
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+        const int n = min(max(n0 + step * p, 0), nd - 1);
+        const float2 *row = w + (int64_t)n * U1;
+#pragma unroll
+        for (int j = 0; j < C; ++j) r.v[p][j] = row[min(lane + 64 * j, U)];
     }
 }
 
-template <int C> __device__ __forceinline__ double pick(const double (&v)[C], int j) {
-    double r = v[0];
-#pragma unroll
-    for (int q = 1; q < C; ++q) r = (q == j) ? v[q] : r;
-    return r;
-}
-
-// Forward variable: alpha(t,u) = log-sum of all partial alignments reaching
-// (t,u).  Messages leaving diagonal n-1: mb = alpha + log P(blank) towards
-// (t+1,u) (same lane), my = alpha + log P(y_{u+1}) towards (t,u+1) (next lane).
-template <int C, int PF>
-__device__ void sweep_alpha(int T, int U, const float *__restrict__ lpb, const float *__restrict__ lpy,
-                            double *__restrict__ alpha, double *logz) {
+template <typename D, int C, int PF>
+__device__ void sweep_forward(const SampleDesc &d, const float2 *__restrict__ w, double *__restrict__ out,
+                              int *__restrict__ eout, double *log2z) {
     const int lane = threadIdx.x & 63;
-    const int U1 = U + 1;
-    const int nd = T + U;
+    const int U = d.U, U1 = U + 1, nd = d.T + U;
     double mb[C], my[C];
 #pragma unroll
-    for (int j = 0; j < C; ++j) { mb[j] = kNegInfD; my[j] = kNegInfD; }
-    float rb[PF][C], ry[PF][C];
-#pragma unroll
-    for (int p = 0; p < PF; ++p) load_diag<C>(lpb, lpy, p, nd, U1, lane, rb[p], ry[p]);
+    for (int j = 0; j < C; ++j) { mb[j] = D::zero(); my[j] = D::zero(); }
+    int E = 0;
+    Ring<C, PF> cur, nxt;
+    load_block<C, PF>(cur, w, U, 0, 1, nd);
     for (int n0 = 0; n0 < nd; n0 += PF) {
+        if (n0 + PF < nd) load_block<C, PF>(nxt, w, U, n0 + PF, 1, nd);
+        double ob[PF][C];
 #pragma unroll
         for (int p = 0; p < PF; ++p) {
             const int n = n0 + p;
             if (n < nd) {
-                const int ulo = max(0, n - T + 1);
-                const int uhi = min(n, U);
-                double inl[C];
+                double a[C];
+                if (n == 0) {
+#pragma unroll
+                    for (int j = 0; j < C; ++j) a[j] = (j == 0 && lane == 0) ? D::one() : D::zero();
+                } else {
+#pragma unroll
+                    for (int j = 0; j < C; ++j) {
+                        const double edge = (j == 0) ? D::zero() : read_lane_d(my[j > 0 ? j - 1 : 0], 63);
+                        a[j] = D::combine(mb[j], shift_up(my[j], edge));
+                    }
+                }
+                if (!D::kLog && (n & 3) == 3) E += renorm<C>(a);
 #pragma unroll
                 for (int j = 0; j < C; ++j) {
-                    const double up = __shfl_up(my[j], 1, 64);
-                    const double wrap = (j > 0) ? __shfl(my[j > 0 ? j - 1 : 0], 63, 64) : kNegInfD;
-                    inl[j] = (lane == 0) ? wrap : up;
+                    ob[p][j] = a[j];
+                    mb[j] = D::edge(a[j], cur.v[p][j].x);
+                    my[j] = D::edge(a[j], cur.v[p][j].y);
                 }
-#pragma unroll
-                for (int j = 0; j < C; ++j) {
-                    const int u = lane + 64 * j;
-                    const bool valid = (u >= ulo) && (u <= uhi);
-                    const double a = (n == 0) ? 0.0 : log_add(mb[j], inl[j]);
-                    if (valid) alpha[(int64_t)n * U1 + u] = a;
-                    mb[j] = valid ? a + (double)rb[p][j] : kNegInfD;
-                    my[j] = (valid && u < U) ? a + (double)ry[p][j] : kNegInfD;
-                }
-                load_diag<C>(lpb, lpy, n + PF, nd, U1, lane, rb[p], ry[p]);
+                if (lane == 0) eout[n] = E;
             }
         }
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            const int n = n0 + p;
+            if (n < nd) {
+#pragma unroll
+                for (int j = 0; j < C; ++j)
+                    if (lane + 64 * j < U1) out[(int64_t)n * U1 + lane + 64 * j] = ob[p][j];
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < PF; ++p)
+#pragma unroll
+            for (int j = 0; j < C; ++j) cur.v[p][j] = nxt.v[p][j];
     }
-    // The last diagonal holds only (T-1, U); its blank message is log P(y|x).
-    const double v = pick<C>(mb, U >> 6);
+    // The last diagonal holds only (T-1, U); its blank message is P(y|x).
+    double v = mb[0];
+#pragma unroll
+    for (int j = 1; j < C; ++j) v = (j == (U >> 6)) ? mb[j] : v;
     const double z = __shfl(v, U & 63, 64);
-    if (lane == 0) *logz = z;
+    if (lane == 0) *log2z = D::kLog ? z : log2_d(z) + (double)E;
 }
 
-// Backward variable: beta(t,u) = log-sum of all alignment suffixes from (t,u),
-// including the final blank, so beta(0,0) = log P(y|x).
-template <int C, int PF>
-__device__ void sweep_beta(int T, int U, const float *__restrict__ lpb, const float *__restrict__ lpy,
-                           double *__restrict__ beta, double *logz) {
+template <typename D, int C, int PF>
+__device__ void sweep_backward(const SampleDesc &d, const float2 *__restrict__ w, double *__restrict__ out,
+                               int *__restrict__ eout, double *log2z) {
     const int lane = threadIdx.x & 63;
-    const int U1 = U + 1;
-    const int nd = T + U;
+    const int U = d.U, U1 = U + 1, nd = d.T + U;
+    // values of the virtual diagonal nd: the empty suffix after the final
+    // blank has probability one at u = U
     double pv[C];
 #pragma unroll
-    for (int j = 0; j < C; ++j) pv[j] = kNegInfD;
-    float rb[PF][C], ry[PF][C];
-#pragma unroll
-    for (int p = 0; p < PF; ++p) load_diag<C>(lpb, lpy, nd - 1 - p, nd, U1, lane, rb[p], ry[p]);
+    for (int j = 0; j < C; ++j) pv[j] = (lane + 64 * j == U) ? D::one() : D::zero();
+    int E = 0;
+    Ring<C, PF> cur, nxt;
+    load_block<C, PF>(cur, w, U, nd - 1, -1, nd);
     for (int n0 = nd - 1; n0 >= 0; n0 -= PF) {
+        if (n0 - PF >= 0) load_block<C, PF>(nxt, w, U, n0 - PF, -1, nd);
+        double ob[PF][C];
 #pragma unroll
         for (int p = 0; p < PF; ++p) {
             const int n = n0 - p;
             if (n >= 0) {
-                const int ulo = max(0, n - T + 1);
-                const int uhi = min(n, U);
-                double nx[C];
+                double b[C];
 #pragma unroll
                 for (int j = 0; j < C; ++j) {
-                    const double dn = __shfl_down(pv[j], 1, 64);
-                    const double wrap = (j + 1 < C) ? __shfl(pv[j + 1 < C ? j + 1 : j], 0, 64) : kNegInfD;
-                    nx[j] = (lane == 63) ? wrap : dn;
+                    const double edge = (j + 1 < C) ? read_lane_d(pv[j + 1 < C ? j + 1 : j], 0) : D::zero();
+                    const double nx = shift_down(pv[j], edge);
+                    b[j] = D::combine(D::edge(pv[j], cur.v[p][j].x), D::edge(nx, cur.v[p][j].y));
                 }
+                if (!D::kLog && ((nd - 1 - n) & 3) == 3) E += renorm<C>(b);
 #pragma unroll
                 for (int j = 0; j < C; ++j) {
-                    const int u = lane + 64 * j;
-                    const bool valid = (u >= ulo) && (u <= uhi);
-                    const double b = (n == nd - 1)
-                                         ? (double)rb[p][j]
-                                         : log_add(pv[j] + (double)rb[p][j], nx[j] + (double)ry[p][j]);
-                    if (valid) beta[(int64_t)n * U1 + u] = b;
-                    pv[j] = valid ? b : kNegInfD;
+                    ob[p][j] = b[j];
+                    pv[j] = b[j];
                 }
-                load_diag<C>(lpb, lpy, n - PF, nd, U1, lane, rb[p], ry[p]);
+                if (lane == 0) eout[n] = E;
             }
         }
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            const int n = n0 - p;
+            if (n >= 0) {
+#pragma unroll
+                for (int j = 0; j < C; ++j)
+                    if (lane + 64 * j < U1) out[(int64_t)n * U1 + lane + 64 * j] = ob[p][j];
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < PF; ++p)
+#pragma unroll
+            for (int j = 0; j < C; ++j) cur.v[p][j] = nxt.v[p][j];
     }
-    const double z = __shfl(pv[0], 0, 64);
-    if (lane == 0) *logz = z;
+    if (lane == 0) *log2z = D::kLog ? pv[0] : log2_d(pv[0]) + (double)E;
 }
 
 template <int C, int PF>
-__device__ void run_sweeps(const SampleDesc &d, const float *lpb, const float *lpy, double *alpha,
-                           double *beta, double *shz) {
+__device__ void run_sweeps(const SampleDesc &d, bool log_mode, const float2 *lp, const float2 *prob, double *alpha,
+                           double *beta, int *ea, int *eb, double *shz) {
     const int wave = threadIdx.x >> 6;
-    if (wave == 0)
-        sweep_alpha<C, PF>(d.T, d.U, lpb + d.slot_off, lpy + d.slot_off, alpha + d.slot_off, &shz[0]);
-    else
-        sweep_beta<C, PF>(d.T, d.U, lpb + d.slot_off, lpy + d.slot_off, beta + d.slot_off, &shz[1]);
+    const int64_t so = d.slot_off;
+    const int64_t dof = d.diag_off;
+    if (log_mode) {
+        if (wave == 0) sweep_forward<LogDomain, C, PF>(d, lp + so, alpha + so, ea + dof, &shz[0]);
+        else sweep_backward<LogDomain, C, PF>(d, lp + so, beta + so, eb + dof, &shz[1]);
+    } else {
+        if (wave == 0) sweep_forward<ProbDomain, C, PF>(d, prob + so, alpha + so, ea + dof, &shz[0]);
+        else sweep_backward<ProbDomain, C, PF>(d, prob + so, beta + so, eb + dof, &shz[1]);
+    }
 }
 
 __global__ __launch_bounds__(128) void k_alpha_beta(const SampleDesc *__restrict__ desc,
                                                     const int32_t *__restrict__ order,
-                                                    const float *__restrict__ lpb, const float *__restrict__ lpy,
-                                                    double *__restrict__ alpha, double *__restrict__ beta,
+                                                    const int *__restrict__ mode, const float2 *__restrict__ lp,
+                                                    const float2 *__restrict__ prob, double *__restrict__ alpha,
+                                                    double *__restrict__ beta, int *__restrict__ ealpha,
+                                                    int *__restrict__ ebeta, double *__restrict__ log2z,
                                                     float *__restrict__ loss, uint32_t *status) {
     __shared__ double shz[2];
     const SampleDesc d = desc[order[blockIdx.x]];
+    const bool lm = mode[d.index] != 0;
     const int U1 = d.U + 1;
-    if (U1 <= 64) run_sweeps<1, 8>(d, lpb, lpy, alpha, beta, shz);
-    else if (U1 <= 128) run_sweeps<2, 8>(d, lpb, lpy, alpha, beta, shz);
-    else if (U1 <= 256) run_sweeps<4, 8>(d, lpb, lpy, alpha, beta, shz);
-    else if (U1 <= 512) run_sweeps<8, 4>(d, lpb, lpy, alpha, beta, shz);
-    else run_sweeps<16, 4>(d, lpb, lpy, alpha, beta, shz);
+    if (U1 <= 64) run_sweeps<1, 32>(d, lm, lp, prob, alpha, beta, ealpha, ebeta, shz);
+    else if (U1 <= 128) run_sweeps<2, 16>(d, lm, lp, prob, alpha, beta, ealpha, ebeta, shz);
+    else if (U1 <= 256) run_sweeps<4, 8>(d, lm, lp, prob, alpha, beta, ealpha, ebeta, shz);
+    else if (U1 <= 512) run_sweeps<8, 2>(d, lm, lp, prob, alpha, beta, ealpha, ebeta, shz);
+    else run_sweeps<16, 1>(d, lm, lp, prob, alpha, beta, ealpha, ebeta, shz);
     __syncthreads();
     if (threadIdx.x == 0) {
-        const double la = -shz[0];
-        const double lb = -shz[1];
+        const double la = -shz[0] * kLn2D;
+        const double lb = -shz[1] * kLn2D;
         loss[d.index] = (float)lb;
+        log2z[d.index] = shz[1];
         const bool agree = (la == lb) || (fabs(la - lb) <= 1e-4 * fmax(1.0, fabs(lb)));
         if (!agree) atomicOr(status, (uint32_t)RNNT_DEV_LOSS_MISMATCH);
     }
@@ -377,88 +651,209 @@ __global__ __launch_bounds__(128) void k_alpha_beta(const SampleDesc *__restrict
 
 // ------------------------------------------------------------ K3: gradient
 // g_k = P(k|t,u) * occ(t,u) - [k = blank] flow_b - [k = y_{u+1}] flow_y, where
-// occ = exp(alpha + beta - logZ) and the flows are the posterior
-// probabilities of leaving (t,u) by blank or by the next label.  P * occ is
-// evaluated as exp2(x * log2(e) + shift) with one per-row shift.
+// occ = alpha*beta/P(y|x) and the flows are the posterior probabilities of
+// leaving (t,u) by blank or by the next label.  P * occ is evaluated as
+// exp2(x * log2(e) + shift) with one per-row shift.
 struct RowTerms {
-    float shift2;  // log2 of (occ * scale / sum_k exp(x_k)), or -inf
+    float shift2;  // log2(occ * scale) - den * log2(e), or -inf
     float fb;      // scaled blank flow
     float fy;      // scaled label flow
     int y;         // next label, -1 at u = U or when invalid
 };
 
-__device__ __forceinline__ RowTerms row_terms(const SampleDesc &d, int lr, int V, float den_row, double logz,
-                                              const float *__restrict__ lpb, const float *__restrict__ lpy,
-                                              const double *__restrict__ alpha, const double *__restrict__ beta,
-                                              const int32_t *__restrict__ targets, int S, float log2_scale,
-                                              float scale, bool fused) {
+struct SampleTerms {
+    double log2z;
+    bool log_mode;
+};
+
+__device__ __forceinline__ double node_log2(const double *__restrict__ v, const int *__restrict__ e, int64_t s,
+                                            int n, bool log_mode) {
+    return log_mode ? v[s] : log2_d(v[s]) + (double)e[n];
+}
+
+__device__ __forceinline__ RowTerms row_terms(const SampleDesc &d, const SampleTerms &st, int lr, const RowRec &rr,
+                                              const float2 *__restrict__ lp, const double *__restrict__ alpha,
+                                              const double *__restrict__ beta, const int *__restrict__ ealpha,
+                                              const int *__restrict__ ebeta, float log2_scale, float scale,
+                                              bool fused) {
     const int U1 = d.U + 1;
     const int t = lr / U1;
     const int u = lr - t * U1;
-    const int64_t s = d.slot_off + (int64_t)(t + u) * U1 + u;
-    const double a = alpha[s];
+    const int n = t + u;
+    const int64_t s = d.slot_off + (int64_t)n * U1 + u;
+    const int *ea = ealpha + d.diag_off;
+    const int *eb = ebeta + d.diag_off;
     double lb = kNegInfD, ly = kNegInfD, lo = kNegInfD;
-    if (logz != kNegInfD) {
-        lo = a + beta[s] - logz;
-        if (t < d.T - 1) lb = a + (double)lpb[s] + beta[s + U1] - logz;
-        else if (u == d.U) lb = a + (double)lpb[s] - logz;
-        if (u < d.U) ly = a + (double)lpy[s] + beta[s + U1 + 1] - logz;
+    if (st.log2z != kNegInfD) {
+        const double a2 = node_log2(alpha, ea, s, n, st.log_mode) - st.log2z;
+        const float2 l = lp[s];
+        lo = a2 + node_log2(beta, eb, s, n, st.log_mode);
+        if (t < d.T - 1) lb = a2 + (double)l.x * kLog2eD + node_log2(beta, eb, s + U1, n + 1, st.log_mode);
+        else if (u == d.U) lb = a2 + (double)l.x * kLog2eD;
+        if (u < d.U) ly = a2 + (double)l.y * kLog2eD + node_log2(beta, eb, s + U1 + 1, n + 1, st.log_mode);
     }
     RowTerms r;
-    r.shift2 = fused ? (float)((lo - (double)den_row) * kLog2eD) + log2_scale : kNegInf;
-    r.fb = exp2_fast((float)(lb * kLog2eD)) * scale;
-    r.fy = exp2_fast((float)(ly * kLog2eD)) * scale;
-    int y = -1;
-    if (u < d.U) {
-        y = targets[(int64_t)d.index * S + u];
-        if (y < 0 || y >= V) y = -1;
-    }
-    r.y = y;
+    r.shift2 = fused ? (float)(lo - (double)rr.den * kLog2eD) + log2_scale : kNegInf;
+    r.fb = exp2_fast((float)lb) * scale;
+    r.fy = exp2_fast((float)ly) * scale;
+    r.y = rr.y;
     return r;
 }
 
-template <typename T, int VEC, int G, bool FUSED>
-__global__ __launch_bounds__(256) void k_grad(const T *logits, T *grad, int V, int blank,
-                                              float clamp, float scale, float log2_scale,
-                                              const SampleDesc *__restrict__ desc,
-                                              const ChunkDesc *__restrict__ chunks, int n_chunks,
-                                              const int32_t *__restrict__ targets, int S,
-                                              const float *__restrict__ den, const float *__restrict__ lpb,
-                                              const float *__restrict__ lpy, const double *__restrict__ alpha,
-                                              const double *__restrict__ beta) {
+struct GradArgs {
+    int V, blank, n_chunks;
+    float clamp, scale, log2_scale;
+    const SampleDesc *desc;
+    const ChunkDesc *chunks;
+    const int *mode;
+    const double *log2z;
+    const RowRec *rec;
+    const float2 *lp;
+    const double *alpha;
+    const double *beta;
+    const int *ealpha;
+    const int *ebeta;
+};
+
+// The workspace arrays reach the gradient kernels as separate restrict
+// parameters, so the compiler knows the gradient stores cannot clobber them
+// and reads their wave-uniform elements through the scalar cache.
+#define RNNT_GRAD_PARAMS                                                                                      \
+    int V, int blank, int n_chunks, float clamp, float scale, float log2_scale,                              \
+        const SampleDesc *__restrict__ desc, const ChunkDesc *__restrict__ chunks, const int *__restrict__ mode, \
+        const double *__restrict__ log2z, const RowRec *__restrict__ rec, const float2 *__restrict__ lp,       \
+        const double *__restrict__ alpha, const double *__restrict__ beta, const int *__restrict__ ealpha,     \
+        const int *__restrict__ ebeta
+#define RNNT_GRAD_ARGS(g)                                                                                     \
+    g.V, g.blank, g.n_chunks, g.clamp, g.scale, g.log2_scale, g.desc, g.chunks, g.mode, g.log2z, g.rec, g.lp, \
+        g.alpha, g.beta, g.ealpha, g.ebeta
+
+__device__ __forceinline__ float clamp_to(float v, float cl, bool do_clamp) {
+    return do_clamp ? fminf(fmaxf(v, -cl), cl) : v;
+}
+
+// The blank and label elements of a row get their flow subtracted by a
+// separate store from the thread that wrote the vector holding them (the
+// two stores are ordered: same thread, same address).  Their input values
+// come from the row record, not from the logits, which an in-place gradient
+// has already overwritten.
+template <typename T, bool FUSED>
+__device__ __forceinline__ void fix_special(T *dst, bool own_b, bool own_y, int blank, const RowRec &rr,
+                                            const RowTerms &rt, bool do_clamp, float cl) {
+    auto fix = [&](int k, float x, float sub) {
+        float v = 0.f;
+        if constexpr (FUSED) v = exp2_fast(fmaf(x, kLog2e, rt.shift2));
+        Elem<T>::store1(dst + k, clamp_to(v - sub, cl, do_clamp));
+    };
+    if (rt.y == blank) {
+        if (own_b) fix(blank, rr.xb, rt.fb + rt.fy);
+    } else {
+        if (own_b) fix(blank, rr.xb, rt.fb);
+        if (own_y) fix(rt.y, rr.xy, rt.fy);
+    }
+}
+
+// One row per wave; the next row's logits are loaded before the current
+// row's gradient is computed and written.
+template <typename T, int NV, bool FULL, bool FUSED, bool CLAMP>
+__global__ __launch_bounds__(256) void k_grad_wide(const T *logits, T *grad, RNNT_GRAD_PARAMS) {
+    constexpr int VEC = Raw<T>::kVec;
     // Chunks run in the reverse of the rowstats order, so the rows read last
     // by that pass, the likeliest to still be cached, are read again first.
     const ChunkDesc c = chunks[n_chunks - 1 - blockIdx.x];
     const SampleDesc d = desc[c.sample];
-    const double logz = beta[d.slot_off];  // beta(0,0)
-    const int sub = (threadIdx.x & 63) & (G - 1);
+    const SampleTerms st{log2z[d.index], mode[d.index] != 0};
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nvec = V / VEC;
+    const float cl = clamp * scale;
+    typename Raw<T>::vec xa[NV], xb[NV];
+    auto load_row = [&](int lr, typename Raw<T>::vec (&x)[NV]) {
+        if constexpr (FUSED) {
+            const T *p = logits + (d.row_off + lr) * (int64_t)V;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int vi = i * 64 + lane;
+                if (FULL || vi < nvec) x[i] = load_raw<T, true>(p + (int64_t)vi * VEC);
+            }
+        }
+    };
+    int r = wave;
+    if (r < c.row_count) load_row(c.row_begin + r, xa);
+    for (; r < c.row_count; r += 4) {
+        const int lr = c.row_begin + r;
+        const int64_t row = d.row_off + lr;
+        const RowRec rr = rec[row];
+        const RowTerms rt = row_terms(d, st, lr, rr, lp, alpha, beta, ealpha, ebeta, log2_scale,
+                                      scale, FUSED);
+        // unconditional (the last row is re-read at the end of the chunk), so
+        // the wait counts for the current row never include these loads
+        load_row(c.row_begin + min(r + 4, c.row_count - 1), xb);
+        T *dst = grad + row * (int64_t)V;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int vi = i * 64 + lane;
+            if (FULL || vi < nvec) {
+                float gv[VEC];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    float v = 0.f;
+                    if constexpr (FUSED) v = exp2_fast(fmaf(Raw<T>::get(xa[i], e), kLog2e, rt.shift2));
+                    gv[e] = clamp_to(v, cl, CLAMP);
+                }
+                store_raw<T, true>(dst + (int64_t)vi * VEC, Raw<T>::put(gv));
+            }
+        }
+        // element k lies in vector k / VEC, held by lane (k / VEC) mod 64
+        const bool ob = ((blank / VEC) & 63) == lane;
+        const bool oy = rt.y >= 0 && ((rt.y / VEC) & 63) == lane;
+        if (ob || oy) fix_special<T, FUSED>(dst, ob, oy, blank, rr, rt, CLAMP, cl);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) xa[i] = xb[i];
+    }
+}
+
+// G < 64 lanes per row (small V), 64/G rows per wave.
+template <typename T, int VEC, int G, bool FUSED>
+__global__ __launch_bounds__(256) void k_grad_narrow(const T *logits, T *grad, RNNT_GRAD_PARAMS) {
+    constexpr int RPW = 64 / G;
+    const ChunkDesc c = chunks[n_chunks - 1 - blockIdx.x];
+    const SampleDesc d = desc[c.sample];
+    const SampleTerms st{log2z[d.index], mode[d.index] != 0};
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int sub = lane & (G - 1);
+    const int grp = lane / G;
     const int nvec = V / VEC;
     const float cl = clamp * scale;
     const bool do_clamp = clamp > 0.f;
-    for_rows<T, VEC, G>(c, [&](bool active, int lr) {
-        if (!active) return;
+    for (int base = wave * RPW; base < c.row_count; base += 4 * RPW) {
+        const int r = base + grp;
+        if (r >= c.row_count) continue;
+        const int lr = c.row_begin + r;
         const int64_t row = d.row_off + lr;
-        const RowTerms rt = row_terms(d, lr, V, FUSED ? den[row] : 0.f, logz, lpb, lpy, alpha, beta, targets, S,
-                                      log2_scale, scale, FUSED);
+        const RowRec rr = rec[row];
+        const RowTerms rt = row_terms(d, st, lr, rr, lp, alpha, beta, ealpha, ebeta, log2_scale,
+                                      scale, FUSED);
         const T *src = logits + row * (int64_t)V;
         T *dst = grad + row * (int64_t)V;
         for (int i = sub; i < nvec; i += G) {
             float x[VEC];
             if constexpr (FUSED) load_n<T, VEC>(src + (int64_t)i * VEC, x);
-            float g[VEC];
+            float gv[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                const int k = i * VEC + e;
                 float v = 0.f;
                 if constexpr (FUSED) v = exp2_fast(fmaf(x[e], kLog2e, rt.shift2));
-                v -= (k == blank) ? rt.fb : 0.f;
-                v -= (k == rt.y) ? rt.fy : 0.f;
-                if (do_clamp) v = fminf(fmaxf(v, -cl), cl);
-                g[e] = v;
+                gv[e] = clamp_to(v, cl, do_clamp);
             }
-            store_n<T, VEC>(dst + (int64_t)i * VEC, g);
+            store_n<T, VEC>(dst + (int64_t)i * VEC, gv);
         }
-    });
+        // the thread whose vectors hold the blank / label element rewrites it
+        const bool ob = ((blank / VEC) % G) == sub;
+        const bool oy = rt.y >= 0 && ((rt.y / VEC) % G) == sub;
+        if (ob || oy) fix_special<T, FUSED>(dst, ob, oy, blank, rr, rt, do_clamp, cl);
+    }
 }
 
 // --------------------------------------------------------------- reduction
@@ -476,15 +871,18 @@ template <typename T, int VEC, int G>
 __global__ __launch_bounds__(256) void k_grad_scale(T *grad, int V, const SampleDesc *__restrict__ desc,
                                                     const ChunkDesc *__restrict__ chunks,
                                                     const float *__restrict__ scale, int per_sample) {
+    constexpr int RPW = 64 / G;
     const ChunkDesc c = chunks[blockIdx.x];
     const SampleDesc d = desc[c.sample];
     const float f = scale[per_sample ? d.index : 0];
     if (f == 1.0f) return;
-    const int sub = (threadIdx.x & 63) & (G - 1);
+    const int lane = threadIdx.x & 63;
+    const int sub = lane & (G - 1);
     const int nvec = V / VEC;
-    for_rows<T, VEC, G>(c, [&](bool active, int lr) {
-        if (!active) return;
-        T *p = grad + (d.row_off + lr) * (int64_t)V;
+    for (int base = (threadIdx.x >> 6) * RPW; base < c.row_count; base += 4 * RPW) {
+        const int r = base + lane / G;
+        if (r >= c.row_count) continue;
+        T *p = grad + (d.row_off + c.row_begin + r) * (int64_t)V;
         for (int i = sub; i < nvec; i += G) {
             float x[VEC];
             load_n<T, VEC>(p + (int64_t)i * VEC, x);
@@ -492,17 +890,18 @@ __global__ __launch_bounds__(256) void k_grad_scale(T *grad, int V, const Sample
             for (int e = 0; e < VEC; ++e) x[e] *= f;
             store_n<T, VEC>(p + (int64_t)i * VEC, x);
         }
-    });
+    }
 }
 
 // ------------------------------------------------------------- dispatchers
-template <typename T, int VEC, int G> struct Tag {
+template <typename T, int VEC, int N> struct Tag {
     using type = T;
     static constexpr int vec = VEC;
-    static constexpr int g = G;
+    static constexpr int n = N;
 };
 
-template <typename Fn> hipError_t with_geom(int esize, int vec, int G, Fn &&fn) {
+// Narrow geometry: N = lanes per row.  Wide geometry: N = vectors per lane.
+template <typename Fn> hipError_t with_narrow(int esize, int vec, int G, Fn &&fn) {
 #define RNNT_CASE_G(T, VEC)                                   \
     switch (G) {                                              \
     case 4: return fn(Tag<T, VEC, 4>{});                      \
@@ -520,6 +919,20 @@ template <typename Fn> hipError_t with_geom(int esize, int vec, int G, Fn &&fn) 
 #undef RNNT_CASE_G
 }
 
+template <typename Fn> hipError_t with_wide(int esize, int nv, Fn &&fn) {
+#define RNNT_CASE_NV(T, VEC)                                  \
+    switch (nv) {                                             \
+    case 1: return fn(Tag<T, VEC, 1>{});                      \
+    case 2: return fn(Tag<T, VEC, 2>{});                      \
+    case 4: return fn(Tag<T, VEC, 4>{});                      \
+    case 8: return fn(Tag<T, VEC, 8>{});                      \
+    default: return fn(Tag<T, VEC, 16>{});                    \
+    }
+    if (esize == 4) { RNNT_CASE_NV(float, 4) }
+    RNNT_CASE_NV(_Float16, 8)
+#undef RNNT_CASE_NV
+}
+
 }  // namespace
 
 RowGeom row_geometry(int V, int esize, bool aligned16) {
@@ -530,6 +943,18 @@ RowGeom row_geometry(int V, int esize, bool aligned16) {
     while (G < 64 && G < nvec) G <<= 1;
     g.lanes_per_row = G;
     g.rows_per_block_iter = 4 * (64 / G);
+    // One row per wave with the row held in registers: 16-byte vectors and at
+    // most 16 of them per lane.
+    g.wide_nv = 0;
+    g.wide_full = false;
+    if (aligned16 && G == 64 && nvec > 64) {
+        int nv = 1;
+        while (nv * 64 < nvec) nv <<= 1;
+        if (nv <= 16) {
+            g.wide_nv = nv;
+            g.wide_full = (nvec == nv * 64);
+        }
+    }
     return g;
 }
 
@@ -541,48 +966,94 @@ hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream) {
         if (a.esize == 4)
             hipLaunchKernelGGL(k_gather<float>, grid, block, 0, stream, static_cast<const float *>(a.logits), a.V,
                                a.blank, WS(const SampleDesc *, desc), WS(const ChunkDesc *, chunks), a.targets, a.S,
-                               WS(float *, lpb), WS(float *, lpy), WS(uint32_t *, status));
+                               WS(RowRec *, rec), WS(float2 *, lp), WS(float2 *, prob), WS(int *, mode),
+                               WS(uint32_t *, status));
         else
             hipLaunchKernelGGL(k_gather<_Float16>, grid, block, 0, stream, static_cast<const _Float16 *>(a.logits),
                                a.V, a.blank, WS(const SampleDesc *, desc), WS(const ChunkDesc *, chunks), a.targets,
-                               a.S, WS(float *, lpb), WS(float *, lpy), WS(uint32_t *, status));
+                               a.S, WS(RowRec *, rec), WS(float2 *, lp), WS(float2 *, prob), WS(int *, mode),
+                               WS(uint32_t *, status));
         return hipGetLastError();
     }
-    return with_geom(a.esize, a.geom.vec, a.geom.lanes_per_row, [&](auto tag) {
+    if (a.geom.wide_nv > 0)
+        return with_wide(a.esize, a.geom.wide_nv, [&](auto tag) {
+            using Tg = decltype(tag);
+            using T = typename Tg::type;
+            auto kern = a.geom.wide_full ? k_rowstats_wide<T, Tg::n, true> : k_rowstats_wide<T, Tg::n, false>;
+            hipLaunchKernelGGL(kern, grid, block, 0, stream, static_cast<const T *>(a.logits), a.V, a.blank,
+                               WS(const SampleDesc *, desc), WS(const ChunkDesc *, chunks), a.targets, a.S,
+                               WS(RowRec *, rec), WS(float2 *, lp), WS(float2 *, prob), WS(int *, mode),
+                               WS(uint32_t *, status));
+            return hipGetLastError();
+        });
+    return with_narrow(a.esize, a.geom.vec, a.geom.lanes_per_row, [&](auto tag) {
         using Tg = decltype(tag);
         using T = typename Tg::type;
-        hipLaunchKernelGGL((k_rowstats<T, Tg::vec, Tg::g>), grid, block, 0, stream, static_cast<const T *>(a.logits),
-                           a.V, a.blank, WS(const SampleDesc *, desc), WS(const ChunkDesc *, chunks), a.targets, a.S,
-                           WS(float *, den), WS(float *, lpb), WS(float *, lpy), WS(uint32_t *, status));
+        hipLaunchKernelGGL((k_rowstats_narrow<T, Tg::vec, Tg::n>), grid, block, 0, stream,
+                           static_cast<const T *>(a.logits), a.V, a.blank, WS(const SampleDesc *, desc),
+                           WS(const ChunkDesc *, chunks), a.targets, a.S, WS(RowRec *, rec), WS(float2 *, lp),
+                           WS(float2 *, prob), WS(int *, mode), WS(uint32_t *, status));
         return hipGetLastError();
     });
 }
 
 hipError_t launch_alpha_beta(const LaunchArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(k_alpha_beta, dim3(a.B), dim3(128), 0, stream, WS(const SampleDesc *, desc),
-                       WS(const int32_t *, order), WS(const float *, lpb), WS(const float *, lpy),
-                       WS(double *, alpha), WS(double *, beta), a.loss, WS(uint32_t *, status));
+                       WS(const int32_t *, order), WS(const int *, mode), WS(const float2 *, lp),
+                       WS(const float2 *, prob), WS(double *, alpha), WS(double *, beta), WS(int *, ealpha),
+                       WS(int *, ebeta), WS(double *, log2z), a.loss, WS(uint32_t *, status));
     return hipGetLastError();
 }
 
 hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
     const dim3 grid(a.lay.n_chunks), block(256);
-    const float log2_scale = log2f(a.grad_scale);
-    return with_geom(a.esize, a.geom.vec, a.geom.lanes_per_row, [&](auto tag) {
+    GradArgs g;
+    g.V = a.V;
+    g.blank = a.blank;
+    g.n_chunks = a.lay.n_chunks;
+    g.clamp = a.clamp;
+    g.scale = a.grad_scale;
+    g.log2_scale = log2f(a.grad_scale);
+    g.desc = WS(const SampleDesc *, desc);
+    g.chunks = WS(const ChunkDesc *, chunks);
+    g.mode = WS(const int *, mode);
+    g.log2z = WS(const double *, log2z);
+    g.rec = WS(const RowRec *, rec);
+    g.lp = WS(const float2 *, lp);
+    g.alpha = WS(const double *, alpha);
+    g.beta = WS(const double *, beta);
+    g.ealpha = WS(const int *, ealpha);
+    g.ebeta = WS(const int *, ebeta);
+    if (a.geom.wide_nv > 0)
+        return with_wide(a.esize, a.geom.wide_nv, [&](auto tag) {
+            using Tg = decltype(tag);
+            using T = typename Tg::type;
+            const T *in = static_cast<const T *>(a.logits);
+            T *out = static_cast<T *>(a.grad);
+            const bool cl = a.clamp > 0.f;
+            const bool fu = a.geom.wide_full;
+            void (*kern)(const T *, T *, int, int, int, float, float, float, const SampleDesc *, const ChunkDesc *,
+                         const int *, const double *, const RowRec *, const float2 *, const double *,
+                         const double *, const int *, const int *);
+            if (a.fused) {
+                if (cl) kern = fu ? k_grad_wide<T, Tg::n, true, true, true> : k_grad_wide<T, Tg::n, false, true, true>;
+                else kern = fu ? k_grad_wide<T, Tg::n, true, true, false> : k_grad_wide<T, Tg::n, false, true, false>;
+            } else {
+                if (cl) kern = fu ? k_grad_wide<T, Tg::n, true, false, true> : k_grad_wide<T, Tg::n, false, false, true>;
+                else kern = fu ? k_grad_wide<T, Tg::n, true, false, false> : k_grad_wide<T, Tg::n, false, false, false>;
+            }
+            hipLaunchKernelGGL(kern, grid, block, 0, stream, in, out, RNNT_GRAD_ARGS(g));
+            return hipGetLastError();
+        });
+    return with_narrow(a.esize, a.geom.vec, a.geom.lanes_per_row, [&](auto tag) {
         using Tg = decltype(tag);
         using T = typename Tg::type;
         if (a.fused)
-            hipLaunchKernelGGL((k_grad<T, Tg::vec, Tg::g, true>), grid, block, 0, stream,
-                               static_cast<const T *>(a.logits), static_cast<T *>(a.grad), a.V, a.blank, a.clamp,
-                               a.grad_scale, log2_scale, WS(const SampleDesc *, desc), WS(const ChunkDesc *, chunks),
-                               a.lay.n_chunks, a.targets, a.S, WS(const float *, den), WS(const float *, lpb),
-                               WS(const float *, lpy), WS(const double *, alpha), WS(const double *, beta));
+            hipLaunchKernelGGL((k_grad_narrow<T, Tg::vec, Tg::n, true>), grid, block, 0, stream,
+                               static_cast<const T *>(a.logits), static_cast<T *>(a.grad), RNNT_GRAD_ARGS(g));
         else
-            hipLaunchKernelGGL((k_grad<T, Tg::vec, Tg::g, false>), grid, block, 0, stream,
-                               static_cast<const T *>(a.logits), static_cast<T *>(a.grad), a.V, a.blank, a.clamp,
-                               a.grad_scale, log2_scale, WS(const SampleDesc *, desc), WS(const ChunkDesc *, chunks),
-                               a.lay.n_chunks, a.targets, a.S, WS(const float *, den), WS(const float *, lpb),
-                               WS(const float *, lpy), WS(const double *, alpha), WS(const double *, beta));
+            hipLaunchKernelGGL((k_grad_narrow<T, Tg::vec, Tg::n, false>), grid, block, 0, stream,
+                               static_cast<const T *>(a.logits), static_cast<T *>(a.grad), RNNT_GRAD_ARGS(g));
         return hipGetLastError();
     });
 }
@@ -599,10 +1070,10 @@ hipError_t launch_grad_scale(void *grad, int esize, int V, const float *scale, i
     const dim3 grid(lay.n_chunks), block(256);
     const SampleDesc *desc = reinterpret_cast<const SampleDesc *>(ws + lay.desc);
     const ChunkDesc *chunks = reinterpret_cast<const ChunkDesc *>(ws + lay.chunks);
-    return with_geom(esize, geom.vec, geom.lanes_per_row, [&](auto tag) {
+    return with_narrow(esize, geom.vec, geom.lanes_per_row, [&](auto tag) {
         using Tg = decltype(tag);
         using T = typename Tg::type;
-        hipLaunchKernelGGL((k_grad_scale<T, Tg::vec, Tg::g>), grid, block, 0, stream, static_cast<T *>(grad), V,
+        hipLaunchKernelGGL((k_grad_scale<T, Tg::vec, Tg::n>), grid, block, 0, stream, static_cast<T *>(grad), V,
                            desc, chunks, scale, per_sample);
         return hipGetLastError();
     });

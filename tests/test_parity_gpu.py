@@ -329,3 +329,48 @@ def test_readme_example_golden(rl):
         out = (loss if case["reduction"] == "none" else red).double().cpu().numpy()
         np.testing.assert_allclose(out, case["loss"], rtol=1e-5, atol=0)
         np.testing.assert_allclose(grad.double().cpu().numpy(), np.array(case["grad"]), rtol=0, atol=1e-5)
+
+
+# ------------------------------------------------ log-domain recursion fallback
+def test_extreme_log_probs_take_the_log_domain_path(rl):
+    """Non-fused inputs with log-probs far outside [-80, 80]: the log-domain sweep must match the oracle.
+
+    Values are multiples of 1/4, exact in fp32 and fp16, so no input rounding enters.
+    """
+    rng = np.random.default_rng(41)
+    Ts, Us, V = [20, 9, 14], [6, 3, 0], 24
+    w = _custom(Ts, Us, V, std=1.0, blank=0, fused=False, reduction="sum", seed=41)
+    x = np.round(rng.uniform(-300.0, -0.25, size=(w.N, V)) * 4) / 4
+    x[::7, 0] = -0.5          # some likely blanks keep the total probability away from underflow
+    w.logits = torch.tensor(x, dtype=torch.float32, device="cuda")
+    loss, red, grad, flags = run(rl, w)
+    assert flags == 0
+    check_against_oracle(w, loss, grad, "sum")
+
+
+def test_extreme_fused_logits(rl):
+    """Fused logits of spread ~N(0, 40^2): log-probs reach -300, the sample takes the log-domain sweep.
+
+    Tolerance derived from fp32 input rounding: |logit| ~ 160 has ulp 1.5e-5, so each
+    log-prob carries up to ~2e-5 absolute error; the loss stays within 1e-5 relative
+    (it is ~1e3-1e4) and the gradient within 2e-4 absolute.
+    """
+    w = _custom([25, 11], [5, 4], 64, std=40.0, blank=-1, reduction="sum", seed=42)
+    loss, red, grad, flags = run(rl, w)
+    assert flags == 0
+    ref = oracle.batch(w.logits.cpu().numpy(), w.targets, w.logit_lengths, w.target_lengths, blank=-1,
+                       reduction="sum")
+    np.testing.assert_allclose(loss.double().cpu().numpy(), ref[0], rtol=1e-5, atol=0)
+    assert np.abs(grad.double().cpu().numpy() - ref[2]).max() <= 2e-4
+
+
+def test_mixed_domains_in_one_batch(rl):
+    """One sample with ordinary log-probs, one with extreme ones: each takes its own sweep."""
+    rng = np.random.default_rng(43)
+    w = _custom([30, 30], [8, 8], 16, std=1.0, blank=-1, fused=False, prenormalise=True, reduction="none", seed=43)
+    x = w.logits.cpu().numpy().astype(np.float64)
+    sl = w.rows(1)
+    x[sl] = np.round(rng.uniform(-200.0, -1.0, size=x[sl].shape) * 4) / 4
+    w.logits = torch.tensor(x, dtype=torch.float32, device="cuda")
+    loss, red, grad, flags = run(rl, w)
+    check_against_oracle(w, loss, grad, "none")
