@@ -75,20 +75,22 @@ rnnt_status build_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t
     rnnt_status st = check_lengths(B, V, T, U);
     if (st != RNNT_SUCCESS) return st;
     p.desc.resize(B);
-    int64_t row = 0, slot = 0, diag = 0;
+    int64_t row = 0, slot = 0, diag = 0, ab = 0;
     p.max_U1 = 1;
     for (int32_t i = 0; i < B; ++i) {
         SampleDesc &d = p.desc[i];
         d.row_off = row;
         d.slot_off = slot;
         d.diag_off = diag;
+        d.ab_off = ab;
         d.T = T[i];
         d.U = U[i];
         d.index = i;
-        d.pad = 0;
+        d.U1p = 64 * cols_per_lane(U[i] + 1);
         row += (int64_t)T[i] * (U[i] + 1);
         slot += ((int64_t)T[i] + U[i]) * (U[i] + 1);
         diag += (int64_t)T[i] + U[i];
+        ab += ((int64_t)T[i] + U[i]) * d.U1p;
         p.max_U1 = std::max(p.max_U1, U[i] + 1);
     }
     if (N >= 0 && row != N) return RNNT_INVALID_VALUE;
@@ -120,14 +122,15 @@ rnnt_status build_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t
     L.chunks = off; off = align_up(off + sizeof(ChunkDesc) * p.chunks.size());
     L.rec = off;    off = align_up(off + sizeof(RowRec) * (size_t)row);
     L.lp = off;     off = align_up(off + 2 * sizeof(float) * (size_t)slot);
-    L.prob = off;   off = align_up(off + 2 * sizeof(float) * (size_t)slot);
-    L.alpha = off;  off = align_up(off + sizeof(double) * (size_t)slot);
-    L.beta = off;   off = align_up(off + sizeof(double) * (size_t)slot);
-    L.ealpha = off; off = align_up(off + sizeof(int32_t) * (size_t)diag);
-    L.ebeta = off;  off = align_up(off + sizeof(int32_t) * (size_t)diag);
+    L.prob = off;   off = align_up(off + 2 * sizeof(double) * (size_t)slot);
+    L.alpha = off;  off = align_up(off + sizeof(double) * (size_t)ab);
+    L.beta = off;   off = align_up(off + sizeof(double) * (size_t)ab);
+    L.ealpha = off; off = align_up(off + sizeof(int32_t) * (size_t)(diag + B));
+    L.ebeta = off;  off = align_up(off + sizeof(int32_t) * (size_t)(diag + B));
     L.log2z = off;  off = align_up(off + sizeof(double) * (size_t)B);
     L.total = off;
     L.n_slots = slot;
+    L.n_ab_slots = ab;
     L.n_diags = diag;
     L.n_chunks = (int32_t)p.chunks.size();
     L.rows_per_chunk = rpc;

@@ -14,17 +14,29 @@ namespace rnnt {
 // row_off + t*(U+1) + u is lattice node (t,u).  The per-node scalars of the
 // recursions live in a skewed layout, one slot per (anti-diagonal n = t+u, u):
 // slot_off + n*(U+1) + u, n in [0, T+U), so every anti-diagonal is contiguous.
-// Per-diagonal values (the recursions' power-of-two exponents) are at
-// diag_off + n.
+// The recursions' outputs (alpha, beta) use the same skewed order with the
+// diagonal padded to a whole number of wavefront column groups:
+// ab_off + n*U1p + u, U1p = 64 * (lattice columns per lane), so every lane of
+// the sweep owns a slot.  Per-diagonal values (the recursions'
+// power-of-two exponents) are at diag_off + n / 8.
 struct SampleDesc {
     int64_t row_off;
     int64_t slot_off;
     int64_t diag_off;
+    int64_t ab_off;
     int32_t T;
     int32_t U;
     int32_t index;  // position of the sample in the batch (targets row)
-    int32_t pad;
+    int32_t U1p;
 };
+
+// Lattice columns each lane of a 64-wide wavefront owns for a lattice of
+// width U1: the smallest power of two C with 64*C >= U1.
+inline int cols_per_lane(int U1) {
+    int c = 1;
+    while (64 * c < U1) c <<= 1;
+    return c;
+}
 
 // A run of rows of one sample processed by one workgroup of the row passes.
 struct ChunkDesc {
@@ -35,12 +47,10 @@ struct ChunkDesc {
 };
 
 // Per packed row, written by the row-statistics pass for the gradient pass:
-// the row's log-sum-exp (0 for log-prob inputs), its blank and label input
-// values, and its label (-1 at u = U or when out of range).
+// the row's log-sum-exp (0 for log-prob inputs) and its label (-1 at u = U or
+// when out of range).
 struct RowRec {
     float den;
-    float xb;
-    float xy;
     int32_t y;
 };
 
@@ -54,14 +64,15 @@ struct WorkspaceLayout {
     size_t chunks;      // ChunkDesc[n_chunks]
     size_t rec;         // RowRec[N]
     size_t lp;          // float2[S]: {log P(blank), log P(next label)} per slot
-    size_t prob;        // float2[S]: the same as probabilities
-    size_t alpha;       // double[S]
-    size_t beta;        // double[S]
-    size_t ealpha;      // int32[D]: per-diagonal exponent of alpha
-    size_t ebeta;       // int32[D]
+    size_t prob;        // double2[S]: the same as probabilities
+    size_t alpha;       // double[S_ab], padded diagonals
+    size_t beta;        // double[S_ab]
+    size_t ealpha;      // int32[D + B]: exponent of alpha per group of 8 diagonals
+    size_t ebeta;       // int32[D + B]
     size_t log2z;       // double[B]: log2 P(y|x) (beta path)
     size_t total;
     int64_t n_slots;
+    int64_t n_ab_slots;
     int64_t n_diags;
     int32_t n_chunks;
     int32_t rows_per_chunk;

@@ -206,23 +206,23 @@ __device__ __forceinline__ double read_lane_d(double x, int lane) {
 
 // ---------------------------------------------------- row statistics output
 // Writes what the recursions and the gradient need about node (t,u):
-//   rec  (row order)  {log-sum-exp of the row (fused) or 0, the blank input
-//                      value, the label input value, the label (-1 if none)},
+//   rec  (row order)  {log-sum-exp of the row (fused) or 0, the label (-1 if
+//                      none)},
 //   lp   (skewed)     {log P(blank), log P(y_{u+1})},
-//   prob (skewed)     the same as fp32 probabilities.
+//   prob (skewed)     the same as probabilities (fp32-accurate, stored as fp64).
 // The blank edge leaving t = T-1 below u = U leaves the lattice and the label
 // edge at u = U does not exist, so both are stored as impossible.
-__device__ __forceinline__ void emit_node(const SampleDesc &d, int t, int u, int64_t row, float dn, float xb,
-                                          float xy, int y, float lpb, float lpy, RowRec *__restrict__ rec,
-                                          float2 *__restrict__ lp, float2 *__restrict__ prob,
+__device__ __forceinline__ void emit_node(const SampleDesc &d, int t, int u, int64_t row, float dn, int y,
+                                          float lpb, float lpy, RowRec *__restrict__ rec,
+                                          float2 *__restrict__ lp, double2 *__restrict__ prob,
                                           int *__restrict__ mode) {
     if (t == d.T - 1 && u < d.U) lpb = kNegInf;
     if (u == d.U) lpy = kNegInf;
-    rec[row] = RowRec{dn, xb, xy, y};
+    rec[row] = RowRec{dn, y};
     const int U1 = d.U + 1;
     const int64_t slot = d.slot_off + (int64_t)(t + u) * U1 + u;
     lp[slot] = make_float2(lpb, lpy);
-    prob[slot] = make_float2(prob_of(lpb), prob_of(lpy));
+    prob[slot] = make_double2((double)prob_of(lpb), (double)prob_of(lpy));
     const bool wide = (lpb != kNegInf && fabsf(lpb) > kProbRange) || (lpy != kNegInf && fabsf(lpy) > kProbRange);
     if (wide) atomicOr(&mode[d.index], 1);
 }
@@ -232,10 +232,10 @@ __device__ __forceinline__ void emit_node(const SampleDesc &d, int t, int u, int
 // column u of the first and the row (T-1,u) column u of the second, so the
 // recursions can read every slot of a diagonal without masks.
 __device__ __forceinline__ void fill_outside(const SampleDesc &d, int t, int u, int lane, int nl,
-                                             float2 *__restrict__ lp, float2 *__restrict__ prob) {
+                                             float2 *__restrict__ lp, double2 *__restrict__ prob) {
     const int U1 = d.U + 1;
     const float2 nlp = make_float2(kNegInf, kNegInf);
-    const float2 np = make_float2(0.f, 0.f);
+    const double2 np = make_double2(0.0, 0.0);
     if (t == 0)
         for (int n = lane; n < u; n += nl) {
             const int64_t s = d.slot_off + (int64_t)n * U1 + u;
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256) void k_rowstats_wide(const T *__restrict__ log
                                                        const ChunkDesc *__restrict__ chunks,
                                                        const int32_t *__restrict__ targets, int S,
                                                        RowRec *__restrict__ rec, float2 *__restrict__ lp,
-                                                       float2 *__restrict__ prob, int *__restrict__ mode,
+                                                       double2 *__restrict__ prob, int *__restrict__ mode,
                                                        uint32_t *status) {
     constexpr int VEC = Raw<T>::kVec;
     const ChunkDesc c = chunks[blockIdx.x];
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(256) void k_rowstats_wide(const T *__restrict__ log
             const bool dead = (dn == kNegInf);
             const float lpb = dead ? kNegInf : hb - dn;
             const float lpy = (dead || y < 0) ? kNegInf : hy - dn;
-            emit_node(d, t, u, row, dn, hb, hy, y, lpb, lpy, rec, lp, prob, mode);
+            emit_node(d, t, u, row, dn, y, lpb, lpy, rec, lp, prob, mode);
         }
         if (t == 0 || t == d.T - 1) fill_outside(d, t, u, lane, 64, lp, prob);
 #pragma unroll
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(256) void k_rowstats_narrow(const T *__restrict__ l
                                                          const ChunkDesc *__restrict__ chunks,
                                                          const int32_t *__restrict__ targets, int S,
                                                          RowRec *__restrict__ rec, float2 *__restrict__ lp,
-                                                         float2 *__restrict__ prob, int *__restrict__ mode,
+                                                         double2 *__restrict__ prob, int *__restrict__ mode,
                                                          uint32_t *status) {
     constexpr int RPW = 64 / G;
     const ChunkDesc c = chunks[blockIdx.x];
@@ -393,7 +393,7 @@ __global__ __launch_bounds__(256) void k_rowstats_narrow(const T *__restrict__ l
             const float hy = (y >= 0) ? Elem<T>::load1(p + y) : 0.f;
             const float lpb = dead ? kNegInf : hb - dn;
             const float lpy = (dead || y < 0) ? kNegInf : hy - dn;
-            emit_node(d, t, u, row, dn, hb, hy, y, lpb, lpy, rec, lp, prob, mode);
+            emit_node(d, t, u, row, dn, y, lpb, lpy, rec, lp, prob, mode);
         }
         if (t == 0 || t == d.T - 1) fill_outside(d, t, u, sub, G, lp, prob);
     }
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(256) void k_gather(const T *__restrict__ logits, in
                                                 const ChunkDesc *__restrict__ chunks,
                                                 const int32_t *__restrict__ targets, int S,
                                                 RowRec *__restrict__ rec, float2 *__restrict__ lp,
-                                                float2 *__restrict__ prob, int *__restrict__ mode,
+                                                double2 *__restrict__ prob, int *__restrict__ mode,
                                                 uint32_t *status) {
     const ChunkDesc c = chunks[blockIdx.x];
     const SampleDesc d = desc[c.sample];
@@ -420,7 +420,7 @@ __global__ __launch_bounds__(256) void k_gather(const T *__restrict__ logits, in
         const int y = read_label(d, u, V, blank, targets, S, status);
         const float lpb = Elem<T>::load1(p + blank);
         const float lpy = (y < 0) ? kNegInf : Elem<T>::load1(p + y);
-        emit_node(d, t, u, row, 0.f, lpb, lpy, y, lpb, lpy, rec, lp, prob, mode);
+        emit_node(d, t, u, row, 0.f, y, lpb, lpy, rec, lp, prob, mode);
         if (t == 0 || t == d.T - 1) fill_outside(d, t, u, 0, 1, lp, prob);
     }
 }
@@ -430,28 +430,39 @@ __global__ __launch_bounds__(256) void k_gather(const T *__restrict__ logits, in
 // width read column U instead: their values start at zero (-inf in the log
 // domain) and only ever receive zero, because the label edge leaving column U
 // is stored as impossible.  The node inputs of PF diagonals are loaded one
-// block ahead; each block's outputs are stored after it, so a wait for a
-// block's loads never waits for the previous block's stores.
+// block ahead into one of two register rings used in turn; each block's
+// outputs are stored after its compute, so a wait for a block's inputs never
+// covers the previous block's stores.
 //
-// Probability domain: node value = mantissa * 2^E[n].  Forward step:
+// Probability domain: node value = mantissa * 2^E, one exponent E per group
+// of eight diagonals.  Forward step:
 //   a(n,u) = a(n-1,u) * pb(n-1,u) + a(n-1,u-1) * py(n-1,u-1)
-// kept as the two messages leaving diagonal n-1.  Backward step:
-//   b(n,u) = b(n+1,u) * pb(n,u) + b(n+1,u+1) * py(n,u).
-// Every fourth diagonal is rescaled by 2^-e so its largest value is in
-// [1, 2): |log-prob| <= 80 bounds the drift over four steps by 2^+-470.
+// carried as the two messages leaving diagonal n-1 (the recursion starts
+// from a blank message of one into (0,0)).  Backward step:
+//   b(n,u) = b(n+1,u) * pb(n,u) + b(n+1,u+1) * py(n,u)
+// from b = 1 at (T-1+1, U), the empty suffix after the final blank.  Every
+// eighth diagonal is rescaled by 2^-e so its largest value is in [1, 2):
+// with |log-prob| <= 80 a value moves by at most 2^+-116.4 per step, so
+// eight steps stay inside fp64's normal range.  The exponent that applies to
+// forward diagonal n is ealpha[(n + 1) / 8], to backward diagonal n
+// ebeta[(nd - n) / 8].
 //
 // Log domain (fallback): the same recursions in log2 units with
 // log2(2^a + 2^b) in place of the sum and log2-prob addition in place of the
-// product; E[n] = 0.
+// product; all exponents are 0.
 struct ProbDomain {
     static constexpr bool kLog = false;
+    using W = double2;
     __device__ static double zero() { return 0.0; }
     __device__ static double one() { return 1.0; }
     __device__ static double combine(double a, double b) { return a + b; }
-    __device__ static double edge(double a, float w) { return a * (double)w; }
+    __device__ static double edge(double a, double w) { return a * w; }
+    __device__ static double wx(const W &w) { return w.x; }
+    __device__ static double wy(const W &w) { return w.y; }
 };
 struct LogDomain {
     static constexpr bool kLog = true;
+    using W = float2;
     __device__ static double zero() { return kNegInfD; }
     __device__ static double one() { return 0.0; }
     __device__ static double combine(double a, double b) {
@@ -460,7 +471,9 @@ struct LogDomain {
         const float l = log2_fast(1.0f + exp2_fast((float)(mn - mx)));
         return (mn == kNegInfD) ? mx : mx + (double)l;
     }
-    __device__ static double edge(double a, float lpv) { return a + (double)lpv * kLog2eD; }
+    __device__ static double edge(double a, double lpv) { return a + lpv * kLog2eD; }
+    __device__ static double wx(const W &w) { return (double)w.x; }
+    __device__ static double wy(const W &w) { return (double)w.y; }
 };
 
 template <int C> __device__ __forceinline__ int renorm(double (&a)[C]) {
@@ -474,77 +487,116 @@ template <int C> __device__ __forceinline__ int renorm(double (&a)[C]) {
     return sh;
 }
 
-template <int C, int PF> struct Ring {
-    float2 v[PF][C];
+template <typename W, int C, int PF> struct Ring {
+    W v[PF][C];
 };
 
 // Diagonals n0, n0+step, ... (clamped into [0, nd)) of a sample's slots.
-template <int C, int PF>
-__device__ __forceinline__ void load_block(Ring<C, PF> &r, const float2 *__restrict__ w, int U, int n0, int step,
-                                           int nd) {
-    const int lane = threadIdx.x & 63;
-    const int U1 = U + 1;
+// voff[j]: the lane's byte offset inside a diagonal (column min(u, U)), so
+// each load is a scalar diagonal base plus a fixed 32-bit lane offset.
+template <typename W, int C, int PF>
+__device__ __forceinline__ void load_block(Ring<W, C, PF> &r, const W *__restrict__ w, int U1,
+                                           const uint32_t (&voff)[C], int n0, int step, int nd) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
         const int n = min(max(n0 + step * p, 0), nd - 1);
-        const float2 *row = w + (int64_t)n * U1;
+        const char *row = reinterpret_cast<const char *>(w + (int64_t)n * U1);
 #pragma unroll
-        for (int j = 0; j < C; ++j) r.v[p][j] = row[min(lane + 64 * j, U)];
+        for (int j = 0; j < C; ++j) r.v[p][j] = *reinterpret_cast<const W *>(row + voff[j]);
+    }
+}
+
+template <int C> __device__ __forceinline__ void lane_offsets(uint32_t (&voff)[C], int U, uint32_t esize) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < C; ++j) voff[j] = (uint32_t)min(lane + 64 * j, U) * esize;
+}
+
+// Value of lane l-1 (lane 0: `edge` of the previous column group, or zero).
+template <typename D, int C>
+__device__ __forceinline__ double from_left(const double (&x)[C], int j) {
+    if (j == 0) {
+        if constexpr (D::kLog) return shift_up(x[0], kNegInfD);
+        const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x[0]), 0x138, 0xf, 0xf, true);
+        const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x[0]), 0x138, 0xf, 0xf, true);
+        return __hiloint2double(hi, lo);
+    }
+    return shift_up(x[j], read_lane_d(x[j > 0 ? j - 1 : 0], 63));
+}
+// Value of lane l+1 (lane 63: lane 0 of the next column group, or zero).
+template <typename D, int C>
+__device__ __forceinline__ double from_right(const double (&x)[C], int j) {
+    if (j == C - 1) {
+        if constexpr (D::kLog) return shift_down(x[C - 1], kNegInfD);
+        const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x[C - 1]), 0x130, 0xf, 0xf, true);
+        const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x[C - 1]), 0x130, 0xf, 0xf, true);
+        return __hiloint2double(hi, lo);
+    }
+    return shift_down(x[j], read_lane_d(x[j + 1 < C ? j + 1 : j], 0));
+}
+
+// One block of PF forward diagonals n0 .. n0+PF-1 from ring r.  GUARD: the
+// block may run past the last diagonal.  Each diagonal is stored as soon as
+// it is computed: the other ring's loads were issued before these stores,
+// so waiting for them never waits for the stores.
+template <typename D, int C, int PF, bool GUARD>
+__device__ __forceinline__ void forward_block(const Ring<typename D::W, C, PF> &r, int n0, int nd, int lane,
+                                              double (&mb)[C], double (&my)[C], int &E, double *__restrict__ out,
+                                              int *__restrict__ eout) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+        const int n = n0 + p;
+        if (!GUARD || n < nd) {
+            double a[C];
+#pragma unroll
+            for (int j = 0; j < C; ++j) a[j] = D::combine(mb[j], from_left<D, C>(my, j));
+            // n0 is a multiple of PF, so for PF % 8 == 0 this test is static
+            if (!D::kLog && (((PF % 8 == 0) ? p : n) & 7) == 7) {
+                E += renorm<C>(a);
+                eout[(n + 1) >> 3] = E;  // uniform value and address
+            }
+            // padded diagonal: every lane owns a slot (uniform base + lane)
+            double *o = out + (int64_t)n * (64 * C);
+#pragma unroll
+            for (int j = 0; j < C; ++j) {
+                o[lane + 64 * j] = a[j];
+                mb[j] = D::edge(a[j], D::wx(r.v[p][j]));
+                my[j] = D::edge(a[j], D::wy(r.v[p][j]));
+            }
+        }
     }
 }
 
 template <typename D, int C, int PF>
-__device__ void sweep_forward(const SampleDesc &d, const float2 *__restrict__ w, double *__restrict__ out,
+__device__ void sweep_forward(const SampleDesc &d, const typename D::W *__restrict__ w, double *__restrict__ out,
                               int *__restrict__ eout, double *log2z) {
+    using W = typename D::W;
     const int lane = threadIdx.x & 63;
     const int U = d.U, U1 = U + 1, nd = d.T + U;
+    // messages into diagonal 0: a blank message of one into (0,0)
     double mb[C], my[C];
 #pragma unroll
-    for (int j = 0; j < C; ++j) { mb[j] = D::zero(); my[j] = D::zero(); }
+    for (int j = 0; j < C; ++j) {
+        mb[j] = (j == 0 && lane == 0) ? D::one() : D::zero();
+        my[j] = D::zero();
+    }
     int E = 0;
-    Ring<C, PF> cur, nxt;
-    load_block<C, PF>(cur, w, U, 0, 1, nd);
-    for (int n0 = 0; n0 < nd; n0 += PF) {
-        if (n0 + PF < nd) load_block<C, PF>(nxt, w, U, n0 + PF, 1, nd);
-        double ob[PF][C];
-#pragma unroll
-        for (int p = 0; p < PF; ++p) {
-            const int n = n0 + p;
-            if (n < nd) {
-                double a[C];
-                if (n == 0) {
-#pragma unroll
-                    for (int j = 0; j < C; ++j) a[j] = (j == 0 && lane == 0) ? D::one() : D::zero();
-                } else {
-#pragma unroll
-                    for (int j = 0; j < C; ++j) {
-                        const double edge = (j == 0) ? D::zero() : read_lane_d(my[j > 0 ? j - 1 : 0], 63);
-                        a[j] = D::combine(mb[j], shift_up(my[j], edge));
-                    }
-                }
-                if (!D::kLog && (n & 3) == 3) E += renorm<C>(a);
-#pragma unroll
-                for (int j = 0; j < C; ++j) {
-                    ob[p][j] = a[j];
-                    mb[j] = D::edge(a[j], cur.v[p][j].x);
-                    my[j] = D::edge(a[j], cur.v[p][j].y);
-                }
-                if (lane == 0) eout[n] = E;
-            }
-        }
-#pragma unroll
-        for (int p = 0; p < PF; ++p) {
-            const int n = n0 + p;
-            if (n < nd) {
-#pragma unroll
-                for (int j = 0; j < C; ++j)
-                    if (lane + 64 * j < U1) out[(int64_t)n * U1 + lane + 64 * j] = ob[p][j];
-            }
-        }
-#pragma unroll
-        for (int p = 0; p < PF; ++p)
-#pragma unroll
-            for (int j = 0; j < C; ++j) cur.v[p][j] = nxt.v[p][j];
+    if (lane == 0) eout[0] = 0;
+    uint32_t voff[C];
+    lane_offsets<C>(voff, U, sizeof(W));
+    Ring<W, C, PF> ra, rb;
+    load_block<W, C, PF>(ra, w, U1, voff, 0, 1, nd);
+    int n0 = 0;
+    for (; n0 + 2 * PF <= nd; n0 += 2 * PF) {
+        load_block<W, C, PF>(rb, w, U1, voff, n0 + PF, 1, nd);
+        forward_block<D, C, PF, false>(ra, n0, nd, lane, mb, my, E, out, eout);
+        load_block<W, C, PF>(ra, w, U1, voff, n0 + 2 * PF, 1, nd);
+        forward_block<D, C, PF, false>(rb, n0 + PF, nd, lane, mb, my, E, out, eout);
+    }
+    if (n0 < nd) {
+        load_block<W, C, PF>(rb, w, U1, voff, n0 + PF, 1, nd);
+        forward_block<D, C, PF, true>(ra, n0, nd, lane, mb, my, E, out, eout);
+        if (n0 + PF < nd) forward_block<D, C, PF, true>(rb, n0 + PF, nd, lane, mb, my, E, out, eout);
     }
     // The last diagonal holds only (T-1, U); its blank message is P(y|x).
     double v = mb[0];
@@ -554,90 +606,103 @@ __device__ void sweep_forward(const SampleDesc &d, const float2 *__restrict__ w,
     if (lane == 0) *log2z = D::kLog ? z : log2_d(z) + (double)E;
 }
 
+// One block of PF backward diagonals n0, n0-1, ..., n0-PF+1 from ring r
+// (nd-1-n0 is a multiple of PF).
+template <typename D, int C, int PF, bool GUARD>
+__device__ __forceinline__ void backward_block(const Ring<typename D::W, C, PF> &r, int n0, int nd, int lane,
+                                               double (&pv)[C], int &E, double *__restrict__ out,
+                                               int *__restrict__ eout) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+        const int n = n0 - p;
+        if (!GUARD || n >= 0) {
+            double b[C];
+#pragma unroll
+            for (int j = 0; j < C; ++j)
+                b[j] = D::combine(D::edge(pv[j], D::wx(r.v[p][j])),
+                                  D::edge(from_right<D, C>(pv, j), D::wy(r.v[p][j])));
+            if (!D::kLog && (((PF % 8 == 0) ? p : (nd - 1 - n)) & 7) == 7) {
+                E += renorm<C>(b);
+                eout[(nd - n) >> 3] = E;  // uniform value and address
+            }
+            double *o = out + (int64_t)n * (64 * C);
+#pragma unroll
+            for (int j = 0; j < C; ++j) {
+                o[lane + 64 * j] = b[j];
+                pv[j] = b[j];
+            }
+        }
+    }
+}
+
 template <typename D, int C, int PF>
-__device__ void sweep_backward(const SampleDesc &d, const float2 *__restrict__ w, double *__restrict__ out,
+__device__ void sweep_backward(const SampleDesc &d, const typename D::W *__restrict__ w, double *__restrict__ out,
                                int *__restrict__ eout, double *log2z) {
+    using W = typename D::W;
     const int lane = threadIdx.x & 63;
     const int U = d.U, U1 = U + 1, nd = d.T + U;
-    // values of the virtual diagonal nd: the empty suffix after the final
-    // blank has probability one at u = U
     double pv[C];
 #pragma unroll
     for (int j = 0; j < C; ++j) pv[j] = (lane + 64 * j == U) ? D::one() : D::zero();
     int E = 0;
-    Ring<C, PF> cur, nxt;
-    load_block<C, PF>(cur, w, U, nd - 1, -1, nd);
-    for (int n0 = nd - 1; n0 >= 0; n0 -= PF) {
-        if (n0 - PF >= 0) load_block<C, PF>(nxt, w, U, n0 - PF, -1, nd);
-        double ob[PF][C];
-#pragma unroll
-        for (int p = 0; p < PF; ++p) {
-            const int n = n0 - p;
-            if (n >= 0) {
-                double b[C];
-#pragma unroll
-                for (int j = 0; j < C; ++j) {
-                    const double edge = (j + 1 < C) ? read_lane_d(pv[j + 1 < C ? j + 1 : j], 0) : D::zero();
-                    const double nx = shift_down(pv[j], edge);
-                    b[j] = D::combine(D::edge(pv[j], cur.v[p][j].x), D::edge(nx, cur.v[p][j].y));
-                }
-                if (!D::kLog && ((nd - 1 - n) & 3) == 3) E += renorm<C>(b);
-#pragma unroll
-                for (int j = 0; j < C; ++j) {
-                    ob[p][j] = b[j];
-                    pv[j] = b[j];
-                }
-                if (lane == 0) eout[n] = E;
-            }
-        }
-#pragma unroll
-        for (int p = 0; p < PF; ++p) {
-            const int n = n0 - p;
-            if (n >= 0) {
-#pragma unroll
-                for (int j = 0; j < C; ++j)
-                    if (lane + 64 * j < U1) out[(int64_t)n * U1 + lane + 64 * j] = ob[p][j];
-            }
-        }
-#pragma unroll
-        for (int p = 0; p < PF; ++p)
-#pragma unroll
-            for (int j = 0; j < C; ++j) cur.v[p][j] = nxt.v[p][j];
+    if (lane == 0) eout[0] = 0;
+    uint32_t voff[C];
+    lane_offsets<C>(voff, U, sizeof(W));
+    Ring<W, C, PF> ra, rb;
+    load_block<W, C, PF>(ra, w, U1, voff, nd - 1, -1, nd);
+    int n0 = nd - 1;
+    for (; n0 - 2 * PF + 1 >= 0; n0 -= 2 * PF) {
+        load_block<W, C, PF>(rb, w, U1, voff, n0 - PF, -1, nd);
+        backward_block<D, C, PF, false>(ra, n0, nd, lane, pv, E, out, eout);
+        load_block<W, C, PF>(ra, w, U1, voff, n0 - 2 * PF, -1, nd);
+        backward_block<D, C, PF, false>(rb, n0 - PF, nd, lane, pv, E, out, eout);
+    }
+    if (n0 >= 0) {
+        load_block<W, C, PF>(rb, w, U1, voff, n0 - PF, -1, nd);
+        backward_block<D, C, PF, true>(ra, n0, nd, lane, pv, E, out, eout);
+        if (n0 - PF >= 0) backward_block<D, C, PF, true>(rb, n0 - PF, nd, lane, pv, E, out, eout);
     }
     if (lane == 0) *log2z = D::kLog ? pv[0] : log2_d(pv[0]) + (double)E;
 }
 
 template <int C, int PF>
-__device__ void run_sweeps(const SampleDesc &d, bool log_mode, const float2 *lp, const float2 *prob, double *alpha,
+__device__ void run_sweeps(const SampleDesc &d, bool log_mode, const float2 *lp, const double2 *prob, double *alpha,
                            double *beta, int *ea, int *eb, double *shz) {
     const int wave = threadIdx.x >> 6;
     const int64_t so = d.slot_off;
+    const int64_t ao = d.ab_off;
     const int64_t dof = d.diag_off;
     if (log_mode) {
-        if (wave == 0) sweep_forward<LogDomain, C, PF>(d, lp + so, alpha + so, ea + dof, &shz[0]);
-        else sweep_backward<LogDomain, C, PF>(d, lp + so, beta + so, eb + dof, &shz[1]);
+        if (wave == 0) sweep_forward<LogDomain, C, PF>(d, lp + so, alpha + ao, ea + dof, &shz[0]);
+        else sweep_backward<LogDomain, C, PF>(d, lp + so, beta + ao, eb + dof, &shz[1]);
     } else {
-        if (wave == 0) sweep_forward<ProbDomain, C, PF>(d, prob + so, alpha + so, ea + dof, &shz[0]);
-        else sweep_backward<ProbDomain, C, PF>(d, prob + so, beta + so, eb + dof, &shz[1]);
+        if (wave == 0) sweep_forward<ProbDomain, C, PF>(d, prob + so, alpha + ao, ea + dof, &shz[0]);
+        else sweep_backward<ProbDomain, C, PF>(d, prob + so, beta + ao, eb + dof, &shz[1]);
     }
 }
 
 __global__ __launch_bounds__(128) void k_alpha_beta(const SampleDesc *__restrict__ desc,
                                                     const int32_t *__restrict__ order,
                                                     const int *__restrict__ mode, const float2 *__restrict__ lp,
-                                                    const float2 *__restrict__ prob, double *__restrict__ alpha,
+                                                    const double2 *__restrict__ prob, double *__restrict__ alpha,
                                                     double *__restrict__ beta, int *__restrict__ ealpha,
                                                     int *__restrict__ ebeta, double *__restrict__ log2z,
                                                     float *__restrict__ loss, uint32_t *status) {
     __shared__ double shz[2];
     const SampleDesc d = desc[order[blockIdx.x]];
     const bool lm = mode[d.index] != 0;
-    const int U1 = d.U + 1;
-    if (U1 <= 64) run_sweeps<1, 32>(d, lm, lp, prob, alpha, beta, ealpha, ebeta, shz);
-    else if (U1 <= 128) run_sweeps<2, 16>(d, lm, lp, prob, alpha, beta, ealpha, ebeta, shz);
-    else if (U1 <= 256) run_sweeps<4, 8>(d, lm, lp, prob, alpha, beta, ealpha, ebeta, shz);
-    else if (U1 <= 512) run_sweeps<8, 2>(d, lm, lp, prob, alpha, beta, ealpha, ebeta, shz);
-    else run_sweeps<16, 1>(d, lm, lp, prob, alpha, beta, ealpha, ebeta, shz);
+    // PF: diagonals per prefetch block.  When a ring is first read, the loads
+    // of that ring (C*PF), the stores of the previous block (C*PF + PF/8) and
+    // the other ring's loads (C*PF) may be outstanding: 3*C*PF must stay
+    // within the 63 vector memory operations the wait counter tracks; two
+    // fp64 rings hold 8*C*PF registers.
+    switch (d.U1p) {
+    case 64: run_sweeps<1, 16>(d, lm, lp, prob, alpha, beta, ealpha, ebeta, shz); break;
+    case 128: run_sweeps<2, 8>(d, lm, lp, prob, alpha, beta, ealpha, ebeta, shz); break;
+    case 256: run_sweeps<4, 4>(d, lm, lp, prob, alpha, beta, ealpha, ebeta, shz); break;
+    case 512: run_sweeps<8, 2>(d, lm, lp, prob, alpha, beta, ealpha, ebeta, shz); break;
+    default: run_sweeps<16, 1>(d, lm, lp, prob, alpha, beta, ealpha, ebeta, shz); break;
+    }
     __syncthreads();
     if (threadIdx.x == 0) {
         const double la = -shz[0] * kLn2D;
@@ -666,9 +731,11 @@ struct SampleTerms {
     bool log_mode;
 };
 
+// log2 of a forward (ge = ealpha group index (n+1)/8) or backward (ge =
+// (nd-n)/8) node value.
 __device__ __forceinline__ double node_log2(const double *__restrict__ v, const int *__restrict__ e, int64_t s,
-                                            int n, bool log_mode) {
-    return log_mode ? v[s] : log2_d(v[s]) + (double)e[n];
+                                            int ge, bool log_mode) {
+    return log_mode ? v[s] : log2_d(v[s]) + (double)e[ge];
 }
 
 __device__ __forceinline__ RowTerms row_terms(const SampleDesc &d, const SampleTerms &st, int lr, const RowRec &rr,
@@ -680,17 +747,21 @@ __device__ __forceinline__ RowTerms row_terms(const SampleDesc &d, const SampleT
     const int t = lr / U1;
     const int u = lr - t * U1;
     const int n = t + u;
-    const int64_t s = d.slot_off + (int64_t)n * U1 + u;
+    const int64_t s = d.slot_off + (int64_t)n * U1 + u;      // lp slot
+    const int64_t q = d.ab_off + (int64_t)n * d.U1p + u;     // alpha / beta slot
+    const int U1p = d.U1p;
     const int *ea = ealpha + d.diag_off;
     const int *eb = ebeta + d.diag_off;
+    const int nd = d.T + d.U;
     double lb = kNegInfD, ly = kNegInfD, lo = kNegInfD;
     if (st.log2z != kNegInfD) {
-        const double a2 = node_log2(alpha, ea, s, n, st.log_mode) - st.log2z;
+        const double a2 = node_log2(alpha, ea, q, (n + 1) >> 3, st.log_mode) - st.log2z;
         const float2 l = lp[s];
-        lo = a2 + node_log2(beta, eb, s, n, st.log_mode);
-        if (t < d.T - 1) lb = a2 + (double)l.x * kLog2eD + node_log2(beta, eb, s + U1, n + 1, st.log_mode);
+        lo = a2 + node_log2(beta, eb, q, (nd - n) >> 3, st.log_mode);
+        const int gnext = (nd - n - 1) >> 3;
+        if (t < d.T - 1) lb = a2 + (double)l.x * kLog2eD + node_log2(beta, eb, q + U1p, gnext, st.log_mode);
         else if (u == d.U) lb = a2 + (double)l.x * kLog2eD;
-        if (u < d.U) ly = a2 + (double)l.y * kLog2eD + node_log2(beta, eb, s + U1 + 1, n + 1, st.log_mode);
+        if (u < d.U) ly = a2 + (double)l.y * kLog2eD + node_log2(beta, eb, q + U1p + 1, gnext, st.log_mode);
     }
     RowTerms r;
     r.shift2 = fused ? (float)(lo - (double)rr.den * kLog2eD) + log2_scale : kNegInf;
@@ -732,27 +803,6 @@ __device__ __forceinline__ float clamp_to(float v, float cl, bool do_clamp) {
     return do_clamp ? fminf(fmaxf(v, -cl), cl) : v;
 }
 
-// The blank and label elements of a row get their flow subtracted by a
-// separate store from the thread that wrote the vector holding them (the
-// two stores are ordered: same thread, same address).  Their input values
-// come from the row record, not from the logits, which an in-place gradient
-// has already overwritten.
-template <typename T, bool FUSED>
-__device__ __forceinline__ void fix_special(T *dst, bool own_b, bool own_y, int blank, const RowRec &rr,
-                                            const RowTerms &rt, bool do_clamp, float cl) {
-    auto fix = [&](int k, float x, float sub) {
-        float v = 0.f;
-        if constexpr (FUSED) v = exp2_fast(fmaf(x, kLog2e, rt.shift2));
-        Elem<T>::store1(dst + k, clamp_to(v - sub, cl, do_clamp));
-    };
-    if (rt.y == blank) {
-        if (own_b) fix(blank, rr.xb, rt.fb + rt.fy);
-    } else {
-        if (own_b) fix(blank, rr.xb, rt.fb);
-        if (own_y) fix(rt.y, rr.xy, rt.fy);
-    }
-}
-
 // One row per wave; the next row's logits are loaded before the current
 // row's gradient is computed and written.
 template <typename T, int NV, bool FULL, bool FUSED, bool CLAMP>
@@ -790,6 +840,12 @@ __global__ __launch_bounds__(256) void k_grad_wide(const T *logits, T *grad, RNN
         // the wait counts for the current row never include these loads
         load_row(c.row_begin + min(r + 4, c.row_count - 1), xb);
         T *dst = grad + row * (int64_t)V;
+        // The blank and label elements get their flow subtracted in the
+        // registers of the vector that holds them: element k is element
+        // k % VEC of vector k / VEC, held by lane (k / VEC) mod 64 as its
+        // vector number (k / VEC) / 64.
+        const int vb = blank / VEC, vy = rt.y >= 0 ? rt.y / VEC : -1;
+        const int eb = blank - vb * VEC, ey = rt.y - vy * VEC;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int vi = i * 64 + lane;
@@ -799,15 +855,21 @@ __global__ __launch_bounds__(256) void k_grad_wide(const T *logits, T *grad, RNN
                 for (int e = 0; e < VEC; ++e) {
                     float v = 0.f;
                     if constexpr (FUSED) v = exp2_fast(fmaf(Raw<T>::get(xa[i], e), kLog2e, rt.shift2));
-                    gv[e] = clamp_to(v, cl, CLAMP);
+                    gv[e] = v;
                 }
+                if ((vb >> 6) == i) {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) gv[e] -= (vi == vb && e == eb) ? rt.fb : 0.f;
+                }
+                if (vy >= 0 && (vy >> 6) == i) {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) gv[e] -= (vi == vy && e == ey) ? rt.fy : 0.f;
+                }
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) gv[e] = clamp_to(gv[e], cl, CLAMP);
                 store_raw<T, true>(dst + (int64_t)vi * VEC, Raw<T>::put(gv));
             }
         }
-        // element k lies in vector k / VEC, held by lane (k / VEC) mod 64
-        const bool ob = ((blank / VEC) & 63) == lane;
-        const bool oy = rt.y >= 0 && ((rt.y / VEC) & 63) == lane;
-        if (ob || oy) fix_special<T, FUSED>(dst, ob, oy, blank, rr, rt, CLAMP, cl);
 #pragma unroll
         for (int i = 0; i < NV; ++i) xa[i] = xb[i];
     }
@@ -837,6 +899,8 @@ __global__ __launch_bounds__(256) void k_grad_narrow(const T *logits, T *grad, R
                                       scale, FUSED);
         const T *src = logits + row * (int64_t)V;
         T *dst = grad + row * (int64_t)V;
+        const int vb = blank / VEC, vy = rt.y >= 0 ? rt.y / VEC : -1;
+        const int eb = blank - vb * VEC, ey = rt.y - vy * VEC;
         for (int i = sub; i < nvec; i += G) {
             float x[VEC];
             if constexpr (FUSED) load_n<T, VEC>(src + (int64_t)i * VEC, x);
@@ -845,14 +909,12 @@ __global__ __launch_bounds__(256) void k_grad_narrow(const T *logits, T *grad, R
             for (int e = 0; e < VEC; ++e) {
                 float v = 0.f;
                 if constexpr (FUSED) v = exp2_fast(fmaf(x[e], kLog2e, rt.shift2));
+                v -= (i == vb && e == eb) ? rt.fb : 0.f;
+                v -= (i == vy && e == ey) ? rt.fy : 0.f;
                 gv[e] = clamp_to(v, cl, do_clamp);
             }
             store_n<T, VEC>(dst + (int64_t)i * VEC, gv);
         }
-        // the thread whose vectors hold the blank / label element rewrites it
-        const bool ob = ((blank / VEC) % G) == sub;
-        const bool oy = rt.y >= 0 && ((rt.y / VEC) % G) == sub;
-        if (ob || oy) fix_special<T, FUSED>(dst, ob, oy, blank, rr, rt, do_clamp, cl);
     }
 }
 
@@ -966,12 +1028,12 @@ hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream) {
         if (a.esize == 4)
             hipLaunchKernelGGL(k_gather<float>, grid, block, 0, stream, static_cast<const float *>(a.logits), a.V,
                                a.blank, WS(const SampleDesc *, desc), WS(const ChunkDesc *, chunks), a.targets, a.S,
-                               WS(RowRec *, rec), WS(float2 *, lp), WS(float2 *, prob), WS(int *, mode),
+                               WS(RowRec *, rec), WS(float2 *, lp), WS(double2 *, prob), WS(int *, mode),
                                WS(uint32_t *, status));
         else
             hipLaunchKernelGGL(k_gather<_Float16>, grid, block, 0, stream, static_cast<const _Float16 *>(a.logits),
                                a.V, a.blank, WS(const SampleDesc *, desc), WS(const ChunkDesc *, chunks), a.targets,
-                               a.S, WS(RowRec *, rec), WS(float2 *, lp), WS(float2 *, prob), WS(int *, mode),
+                               a.S, WS(RowRec *, rec), WS(float2 *, lp), WS(double2 *, prob), WS(int *, mode),
                                WS(uint32_t *, status));
         return hipGetLastError();
     }
@@ -982,7 +1044,7 @@ hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream) {
             auto kern = a.geom.wide_full ? k_rowstats_wide<T, Tg::n, true> : k_rowstats_wide<T, Tg::n, false>;
             hipLaunchKernelGGL(kern, grid, block, 0, stream, static_cast<const T *>(a.logits), a.V, a.blank,
                                WS(const SampleDesc *, desc), WS(const ChunkDesc *, chunks), a.targets, a.S,
-                               WS(RowRec *, rec), WS(float2 *, lp), WS(float2 *, prob), WS(int *, mode),
+                               WS(RowRec *, rec), WS(float2 *, lp), WS(double2 *, prob), WS(int *, mode),
                                WS(uint32_t *, status));
             return hipGetLastError();
         });
@@ -992,7 +1054,7 @@ hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream) {
         hipLaunchKernelGGL((k_rowstats_narrow<T, Tg::vec, Tg::n>), grid, block, 0, stream,
                            static_cast<const T *>(a.logits), a.V, a.blank, WS(const SampleDesc *, desc),
                            WS(const ChunkDesc *, chunks), a.targets, a.S, WS(RowRec *, rec), WS(float2 *, lp),
-                           WS(float2 *, prob), WS(int *, mode), WS(uint32_t *, status));
+                           WS(double2 *, prob), WS(int *, mode), WS(uint32_t *, status));
         return hipGetLastError();
     });
 }
@@ -1000,7 +1062,7 @@ hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream) {
 hipError_t launch_alpha_beta(const LaunchArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(k_alpha_beta, dim3(a.B), dim3(128), 0, stream, WS(const SampleDesc *, desc),
                        WS(const int32_t *, order), WS(const int *, mode), WS(const float2 *, lp),
-                       WS(const float2 *, prob), WS(double *, alpha), WS(double *, beta), WS(int *, ealpha),
+                       WS(const double2 *, prob), WS(double *, alpha), WS(double *, beta), WS(int *, ealpha),
                        WS(int *, ebeta), WS(double *, log2z), a.loss, WS(uint32_t *, status));
     return hipGetLastError();
 }
