@@ -23,6 +23,7 @@ namespace rnnt {
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr int64_t kCachedTailBytes = 160ll << 20;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
@@ -134,6 +135,20 @@ rnnt_status build_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t
     L.n_diags = diag;
     L.n_chunks = (int32_t)p.chunks.size();
     L.rows_per_chunk = rpc;
+    // The gradient pass walks the chunks in reverse, so the rows the
+    // rowstats pass reads last are read again first: those last ~160 MB
+    // (within the 256 MB memory-side cache) are read with caching loads,
+    // everything before them with non-temporal loads.
+    {
+        const int64_t row_bytes = (int64_t)V * esize;
+        int64_t tail = 0;
+        int32_t k = L.n_chunks;
+        while (k > 0 && tail < kCachedTailBytes) {
+            --k;
+            tail += (int64_t)p.chunks[k].row_count * row_bytes;
+        }
+        L.first_cached_chunk = k;
+    }
     return RNNT_SUCCESS;
 }
 
@@ -385,6 +400,7 @@ rnnt_status rnnt_loss_fused(const void *logits, rnnt_dtype dtype, int64_t N, int
     a.lay = plan.lay;
     a.geom = row_geometry(V, es, aligned16);
     a.max_U1 = plan.max_U1;
+    a.first_cached_chunk = plan.lay.first_cached_chunk;
     a.aligned16 = aligned16;
 
     if (plan.lay.n_chunks > 0 && timed(0, stream, [&] { return launch_rowstats(a, stream); }) != hipSuccess)

@@ -76,6 +76,7 @@ struct WorkspaceLayout {
     int64_t n_diags;
     int32_t n_chunks;
     int32_t rows_per_chunk;
+    int32_t first_cached_chunk;  // see LaunchArgs
 };
 
 // Row-pass geometry chosen from V and the element size.
@@ -111,6 +112,7 @@ struct LaunchArgs {
     WorkspaceLayout lay;
     RowGeom geom;
     int max_U1;          // max_i (U_i + 1)
+    int first_cached_chunk;  // chunks from here on are read with caching loads by rowstats
     bool aligned16;
 };
 

@@ -259,23 +259,55 @@ __device__ __forceinline__ int read_label(const SampleDesc &d, int u, int V, int
     return in_range ? y : -1;
 }
 
+// Element k (wave-uniform) of a row held the way the wide kernels hold it:
+// lane l keeps vectors i*64 + l, i < NV, of VEC elements each.  Selected in
+// registers and read from the owning lane, so no second load of the row.
+template <typename T, int NV>
+__device__ __forceinline__ float row_element(const typename Raw<T>::vec (&x)[NV], int k) {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    constexpr int VEC = Raw<T>::kVec;
+    constexpr int EPD = VEC / 4;  // elements per 32-bit word: 1 (fp32) or 2 (fp16)
+    const int v = k / VEC;
+    const int e = k - v * VEC;
+    const int target = (v >> 6) * 4 + e / EPD;  // word among the lane's 4*NV words
+    uint32_t bits = 0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const u4 q = __builtin_bit_cast(u4, x[j]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) bits = (j * 4 + c == target) ? q[c] : bits;
+    }
+    bits = (uint32_t)__builtin_amdgcn_readlane((int)bits, v & 63);
+    if constexpr (EPD == 1) return __uint_as_float(bits);
+    const uint16_t h = (uint16_t)((e & 1) ? (bits >> 16) : (bits & 0xffffu));
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Lattice node of the row `step` rows further on in the same sample.
+__device__ __forceinline__ void advance_node(int &t, int &u, int step, int U1) {
+    u += step;
+    while (u >= U1) {
+        u -= U1;
+        ++t;
+    }
+}
+
 // --------------------------------------------- K1 rowstats, one row per wave
 // Lane l holds elements (i*64 + l)*VEC .. +VEC-1 of a row, i < NV; the loads
-// of the wave's next row are issued before the current row is reduced.
-template <typename T, int NV, bool FULL>
-__global__ __launch_bounds__(256) void k_rowstats_wide(const T *__restrict__ logits, int V, int blank,
-                                                       const SampleDesc *__restrict__ desc,
-                                                       const ChunkDesc *__restrict__ chunks,
-                                                       const int32_t *__restrict__ targets, int S,
-                                                       RowRec *__restrict__ rec, float2 *__restrict__ lp,
-                                                       double2 *__restrict__ prob, int *__restrict__ mode,
-                                                       uint32_t *status) {
+// of the wave's next row (and its label) are issued before the current row is
+// reduced.  NT: non-temporal loads, for rows the gradient pass will not find
+// in the cache anyway; the chunks issued last use ordinary loads because the
+// gradient pass reads them again first.
+template <typename T, int NV, bool FULL, bool NT>
+__device__ __forceinline__ void rowstats_wide_chunk(const T *__restrict__ logits, int V, int blank,
+                                                    const SampleDesc &d, const ChunkDesc &c,
+                                                    const int32_t *__restrict__ targets, int S,
+                                                    RowRec *__restrict__ rec, float2 *__restrict__ lp,
+                                                    double2 *__restrict__ prob, int *__restrict__ mode,
+                                                    uint32_t *status) {
     constexpr int VEC = Raw<T>::kVec;
-    const ChunkDesc c = chunks[blockIdx.x];
-    const SampleDesc d = desc[c.sample];
     const int lane = threadIdx.x & 63;
-    // wave-uniform, so per-row scalars travel through scalar loads and do not
-    // share the vector memory counter with the row prefetch
+    // wave-uniform, so per-row scalars stay in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nvec = V / VEC;
     const int U1 = d.U + 1;
@@ -285,23 +317,25 @@ __global__ __launch_bounds__(256) void k_rowstats_wide(const T *__restrict__ log
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int vi = i * 64 + lane;
-            if (FULL || vi < nvec) x[i] = load_raw<T, false>(p + (int64_t)vi * VEC);
+            if (FULL || vi < nvec) x[i] = load_raw<T, NT>(p + (int64_t)vi * VEC);
         }
     };
     int r = wave;
-    if (r < c.row_count) load_row(c.row_begin + r, xa);
+    if (r >= c.row_count) return;
+    int t = (c.row_begin + r) / U1;
+    int u = (c.row_begin + r) - t * U1;
+    int y = __builtin_amdgcn_readfirstlane(read_label(d, u, V, blank, targets, S, status));
+    load_row(c.row_begin + r, xa);
     for (; r < c.row_count; r += 4) {
-        const int lr = c.row_begin + r;
-        const int t = lr / U1;
-        const int u = lr - t * U1;
-        const int64_t row = d.row_off + lr;
-        const T *p = logits + row * (int64_t)V;
-        const int y = read_label(d, u, V, blank, targets, S, status);
-        const float hb = Elem<T>::load1(p + blank);
-        const float hy = (y >= 0) ? Elem<T>::load1(p + y) : 0.f;
-        // unconditional (the last row is re-read at the end of the chunk), so
-        // the wait counts for the current row never include these loads
-        load_row(c.row_begin + min(r + 4, c.row_count - 1), xb);
+        const int64_t row = d.row_off + c.row_begin + r;
+        // next row of this wave: its logits and label are in flight while
+        // this row is reduced (the last row is loaded again at the end of
+        // the chunk, so every wait count covers exactly one row)
+        int tn = t, un = u;
+        advance_node(tn, un, 4, U1);
+        const bool more = r + 4 < c.row_count;
+        const int yn = more ? __builtin_amdgcn_readfirstlane(read_label(d, un, V, blank, targets, S, status)) : -1;
+        load_row(c.row_begin + (more ? r + 4 : r), xb);
         float m = kNegInf;
 #pragma unroll
         for (int i = 0; i < NV; ++i)
@@ -319,6 +353,8 @@ __global__ __launch_bounds__(256) void k_rowstats_wide(const T *__restrict__ log
                 for (int e = 0; e < VEC; ++e) s += exp2_fast(fmaf(Raw<T>::get(xa[i], e), kLog2e, nm));
         s = wave_sum_f(s);
         const float dn = (m == kNegInf) ? kNegInf : m + log2_fast(s) * kLn2;
+        const float hb = row_element<T, NV>(xa, blank);
+        const float hy = (y >= 0) ? row_element<T, NV>(xa, y) : 0.f;
         if (lane == 0) {
             const bool dead = (dn == kNegInf);
             const float lpb = dead ? kNegInf : hb - dn;
@@ -328,7 +364,26 @@ __global__ __launch_bounds__(256) void k_rowstats_wide(const T *__restrict__ log
         if (t == 0 || t == d.T - 1) fill_outside(d, t, u, lane, 64, lp, prob);
 #pragma unroll
         for (int i = 0; i < NV; ++i) xa[i] = xb[i];
+        t = tn;
+        u = un;
+        y = yn;
     }
+}
+
+template <typename T, int NV, bool FULL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FULL && NV * sizeof(T) <= 16 ? 5 : 1))) void k_rowstats_wide(const T *__restrict__ logits, int V, int blank,
+                                                       const SampleDesc *__restrict__ desc,
+                                                       const ChunkDesc *__restrict__ chunks, int first_cached,
+                                                       const int32_t *__restrict__ targets, int S,
+                                                       RowRec *__restrict__ rec, float2 *__restrict__ lp,
+                                                       double2 *__restrict__ prob, int *__restrict__ mode,
+                                                       uint32_t *status) {
+    const ChunkDesc c = chunks[blockIdx.x];
+    const SampleDesc d = desc[c.sample];
+    if ((int)blockIdx.x < first_cached)
+        rowstats_wide_chunk<T, NV, FULL, true>(logits, V, blank, d, c, targets, S, rec, lp, prob, mode, status);
+    else
+        rowstats_wide_chunk<T, NV, FULL, false>(logits, V, blank, d, c, targets, S, rec, lp, prob, mode, status);
 }
 
 // --------------------------------- K1 rowstats, G < 64 lanes per row (small V)
@@ -1043,7 +1098,8 @@ hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream) {
             using T = typename Tg::type;
             auto kern = a.geom.wide_full ? k_rowstats_wide<T, Tg::n, true> : k_rowstats_wide<T, Tg::n, false>;
             hipLaunchKernelGGL(kern, grid, block, 0, stream, static_cast<const T *>(a.logits), a.V, a.blank,
-                               WS(const SampleDesc *, desc), WS(const ChunkDesc *, chunks), a.targets, a.S,
+                               WS(const SampleDesc *, desc), WS(const ChunkDesc *, chunks), a.first_cached_chunk,
+                               a.targets, a.S,
                                WS(RowRec *, rec), WS(float2 *, lp), WS(double2 *, prob), WS(int *, mode),
                                WS(uint32_t *, status));
             return hipGetLastError();
