@@ -11,8 +11,9 @@ outputs and workspace are resident in HBM before the timed region starts.
 Prints one JSON line.  ``value`` is packed logits elements per second
 (N*V per step / time per step); the line also carries the effective HBM
 bandwidth of the whole step, the roofline of the dominant kernel (its
-algorithmic bytes per launch over its average launch time, measured with
-HIP events on the library's stream) and the fp64 CPU oracle timed on a
+algorithmic bytes per step over its device time per step, measured with HIP
+events around each of its launches on the stream the launch runs on; a step
+makes one or two launches of each pass) and the fp64 CPU oracle timed on a
 bounded sample of the same batch on this host's cores.
 
 ``--copy-calibration`` instead runs a plain device-to-device copy of known
@@ -69,7 +70,7 @@ def kernel_source_hash() -> str:
 
 
 def committed_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if it matches this kernel source."""
+    """HBM bytes per step from a committed rocprofv3 counter summary, if it matches this kernel source."""
     want = kernel_source_hash()
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         text = open(path).read()
@@ -80,7 +81,7 @@ def committed_traffic(kernel: str, workload: str):
                 continue
             if (d.get("kind") == "pmc_traffic" and d.get("kernel") == kernel and d.get("workload") == workload
                     and d.get("source_sha256_16") == want):
-                return d.get("traffic_bytes_per_launch")
+                return d.get("traffic_bytes_per_step")
     return None
 
 
@@ -210,14 +211,17 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     print(f"bench: {ms:.4f} ms/step (host wall {wall_ms:.4f})", file=sys.stderr, flush=True)
 
-    # per-kernel timing: events around each launch, on the library's stream
+    # per-kernel timing: HIP events around each launch, on the stream the
+    # launch runs on (a step makes one or two launches of each pass, see
+    # launches_per_step); times are summed per step
     rl._lib.timing_enable(True)
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     kt = rl._lib.timing_read()
     rl._lib.timing_enable(False)
-    per_kernel = {k: (v[0] / v[1] if v[1] else None) for k, v in kt.items()}
+    per_kernel = {k: (v[0] / args.steps if v[1] else None) for k, v in kt.items()}
+    launches = {k: v[1] / args.steps for k, v in kt.items()}
 
     ab = algorithmic_bytes(w)
     dominant = max((k for k in per_kernel if per_kernel[k] is not None), key=lambda k: per_kernel[k])
@@ -228,8 +232,9 @@ def main():
         traffic = committed_traffic(KERNEL_SYMBOLS[dominant], w.name)
         roofline = {"bound": "hbm", "kernel": KERNEL_SYMBOLS[dominant], "achieved": round(ach, 1),
                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4),
-                    "traffic": traffic, "algorithmic_bytes_per_launch": dom_bytes,
-                    "avg_launch_ms": round(per_kernel[dominant], 5)}
+                    "traffic": traffic, "algorithmic_bytes_per_step": dom_bytes,
+                    "kernel_ms_per_step": round(per_kernel[dominant], 5),
+                    "launches_per_step": launches[dominant]}
 
     eff = ab["path"] / (ms * 1e-3) / 1e9
     cpu = None
@@ -258,6 +263,7 @@ def main():
         "effective_frac_of_peak": round(eff / PEAK_HBM_GBPS, 4),
         "algorithmic_bytes_per_step": ab["path"],
         "kernel_ms": {k: (round(v, 5) if v is not None else None) for k, v in per_kernel.items()},
+        "launches_per_step": launches,
         "host_wall_ms_per_step": round(wall_ms, 4),
         "device_flags": flags,
         "roofline": roofline,

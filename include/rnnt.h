@@ -167,20 +167,30 @@ const char *rnnt_status_string(rnnt_status s);
 
 /*
  * Host-side schedule of a batch, for inspection and tests; touches no GPU.
- * Fills up to `cap` entries of each array:
+ * Fills up to `cap` entries of each array (any may be NULL):
  *   sample_order  int32[B]: samples by decreasing lattice area T*(U+1)
  *                 (ties: larger T+U first, then lower index) -- the order in
- *                 which the alpha/beta work of each sample is started.
+ *                 which the alpha/beta work of each sample is started
+ *                 (README "Operator features": largest tasks first).
  *   chunk_sample, chunk_row_begin, chunk_row_count   int32[n_chunks]: the
- *                 row chunks of the row passes, in issue order; each chunk
- *                 lies inside one sample; rows are sample-local.
+ *                 runs of lattice nodes the row passes hand to one
+ *                 workgroup each, in issue order; each lies inside one
+ *                 sample.  Kernels that take several short rows per
+ *                 wavefront walk a run in row order: sample-local rows
+ *                 chunk_row_begin .. +chunk_row_count-1.
+ *   chunk_diag, chunk_col   int32[n_chunks]: kernels that take one row per
+ *                 wavefront walk the same number of nodes in anti-diagonal
+ *                 order (diagonal n = t+u, then column u), from node
+ *                 (n, u) = (chunk_diag, chunk_col); both orders cut every
+ *                 sample after the same node counts.
  *   n_chunks      out: total number of chunks (may exceed cap).
  * Returns RNNT_INVALID_VALUE under the same length checks as _workspace_size.
  */
 rnnt_status rnnt_plan_describe(int32_t B, int32_t V, rnnt_dtype dtype,
                                const int32_t *logit_lengths, const int32_t *target_lengths,
                                int32_t cap, int32_t *sample_order, int32_t *chunk_sample,
-                               int32_t *chunk_row_begin, int32_t *chunk_row_count, int32_t *n_chunks);
+                               int32_t *chunk_row_begin, int32_t *chunk_row_count,
+                               int32_t *chunk_diag, int32_t *chunk_col, int32_t *n_chunks);
 
 /*
  * Per-kernel timing for measurement.  While enabled, every rnnt_loss_fused

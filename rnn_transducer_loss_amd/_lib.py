@@ -62,7 +62,7 @@ def load():
         lib.rnnt_loss_fused_check.argtypes = [_vp, _vp, ctypes.POINTER(ctypes.c_uint32)]
         lib.rnnt_loss_fused_check.restype = ctypes.c_int
         lib.rnnt_plan_describe.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int, _i32p, _i32p, ctypes.c_int32,
-                                           _i32p, _i32p, _i32p, _i32p, _i32p]
+                                           _i32p, _i32p, _i32p, _i32p, _i32p, _i32p, _i32p]
         lib.rnnt_plan_describe.restype = ctypes.c_int
         lib.rnnt_timing_enable.argtypes = [ctypes.c_int]
         lib.rnnt_timing_enable.restype = ctypes.c_int
@@ -144,23 +144,29 @@ def device_flags(ws_ptr: int, stream: int) -> int:
     return int(out.value)
 
 
-def plan_describe(V: int, dtype_code: int, logit_lengths, target_lengths):
-    """(sample_order, chunks[(sample, row_begin, row_count)]) of the host schedule; no GPU needed."""
+def plan_describe(V: int, dtype_code: int, logit_lengths, target_lengths, diagonal: bool = False):
+    """Host schedule; no GPU needed.
+
+    Returns (sample_order, chunks) with chunks[k] = (sample, row_begin, row_count)
+    (row order), or with diagonal=True chunks[k] = (sample, diag, col, count):
+    the same runs walked in anti-diagonal order from node (diag, col).
+    """
     T = host_i32(logit_lengths)
     U = host_i32(target_lengths)
     B = len(T)
     n = ctypes.c_int32()
     lib = load()
-    check(lib.rnnt_plan_describe(B, V, dtype_code, _p(T), _p(U), 0, None, None, None, None, ctypes.byref(n)),
-          "rnnt_plan_describe")
+    check(lib.rnnt_plan_describe(B, V, dtype_code, _p(T), _p(U), 0, None, None, None, None, None, None,
+                                 ctypes.byref(n)), "rnnt_plan_describe")
     cap = max(B, n.value)
     order = np.zeros(cap, np.int32)
-    cs = np.zeros(cap, np.int32)
-    cb = np.zeros(cap, np.int32)
-    cc = np.zeros(cap, np.int32)
-    check(lib.rnnt_plan_describe(B, V, dtype_code, _p(T), _p(U), cap, _p(order), _p(cs), _p(cb), _p(cc),
-                                 ctypes.byref(n)), "rnnt_plan_describe")
-    return order[:B].copy(), np.stack([cs[:n.value], cb[:n.value], cc[:n.value]], axis=1)
+    cs, cb, cc, cd, cu = (np.zeros(cap, np.int32) for _ in range(5))
+    check(lib.rnnt_plan_describe(B, V, dtype_code, _p(T), _p(U), cap, _p(order), _p(cs), _p(cb), _p(cc), _p(cd),
+                                 _p(cu), ctypes.byref(n)), "rnnt_plan_describe")
+    k = n.value
+    if diagonal:
+        return order[:B].copy(), np.stack([cs[:k], cd[:k], cu[:k], cc[:k]], axis=1)
+    return order[:B].copy(), np.stack([cs[:k], cb[:k], cc[:k]], axis=1)
 
 
 def timing_enable(on: bool):

@@ -34,6 +34,23 @@ struct Plan {
     int max_U1 = 1;
 };
 
+// Node (n, u) of the anti-diagonal order of a T x (U+1) lattice that lies
+// `k` nodes after the first node of diagonal n0 (diagonal n holds columns
+// max(0, n-T+1) .. min(n, U)).
+void diag_node(int32_t T, int32_t U, int64_t k, int32_t &n, int32_t &u, int32_t n0) {
+    n = n0;
+    for (;;) {
+        const int64_t lo = std::max<int64_t>(0, (int64_t)n - T + 1), hi = std::min<int64_t>(n, U);
+        const int64_t len = hi - lo + 1;
+        if (k < len) {
+            u = (int32_t)(lo + k);
+            return;
+        }
+        k -= len;
+        ++n;
+    }
+}
+
 rnnt_status check_lengths(int32_t B, int32_t V, const int32_t *T, const int32_t *U) {
     if (B < 1 || V < 1 || !T || !U) return RNNT_INVALID_VALUE;
     for (int32_t i = 0; i < B; ++i) {
@@ -103,13 +120,15 @@ rnnt_status build_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t
         const int32_t i = p.order[k];
         const int64_t rows = (int64_t)T[i] * (U[i] + 1);
         if (rows > INT32_MAX) return RNNT_INVALID_VALUE;
+        // the diagonal-order start of every run, walked once along the diagonals
+        int32_t n = 0;
+        int64_t before_n = 0;  // nodes on the diagonals before n
         for (int64_t r0 = 0; r0 < rows; r0 += rpc) {
-            ChunkDesc c;
-            c.sample = i;
-            c.row_begin = (int32_t)r0;
-            c.row_count = (int32_t)std::min<int64_t>(rpc, rows - r0);
-            c.pad = 0;
-            p.chunks.push_back(c);
+            int32_t nn = 0, uu = 0;
+            diag_node(T[i], U[i], r0 - before_n, nn, uu, n);
+            for (; n < nn; ++n)
+                before_n += std::min<int64_t>(n, U[i]) - std::max<int64_t>(0, (int64_t)n - T[i] + 1) + 1;
+            p.chunks.push_back(ChunkDesc{i, (int32_t)r0, (int32_t)std::min<int64_t>(rpc, rows - r0), nn, uu});
         }
     }
     if (p.chunks.size() > (size_t)INT32_MAX) return RNNT_INVALID_VALUE;
@@ -121,8 +140,7 @@ rnnt_status build_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t
     L.desc = off;   off = align_up(off + sizeof(SampleDesc) * B);
     L.order = off;  off = align_up(off + sizeof(int32_t) * B);
     L.chunks = off; off = align_up(off + sizeof(ChunkDesc) * p.chunks.size());
-    L.rec = off;    off = align_up(off + sizeof(RowRec) * (size_t)row);
-    L.lp = off;     off = align_up(off + 2 * sizeof(float) * (size_t)slot);
+    L.node = off;   off = align_up(off + 4 * sizeof(float) * (size_t)slot);
     L.prob = off;   off = align_up(off + 2 * sizeof(double) * (size_t)slot);
     L.alpha = off;  off = align_up(off + sizeof(double) * (size_t)ab);
     L.beta = off;   off = align_up(off + sizeof(double) * (size_t)ab);
@@ -145,7 +163,7 @@ rnnt_status build_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t
         int32_t k = L.n_chunks;
         while (k > 0 && tail < kCachedTailBytes) {
             --k;
-            tail += (int64_t)p.chunks[k].row_count * row_bytes;
+            tail += (int64_t)p.chunks[k].count * row_bytes;
         }
         L.first_cached_chunk = k;
     }
@@ -203,7 +221,7 @@ rnnt_status upload(void *dst, const std::vector<uint8_t> &src, hipStream_t strea
 // The header, descriptors, order and chunks are contiguous at the start of
 // the workspace and go up in one copy (the status word is cleared with it).
 std::vector<uint8_t> pack_plan(const Plan &p) {
-    std::vector<uint8_t> buf(p.lay.rec, 0);
+    std::vector<uint8_t> buf(p.lay.node, 0);
     std::memcpy(buf.data() + p.lay.desc, p.desc.data(), sizeof(SampleDesc) * p.desc.size());
     std::memcpy(buf.data() + p.lay.order, p.order.data(), sizeof(int32_t) * p.order.size());
     std::memcpy(buf.data() + p.lay.chunks, p.chunks.data(), sizeof(ChunkDesc) * p.chunks.size());
@@ -331,7 +349,7 @@ rnnt_status rnnt_loss_fused_workspace_size(int32_t B, int32_t V, int64_t N, rnnt
 rnnt_status rnnt_plan_describe(int32_t B, int32_t V, rnnt_dtype dtype, const int32_t *logit_lengths,
                                const int32_t *target_lengths, int32_t cap, int32_t *sample_order,
                                int32_t *chunk_sample, int32_t *chunk_row_begin, int32_t *chunk_row_count,
-                               int32_t *n_chunks) {
+                               int32_t *chunk_diag, int32_t *chunk_col, int32_t *n_chunks) {
     const int es = esize_of(dtype);
     if (!es || cap < 0) return RNNT_INVALID_VALUE;
     Plan p;
@@ -343,7 +361,9 @@ rnnt_status rnnt_plan_describe(int32_t B, int32_t V, rnnt_dtype dtype, const int
     for (int32_t k = 0; k < nc && k < cap; ++k) {
         if (chunk_sample) chunk_sample[k] = p.chunks[k].sample;
         if (chunk_row_begin) chunk_row_begin[k] = p.chunks[k].row_begin;
-        if (chunk_row_count) chunk_row_count[k] = p.chunks[k].row_count;
+        if (chunk_row_count) chunk_row_count[k] = p.chunks[k].count;
+        if (chunk_diag) chunk_diag[k] = p.chunks[k].diag;
+        if (chunk_col) chunk_col[k] = p.chunks[k].col;
     }
     if (n_chunks) *n_chunks = nc;
     return RNNT_SUCCESS;
@@ -377,6 +397,7 @@ rnnt_status rnnt_loss_fused(const void *logits, rnnt_dtype dtype, int64_t N, int
     if ((uintptr_t)workspace % kAlign != 0) return RNNT_INVALID_VALUE;
 
     hipStream_t stream = static_cast<hipStream_t>(stream_);
+    const RowGeom geom = row_geometry(V, es, aligned16);
     st = upload(workspace, e->packed, stream);
     if (st != RNNT_SUCCESS) return st;
 
@@ -398,9 +419,8 @@ rnnt_status rnnt_loss_fused(const void *logits, rnnt_dtype dtype, int64_t N, int
     a.reduction = reduction;
     a.ws = static_cast<uint8_t *>(workspace);
     a.lay = plan.lay;
-    a.geom = row_geometry(V, es, aligned16);
+    a.geom = geom;
     a.max_U1 = plan.max_U1;
-    a.first_cached_chunk = plan.lay.first_cached_chunk;
     a.aligned16 = aligned16;
 
     if (plan.lay.n_chunks > 0 && timed(0, stream, [&] { return launch_rowstats(a, stream); }) != hipSuccess)
@@ -424,10 +444,10 @@ rnnt_status rnnt_grad_scale(void *grad, rnnt_dtype dtype, int64_t N, int32_t V, 
     if (st != RNNT_SUCCESS) return st;
     const Plan &p = e->plan;
     if (workspace_bytes < p.lay.total) return RNNT_WORKSPACE_TOO_SMALL;
-    if (p.lay.n_chunks == 0) return RNNT_SUCCESS;
+    if (N == 0) return RNNT_SUCCESS;
     const bool aligned16 = ((int64_t)V * es) % 16 == 0 && (uintptr_t)grad % 16 == 0;
-    if (launch_grad_scale(grad, es, V, scale, per_sample, static_cast<const uint8_t *>(workspace), p.lay,
-                          row_geometry(V, es, aligned16), aligned16, static_cast<hipStream_t>(stream_)) != hipSuccess)
+    if (launch_grad_scale(grad, es, V, N, B, scale, per_sample, static_cast<const uint8_t *>(workspace), p.lay,
+                          row_geometry(V, es, aligned16), static_cast<hipStream_t>(stream_)) != hipSuccess)
         return RNNT_EXECUTION_FAILED;
     return RNNT_SUCCESS;
 }

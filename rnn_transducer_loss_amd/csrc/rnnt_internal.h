@@ -11,14 +11,15 @@
 namespace rnnt {
 
 // One sample of the packed batch.  Rows are t-major: packed row
-// row_off + t*(U+1) + u is lattice node (t,u).  The per-node scalars of the
-// recursions live in a skewed layout, one slot per (anti-diagonal n = t+u, u):
-// slot_off + n*(U+1) + u, n in [0, T+U), so every anti-diagonal is contiguous.
-// The recursions' outputs (alpha, beta) use the same skewed order with the
-// diagonal padded to a whole number of wavefront column groups:
+// row_off + t*(U+1) + u is lattice node (t,u).  The per-node values written
+// by the row pass live in a skewed layout, one slot per (anti-diagonal
+// n = t+u, u): slot_off + n*(U+1) + u, n in [0, T+U), so every anti-diagonal
+// is contiguous; slots with t = n-u outside [0, T) hold "impossible"
+// weights.  The recursions' outputs (alpha, beta) use the same skewed order
+// with the diagonal padded to a whole number of wavefront column groups:
 // ab_off + n*U1p + u, U1p = 64 * (lattice columns per lane), so every lane of
-// the sweep owns a slot.  Per-diagonal values (the recursions'
-// power-of-two exponents) are at diag_off + n / 8.
+// the sweep owns a slot.  Per-diagonal values (the recursions' power-of-two
+// exponents) are at diag_off + n / 8.
 struct SampleDesc {
     int64_t row_off;
     int64_t slot_off;
@@ -38,33 +39,37 @@ inline int cols_per_lane(int U1) {
     return c;
 }
 
-// A run of rows of one sample processed by one workgroup of the row passes.
+// A run of `count` lattice nodes of one sample handed to one workgroup of a
+// row pass, in one of two orders:
+//   row order: the sample-local rows row_begin .. row_begin+count-1 (the
+//     gradient pass, and the row-statistics pass when a wavefront takes
+//     several short rows);
+//   diagonal order: by anti-diagonal n, then column u, from node
+//     (n, u) = (diag, col); node (n, u) is row (n-u)*(U+1) + u (the
+//     row-statistics pass when a wavefront takes one row, so that its
+//     per-node outputs land in consecutive slots).
+// Both orders cut every sample after the same node counts.
 struct ChunkDesc {
     int32_t sample;
-    int32_t row_begin;  // sample-local first row
-    int32_t row_count;
-    int32_t pad;
-};
-
-// Per packed row, written by the row-statistics pass for the gradient pass:
-// the row's log-sum-exp (0 for log-prob inputs) and its label (-1 at u = U or
-// when out of range).
-struct RowRec {
-    float den;
-    int32_t y;
+    int32_t row_begin;
+    int32_t count;
+    int32_t diag;
+    int32_t col;
 };
 
 // Byte offsets of the workspace regions (each 256-byte aligned).  Everything
-// before `rec` is written by the per-call upload.
+// before `node` is written by the per-call upload.  Per skewed slot:
+//   node  {log P(blank), log P(next label), log-sum-exp of the row (fused) or
+//         0, the next label as int bits (-1 if none)};
+//   prob  {P(blank), P(next label)}, fp32-accurate values held as fp64.
 struct WorkspaceLayout {
     size_t status;      // uint32 status word
     size_t mode;        // int32[B]: 1 = log-domain recursion (set by rowstats)
     size_t desc;        // SampleDesc[B]
     size_t order;       // int32[B], samples by decreasing cost
     size_t chunks;      // ChunkDesc[n_chunks]
-    size_t rec;         // RowRec[N]
-    size_t lp;          // float2[S]: {log P(blank), log P(next label)} per slot
-    size_t prob;        // double2[S]: the same as probabilities
+    size_t node;        // float4[S]
+    size_t prob;        // double2[S]
     size_t alpha;       // double[S_ab], padded diagonals
     size_t beta;        // double[S_ab]
     size_t ealpha;      // int32[D + B]: exponent of alpha per group of 8 diagonals
@@ -76,7 +81,7 @@ struct WorkspaceLayout {
     int64_t n_diags;
     int32_t n_chunks;
     int32_t rows_per_chunk;
-    int32_t first_cached_chunk;  // see LaunchArgs
+    int32_t first_cached_chunk;  // rowstats: chunks from here on use caching loads
 };
 
 // Row-pass geometry chosen from V and the element size.
@@ -112,7 +117,6 @@ struct LaunchArgs {
     WorkspaceLayout lay;
     RowGeom geom;
     int max_U1;          // max_i (U_i + 1)
-    int first_cached_chunk;  // chunks from here on are read with caching loads by rowstats
     bool aligned16;
 };
 
@@ -120,9 +124,9 @@ hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream);
 hipError_t launch_alpha_beta(const LaunchArgs &a, hipStream_t stream);
 hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream);
 hipError_t launch_reduce(const LaunchArgs &a, hipStream_t stream);
-hipError_t launch_grad_scale(void *grad, int esize, int V, const float *scale, int per_sample,
+hipError_t launch_grad_scale(void *grad, int esize, int V, int64_t N, int B, const float *scale, int per_sample,
                              const uint8_t *ws, const WorkspaceLayout &lay, const RowGeom &geom,
-                             bool aligned16, hipStream_t stream);
+                             hipStream_t stream);
 
 // Largest lattice width (U+1) the alpha/beta kernel supports.
 constexpr int kMaxU1 = 1024;

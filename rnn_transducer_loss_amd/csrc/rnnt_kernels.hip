@@ -31,6 +31,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "rnnt_internal.h"
 
 namespace rnnt {
@@ -205,48 +207,63 @@ __device__ __forceinline__ double read_lane_d(double x, int lane) {
 }
 
 // ---------------------------------------------------- row statistics output
-// Writes what the recursions and the gradient need about node (t,u):
-//   rec  (row order)  {log-sum-exp of the row (fused) or 0, the label (-1 if
-//                      none)},
-//   lp   (skewed)     {log P(blank), log P(y_{u+1})},
-//   prob (skewed)     the same as probabilities (fp32-accurate, stored as fp64).
-// The blank edge leaving t = T-1 below u = U leaves the lattice and the label
-// edge at u = U does not exist, so both are stored as impossible.
-__device__ __forceinline__ void emit_node(const SampleDesc &d, int t, int u, int64_t row, float dn, int y,
-                                          float lpb, float lpy, RowRec *__restrict__ rec,
-                                          float2 *__restrict__ lp, double2 *__restrict__ prob,
+// Writes what the recursions and the gradient need about node (t,u), at its
+// skewed slot: node = {log P(blank), log P(y_{u+1}), log-sum-exp of the row
+// (fused) or 0, the label (-1 if none)} and prob = the two probabilities
+// (fp32-accurate, held as fp64).  The blank edge leaving t = T-1 below u = U
+// leaves the lattice and the label edge at u = U does not exist, so both are
+// stored as impossible.  The wide kernel calls it from every lane with
+// wave-uniform values (the stores are then unconditional and the compiler's
+// wait counts stay exact); the others from one lane per row.
+__device__ __forceinline__ void emit_node(const SampleDesc &d, int t, int u, float dn, int y, float lpb, float lpy,
+                                          float4 *__restrict__ node, double2 *__restrict__ prob,
                                           int *__restrict__ mode) {
     if (t == d.T - 1 && u < d.U) lpb = kNegInf;
     if (u == d.U) lpy = kNegInf;
-    rec[row] = RowRec{dn, y};
-    const int U1 = d.U + 1;
-    const int64_t slot = d.slot_off + (int64_t)(t + u) * U1 + u;
-    lp[slot] = make_float2(lpb, lpy);
+    const int64_t slot = d.slot_off + (int64_t)(t + u) * (d.U + 1) + u;
+    node[slot] = make_float4(lpb, lpy, dn, __int_as_float(y));
     prob[slot] = make_double2((double)prob_of(lpb), (double)prob_of(lpy));
     const bool wide = (lpb != kNegInf && fabsf(lpb) > kProbRange) || (lpy != kNegInf && fabsf(lpy) > kProbRange);
     if (wide) atomicOr(&mode[d.index], 1);
 }
 
-// The skewed layout has slots (n,u) with t = n-u outside [0, T): the upper
-// triangle n < u and the lower triangle n >= T + u.  The row (0,u) clears
-// column u of the first and the row (T-1,u) column u of the second, so the
-// recursions can read every slot of a diagonal without masks.
-__device__ __forceinline__ void fill_outside(const SampleDesc &d, int t, int u, int lane, int nl,
-                                             float2 *__restrict__ lp, double2 *__restrict__ prob) {
+// Slots u0 .. u1-1 of diagonal n hold no lattice node: give them impossible
+// weights, so the recursions read whole diagonals without masks.  `lane`
+// of `nl` cooperating threads.
+__device__ __forceinline__ void fill_slots(const SampleDesc &d, int n, int u0, int u1, int lane, int nl,
+                                           float4 *__restrict__ node, double2 *__restrict__ prob) {
+    const int64_t base = d.slot_off + (int64_t)n * (d.U + 1);
+    for (int u = u0 + lane; u < u1; u += nl) {
+        node[base + u] = make_float4(kNegInf, kNegInf, 0.f, __int_as_float(-1));
+        prob[base + u] = make_double2(0.0, 0.0);
+    }
+}
+
+// Diagonal order: the first node of diagonal n (u = max(0, n-T+1)) fills the
+// slots below it (t >= T), the last (u = min(n, U)) those above it (t < 0).
+__device__ __forceinline__ void fill_diagonal_ends(const SampleDesc &d, int n, int u, int lane, int nl,
+                                                   float4 *__restrict__ node, double2 *__restrict__ prob) {
+    const int lo = max(0, n - d.T + 1), hi = min(n, d.U);
+    if (u == lo && lo > 0) fill_slots(d, n, 0, lo, lane, nl, node, prob);
+    if (u == hi && hi < d.U) fill_slots(d, n, hi + 1, d.U + 1, lane, nl, node, prob);
+}
+
+// Row order: row (0,u) fills column u of the diagonals n < u (t < 0), row
+// (T-1,u) column u of the diagonals n >= T+u (t >= T).
+__device__ __forceinline__ void fill_columns(const SampleDesc &d, int t, int u, int lane, int nl,
+                                             float4 *__restrict__ node, double2 *__restrict__ prob) {
     const int U1 = d.U + 1;
-    const float2 nlp = make_float2(kNegInf, kNegInf);
-    const double2 np = make_double2(0.0, 0.0);
     if (t == 0)
         for (int n = lane; n < u; n += nl) {
             const int64_t s = d.slot_off + (int64_t)n * U1 + u;
-            lp[s] = nlp;
-            prob[s] = np;
+            node[s] = make_float4(kNegInf, kNegInf, 0.f, __int_as_float(-1));
+            prob[s] = make_double2(0.0, 0.0);
         }
     if (t == d.T - 1)
         for (int n = d.T + u + lane; n < d.T + d.U; n += nl) {
             const int64_t s = d.slot_off + (int64_t)n * U1 + u;
-            lp[s] = nlp;
-            prob[s] = np;
+            node[s] = make_float4(kNegInf, kNegInf, 0.f, __int_as_float(-1));
+            prob[s] = make_double2(0.0, 0.0);
         }
 }
 
@@ -283,7 +300,7 @@ __device__ __forceinline__ float row_element(const typename Raw<T>::vec (&x)[NV]
     return (float)__builtin_bit_cast(_Float16, h);
 }
 
-// Lattice node of the row `step` rows further on in the same sample.
+// Lattice node of the row `step` rows further on in the same sample (row order).
 __device__ __forceinline__ void advance_node(int &t, int &u, int step, int U1) {
     u += step;
     while (u >= U1) {
@@ -292,28 +309,41 @@ __device__ __forceinline__ void advance_node(int &t, int &u, int step, int U1) {
     }
 }
 
+// Node `step` nodes further on in diagonal order (anti-diagonal n, then
+// column u; diagonal n holds columns max(0, n-T+1) .. min(n, U)).  Stops at
+// the last diagonal, so a step past the end of the lattice leaves u out of
+// range there.
+__device__ __forceinline__ void advance_diag(int &n, int &u, int step, int T, int U) {
+    u += step;
+    while (u > min(n, U) && n < T + U - 1) {
+        u -= min(n, U) + 1;
+        ++n;
+        u += max(0, n - T + 1);
+    }
+}
+
 // --------------------------------------------- K1 rowstats, one row per wave
-// Lane l holds elements (i*64 + l)*VEC .. +VEC-1 of a row, i < NV; the loads
-// of the wave's next row (and its label) are issued before the current row is
-// reduced.  NT: non-temporal loads, for rows the gradient pass will not find
-// in the cache anyway; the chunks issued last use ordinary loads because the
-// gradient pass reads them again first.
+// Lane l holds elements (i*64 + l)*VEC .. +VEC-1 of a row, i < NV.  The
+// chunk's nodes are walked in diagonal order, so the per-node outputs of the
+// four waves land in consecutive slots, and each node's row is one
+// contiguous read.  NT: non-temporal loads, for rows the gradient pass will
+// not find in the cache anyway; the chunks issued last use ordinary loads
+// because the gradient pass reads them again first.
 template <typename T, int NV, bool FULL, bool NT>
 __device__ __forceinline__ void rowstats_wide_chunk(const T *__restrict__ logits, int V, int blank,
                                                     const SampleDesc &d, const ChunkDesc &c,
                                                     const int32_t *__restrict__ targets, int S,
-                                                    RowRec *__restrict__ rec, float2 *__restrict__ lp,
-                                                    double2 *__restrict__ prob, int *__restrict__ mode,
-                                                    uint32_t *status) {
+                                                    float4 *__restrict__ node, double2 *__restrict__ prob,
+                                                    int *__restrict__ mode, uint32_t *status) {
     constexpr int VEC = Raw<T>::kVec;
+    using Vec = typename Raw<T>::vec;
     const int lane = threadIdx.x & 63;
     // wave-uniform, so per-row scalars stay in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nvec = V / VEC;
     const int U1 = d.U + 1;
-    typename Raw<T>::vec xa[NV], xb[NV];
-    auto load_row = [&](int lr, typename Raw<T>::vec (&x)[NV]) {
-        const T *p = logits + (d.row_off + lr) * (int64_t)V;
+    auto load_row = [&](int n, int u, Vec (&x)[NV]) {
+        const T *p = logits + (d.row_off + (int64_t)(n - u) * U1 + u) * (int64_t)V;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int vi = i * 64 + lane;
@@ -321,27 +351,30 @@ __device__ __forceinline__ void rowstats_wide_chunk(const T *__restrict__ logits
         }
     };
     int r = wave;
-    if (r >= c.row_count) return;
-    int t = (c.row_begin + r) / U1;
-    int u = (c.row_begin + r) - t * U1;
+    if (r >= c.count) return;
+    int n = c.diag, u = c.col;
+    advance_diag(n, u, r, d.T, d.U);
     int y = __builtin_amdgcn_readfirstlane(read_label(d, u, V, blank, targets, S, status));
-    load_row(c.row_begin + r, xa);
-    for (; r < c.row_count; r += 4) {
-        const int64_t row = d.row_off + c.row_begin + r;
-        // next row of this wave: its logits and label are in flight while
-        // this row is reduced (the last row is loaded again at the end of
-        // the chunk, so every wait count covers exactly one row)
-        int tn = t, un = u;
-        advance_node(tn, un, 4, U1);
-        const bool more = r + 4 < c.row_count;
+    // One row: the next row's logits (and label) are requested first, into
+    // the next of three buffers used in turn, then this row is reduced.  With
+    // three buffers a buffer is reloaded two rows after the stores issued
+    // while it was current, so the loads never wait for those stores to
+    // release their registers, and every wait covers exactly the buffer about
+    // to be used.  The last row of the wave loads itself again (a cache hit)
+    // to keep the wait counts static.
+    auto row_step = [&](Vec (&xc)[NV], Vec (&xn)[NV]) -> bool {
+        const bool more = r + 4 < c.count;
+        int nn = n, un = u;
+        advance_diag(nn, un, 4, d.T, d.U);
+        if (more) load_row(nn, un, xn);
+        else load_row(n, u, xn);
         const int yn = more ? __builtin_amdgcn_readfirstlane(read_label(d, un, V, blank, targets, S, status)) : -1;
-        load_row(c.row_begin + (more ? r + 4 : r), xb);
         float m = kNegInf;
 #pragma unroll
         for (int i = 0; i < NV; ++i)
             if (FULL || i * 64 + lane < nvec)
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) m = fmaxf(m, Raw<T>::get(xa[i], e));
+                for (int e = 0; e < VEC; ++e) m = fmaxf(m, Raw<T>::get(xc[i], e));
         m = wave_max_f(m);
         const float mr = (m == kNegInf) ? 0.f : m;
         const float nm = -mr * kLog2e;
@@ -350,51 +383,53 @@ __device__ __forceinline__ void rowstats_wide_chunk(const T *__restrict__ logits
         for (int i = 0; i < NV; ++i)
             if (FULL || i * 64 + lane < nvec)
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) s += exp2_fast(fmaf(Raw<T>::get(xa[i], e), kLog2e, nm));
+                for (int e = 0; e < VEC; ++e) s += exp2_fast(fmaf(Raw<T>::get(xc[i], e), kLog2e, nm));
         s = wave_sum_f(s);
         const float dn = (m == kNegInf) ? kNegInf : m + log2_fast(s) * kLn2;
-        const float hb = row_element<T, NV>(xa, blank);
-        const float hy = (y >= 0) ? row_element<T, NV>(xa, y) : 0.f;
-        if (lane == 0) {
-            const bool dead = (dn == kNegInf);
-            const float lpb = dead ? kNegInf : hb - dn;
-            const float lpy = (dead || y < 0) ? kNegInf : hy - dn;
-            emit_node(d, t, u, row, dn, y, lpb, lpy, rec, lp, prob, mode);
-        }
-        if (t == 0 || t == d.T - 1) fill_outside(d, t, u, lane, 64, lp, prob);
-#pragma unroll
-        for (int i = 0; i < NV; ++i) xa[i] = xb[i];
-        t = tn;
+        const float hb = row_element<T, NV>(xc, blank);
+        const float hy = (y >= 0) ? row_element<T, NV>(xc, y) : 0.f;
+        const bool dead = (dn == kNegInf);
+        const float lpb = dead ? kNegInf : hb - dn;
+        const float lpy = (dead || y < 0) ? kNegInf : hy - dn;
+        emit_node(d, n - u, u, dn, y, lpb, lpy, node, prob, mode);
+        fill_diagonal_ends(d, n, u, lane, 64, node, prob);
+        n = nn;
         u = un;
         y = yn;
+        r += 4;
+        return more;
+    };
+    Vec x0[NV], x1[NV], x2[NV];
+    load_row(n, u, x0);
+    while (row_step(x0, x1) && row_step(x1, x2) && row_step(x2, x0)) {
     }
 }
 
 template <typename T, int NV, bool FULL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FULL && NV * sizeof(T) <= 16 ? 5 : 1))) void k_rowstats_wide(const T *__restrict__ logits, int V, int blank,
+__global__ __launch_bounds__(256) void k_rowstats_wide(const T *__restrict__ logits, int V, int blank,
                                                        const SampleDesc *__restrict__ desc,
                                                        const ChunkDesc *__restrict__ chunks, int first_cached,
                                                        const int32_t *__restrict__ targets, int S,
-                                                       RowRec *__restrict__ rec, float2 *__restrict__ lp,
-                                                       double2 *__restrict__ prob, int *__restrict__ mode,
-                                                       uint32_t *status) {
+                                                       float4 *__restrict__ node, double2 *__restrict__ prob,
+                                                       int *__restrict__ mode, uint32_t *status) {
     const ChunkDesc c = chunks[blockIdx.x];
     const SampleDesc d = desc[c.sample];
     if ((int)blockIdx.x < first_cached)
-        rowstats_wide_chunk<T, NV, FULL, true>(logits, V, blank, d, c, targets, S, rec, lp, prob, mode, status);
+        rowstats_wide_chunk<T, NV, FULL, true>(logits, V, blank, d, c, targets, S, node, prob, mode, status);
     else
-        rowstats_wide_chunk<T, NV, FULL, false>(logits, V, blank, d, c, targets, S, rec, lp, prob, mode, status);
+        rowstats_wide_chunk<T, NV, FULL, false>(logits, V, blank, d, c, targets, S, node, prob, mode, status);
 }
 
 // --------------------------------- K1 rowstats, G < 64 lanes per row (small V)
+// Rows in row order (several short rows per wave); each row's outputs go to
+// its skewed slot.
 template <typename T, int VEC, int G>
 __global__ __launch_bounds__(256) void k_rowstats_narrow(const T *__restrict__ logits, int V, int blank,
                                                          const SampleDesc *__restrict__ desc,
                                                          const ChunkDesc *__restrict__ chunks,
                                                          const int32_t *__restrict__ targets, int S,
-                                                         RowRec *__restrict__ rec, float2 *__restrict__ lp,
-                                                         double2 *__restrict__ prob, int *__restrict__ mode,
-                                                         uint32_t *status) {
+                                                         float4 *__restrict__ node, double2 *__restrict__ prob,
+                                                         int *__restrict__ mode, uint32_t *status) {
     constexpr int RPW = 64 / G;
     const ChunkDesc c = chunks[blockIdx.x];
     const SampleDesc d = desc[c.sample];
@@ -404,9 +439,9 @@ __global__ __launch_bounds__(256) void k_rowstats_narrow(const T *__restrict__ l
     const int sub = lane & (G - 1);
     const int grp = lane / G;
     const int nvec = V / VEC;
-    for (int base = wave * RPW; base < c.row_count; base += 4 * RPW) {
+    for (int base = wave * RPW; base < c.count; base += 4 * RPW) {
         const int r = base + grp;
-        const bool active = r < c.row_count;
+        const bool active = r < c.count;
         const int lr = c.row_begin + (active ? r : 0);
         const int64_t row = d.row_off + lr;
         const T *p = logits + row * (int64_t)V;
@@ -448,35 +483,43 @@ __global__ __launch_bounds__(256) void k_rowstats_narrow(const T *__restrict__ l
             const float hy = (y >= 0) ? Elem<T>::load1(p + y) : 0.f;
             const float lpb = dead ? kNegInf : hb - dn;
             const float lpy = (dead || y < 0) ? kNegInf : hy - dn;
-            emit_node(d, t, u, row, dn, y, lpb, lpy, rec, lp, prob, mode);
+            emit_node(d, t, u, dn, y, lpb, lpy, node, prob, mode);
         }
-        if (t == 0 || t == d.T - 1) fill_outside(d, t, u, sub, G, lp, prob);
+        if (t == 0 || t == d.T - 1) fill_columns(d, t, u, sub, G, node, prob);
     }
 }
 
 // Non-fused inputs are already log-probabilities: gather the two values only.
-template <typename T>
+// One node per thread, in the chunk's order (DIAG: diagonal order).
+template <typename T, bool DIAG>
 __global__ __launch_bounds__(256) void k_gather(const T *__restrict__ logits, int V, int blank,
                                                 const SampleDesc *__restrict__ desc,
                                                 const ChunkDesc *__restrict__ chunks,
                                                 const int32_t *__restrict__ targets, int S,
-                                                RowRec *__restrict__ rec, float2 *__restrict__ lp,
-                                                double2 *__restrict__ prob, int *__restrict__ mode,
-                                                uint32_t *status) {
+                                                float4 *__restrict__ node, double2 *__restrict__ prob,
+                                                int *__restrict__ mode, uint32_t *status) {
     const ChunkDesc c = chunks[blockIdx.x];
     const SampleDesc d = desc[c.sample];
     const int U1 = d.U + 1;
-    for (int r = threadIdx.x; r < c.row_count; r += blockDim.x) {
-        const int lr = c.row_begin + r;
-        const int t = lr / U1;
-        const int u = lr - t * U1;
-        const int64_t row = d.row_off + lr;
-        const T *p = logits + row * (int64_t)V;
+    for (int r = threadIdx.x; r < c.count; r += blockDim.x) {
+        int t, u;
+        if constexpr (DIAG) {
+            int n = c.diag;
+            u = c.col;
+            advance_diag(n, u, r, d.T, d.U);
+            t = n - u;
+            fill_diagonal_ends(d, n, u, 0, 1, node, prob);
+        } else {
+            const int lr = c.row_begin + r;
+            t = lr / U1;
+            u = lr - t * U1;
+            if (t == 0 || t == d.T - 1) fill_columns(d, t, u, 0, 1, node, prob);
+        }
+        const T *p = logits + (d.row_off + (int64_t)t * U1 + u) * (int64_t)V;
         const int y = read_label(d, u, V, blank, targets, S, status);
         const float lpb = Elem<T>::load1(p + blank);
         const float lpy = (y < 0) ? kNegInf : Elem<T>::load1(p + y);
-        emit_node(d, t, u, row, 0.f, y, lpb, lpy, rec, lp, prob, mode);
-        if (t == 0 || t == d.T - 1) fill_outside(d, t, u, 0, 1, lp, prob);
+        emit_node(d, t, u, 0.f, y, lpb, lpy, node, prob, mode);
     }
 }
 
@@ -484,7 +527,9 @@ __global__ __launch_bounds__(256) void k_gather(const T *__restrict__ logits, in
 // Lane l owns lattice columns u = l + 64*j, j < C.  Lanes past the lattice
 // width read column U instead: their values start at zero (-inf in the log
 // domain) and only ever receive zero, because the label edge leaving column U
-// is stored as impossible.  The node inputs of PF diagonals are loaded one
+// is stored as impossible.  Every slot of a diagonal holds weights (the row
+// pass fills those outside the lattice with "impossible"), so no step needs
+// a mask.  The node inputs of PF diagonals are loaded one
 // block ahead into one of two register rings used in turn; each block's
 // outputs are stored after its compute, so a wait for a block's inputs never
 // covers the previous block's stores.
@@ -507,7 +552,8 @@ __global__ __launch_bounds__(256) void k_gather(const T *__restrict__ logits, in
 // product; all exponents are 0.
 struct ProbDomain {
     static constexpr bool kLog = false;
-    using W = double2;
+    using W = double2;                       // prob[] slot: {P(blank), P(label)}
+    static constexpr uint32_t kStride = 16;  // bytes per slot
     __device__ static double zero() { return 0.0; }
     __device__ static double one() { return 1.0; }
     __device__ static double combine(double a, double b) { return a + b; }
@@ -517,7 +563,8 @@ struct ProbDomain {
 };
 struct LogDomain {
     static constexpr bool kLog = true;
-    using W = float2;
+    using W = float2;                        // first half of the node[] slot: {log P(blank), log P(label)}
+    static constexpr uint32_t kStride = 16;
     __device__ static double zero() { return kNegInfD; }
     __device__ static double one() { return 0.0; }
     __device__ static double combine(double a, double b) {
@@ -546,16 +593,17 @@ template <typename W, int C, int PF> struct Ring {
     W v[PF][C];
 };
 
-// Diagonals n0, n0+step, ... (clamped into [0, nd)) of a sample's slots.
-// voff[j]: the lane's byte offset inside a diagonal (column min(u, U)), so
-// each load is a scalar diagonal base plus a fixed 32-bit lane offset.
+// Diagonals n0, n0+step, ... (clamped into [0, nd)) of a sample's slots
+// (w: the sample's first slot, `stride` bytes per slot).  voff[j]: the
+// lane's byte offset inside a diagonal (column min(u, U)), so each load is a
+// scalar diagonal base plus a fixed 32-bit lane offset.
 template <typename W, int C, int PF>
-__device__ __forceinline__ void load_block(Ring<W, C, PF> &r, const W *__restrict__ w, int U1,
+__device__ __forceinline__ void load_block(Ring<W, C, PF> &r, const char *__restrict__ w, int64_t diag_bytes,
                                            const uint32_t (&voff)[C], int n0, int step, int nd) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
         const int n = min(max(n0 + step * p, 0), nd - 1);
-        const char *row = reinterpret_cast<const char *>(w + (int64_t)n * U1);
+        const char *row = w + (int64_t)n * diag_bytes;
 #pragma unroll
         for (int j = 0; j < C; ++j) r.v[p][j] = *reinterpret_cast<const W *>(row + voff[j]);
     }
@@ -623,7 +671,7 @@ __device__ __forceinline__ void forward_block(const Ring<typename D::W, C, PF> &
 }
 
 template <typename D, int C, int PF>
-__device__ void sweep_forward(const SampleDesc &d, const typename D::W *__restrict__ w, double *__restrict__ out,
+__device__ void sweep_forward(const SampleDesc &d, const char *__restrict__ w, double *__restrict__ out,
                               int *__restrict__ eout, double *log2z) {
     using W = typename D::W;
     const int lane = threadIdx.x & 63;
@@ -638,18 +686,19 @@ __device__ void sweep_forward(const SampleDesc &d, const typename D::W *__restri
     int E = 0;
     if (lane == 0) eout[0] = 0;
     uint32_t voff[C];
-    lane_offsets<C>(voff, U, sizeof(W));
+    lane_offsets<C>(voff, U, D::kStride);
+    const int64_t diag_bytes = (int64_t)U1 * D::kStride;
     Ring<W, C, PF> ra, rb;
-    load_block<W, C, PF>(ra, w, U1, voff, 0, 1, nd);
+    load_block<W, C, PF>(ra, w, diag_bytes, voff, 0, 1, nd);
     int n0 = 0;
     for (; n0 + 2 * PF <= nd; n0 += 2 * PF) {
-        load_block<W, C, PF>(rb, w, U1, voff, n0 + PF, 1, nd);
+        load_block<W, C, PF>(rb, w, diag_bytes, voff, n0 + PF, 1, nd);
         forward_block<D, C, PF, false>(ra, n0, nd, lane, mb, my, E, out, eout);
-        load_block<W, C, PF>(ra, w, U1, voff, n0 + 2 * PF, 1, nd);
+        load_block<W, C, PF>(ra, w, diag_bytes, voff, n0 + 2 * PF, 1, nd);
         forward_block<D, C, PF, false>(rb, n0 + PF, nd, lane, mb, my, E, out, eout);
     }
     if (n0 < nd) {
-        load_block<W, C, PF>(rb, w, U1, voff, n0 + PF, 1, nd);
+        load_block<W, C, PF>(rb, w, diag_bytes, voff, n0 + PF, 1, nd);
         forward_block<D, C, PF, true>(ra, n0, nd, lane, mb, my, E, out, eout);
         if (n0 + PF < nd) forward_block<D, C, PF, true>(rb, n0 + PF, nd, lane, mb, my, E, out, eout);
     }
@@ -691,7 +740,7 @@ __device__ __forceinline__ void backward_block(const Ring<typename D::W, C, PF> 
 }
 
 template <typename D, int C, int PF>
-__device__ void sweep_backward(const SampleDesc &d, const typename D::W *__restrict__ w, double *__restrict__ out,
+__device__ void sweep_backward(const SampleDesc &d, const char *__restrict__ w, double *__restrict__ out,
                                int *__restrict__ eout, double *log2z) {
     using W = typename D::W;
     const int lane = threadIdx.x & 63;
@@ -702,18 +751,19 @@ __device__ void sweep_backward(const SampleDesc &d, const typename D::W *__restr
     int E = 0;
     if (lane == 0) eout[0] = 0;
     uint32_t voff[C];
-    lane_offsets<C>(voff, U, sizeof(W));
+    lane_offsets<C>(voff, U, D::kStride);
+    const int64_t diag_bytes = (int64_t)U1 * D::kStride;
     Ring<W, C, PF> ra, rb;
-    load_block<W, C, PF>(ra, w, U1, voff, nd - 1, -1, nd);
+    load_block<W, C, PF>(ra, w, diag_bytes, voff, nd - 1, -1, nd);
     int n0 = nd - 1;
     for (; n0 - 2 * PF + 1 >= 0; n0 -= 2 * PF) {
-        load_block<W, C, PF>(rb, w, U1, voff, n0 - PF, -1, nd);
+        load_block<W, C, PF>(rb, w, diag_bytes, voff, n0 - PF, -1, nd);
         backward_block<D, C, PF, false>(ra, n0, nd, lane, pv, E, out, eout);
-        load_block<W, C, PF>(ra, w, U1, voff, n0 - 2 * PF, -1, nd);
+        load_block<W, C, PF>(ra, w, diag_bytes, voff, n0 - 2 * PF, -1, nd);
         backward_block<D, C, PF, false>(rb, n0 - PF, nd, lane, pv, E, out, eout);
     }
     if (n0 >= 0) {
-        load_block<W, C, PF>(rb, w, U1, voff, n0 - PF, -1, nd);
+        load_block<W, C, PF>(rb, w, diag_bytes, voff, n0 - PF, -1, nd);
         backward_block<D, C, PF, true>(ra, n0, nd, lane, pv, E, out, eout);
         if (n0 - PF >= 0) backward_block<D, C, PF, true>(rb, n0 - PF, nd, lane, pv, E, out, eout);
     }
@@ -721,24 +771,26 @@ __device__ void sweep_backward(const SampleDesc &d, const typename D::W *__restr
 }
 
 template <int C, int PF>
-__device__ void run_sweeps(const SampleDesc &d, bool log_mode, const float2 *lp, const double2 *prob, double *alpha,
-                           double *beta, int *ea, int *eb, double *shz) {
+__device__ void run_sweeps(const SampleDesc &d, bool log_mode, const float4 *node, const double2 *prob,
+                           double *alpha, double *beta, int *ea, int *eb, double *shz) {
     const int wave = threadIdx.x >> 6;
     const int64_t so = d.slot_off;
     const int64_t ao = d.ab_off;
     const int64_t dof = d.diag_off;
     if (log_mode) {
-        if (wave == 0) sweep_forward<LogDomain, C, PF>(d, lp + so, alpha + ao, ea + dof, &shz[0]);
-        else sweep_backward<LogDomain, C, PF>(d, lp + so, beta + ao, eb + dof, &shz[1]);
+        const char *w = reinterpret_cast<const char *>(node + so);
+        if (wave == 0) sweep_forward<LogDomain, C, PF>(d, w, alpha + ao, ea + dof, &shz[0]);
+        else sweep_backward<LogDomain, C, PF>(d, w, beta + ao, eb + dof, &shz[1]);
     } else {
-        if (wave == 0) sweep_forward<ProbDomain, C, PF>(d, prob + so, alpha + ao, ea + dof, &shz[0]);
-        else sweep_backward<ProbDomain, C, PF>(d, prob + so, beta + ao, eb + dof, &shz[1]);
+        const char *w = reinterpret_cast<const char *>(prob + so);
+        if (wave == 0) sweep_forward<ProbDomain, C, PF>(d, w, alpha + ao, ea + dof, &shz[0]);
+        else sweep_backward<ProbDomain, C, PF>(d, w, beta + ao, eb + dof, &shz[1]);
     }
 }
 
 __global__ __launch_bounds__(128) void k_alpha_beta(const SampleDesc *__restrict__ desc,
                                                     const int32_t *__restrict__ order,
-                                                    const int *__restrict__ mode, const float2 *__restrict__ lp,
+                                                    const int *__restrict__ mode, const float4 *__restrict__ node,
                                                     const double2 *__restrict__ prob, double *__restrict__ alpha,
                                                     double *__restrict__ beta, int *__restrict__ ealpha,
                                                     int *__restrict__ ebeta, double *__restrict__ log2z,
@@ -752,11 +804,11 @@ __global__ __launch_bounds__(128) void k_alpha_beta(const SampleDesc *__restrict
     // within the 63 vector memory operations the wait counter tracks; two
     // fp64 rings hold 8*C*PF registers.
     switch (d.U1p) {
-    case 64: run_sweeps<1, 16>(d, lm, lp, prob, alpha, beta, ealpha, ebeta, shz); break;
-    case 128: run_sweeps<2, 8>(d, lm, lp, prob, alpha, beta, ealpha, ebeta, shz); break;
-    case 256: run_sweeps<4, 4>(d, lm, lp, prob, alpha, beta, ealpha, ebeta, shz); break;
-    case 512: run_sweeps<8, 2>(d, lm, lp, prob, alpha, beta, ealpha, ebeta, shz); break;
-    default: run_sweeps<16, 1>(d, lm, lp, prob, alpha, beta, ealpha, ebeta, shz); break;
+    case 64: run_sweeps<1, 16>(d, lm, node, prob, alpha, beta, ealpha, ebeta, shz); break;
+    case 128: run_sweeps<2, 8>(d, lm, node, prob, alpha, beta, ealpha, ebeta, shz); break;
+    case 256: run_sweeps<4, 4>(d, lm, node, prob, alpha, beta, ealpha, ebeta, shz); break;
+    case 512: run_sweeps<8, 2>(d, lm, node, prob, alpha, beta, ealpha, ebeta, shz); break;
+    default: run_sweeps<16, 1>(d, lm, node, prob, alpha, beta, ealpha, ebeta, shz); break;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -793,25 +845,25 @@ __device__ __forceinline__ double node_log2(const double *__restrict__ v, const 
     return log_mode ? v[s] : log2_d(v[s]) + (double)e[ge];
 }
 
-__device__ __forceinline__ RowTerms row_terms(const SampleDesc &d, const SampleTerms &st, int lr, const RowRec &rr,
-                                              const float2 *__restrict__ lp, const double *__restrict__ alpha,
+// Terms of node (t, u) from its skewed slots: the row's log-sum-exp, label
+// and log-probs (node), alpha, beta and beta of the two successors.
+__device__ __forceinline__ RowTerms row_terms(const SampleDesc &d, const SampleTerms &st, int t, int u,
+                                              const float4 *__restrict__ node, const double *__restrict__ alpha,
                                               const double *__restrict__ beta, const int *__restrict__ ealpha,
                                               const int *__restrict__ ebeta, float log2_scale, float scale,
                                               bool fused) {
     const int U1 = d.U + 1;
-    const int t = lr / U1;
-    const int u = lr - t * U1;
     const int n = t + u;
-    const int64_t s = d.slot_off + (int64_t)n * U1 + u;      // lp slot
+    const int64_t s = d.slot_off + (int64_t)n * U1 + u;      // node slot
     const int64_t q = d.ab_off + (int64_t)n * d.U1p + u;     // alpha / beta slot
     const int U1p = d.U1p;
     const int *ea = ealpha + d.diag_off;
     const int *eb = ebeta + d.diag_off;
     const int nd = d.T + d.U;
+    const float4 l = node[s];
     double lb = kNegInfD, ly = kNegInfD, lo = kNegInfD;
     if (st.log2z != kNegInfD) {
         const double a2 = node_log2(alpha, ea, q, (n + 1) >> 3, st.log_mode) - st.log2z;
-        const float2 l = lp[s];
         lo = a2 + node_log2(beta, eb, q, (nd - n) >> 3, st.log_mode);
         const int gnext = (nd - n - 1) >> 3;
         if (t < d.T - 1) lb = a2 + (double)l.x * kLog2eD + node_log2(beta, eb, q + U1p, gnext, st.log_mode);
@@ -819,10 +871,10 @@ __device__ __forceinline__ RowTerms row_terms(const SampleDesc &d, const SampleT
         if (u < d.U) ly = a2 + (double)l.y * kLog2eD + node_log2(beta, eb, q + U1p + 1, gnext, st.log_mode);
     }
     RowTerms r;
-    r.shift2 = fused ? (float)(lo - (double)rr.den * kLog2eD) + log2_scale : kNegInf;
+    r.shift2 = fused ? (float)(lo - (double)l.z * kLog2eD) + log2_scale : kNegInf;
     r.fb = exp2_fast((float)lb) * scale;
     r.fy = exp2_fast((float)ly) * scale;
-    r.y = rr.y;
+    r.y = __float_as_int(l.w);
     return r;
 }
 
@@ -833,8 +885,7 @@ struct GradArgs {
     const ChunkDesc *chunks;
     const int *mode;
     const double *log2z;
-    const RowRec *rec;
-    const float2 *lp;
+    const float4 *node;
     const double *alpha;
     const double *beta;
     const int *ealpha;
@@ -847,19 +898,18 @@ struct GradArgs {
 #define RNNT_GRAD_PARAMS                                                                                      \
     int V, int blank, int n_chunks, float clamp, float scale, float log2_scale,                              \
         const SampleDesc *__restrict__ desc, const ChunkDesc *__restrict__ chunks, const int *__restrict__ mode, \
-        const double *__restrict__ log2z, const RowRec *__restrict__ rec, const float2 *__restrict__ lp,       \
-        const double *__restrict__ alpha, const double *__restrict__ beta, const int *__restrict__ ealpha,     \
-        const int *__restrict__ ebeta
-#define RNNT_GRAD_ARGS(g)                                                                                     \
-    g.V, g.blank, g.n_chunks, g.clamp, g.scale, g.log2_scale, g.desc, g.chunks, g.mode, g.log2z, g.rec, g.lp, \
+        const double *__restrict__ log2z, const float4 *__restrict__ node, const double *__restrict__ alpha,   \
+        const double *__restrict__ beta, const int *__restrict__ ealpha, const int *__restrict__ ebeta
+#define RNNT_GRAD_ARGS(g)                                                                                  \
+    g.V, g.blank, g.n_chunks, g.clamp, g.scale, g.log2_scale, g.desc, g.chunks, g.mode, g.log2z, g.node,   \
         g.alpha, g.beta, g.ealpha, g.ebeta
 
 __device__ __forceinline__ float clamp_to(float v, float cl, bool do_clamp) {
     return do_clamp ? fminf(fmaxf(v, -cl), cl) : v;
 }
 
-// One row per wave; the next row's logits are loaded before the current
-// row's gradient is computed and written.
+// One row per wave, rows in row order (consecutive rows of the chunk are
+// contiguous in memory).
 template <typename T, int NV, bool FULL, bool FUSED, bool CLAMP>
 __global__ __launch_bounds__(256) void k_grad_wide(const T *logits, T *grad, RNNT_GRAD_PARAMS) {
     constexpr int VEC = Raw<T>::kVec;
@@ -871,9 +921,10 @@ __global__ __launch_bounds__(256) void k_grad_wide(const T *logits, T *grad, RNN
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nvec = V / VEC;
+    const int U1 = d.U + 1;
     const float cl = clamp * scale;
-    typename Raw<T>::vec xa[NV], xb[NV];
-    auto load_row = [&](int lr, typename Raw<T>::vec (&x)[NV]) {
+    using Vec = typename Raw<T>::vec;
+    auto load_row = [&](int lr, Vec (&x)[NV]) {
         if constexpr (FUSED) {
             const T *p = logits + (d.row_off + lr) * (int64_t)V;
 #pragma unroll
@@ -884,16 +935,21 @@ __global__ __launch_bounds__(256) void k_grad_wide(const T *logits, T *grad, RNN
         }
     };
     int r = wave;
-    if (r < c.row_count) load_row(c.row_begin + r, xa);
-    for (; r < c.row_count; r += 4) {
-        const int lr = c.row_begin + r;
-        const int64_t row = d.row_off + lr;
-        const RowRec rr = rec[row];
-        const RowTerms rt = row_terms(d, st, lr, rr, lp, alpha, beta, ealpha, ebeta, log2_scale,
-                                      scale, FUSED);
-        // unconditional (the last row is re-read at the end of the chunk), so
-        // the wait counts for the current row never include these loads
-        load_row(c.row_begin + min(r + 4, c.row_count - 1), xb);
+    if (r >= c.count) return;
+    int t = (c.row_begin + r) / U1;
+    int u = (c.row_begin + r) - t * U1;
+    // One row: the next row's logits are requested first, into the next of
+    // three buffers used in turn, then this row's gradient is computed in
+    // place and written.  With three buffers a buffer is reloaded two rows
+    // after its gradient stores were issued, so the loads never wait for
+    // those stores to release their registers, and every wait covers exactly
+    // the buffer about to be used.  The last row loads itself again to keep
+    // the wait counts static.
+    auto row_step = [&](Vec (&xc)[NV], Vec (&xn)[NV]) -> bool {
+        const bool more = r + 4 < c.count;
+        load_row(c.row_begin + (more ? r + 4 : r), xn);
+        const int64_t row = d.row_off + c.row_begin + r;
+        const RowTerms rt = row_terms(d, st, t, u, node, alpha, beta, ealpha, ebeta, log2_scale, scale, FUSED);
         T *dst = grad + row * (int64_t)V;
         // The blank and label elements get their flow subtracted in the
         // registers of the vector that holds them: element k is element
@@ -909,7 +965,7 @@ __global__ __launch_bounds__(256) void k_grad_wide(const T *logits, T *grad, RNN
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
                     float v = 0.f;
-                    if constexpr (FUSED) v = exp2_fast(fmaf(Raw<T>::get(xa[i], e), kLog2e, rt.shift2));
+                    if constexpr (FUSED) v = exp2_fast(fmaf(Raw<T>::get(xc[i], e), kLog2e, rt.shift2));
                     gv[e] = v;
                 }
                 if ((vb >> 6) == i) {
@@ -922,21 +978,28 @@ __global__ __launch_bounds__(256) void k_grad_wide(const T *logits, T *grad, RNN
                 }
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) gv[e] = clamp_to(gv[e], cl, CLAMP);
-                store_raw<T, true>(dst + (int64_t)vi * VEC, Raw<T>::put(gv));
+                xc[i] = Raw<T>::put(gv);
+                store_raw<T, true>(dst + (int64_t)vi * VEC, xc[i]);
             }
         }
-#pragma unroll
-        for (int i = 0; i < NV; ++i) xa[i] = xb[i];
+        advance_node(t, u, 4, U1);
+        r += 4;
+        return more;
+    };
+    Vec x0[NV], x1[NV], x2[NV];
+    load_row(c.row_begin + r, x0);
+    while (row_step(x0, x1) && row_step(x1, x2) && row_step(x2, x0)) {
     }
 }
 
-// G < 64 lanes per row (small V), 64/G rows per wave.
+// G < 64 lanes per row (small V), 64/G rows per wave, rows in row order.
 template <typename T, int VEC, int G, bool FUSED>
 __global__ __launch_bounds__(256) void k_grad_narrow(const T *logits, T *grad, RNNT_GRAD_PARAMS) {
     constexpr int RPW = 64 / G;
     const ChunkDesc c = chunks[n_chunks - 1 - blockIdx.x];
     const SampleDesc d = desc[c.sample];
     const SampleTerms st{log2z[d.index], mode[d.index] != 0};
+    const int U1 = d.U + 1;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int sub = lane & (G - 1);
@@ -944,14 +1007,14 @@ __global__ __launch_bounds__(256) void k_grad_narrow(const T *logits, T *grad, R
     const int nvec = V / VEC;
     const float cl = clamp * scale;
     const bool do_clamp = clamp > 0.f;
-    for (int base = wave * RPW; base < c.row_count; base += 4 * RPW) {
+    for (int base = wave * RPW; base < c.count; base += 4 * RPW) {
         const int r = base + grp;
-        if (r >= c.row_count) continue;
+        if (r >= c.count) continue;
         const int lr = c.row_begin + r;
+        const int t = lr / U1;
+        const int u = lr - t * U1;
         const int64_t row = d.row_off + lr;
-        const RowRec rr = rec[row];
-        const RowTerms rt = row_terms(d, st, lr, rr, lp, alpha, beta, ealpha, ebeta, log2_scale,
-                                      scale, FUSED);
+        const RowTerms rt = row_terms(d, st, t, u, node, alpha, beta, ealpha, ebeta, log2_scale, scale, FUSED);
         const T *src = logits + row * (int64_t)V;
         T *dst = grad + row * (int64_t)V;
         const int vb = blank / VEC, vy = rt.y >= 0 ? rt.y / VEC : -1;
@@ -983,30 +1046,38 @@ __global__ __launch_bounds__(64) void k_reduce(const float *__restrict__ loss, i
     if (threadIdx.x == 0) out[0] = (float)(mean ? s / (double)B : s);
 }
 
-// Upstream-gradient scaling of an already written gradient.
+// Upstream-gradient scaling of an already written gradient: each workgroup
+// takes 4 * 64/G consecutive packed rows; with a per-sample factor, a row's
+// sample is found by binary search over the samples' first rows.
 template <typename T, int VEC, int G>
-__global__ __launch_bounds__(256) void k_grad_scale(T *grad, int V, const SampleDesc *__restrict__ desc,
-                                                    const ChunkDesc *__restrict__ chunks,
+__global__ __launch_bounds__(256) void k_grad_scale(T *grad, int V, int64_t N, int B,
+                                                    const SampleDesc *__restrict__ desc,
                                                     const float *__restrict__ scale, int per_sample) {
     constexpr int RPW = 64 / G;
-    const ChunkDesc c = chunks[blockIdx.x];
-    const SampleDesc d = desc[c.sample];
-    const float f = scale[per_sample ? d.index : 0];
-    if (f == 1.0f) return;
     const int lane = threadIdx.x & 63;
     const int sub = lane & (G - 1);
-    const int nvec = V / VEC;
-    for (int base = (threadIdx.x >> 6) * RPW; base < c.row_count; base += 4 * RPW) {
-        const int r = base + lane / G;
-        if (r >= c.row_count) continue;
-        T *p = grad + (d.row_off + c.row_begin + r) * (int64_t)V;
-        for (int i = sub; i < nvec; i += G) {
-            float x[VEC];
-            load_n<T, VEC>(p + (int64_t)i * VEC, x);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) x[e] *= f;
-            store_n<T, VEC>(p + (int64_t)i * VEC, x);
+    const int64_t row = (int64_t)blockIdx.x * (4 * RPW) + (threadIdx.x >> 6) * RPW + lane / G;
+    if (row >= N) return;
+    int s = 0;
+    if (per_sample) {
+        int lo = 0, hi = B - 1;  // last sample whose first row is <= row
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (desc[mid].row_off <= row) lo = mid;
+            else hi = mid - 1;
         }
+        s = desc[lo].index;
+    }
+    const float f = scale[s];
+    if (f == 1.0f) return;
+    T *p = grad + row * (int64_t)V;
+    const int nvec = V / VEC;
+    for (int i = sub; i < nvec; i += G) {
+        float x[VEC];
+        load_n<T, VEC>(p + (int64_t)i * VEC, x);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) x[e] *= f;
+        store_n<T, VEC>(p + (int64_t)i * VEC, x);
     }
 }
 
@@ -1079,28 +1150,28 @@ RowGeom row_geometry(int V, int esize, bool aligned16) {
 
 hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream) {
     const dim3 grid(a.lay.n_chunks), block(256);
+    const bool diag = a.geom.wide_nv > 0;  // the uploaded chunk table is in diagonal order
     if (!a.fused) {
-        if (a.esize == 4)
-            hipLaunchKernelGGL(k_gather<float>, grid, block, 0, stream, static_cast<const float *>(a.logits), a.V,
+        auto go = [&](auto tag, auto dtag) {
+            using T = decltype(tag);
+            constexpr bool D = decltype(dtag)::value;
+            hipLaunchKernelGGL((k_gather<T, D>), grid, block, 0, stream, static_cast<const T *>(a.logits), a.V,
                                a.blank, WS(const SampleDesc *, desc), WS(const ChunkDesc *, chunks), a.targets, a.S,
-                               WS(RowRec *, rec), WS(float2 *, lp), WS(double2 *, prob), WS(int *, mode),
-                               WS(uint32_t *, status));
-        else
-            hipLaunchKernelGGL(k_gather<_Float16>, grid, block, 0, stream, static_cast<const _Float16 *>(a.logits),
-                               a.V, a.blank, WS(const SampleDesc *, desc), WS(const ChunkDesc *, chunks), a.targets,
-                               a.S, WS(RowRec *, rec), WS(float2 *, lp), WS(double2 *, prob), WS(int *, mode),
-                               WS(uint32_t *, status));
-        return hipGetLastError();
+                               WS(float4 *, node), WS(double2 *, prob), WS(int *, mode), WS(uint32_t *, status));
+            return hipGetLastError();
+        };
+        if (a.esize == 4)
+            return diag ? go(float{}, std::true_type{}) : go(float{}, std::false_type{});
+        return diag ? go(_Float16{}, std::true_type{}) : go(_Float16{}, std::false_type{});
     }
-    if (a.geom.wide_nv > 0)
+    if (diag)
         return with_wide(a.esize, a.geom.wide_nv, [&](auto tag) {
             using Tg = decltype(tag);
             using T = typename Tg::type;
             auto kern = a.geom.wide_full ? k_rowstats_wide<T, Tg::n, true> : k_rowstats_wide<T, Tg::n, false>;
             hipLaunchKernelGGL(kern, grid, block, 0, stream, static_cast<const T *>(a.logits), a.V, a.blank,
-                               WS(const SampleDesc *, desc), WS(const ChunkDesc *, chunks), a.first_cached_chunk,
-                               a.targets, a.S,
-                               WS(RowRec *, rec), WS(float2 *, lp), WS(double2 *, prob), WS(int *, mode),
+                               WS(const SampleDesc *, desc), WS(const ChunkDesc *, chunks), a.lay.first_cached_chunk,
+                               a.targets, a.S, WS(float4 *, node), WS(double2 *, prob), WS(int *, mode),
                                WS(uint32_t *, status));
             return hipGetLastError();
         });
@@ -1109,15 +1180,15 @@ hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream) {
         using T = typename Tg::type;
         hipLaunchKernelGGL((k_rowstats_narrow<T, Tg::vec, Tg::n>), grid, block, 0, stream,
                            static_cast<const T *>(a.logits), a.V, a.blank, WS(const SampleDesc *, desc),
-                           WS(const ChunkDesc *, chunks), a.targets, a.S, WS(RowRec *, rec), WS(float2 *, lp),
-                           WS(double2 *, prob), WS(int *, mode), WS(uint32_t *, status));
+                           WS(const ChunkDesc *, chunks), a.targets, a.S, WS(float4 *, node), WS(double2 *, prob),
+                           WS(int *, mode), WS(uint32_t *, status));
         return hipGetLastError();
     });
 }
 
 hipError_t launch_alpha_beta(const LaunchArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(k_alpha_beta, dim3(a.B), dim3(128), 0, stream, WS(const SampleDesc *, desc),
-                       WS(const int32_t *, order), WS(const int *, mode), WS(const float2 *, lp),
+                       WS(const int32_t *, order), WS(const int *, mode), WS(const float4 *, node),
                        WS(const double2 *, prob), WS(double *, alpha), WS(double *, beta), WS(int *, ealpha),
                        WS(int *, ebeta), WS(double *, log2z), a.loss, WS(uint32_t *, status));
     return hipGetLastError();
@@ -1136,8 +1207,7 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
     g.chunks = WS(const ChunkDesc *, chunks);
     g.mode = WS(const int *, mode);
     g.log2z = WS(const double *, log2z);
-    g.rec = WS(const RowRec *, rec);
-    g.lp = WS(const float2 *, lp);
+    g.node = WS(const float4 *, node);
     g.alpha = WS(const double *, alpha);
     g.beta = WS(const double *, beta);
     g.ealpha = WS(const int *, ealpha);
@@ -1151,8 +1221,8 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
             const bool cl = a.clamp > 0.f;
             const bool fu = a.geom.wide_full;
             void (*kern)(const T *, T *, int, int, int, float, float, float, const SampleDesc *, const ChunkDesc *,
-                         const int *, const double *, const RowRec *, const float2 *, const double *,
-                         const double *, const int *, const int *);
+                         const int *, const double *, const float4 *, const double *, const double *, const int *,
+                         const int *);
             if (a.fused) {
                 if (cl) kern = fu ? k_grad_wide<T, Tg::n, true, true, true> : k_grad_wide<T, Tg::n, false, true, true>;
                 else kern = fu ? k_grad_wide<T, Tg::n, true, true, false> : k_grad_wide<T, Tg::n, false, true, false>;
@@ -1182,17 +1252,17 @@ hipError_t launch_reduce(const LaunchArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_grad_scale(void *grad, int esize, int V, const float *scale, int per_sample, const uint8_t *ws,
-                             const WorkspaceLayout &lay, const RowGeom &geom, bool aligned16, hipStream_t stream) {
-    (void)aligned16;
-    const dim3 grid(lay.n_chunks), block(256);
+hipError_t launch_grad_scale(void *grad, int esize, int V, int64_t N, int B, const float *scale, int per_sample,
+                             const uint8_t *ws, const WorkspaceLayout &lay, const RowGeom &geom,
+                             hipStream_t stream) {
+    const int64_t rows_per_block = 4 * (64 / geom.lanes_per_row);
+    const dim3 grid((unsigned)((N + rows_per_block - 1) / rows_per_block)), block(256);
     const SampleDesc *desc = reinterpret_cast<const SampleDesc *>(ws + lay.desc);
-    const ChunkDesc *chunks = reinterpret_cast<const ChunkDesc *>(ws + lay.chunks);
     return with_narrow(esize, geom.vec, geom.lanes_per_row, [&](auto tag) {
         using Tg = decltype(tag);
         using T = typename Tg::type;
-        hipLaunchKernelGGL((k_grad_scale<T, Tg::vec, Tg::n>), grid, block, 0, stream, static_cast<T *>(grad), V,
-                           desc, chunks, scale, per_sample);
+        hipLaunchKernelGGL((k_grad_scale<T, Tg::vec, Tg::n>), grid, block, 0, stream, static_cast<T *>(grad), V, N,
+                           B, desc, scale, per_sample);
         return hipGetLastError();
     });
 }

@@ -137,6 +137,39 @@ def test_schedule_is_longest_first_and_covers_every_row_once(V, dtype):
         assert (seen[i] == 1).all()
 
 
+@pytest.mark.parametrize("V,dtype", [(29, _lib.RNNT_F32), (1024, _lib.RNNT_F32), (4096, _lib.RNNT_F16)])
+def test_diagonal_order_runs_match_the_row_order_runs(V, dtype):
+    # The wide kernels walk each run in anti-diagonal order from its first
+    # node: the runs must have the same sizes as the row-order runs and,
+    # walked node by node, cover every lattice node of every sample once.
+    rng = np.random.default_rng(V + 1)
+    B = 23
+    T = rng.integers(1, 160, size=B).astype(np.int32)
+    U = rng.integers(0, 80, size=B).astype(np.int32)
+    T[0], U[0] = 1, 0
+    T[1], U[1] = 1, 70
+    T[2], U[2] = 150, 0
+    order, rows = _lib.plan_describe(V, dtype, T, U)
+    _, diag = _lib.plan_describe(V, dtype, T, U, diagonal=True)
+    assert len(rows) == len(diag)
+    assert (rows[:, 0] == diag[:, 0]).all() and (rows[:, 2] == diag[:, 3]).all()
+    seen = {i: np.zeros((T[i], U[i] + 1), np.int32) for i in range(B)}
+    for s, n, u, cnt in diag:
+        Ti, Ui = int(T[s]), int(U[s])
+        for _ in range(cnt):
+            t = n - u
+            assert 0 <= u <= Ui and 0 <= t < Ti
+            seen[int(s)][t, u] += 1
+            # next node in anti-diagonal order
+            if u < min(n, Ui):
+                u += 1
+            else:
+                n += 1
+                u = max(0, n - Ti + 1)
+    for i in range(B):
+        assert (seen[i] == 1).all()
+
+
 def test_schedule_chunk_sizes_follow_row_bytes():
     T = np.array([400] * 8, np.int32)
     U = np.array([100] * 8, np.int32)
