@@ -156,6 +156,42 @@ rnnt_status rnnt_grad_scale(void *grad, rnnt_dtype dtype, int64_t N, int32_t V, 
                             const void *workspace, size_t workspace_bytes, rnnt_stream_t stream);
 
 /*
+ * The same loss and gradient for logits in the padded (B, max_T, max_U1, V)
+ * layout that warp-transducer / GPURNNT style pipelines hand over (GPURNNT
+ * API page: activations of shape [B, T, U, V+1], T and U the batch maxima):
+ * node (t, u) of sample i is row (i*max_T + t)*max_U1 + u of a row-major
+ * (B*max_T*max_U1, V) matrix; rows with t >= T_i or u > U_i are padding.
+ *
+ *   max_T, max_U1     the padded extents: T_i <= max_T and U_i + 1 <= max_U1
+ *                     for every sample, else RNNT_INVALID_VALUE.
+ *   logits, grad      device (B*max_T*max_U1, V) of dtype.  Padding rows of
+ *                     logits are never read.  Every element of grad is
+ *                     written: the rows of each lattice as by rnnt_loss_fused,
+ *                     the padding rows with zeros (no zero fill is needed
+ *                     beforehand, unlike GPURNNT's grads).  grad may equal
+ *                     logits exactly; any other overlap is RNNT_INVALID_VALUE.
+ *   everything else   as for rnnt_loss_fused; the workspace size comes from
+ *                     rnnt_loss_padded_workspace_size with the same extents.
+ */
+rnnt_status rnnt_loss_padded_workspace_size(int32_t B, int32_t V, int32_t max_T, int32_t max_U1, rnnt_dtype dtype,
+                                            const int32_t *logit_lengths, const int32_t *target_lengths,
+                                            size_t *workspace_bytes);
+rnnt_status rnnt_loss_padded(const void *logits, rnnt_dtype dtype, int32_t max_T, int32_t max_U1, int32_t V,
+                             const int32_t *targets, int32_t S, const int32_t *logit_lengths,
+                             const int32_t *target_lengths, int32_t B, int64_t blank, float clamp,
+                             int fused_log_softmax, rnnt_reduction reduction, float *loss, float *loss_reduced,
+                             void *grad, void *workspace, size_t workspace_bytes, rnnt_stream_t stream);
+
+/*
+ * rnnt_grad_scale for a gradient written by rnnt_loss_padded (all
+ * B*max_T*max_U1 rows are scaled; padding rows stay zero).
+ */
+rnnt_status rnnt_grad_scale_padded(void *grad, rnnt_dtype dtype, int32_t max_T, int32_t max_U1, int32_t V,
+                                   const int32_t *logit_lengths, const int32_t *target_lengths, int32_t B,
+                                   const float *scale, int per_sample, const void *workspace,
+                                   size_t workspace_bytes, rnnt_stream_t stream);
+
+/*
  * Synchronises `stream`, then copies into *dev_flags the device status word
  * (RNNT_DEV_* bits) of the most recent rnnt_loss_fused call that used
  * `workspace`; every rnnt_loss_fused call clears it when it starts.

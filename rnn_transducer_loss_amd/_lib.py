@@ -24,7 +24,8 @@ RNNT_DEV_LOSS_MISMATCH = 1
 RNNT_DEV_BAD_TARGET = 2
 
 EXPORTS = ("rnnt_loss_fused_workspace_size", "rnnt_loss_fused", "rnnt_grad_scale", "rnnt_loss_fused_check",
-           "rnnt_status_string", "rnnt_plan_describe", "rnnt_timing_enable", "rnnt_timing_read")
+           "rnnt_status_string", "rnnt_plan_describe", "rnnt_timing_enable", "rnnt_timing_read",
+           "rnnt_loss_padded_workspace_size", "rnnt_loss_padded", "rnnt_grad_scale_padded")
 KERNELS = ("rowstats", "alpha_beta", "grad", "reduce")
 
 _lib = None
@@ -59,6 +60,18 @@ def load():
         lib.rnnt_grad_scale.argtypes = [_vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, _i32p, _i32p,
                                         ctypes.c_int32, _vp, ctypes.c_int, _vp, ctypes.c_size_t, _vp]
         lib.rnnt_grad_scale.restype = ctypes.c_int
+        lib.rnnt_loss_padded_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                         ctypes.c_int32, ctypes.c_int, _i32p, _i32p,
+                                                         ctypes.POINTER(ctypes.c_size_t)]
+        lib.rnnt_loss_padded_workspace_size.restype = ctypes.c_int
+        lib.rnnt_loss_padded.argtypes = [_vp, ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp,
+                                         ctypes.c_int32, _i32p, _i32p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                                         ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        lib.rnnt_loss_padded.restype = ctypes.c_int
+        lib.rnnt_grad_scale_padded.argtypes = [_vp, ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                               _i32p, _i32p, ctypes.c_int32, _vp, ctypes.c_int, _vp, ctypes.c_size_t,
+                                               _vp]
+        lib.rnnt_grad_scale_padded.restype = ctypes.c_int
         lib.rnnt_loss_fused_check.argtypes = [_vp, _vp, ctypes.POINTER(ctypes.c_uint32)]
         lib.rnnt_loss_fused_check.restype = ctypes.c_int
         lib.rnnt_plan_describe.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int, _i32p, _i32p, ctypes.c_int32,
@@ -136,6 +149,45 @@ def grad_scale(grad_ptr: int, dtype_code: int, N: int, V: int, logit_lengths, ta
     rc = load().rnnt_grad_scale(grad_ptr or None, dtype_code, N, V, _p(T), _p(U), len(T), scale_ptr or None,
                                 int(bool(per_sample)), ws_ptr or None, ws_bytes, stream or None)
     check(rc, "rnnt_grad_scale")
+
+
+def workspace_size_padded(B: int, V: int, max_T: int, max_U1: int, dtype_code: int, logit_lengths,
+                          target_lengths) -> int:
+    T = host_i32(logit_lengths)
+    U = host_i32(target_lengths)
+    if len(T) != B or len(U) != B:
+        raise ValueError("length vectors must have B entries")
+    out = ctypes.c_size_t()
+    check(load().rnnt_loss_padded_workspace_size(B, V, max_T, max_U1, dtype_code, _p(T), _p(U), ctypes.byref(out)),
+          "rnnt_loss_padded_workspace_size")
+    return int(out.value)
+
+
+def loss_padded(logits_ptr: int, dtype_code: int, max_T: int, max_U1: int, V: int, targets_ptr: int, S: int,
+                logit_lengths, target_lengths, blank: int, clamp: float, fused: bool, reduction: str, loss_ptr: int,
+                loss_reduced_ptr: int, grad_ptr: int, ws_ptr: int, ws_bytes: int, stream: int):
+    T = host_i32(logit_lengths)
+    U = host_i32(target_lengths)
+    B = len(T)
+    if len(U) != B:
+        raise ValueError("length vectors must have B entries")
+    if reduction not in REDUCTIONS:
+        raise ValueError(f"reduction must be one of {sorted(REDUCTIONS)}")
+    rc = load().rnnt_loss_padded(logits_ptr or None, dtype_code, max_T, max_U1, V, targets_ptr or None, S, _p(T),
+                                 _p(U), B, int(blank), float(clamp), int(bool(fused)), REDUCTIONS[reduction],
+                                 loss_ptr or None, loss_reduced_ptr or None, grad_ptr or None, ws_ptr or None,
+                                 ws_bytes, stream or None)
+    check(rc, "rnnt_loss_padded")
+
+
+def grad_scale_padded(grad_ptr: int, dtype_code: int, max_T: int, max_U1: int, V: int, logit_lengths,
+                      target_lengths, scale_ptr: int, per_sample: bool, ws_ptr: int, ws_bytes: int, stream: int):
+    T = host_i32(logit_lengths)
+    U = host_i32(target_lengths)
+    rc = load().rnnt_grad_scale_padded(grad_ptr or None, dtype_code, max_T, max_U1, V, _p(T), _p(U), len(T),
+                                       scale_ptr or None, int(bool(per_sample)), ws_ptr or None, ws_bytes,
+                                       stream or None)
+    check(rc, "rnnt_grad_scale_padded")
 
 
 def device_flags(ws_ptr: int, stream: int) -> int:

@@ -26,6 +26,13 @@ constexpr size_t kAlign = 256;
 constexpr int64_t kCachedTailBytes = 160ll << 20;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Padded (B, max_T, max_U1, V) layout, or packed when max_T == 0.
+struct Padding {
+    int32_t max_T = 0;
+    int32_t max_U1 = 0;
+    bool on() const { return max_T > 0; }
+};
+
 struct Plan {
     std::vector<SampleDesc> desc;
     std::vector<int32_t> order;
@@ -89,15 +96,23 @@ int32_t rows_per_chunk(int64_t N, int32_t V, int esize) {
 }
 
 rnnt_status build_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t *T, const int32_t *U,
-                       Plan &p) {
+                       Plan &p, const Padding &pad = Padding()) {
     rnnt_status st = check_lengths(B, V, T, U);
     if (st != RNNT_SUCCESS) return st;
+    if (pad.on()) {
+        if (pad.max_U1 < 1) return RNNT_INVALID_VALUE;
+        for (int32_t i = 0; i < B; ++i)
+            if (T[i] > pad.max_T || U[i] + 1 > pad.max_U1) return RNNT_INVALID_VALUE;
+        if ((int64_t)B * pad.max_T * pad.max_U1 >= ((int64_t)1 << 62) / std::max(1, V)) return RNNT_INVALID_VALUE;
+    }
     p.desc.resize(B);
     int64_t row = 0, slot = 0, diag = 0, ab = 0;
     p.max_U1 = 1;
     for (int32_t i = 0; i < B; ++i) {
         SampleDesc &d = p.desc[i];
-        d.row_off = row;
+        d.row_off = pad.on() ? (int64_t)i * pad.max_T * pad.max_U1 : row;
+        d.tstride = pad.on() ? pad.max_U1 : U[i] + 1;
+        d.pad = 0;
         d.slot_off = slot;
         d.diag_off = diag;
         d.ab_off = ab;
@@ -244,22 +259,25 @@ struct PlanEntry {
 std::mutex g_plan_mu;
 std::shared_ptr<const PlanEntry> g_plan_cache;
 
-std::vector<int32_t> plan_key(int32_t B, int32_t V, int esize, const int32_t *T, const int32_t *U) {
+std::vector<int32_t> plan_key(int32_t B, int32_t V, int esize, const int32_t *T, const int32_t *U,
+                              const Padding &pad) {
     std::vector<int32_t> k;
-    k.reserve(3 + 2 * (size_t)B);
+    k.reserve(5 + 2 * (size_t)B);
     k.push_back(B);
     k.push_back(V);
     k.push_back(esize);
+    k.push_back(pad.max_T);
+    k.push_back(pad.max_U1);
     k.insert(k.end(), T, T + B);
     k.insert(k.end(), U, U + B);
     return k;
 }
 
 rnnt_status get_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t *T, const int32_t *U,
-                     std::shared_ptr<const PlanEntry> &out) {
+                     std::shared_ptr<const PlanEntry> &out, const Padding &pad = Padding()) {
     rnnt_status st = check_lengths(B, V, T, U);
     if (st != RNNT_SUCCESS) return st;
-    std::vector<int32_t> key = plan_key(B, V, esize, T, U);
+    std::vector<int32_t> key = plan_key(B, V, esize, T, U, pad);
     {
         std::lock_guard<std::mutex> lk(g_plan_mu);
         if (g_plan_cache && g_plan_cache->key == key) out = g_plan_cache;
@@ -267,7 +285,7 @@ rnnt_status get_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t *
     }
     if (!out) {
         auto e = std::make_shared<PlanEntry>();
-        st = build_plan(B, V, -1, esize, T, U, e->plan);
+        st = build_plan(B, V, -1, esize, T, U, e->plan, pad);
         if (st != RNNT_SUCCESS) return st;
         e->key = std::move(key);
         e->packed = pack_plan(e->plan);
@@ -369,34 +387,41 @@ rnnt_status rnnt_plan_describe(int32_t B, int32_t V, rnnt_dtype dtype, const int
     return RNNT_SUCCESS;
 }
 
-rnnt_status rnnt_loss_fused(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V, const int32_t *targets,
-                            int32_t S, const int32_t *logit_lengths, const int32_t *target_lengths, int32_t B,
-                            int64_t blank, float clamp, int fused_log_softmax, rnnt_reduction reduction,
-                            float *loss, float *loss_reduced, void *grad, void *workspace, size_t workspace_bytes,
-                            rnnt_stream_t stream_) {
+}  // extern "C"
+
+namespace rnnt {
+namespace {
+
+// The loss and gradient for the packed layout (pad off, N rows) or the
+// padded (B, max_T, max_U1, V) layout (pad on, N ignored).
+rnnt_status loss_impl(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V, const int32_t *targets, int32_t S,
+                      const int32_t *logit_lengths, const int32_t *target_lengths, int32_t B, int64_t blank,
+                      float clamp, int fused_log_softmax, rnnt_reduction reduction, float *loss, float *loss_reduced,
+                      void *grad, void *workspace, size_t workspace_bytes, hipStream_t stream, const Padding &pad) {
     const int es = esize_of(dtype);
-    if (!es || N < 0 || V < 1 || B < 1) return RNNT_INVALID_VALUE;
+    if (!es || V < 1 || B < 1) return RNNT_INVALID_VALUE;
+    if (pad.on() ? (pad.max_U1 < 1) : (N < 0)) return RNNT_INVALID_VALUE;
     if (reduction != RNNT_REDUCTION_NONE && reduction != RNNT_REDUCTION_MEAN && reduction != RNNT_REDUCTION_SUM)
         return RNNT_INVALID_VALUE;
     if (blank < -(int64_t)V || blank > (int64_t)V - 1) return RNNT_INVALID_VALUE;
     if (!logit_lengths || !target_lengths || !loss || !workspace) return RNNT_INVALID_VALUE;
-    if (N > 0 && !logits) return RNNT_INVALID_VALUE;
+    const int64_t rows = pad.on() ? (int64_t)B * pad.max_T * pad.max_U1 : N;
+    if (rows > 0 && !logits) return RNNT_INVALID_VALUE;
     int32_t maxU = 0;
     for (int32_t i = 0; i < B; ++i) maxU = std::max(maxU, target_lengths[i]);
     if (maxU > 0 && (!targets || S < maxU)) return RNNT_INVALID_VALUE;
     if (S < 0) return RNNT_INVALID_VALUE;
-    const size_t bytes = (size_t)N * (size_t)V * (size_t)es;
+    const size_t bytes = (size_t)rows * (size_t)V * (size_t)es;
     if (grad && grad != logits && bytes > 0 && ranges_overlap(grad, bytes, logits, bytes)) return RNNT_INVALID_VALUE;
     const bool aligned16 = ((int64_t)V * es) % 16 == 0 && ((uintptr_t)logits % 16 == 0) &&
                            (!grad || (uintptr_t)grad % 16 == 0);
     std::shared_ptr<const PlanEntry> e;
-    rnnt_status st = get_plan(B, V, N, es, logit_lengths, target_lengths, e);
+    rnnt_status st = get_plan(B, V, pad.on() ? -1 : N, es, logit_lengths, target_lengths, e, pad);
     if (st != RNNT_SUCCESS) return st;
     const Plan &plan = e->plan;
     if (workspace_bytes < plan.lay.total) return RNNT_WORKSPACE_TOO_SMALL;
     if ((uintptr_t)workspace % kAlign != 0) return RNNT_INVALID_VALUE;
 
-    hipStream_t stream = static_cast<hipStream_t>(stream_);
     const RowGeom geom = row_geometry(V, es, aligned16);
     st = upload(workspace, e->packed, stream);
     if (st != RNNT_SUCCESS) return st;
@@ -405,7 +430,7 @@ rnnt_status rnnt_loss_fused(const void *logits, rnnt_dtype dtype, int64_t N, int
     a.logits = logits;
     a.grad = grad;
     a.esize = es;
-    a.N = N;
+    a.N = rows;
     a.V = V;
     a.B = B;
     a.S = S;
@@ -428,28 +453,96 @@ rnnt_status rnnt_loss_fused(const void *logits, rnnt_dtype dtype, int64_t N, int
     if (timed(1, stream, [&] { return launch_alpha_beta(a, stream); }) != hipSuccess) return RNNT_EXECUTION_FAILED;
     if (grad && plan.lay.n_chunks > 0 && timed(2, stream, [&] { return launch_grad(a, stream); }) != hipSuccess)
         return RNNT_EXECUTION_FAILED;
+    if (grad && pad.on() &&
+        launch_zero_padding(grad, es, V, B, pad.max_T, pad.max_U1, a.ws, plan.lay, geom, stream) != hipSuccess)
+        return RNNT_EXECUTION_FAILED;
     if (reduction != RNNT_REDUCTION_NONE && loss_reduced &&
         timed(3, stream, [&] { return launch_reduce(a, stream); }) != hipSuccess)
         return RNNT_EXECUTION_FAILED;
     return RNNT_SUCCESS;
 }
 
-rnnt_status rnnt_grad_scale(void *grad, rnnt_dtype dtype, int64_t N, int32_t V, const int32_t *logit_lengths,
+rnnt_status grad_scale_impl(void *grad, rnnt_dtype dtype, int64_t N, int32_t V, const int32_t *logit_lengths,
                             const int32_t *target_lengths, int32_t B, const float *scale, int per_sample,
-                            const void *workspace, size_t workspace_bytes, rnnt_stream_t stream_) {
+                            const void *workspace, size_t workspace_bytes, hipStream_t stream, const Padding &pad) {
     const int es = esize_of(dtype);
-    if (!es || !grad || !scale || !workspace || V < 1 || B < 1 || N < 0) return RNNT_INVALID_VALUE;
+    if (!es || !grad || !scale || !workspace || V < 1 || B < 1) return RNNT_INVALID_VALUE;
+    if (pad.on() ? (pad.max_U1 < 1) : (N < 0)) return RNNT_INVALID_VALUE;
     std::shared_ptr<const PlanEntry> e;
-    rnnt_status st = get_plan(B, V, N, es, logit_lengths, target_lengths, e);
+    rnnt_status st = get_plan(B, V, pad.on() ? -1 : N, es, logit_lengths, target_lengths, e, pad);
     if (st != RNNT_SUCCESS) return st;
     const Plan &p = e->plan;
     if (workspace_bytes < p.lay.total) return RNNT_WORKSPACE_TOO_SMALL;
-    if (N == 0) return RNNT_SUCCESS;
+    const int64_t rows = pad.on() ? (int64_t)B * pad.max_T * pad.max_U1 : N;
+    if (rows == 0) return RNNT_SUCCESS;
     const bool aligned16 = ((int64_t)V * es) % 16 == 0 && (uintptr_t)grad % 16 == 0;
-    if (launch_grad_scale(grad, es, V, N, B, scale, per_sample, static_cast<const uint8_t *>(workspace), p.lay,
-                          row_geometry(V, es, aligned16), static_cast<hipStream_t>(stream_)) != hipSuccess)
+    if (launch_grad_scale(grad, es, V, rows, B, scale, per_sample, static_cast<const uint8_t *>(workspace), p.lay,
+                          row_geometry(V, es, aligned16), stream) != hipSuccess)
         return RNNT_EXECUTION_FAILED;
     return RNNT_SUCCESS;
+}
+
+}  // namespace
+}  // namespace rnnt
+
+extern "C" {
+
+rnnt_status rnnt_loss_fused(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V, const int32_t *targets,
+                            int32_t S, const int32_t *logit_lengths, const int32_t *target_lengths, int32_t B,
+                            int64_t blank, float clamp, int fused_log_softmax, rnnt_reduction reduction,
+                            float *loss, float *loss_reduced, void *grad, void *workspace, size_t workspace_bytes,
+                            rnnt_stream_t stream) {
+    return loss_impl(logits, dtype, N, V, targets, S, logit_lengths, target_lengths, B, blank, clamp,
+                     fused_log_softmax, reduction, loss, loss_reduced, grad, workspace, workspace_bytes,
+                     static_cast<hipStream_t>(stream), Padding());
+}
+
+rnnt_status rnnt_loss_padded_workspace_size(int32_t B, int32_t V, int32_t max_T, int32_t max_U1, rnnt_dtype dtype,
+                                            const int32_t *logit_lengths, const int32_t *target_lengths,
+                                            size_t *workspace_bytes) {
+    const int es = esize_of(dtype);
+    if (!es || !workspace_bytes || max_T < 1 || max_U1 < 1) return RNNT_INVALID_VALUE;
+    Padding pad;
+    pad.max_T = max_T;
+    pad.max_U1 = max_U1;
+    std::shared_ptr<const PlanEntry> e;
+    rnnt_status st = get_plan(B, V, -1, es, logit_lengths, target_lengths, e, pad);
+    if (st != RNNT_SUCCESS) return st;
+    *workspace_bytes = e->plan.lay.total;
+    return RNNT_SUCCESS;
+}
+
+rnnt_status rnnt_loss_padded(const void *logits, rnnt_dtype dtype, int32_t max_T, int32_t max_U1, int32_t V,
+                             const int32_t *targets, int32_t S, const int32_t *logit_lengths,
+                             const int32_t *target_lengths, int32_t B, int64_t blank, float clamp,
+                             int fused_log_softmax, rnnt_reduction reduction, float *loss, float *loss_reduced,
+                             void *grad, void *workspace, size_t workspace_bytes, rnnt_stream_t stream) {
+    if (max_T < 1 || max_U1 < 1) return RNNT_INVALID_VALUE;
+    Padding pad;
+    pad.max_T = max_T;
+    pad.max_U1 = max_U1;
+    return loss_impl(logits, dtype, -1, V, targets, S, logit_lengths, target_lengths, B, blank, clamp,
+                     fused_log_softmax, reduction, loss, loss_reduced, grad, workspace, workspace_bytes,
+                     static_cast<hipStream_t>(stream), pad);
+}
+
+rnnt_status rnnt_grad_scale(void *grad, rnnt_dtype dtype, int64_t N, int32_t V, const int32_t *logit_lengths,
+                            const int32_t *target_lengths, int32_t B, const float *scale, int per_sample,
+                            const void *workspace, size_t workspace_bytes, rnnt_stream_t stream) {
+    return grad_scale_impl(grad, dtype, N, V, logit_lengths, target_lengths, B, scale, per_sample, workspace,
+                           workspace_bytes, static_cast<hipStream_t>(stream), Padding());
+}
+
+rnnt_status rnnt_grad_scale_padded(void *grad, rnnt_dtype dtype, int32_t max_T, int32_t max_U1, int32_t V,
+                                   const int32_t *logit_lengths, const int32_t *target_lengths, int32_t B,
+                                   const float *scale, int per_sample, const void *workspace,
+                                   size_t workspace_bytes, rnnt_stream_t stream) {
+    if (max_T < 1 || max_U1 < 1) return RNNT_INVALID_VALUE;
+    Padding pad;
+    pad.max_T = max_T;
+    pad.max_U1 = max_U1;
+    return grad_scale_impl(grad, dtype, -1, V, logit_lengths, target_lengths, B, scale, per_sample, workspace,
+                           workspace_bytes, static_cast<hipStream_t>(stream), pad);
 }
 
 rnnt_status rnnt_timing_enable(int on) {

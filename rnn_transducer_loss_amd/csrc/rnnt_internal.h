@@ -10,8 +10,10 @@
 
 namespace rnnt {
 
-// One sample of the packed batch.  Rows are t-major: packed row
-// row_off + t*(U+1) + u is lattice node (t,u).  The per-node values written
+// One sample of the batch.  Rows are t-major: row row_off + t*tstride + u is
+// lattice node (t,u); tstride = U+1 in the packed layout (samples follow
+// each other without padding) and max_U+1 in the padded (B, max_T, max_U+1,
+// V) layout, where row_off = i*max_T*(max_U+1).  The per-node values written
 // by the row pass live in a skewed layout, one slot per (anti-diagonal
 // n = t+u, u): slot_off + n*(U+1) + u, n in [0, T+U), so every anti-diagonal
 // is contiguous; slots with t = n-u outside [0, T) hold "impossible"
@@ -29,6 +31,8 @@ struct SampleDesc {
     int32_t U;
     int32_t index;  // position of the sample in the batch (targets row)
     int32_t U1p;
+    int32_t tstride;  // rows between (t,u) and (t+1,u)
+    int32_t pad;
 };
 
 // Lattice columns each lane of a 64-wide wavefront owns for a lattice of
@@ -127,6 +131,9 @@ hipError_t launch_reduce(const LaunchArgs &a, hipStream_t stream);
 hipError_t launch_grad_scale(void *grad, int esize, int V, int64_t N, int B, const float *scale, int per_sample,
                              const uint8_t *ws, const WorkspaceLayout &lay, const RowGeom &geom,
                              hipStream_t stream);
+// Padded layout: zero the gradient rows outside every sample's lattice.
+hipError_t launch_zero_padding(void *grad, int esize, int V, int B, int max_T, int max_U1, const uint8_t *ws,
+                               const WorkspaceLayout &lay, const RowGeom &geom, hipStream_t stream);
 
 // Largest lattice width (U+1) the alpha/beta kernel supports.
 constexpr int kMaxU1 = 1024;

@@ -31,6 +31,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "rnnt_internal.h"
@@ -267,6 +268,11 @@ __device__ __forceinline__ void fill_columns(const SampleDesc &d, int t, int u, 
         }
 }
 
+// Row of lattice node (t,u) (packed or padded layout).
+__device__ __forceinline__ int64_t row_of(const SampleDesc &d, int t, int u) {
+    return d.row_off + (int64_t)t * d.tstride + u;
+}
+
 __device__ __forceinline__ int read_label(const SampleDesc &d, int u, int V, int blank,
                                           const int32_t *__restrict__ targets, int S, uint32_t *status) {
     if (u >= d.U) return -1;
@@ -343,7 +349,7 @@ __device__ __forceinline__ void rowstats_wide_chunk(const T *__restrict__ logits
     const int nvec = V / VEC;
     const int U1 = d.U + 1;
     auto load_row = [&](int n, int u, Vec (&x)[NV]) {
-        const T *p = logits + (d.row_off + (int64_t)(n - u) * U1 + u) * (int64_t)V;
+        const T *p = logits + row_of(d, n - u, u) * (int64_t)V;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int vi = i * 64 + lane;
@@ -443,8 +449,9 @@ __global__ __launch_bounds__(256) void k_rowstats_narrow(const T *__restrict__ l
         const int r = base + grp;
         const bool active = r < c.count;
         const int lr = c.row_begin + (active ? r : 0);
-        const int64_t row = d.row_off + lr;
-        const T *p = logits + row * (int64_t)V;
+        const int t = lr / U1;
+        const int u = lr - t * U1;
+        const T *p = logits + row_of(d, t, u) * (int64_t)V;
         float m = kNegInf, s = 0.f;
         if (active) {
             for (int i = sub; i < nvec; i += G) {
@@ -473,8 +480,6 @@ __global__ __launch_bounds__(256) void k_rowstats_narrow(const T *__restrict__ l
             m = mn;
         }
         if (!active) continue;
-        const int t = lr / U1;
-        const int u = lr - t * U1;
         if (sub == 0) {
             const float dn = (m == kNegInf) ? kNegInf : m + log2_fast(s) * kLn2;
             const int y = read_label(d, u, V, blank, targets, S, status);
@@ -515,7 +520,7 @@ __global__ __launch_bounds__(256) void k_gather(const T *__restrict__ logits, in
             u = lr - t * U1;
             if (t == 0 || t == d.T - 1) fill_columns(d, t, u, 0, 1, node, prob);
         }
-        const T *p = logits + (d.row_off + (int64_t)t * U1 + u) * (int64_t)V;
+        const T *p = logits + row_of(d, t, u) * (int64_t)V;
         const int y = read_label(d, u, V, blank, targets, S, status);
         const float lpb = Elem<T>::load1(p + blank);
         const float lpy = (y < 0) ? kNegInf : Elem<T>::load1(p + y);
@@ -924,9 +929,9 @@ __global__ __launch_bounds__(256) void k_grad_wide(const T *logits, T *grad, RNN
     const int U1 = d.U + 1;
     const float cl = clamp * scale;
     using Vec = typename Raw<T>::vec;
-    auto load_row = [&](int lr, Vec (&x)[NV]) {
+    auto load_row = [&](int t, int u, Vec (&x)[NV]) {
         if constexpr (FUSED) {
-            const T *p = logits + (d.row_off + lr) * (int64_t)V;
+            const T *p = logits + row_of(d, t, u) * (int64_t)V;
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
                 const int vi = i * 64 + lane;
@@ -947,8 +952,11 @@ __global__ __launch_bounds__(256) void k_grad_wide(const T *logits, T *grad, RNN
     // the wait counts static.
     auto row_step = [&](Vec (&xc)[NV], Vec (&xn)[NV]) -> bool {
         const bool more = r + 4 < c.count;
-        load_row(c.row_begin + (more ? r + 4 : r), xn);
-        const int64_t row = d.row_off + c.row_begin + r;
+        int tn = t, un = u;
+        advance_node(tn, un, 4, U1);
+        if (more) load_row(tn, un, xn);
+        else load_row(t, u, xn);
+        const int64_t row = row_of(d, t, u);
         const RowTerms rt = row_terms(d, st, t, u, node, alpha, beta, ealpha, ebeta, log2_scale, scale, FUSED);
         T *dst = grad + row * (int64_t)V;
         // The blank and label elements get their flow subtracted in the
@@ -982,12 +990,13 @@ __global__ __launch_bounds__(256) void k_grad_wide(const T *logits, T *grad, RNN
                 store_raw<T, true>(dst + (int64_t)vi * VEC, xc[i]);
             }
         }
-        advance_node(t, u, 4, U1);
+        t = tn;
+        u = un;
         r += 4;
         return more;
     };
     Vec x0[NV], x1[NV], x2[NV];
-    load_row(c.row_begin + r, x0);
+    load_row(t, u, x0);
     while (row_step(x0, x1) && row_step(x1, x2) && row_step(x2, x0)) {
     }
 }
@@ -1013,7 +1022,7 @@ __global__ __launch_bounds__(256) void k_grad_narrow(const T *logits, T *grad, R
         const int lr = c.row_begin + r;
         const int t = lr / U1;
         const int u = lr - t * U1;
-        const int64_t row = d.row_off + lr;
+        const int64_t row = row_of(d, t, u);
         const RowTerms rt = row_terms(d, st, t, u, node, alpha, beta, ealpha, ebeta, log2_scale, scale, FUSED);
         const T *src = logits + row * (int64_t)V;
         T *dst = grad + row * (int64_t)V;
@@ -1078,6 +1087,36 @@ __global__ __launch_bounds__(256) void k_grad_scale(T *grad, int V, int64_t N, i
 #pragma unroll
         for (int e = 0; e < VEC; ++e) x[e] *= f;
         store_n<T, VEC>(p + (int64_t)i * VEC, x);
+    }
+}
+
+// Padded layout: write zeros to every gradient row outside its sample's
+// lattice (t >= T_i or u > U_i), so the padded gradient is fully defined.
+// One row per group of G lanes; rows of a sample are (t, u) for t < max_T,
+// u < max_U1.
+template <typename T, int VEC, int G>
+__global__ __launch_bounds__(256) void k_zero_padding(T *grad, int V, int B, int max_T, int max_U1,
+                                                      const SampleDesc *__restrict__ desc) {
+    constexpr int RPW = 64 / G;
+    const int64_t per_sample = (int64_t)max_T * max_U1;
+    const int64_t rows = per_sample * B;
+    const int lane = threadIdx.x & 63;
+    const int sub = lane & (G - 1);
+    const int nvec = V / VEC;
+    const int64_t step = (int64_t)gridDim.x * 4 * RPW;
+    for (int64_t row = (int64_t)blockIdx.x * (4 * RPW) + (threadIdx.x >> 6) * RPW + lane / G; row < rows;
+         row += step) {
+        const int i = (int)(row / per_sample);
+        const int64_t r = row - (int64_t)i * per_sample;
+        const int t = (int)(r / max_U1);
+        const int u = (int)(r - (int64_t)t * max_U1);
+        const SampleDesc d = desc[i];
+        if (t < d.T && u <= d.U) continue;
+        T *p = grad + row * (int64_t)V;
+        float z[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) z[e] = 0.f;
+        for (int k = sub; k < nvec; k += G) store_n<T, VEC>(p + (int64_t)k * VEC, z);
     }
 }
 
@@ -1263,6 +1302,21 @@ hipError_t launch_grad_scale(void *grad, int esize, int V, int64_t N, int B, con
         using T = typename Tg::type;
         hipLaunchKernelGGL((k_grad_scale<T, Tg::vec, Tg::n>), grid, block, 0, stream, static_cast<T *>(grad), V, N,
                            B, desc, scale, per_sample);
+        return hipGetLastError();
+    });
+}
+
+hipError_t launch_zero_padding(void *grad, int esize, int V, int B, int max_T, int max_U1, const uint8_t *ws,
+                               const WorkspaceLayout &lay, const RowGeom &geom, hipStream_t stream) {
+    const SampleDesc *desc = reinterpret_cast<const SampleDesc *>(ws + lay.desc);
+    const int64_t rows = (int64_t)B * max_T * max_U1;
+    const int64_t per_block = 4 * (64 / geom.lanes_per_row);
+    const unsigned grid = (unsigned)std::min<int64_t>((rows + per_block - 1) / per_block, 1 << 16);
+    return with_narrow(esize, geom.vec, geom.lanes_per_row, [&](auto tag) {
+        using Tg = decltype(tag);
+        using T = typename Tg::type;
+        hipLaunchKernelGGL((k_zero_padding<T, Tg::vec, Tg::n>), dim3(grid), dim3(256), 0, stream,
+                           static_cast<T *>(grad), V, B, max_T, max_U1, desc);
         return hipGetLastError();
     });
 }

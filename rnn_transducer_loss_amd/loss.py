@@ -4,6 +4,9 @@ Signature and semantics follow the rnnt-loss-ascend README (parameter table,
 usage example): ``rnnt_loss(logits, targets, logit_lengths, target_lengths,
 blank=-1, clamp=-1.0, reduction="mean", fused_log_softmax=True)`` on packed
 ``(sum_i T_i*(U_i+1), V)`` logits; ``loss.backward()`` fills ``logits.grad``.
+Padded ``(B, max_T, max_U+1, V)`` logits (the layout of warp-transducer /
+GPURNNT style pipelines) are accepted as well; their gradient is zero at the
+padding positions.
 
 This module only marshals arguments.  The loss, the gradient, the reduction
 and the backward scaling all run in librnnt's kernels on the current HIP
@@ -27,8 +30,9 @@ def _dtype_code(dt: torch.dtype) -> int:
 
 
 def _prepare(logits: torch.Tensor, targets: torch.Tensor):
-    if not isinstance(logits, torch.Tensor) or logits.dim() != 2:
-        raise ValueError("logits must be a 2-D (sum_i T_i*(U_i+1), V) tensor")
+    if not isinstance(logits, torch.Tensor) or logits.dim() not in (2, 4):
+        raise ValueError("logits must be a packed 2-D (sum_i T_i*(U_i+1), V) or a padded 4-D "
+                         "(B, max_T, max_U+1, V) tensor")
     if logits.device.type != "cuda":
         raise ValueError("logits must be on a GPU device")
     if not logits.is_contiguous():
@@ -44,6 +48,9 @@ def _prepare(logits: torch.Tensor, targets: torch.Tensor):
 def workspace_bytes(logits: torch.Tensor, logit_lengths, target_lengths) -> int:
     T = _lib.host_i32(logit_lengths)
     U = _lib.host_i32(target_lengths)
+    if logits.dim() == 4:
+        return _lib.workspace_size_padded(len(T), logits.shape[3], logits.shape[1], logits.shape[2],
+                                          _dtype_code(logits.dtype), T, U)
     return _lib.workspace_size(len(T), logits.shape[1], logits.shape[0], _dtype_code(logits.dtype), T, U)
 
 
@@ -68,8 +75,15 @@ def rnnt_loss_fused(logits: torch.Tensor, targets: torch.Tensor, logit_lengths, 
         raise ValueError("logit_lengths and target_lengths must have the same length")
     dev = logits.device
     code = _dtype_code(logits.dtype)
-    N, V = logits.shape
-    need = _lib.workspace_size(B, V, N, code, T, U)
+    padded = logits.dim() == 4
+    if padded:
+        if logits.shape[0] != B:
+            raise ValueError("padded logits must have one (max_T, max_U+1, V) block per sample")
+        max_T, max_U1, V = logits.shape[1], logits.shape[2], logits.shape[3]
+        need = _lib.workspace_size_padded(B, V, max_T, max_U1, code, T, U)
+    else:
+        N, V = logits.shape
+        need = _lib.workspace_size(B, V, N, code, T, U)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     if loss is None:
@@ -87,10 +101,16 @@ def rnnt_loss_fused(logits: torch.Tensor, targets: torch.Tensor, logit_lengths, 
         grad = None
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        _lib.loss_fused(logits.data_ptr(), code, N, V, tg.data_ptr() if tg.numel() else 0, tg.shape[1], T, U, blank,
-                        clamp, fused_log_softmax, reduction, loss.data_ptr(),
-                        loss_reduced.data_ptr() if reduction != "none" else 0,
-                        grad.data_ptr() if grad is not None else 0, workspace.data_ptr(), workspace.numel(), stream)
+        tgp = tg.data_ptr() if tg.numel() else 0
+        redp = loss_reduced.data_ptr() if reduction != "none" else 0
+        gp = grad.data_ptr() if grad is not None else 0
+        if padded:
+            _lib.loss_padded(logits.data_ptr(), code, max_T, max_U1, V, tgp, tg.shape[1], T, U, blank, clamp,
+                             fused_log_softmax, reduction, loss.data_ptr(), redp, gp, workspace.data_ptr(),
+                             workspace.numel(), stream)
+        else:
+            _lib.loss_fused(logits.data_ptr(), code, N, V, tgp, tg.shape[1], T, U, blank, clamp, fused_log_softmax,
+                            reduction, loss.data_ptr(), redp, gp, workspace.data_ptr(), workspace.numel(), stream)
     return loss, (loss_reduced if reduction != "none" else None), grad, workspace
 
 
@@ -124,15 +144,19 @@ class _RNNTLossFunction(torch.autograd.Function):
         grad, ws = ctx.saved_tensors
         scale = grad_out.detach().to(device=grad.device, dtype=torch.float32).contiguous().reshape(-1)
         with torch.cuda.device(grad.device):
-            _lib.grad_scale(grad.data_ptr(), _dtype_code(dtype), shape[0], shape[1], T, U, scale.data_ptr(),
-                            reduction == "none", ws.data_ptr(), ws.numel(),
-                            torch.cuda.current_stream(grad.device).cuda_stream)
+            stream = torch.cuda.current_stream(grad.device).cuda_stream
+            if len(shape) == 4:
+                _lib.grad_scale_padded(grad.data_ptr(), _dtype_code(dtype), shape[1], shape[2], shape[3], T, U,
+                                       scale.data_ptr(), reduction == "none", ws.data_ptr(), ws.numel(), stream)
+            else:
+                _lib.grad_scale(grad.data_ptr(), _dtype_code(dtype), shape[0], shape[1], T, U, scale.data_ptr(),
+                                reduction == "none", ws.data_ptr(), ws.numel(), stream)
         return grad, None, None, None, None, None, None, None
 
 
 def rnnt_loss(logits: torch.Tensor, targets: torch.Tensor, logit_lengths, target_lengths, blank: int = -1,
               clamp: float = -1.0, reduction: str = "mean", fused_log_softmax: bool = True) -> torch.Tensor:
-    """RNN-T loss over packed logits; differentiable with respect to ``logits``.
+    """RNN-T loss over packed (or padded 4-D) logits; differentiable with respect to ``logits``.
 
     ``blank`` in [-V, V-1] (negative counts from the end), ``clamp > 0`` clips
     each gradient element to [-clamp, clamp], ``reduction`` is none (per

@@ -170,6 +170,19 @@ def test_diagonal_order_runs_match_the_row_order_runs(V, dtype):
         assert (seen[i] == 1).all()
 
 
+def test_padded_workspace_matches_packed_and_checks_extents():
+    T = np.array([12, 9, 30], np.int32)
+    U = np.array([4, 3, 11], np.int32)
+    N = int((T * (U + 1)).sum())
+    packed = _lib.workspace_size(3, 64, N, _lib.RNNT_F32, T, U)
+    padded = _lib.workspace_size_padded(3, 64, 30, 12, _lib.RNNT_F32, T, U)
+    assert packed == padded
+    assert _lib.workspace_size_padded(3, 64, 40, 20, _lib.RNNT_F32, T, U) == packed
+    for max_T, max_U1 in [(29, 12), (30, 11), (0, 12), (30, 0)]:
+        with pytest.raises(ValueError):
+            _lib.workspace_size_padded(3, 64, max_T, max_U1, _lib.RNNT_F32, T, U)
+
+
 def test_schedule_chunk_sizes_follow_row_bytes():
     T = np.array([400] * 8, np.int32)
     U = np.array([100] * 8, np.int32)

@@ -189,6 +189,75 @@ def _custom(Ts, Us, V, **kw):
     return workloads.make_custom(Ts, Us, V, device="cuda", **kw)
 
 
+def _to_padded(w, max_T, max_U1, fill=float("nan")):
+    """The packed logits of w scattered into a (B, max_T, max_U1, V) tensor; padding holds `fill`."""
+    x = torch.full((w.B, max_T, max_U1, w.V), fill, dtype=w.logits.dtype, device=w.logits.device)
+    for i in range(w.B):
+        T, U = int(w.logit_lengths[i]), int(w.target_lengths[i])
+        x[i, :T, :U + 1] = w.logits[w.rows(i)].reshape(T, U + 1, w.V)
+    return x
+
+
+def _padded_rows(w, g, max_T, max_U1):
+    """(valid rows of a padded gradient in packed order, its padding entries)."""
+    valid = torch.zeros((w.B, max_T, max_U1), dtype=torch.bool, device=g.device)
+    parts = []
+    for i in range(w.B):
+        T, U = int(w.logit_lengths[i]), int(w.target_lengths[i])
+        valid[i, :T, :U + 1] = True
+        parts.append(g[i, :T, :U + 1].reshape(-1, w.V))
+    return torch.cat(parts), g[~valid]
+
+
+@pytest.mark.parametrize("V,dtype,fused", [(300, torch.float32, True), (29, torch.float32, True),
+                                           (512, torch.float16, True), (256, torch.float16, False)])
+def test_padded_layout_matches_packed(rl, V, dtype, fused):
+    # padded (B, max_T, max_U+1, V) input: same losses and, row for row, the
+    # same gradient bits as the packed call on the same values; the padding
+    # (NaN here, never read) gets a zero gradient
+    Ts, Us = [40, 17, 33, 1, 25], [9, 0, 14, 6, 3]
+    w = workloads.make_custom(Ts, Us, V, dtype=dtype, std=2.0 if fused else 1.5, fused=fused, reduction="sum",
+                              seed=77, device="cuda", prenormalise=not fused)
+    max_T, max_U1 = max(Ts) + 3, max(Us) + 4
+    xp = _to_padded(w, max_T, max_U1)
+    tg = torch.from_numpy(w.targets).to("cuda")
+    loss_p, red_p, grad_p, ws = rl.rnnt_loss_fused(xp, tg, w.logit_lengths, w.target_lengths, blank=w.blank,
+                                                   reduction="sum", fused_log_softmax=fused)
+    assert rl.device_flags(ws) == 0
+    loss, red, grad, _ = run(rl, w)
+    torch.cuda.synchronize()
+    assert torch.equal(loss_p, loss) and torch.equal(red_p, red)
+    rows, pad = _padded_rows(w, grad_p, max_T, max_U1)
+    assert torch.equal(rows, grad)
+    assert pad.numel() > 0 and bool((pad == 0).all())
+    check_against_oracle(w, loss, grad, "sum", grad_rows="all" if fused else 64)
+
+
+def test_padded_inplace_and_autograd(rl):
+    Ts, Us = [30, 12, 21], [7, 3, 10]
+    w = workloads.make_custom(Ts, Us, 320, std=2.0, reduction="none", seed=78, device="cuda")
+    max_T, max_U1 = 32, 12
+    tg = torch.from_numpy(w.targets).to("cuda")
+    xp = _to_padded(w, max_T, max_U1, fill=0.0)
+    ref_loss, _, ref_grad, _ = rl.rnnt_loss_fused(xp, tg, w.logit_lengths, w.target_lengths, blank=w.blank,
+                                                  reduction="none")
+    y = xp.clone()
+    loss_i, _, grad_i, _ = rl.rnnt_loss_fused(y, tg, w.logit_lengths, w.target_lengths, blank=w.blank,
+                                              reduction="none", inplace=True)
+    torch.cuda.synchronize()
+    assert grad_i.data_ptr() == y.data_ptr()
+    assert torch.equal(loss_i, ref_loss) and torch.equal(y, ref_grad)
+    # autograd with a per-sample upstream gradient (reduction none)
+    x = xp.clone().requires_grad_(True)
+    out = rl.rnnt_loss(x, tg, w.logit_lengths, w.target_lengths, blank=w.blank, reduction="none")
+    up = torch.tensor([0.5, -2.0, 3.0], device="cuda")
+    out.backward(up)
+    torch.cuda.synchronize()
+    want = ref_grad * up.view(-1, 1, 1, 1).to(ref_grad.dtype)
+    assert torch.allclose(x.grad, want, rtol=1e-6, atol=0)
+    assert torch.equal(out.detach(), ref_loss)
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.float16])
 def test_single_path_and_degenerate_lattices(rl, dtype):
     # U = 0 (all-blank lattice), T = 1 (single path), 1x1, and ordinary samples mixed
