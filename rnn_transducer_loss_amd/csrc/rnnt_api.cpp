@@ -119,7 +119,7 @@ rnnt_status build_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t
         d.T = T[i];
         d.U = U[i];
         d.index = i;
-        d.U1p = 64 * cols_per_lane(U[i] + 1);
+        d.U1p = 128 * pairs_per_lane(U[i] + 1);
         row += (int64_t)T[i] * (U[i] + 1);
         slot += ((int64_t)T[i] + U[i]) * (U[i] + 1);
         diag += (int64_t)T[i] + U[i];
@@ -156,7 +156,7 @@ rnnt_status build_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t
     L.order = off;  off = align_up(off + sizeof(int32_t) * B);
     L.chunks = off; off = align_up(off + sizeof(ChunkDesc) * p.chunks.size());
     L.node = off;   off = align_up(off + 4 * sizeof(float) * (size_t)slot);
-    L.prob = off;   off = align_up(off + 2 * sizeof(double) * (size_t)slot);
+    L.prob = off;   off = align_up(off + 2 * sizeof(float) * (size_t)slot);
     L.alpha = off;  off = align_up(off + sizeof(double) * (size_t)ab);
     L.beta = off;   off = align_up(off + sizeof(double) * (size_t)ab);
     L.ealpha = off; off = align_up(off + sizeof(int32_t) * (size_t)(diag + B));

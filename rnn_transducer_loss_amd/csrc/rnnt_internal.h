@@ -19,8 +19,8 @@ namespace rnnt {
 // is contiguous; slots with t = n-u outside [0, T) hold "impossible"
 // weights.  The recursions' outputs (alpha, beta) use the same skewed order
 // with the diagonal padded to a whole number of wavefront column groups:
-// ab_off + n*U1p + u, U1p = 64 * (lattice columns per lane), so every lane of
-// the sweep owns a slot.  Per-diagonal values (the recursions' power-of-two
+// ab_off + n*U1p + u, U1p = 128 * (column pairs per lane), so every lane of
+// the sweep owns a pair of slots.  Per-diagonal values (the recursions' power-of-two
 // exponents) are at diag_off + n / 8.
 struct SampleDesc {
     int64_t row_off;
@@ -35,11 +35,11 @@ struct SampleDesc {
     int32_t pad;
 };
 
-// Lattice columns each lane of a 64-wide wavefront owns for a lattice of
-// width U1: the smallest power of two C with 64*C >= U1.
-inline int cols_per_lane(int U1) {
+// Column pairs each lane of a 64-wide wavefront owns for a lattice of width
+// U1: the smallest power of two C2 with 128*C2 >= U1.
+inline int pairs_per_lane(int U1) {
     int c = 1;
-    while (64 * c < U1) c <<= 1;
+    while (128 * c < U1) c <<= 1;
     return c;
 }
 
@@ -65,7 +65,7 @@ struct ChunkDesc {
 // before `node` is written by the per-call upload.  Per skewed slot:
 //   node  {log P(blank), log P(next label), log-sum-exp of the row (fused) or
 //         0, the next label as int bits (-1 if none)};
-//   prob  {P(blank), P(next label)}, fp32-accurate values held as fp64.
+//   prob  {P(blank), P(next label)} in fp32.
 struct WorkspaceLayout {
     size_t status;      // uint32 status word
     size_t mode;        // int32[B]: 1 = log-domain recursion (set by rowstats)
@@ -73,7 +73,7 @@ struct WorkspaceLayout {
     size_t order;       // int32[B], samples by decreasing cost
     size_t chunks;      // ChunkDesc[n_chunks]
     size_t node;        // float4[S]
-    size_t prob;        // double2[S]
+    size_t prob;        // float2[S]
     size_t alpha;       // double[S_ab], padded diagonals
     size_t beta;        // double[S_ab]
     size_t ealpha;      // int32[D + B]: exponent of alpha per group of 8 diagonals

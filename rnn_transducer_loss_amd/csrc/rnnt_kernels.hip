@@ -17,9 +17,9 @@
 //   reduce                none / mean / sum of the per-sample losses.
 //
 // The recursions run in a scaled probability domain: node values are fp64
-// mantissas with one power-of-two exponent per anti-diagonal, renormalised
-// exactly (by a power of two) every four diagonals.  A step is then one add
-// and two multiplies per node instead of a log-sum-exp.  A sample whose
+// mantissas with one power-of-two exponent per group of eight anti-diagonals,
+// renormalised exactly (by a power of two).  A step is then one multiply and
+// one fused multiply-add per node instead of a log-sum-exp.  A sample whose
 // log-probs leave [-80, 80] (so that an fp32 probability could underflow)
 // is flagged by rowstats and takes a log-domain variant of the same sweep.
 //
@@ -189,41 +189,23 @@ __device__ __forceinline__ int wave_max_i(int v) {
     return __builtin_amdgcn_readlane(v, 63);
 }
 
-// fp64 lane shifts across the wave: lane l receives lane l-1 (up) or l+1
-// (down); the lane at the wave edge receives `edge`.
-__device__ __forceinline__ double shift_up(double x, double edge) {
-    const int lo = __builtin_amdgcn_update_dpp(__double2loint(edge), __double2loint(x), 0x138, 0xf, 0xf, false);
-    const int hi = __builtin_amdgcn_update_dpp(__double2hiint(edge), __double2hiint(x), 0x138, 0xf, 0xf, false);
-    return __hiloint2double(hi, lo);
-}
-__device__ __forceinline__ double shift_down(double x, double edge) {
-    const int lo = __builtin_amdgcn_update_dpp(__double2loint(edge), __double2loint(x), 0x130, 0xf, 0xf, false);
-    const int hi = __builtin_amdgcn_update_dpp(__double2hiint(edge), __double2hiint(x), 0x130, 0xf, 0xf, false);
-    return __hiloint2double(hi, lo);
-}
-__device__ __forceinline__ double read_lane_d(double x, int lane) {
-    const int lo = __builtin_amdgcn_readlane(__double2loint(x), lane);
-    const int hi = __builtin_amdgcn_readlane(__double2hiint(x), lane);
-    return __hiloint2double(hi, lo);
-}
-
 // ---------------------------------------------------- row statistics output
 // Writes what the recursions and the gradient need about node (t,u), at its
 // skewed slot: node = {log P(blank), log P(y_{u+1}), log-sum-exp of the row
-// (fused) or 0, the label (-1 if none)} and prob = the two probabilities
-// (fp32-accurate, held as fp64).  The blank edge leaving t = T-1 below u = U
+// (fused) or 0, the label (-1 if none)} and prob = the two probabilities in
+// fp32.  The blank edge leaving t = T-1 below u = U
 // leaves the lattice and the label edge at u = U does not exist, so both are
 // stored as impossible.  The wide kernel calls it from every lane with
 // wave-uniform values (the stores are then unconditional and the compiler's
 // wait counts stay exact); the others from one lane per row.
 __device__ __forceinline__ void emit_node(const SampleDesc &d, int t, int u, float dn, int y, float lpb, float lpy,
-                                          float4 *__restrict__ node, double2 *__restrict__ prob,
+                                          float4 *__restrict__ node, float2 *__restrict__ prob,
                                           int *__restrict__ mode) {
     if (t == d.T - 1 && u < d.U) lpb = kNegInf;
     if (u == d.U) lpy = kNegInf;
     const int64_t slot = d.slot_off + (int64_t)(t + u) * (d.U + 1) + u;
     node[slot] = make_float4(lpb, lpy, dn, __int_as_float(y));
-    prob[slot] = make_double2((double)prob_of(lpb), (double)prob_of(lpy));
+    prob[slot] = make_float2(prob_of(lpb), prob_of(lpy));
     const bool wide = (lpb != kNegInf && fabsf(lpb) > kProbRange) || (lpy != kNegInf && fabsf(lpy) > kProbRange);
     if (wide) atomicOr(&mode[d.index], 1);
 }
@@ -232,18 +214,18 @@ __device__ __forceinline__ void emit_node(const SampleDesc &d, int t, int u, flo
 // weights, so the recursions read whole diagonals without masks.  `lane`
 // of `nl` cooperating threads.
 __device__ __forceinline__ void fill_slots(const SampleDesc &d, int n, int u0, int u1, int lane, int nl,
-                                           float4 *__restrict__ node, double2 *__restrict__ prob) {
+                                           float4 *__restrict__ node, float2 *__restrict__ prob) {
     const int64_t base = d.slot_off + (int64_t)n * (d.U + 1);
     for (int u = u0 + lane; u < u1; u += nl) {
         node[base + u] = make_float4(kNegInf, kNegInf, 0.f, __int_as_float(-1));
-        prob[base + u] = make_double2(0.0, 0.0);
+        prob[base + u] = make_float2(0.f, 0.f);
     }
 }
 
 // Diagonal order: the first node of diagonal n (u = max(0, n-T+1)) fills the
 // slots below it (t >= T), the last (u = min(n, U)) those above it (t < 0).
 __device__ __forceinline__ void fill_diagonal_ends(const SampleDesc &d, int n, int u, int lane, int nl,
-                                                   float4 *__restrict__ node, double2 *__restrict__ prob) {
+                                                   float4 *__restrict__ node, float2 *__restrict__ prob) {
     const int lo = max(0, n - d.T + 1), hi = min(n, d.U);
     if (u == lo && lo > 0) fill_slots(d, n, 0, lo, lane, nl, node, prob);
     if (u == hi && hi < d.U) fill_slots(d, n, hi + 1, d.U + 1, lane, nl, node, prob);
@@ -252,19 +234,19 @@ __device__ __forceinline__ void fill_diagonal_ends(const SampleDesc &d, int n, i
 // Row order: row (0,u) fills column u of the diagonals n < u (t < 0), row
 // (T-1,u) column u of the diagonals n >= T+u (t >= T).
 __device__ __forceinline__ void fill_columns(const SampleDesc &d, int t, int u, int lane, int nl,
-                                             float4 *__restrict__ node, double2 *__restrict__ prob) {
+                                             float4 *__restrict__ node, float2 *__restrict__ prob) {
     const int U1 = d.U + 1;
     if (t == 0)
         for (int n = lane; n < u; n += nl) {
             const int64_t s = d.slot_off + (int64_t)n * U1 + u;
             node[s] = make_float4(kNegInf, kNegInf, 0.f, __int_as_float(-1));
-            prob[s] = make_double2(0.0, 0.0);
+            prob[s] = make_float2(0.f, 0.f);
         }
     if (t == d.T - 1)
         for (int n = d.T + u + lane; n < d.T + d.U; n += nl) {
             const int64_t s = d.slot_off + (int64_t)n * U1 + u;
             node[s] = make_float4(kNegInf, kNegInf, 0.f, __int_as_float(-1));
-            prob[s] = make_double2(0.0, 0.0);
+            prob[s] = make_float2(0.f, 0.f);
         }
 }
 
@@ -339,7 +321,7 @@ template <typename T, int NV, bool FULL, bool NT>
 __device__ __forceinline__ void rowstats_wide_chunk(const T *__restrict__ logits, int V, int blank,
                                                     const SampleDesc &d, const ChunkDesc &c,
                                                     const int32_t *__restrict__ targets, int S,
-                                                    float4 *__restrict__ node, double2 *__restrict__ prob,
+                                                    float4 *__restrict__ node, float2 *__restrict__ prob,
                                                     int *__restrict__ mode, uint32_t *status) {
     constexpr int VEC = Raw<T>::kVec;
     using Vec = typename Raw<T>::vec;
@@ -416,7 +398,7 @@ __global__ __launch_bounds__(256) void k_rowstats_wide(const T *__restrict__ log
                                                        const SampleDesc *__restrict__ desc,
                                                        const ChunkDesc *__restrict__ chunks, int first_cached,
                                                        const int32_t *__restrict__ targets, int S,
-                                                       float4 *__restrict__ node, double2 *__restrict__ prob,
+                                                       float4 *__restrict__ node, float2 *__restrict__ prob,
                                                        int *__restrict__ mode, uint32_t *status) {
     const ChunkDesc c = chunks[blockIdx.x];
     const SampleDesc d = desc[c.sample];
@@ -434,7 +416,7 @@ __global__ __launch_bounds__(256) void k_rowstats_narrow(const T *__restrict__ l
                                                          const SampleDesc *__restrict__ desc,
                                                          const ChunkDesc *__restrict__ chunks,
                                                          const int32_t *__restrict__ targets, int S,
-                                                         float4 *__restrict__ node, double2 *__restrict__ prob,
+                                                         float4 *__restrict__ node, float2 *__restrict__ prob,
                                                          int *__restrict__ mode, uint32_t *status) {
     constexpr int RPW = 64 / G;
     const ChunkDesc c = chunks[blockIdx.x];
@@ -501,7 +483,7 @@ __global__ __launch_bounds__(256) void k_gather(const T *__restrict__ logits, in
                                                 const SampleDesc *__restrict__ desc,
                                                 const ChunkDesc *__restrict__ chunks,
                                                 const int32_t *__restrict__ targets, int S,
-                                                float4 *__restrict__ node, double2 *__restrict__ prob,
+                                                float4 *__restrict__ node, float2 *__restrict__ prob,
                                                 int *__restrict__ mode, uint32_t *status) {
     const ChunkDesc c = chunks[blockIdx.x];
     const SampleDesc d = desc[c.sample];
@@ -529,21 +511,26 @@ __global__ __launch_bounds__(256) void k_gather(const T *__restrict__ logits, in
 }
 
 // ----------------------------------------------------- K2: alpha/beta sweeps
-// Lane l owns lattice columns u = l + 64*j, j < C.  Lanes past the lattice
-// width read column U instead: their values start at zero (-inf in the log
-// domain) and only ever receive zero, because the label edge leaving column U
-// is stored as impossible.  Every slot of a diagonal holds weights (the row
-// pass fills those outside the lattice with "impossible"), so no step needs
-// a mask.  The node inputs of PF diagonals are loaded one
-// block ahead into one of two register rings used in turn; each block's
-// outputs are stored after its compute, so a wait for a block's inputs never
-// covers the previous block's stores.
+// Lane l owns the column pairs u = 128*g + 2*l + {0, 1}, g < C2 (U1p = 128*C2
+// padded columns), so a lane's two columns move in one 16-byte access: the
+// fp32 probabilities {P(blank), P(label)} of both going in, their two fp64
+// values going out.  Only the first column of a pair needs a value from
+// another lane (the second column of lane l-1, or of lane 63 of the previous
+// group for lane 0): one wave rotation per group and a select on lane 0.
+// Diagonal n is read and written through buffer resources based at the
+// diagonal, whose range check returns zero for the columns past U: those
+// columns start at zero (-inf in the log domain) and only ever receive zero,
+// because the label edge leaving column U is stored as impossible.  Every
+// slot of a diagonal up to U holds weights (the row pass fills those outside
+// the lattice with "impossible"), so no step needs a mask.  The inputs of PF
+// diagonals are loaded one block ahead into one of two register rings used
+// in turn.
 //
 // Probability domain: node value = mantissa * 2^E, one exponent E per group
-// of eight diagonals.  Forward step:
-//   a(n,u) = a(n-1,u) * pb(n-1,u) + a(n-1,u-1) * py(n-1,u-1)
-// carried as the two messages leaving diagonal n-1 (the recursion starts
-// from a blank message of one into (0,0)).  Backward step:
+// of eight diagonals.  Forward step, from diagonal n to n+1:
+//   a(n+1,u) = a(n,u) * pb(n,u) + a(n,u-1) * py(n,u-1)
+// from a = 1 at (0,0); one step past the last diagonal leaves
+// P(y|x) = a(T-1,U) * pb(T-1,U) in column U.  Backward step:
 //   b(n,u) = b(n+1,u) * pb(n,u) + b(n+1,u+1) * py(n,u)
 // from b = 1 at (T-1+1, U), the empty suffix after the final blank.  Every
 // eighth diagonal is rescaled by 2^-e so its largest value is in [1, 2):
@@ -555,21 +542,32 @@ __global__ __launch_bounds__(256) void k_gather(const T *__restrict__ logits, in
 // Log domain (fallback): the same recursions in log2 units with
 // log2(2^a + 2^b) in place of the sum and log2-prob addition in place of the
 // product; all exponents are 0.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+// Raw (unstrided) buffer resource over `bytes` bytes from `base`: a load
+// past `bytes` returns zero without touching memory, a store there is
+// dropped.
+__device__ __forceinline__ Rsrc buffer_at(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 struct ProbDomain {
     static constexpr bool kLog = false;
-    using W = double2;                       // prob[] slot: {P(blank), P(label)}
-    static constexpr uint32_t kStride = 16;  // bytes per slot
+    static constexpr uint32_t kSlot = 8;  // prob[] slot: float2 {P(blank), P(label)}
     __device__ static double zero() { return 0.0; }
     __device__ static double one() { return 1.0; }
     __device__ static double combine(double a, double b) { return a + b; }
-    __device__ static double edge(double a, double w) { return a * w; }
-    __device__ static double wx(const W &w) { return w.x; }
-    __device__ static double wy(const W &w) { return w.y; }
+    __device__ static double edge(double a, float w) { return a * (double)w; }
+    // The four weights of the pair at byte offset voff[0] (one load).
+    __device__ static float4 load(Rsrc r, const uint32_t (&voff)[2]) {
+        return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff[0], 0, 0));
+    }
 };
 struct LogDomain {
     static constexpr bool kLog = true;
-    using W = float2;                        // first half of the node[] slot: {log P(blank), log P(label)}
-    static constexpr uint32_t kStride = 16;
+    static constexpr uint32_t kSlot = 16;  // node[] slot: float4, of which {log P(blank), log P(label)}
     __device__ static double zero() { return kNegInfD; }
     __device__ static double one() { return 0.0; }
     __device__ static double combine(double a, double b) {
@@ -578,205 +576,253 @@ struct LogDomain {
         const float l = log2_fast(1.0f + exp2_fast((float)(mn - mx)));
         return (mn == kNegInfD) ? mx : mx + (double)l;
     }
-    __device__ static double edge(double a, double lpv) { return a + lpv * kLog2eD; }
-    __device__ static double wx(const W &w) { return (double)w.x; }
-    __device__ static double wy(const W &w) { return (double)w.y; }
+    __device__ static double edge(double a, float lpv) { return a + (double)lpv * kLog2eD; }
+    // The first eight bytes of the two slots at voff[0], voff[1] (each clamped
+    // to column U by the caller: a log-prob of 0 would not be impossible).
+    __device__ static float4 load(Rsrc r, const uint32_t (&voff)[2]) {
+        const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, voff[0], 0, 0);
+        const u32x2 y = __builtin_amdgcn_raw_buffer_load_b64(r, voff[1], 0, 0);
+        return make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(y[0]),
+                           __uint_as_float(y[1]));
+    }
 };
 
-template <int C> __device__ __forceinline__ int renorm(double (&a)[C]) {
+// fp64 wave rotations: lane l receives lane l-1 (lane 0: lane 63), or lane
+// l+1 (lane 63: lane 0).
+__device__ __forceinline__ double rotate_up(double x) {
+    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(x), 0x13c, 0xf, 0xf, true);
+    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(x), 0x13c, 0xf, 0xf, true);
+    return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double rotate_down(double x) {
+    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(x), 0x134, 0xf, 0xf, true);
+    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(x), 0x134, 0xf, 0xf, true);
+    return __hiloint2double(hi, lo);
+}
+
+template <int C2> __device__ __forceinline__ int renorm(double (&a0)[C2], double (&a1)[C2]) {
     int eb = 0;
 #pragma unroll
-    for (int j = 0; j < C; ++j) eb = max(eb, (__double2hiint(a[j]) >> 20) & 0x7ff);
+    for (int g = 0; g < C2; ++g) {
+        eb = max(eb, (__double2hiint(a0[g]) >> 20) & 0x7ff);
+        eb = max(eb, (__double2hiint(a1[g]) >> 20) & 0x7ff);
+    }
     eb = wave_max_i(eb);
     const int sh = eb - 1023;
 #pragma unroll
-    for (int j = 0; j < C; ++j) a[j] = __builtin_amdgcn_ldexp(a[j], -sh);
+    for (int g = 0; g < C2; ++g) {
+        a0[g] = __builtin_amdgcn_ldexp(a0[g], -sh);
+        a1[g] = __builtin_amdgcn_ldexp(a1[g], -sh);
+    }
     return sh;
 }
 
-template <typename W, int C, int PF> struct Ring {
-    W v[PF][C];
+template <int C2, int PF> struct Ring {
+    float4 v[PF][C2];
 };
 
-// Diagonals n0, n0+step, ... (clamped into [0, nd)) of a sample's slots
-// (w: the sample's first slot, `stride` bytes per slot).  voff[j]: the
-// lane's byte offset inside a diagonal (column min(u, U)), so each load is a
-// scalar diagonal base plus a fixed 32-bit lane offset.
-template <typename W, int C, int PF>
-__device__ __forceinline__ void load_block(Ring<W, C, PF> &r, const char *__restrict__ w, int64_t diag_bytes,
-                                           const uint32_t (&voff)[C], int n0, int step, int nd) {
+// Where a sweep reads and writes: the sample's first weight slot and first
+// output slot, the byte sizes of one diagonal of each, and the lane's byte
+// offsets inside a diagonal.
+template <typename D, int C2> struct SweepIO {
+    const char *w;
+    char *out;
+    uint32_t w_bytes;    // U1 * kSlot
+    uint32_t out_bytes;  // U1p * 8
+    uint32_t win[C2][2];
+    uint32_t wout[C2];
+
+    __device__ SweepIO(const char *w_, double *out_, int U) : w(w_), out(reinterpret_cast<char *>(out_)) {
+        const int lane = threadIdx.x & 63;
+        const uint32_t U1 = (uint32_t)U + 1;
+        w_bytes = U1 * D::kSlot;
+        out_bytes = 128u * C2 * 8u;
 #pragma unroll
-    for (int p = 0; p < PF; ++p) {
-        const int n = min(max(n0 + step * p, 0), nd - 1);
-        const char *row = w + (int64_t)n * diag_bytes;
+        for (int g = 0; g < C2; ++g) {
+            const uint32_t c0 = 128u * g + 2u * lane;
+            if constexpr (D::kLog) {
+                win[g][0] = min(c0, (uint32_t)U) * D::kSlot;
+                win[g][1] = min(c0 + 1, (uint32_t)U) * D::kSlot;
+            } else {
+                win[g][0] = min(c0, U1) * D::kSlot;  // past U: zeros from the range check
+                win[g][1] = 0;
+            }
+            wout[g] = c0 * 8u;
+        }
+    }
+    __device__ void load(float4 (&r)[C2], int n) const {
+        const Rsrc rs = buffer_at(w + (int64_t)n * w_bytes, w_bytes);
 #pragma unroll
-        for (int j = 0; j < C; ++j) r.v[p][j] = *reinterpret_cast<const W *>(row + voff[j]);
+        for (int g = 0; g < C2; ++g) r[g] = D::load(rs, win[g]);
+    }
+    __device__ void store(int n, const double (&a0)[C2], const double (&a1)[C2]) const {
+        const Rsrc rs = buffer_at(out + (int64_t)n * out_bytes, out_bytes);
+#pragma unroll
+        for (int g = 0; g < C2; ++g) {
+            const u32x4 v = {(uint32_t)__double2loint(a0[g]), (uint32_t)__double2hiint(a0[g]),
+                             (uint32_t)__double2loint(a1[g]), (uint32_t)__double2hiint(a1[g])};
+            __builtin_amdgcn_raw_buffer_store_b128(v, rs, wout[g], 0, 0);
+        }
+    }
+};
+
+// Diagonals n0, n0+step, ... (clamped into [0, nd)) into ring r.
+template <typename D, int C2, int PF>
+__device__ __forceinline__ void load_block(Ring<C2, PF> &r, const SweepIO<D, C2> &io, int n0, int step, int nd) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) io.load(r.v[p], min(max(n0 + step * p, 0), nd - 1));
+}
+
+// One forward step: the values of diagonal n (a0, a1, already stored) and its
+// weights w give those of diagonal n+1.
+template <typename D, int C2>
+__device__ __forceinline__ void forward_step(double (&a0)[C2], double (&a1)[C2], const float4 (&w)[C2],
+                                             bool lane0) {
+    double my0[C2], r1[C2];
+#pragma unroll
+    for (int g = 0; g < C2; ++g) {
+        my0[g] = D::edge(a0[g], w[g].y);
+        r1[g] = rotate_up(D::edge(a1[g], w[g].w));
+    }
+#pragma unroll
+    for (int g = 0; g < C2; ++g) {
+        const double left = lane0 ? (g > 0 ? r1[g > 0 ? g - 1 : 0] : D::zero()) : r1[g];
+        a0[g] = D::combine(D::edge(a0[g], w[g].x), left);
+        a1[g] = D::combine(D::edge(a1[g], w[g].z), my0[g]);
     }
 }
 
-template <int C> __device__ __forceinline__ void lane_offsets(uint32_t (&voff)[C], int U, uint32_t esize) {
-    const int lane = threadIdx.x & 63;
+// One backward step: the values of diagonal n+1 (b0, b1) and the weights w
+// of diagonal n give those of diagonal n.
+template <typename D, int C2>
+__device__ __forceinline__ void backward_step(double (&b0)[C2], double (&b1)[C2], const float4 (&w)[C2],
+                                              bool lane63) {
+    double l0[C2];
 #pragma unroll
-    for (int j = 0; j < C; ++j) voff[j] = (uint32_t)min(lane + 64 * j, U) * esize;
+    for (int g = 0; g < C2; ++g) l0[g] = rotate_down(b0[g]);
+#pragma unroll
+    for (int g = 0; g < C2; ++g) {
+        const double right = lane63 ? (g + 1 < C2 ? l0[g + 1 < C2 ? g + 1 : g] : D::zero()) : l0[g];
+        const double n0 = D::combine(D::edge(b0[g], w[g].x), D::edge(b1[g], w[g].y));
+        b1[g] = D::combine(D::edge(b1[g], w[g].z), D::edge(right, w[g].w));
+        b0[g] = n0;
+    }
 }
 
-// Value of lane l-1 (lane 0: `edge` of the previous column group, or zero).
-template <typename D, int C>
-__device__ __forceinline__ double from_left(const double (&x)[C], int j) {
-    if (j == 0) {
-        if constexpr (D::kLog) return shift_up(x[0], kNegInfD);
-        const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x[0]), 0x138, 0xf, 0xf, true);
-        const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x[0]), 0x138, 0xf, 0xf, true);
-        return __hiloint2double(hi, lo);
-    }
-    return shift_up(x[j], read_lane_d(x[j > 0 ? j - 1 : 0], 63));
-}
-// Value of lane l+1 (lane 63: lane 0 of the next column group, or zero).
-template <typename D, int C>
-__device__ __forceinline__ double from_right(const double (&x)[C], int j) {
-    if (j == C - 1) {
-        if constexpr (D::kLog) return shift_down(x[C - 1], kNegInfD);
-        const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x[C - 1]), 0x130, 0xf, 0xf, true);
-        const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x[C - 1]), 0x130, 0xf, 0xf, true);
-        return __hiloint2double(hi, lo);
-    }
-    return shift_down(x[j], read_lane_d(x[j + 1 < C ? j + 1 : j], 0));
-}
-
-// One block of PF forward diagonals n0 .. n0+PF-1 from ring r.  GUARD: the
-// block may run past the last diagonal.  Each diagonal is stored as soon as
-// it is computed: the other ring's loads were issued before these stores,
-// so waiting for them never waits for the stores.
-template <typename D, int C, int PF, bool GUARD>
-__device__ __forceinline__ void forward_block(const Ring<typename D::W, C, PF> &r, int n0, int nd, int lane,
-                                              double (&mb)[C], double (&my)[C], int &E, double *__restrict__ out,
+// One block of PF forward diagonals n0 .. n0+PF-1 from ring r: each
+// diagonal is rescaled (every eighth), stored, then stepped.  GUARD: the
+// block may run past the last diagonal.
+template <typename D, int C2, int PF, bool GUARD>
+__device__ __forceinline__ void forward_block(const Ring<C2, PF> &r, const SweepIO<D, C2> &io, int n0, int nd,
+                                              bool lane0, double (&a0)[C2], double (&a1)[C2], int &E,
                                               int *__restrict__ eout) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
         const int n = n0 + p;
         if (!GUARD || n < nd) {
-            double a[C];
-#pragma unroll
-            for (int j = 0; j < C; ++j) a[j] = D::combine(mb[j], from_left<D, C>(my, j));
-            // n0 is a multiple of PF, so for PF % 8 == 0 this test is static
-            if (!D::kLog && (((PF % 8 == 0) ? p : n) & 7) == 7) {
-                E += renorm<C>(a);
+            if (!D::kLog && (n & 7) == 7) {
+                E += renorm<C2>(a0, a1);
                 eout[(n + 1) >> 3] = E;  // uniform value and address
             }
-            // padded diagonal: every lane owns a slot (uniform base + lane)
-            double *o = out + (int64_t)n * (64 * C);
-#pragma unroll
-            for (int j = 0; j < C; ++j) {
-                o[lane + 64 * j] = a[j];
-                mb[j] = D::edge(a[j], D::wx(r.v[p][j]));
-                my[j] = D::edge(a[j], D::wy(r.v[p][j]));
-            }
+            io.store(n, a0, a1);
+            forward_step<D, C2>(a0, a1, r.v[p], lane0);
         }
     }
 }
 
-template <typename D, int C, int PF>
+template <typename D, int C2, int PF>
 __device__ void sweep_forward(const SampleDesc &d, const char *__restrict__ w, double *__restrict__ out,
                               int *__restrict__ eout, double *log2z) {
-    using W = typename D::W;
     const int lane = threadIdx.x & 63;
-    const int U = d.U, U1 = U + 1, nd = d.T + U;
-    // messages into diagonal 0: a blank message of one into (0,0)
-    double mb[C], my[C];
+    const bool lane0 = lane == 0;
+    const int U = d.U, nd = d.T + U;
+    double a0[C2], a1[C2];
 #pragma unroll
-    for (int j = 0; j < C; ++j) {
-        mb[j] = (j == 0 && lane == 0) ? D::one() : D::zero();
-        my[j] = D::zero();
+    for (int g = 0; g < C2; ++g) {
+        a0[g] = (g == 0 && lane0) ? D::one() : D::zero();
+        a1[g] = D::zero();
     }
     int E = 0;
     if (lane == 0) eout[0] = 0;
-    uint32_t voff[C];
-    lane_offsets<C>(voff, U, D::kStride);
-    const int64_t diag_bytes = (int64_t)U1 * D::kStride;
-    Ring<W, C, PF> ra, rb;
-    load_block<W, C, PF>(ra, w, diag_bytes, voff, 0, 1, nd);
+    const SweepIO<D, C2> io(w, out, U);
+    Ring<C2, PF> ra, rb;
+    load_block<D, C2, PF>(ra, io, 0, 1, nd);
     int n0 = 0;
     for (; n0 + 2 * PF <= nd; n0 += 2 * PF) {
-        load_block<W, C, PF>(rb, w, diag_bytes, voff, n0 + PF, 1, nd);
-        forward_block<D, C, PF, false>(ra, n0, nd, lane, mb, my, E, out, eout);
-        load_block<W, C, PF>(ra, w, diag_bytes, voff, n0 + 2 * PF, 1, nd);
-        forward_block<D, C, PF, false>(rb, n0 + PF, nd, lane, mb, my, E, out, eout);
+        load_block<D, C2, PF>(rb, io, n0 + PF, 1, nd);
+        forward_block<D, C2, PF, false>(ra, io, n0, nd, lane0, a0, a1, E, eout);
+        load_block<D, C2, PF>(ra, io, n0 + 2 * PF, 1, nd);
+        forward_block<D, C2, PF, false>(rb, io, n0 + PF, nd, lane0, a0, a1, E, eout);
     }
     if (n0 < nd) {
-        load_block<W, C, PF>(rb, w, diag_bytes, voff, n0 + PF, 1, nd);
-        forward_block<D, C, PF, true>(ra, n0, nd, lane, mb, my, E, out, eout);
-        if (n0 + PF < nd) forward_block<D, C, PF, true>(rb, n0 + PF, nd, lane, mb, my, E, out, eout);
+        load_block<D, C2, PF>(rb, io, n0 + PF, 1, nd);
+        forward_block<D, C2, PF, true>(ra, io, n0, nd, lane0, a0, a1, E, eout);
+        if (n0 + PF < nd) forward_block<D, C2, PF, true>(rb, io, n0 + PF, nd, lane0, a0, a1, E, eout);
     }
-    // The last diagonal holds only (T-1, U); its blank message is P(y|x).
-    double v = mb[0];
+    // One step past the last diagonal: column U holds P(y|x).
+    const int gU = U >> 7;
+    double v = 0.0;
 #pragma unroll
-    for (int j = 1; j < C; ++j) v = (j == (U >> 6)) ? mb[j] : v;
-    const double z = __shfl(v, U & 63, 64);
+    for (int g = 0; g < C2; ++g) v = (g == gU) ? ((U & 1) ? a1[g] : a0[g]) : v;
+    const double z = __shfl(v, (U & 127) >> 1, 64);
     if (lane == 0) *log2z = D::kLog ? z : log2_d(z) + (double)E;
 }
 
 // One block of PF backward diagonals n0, n0-1, ..., n0-PF+1 from ring r
 // (nd-1-n0 is a multiple of PF).
-template <typename D, int C, int PF, bool GUARD>
-__device__ __forceinline__ void backward_block(const Ring<typename D::W, C, PF> &r, int n0, int nd, int lane,
-                                               double (&pv)[C], int &E, double *__restrict__ out,
+template <typename D, int C2, int PF, bool GUARD>
+__device__ __forceinline__ void backward_block(const Ring<C2, PF> &r, const SweepIO<D, C2> &io, int n0, int nd,
+                                               bool lane63, double (&b0)[C2], double (&b1)[C2], int &E,
                                                int *__restrict__ eout) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
         const int n = n0 - p;
         if (!GUARD || n >= 0) {
-            double b[C];
-#pragma unroll
-            for (int j = 0; j < C; ++j)
-                b[j] = D::combine(D::edge(pv[j], D::wx(r.v[p][j])),
-                                  D::edge(from_right<D, C>(pv, j), D::wy(r.v[p][j])));
-            if (!D::kLog && (((PF % 8 == 0) ? p : (nd - 1 - n)) & 7) == 7) {
-                E += renorm<C>(b);
+            backward_step<D, C2>(b0, b1, r.v[p], lane63);
+            if (!D::kLog && ((nd - 1 - n) & 7) == 7) {
+                E += renorm<C2>(b0, b1);
                 eout[(nd - n) >> 3] = E;  // uniform value and address
             }
-            double *o = out + (int64_t)n * (64 * C);
-#pragma unroll
-            for (int j = 0; j < C; ++j) {
-                o[lane + 64 * j] = b[j];
-                pv[j] = b[j];
-            }
+            io.store(n, b0, b1);
         }
     }
 }
 
-template <typename D, int C, int PF>
+template <typename D, int C2, int PF>
 __device__ void sweep_backward(const SampleDesc &d, const char *__restrict__ w, double *__restrict__ out,
                                int *__restrict__ eout, double *log2z) {
-    using W = typename D::W;
     const int lane = threadIdx.x & 63;
-    const int U = d.U, U1 = U + 1, nd = d.T + U;
-    double pv[C];
+    const bool lane63 = lane == 63;
+    const int U = d.U, nd = d.T + U;
+    double b0[C2], b1[C2];
 #pragma unroll
-    for (int j = 0; j < C; ++j) pv[j] = (lane + 64 * j == U) ? D::one() : D::zero();
+    for (int g = 0; g < C2; ++g) {
+        const int c0 = 128 * g + 2 * lane;
+        b0[g] = (c0 == U) ? D::one() : D::zero();
+        b1[g] = (c0 + 1 == U) ? D::one() : D::zero();
+    }
     int E = 0;
     if (lane == 0) eout[0] = 0;
-    uint32_t voff[C];
-    lane_offsets<C>(voff, U, D::kStride);
-    const int64_t diag_bytes = (int64_t)U1 * D::kStride;
-    Ring<W, C, PF> ra, rb;
-    load_block<W, C, PF>(ra, w, diag_bytes, voff, nd - 1, -1, nd);
+    const SweepIO<D, C2> io(w, out, U);
+    Ring<C2, PF> ra, rb;
+    load_block<D, C2, PF>(ra, io, nd - 1, -1, nd);
     int n0 = nd - 1;
     for (; n0 - 2 * PF + 1 >= 0; n0 -= 2 * PF) {
-        load_block<W, C, PF>(rb, w, diag_bytes, voff, n0 - PF, -1, nd);
-        backward_block<D, C, PF, false>(ra, n0, nd, lane, pv, E, out, eout);
-        load_block<W, C, PF>(ra, w, diag_bytes, voff, n0 - 2 * PF, -1, nd);
-        backward_block<D, C, PF, false>(rb, n0 - PF, nd, lane, pv, E, out, eout);
+        load_block<D, C2, PF>(rb, io, n0 - PF, -1, nd);
+        backward_block<D, C2, PF, false>(ra, io, n0, nd, lane63, b0, b1, E, eout);
+        load_block<D, C2, PF>(ra, io, n0 - 2 * PF, -1, nd);
+        backward_block<D, C2, PF, false>(rb, io, n0 - PF, nd, lane63, b0, b1, E, eout);
     }
     if (n0 >= 0) {
-        load_block<W, C, PF>(rb, w, diag_bytes, voff, n0 - PF, -1, nd);
-        backward_block<D, C, PF, true>(ra, n0, nd, lane, pv, E, out, eout);
-        if (n0 - PF >= 0) backward_block<D, C, PF, true>(rb, n0 - PF, nd, lane, pv, E, out, eout);
+        load_block<D, C2, PF>(rb, io, n0 - PF, -1, nd);
+        backward_block<D, C2, PF, true>(ra, io, n0, nd, lane63, b0, b1, E, eout);
+        if (n0 - PF >= 0) backward_block<D, C2, PF, true>(rb, io, n0 - PF, nd, lane63, b0, b1, E, eout);
     }
-    if (lane == 0) *log2z = D::kLog ? pv[0] : log2_d(pv[0]) + (double)E;
+    if (lane == 0) *log2z = D::kLog ? b0[0] : log2_d(b0[0]) + (double)E;
 }
 
-template <int C, int PF>
-__device__ void run_sweeps(const SampleDesc &d, bool log_mode, const float4 *node, const double2 *prob,
+template <int C2, int PF>
+__device__ void run_sweeps(const SampleDesc &d, bool log_mode, const float4 *node, const float2 *prob,
                            double *alpha, double *beta, int *ea, int *eb, double *shz) {
     const int wave = threadIdx.x >> 6;
     const int64_t so = d.slot_off;
@@ -784,36 +830,34 @@ __device__ void run_sweeps(const SampleDesc &d, bool log_mode, const float4 *nod
     const int64_t dof = d.diag_off;
     if (log_mode) {
         const char *w = reinterpret_cast<const char *>(node + so);
-        if (wave == 0) sweep_forward<LogDomain, C, PF>(d, w, alpha + ao, ea + dof, &shz[0]);
-        else sweep_backward<LogDomain, C, PF>(d, w, beta + ao, eb + dof, &shz[1]);
+        if (wave == 0) sweep_forward<LogDomain, C2, PF>(d, w, alpha + ao, ea + dof, &shz[0]);
+        else sweep_backward<LogDomain, C2, PF>(d, w, beta + ao, eb + dof, &shz[1]);
     } else {
         const char *w = reinterpret_cast<const char *>(prob + so);
-        if (wave == 0) sweep_forward<ProbDomain, C, PF>(d, w, alpha + ao, ea + dof, &shz[0]);
-        else sweep_backward<ProbDomain, C, PF>(d, w, beta + ao, eb + dof, &shz[1]);
+        if (wave == 0) sweep_forward<ProbDomain, C2, PF>(d, w, alpha + ao, ea + dof, &shz[0]);
+        else sweep_backward<ProbDomain, C2, PF>(d, w, beta + ao, eb + dof, &shz[1]);
     }
 }
 
 __global__ __launch_bounds__(128) void k_alpha_beta(const SampleDesc *__restrict__ desc,
                                                     const int32_t *__restrict__ order,
                                                     const int *__restrict__ mode, const float4 *__restrict__ node,
-                                                    const double2 *__restrict__ prob, double *__restrict__ alpha,
+                                                    const float2 *__restrict__ prob, double *__restrict__ alpha,
                                                     double *__restrict__ beta, int *__restrict__ ealpha,
                                                     int *__restrict__ ebeta, double *__restrict__ log2z,
                                                     float *__restrict__ loss, uint32_t *status) {
     __shared__ double shz[2];
     const SampleDesc d = desc[order[blockIdx.x]];
     const bool lm = mode[d.index] != 0;
-    // PF: diagonals per prefetch block.  When a ring is first read, the loads
-    // of that ring (C*PF), the stores of the previous block (C*PF + PF/8) and
-    // the other ring's loads (C*PF) may be outstanding: 3*C*PF must stay
-    // within the 63 vector memory operations the wait counter tracks; two
-    // fp64 rings hold 8*C*PF registers.
+    // PF: diagonals per prefetch block.  A ring holds C2*PF 16-byte loads (the
+    // log domain: twice as many 8-byte ones); when a ring is first read, its
+    // loads, the other ring's and about one block of stores are in flight,
+    // within the 63 vector memory operations the wait counter tracks.
     switch (d.U1p) {
-    case 64: run_sweeps<1, 16>(d, lm, node, prob, alpha, beta, ealpha, ebeta, shz); break;
-    case 128: run_sweeps<2, 8>(d, lm, node, prob, alpha, beta, ealpha, ebeta, shz); break;
-    case 256: run_sweeps<4, 4>(d, lm, node, prob, alpha, beta, ealpha, ebeta, shz); break;
-    case 512: run_sweeps<8, 2>(d, lm, node, prob, alpha, beta, ealpha, ebeta, shz); break;
-    default: run_sweeps<16, 1>(d, lm, node, prob, alpha, beta, ealpha, ebeta, shz); break;
+    case 128: run_sweeps<1, 16>(d, lm, node, prob, alpha, beta, ealpha, ebeta, shz); break;
+    case 256: run_sweeps<2, 8>(d, lm, node, prob, alpha, beta, ealpha, ebeta, shz); break;
+    case 512: run_sweeps<4, 4>(d, lm, node, prob, alpha, beta, ealpha, ebeta, shz); break;
+    default: run_sweeps<8, 2>(d, lm, node, prob, alpha, beta, ealpha, ebeta, shz); break;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -1196,7 +1240,7 @@ hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream) {
             constexpr bool D = decltype(dtag)::value;
             hipLaunchKernelGGL((k_gather<T, D>), grid, block, 0, stream, static_cast<const T *>(a.logits), a.V,
                                a.blank, WS(const SampleDesc *, desc), WS(const ChunkDesc *, chunks), a.targets, a.S,
-                               WS(float4 *, node), WS(double2 *, prob), WS(int *, mode), WS(uint32_t *, status));
+                               WS(float4 *, node), WS(float2 *, prob), WS(int *, mode), WS(uint32_t *, status));
             return hipGetLastError();
         };
         if (a.esize == 4)
@@ -1210,7 +1254,7 @@ hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream) {
             auto kern = a.geom.wide_full ? k_rowstats_wide<T, Tg::n, true> : k_rowstats_wide<T, Tg::n, false>;
             hipLaunchKernelGGL(kern, grid, block, 0, stream, static_cast<const T *>(a.logits), a.V, a.blank,
                                WS(const SampleDesc *, desc), WS(const ChunkDesc *, chunks), a.lay.first_cached_chunk,
-                               a.targets, a.S, WS(float4 *, node), WS(double2 *, prob), WS(int *, mode),
+                               a.targets, a.S, WS(float4 *, node), WS(float2 *, prob), WS(int *, mode),
                                WS(uint32_t *, status));
             return hipGetLastError();
         });
@@ -1219,7 +1263,7 @@ hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream) {
         using T = typename Tg::type;
         hipLaunchKernelGGL((k_rowstats_narrow<T, Tg::vec, Tg::n>), grid, block, 0, stream,
                            static_cast<const T *>(a.logits), a.V, a.blank, WS(const SampleDesc *, desc),
-                           WS(const ChunkDesc *, chunks), a.targets, a.S, WS(float4 *, node), WS(double2 *, prob),
+                           WS(const ChunkDesc *, chunks), a.targets, a.S, WS(float4 *, node), WS(float2 *, prob),
                            WS(int *, mode), WS(uint32_t *, status));
         return hipGetLastError();
     });
@@ -1228,7 +1272,7 @@ hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream) {
 hipError_t launch_alpha_beta(const LaunchArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(k_alpha_beta, dim3(a.B), dim3(128), 0, stream, WS(const SampleDesc *, desc),
                        WS(const int32_t *, order), WS(const int *, mode), WS(const float4 *, node),
-                       WS(const double2 *, prob), WS(double *, alpha), WS(double *, beta), WS(int *, ealpha),
+                       WS(const float2 *, prob), WS(double *, alpha), WS(double *, beta), WS(int *, ealpha),
                        WS(int *, ebeta), WS(double *, log2z), a.loss, WS(uint32_t *, status));
     return hipGetLastError();
 }
