@@ -119,7 +119,7 @@ rnnt_status build_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t
         d.T = T[i];
         d.U = U[i];
         d.index = i;
-        d.U1p = 128 * pairs_per_lane(U[i] + 1);
+        d.U1p = padded_width(U[i] + 1);
         row += (int64_t)T[i] * (U[i] + 1);
         slot += ((int64_t)T[i] + U[i]) * (U[i] + 1);
         diag += (int64_t)T[i] + U[i];
@@ -161,7 +161,7 @@ rnnt_status build_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t
     L.beta = off;   off = align_up(off + sizeof(double) * (size_t)ab);
     L.ealpha = off; off = align_up(off + sizeof(int32_t) * (size_t)(diag + B));
     L.ebeta = off;  off = align_up(off + sizeof(int32_t) * (size_t)(diag + B));
-    L.log2z = off;  off = align_up(off + sizeof(double) * (size_t)B);
+    L.log2z = off;  off = align_up(off + sizeof(double) * 2 * (size_t)B);
     L.total = off;
     L.n_slots = slot;
     L.n_ab_slots = ab;
@@ -456,8 +456,7 @@ rnnt_status loss_impl(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V
     if (grad && pad.on() &&
         launch_zero_padding(grad, es, V, B, pad.max_T, pad.max_U1, a.ws, plan.lay, geom, stream) != hipSuccess)
         return RNNT_EXECUTION_FAILED;
-    if (reduction != RNNT_REDUCTION_NONE && loss_reduced &&
-        timed(3, stream, [&] { return launch_reduce(a, stream); }) != hipSuccess)
+    if (timed(3, stream, [&] { return launch_reduce(a, stream); }) != hipSuccess)
         return RNNT_EXECUTION_FAILED;
     return RNNT_SUCCESS;
 }

@@ -19,8 +19,8 @@ namespace rnnt {
 // is contiguous; slots with t = n-u outside [0, T) hold "impossible"
 // weights.  The recursions' outputs (alpha, beta) use the same skewed order
 // with the diagonal padded to a whole number of wavefront column groups:
-// ab_off + n*U1p + u, U1p = 128 * (column pairs per lane), so every lane of
-// the sweep owns a pair of slots.  Per-diagonal values (the recursions' power-of-two
+// ab_off + n*U1p + u, U1p = padded_width(U+1), so every lane of the sweep
+// owns whole slots.  Per-diagonal values (the recursions' power-of-two
 // exponents) are at diag_off + n / 8.
 struct SampleDesc {
     int64_t row_off;
@@ -35,13 +35,10 @@ struct SampleDesc {
     int32_t pad;
 };
 
-// Column pairs each lane of a 64-wide wavefront owns for a lattice of width
-// U1: the smallest power of two C2 with 128*C2 >= U1.
-inline int pairs_per_lane(int U1) {
-    int c = 1;
-    while (128 * c < U1) c <<= 1;
-    return c;
-}
+// Padded width of a lattice of width U1 in the alpha/beta sweeps (a 64-wide
+// wavefront with K columns per lane per group): 128 (K = 2) up to 128
+// columns, else a multiple of 256 (K = 4).
+inline int padded_width(int U1) { return U1 <= 128 ? 128 : (U1 + 255) / 256 * 256; }
 
 // A run of `count` lattice nodes of one sample handed to one workgroup of a
 // row pass, in one of two orders:
@@ -78,7 +75,7 @@ struct WorkspaceLayout {
     size_t beta;        // double[S_ab]
     size_t ealpha;      // int32[D + B]: exponent of alpha per group of 8 diagonals
     size_t ebeta;       // int32[D + B]
-    size_t log2z;       // double[B]: log2 P(y|x) (beta path)
+    size_t log2z;       // double[2B]: log2 P(y|x), beta path at [i], alpha path at [B + i]
     size_t total;
     int64_t n_slots;
     int64_t n_ab_slots;

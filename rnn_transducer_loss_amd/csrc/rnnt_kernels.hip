@@ -511,20 +511,22 @@ __global__ __launch_bounds__(256) void k_gather(const T *__restrict__ logits, in
 }
 
 // ----------------------------------------------------- K2: alpha/beta sweeps
-// Lane l owns the column pairs u = 128*g + 2*l + {0, 1}, g < C2 (U1p = 128*C2
-// padded columns), so a lane's two columns move in one 16-byte access: the
-// fp32 probabilities {P(blank), P(label)} of both going in, their two fp64
-// values going out.  Only the first column of a pair needs a value from
-// another lane (the second column of lane l-1, or of lane 63 of the previous
-// group for lane 0): one wave rotation per group and a select on lane 0.
-// Diagonal n is read and written through buffer resources based at the
-// diagonal, whose range check returns zero for the columns past U: those
-// columns start at zero (-inf in the log domain) and only ever receive zero,
-// because the label edge leaving column U is stored as impossible.  Every
-// slot of a diagonal up to U holds weights (the row pass fills those outside
-// the lattice with "impossible"), so no step needs a mask.  The inputs of PF
-// diagonals are loaded one block ahead into one of two register rings used
-// in turn.
+// Lane l owns K consecutive lattice columns in each of G column groups,
+// u = 64*K*g + K*l + k (k < K, g < G; U1p = 64*K*G padded columns, K = 2 for
+// lattices up to 128 columns wide, else 4).  A lane's columns move in
+// 16-byte accesses: the fp32 probabilities {P(blank), P(label)} of two
+// columns per load, two fp64 values per store.  Only a lane's first column
+// needs a value from another lane (the last column of lane l-1, or of lane
+// 63 of the previous group for lane 0): one wave rotation per group and a
+// select on lane 0 (a plain shift when there is one group).  Diagonal n is
+// read and written through buffer resources based at the diagonal, whose
+// range check returns zero for the columns past U: those columns start at
+// zero and only ever receive zero, because the label edge leaving column U
+// is stored as impossible (the log domain, where zero is -inf, clamps its
+// reads to column U instead).  Every slot of a diagonal up to U holds
+// weights (the row pass fills those outside the lattice with
+// "impossible"), so no step needs a mask.  The inputs of PF diagonals are
+// loaded one block ahead into one of two register rings used in turn.
 //
 // Probability domain: node value = mantissa * 2^E, one exponent E per group
 // of eight diagonals.  Forward step, from diagonal n to n+1:
@@ -546,12 +548,20 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 
-// Raw (unstrided) buffer resource over `bytes` bytes from `base`: a load
-// past `bytes` returns zero without touching memory, a store there is
-// dropped.
+// Raw (unstrided) buffer resource over `bytes` bytes from `base`: each
+// dword of a load past `bytes` reads zero without touching memory, a store
+// there is dropped.
 __device__ __forceinline__ Rsrc buffer_at(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
+
+// The weights of a lane's K columns of one group on one diagonal:
+// q[h] = {pb(2h), py(2h), pb(2h+1), py(2h+1)}.
+template <int K> struct Wts {
+    float4 q[K / 2];
+    __device__ float pb(int k) const { return (k & 1) ? q[k >> 1].z : q[k >> 1].x; }
+    __device__ float py(int k) const { return (k & 1) ? q[k >> 1].w : q[k >> 1].y; }
+};
 
 struct ProbDomain {
     static constexpr bool kLog = false;
@@ -560,9 +570,11 @@ struct ProbDomain {
     __device__ static double one() { return 1.0; }
     __device__ static double combine(double a, double b) { return a + b; }
     __device__ static double edge(double a, float w) { return a * (double)w; }
-    // The four weights of the pair at byte offset voff[0] (one load).
-    __device__ static float4 load(Rsrc r, const uint32_t (&voff)[2]) {
-        return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff[0], 0, 0));
+    // voff[k]: byte offset of column k of the lane's group (even k used).
+    template <int K> __device__ static void load(Wts<K> &w, Rsrc r, const uint32_t (&voff)[K]) {
+#pragma unroll
+        for (int h = 0; h < K / 2; ++h)
+            w.q[h] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff[2 * h], 0, 0));
     }
 };
 struct LogDomain {
@@ -577,297 +589,304 @@ struct LogDomain {
         return (mn == kNegInfD) ? mx : mx + (double)l;
     }
     __device__ static double edge(double a, float lpv) { return a + (double)lpv * kLog2eD; }
-    // The first eight bytes of the two slots at voff[0], voff[1] (each clamped
-    // to column U by the caller: a log-prob of 0 would not be impossible).
-    __device__ static float4 load(Rsrc r, const uint32_t (&voff)[2]) {
-        const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, voff[0], 0, 0);
-        const u32x2 y = __builtin_amdgcn_raw_buffer_load_b64(r, voff[1], 0, 0);
-        return make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(y[0]),
-                           __uint_as_float(y[1]));
+    // The first eight bytes of each column's slot (offsets clamped to column
+    // U by the caller: a log-prob of 0 would not be impossible).
+    template <int K> __device__ static void load(Wts<K> &w, Rsrc r, const uint32_t (&voff)[K]) {
+#pragma unroll
+        for (int h = 0; h < K / 2; ++h) {
+            const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, voff[2 * h], 0, 0);
+            const u32x2 y = __builtin_amdgcn_raw_buffer_load_b64(r, voff[2 * h + 1], 0, 0);
+            w.q[h] = make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(y[0]),
+                                 __uint_as_float(y[1]));
+        }
     }
 };
 
-// fp64 wave rotations: lane l receives lane l-1 (lane 0: lane 63), or lane
-// l+1 (lane 63: lane 0).
-__device__ __forceinline__ double rotate_up(double x) {
-    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(x), 0x13c, 0xf, 0xf, true);
-    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(x), 0x13c, 0xf, 0xf, true);
+// fp64 lane moves across the wave (two 32-bit DPP moves): rotations (lane l
+// receives lane l-1, lane 0 lane 63; or lane l+1, lane 63 lane 0) and
+// shifts that give the edge lane zero.
+template <int CTRL, bool ZERO_EDGE> __device__ __forceinline__ double lane_move(double x) {
+    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(x), CTRL, 0xf, 0xf, ZERO_EDGE);
+    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(x), CTRL, 0xf, 0xf, ZERO_EDGE);
     return __hiloint2double(hi, lo);
 }
-__device__ __forceinline__ double rotate_down(double x) {
-    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(x), 0x134, 0xf, 0xf, true);
-    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(x), 0x134, 0xf, 0xf, true);
-    return __hiloint2double(hi, lo);
-}
+__device__ __forceinline__ double rotate_up(double x) { return lane_move<0x13c, false>(x); }
+__device__ __forceinline__ double rotate_down(double x) { return lane_move<0x134, false>(x); }
+__device__ __forceinline__ double shift_up_zero(double x) { return lane_move<0x138, true>(x); }
+__device__ __forceinline__ double shift_down_zero(double x) { return lane_move<0x130, true>(x); }
 
-template <int C2> __device__ __forceinline__ int renorm(double (&a0)[C2], double (&a1)[C2]) {
+template <int K, int G> __device__ __forceinline__ int renorm(double (&a)[G][K]) {
     int eb = 0;
 #pragma unroll
-    for (int g = 0; g < C2; ++g) {
-        eb = max(eb, (__double2hiint(a0[g]) >> 20) & 0x7ff);
-        eb = max(eb, (__double2hiint(a1[g]) >> 20) & 0x7ff);
-    }
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int k = 0; k < K; ++k) eb = max(eb, (__double2hiint(a[g][k]) >> 20) & 0x7ff);
     eb = wave_max_i(eb);
     const int sh = eb - 1023;
 #pragma unroll
-    for (int g = 0; g < C2; ++g) {
-        a0[g] = __builtin_amdgcn_ldexp(a0[g], -sh);
-        a1[g] = __builtin_amdgcn_ldexp(a1[g], -sh);
-    }
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int k = 0; k < K; ++k) a[g][k] = __builtin_amdgcn_ldexp(a[g][k], -sh);
     return sh;
 }
 
-template <int C2, int PF> struct Ring {
-    float4 v[PF][C2];
+template <int K, int G, int PF> struct Ring {
+    Wts<K> v[PF][G];
 };
 
 // Where a sweep reads and writes: the sample's first weight slot and first
 // output slot, the byte sizes of one diagonal of each, and the lane's byte
 // offsets inside a diagonal.
-template <typename D, int C2> struct SweepIO {
+template <typename D, int K, int G> struct SweepIO {
     const char *w;
     char *out;
     uint32_t w_bytes;    // U1 * kSlot
     uint32_t out_bytes;  // U1p * 8
-    uint32_t win[C2][2];
-    uint32_t wout[C2];
+    uint32_t win[G][K];
+    uint32_t wout[G];
 
     __device__ SweepIO(const char *w_, double *out_, int U) : w(w_), out(reinterpret_cast<char *>(out_)) {
-        const int lane = threadIdx.x & 63;
+        const uint32_t lane = threadIdx.x & 63;
         const uint32_t U1 = (uint32_t)U + 1;
         w_bytes = U1 * D::kSlot;
-        out_bytes = 128u * C2 * 8u;
+        out_bytes = 64u * K * G * 8u;
 #pragma unroll
-        for (int g = 0; g < C2; ++g) {
-            const uint32_t c0 = 128u * g + 2u * lane;
-            if constexpr (D::kLog) {
-                win[g][0] = min(c0, (uint32_t)U) * D::kSlot;
-                win[g][1] = min(c0 + 1, (uint32_t)U) * D::kSlot;
-            } else {
-                win[g][0] = min(c0, U1) * D::kSlot;  // past U: zeros from the range check
-                win[g][1] = 0;
-            }
-            wout[g] = c0 * 8u;
+        for (int g = 0; g < G; ++g) {
+            const uint32_t c = 64u * K * g + K * lane;
+#pragma unroll
+            for (int k = 0; k < K; ++k)  // the log domain clamps to U, the probability domain to the range end
+                win[g][k] = (D::kLog ? min(c + k, (uint32_t)U) : min(c + k, U1)) * D::kSlot;
+            wout[g] = c * 8u;
         }
     }
-    __device__ void load(float4 (&r)[C2], int n) const {
+    __device__ void load(Wts<K> (&r)[G], int n) const {
         const Rsrc rs = buffer_at(w + (int64_t)n * w_bytes, w_bytes);
 #pragma unroll
-        for (int g = 0; g < C2; ++g) r[g] = D::load(rs, win[g]);
+        for (int g = 0; g < G; ++g) D::template load<K>(r[g], rs, win[g]);
     }
-    __device__ void store(int n, const double (&a0)[C2], const double (&a1)[C2]) const {
+    __device__ void store(int n, const double (&a)[G][K]) const {
         const Rsrc rs = buffer_at(out + (int64_t)n * out_bytes, out_bytes);
 #pragma unroll
-        for (int g = 0; g < C2; ++g) {
-            const u32x4 v = {(uint32_t)__double2loint(a0[g]), (uint32_t)__double2hiint(a0[g]),
-                             (uint32_t)__double2loint(a1[g]), (uint32_t)__double2hiint(a1[g])};
-            __builtin_amdgcn_raw_buffer_store_b128(v, rs, wout[g], 0, 0);
-        }
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int h = 0; h < K / 2; ++h) {
+                const u32x4 v = {(uint32_t)__double2loint(a[g][2 * h]), (uint32_t)__double2hiint(a[g][2 * h]),
+                                 (uint32_t)__double2loint(a[g][2 * h + 1]),
+                                 (uint32_t)__double2hiint(a[g][2 * h + 1])};
+                __builtin_amdgcn_raw_buffer_store_b128(v, rs, wout[g] + 16u * h, 0, 0);
+            }
     }
 };
 
 // Diagonals n0, n0+step, ... (clamped into [0, nd)) into ring r.
-template <typename D, int C2, int PF>
-__device__ __forceinline__ void load_block(Ring<C2, PF> &r, const SweepIO<D, C2> &io, int n0, int step, int nd) {
+template <typename D, int K, int G, int PF>
+__device__ __forceinline__ void load_block(Ring<K, G, PF> &r, const SweepIO<D, K, G> &io, int n0, int step,
+                                           int nd) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) io.load(r.v[p], min(max(n0 + step * p, 0), nd - 1));
 }
 
-// One forward step: the values of diagonal n (a0, a1, already stored) and its
+// One forward step: the values of diagonal n (already stored) and its
 // weights w give those of diagonal n+1.
-template <typename D, int C2>
-__device__ __forceinline__ void forward_step(double (&a0)[C2], double (&a1)[C2], const float4 (&w)[C2],
-                                             bool lane0) {
-    double my0[C2], r1[C2];
+template <typename D, int K, int G>
+__device__ __forceinline__ void forward_step(double (&a)[G][K], const Wts<K> (&w)[G], bool lane0) {
+    double my[G][K], r[G];
 #pragma unroll
-    for (int g = 0; g < C2; ++g) {
-        my0[g] = D::edge(a0[g], w[g].y);
-        r1[g] = rotate_up(D::edge(a1[g], w[g].w));
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int k = 0; k < K; ++k) my[g][k] = D::edge(a[g][k], w[g].py(k));
+    if constexpr (G > 1 || D::kLog) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) r[g] = rotate_up(my[g][K - 1]);
     }
 #pragma unroll
-    for (int g = 0; g < C2; ++g) {
-        const double left = lane0 ? (g > 0 ? r1[g > 0 ? g - 1 : 0] : D::zero()) : r1[g];
-        a0[g] = D::combine(D::edge(a0[g], w[g].x), left);
-        a1[g] = D::combine(D::edge(a1[g], w[g].z), my0[g]);
+    for (int g = 0; g < G; ++g) {
+        double left;
+        if constexpr (G == 1 && !D::kLog) left = shift_up_zero(my[0][K - 1]);
+        else left = lane0 ? (g > 0 ? r[g > 0 ? g - 1 : 0] : D::zero()) : r[g];
+        a[g][0] = D::combine(D::edge(a[g][0], w[g].pb(0)), left);
+#pragma unroll
+        for (int k = 1; k < K; ++k) a[g][k] = D::combine(D::edge(a[g][k], w[g].pb(k)), my[g][k - 1]);
     }
 }
 
-// One backward step: the values of diagonal n+1 (b0, b1) and the weights w
-// of diagonal n give those of diagonal n.
-template <typename D, int C2>
-__device__ __forceinline__ void backward_step(double (&b0)[C2], double (&b1)[C2], const float4 (&w)[C2],
-                                              bool lane63) {
-    double l0[C2];
+// One backward step: the values of diagonal n+1 and the weights w of
+// diagonal n give those of diagonal n.
+template <typename D, int K, int G>
+__device__ __forceinline__ void backward_step(double (&b)[G][K], const Wts<K> (&w)[G], bool lane63) {
+    double l0[G];
+    if constexpr (G > 1 || D::kLog) {
 #pragma unroll
-    for (int g = 0; g < C2; ++g) l0[g] = rotate_down(b0[g]);
+        for (int g = 0; g < G; ++g) l0[g] = rotate_down(b[g][0]);
+    }
 #pragma unroll
-    for (int g = 0; g < C2; ++g) {
-        const double right = lane63 ? (g + 1 < C2 ? l0[g + 1 < C2 ? g + 1 : g] : D::zero()) : l0[g];
-        const double n0 = D::combine(D::edge(b0[g], w[g].x), D::edge(b1[g], w[g].y));
-        b1[g] = D::combine(D::edge(b1[g], w[g].z), D::edge(right, w[g].w));
-        b0[g] = n0;
+    for (int g = 0; g < G; ++g) {
+        double right;
+        if constexpr (G == 1 && !D::kLog) right = shift_down_zero(b[0][0]);
+        else right = lane63 ? (g + 1 < G ? l0[g + 1 < G ? g + 1 : g] : D::zero()) : l0[g];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const double nxt = (k + 1 < K) ? b[g][k + 1 < K ? k + 1 : k] : right;
+            b[g][k] = D::combine(D::edge(b[g][k], w[g].pb(k)), D::edge(nxt, w[g].py(k)));
+        }
     }
 }
 
 // One block of PF forward diagonals n0 .. n0+PF-1 from ring r: each
 // diagonal is rescaled (every eighth), stored, then stepped.  GUARD: the
 // block may run past the last diagonal.
-template <typename D, int C2, int PF, bool GUARD>
-__device__ __forceinline__ void forward_block(const Ring<C2, PF> &r, const SweepIO<D, C2> &io, int n0, int nd,
-                                              bool lane0, double (&a0)[C2], double (&a1)[C2], int &E,
-                                              int *__restrict__ eout) {
+template <typename D, int K, int G, int PF, bool GUARD>
+__device__ __forceinline__ void forward_block(const Ring<K, G, PF> &r, const SweepIO<D, K, G> &io, int n0, int nd,
+                                              bool lane0, double (&a)[G][K], int &E, int *__restrict__ eout) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
         const int n = n0 + p;
         if (!GUARD || n < nd) {
             if (!D::kLog && (n & 7) == 7) {
-                E += renorm<C2>(a0, a1);
+                E += renorm<K, G>(a);
                 eout[(n + 1) >> 3] = E;  // uniform value and address
             }
-            io.store(n, a0, a1);
-            forward_step<D, C2>(a0, a1, r.v[p], lane0);
+            io.store(n, a);
+            forward_step<D, K, G>(a, r.v[p], lane0);
         }
     }
 }
 
-template <typename D, int C2, int PF>
+template <typename D, int K, int G, int PF>
 __device__ void sweep_forward(const SampleDesc &d, const char *__restrict__ w, double *__restrict__ out,
                               int *__restrict__ eout, double *log2z) {
     const int lane = threadIdx.x & 63;
     const bool lane0 = lane == 0;
     const int U = d.U, nd = d.T + U;
-    double a0[C2], a1[C2];
+    double a[G][K];
 #pragma unroll
-    for (int g = 0; g < C2; ++g) {
-        a0[g] = (g == 0 && lane0) ? D::one() : D::zero();
-        a1[g] = D::zero();
-    }
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int k = 0; k < K; ++k) a[g][k] = (g == 0 && k == 0 && lane0) ? D::one() : D::zero();
     int E = 0;
     if (lane == 0) eout[0] = 0;
-    const SweepIO<D, C2> io(w, out, U);
-    Ring<C2, PF> ra, rb;
-    load_block<D, C2, PF>(ra, io, 0, 1, nd);
+    const SweepIO<D, K, G> io(w, out, U);
+    Ring<K, G, PF> ra, rb;
+    load_block<D, K, G, PF>(ra, io, 0, 1, nd);
     int n0 = 0;
     for (; n0 + 2 * PF <= nd; n0 += 2 * PF) {
-        load_block<D, C2, PF>(rb, io, n0 + PF, 1, nd);
-        forward_block<D, C2, PF, false>(ra, io, n0, nd, lane0, a0, a1, E, eout);
-        load_block<D, C2, PF>(ra, io, n0 + 2 * PF, 1, nd);
-        forward_block<D, C2, PF, false>(rb, io, n0 + PF, nd, lane0, a0, a1, E, eout);
+        load_block<D, K, G, PF>(rb, io, n0 + PF, 1, nd);
+        forward_block<D, K, G, PF, false>(ra, io, n0, nd, lane0, a, E, eout);
+        load_block<D, K, G, PF>(ra, io, n0 + 2 * PF, 1, nd);
+        forward_block<D, K, G, PF, false>(rb, io, n0 + PF, nd, lane0, a, E, eout);
     }
     if (n0 < nd) {
-        load_block<D, C2, PF>(rb, io, n0 + PF, 1, nd);
-        forward_block<D, C2, PF, true>(ra, io, n0, nd, lane0, a0, a1, E, eout);
-        if (n0 + PF < nd) forward_block<D, C2, PF, true>(rb, io, n0 + PF, nd, lane0, a0, a1, E, eout);
+        load_block<D, K, G, PF>(rb, io, n0 + PF, 1, nd);
+        forward_block<D, K, G, PF, true>(ra, io, n0, nd, lane0, a, E, eout);
+        if (n0 + PF < nd) forward_block<D, K, G, PF, true>(rb, io, n0 + PF, nd, lane0, a, E, eout);
     }
     // One step past the last diagonal: column U holds P(y|x).
-    const int gU = U >> 7;
+    const int gU = U / (64 * K), kU = U % K;
     double v = 0.0;
 #pragma unroll
-    for (int g = 0; g < C2; ++g) v = (g == gU) ? ((U & 1) ? a1[g] : a0[g]) : v;
-    const double z = __shfl(v, (U & 127) >> 1, 64);
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int k = 0; k < K; ++k) v = (g == gU && k == kU) ? a[g][k] : v;
+    const double z = __shfl(v, (U % (64 * K)) / K, 64);
     if (lane == 0) *log2z = D::kLog ? z : log2_d(z) + (double)E;
 }
 
 // One block of PF backward diagonals n0, n0-1, ..., n0-PF+1 from ring r
 // (nd-1-n0 is a multiple of PF).
-template <typename D, int C2, int PF, bool GUARD>
-__device__ __forceinline__ void backward_block(const Ring<C2, PF> &r, const SweepIO<D, C2> &io, int n0, int nd,
-                                               bool lane63, double (&b0)[C2], double (&b1)[C2], int &E,
-                                               int *__restrict__ eout) {
+template <typename D, int K, int G, int PF, bool GUARD>
+__device__ __forceinline__ void backward_block(const Ring<K, G, PF> &r, const SweepIO<D, K, G> &io, int n0, int nd,
+                                               bool lane63, double (&b)[G][K], int &E, int *__restrict__ eout) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
         const int n = n0 - p;
         if (!GUARD || n >= 0) {
-            backward_step<D, C2>(b0, b1, r.v[p], lane63);
+            backward_step<D, K, G>(b, r.v[p], lane63);
             if (!D::kLog && ((nd - 1 - n) & 7) == 7) {
-                E += renorm<C2>(b0, b1);
+                E += renorm<K, G>(b);
                 eout[(nd - n) >> 3] = E;  // uniform value and address
             }
-            io.store(n, b0, b1);
+            io.store(n, b);
         }
     }
 }
 
-template <typename D, int C2, int PF>
+template <typename D, int K, int G, int PF>
 __device__ void sweep_backward(const SampleDesc &d, const char *__restrict__ w, double *__restrict__ out,
                                int *__restrict__ eout, double *log2z) {
     const int lane = threadIdx.x & 63;
     const bool lane63 = lane == 63;
     const int U = d.U, nd = d.T + U;
-    double b0[C2], b1[C2];
+    double b[G][K];
 #pragma unroll
-    for (int g = 0; g < C2; ++g) {
-        const int c0 = 128 * g + 2 * lane;
-        b0[g] = (c0 == U) ? D::one() : D::zero();
-        b1[g] = (c0 + 1 == U) ? D::one() : D::zero();
-    }
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int k = 0; k < K; ++k) b[g][k] = (64 * K * g + K * lane + k == U) ? D::one() : D::zero();
     int E = 0;
     if (lane == 0) eout[0] = 0;
-    const SweepIO<D, C2> io(w, out, U);
-    Ring<C2, PF> ra, rb;
-    load_block<D, C2, PF>(ra, io, nd - 1, -1, nd);
+    const SweepIO<D, K, G> io(w, out, U);
+    Ring<K, G, PF> ra, rb;
+    load_block<D, K, G, PF>(ra, io, nd - 1, -1, nd);
     int n0 = nd - 1;
     for (; n0 - 2 * PF + 1 >= 0; n0 -= 2 * PF) {
-        load_block<D, C2, PF>(rb, io, n0 - PF, -1, nd);
-        backward_block<D, C2, PF, false>(ra, io, n0, nd, lane63, b0, b1, E, eout);
-        load_block<D, C2, PF>(ra, io, n0 - 2 * PF, -1, nd);
-        backward_block<D, C2, PF, false>(rb, io, n0 - PF, nd, lane63, b0, b1, E, eout);
+        load_block<D, K, G, PF>(rb, io, n0 - PF, -1, nd);
+        backward_block<D, K, G, PF, false>(ra, io, n0, nd, lane63, b, E, eout);
+        load_block<D, K, G, PF>(ra, io, n0 - 2 * PF, -1, nd);
+        backward_block<D, K, G, PF, false>(rb, io, n0 - PF, nd, lane63, b, E, eout);
     }
     if (n0 >= 0) {
-        load_block<D, C2, PF>(rb, io, n0 - PF, -1, nd);
-        backward_block<D, C2, PF, true>(ra, io, n0, nd, lane63, b0, b1, E, eout);
-        if (n0 - PF >= 0) backward_block<D, C2, PF, true>(rb, io, n0 - PF, nd, lane63, b0, b1, E, eout);
+        load_block<D, K, G, PF>(rb, io, n0 - PF, -1, nd);
+        backward_block<D, K, G, PF, true>(ra, io, n0, nd, lane63, b, E, eout);
+        if (n0 - PF >= 0) backward_block<D, K, G, PF, true>(rb, io, n0 - PF, nd, lane63, b, E, eout);
     }
-    if (lane == 0) *log2z = D::kLog ? b0[0] : log2_d(b0[0]) + (double)E;
+    if (lane == 0) *log2z = D::kLog ? b[0][0] : log2_d(b[0][0]) + (double)E;
 }
 
-template <int C2, int PF>
-__device__ void run_sweeps(const SampleDesc &d, bool log_mode, const float4 *node, const float2 *prob,
-                           double *alpha, double *beta, int *ea, int *eb, double *shz) {
-    const int wave = threadIdx.x >> 6;
+template <int K, int G, int PF>
+__device__ void run_sweep(const SampleDesc &d, bool backward, bool log_mode, const float4 *node, const float2 *prob,
+                          double *alpha, double *beta, int *ea, int *eb, double *z) {
     const int64_t so = d.slot_off;
     const int64_t ao = d.ab_off;
     const int64_t dof = d.diag_off;
     if (log_mode) {
         const char *w = reinterpret_cast<const char *>(node + so);
-        if (wave == 0) sweep_forward<LogDomain, C2, PF>(d, w, alpha + ao, ea + dof, &shz[0]);
-        else sweep_backward<LogDomain, C2, PF>(d, w, beta + ao, eb + dof, &shz[1]);
+        if (!backward) sweep_forward<LogDomain, K, G, PF>(d, w, alpha + ao, ea + dof, z);
+        else sweep_backward<LogDomain, K, G, PF>(d, w, beta + ao, eb + dof, z);
     } else {
         const char *w = reinterpret_cast<const char *>(prob + so);
-        if (wave == 0) sweep_forward<ProbDomain, C2, PF>(d, w, alpha + ao, ea + dof, &shz[0]);
-        else sweep_backward<ProbDomain, C2, PF>(d, w, beta + ao, eb + dof, &shz[1]);
+        if (!backward) sweep_forward<ProbDomain, K, G, PF>(d, w, alpha + ao, ea + dof, z);
+        else sweep_backward<ProbDomain, K, G, PF>(d, w, beta + ao, eb + dof, z);
     }
 }
 
-__global__ __launch_bounds__(128) void k_alpha_beta(const SampleDesc *__restrict__ desc,
-                                                    const int32_t *__restrict__ order,
-                                                    const int *__restrict__ mode, const float4 *__restrict__ node,
-                                                    const float2 *__restrict__ prob, double *__restrict__ alpha,
-                                                    double *__restrict__ beta, int *__restrict__ ealpha,
-                                                    int *__restrict__ ebeta, double *__restrict__ log2z,
-                                                    float *__restrict__ loss, uint32_t *status) {
-    __shared__ double shz[2];
-    const SampleDesc d = desc[order[blockIdx.x]];
+// One wave per workgroup: workgroup 2k runs the forward sweep and 2k+1 the
+// backward sweep of the k-th sample in cost order, so the two sweeps of a
+// sample run on different compute units and do not share one unit's vector
+// memory path.  The backward sweep writes the loss and log2 P(y|x) at
+// log2z[i], the forward sweep its own log2 P(y|x) at log2z[B + i]; the
+// reduction kernel compares the two.
+__global__ __launch_bounds__(64) void k_alpha_beta(const SampleDesc *__restrict__ desc,
+                                                   const int32_t *__restrict__ order, int B,
+                                                   const int *__restrict__ mode, const float4 *__restrict__ node,
+                                                   const float2 *__restrict__ prob, double *__restrict__ alpha,
+                                                   double *__restrict__ beta, int *__restrict__ ealpha,
+                                                   int *__restrict__ ebeta, double *__restrict__ log2z,
+                                                   float *__restrict__ loss) {
+    const SampleDesc d = desc[order[blockIdx.x >> 1]];
+    const bool bw = (blockIdx.x & 1) != 0;
     const bool lm = mode[d.index] != 0;
-    // PF: diagonals per prefetch block.  A ring holds C2*PF 16-byte loads (the
-    // log domain: twice as many 8-byte ones); when a ring is first read, its
-    // loads, the other ring's and about one block of stores are in flight,
-    // within the 63 vector memory operations the wait counter tracks.
+    double *z = bw ? &log2z[d.index] : &log2z[B + d.index];
+    // PF: diagonals per prefetch block.  A ring holds G*K/2*PF 16-byte loads
+    // (the log domain: twice as many 8-byte ones); when a ring is first read,
+    // its loads, the other ring's and about one block of stores are in
+    // flight, within the 63 vector memory operations the wait counter tracks.
     switch (d.U1p) {
-    case 128: run_sweeps<1, 16>(d, lm, node, prob, alpha, beta, ealpha, ebeta, shz); break;
-    case 256: run_sweeps<2, 8>(d, lm, node, prob, alpha, beta, ealpha, ebeta, shz); break;
-    case 512: run_sweeps<4, 4>(d, lm, node, prob, alpha, beta, ealpha, ebeta, shz); break;
-    default: run_sweeps<8, 2>(d, lm, node, prob, alpha, beta, ealpha, ebeta, shz); break;
+    case 128: run_sweep<2, 1, 16>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z); break;
+    case 256: run_sweep<4, 1, 8>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z); break;
+    case 512: run_sweep<4, 2, 4>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z); break;
+    case 768: run_sweep<4, 3, 3>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z); break;
+    default: run_sweep<4, 4, 2>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z); break;
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const double la = -shz[0] * kLn2D;
-        const double lb = -shz[1] * kLn2D;
-        loss[d.index] = (float)lb;
-        log2z[d.index] = shz[1];
-        const bool agree = (la == lb) || (fabs(la - lb) <= 1e-4 * fmax(1.0, fabs(lb)));
-        if (!agree) atomicOr(status, (uint32_t)RNNT_DEV_LOSS_MISMATCH);
-    }
+    if (bw && threadIdx.x == 0) loss[d.index] = (float)(-log2z[d.index] * kLn2D);
 }
 
 // ------------------------------------------------------------ K3: gradient
@@ -957,95 +976,87 @@ __device__ __forceinline__ float clamp_to(float v, float cl, bool do_clamp) {
     return do_clamp ? fminf(fmaxf(v, -cl), cl) : v;
 }
 
-// One row per wave, rows in row order (consecutive rows of the chunk are
-// contiguous in memory).
+// The gradient of (part of) one row held the way the wide kernels hold it:
+// lane l keeps vectors (i0 + i)*64 + l, i < NV, written to dst (the row).
+// The blank and label elements get their flow subtracted in the registers
+// of the vector that holds them: element k is element k % VEC of vector
+// k / VEC, held by lane (k / VEC) mod 64 as its vector number (k / VEC) / 64.
+// The registers are overwritten with the stored gradient.
 template <typename T, int NV, bool FULL, bool FUSED, bool CLAMP>
-__global__ __launch_bounds__(256) void k_grad_wide(const T *logits, T *grad, RNNT_GRAD_PARAMS) {
+__device__ __forceinline__ void grad_row(typename Raw<T>::vec (&xc)[NV], T *dst, const RowTerms &rt, int blank,
+                                         int nvec, float cl, int i0 = 0) {
     constexpr int VEC = Raw<T>::kVec;
-    // Chunks run in the reverse of the rowstats order, so the rows read last
-    // by that pass, the likeliest to still be cached, are read again first.
-    const ChunkDesc c = chunks[n_chunks - 1 - blockIdx.x];
-    const SampleDesc d = desc[c.sample];
-    const SampleTerms st{log2z[d.index], mode[d.index] != 0};
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int nvec = V / VEC;
-    const int U1 = d.U + 1;
-    const float cl = clamp * scale;
-    using Vec = typename Raw<T>::vec;
-    auto load_row = [&](int t, int u, Vec (&x)[NV]) {
-        if constexpr (FUSED) {
-            const T *p = logits + row_of(d, t, u) * (int64_t)V;
+    const int vb = blank / VEC, vy = rt.y >= 0 ? rt.y / VEC : -1;
+    const int eb = blank - vb * VEC, ey = rt.y - vy * VEC;
 #pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                const int vi = i * 64 + lane;
-                if (FULL || vi < nvec) x[i] = load_raw<T, true>(p + (int64_t)vi * VEC);
+    for (int j = 0; j < NV; ++j) {
+        const int i = i0 + j;
+        const int vi = i * 64 + lane;
+        if (FULL || vi < nvec) {
+            float gv[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                float v = 0.f;
+                if constexpr (FUSED) v = exp2_fast(fmaf(Raw<T>::get(xc[j], e), kLog2e, rt.shift2));
+                gv[e] = v;
             }
-        }
-    };
-    int r = wave;
-    if (r >= c.count) return;
-    int t = (c.row_begin + r) / U1;
-    int u = (c.row_begin + r) - t * U1;
-    // One row: the next row's logits are requested first, into the next of
-    // three buffers used in turn, then this row's gradient is computed in
-    // place and written.  With three buffers a buffer is reloaded two rows
-    // after its gradient stores were issued, so the loads never wait for
-    // those stores to release their registers, and every wait covers exactly
-    // the buffer about to be used.  The last row loads itself again to keep
-    // the wait counts static.
-    auto row_step = [&](Vec (&xc)[NV], Vec (&xn)[NV]) -> bool {
-        const bool more = r + 4 < c.count;
-        int tn = t, un = u;
-        advance_node(tn, un, 4, U1);
-        if (more) load_row(tn, un, xn);
-        else load_row(t, u, xn);
-        const int64_t row = row_of(d, t, u);
-        const RowTerms rt = row_terms(d, st, t, u, node, alpha, beta, ealpha, ebeta, log2_scale, scale, FUSED);
-        T *dst = grad + row * (int64_t)V;
-        // The blank and label elements get their flow subtracted in the
-        // registers of the vector that holds them: element k is element
-        // k % VEC of vector k / VEC, held by lane (k / VEC) mod 64 as its
-        // vector number (k / VEC) / 64.
-        const int vb = blank / VEC, vy = rt.y >= 0 ? rt.y / VEC : -1;
-        const int eb = blank - vb * VEC, ey = rt.y - vy * VEC;
+            if ((vb >> 6) == i) {
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int vi = i * 64 + lane;
-            if (FULL || vi < nvec) {
-                float gv[VEC];
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    float v = 0.f;
-                    if constexpr (FUSED) v = exp2_fast(fmaf(Raw<T>::get(xc[i], e), kLog2e, rt.shift2));
-                    gv[e] = v;
-                }
-                if ((vb >> 6) == i) {
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) gv[e] -= (vi == vb && e == eb) ? rt.fb : 0.f;
-                }
-                if (vy >= 0 && (vy >> 6) == i) {
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) gv[e] -= (vi == vy && e == ey) ? rt.fy : 0.f;
-                }
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) gv[e] = clamp_to(gv[e], cl, CLAMP);
-                xc[i] = Raw<T>::put(gv);
-                store_raw<T, true>(dst + (int64_t)vi * VEC, xc[i]);
+                for (int e = 0; e < VEC; ++e) gv[e] -= (vi == vb && e == eb) ? rt.fb : 0.f;
             }
+            if (vy >= 0 && (vy >> 6) == i) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) gv[e] -= (vi == vy && e == ey) ? rt.fy : 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) gv[e] = clamp_to(gv[e], cl, CLAMP);
+            xc[j] = Raw<T>::put(gv);
+            store_raw<T, true>(dst + (int64_t)vi * VEC, xc[j]);
         }
-        t = tn;
-        u = un;
-        r += 4;
-        return more;
-    };
-    Vec x0[NV], x1[NV], x2[NV];
-    load_row(t, u, x0);
-    while (row_step(x0, x1) && row_step(x1, x2) && row_step(x2, x0)) {
     }
 }
 
-// G < 64 lanes per row (small V), 64/G rows per wave, rows in row order.
+// The gradient, S waves per row (each NV vectors per lane: rows of up to
+// 4 KiB take one wave) and four waves per workgroup: each wave loads its
+// part of the row, computes and stores it, and exits; the many short
+// workgroups keep enough rows in flight without a prefetch ring.  Workgroup
+// b takes the rows (b % PB)*4/S .. of chunk n_chunks-1-b/PB (PB = rows per
+// chunk * S / 4, row order), so the chunks run in the reverse of the
+// rowstats order and the rows that pass read last, the likeliest to still be
+// cached, are read again first.
+template <typename T, int NV, int S, bool FULL, bool FUSED, bool CLAMP>
+__global__ __launch_bounds__(256) void k_grad_rows(const T *logits, T *grad, int blocks_per_chunk,
+                                                   RNNT_GRAD_PARAMS) {
+    constexpr int VEC = Raw<T>::kVec;
+    const int bpc = blocks_per_chunk;
+    const ChunkDesc c = chunks[n_chunks - 1 - (int)blockIdx.x / bpc];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = ((int)blockIdx.x % bpc) * (4 / S) + wave / S;
+    if (r >= c.count) return;
+    const int i0 = (wave % S) * NV;  // first vector number of this wave's part
+    const SampleDesc d = desc[c.sample];
+    const int lane = threadIdx.x & 63;
+    const int nvec = V / VEC;
+    const int U1 = d.U + 1;
+    const int t = (c.row_begin + r) / U1;
+    const int u = (c.row_begin + r) - t * U1;
+    const int64_t row = row_of(d, t, u);
+    using Vec = typename Raw<T>::vec;
+    Vec x[NV];
+    if constexpr (FUSED) {
+        const T *p = logits + row * (int64_t)V;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int vi = (i0 + j) * 64 + lane;
+            if (FULL || vi < nvec) x[j] = load_raw<T, true>(p + (int64_t)vi * VEC);
+        }
+    }
+    const SampleTerms st{log2z[d.index], mode[d.index] != 0};
+    const RowTerms rt = row_terms(d, st, t, u, node, alpha, beta, ealpha, ebeta, log2_scale, scale, FUSED);
+    grad_row<T, NV, FULL, FUSED, CLAMP>(x, grad + row * (int64_t)V, rt, blank, nvec, clamp * scale, i0);
+}
+
 template <typename T, int VEC, int G, bool FUSED>
 __global__ __launch_bounds__(256) void k_grad_narrow(const T *logits, T *grad, RNNT_GRAD_PARAMS) {
     constexpr int RPW = 64 / G;
@@ -1090,10 +1101,20 @@ __global__ __launch_bounds__(256) void k_grad_narrow(const T *logits, T *grad, R
 }
 
 // --------------------------------------------------------------- reduction
-__global__ __launch_bounds__(64) void k_reduce(const float *__restrict__ loss, int B, int mean,
-                                               float *__restrict__ out) {
+// Cross-checks the two sweeps' log2 P(y|x) of every sample, then (out
+// non-null) reduces the per-sample losses: sum, or mean over B.
+__global__ __launch_bounds__(64) void k_reduce(const float *__restrict__ loss, const double *__restrict__ log2z,
+                                               int B, int mean, float *__restrict__ out, uint32_t *status) {
     double s = 0.0;
-    for (int i = threadIdx.x; i < B; i += 64) s += (double)loss[i];
+    bool agree = true;
+    for (int i = threadIdx.x; i < B; i += 64) {
+        s += (double)loss[i];
+        const double lb = -log2z[i] * kLn2D;
+        const double la = -log2z[B + i] * kLn2D;
+        agree = agree && ((la == lb) || (fabs(la - lb) <= 1e-4 * fmax(1.0, fabs(lb))));
+    }
+    if (__any(!agree) && threadIdx.x == 0) atomicOr(status, (uint32_t)RNNT_DEV_LOSS_MISMATCH);
+    if (!out) return;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
     if (threadIdx.x == 0) out[0] = (float)(mean ? s / (double)B : s);
@@ -1270,10 +1291,10 @@ hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_alpha_beta(const LaunchArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL(k_alpha_beta, dim3(a.B), dim3(128), 0, stream, WS(const SampleDesc *, desc),
-                       WS(const int32_t *, order), WS(const int *, mode), WS(const float4 *, node),
+    hipLaunchKernelGGL(k_alpha_beta, dim3(2 * a.B), dim3(64), 0, stream, WS(const SampleDesc *, desc),
+                       WS(const int32_t *, order), a.B, WS(const int *, mode), WS(const float4 *, node),
                        WS(const float2 *, prob), WS(double *, alpha), WS(double *, beta), WS(int *, ealpha),
-                       WS(int *, ebeta), WS(double *, log2z), a.loss, WS(uint32_t *, status));
+                       WS(int *, ebeta), WS(double *, log2z), a.loss);
     return hipGetLastError();
 }
 
@@ -1303,17 +1324,22 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
             T *out = static_cast<T *>(a.grad);
             const bool cl = a.clamp > 0.f;
             const bool fu = a.geom.wide_full;
-            void (*kern)(const T *, T *, int, int, int, float, float, float, const SampleDesc *, const ChunkDesc *,
-                         const int *, const double *, const float4 *, const double *, const double *, const int *,
-                         const int *);
+            // waves per row: rows of up to 4 KiB (four vectors per lane) take one
+            constexpr int S = Tg::n > 4 ? Tg::n / 4 : 1;
+            constexpr int NVW = Tg::n / S;
+            void (*kern)(const T *, T *, int, int, int, int, float, float, float, const SampleDesc *,
+                         const ChunkDesc *, const int *, const double *, const float4 *, const double *,
+                         const double *, const int *, const int *);
             if (a.fused) {
-                if (cl) kern = fu ? k_grad_wide<T, Tg::n, true, true, true> : k_grad_wide<T, Tg::n, false, true, true>;
-                else kern = fu ? k_grad_wide<T, Tg::n, true, true, false> : k_grad_wide<T, Tg::n, false, true, false>;
+                if (cl) kern = fu ? k_grad_rows<T, NVW, S, true, true, true> : k_grad_rows<T, NVW, S, false, true, true>;
+                else kern = fu ? k_grad_rows<T, NVW, S, true, true, false> : k_grad_rows<T, NVW, S, false, true, false>;
             } else {
-                if (cl) kern = fu ? k_grad_wide<T, Tg::n, true, false, true> : k_grad_wide<T, Tg::n, false, false, true>;
-                else kern = fu ? k_grad_wide<T, Tg::n, true, false, false> : k_grad_wide<T, Tg::n, false, false, false>;
+                if (cl) kern = fu ? k_grad_rows<T, NVW, S, true, false, true> : k_grad_rows<T, NVW, S, false, false, true>;
+                else kern = fu ? k_grad_rows<T, NVW, S, true, false, false> : k_grad_rows<T, NVW, S, false, false, false>;
             }
-            hipLaunchKernelGGL(kern, grid, block, 0, stream, in, out, RNNT_GRAD_ARGS(g));
+            const int bpc = a.lay.rows_per_chunk * S / 4;
+            hipLaunchKernelGGL(kern, dim3((unsigned)a.lay.n_chunks * bpc), block, 0, stream, in, out, bpc,
+                               RNNT_GRAD_ARGS(g));
             return hipGetLastError();
         });
     return with_narrow(a.esize, a.geom.vec, a.geom.lanes_per_row, [&](auto tag) {
@@ -1330,8 +1356,9 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_reduce(const LaunchArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL(k_reduce, dim3(1), dim3(64), 0, stream, a.loss, a.B, a.reduction == RNNT_REDUCTION_MEAN,
-                       a.loss_reduced);
+    float *out = (a.reduction != RNNT_REDUCTION_NONE) ? a.loss_reduced : nullptr;
+    hipLaunchKernelGGL(k_reduce, dim3(1), dim3(64), 0, stream, a.loss, WS(const double *, log2z), a.B,
+                       a.reduction == RNNT_REDUCTION_MEAN, out, WS(uint32_t *, status));
     return hipGetLastError();
 }
 
