@@ -264,28 +264,33 @@ __device__ __forceinline__ int read_label(const SampleDesc &d, int u, int V, int
     return in_range ? y : -1;
 }
 
-// Element k (wave-uniform) of a row held the way the wide kernels hold it:
-// lane l keeps vectors i*64 + l, i < NV, of VEC elements each.  Selected in
-// registers and read from the owning lane, so no second load of the row.
-template <typename T, int NV>
-__device__ __forceinline__ float row_element(const typename Raw<T>::vec (&x)[NV], int k) {
-    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-    constexpr int VEC = Raw<T>::kVec;
-    constexpr int EPD = VEC / 4;  // elements per 32-bit word: 1 (fp32) or 2 (fp16)
-    const int v = k / VEC;
-    const int e = k - v * VEC;
-    const int target = (v >> 6) * 4 + e / EPD;  // word among the lane's 4*NV words
-    uint32_t bits = 0;
+// Lane-local maximum of a row held the way the wide kernels hold it.  fp16
+// rows are reduced in fp16 with packed maxima (exact, and no conversions
+// until the last value).
+template <typename T, int NV, bool FULL>
+__device__ __forceinline__ float row_max(const typename Raw<T>::vec (&x)[NV], int nvec) {
+    const int lane = threadIdx.x & 63;
+    if constexpr (std::is_same_v<T, _Float16>) {
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        typename Raw<T>::vec hm = (_Float16)kNegInf;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        const u4 q = __builtin_bit_cast(u4, x[j]);
+        for (int i = 0; i < NV; ++i)
+            if (FULL || i * 64 + lane < nvec) hm = __builtin_elementwise_maximum(hm, x[i]);
+        const h4 m4 = __builtin_elementwise_maximum(__builtin_shufflevector(hm, hm, 0, 1, 2, 3),
+                                                __builtin_shufflevector(hm, hm, 4, 5, 6, 7));
+        const h2 m2 = __builtin_elementwise_maximum(__builtin_shufflevector(m4, m4, 0, 1),
+                                                __builtin_shufflevector(m4, m4, 2, 3));
+        return fmaxf((float)m2[0], (float)m2[1]);
+    } else {
+        float m = kNegInf;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) bits = (j * 4 + c == target) ? q[c] : bits;
+        for (int i = 0; i < NV; ++i)
+            if (FULL || i * 64 + lane < nvec)
+#pragma unroll
+                for (int e = 0; e < Raw<T>::kVec; ++e) m = fmaxf(m, Raw<T>::get(x[i], e));
+        return m;
     }
-    bits = (uint32_t)__builtin_amdgcn_readlane((int)bits, v & 63);
-    if constexpr (EPD == 1) return __uint_as_float(bits);
-    const uint16_t h = (uint16_t)((e & 1) ? (bits >> 16) : (bits & 0xffffu));
-    return (float)__builtin_bit_cast(_Float16, h);
 }
 
 // Lattice node of the row `step` rows further on in the same sample (row order).
@@ -343,8 +348,15 @@ __device__ __forceinline__ void rowstats_wide_chunk(const T *__restrict__ logits
     int n = c.diag, u = c.col;
     advance_diag(n, u, r, d.T, d.U);
     int y = __builtin_amdgcn_readfirstlane(read_label(d, u, V, blank, targets, S, status));
-    // One row: the next row's logits (and label) are requested first, into
-    // the next of three buffers used in turn, then this row is reduced.  With
+    auto elem = [&](int nn, int uu, int k) -> float {
+        return Elem<T>::load1(logits + row_of(d, nn - uu, uu) * (int64_t)V + k);
+    };
+    float hb = elem(n, u, blank);
+    float hy = (y >= 0) ? elem(n, u, y) : 0.f;
+    // One row: the next row's logits, its label and its blank and label
+    // logits (two wave-uniform loads, cheaper than selecting them out of the
+    // row's registers) are requested first, the logits into the next of
+    // three buffers used in turn, then this row is reduced.  With
     // three buffers a buffer is reloaded two rows after the stores issued
     // while it was current, so the loads never wait for those stores to
     // release their registers, and every wait covers exactly the buffer about
@@ -357,12 +369,9 @@ __device__ __forceinline__ void rowstats_wide_chunk(const T *__restrict__ logits
         if (more) load_row(nn, un, xn);
         else load_row(n, u, xn);
         const int yn = more ? __builtin_amdgcn_readfirstlane(read_label(d, un, V, blank, targets, S, status)) : -1;
-        float m = kNegInf;
-#pragma unroll
-        for (int i = 0; i < NV; ++i)
-            if (FULL || i * 64 + lane < nvec)
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) m = fmaxf(m, Raw<T>::get(xc[i], e));
+        const float hbn = more ? elem(nn, un, blank) : 0.f;
+        const float hyn = (yn >= 0) ? elem(nn, un, yn) : 0.f;
+        float m = row_max<T, NV, FULL>(xc, nvec);
         m = wave_max_f(m);
         const float mr = (m == kNegInf) ? 0.f : m;
         const float nm = -mr * kLog2e;
@@ -374,8 +383,6 @@ __device__ __forceinline__ void rowstats_wide_chunk(const T *__restrict__ logits
                 for (int e = 0; e < VEC; ++e) s += exp2_fast(fmaf(Raw<T>::get(xc[i], e), kLog2e, nm));
         s = wave_sum_f(s);
         const float dn = (m == kNegInf) ? kNegInf : m + log2_fast(s) * kLn2;
-        const float hb = row_element<T, NV>(xc, blank);
-        const float hy = (y >= 0) ? row_element<T, NV>(xc, y) : 0.f;
         const bool dead = (dn == kNegInf);
         const float lpb = dead ? kNegInf : hb - dn;
         const float lpy = (dead || y < 0) ? kNegInf : hy - dn;
@@ -384,6 +391,8 @@ __device__ __forceinline__ void rowstats_wide_chunk(const T *__restrict__ logits
         n = nn;
         u = un;
         y = yn;
+        hb = hbn;
+        hy = hyn;
         r += 4;
         return more;
     };
