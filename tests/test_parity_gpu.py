@@ -277,9 +277,10 @@ def test_vocab_sizes(rl, V):
     check_against_oracle(w, loss, grad, "mean")
 
 
-@pytest.mark.parametrize("U", [63, 64, 127, 128, 255, 256, 511, 512, 700, 1023])
+@pytest.mark.parametrize("U", [63, 64, 127, 128, 255, 256, 511, 512, 700, 767, 768, 1023])
 def test_lattice_widths_across_register_tiles(rl, U):
-    # U+1 crosses each multiple of 64 nodes the alpha/beta wavefront holds per lane
+    # U+1 crosses each width of the alpha/beta sweeps' lane tiles: 128 columns (two per lane), then
+    # groups of 256 (four per lane), up to four groups
     w = _custom([3, 40], [U, min(U, 20)], 8, std=1.0, blank=0, reduction="none", seed=U)
     loss, red, grad, flags = run(rl, w)
     assert flags == 0
@@ -415,6 +416,24 @@ def test_extreme_log_probs_take_the_log_domain_path(rl):
     loss, red, grad, flags = run(rl, w)
     assert flags == 0
     check_against_oracle(w, loss, grad, "sum")
+
+
+@pytest.mark.parametrize("U", [130, 300, 600, 900])
+def test_log_domain_across_register_tiles(rl, U):
+    """The log-domain sweep on lattices wide enough for one to four column groups per lane.
+
+    Values are multiples of 1/4 (exact in fp32); one in five blank log-probs is -0.5 so the total
+    probability stays away from underflow in fp64.
+    """
+    rng = np.random.default_rng(U)
+    Ts, Us, V = [4, 3], [U, U // 2], 12
+    w = _custom(Ts, Us, V, std=1.0, blank=0, fused=False, reduction="none", seed=U)
+    x = np.round(rng.uniform(-200.0, -0.25, size=(w.N, V)) * 4) / 4
+    x[::5, 0] = -0.5
+    w.logits = torch.tensor(x, dtype=torch.float32, device="cuda")
+    loss, red, grad, flags = run(rl, w)
+    assert flags == 0
+    check_against_oracle(w, loss, grad, "none")
 
 
 def test_extreme_fused_logits(rl):
