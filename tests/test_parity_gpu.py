@@ -277,6 +277,17 @@ def test_vocab_sizes(rl, V):
     check_against_oracle(w, loss, grad, "mean")
 
 
+@pytest.mark.parametrize("V,dtype,clamp", [(2048, torch.float32, -1.0), (4096, torch.float32, 0.5),
+                                           (8192, torch.float16, -1.0), (3000, torch.float16, 0.05)])
+def test_wide_rows_split_over_waves(rl, V, dtype, clamp):
+    # rows of 8-16 KiB: the gradient pass splits each row over two or four waves (the flows land in
+    # whichever part holds the blank / label), the row pass holds the whole row in one wave
+    w = _custom([7, 5], [6, 9], V, dtype=dtype, std=2.0, blank=-1, clamp=clamp, reduction="mean", seed=V)
+    loss, red, grad, flags = run(rl, w)
+    assert flags == 0
+    check_against_oracle(w, loss, grad, "mean")
+
+
 @pytest.mark.parametrize("U", [63, 64, 127, 128, 255, 256, 511, 512, 700, 767, 768, 1023])
 def test_lattice_widths_across_register_tiles(rl, U):
     # U+1 crosses each width of the alpha/beta sweeps' lane tiles: 128 columns (two per lane), then
