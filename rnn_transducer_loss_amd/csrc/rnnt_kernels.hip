@@ -1026,24 +1026,26 @@ __device__ __forceinline__ void grad_row(typename Raw<T>::vec (&xc)[NV], T *dst,
     }
 }
 
-// The gradient, S waves per row (each NV vectors per lane: rows of up to
-// 4 KiB take one wave) and four waves per workgroup: each wave loads its
-// part of the row, computes and stores it, and exits; the many short
-// workgroups keep enough rows in flight without a prefetch ring.  Workgroup
-// b takes the rows (b % PB)*4/S .. of chunk n_chunks-1-b/PB (PB = rows per
-// chunk * S / 4, row order), so the chunks run in the reverse of the
-// rowstats order and the rows that pass read last, the likeliest to still be
-// cached, are read again first.
+// The gradient, one wave per workgroup and S workgroups per row (each NV
+// vectors per lane: rows of up to 4 KiB take one): each wave loads its part
+// of the row, computes and stores it, and exits.  Many single-wave
+// workgroups of 4 KiB keep enough rows in flight without a prefetch ring
+// (and run faster than four-wave workgroups over four rows).  Workgroup b
+// takes part (b % PB) % S of row (b % PB) / S of chunk n_chunks-1-b/PB
+// (PB = rows per chunk * S, row order), so the chunks run in the reverse of
+// the rowstats order and the rows that pass read last, the likeliest to
+// still be cached, are read again first.
 template <typename T, int NV, int S, bool FULL, bool FUSED, bool CLAMP>
-__global__ __launch_bounds__(256) void k_grad_rows(const T *logits, T *grad, int blocks_per_chunk,
-                                                   RNNT_GRAD_PARAMS) {
+__global__ __launch_bounds__(64) void k_grad_rows(const T *logits, T *grad, int blocks_per_chunk,
+                                                  int64_t block_base, RNNT_GRAD_PARAMS) {
     constexpr int VEC = Raw<T>::kVec;
     const int bpc = blocks_per_chunk;
-    const ChunkDesc c = chunks[n_chunks - 1 - (int)blockIdx.x / bpc];
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int r = ((int)blockIdx.x % bpc) * (4 / S) + wave / S;
+    const int64_t b = block_base + blockIdx.x;
+    const ChunkDesc c = chunks[n_chunks - 1 - (int)(b / bpc)];
+    const int part = (int)(b % bpc);
+    const int r = part / S;
     if (r >= c.count) return;
-    const int i0 = (wave % S) * NV;  // first vector number of this wave's part
+    const int i0 = (part % S) * NV;  // first vector number of this wave's part
     const SampleDesc d = desc[c.sample];
     const int lane = threadIdx.x & 63;
     const int nvec = V / VEC;
@@ -1336,7 +1338,7 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
             // waves per row: rows of up to 4 KiB (four vectors per lane) take one
             constexpr int S = Tg::n > 4 ? Tg::n / 4 : 1;
             constexpr int NVW = Tg::n / S;
-            void (*kern)(const T *, T *, int, int, int, int, float, float, float, const SampleDesc *,
+            void (*kern)(const T *, T *, int, int64_t, int, int, int, float, float, float, const SampleDesc *,
                          const ChunkDesc *, const int *, const double *, const float4 *, const double *,
                          const double *, const int *, const int *);
             if (a.fused) {
@@ -1346,9 +1348,14 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
                 if (cl) kern = fu ? k_grad_rows<T, NVW, S, true, false, true> : k_grad_rows<T, NVW, S, false, false, true>;
                 else kern = fu ? k_grad_rows<T, NVW, S, true, false, false> : k_grad_rows<T, NVW, S, false, false, false>;
             }
-            const int bpc = a.lay.rows_per_chunk * S / 4;
-            hipLaunchKernelGGL(kern, dim3((unsigned)a.lay.n_chunks * bpc), block, 0, stream, in, out, bpc,
-                               RNNT_GRAD_ARGS(g));
+            // one launch per 2^24 workgroups, so no launch exceeds 32-bit work-item counts
+            const int bpc = a.lay.rows_per_chunk * S;
+            const int64_t total = (int64_t)a.lay.n_chunks * bpc;
+            constexpr int64_t kMaxBlocks = (int64_t)1 << 24;
+            for (int64_t base = 0; base < total; base += kMaxBlocks) {
+                const unsigned nb = (unsigned)std::min<int64_t>(kMaxBlocks, total - base);
+                hipLaunchKernelGGL(kern, dim3(nb), dim3(64), 0, stream, in, out, bpc, base, RNNT_GRAD_ARGS(g));
+            }
             return hipGetLastError();
         });
     return with_narrow(a.esize, a.geom.vec, a.geom.lanes_per_row, [&](auto tag) {
