@@ -41,23 +41,6 @@ struct Plan {
     int max_U1 = 1;
 };
 
-// Node (n, u) of the anti-diagonal order of a T x (U+1) lattice that lies
-// `k` nodes after the first node of diagonal n0 (diagonal n holds columns
-// max(0, n-T+1) .. min(n, U)).
-void diag_node(int32_t T, int32_t U, int64_t k, int32_t &n, int32_t &u, int32_t n0) {
-    n = n0;
-    for (;;) {
-        const int64_t lo = std::max<int64_t>(0, (int64_t)n - T + 1), hi = std::min<int64_t>(n, U);
-        const int64_t len = hi - lo + 1;
-        if (k < len) {
-            u = (int32_t)(lo + k);
-            return;
-        }
-        k -= len;
-        ++n;
-    }
-}
-
 rnnt_status check_lengths(int32_t B, int32_t V, const int32_t *T, const int32_t *U) {
     if (B < 1 || V < 1 || !T || !U) return RNNT_INVALID_VALUE;
     for (int32_t i = 0; i < B; ++i) {
@@ -112,7 +95,7 @@ rnnt_status build_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t
         SampleDesc &d = p.desc[i];
         d.row_off = pad.on() ? (int64_t)i * pad.max_T * pad.max_U1 : row;
         d.tstride = pad.on() ? pad.max_U1 : U[i] + 1;
-        d.pad = 0;
+        d.chunk0 = 0;
         d.slot_off = slot;
         d.diag_off = diag;
         d.ab_off = ab;
@@ -131,20 +114,15 @@ rnnt_status build_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t
     p.order = lpt_order(B, T, U);
     const int32_t rpc = rows_per_chunk(row, V, esize);
     p.chunks.clear();
+    int64_t max_sample_chunks = 0;
     for (int32_t k = 0; k < B; ++k) {
         const int32_t i = p.order[k];
         const int64_t rows = (int64_t)T[i] * (U[i] + 1);
         if (rows > INT32_MAX) return RNNT_INVALID_VALUE;
-        // the diagonal-order start of every run, walked once along the diagonals
-        int32_t n = 0;
-        int64_t before_n = 0;  // nodes on the diagonals before n
-        for (int64_t r0 = 0; r0 < rows; r0 += rpc) {
-            int32_t nn = 0, uu = 0;
-            diag_node(T[i], U[i], r0 - before_n, nn, uu, n);
-            for (; n < nn; ++n)
-                before_n += std::min<int64_t>(n, U[i]) - std::max<int64_t>(0, (int64_t)n - T[i] + 1) + 1;
-            p.chunks.push_back(ChunkDesc{i, (int32_t)r0, (int32_t)std::min<int64_t>(rpc, rows - r0), nn, uu});
-        }
+        p.desc[i].chunk0 = (int32_t)std::min<size_t>(p.chunks.size(), INT32_MAX);
+        const int64_t n = (rows + rpc - 1) / rpc;
+        max_sample_chunks = std::max(max_sample_chunks, n);
+        for (int64_t j = 0; j < n; ++j) p.chunks.push_back(make_chunk(p.desc[i], i, (int32_t)j, rpc));
     }
     if (p.chunks.size() > (size_t)INT32_MAX) return RNNT_INVALID_VALUE;
     WorkspaceLayout &L = p.lay;
@@ -168,6 +146,7 @@ rnnt_status build_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t
     L.n_diags = diag;
     L.n_chunks = (int32_t)p.chunks.size();
     L.rows_per_chunk = rpc;
+    L.max_sample_chunks = (int32_t)max_sample_chunks;
     // The gradient pass walks the chunks in reverse, so the rows the
     // rowstats pass reads last are read again first: those last ~160 MB
     // (within the 256 MB memory-side cache) are read with caching loads,
@@ -233,13 +212,13 @@ rnnt_status upload(void *dst, const std::vector<uint8_t> &src, hipStream_t strea
     return RNNT_SUCCESS;
 }
 
-// The header, descriptors, order and chunks are contiguous at the start of
-// the workspace and go up in one copy (the status word is cleared with it).
+// The header, mode flags, descriptors and order are contiguous at the start
+// of the workspace and go up in one copy (the status word and the flags are
+// cleared with it); the chunk table after them is built on the device.
 std::vector<uint8_t> pack_plan(const Plan &p) {
-    std::vector<uint8_t> buf(p.lay.node, 0);
+    std::vector<uint8_t> buf(p.lay.chunks, 0);
     std::memcpy(buf.data() + p.lay.desc, p.desc.data(), sizeof(SampleDesc) * p.desc.size());
     std::memcpy(buf.data() + p.lay.order, p.order.data(), sizeof(int32_t) * p.order.size());
-    std::memcpy(buf.data() + p.lay.chunks, p.chunks.data(), sizeof(ChunkDesc) * p.chunks.size());
     return buf;
 }
 
@@ -448,6 +427,7 @@ rnnt_status loss_impl(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V
     a.max_U1 = plan.max_U1;
     a.aligned16 = aligned16;
 
+    if (plan.lay.n_chunks > 0 && launch_plan(a, stream) != hipSuccess) return RNNT_EXECUTION_FAILED;
     if (plan.lay.n_chunks > 0 && timed(0, stream, [&] { return launch_rowstats(a, stream); }) != hipSuccess)
         return RNNT_EXECUTION_FAILED;
     if (timed(1, stream, [&] { return launch_alpha_beta(a, stream); }) != hipSuccess) return RNNT_EXECUTION_FAILED;

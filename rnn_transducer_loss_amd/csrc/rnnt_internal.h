@@ -2,7 +2,7 @@
 // its gfx950 kernels (rnnt_kernels.hip).  Not part of the public ABI.
 #pragma once
 
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -32,7 +32,7 @@ struct SampleDesc {
     int32_t index;  // position of the sample in the batch (targets row)
     int32_t U1p;
     int32_t tstride;  // rows between (t,u) and (t+1,u)
-    int32_t pad;
+    int32_t chunk0;   // index of the sample's first chunk in the chunk table
 };
 
 // Padded width of a lattice of width U1 in the alpha/beta sweeps (a 64-wide
@@ -58,8 +58,44 @@ struct ChunkDesc {
     int32_t col;
 };
 
+// Lattice nodes of a T x (U+1) lattice on the anti-diagonals before n
+// (diagonal m holds columns max(0, m-T+1) .. min(m, U)).
+__host__ __device__ inline int64_t diag_prefix(int64_t n, int64_t T, int64_t U) {
+    const int64_t a = (n <= U + 1) ? n * (n + 1) / 2 : (U + 1) * (U + 2) / 2 + (n - U - 1) * (U + 1);
+    const int64_t b = (n <= T) ? 0 : (n - T) * (n - T + 1) / 2;
+    return a - b;
+}
+
+// Node number r0 of the lattice in anti-diagonal order (diagonal n, then
+// column u): the largest n with diag_prefix(n) <= r0, found by bisection.
+__host__ __device__ inline void diag_start(int32_t T, int32_t U, int64_t r0, int32_t &n, int32_t &u) {
+    int64_t lo = 0, hi = (int64_t)T + U - 1;  // diag_prefix(lo) <= r0 < diag_prefix(hi + 1)
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) / 2;
+        if (diag_prefix(mid, T, U) <= r0) lo = mid;
+        else hi = mid - 1;
+    }
+    n = (int32_t)lo;
+    const int64_t first = lo - T + 1 > 0 ? lo - T + 1 : 0;
+    u = (int32_t)(first + (r0 - diag_prefix(lo, T, U)));
+}
+
+// Chunk j of sample `sample` (descriptor d): rows j*rpc .. in row order, the
+// same count of nodes in anti-diagonal order from (diag, col).
+__host__ __device__ inline ChunkDesc make_chunk(const SampleDesc &d, int32_t sample, int32_t j, int32_t rpc) {
+    const int64_t rows = (int64_t)d.T * (d.U + 1);
+    const int64_t r0 = (int64_t)j * rpc;
+    ChunkDesc c;
+    c.sample = sample;
+    c.row_begin = (int32_t)r0;
+    c.count = (int32_t)(rows - r0 < rpc ? rows - r0 : rpc);
+    diag_start(d.T, d.U, r0, c.diag, c.col);
+    return c;
+}
+
 // Byte offsets of the workspace regions (each 256-byte aligned).  Everything
-// before `node` is written by the per-call upload.  Per skewed slot:
+// before `chunks` is written by the per-call upload; the chunk table is built
+// on the device from the sample descriptors (launch_plan).  Per skewed slot:
 //   node  {log P(blank), log P(next label), log-sum-exp of the row (fused) or
 //         0, the next label as int bits (-1 if none)};
 //   prob  {P(blank), P(next label)} in fp32.
@@ -83,6 +119,7 @@ struct WorkspaceLayout {
     int32_t n_chunks;
     int32_t rows_per_chunk;
     int32_t first_cached_chunk;  // rowstats: chunks from here on use caching loads
+    int32_t max_sample_chunks;   // most chunks of any one sample
 };
 
 // Row-pass geometry chosen from V and the element size.
@@ -121,6 +158,7 @@ struct LaunchArgs {
     bool aligned16;
 };
 
+hipError_t launch_plan(const LaunchArgs &a, hipStream_t stream);
 hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream);
 hipError_t launch_alpha_beta(const LaunchArgs &a, hipStream_t stream);
 hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream);

@@ -315,6 +315,21 @@ __device__ __forceinline__ void advance_diag(int &n, int &u, int step, int T, in
     }
 }
 
+// ------------------------------------------------------------ chunk table
+// Workgroup i*GX + x writes chunks 256x .. 256x+255 of sample i, with the
+// arithmetic the host uses to describe the schedule (make_chunk), so only
+// the sample descriptors travel from the host each call.
+__global__ __launch_bounds__(256) void k_plan(const SampleDesc *__restrict__ desc, int rpc, int gx,
+                                              ChunkDesc *__restrict__ chunks) {
+    const int i = (int)(blockIdx.x / (unsigned)gx);
+    const int x = (int)(blockIdx.x % (unsigned)gx);
+    const SampleDesc d = desc[i];
+    const int64_t rows = (int64_t)d.T * (d.U + 1);
+    const int n = (int)((rows + rpc - 1) / rpc);
+    const int j = x * 256 + threadIdx.x;
+    if (j < n) chunks[d.chunk0 + j] = make_chunk(d, i, j, rpc);
+}
+
 // --------------------------------------------- K1 rowstats, one row per wave
 // Lane l holds elements (i*64 + l)*VEC .. +VEC-1 of a row, i < NV.  The
 // chunk's nodes are walked in diagonal order, so the per-node outputs of the
@@ -1262,6 +1277,13 @@ RowGeom row_geometry(int V, int esize, bool aligned16) {
 }
 
 #define WS(type, field) reinterpret_cast<type>(a.ws + a.lay.field)
+
+hipError_t launch_plan(const LaunchArgs &a, hipStream_t stream) {
+    const int gx = (a.lay.max_sample_chunks + 255) / 256;
+    hipLaunchKernelGGL(k_plan, dim3((unsigned)((int64_t)gx * a.B)), dim3(256), 0, stream, WS(const SampleDesc *, desc),
+                       a.lay.rows_per_chunk, gx, WS(ChunkDesc *, chunks));
+    return hipGetLastError();
+}
 
 hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream) {
     const dim3 grid(a.lay.n_chunks), block(256);
