@@ -234,6 +234,7 @@ struct PlanEntry {
     std::vector<int32_t> key;
     Plan plan;
     std::vector<uint8_t> packed;
+    std::unique_ptr<PlanArgs> args;  // batches of up to kArgSamples samples
 };
 std::mutex g_plan_mu;
 std::shared_ptr<const PlanEntry> g_plan_cache;
@@ -268,6 +269,14 @@ rnnt_status get_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t *
         if (st != RNNT_SUCCESS) return st;
         e->key = std::move(key);
         e->packed = pack_plan(e->plan);
+        if (B <= kArgSamples) {
+            e->args.reset(new PlanArgs{});
+            e->args->B = B;
+            for (int32_t i = 0; i < B; ++i) {
+                e->args->desc[i] = e->plan.desc[i];
+                e->args->order[i] = e->plan.order[i];
+            }
+        }
         std::lock_guard<std::mutex> lk(g_plan_mu);
         g_plan_cache = e;
         out = e;
@@ -402,8 +411,10 @@ rnnt_status loss_impl(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V
     if ((uintptr_t)workspace % kAlign != 0) return RNNT_INVALID_VALUE;
 
     const RowGeom geom = row_geometry(V, es, aligned16);
-    st = upload(workspace, e->packed, stream);
-    if (st != RNNT_SUCCESS) return st;
+    if (!e->args) {
+        st = upload(workspace, e->packed, stream);
+        if (st != RNNT_SUCCESS) return st;
+    }
 
     LaunchArgs a{};
     a.logits = logits;
@@ -427,7 +438,7 @@ rnnt_status loss_impl(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V
     a.max_U1 = plan.max_U1;
     a.aligned16 = aligned16;
 
-    if (plan.lay.n_chunks > 0 && launch_plan(a, stream) != hipSuccess) return RNNT_EXECUTION_FAILED;
+    if (launch_plan(a, e->args.get(), stream) != hipSuccess) return RNNT_EXECUTION_FAILED;
     if (plan.lay.n_chunks > 0 && timed(0, stream, [&] { return launch_rowstats(a, stream); }) != hipSuccess)
         return RNNT_EXECUTION_FAILED;
     if (timed(1, stream, [&] { return launch_alpha_beta(a, stream); }) != hipSuccess) return RNNT_EXECUTION_FAILED;

@@ -158,7 +158,20 @@ struct LaunchArgs {
     bool aligned16;
 };
 
-hipError_t launch_plan(const LaunchArgs &a, hipStream_t stream);
+// Batches of up to kArgSamples samples pass their descriptors and order to
+// the chunk-table kernel as kernel arguments; it writes them, clears the
+// status word and the mode flags, and no host-to-device copy is needed.
+constexpr int kArgSamples = 64;
+struct PlanArgs {
+    int32_t B;
+    int32_t pad;
+    SampleDesc desc[kArgSamples];
+    int32_t order[kArgSamples];
+};
+static_assert(sizeof(PlanArgs) <= 3900, "kernel arguments are limited to 4 KiB");
+
+// `pa` null: the descriptors were uploaded with the workspace header.
+hipError_t launch_plan(const LaunchArgs &a, const PlanArgs *pa, hipStream_t stream);
 hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream);
 hipError_t launch_alpha_beta(const LaunchArgs &a, hipStream_t stream);
 hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream);

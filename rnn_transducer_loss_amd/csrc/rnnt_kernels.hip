@@ -318,12 +318,24 @@ __device__ __forceinline__ void advance_diag(int &n, int &u, int step, int T, in
 // ------------------------------------------------------------ chunk table
 // Workgroup i*GX + x writes chunks 256x .. 256x+255 of sample i, with the
 // arithmetic the host uses to describe the schedule (make_chunk), so only
-// the sample descriptors travel from the host each call.
+// the sample descriptors travel from the host each call.  ARGS: the
+// descriptors and order come as kernel arguments; workgroup 0 also writes
+// them to the workspace and clears the status word and the mode flags.
+template <bool ARGS>
 __global__ __launch_bounds__(256) void k_plan(const SampleDesc *__restrict__ desc, int rpc, int gx,
-                                              ChunkDesc *__restrict__ chunks) {
+                                              ChunkDesc *__restrict__ chunks, PlanArgs pa, SampleDesc *ws_desc,
+                                              int32_t *ws_order, int *ws_mode, uint32_t *ws_status) {
     const int i = (int)(blockIdx.x / (unsigned)gx);
     const int x = (int)(blockIdx.x % (unsigned)gx);
-    const SampleDesc d = desc[i];
+    const SampleDesc d = ARGS ? pa.desc[i] : desc[i];
+    if (ARGS && blockIdx.x == 0) {
+        for (int k = threadIdx.x; k < pa.B; k += blockDim.x) {
+            ws_desc[k] = pa.desc[k];
+            ws_order[k] = pa.order[k];
+            ws_mode[k] = 0;
+        }
+        if (threadIdx.x == 0) *ws_status = 0u;
+    }
     const int64_t rows = (int64_t)d.T * (d.U + 1);
     const int n = (int)((rows + rpc - 1) / rpc);
     const int j = x * 256 + threadIdx.x;
@@ -1278,10 +1290,16 @@ RowGeom row_geometry(int V, int esize, bool aligned16) {
 
 #define WS(type, field) reinterpret_cast<type>(a.ws + a.lay.field)
 
-hipError_t launch_plan(const LaunchArgs &a, hipStream_t stream) {
+hipError_t launch_plan(const LaunchArgs &a, const PlanArgs *pa, hipStream_t stream) {
     const int gx = (a.lay.max_sample_chunks + 255) / 256;
-    hipLaunchKernelGGL(k_plan, dim3((unsigned)((int64_t)gx * a.B)), dim3(256), 0, stream, WS(const SampleDesc *, desc),
-                       a.lay.rows_per_chunk, gx, WS(ChunkDesc *, chunks));
+    const dim3 grid((unsigned)((int64_t)gx * a.B)), block(256);
+    if (pa)
+        hipLaunchKernelGGL(k_plan<true>, grid, block, 0, stream, WS(const SampleDesc *, desc), a.lay.rows_per_chunk,
+                           gx, WS(ChunkDesc *, chunks), *pa, WS(SampleDesc *, desc), WS(int32_t *, order),
+                           WS(int *, mode), WS(uint32_t *, status));
+    else
+        hipLaunchKernelGGL(k_plan<false>, grid, block, 0, stream, WS(const SampleDesc *, desc), a.lay.rows_per_chunk,
+                           gx, WS(ChunkDesc *, chunks), PlanArgs{}, nullptr, nullptr, nullptr, nullptr);
     return hipGetLastError();
 }
 
