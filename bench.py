@@ -85,8 +85,13 @@ def committed_traffic(kernel: str, workload: str):
     return None
 
 
-def cpu_baseline(w, budget_s: float = 12.0):
-    """The fp64 oracle on this host's cores over a bounded set of the batch's samples."""
+def cpu_baseline(w, budget_s: float = 12.0, min_wall_s: float = 1.5):
+    """The fp64 oracle on this host's cores over a bounded set of the batch's samples.
+
+    Samples go out one per thread in batch order until ``budget_s`` of wall time is spent; when the whole batch
+    takes less than ``min_wall_s`` it is run again (whole passes) until that much time has passed, so the rate
+    rests on ~10-30 s of CPU work.
+    """
     import concurrent.futures as cf
     import numpy as np
     import oracle
@@ -107,27 +112,33 @@ def cpu_baseline(w, budget_s: float = 12.0):
                           w.clamp, want_grad=True)
         return int(rows[i]) * w.V, r.loss
 
-    done_elems, done_samples = 0, 0
+    done_elems, done_samples, passes = 0, 0, 0
     elapsed = 0.0
     with cf.ThreadPoolExecutor(threads) as ex:
-        k = 0
-        while k < len(cand) and elapsed < budget_s:
-            wave = cand[k:k + threads]
-            k += len(wave)
-            for i in wave:
-                host[i] = w.logits[w.rows(i)].cpu().numpy()
-            t0 = time.perf_counter()
-            for n, _ in ex.map(one, wave):
-                done_elems += n
-            elapsed += time.perf_counter() - t0
-            done_samples += len(wave)
-            for i in wave:
-                host.pop(i, None)
+        while True:
+            k = 0
+            while k < len(cand) and elapsed < budget_s:
+                wave = cand[k:k + threads]
+                k += len(wave)
+                for i in wave:
+                    host[i] = w.logits[w.rows(i)].cpu().numpy()
+                t0 = time.perf_counter()
+                for n, _ in ex.map(one, wave):
+                    done_elems += n
+                elapsed += time.perf_counter() - t0
+                done_samples += len(wave)
+                for i in wave:
+                    host.pop(i, None)
+            passes += 1
+            if k < len(cand) or elapsed >= min_wall_s or not cand:
+                break
     if done_samples == 0:
         return None
+    what = (f"{passes} pass(es) over the {len(cand)} samples" if k >= len(cand)
+            else f"{done_samples} of {w.B} samples")
     return {"value": done_elems / elapsed, "unit": "elements/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done_samples} of {w.B} samples of the {w.name} batch ({done_elems} packed elements), "
-                      f"loss and full gradient, fp64, one sample per thread, {elapsed:.2f} s wall"}
+            "sample": f"{what} of the {w.name} batch ({done_elems} packed elements), loss and full gradient, "
+                      f"fp64, one sample per thread, {elapsed:.2f} s wall"}
 
 
 def copy_calibration(steps: int):
