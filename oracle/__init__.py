@@ -11,7 +11,10 @@ lattice).  This module only builds/loads it and marshals numpy arrays.
 Semantics follow the rnnt-loss-ascend README (parameter table and usage
 example): ``blank`` in [-V, V-1] with negative values counted from the end,
 ``clamp <= 0`` disables clipping, and ``reduction`` is one of none / mean
-(batch mean) / sum.
+(batch mean) / sum.  ``fastemit_lambda`` (the GPURNNT parameter of the ESPnet
+multi-blank utilities page, defined by the FastEmit paper it refers to)
+multiplies the loss's derivative with respect to every label-emission
+log-probability by (1 + lambda); the loss value itself is unchanged.
 """
 from __future__ import annotations
 
@@ -57,7 +60,7 @@ def _load():
             lib.rnnt_oracle_sample.restype = ctypes.c_int
             lib.rnnt_oracle_sample_ex.argtypes = [
                 ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double,
                 ctypes.POINTER(ctypes.c_int64), ctypes.c_long, dp, dp, dp, dp, dp]
             lib.rnnt_oracle_sample_ex.restype = ctypes.c_int
             lib.rnnt_oracle_half_to_double.argtypes = [ctypes.c_uint16]
@@ -99,7 +102,8 @@ def half_to_double(h: int) -> float:
 
 
 def sample(x, T: int, U: int, y, blank: int, fused: bool = True, clamp: float = -1.0,
-           want_grad: bool = True, want_tables: bool = False, rows=None) -> SampleResult:
+           want_grad: bool = True, want_tables: bool = False, rows=None,
+           fastemit_lambda: float = 0.0) -> SampleResult:
     """Loss (and optionally gradient / alpha / beta tables) of one sample.
 
     ``x`` holds the sample's T*(U+1) rows of V values as float64, float32 or
@@ -132,7 +136,7 @@ def sample(x, T: int, U: int, y, blank: int, fused: bool = True, clamp: float = 
     lb = ctypes.c_double()
     rc = lib.rnnt_oracle_sample_ex(
         x.ctypes.data_as(ctypes.c_void_p), _DT[x.dtype], T, U, V, yy.ctypes.data_as(ctypes.POINTER(ctypes.c_int)),
-        int(blank), int(bool(fused)), float(clamp),
+        int(blank), int(bool(fused)), float(clamp), float(fastemit_lambda),
         rr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)) if rr is not None else None, nr,
         _ptr(grad), _ptr(al), _ptr(be), ctypes.byref(la), ctypes.byref(lb))
     if rc == ORACLE_BAD_TARGET:
@@ -143,7 +147,7 @@ def sample(x, T: int, U: int, y, blank: int, fused: bool = True, clamp: float = 
 
 
 def batch(logits, targets, logit_lengths, target_lengths, blank: int = -1, clamp: float = -1.0,
-          reduction: str = "mean", fused: bool = True, want_grad: bool = True):
+          reduction: str = "mean", fused: bool = True, want_grad: bool = True, fastemit_lambda: float = 0.0):
     """Whole-batch oracle over the packed (sum_i T_i*(U_i+1), V) layout.
 
     Returns ``(loss_per_sample, reduced_loss, grad_per_sample, grad_reduced)``.
@@ -168,7 +172,7 @@ def batch(logits, targets, logit_lengths, target_lengths, blank: int = -1, clamp
     off = 0
     for i in range(B):
         res = sample(logits[off:off + rows[i]], Ts[i], Us[i], np.asarray(targets[i]), b, fused, clamp,
-                     want_grad=want_grad)
+                     want_grad=want_grad, fastemit_lambda=fastemit_lambda)
         losses[i] = res.loss
         if want_grad:
             grad[off:off + rows[i]] = res.grad

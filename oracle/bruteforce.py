@@ -11,6 +11,9 @@ each path's probability is a product along the path.
 
 The gradient is the expected number of times each (node, symbol) edge is used,
 pushed through the log_softmax Jacobian written as an explicit V x V matrix.
+With ``fastemit_lambda`` the label edges' expected uses count (1 + lambda)
+times (the FastEmit gradient rule, read from the paper the GPURNNT parameter
+list of the ESPnet multi-blank utilities page refers to).
 """
 from __future__ import annotations
 
@@ -49,7 +52,7 @@ def _log_probs(x: np.ndarray, fused: bool) -> np.ndarray:
     return out
 
 
-def sample(x, T: int, U: int, y, blank: int, fused: bool = True):
+def sample(x, T: int, U: int, y, blank: int, fused: bool = True, fastemit_lambda: float = 0.0):
     """Return (loss, grad) of one sample by full path enumeration."""
     x = np.asarray(x, dtype=np.float64)
     V = x.shape[1]
@@ -69,13 +72,14 @@ def sample(x, T: int, U: int, y, blank: int, fused: bool = True):
     Z = sum(math.exp(p - m) for p in path_logp)
     loss = -(m + math.log(Z))
 
-    # d loss / d lp(node, k) = - E[number of uses of edge (node, k)].
+    # d loss / d lp(node, k) = - E[number of uses of edge (node, k)]; a label
+    # edge's uses weigh (1 + fastemit_lambda).
     d_lp = np.zeros_like(lp)
     for p, steps in zip(path_logp, path_steps):
         w = math.exp(p - m) / Z
         for (t, u, e) in steps:
             k = blank if e == "blank" else int(y[u])
-            d_lp[t * U1 + u, k] -= w
+            d_lp[t * U1 + u, k] -= w if e == "blank" else w * (1.0 + fastemit_lambda)
     if not fused:
         return loss, d_lp
     grad = np.zeros_like(lp)

@@ -37,6 +37,14 @@
  *  - Clamp (README "Operator features": for clamp > 0 every gradient element
  *    is clipped to [-clamp, clamp]; clamp <= 0 disables it).
  *
+ *  - FastEmit (the GPURNNT parameter list of the ESPnet multi-blank utilities
+ *    page names fastemit_lambda as the scale of the FastEmit regularisation
+ *    and defers its definition to the FastEmit paper, Yu et al. 2021).  The
+ *    reading taken here is that paper's gradient rule: the derivative of the
+ *    loss with respect to every label-emission log-probability is multiplied
+ *    by (1 + lambda), the blank emissions keep theirs, and the reported loss
+ *    value is the unregularised one.  lambda = 0 is the plain loss.
+ *
  * The loops run row-major over (t,u), never along anti-diagonals, so the
  * oracle has no structure in common with the GPU kernels.
  */
@@ -110,6 +118,8 @@ static double row_logsumexp(const void *x, int dtype, long r, int V)
  *   blank    already normalised to [0,V).
  *   grad_rows, n_grad_rows   sample-local rows whose gradient is wanted
  *            (NULL with n_grad_rows < 0 means every row, in order).
+ *   fastemit_lambda  >= 0; scales the label-emission derivatives by
+ *            (1 + fastemit_lambda) (0: the plain gradient).
  *   grad     optional n x V output (n = rows requested): d loss / d x of
  *            those rows, clamped if clamp > 0.
  *   alpha, beta  optional T*(U+1) outputs of the log forward / backward
@@ -119,10 +129,12 @@ static double row_logsumexp(const void *x, int dtype, long r, int V)
  * Returns ORACLE_OK or an error code.
  */
 int rnnt_oracle_sample_ex(const void *x, int dtype, int T, int U, int V, const int *y, int blank, int fused,
-                          double clamp, const int64_t *grad_rows, long n_grad_rows, double *grad,
-                          double *alpha_out, double *beta_out, double *loss_alpha, double *loss_beta)
+                          double clamp, double fastemit_lambda, const int64_t *grad_rows, long n_grad_rows,
+                          double *grad, double *alpha_out, double *beta_out, double *loss_alpha,
+                          double *loss_beta)
 {
     if (T < 1 || U < 0 || V < 1 || blank < 0 || blank >= V) return ORACLE_BAD_ARGS;
+    if (!(fastemit_lambda >= 0.0) || isinf(fastemit_lambda)) return ORACLE_BAD_ARGS;
     if (dtype != ORACLE_F64 && dtype != ORACLE_F32 && dtype != ORACLE_F16) return ORACLE_BAD_ARGS;
     for (int u = 0; u < U; ++u)
         if (y[u] < 0 || y[u] >= V || y[u] == blank) return ORACLE_BAD_TARGET;
@@ -204,6 +216,8 @@ int rnnt_oracle_sample_ex(const void *x, int dtype, int T, int U, int V, const i
                 if (u < U)
                     d_label = -exp(al[c] + lpy[c] + be[c + 1] - logz);
             }
+            /* FastEmit: the label edge's derivative weighted by (1 + lambda). */
+            d_label *= 1.0 + fastemit_lambda;
             for (int k = 0; k < V; ++k) g[k] = 0.0;
             g[blank] += d_blank;
             if (u < U) g[y[u]] += d_label;
@@ -231,6 +245,6 @@ int rnnt_oracle_sample_ex(const void *x, int dtype, int T, int U, int V, const i
 int rnnt_oracle_sample(const double *x, int T, int U, int V, const int *y, int blank, int fused, double clamp,
                        double *grad, double *alpha_out, double *beta_out, double *loss_alpha, double *loss_beta)
 {
-    return rnnt_oracle_sample_ex(x, ORACLE_F64, T, U, V, y, blank, fused, clamp, NULL, -1, grad, alpha_out,
+    return rnnt_oracle_sample_ex(x, ORACLE_F64, T, U, V, y, blank, fused, clamp, 0.0, NULL, -1, grad, alpha_out,
                                  beta_out, loss_alpha, loss_beta);
 }

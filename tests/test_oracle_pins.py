@@ -318,3 +318,102 @@ def test_native_dtypes_and_row_subsets():
         rows = [7, 0, T * (U + 1) - 1, 3]
         c = oracle.sample(xd, T, U, y, blank, True, rows=rows)
         np.testing.assert_array_equal(c.grad, a.grad[rows])
+
+
+# FastEmit (fastemit_lambda of the GPURNNT parameter list on the ESPnet
+# multi-blank utilities page, defined by the FastEmit paper it refers to):
+# the derivative with respect to every label-emission log-probability is
+# weighted by (1 + lambda); blank emissions and the loss value are unchanged.
+
+@pytest.mark.parametrize("lam", [0.01, 0.5, 2.0])
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("T,U", [(1, 3), (3, 2), (4, 3), (2, 5), (6, 4)])
+def test_fastemit_bruteforce(T, U, fused, lam):
+    rng = np.random.default_rng(1000 * T + 10 * U + int(fused))
+    V, blank = 6, 0
+    x, y = _rand_case(rng, T, U, V, blank, std=1.5)
+    if not fused:
+        x = sp_log_softmax(x, axis=1) + rng.normal(0, 0.1, size=x.shape)
+    bf_loss, bf_grad = bruteforce.sample(x, T, U, y, blank, fused, fastemit_lambda=lam)
+    r = oracle.sample(x, T, U, y, blank, fused, fastemit_lambda=lam)
+    assert abs(r.loss - bf_loss) <= 1e-12 * max(1.0, abs(bf_loss))
+    np.testing.assert_allclose(r.grad, bf_grad, atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("T,U,V,blank,lam", [(3, 2, 5, 4, 0.3), (7, 3, 6, 0, 0.01), (12, 4, 16, 15, 1.5)])
+def test_fastemit_zero_logits_closed_form(T, U, V, blank, lam):
+    """All-zero logits, with the path-count flows of the plain closed form:
+    grad_k = (occ + lam flow_y)/V - [k=blank] flow_b - [k=y_{u+1}] (1+lam) flow_y."""
+    rng = np.random.default_rng(T * 17 + U)
+    ids = [k for k in range(V) if k != blank]
+    y = rng.choice(ids, size=U)
+    x = np.zeros((T * (U + 1), V))
+    r = oracle.sample(x, T, U, y, blank, True, fastemit_lambda=lam)
+    C = math.comb
+    total = C(T - 1 + U, U)
+    expect = np.zeros_like(x)
+    for t in range(T):
+        for u in range(U + 1):
+            row = t * (U + 1) + u
+            occ = C(t + u, u) * C(T - 1 - t + U - u, U - u) / total
+            fb = (C(t + u, u) * C(T - 2 - t + U - u, U - u) / total if t < T - 1
+                  else (occ if u == U else 0.0))
+            fy = C(t + u, u) * C(T - 2 - t + U - u, U - u - 1) / total if u < U else 0.0
+            expect[row, :] = (occ + lam * fy) / V
+            expect[row, blank] -= fb
+            if u < U:
+                expect[row, y[u]] -= (1.0 + lam) * fy
+    np.testing.assert_allclose(r.grad, expect, atol=1e-14, rtol=0)
+
+
+def test_fastemit_invariants():
+    """Loss unchanged; fused rows still sum to zero; the non-fused gradient sums to -(T + (1+lam) U) with the
+    blank column untouched."""
+    rng = np.random.default_rng(21)
+    T, U, V, blank, lam = 30, 9, 17, 16, 0.25
+    x, y = _rand_case(rng, T, U, V, blank, std=2.0)
+    a = oracle.sample(x, T, U, y, blank, True)
+    b = oracle.sample(x, T, U, y, blank, True, fastemit_lambda=lam)
+    assert a.loss == b.loss and a.loss_alpha == b.loss_alpha
+    assert np.abs(b.grad.sum(axis=1)).max() < 1e-13
+    lp = sp_log_softmax(x, axis=1)
+    n0 = oracle.sample(lp, T, U, y, blank, False)
+    n1 = oracle.sample(lp, T, U, y, blank, False, fastemit_lambda=lam)
+    assert abs(n1.grad.sum() + (T + (1 + lam) * U)) < 1e-10
+    np.testing.assert_array_equal(n1.grad[:, blank], n0.grad[:, blank])
+    with pytest.raises(ValueError):
+        oracle.sample(x, T, U, y, blank, True, fastemit_lambda=-0.1)
+    with pytest.raises(ValueError):
+        oracle.sample(x, T, U, y, blank, True, fastemit_lambda=float("inf"))
+
+
+def test_fastemit_finite_differences():
+    """Central differences split the fused gradient into its label-emission part: perturbing x only where it
+    enters the label log-probabilities (the blank log-probabilities keep the unperturbed x).  FastEmit adds
+    lam times that part to the full derivative."""
+    rng = np.random.default_rng(22)
+    T, U, V, blank, lam = 6, 4, 7, 0, 0.7
+    x, y = _rand_case(rng, T, U, V, blank)
+    g = oracle.sample(x, T, U, y, blank, True, fastemit_lambda=lam).grad
+    lp0 = sp_log_softmax(x, axis=1)
+    U1 = U + 1
+
+    def loss_full(xx):
+        return oracle.sample(xx, T, U, y, blank, True, want_grad=False).loss
+
+    def loss_label_only(xx, r):
+        lp = lp0.copy()
+        u = r % U1
+        if u < U:
+            lp[r, y[u]] = sp_log_softmax(xx[r])[y[u]]
+        return oracle.sample(lp, T, U, y, blank, False, want_grad=False).loss
+
+    eps = 1e-6
+    for _ in range(40):
+        r = int(rng.integers(0, x.shape[0]))
+        k = int(rng.integers(0, V))
+        xp = x.copy(); xp[r, k] += eps
+        xm = x.copy(); xm[r, k] -= eps
+        fd_full = (loss_full(xp) - loss_full(xm)) / (2 * eps)
+        fd_label = (loss_label_only(xp, r) - loss_label_only(xm, r)) / (2 * eps)
+        assert abs(fd_full + lam * fd_label - g[r, k]) < 1e-8, (r, k)
