@@ -85,7 +85,7 @@ def committed_traffic(kernel: str, workload: str):
     return None
 
 
-def cpu_baseline(w, budget_s: float = 12.0, min_wall_s: float = 1.5):
+def cpu_baseline(w, budget_s: float = 12.0, min_wall_s: float = 1.5, fastemit_lambda: float = 0.0):
     """The fp64 oracle on this host's cores over a bounded set of the batch's samples.
 
     Samples go out one per thread in batch order until ``budget_s`` of wall time is spent; when the whole batch
@@ -109,7 +109,7 @@ def cpu_baseline(w, budget_s: float = 12.0, min_wall_s: float = 1.5):
 
     def one(i):
         r = oracle.sample(host[i], int(w.logit_lengths[i]), int(w.target_lengths[i]), w.targets[i], b, w.fused,
-                          w.clamp, want_grad=True)
+                          w.clamp, want_grad=True, fastemit_lambda=fastemit_lambda)
         return int(rows[i]) * w.V, r.loss
 
     done_elems, done_samples, passes = 0, 0, 0
@@ -167,6 +167,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="bpe", choices=["tiny", "char", "bpe", "half", "skewed"])
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--fastemit-lambda", type=float, default=0.0,
+                    help="FastEmit weight on the label-emission gradient (0: the plain loss)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -200,7 +202,8 @@ def main():
 
     def step():
         rl.rnnt_loss_fused(w.logits, tg, T, U, blank=w.blank, clamp=w.clamp, reduction=w.reduction,
-                           fused_log_softmax=w.fused, grad=grad, workspace=ws, loss=loss, loss_reduced=red)
+                           fused_log_softmax=w.fused, grad=grad, workspace=ws, loss=loss, loss_reduced=red,
+                           fastemit_lambda=args.fastemit_lambda)
 
     print(f"bench: N={w.N} V={w.V} B={w.B}; warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -251,7 +254,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w)
+        cpu = cpu_baseline(w, fastemit_lambda=args.fastemit_lambda)
 
     out = {
         "metric": METRIC,
@@ -268,8 +271,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "V": w.V, "rows": w.N, "elements": w.N * w.V,
                    "io_dtype": "fp16" if esize(w.dtype) == 2 else "fp32", "fused_log_softmax": w.fused,
-                   "reduction": w.reduction, "clamp": w.clamp, "T_max": int(T.max()), "U_max": int(U.max()),
-                   "recursion_dtype": "f64"},
+                   "reduction": w.reduction, "clamp": w.clamp, "fastemit_lambda": args.fastemit_lambda,
+                   "T_max": int(T.max()), "U_max": int(U.max()), "recursion_dtype": "f64"},
         "effective_GBps": round(eff, 1),
         "effective_frac_of_peak": round(eff / PEAK_HBM_GBPS, 4),
         "algorithmic_bytes_per_step": ab["path"],

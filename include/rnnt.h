@@ -106,6 +106,14 @@ rnnt_status rnnt_loss_fused_workspace_size(int32_t B, int32_t V, int64_t N, rnnt
  *                     (-1 is V-1, -V is 0).
  *   clamp             > 0 clips each per-sample gradient element to
  *                     [-clamp, clamp]; <= 0 disables clipping.
+ *   fastemit_lambda   FastEmit regularisation weight, finite and >= 0 (the
+ *                     fastemit_lambda of the GPURNNT parameter list on the
+ *                     ESPnet multi-blank utilities page, defined by the
+ *                     FastEmit paper it refers to): the gradient with
+ *                     respect to every label-emission log-probability is
+ *                     multiplied by (1 + fastemit_lambda) before the
+ *                     log_softmax chain rule and the clamp; blank emissions
+ *                     and the loss value are unchanged.  0: the plain loss.
  *   fused_log_softmax non-zero: apply log_softmax over V at each node.
  *   reduction         RNNT_REDUCTION_NONE / _MEAN / _SUM.
  *   loss              device float[B]: per-sample loss -log P(y|x) (beta
@@ -121,7 +129,8 @@ rnnt_status rnnt_loss_fused_workspace_size(int32_t B, int32_t V, int64_t N, rnnt
  *   workspace         device, workspace_bytes >= the _workspace_size value.
  *   stream            hipStream_t for all device work.
  * Returns RNNT_INVALID_VALUE for a NULL required pointer, bad dtype or
- * reduction, V < 1, B < 1, blank out of range, T_i < 1, U_i < 0, U_i > 1023, U_i > S,
+ * reduction, V < 1, B < 1, blank out of range, fastemit_lambda negative or not
+ * finite, T_i < 1, U_i < 0, U_i > 1023, U_i > S,
  * sum_i T_i*(U_i+1) != N or partial overlap of grad and logits;
  * RNNT_WORKSPACE_TOO_SMALL; RNNT_MEMOPS_FAILED; RNNT_EXECUTION_FAILED.
  * Invalid label values are only visible on the device: they set
@@ -131,8 +140,8 @@ rnnt_status rnnt_loss_fused_workspace_size(int32_t B, int32_t V, int64_t N, rnnt
 rnnt_status rnnt_loss_fused(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V,
                             const int32_t *targets, int32_t S,
                             const int32_t *logit_lengths, const int32_t *target_lengths, int32_t B,
-                            int64_t blank, float clamp, int fused_log_softmax, rnnt_reduction reduction,
-                            float *loss, float *loss_reduced, void *grad,
+                            int64_t blank, float clamp, float fastemit_lambda, int fused_log_softmax,
+                            rnnt_reduction reduction, float *loss, float *loss_reduced, void *grad,
                             void *workspace, size_t workspace_bytes, rnnt_stream_t stream);
 
 /*
@@ -179,8 +188,9 @@ rnnt_status rnnt_loss_padded_workspace_size(int32_t B, int32_t V, int32_t max_T,
 rnnt_status rnnt_loss_padded(const void *logits, rnnt_dtype dtype, int32_t max_T, int32_t max_U1, int32_t V,
                              const int32_t *targets, int32_t S, const int32_t *logit_lengths,
                              const int32_t *target_lengths, int32_t B, int64_t blank, float clamp,
-                             int fused_log_softmax, rnnt_reduction reduction, float *loss, float *loss_reduced,
-                             void *grad, void *workspace, size_t workspace_bytes, rnnt_stream_t stream);
+                             float fastemit_lambda, int fused_log_softmax, rnnt_reduction reduction, float *loss,
+                             float *loss_reduced, void *grad, void *workspace, size_t workspace_bytes,
+                             rnnt_stream_t stream);
 
 /*
  * rnnt_grad_scale for a gradient written by rnnt_loss_padded (all

@@ -54,8 +54,9 @@ def load():
                                                        _i32p, _i32p, ctypes.POINTER(ctypes.c_size_t)]
         lib.rnnt_loss_fused_workspace_size.restype = ctypes.c_int
         lib.rnnt_loss_fused.argtypes = [_vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, _vp, ctypes.c_int32,
-                                        _i32p, _i32p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_int,
-                                        ctypes.c_int, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+                                        _i32p, _i32p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                                        ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                        ctypes.c_size_t, _vp]
         lib.rnnt_loss_fused.restype = ctypes.c_int
         lib.rnnt_grad_scale.argtypes = [_vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, _i32p, _i32p,
                                         ctypes.c_int32, _vp, ctypes.c_int, _vp, ctypes.c_size_t, _vp]
@@ -66,7 +67,8 @@ def load():
         lib.rnnt_loss_padded_workspace_size.restype = ctypes.c_int
         lib.rnnt_loss_padded.argtypes = [_vp, ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp,
                                          ctypes.c_int32, _i32p, _i32p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
-                                         ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+                                         ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                         ctypes.c_size_t, _vp]
         lib.rnnt_loss_padded.restype = ctypes.c_int
         lib.rnnt_grad_scale_padded.argtypes = [_vp, ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                _i32p, _i32p, ctypes.c_int32, _vp, ctypes.c_int, _vp, ctypes.c_size_t,
@@ -127,7 +129,8 @@ def workspace_size(B: int, V: int, N: int, dtype_code: int, logit_lengths, targe
 
 def loss_fused(logits_ptr: int, dtype_code: int, N: int, V: int, targets_ptr: int, S: int, logit_lengths,
                target_lengths, blank: int, clamp: float, fused: bool, reduction: str, loss_ptr: int,
-               loss_reduced_ptr: int, grad_ptr: int, ws_ptr: int, ws_bytes: int, stream: int):
+               loss_reduced_ptr: int, grad_ptr: int, ws_ptr: int, ws_bytes: int, stream: int,
+               fastemit_lambda: float = 0.0):
     T = host_i32(logit_lengths)
     U = host_i32(target_lengths)
     B = len(T)
@@ -136,7 +139,8 @@ def loss_fused(logits_ptr: int, dtype_code: int, N: int, V: int, targets_ptr: in
     if reduction not in REDUCTIONS:
         raise ValueError(f"reduction must be one of {sorted(REDUCTIONS)}")
     rc = load().rnnt_loss_fused(logits_ptr or None, dtype_code, N, V, targets_ptr or None, S, _p(T), _p(U), B,
-                                int(blank), float(clamp), int(bool(fused)), REDUCTIONS[reduction], loss_ptr or None,
+                                int(blank), float(clamp), float(fastemit_lambda), int(bool(fused)),
+                                REDUCTIONS[reduction], loss_ptr or None,
                                 loss_reduced_ptr or None, grad_ptr or None, ws_ptr or None, ws_bytes,
                                 stream or None)
     check(rc, "rnnt_loss_fused")
@@ -165,7 +169,8 @@ def workspace_size_padded(B: int, V: int, max_T: int, max_U1: int, dtype_code: i
 
 def loss_padded(logits_ptr: int, dtype_code: int, max_T: int, max_U1: int, V: int, targets_ptr: int, S: int,
                 logit_lengths, target_lengths, blank: int, clamp: float, fused: bool, reduction: str, loss_ptr: int,
-                loss_reduced_ptr: int, grad_ptr: int, ws_ptr: int, ws_bytes: int, stream: int):
+                loss_reduced_ptr: int, grad_ptr: int, ws_ptr: int, ws_bytes: int, stream: int,
+                fastemit_lambda: float = 0.0):
     T = host_i32(logit_lengths)
     U = host_i32(target_lengths)
     B = len(T)
@@ -174,7 +179,8 @@ def loss_padded(logits_ptr: int, dtype_code: int, max_T: int, max_U1: int, V: in
     if reduction not in REDUCTIONS:
         raise ValueError(f"reduction must be one of {sorted(REDUCTIONS)}")
     rc = load().rnnt_loss_padded(logits_ptr or None, dtype_code, max_T, max_U1, V, targets_ptr or None, S, _p(T),
-                                 _p(U), B, int(blank), float(clamp), int(bool(fused)), REDUCTIONS[reduction],
+                                 _p(U), B, int(blank), float(clamp), float(fastemit_lambda), int(bool(fused)),
+                                 REDUCTIONS[reduction],
                                  loss_ptr or None, loss_reduced_ptr or None, grad_ptr or None, ws_ptr or None,
                                  ws_bytes, stream or None)
     check(rc, "rnnt_loss_padded")

@@ -10,6 +10,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <map>
 #include <memory>
@@ -384,14 +385,16 @@ namespace {
 // padded (B, max_T, max_U1, V) layout (pad on, N ignored).
 rnnt_status loss_impl(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V, const int32_t *targets, int32_t S,
                       const int32_t *logit_lengths, const int32_t *target_lengths, int32_t B, int64_t blank,
-                      float clamp, int fused_log_softmax, rnnt_reduction reduction, float *loss, float *loss_reduced,
-                      void *grad, void *workspace, size_t workspace_bytes, hipStream_t stream, const Padding &pad) {
+                      float clamp, float fastemit_lambda, int fused_log_softmax, rnnt_reduction reduction,
+                      float *loss, float *loss_reduced, void *grad, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream, const Padding &pad) {
     const int es = esize_of(dtype);
     if (!es || V < 1 || B < 1) return RNNT_INVALID_VALUE;
     if (pad.on() ? (pad.max_U1 < 1) : (N < 0)) return RNNT_INVALID_VALUE;
     if (reduction != RNNT_REDUCTION_NONE && reduction != RNNT_REDUCTION_MEAN && reduction != RNNT_REDUCTION_SUM)
         return RNNT_INVALID_VALUE;
     if (blank < -(int64_t)V || blank > (int64_t)V - 1) return RNNT_INVALID_VALUE;
+    if (!(fastemit_lambda >= 0.0f) || std::isinf(fastemit_lambda)) return RNNT_INVALID_VALUE;
     if (!logit_lengths || !target_lengths || !loss || !workspace) return RNNT_INVALID_VALUE;
     const int64_t rows = pad.on() ? (int64_t)B * pad.max_T * pad.max_U1 : N;
     if (rows > 0 && !logits) return RNNT_INVALID_VALUE;
@@ -427,6 +430,7 @@ rnnt_status loss_impl(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V
     a.blank = (int)(blank < 0 ? blank + V : blank);
     a.fused = fused_log_softmax ? 1 : 0;
     a.clamp = clamp;
+    a.fastemit = fastemit_lambda;
     a.grad_scale = reduction == RNNT_REDUCTION_MEAN ? 1.0f / (float)B : 1.0f;
     a.targets = targets;
     a.loss = loss;
@@ -479,11 +483,11 @@ extern "C" {
 
 rnnt_status rnnt_loss_fused(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V, const int32_t *targets,
                             int32_t S, const int32_t *logit_lengths, const int32_t *target_lengths, int32_t B,
-                            int64_t blank, float clamp, int fused_log_softmax, rnnt_reduction reduction,
-                            float *loss, float *loss_reduced, void *grad, void *workspace, size_t workspace_bytes,
-                            rnnt_stream_t stream) {
+                            int64_t blank, float clamp, float fastemit_lambda, int fused_log_softmax,
+                            rnnt_reduction reduction, float *loss, float *loss_reduced, void *grad, void *workspace,
+                            size_t workspace_bytes, rnnt_stream_t stream) {
     return loss_impl(logits, dtype, N, V, targets, S, logit_lengths, target_lengths, B, blank, clamp,
-                     fused_log_softmax, reduction, loss, loss_reduced, grad, workspace, workspace_bytes,
+                     fastemit_lambda, fused_log_softmax, reduction, loss, loss_reduced, grad, workspace, workspace_bytes,
                      static_cast<hipStream_t>(stream), Padding());
 }
 
@@ -505,14 +509,15 @@ rnnt_status rnnt_loss_padded_workspace_size(int32_t B, int32_t V, int32_t max_T,
 rnnt_status rnnt_loss_padded(const void *logits, rnnt_dtype dtype, int32_t max_T, int32_t max_U1, int32_t V,
                              const int32_t *targets, int32_t S, const int32_t *logit_lengths,
                              const int32_t *target_lengths, int32_t B, int64_t blank, float clamp,
-                             int fused_log_softmax, rnnt_reduction reduction, float *loss, float *loss_reduced,
-                             void *grad, void *workspace, size_t workspace_bytes, rnnt_stream_t stream) {
+                             float fastemit_lambda, int fused_log_softmax, rnnt_reduction reduction, float *loss,
+                             float *loss_reduced, void *grad, void *workspace, size_t workspace_bytes,
+                             rnnt_stream_t stream) {
     if (max_T < 1 || max_U1 < 1) return RNNT_INVALID_VALUE;
     Padding pad;
     pad.max_T = max_T;
     pad.max_U1 = max_U1;
     return loss_impl(logits, dtype, -1, V, targets, S, logit_lengths, target_lengths, B, blank, clamp,
-                     fused_log_softmax, reduction, loss, loss_reduced, grad, workspace, workspace_bytes,
+                     fastemit_lambda, fused_log_softmax, reduction, loss, loss_reduced, grad, workspace, workspace_bytes,
                      static_cast<hipStream_t>(stream), pad);
 }
 

@@ -146,6 +146,7 @@ struct LaunchArgs {
     int blank;           // normalised
     int fused;
     float clamp;         // <= 0: off
+    float fastemit;      // FastEmit weight lambda >= 0 on the label-emission derivatives
     float grad_scale;    // 1 or 1/B
     const int32_t *targets;
     float *loss;

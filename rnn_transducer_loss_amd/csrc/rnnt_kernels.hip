@@ -929,7 +929,10 @@ __global__ __launch_bounds__(64) void k_alpha_beta(const SampleDesc *__restrict_
 // g_k = P(k|t,u) * occ(t,u) - [k = blank] flow_b - [k = y_{u+1}] flow_y, where
 // occ = alpha*beta/P(y|x) and the flows are the posterior probabilities of
 // leaving (t,u) by blank or by the next label.  P * occ is evaluated as
-// exp2(x * log2(e) + shift) with one per-row shift.
+// exp2(x * log2(e) + shift) with one per-row shift.  With a FastEmit weight
+// lambda (the FastEmit paper's rule: the label-emission derivatives times
+// 1 + lambda) the label flow is (1 + lambda) flow_y and, through the
+// log_softmax chain rule, the softmax term carries occ + lambda flow_y.
 struct RowTerms {
     float shift2;  // log2(occ * scale) - den * log2(e), or -inf
     float fb;      // scaled blank flow
@@ -955,7 +958,7 @@ __device__ __forceinline__ RowTerms row_terms(const SampleDesc &d, const SampleT
                                               const float4 *__restrict__ node, const double *__restrict__ alpha,
                                               const double *__restrict__ beta, const int *__restrict__ ealpha,
                                               const int *__restrict__ ebeta, float log2_scale, float scale,
-                                              bool fused) {
+                                              float fastemit, float scale_y, bool fused) {
     const int U1 = d.U + 1;
     const int n = t + u;
     const int64_t s = d.slot_off + (int64_t)n * U1 + u;      // node slot
@@ -974,10 +977,13 @@ __device__ __forceinline__ RowTerms row_terms(const SampleDesc &d, const SampleT
         else if (u == d.U) lb = a2 + (double)l.x * kLog2eD;
         if (u < d.U) ly = a2 + (double)l.y * kLog2eD + node_log2(beta, eb, q + U1p + 1, gnext, st.log_mode);
     }
+    // occ + lambda flow_y = occ (1 + lambda 2^(ly - lo)); flow_y <= occ, so
+    // the exponent is at most about zero.
+    if (fastemit > 0.f && ly != kNegInfD) lo += (double)log2f(1.f + fastemit * exp2_fast((float)(ly - lo)));
     RowTerms r;
     r.shift2 = fused ? (float)(lo - (double)l.z * kLog2eD) + log2_scale : kNegInf;
     r.fb = exp2_fast((float)lb) * scale;
-    r.fy = exp2_fast((float)ly) * scale;
+    r.fy = exp2_fast((float)ly) * scale_y;
     r.y = __float_as_int(l.w);
     return r;
 }
@@ -985,6 +991,7 @@ __device__ __forceinline__ RowTerms row_terms(const SampleDesc &d, const SampleT
 struct GradArgs {
     int V, blank, n_chunks;
     float clamp, scale, log2_scale;
+    float fastemit, scale_y;  // FastEmit weight; scale * (1 + fastemit)
     const SampleDesc *desc;
     const ChunkDesc *chunks;
     const int *mode;
@@ -1000,13 +1007,13 @@ struct GradArgs {
 // parameters, so the compiler knows the gradient stores cannot clobber them
 // and reads their wave-uniform elements through the scalar cache.
 #define RNNT_GRAD_PARAMS                                                                                      \
-    int V, int blank, int n_chunks, float clamp, float scale, float log2_scale,                              \
+    int V, int blank, int n_chunks, float clamp, float scale, float log2_scale, float fastemit, float scale_y, \
         const SampleDesc *__restrict__ desc, const ChunkDesc *__restrict__ chunks, const int *__restrict__ mode, \
         const double *__restrict__ log2z, const float4 *__restrict__ node, const double *__restrict__ alpha,   \
         const double *__restrict__ beta, const int *__restrict__ ealpha, const int *__restrict__ ebeta
 #define RNNT_GRAD_ARGS(g)                                                                                  \
-    g.V, g.blank, g.n_chunks, g.clamp, g.scale, g.log2_scale, g.desc, g.chunks, g.mode, g.log2z, g.node,   \
-        g.alpha, g.beta, g.ealpha, g.ebeta
+    g.V, g.blank, g.n_chunks, g.clamp, g.scale, g.log2_scale, g.fastemit, g.scale_y, g.desc, g.chunks, g.mode, \
+        g.log2z, g.node, g.alpha, g.beta, g.ealpha, g.ebeta
 
 __device__ __forceinline__ float clamp_to(float v, float cl, bool do_clamp) {
     return do_clamp ? fminf(fmaxf(v, -cl), cl) : v;
@@ -1091,7 +1098,8 @@ __global__ __launch_bounds__(64) void k_grad_rows(const T *logits, T *grad, int 
         }
     }
     const SampleTerms st{log2z[d.index], mode[d.index] != 0};
-    const RowTerms rt = row_terms(d, st, t, u, node, alpha, beta, ealpha, ebeta, log2_scale, scale, FUSED);
+    const RowTerms rt =
+        row_terms(d, st, t, u, node, alpha, beta, ealpha, ebeta, log2_scale, scale, fastemit, scale_y, FUSED);
     grad_row<T, NV, FULL, FUSED, CLAMP>(x, grad + row * (int64_t)V, rt, blank, nvec, clamp * scale, i0);
 }
 
@@ -1116,7 +1124,8 @@ __global__ __launch_bounds__(256) void k_grad_narrow(const T *logits, T *grad, R
         const int t = lr / U1;
         const int u = lr - t * U1;
         const int64_t row = row_of(d, t, u);
-        const RowTerms rt = row_terms(d, st, t, u, node, alpha, beta, ealpha, ebeta, log2_scale, scale, FUSED);
+        const RowTerms rt =
+        row_terms(d, st, t, u, node, alpha, beta, ealpha, ebeta, log2_scale, scale, fastemit, scale_y, FUSED);
         const T *src = logits + row * (int64_t)V;
         T *dst = grad + row * (int64_t)V;
         const int vb = blank / VEC, vy = rt.y >= 0 ? rt.y / VEC : -1;
@@ -1358,6 +1367,8 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
     g.clamp = a.clamp;
     g.scale = a.grad_scale;
     g.log2_scale = log2f(a.grad_scale);
+    g.fastemit = a.fastemit;
+    g.scale_y = a.grad_scale * (1.0f + a.fastemit);
     g.desc = WS(const SampleDesc *, desc);
     g.chunks = WS(const ChunkDesc *, chunks);
     g.mode = WS(const int *, mode);
@@ -1378,7 +1389,8 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
             // waves per row: rows of up to 4 KiB (four vectors per lane) take one
             constexpr int S = Tg::n > 4 ? Tg::n / 4 : 1;
             constexpr int NVW = Tg::n / S;
-            void (*kern)(const T *, T *, int, int64_t, int, int, int, float, float, float, const SampleDesc *,
+            void (*kern)(const T *, T *, int, int64_t, int, int, int, float, float, float, float, float,
+                         const SampleDesc *,
                          const ChunkDesc *, const int *, const double *, const float4 *, const double *,
                          const double *, const int *, const int *);
             if (a.fused) {

@@ -58,13 +58,15 @@ def rnnt_loss_fused(logits: torch.Tensor, targets: torch.Tensor, logit_lengths, 
                     clamp: float = -1.0, reduction: str = "mean", fused_log_softmax: bool = True,
                     compute_grad: bool = True, grad: Optional[torch.Tensor] = None, inplace: bool = False,
                     workspace: Optional[torch.Tensor] = None, loss: Optional[torch.Tensor] = None,
-                    loss_reduced: Optional[torch.Tensor] = None):
+                    loss_reduced: Optional[torch.Tensor] = None, fastemit_lambda: float = 0.0):
     """One librnnt call.  Returns ``(loss, loss_reduced, grad, workspace)``.
 
     ``loss`` is the fp32 per-sample loss (B,), ``loss_reduced`` a (1,) fp32
     tensor for mean/sum (None for none).  ``grad`` is d(reduced loss)/d(logits)
     for a unit upstream gradient (clamped per sample, times 1/B for mean), in
     the logits dtype; with ``inplace=True`` it is written over ``logits``.
+    ``fastemit_lambda >= 0`` weights the label-emission derivatives by
+    (1 + lambda) (FastEmit); the loss value does not depend on it.
     Buffers may be passed in to avoid allocation (the bench does).
     """
     tg = _prepare(logits, targets)
@@ -107,10 +109,11 @@ def rnnt_loss_fused(logits: torch.Tensor, targets: torch.Tensor, logit_lengths, 
         if padded:
             _lib.loss_padded(logits.data_ptr(), code, max_T, max_U1, V, tgp, tg.shape[1], T, U, blank, clamp,
                              fused_log_softmax, reduction, loss.data_ptr(), redp, gp, workspace.data_ptr(),
-                             workspace.numel(), stream)
+                             workspace.numel(), stream, fastemit_lambda)
         else:
             _lib.loss_fused(logits.data_ptr(), code, N, V, tgp, tg.shape[1], T, U, blank, clamp, fused_log_softmax,
-                            reduction, loss.data_ptr(), redp, gp, workspace.data_ptr(), workspace.numel(), stream)
+                            reduction, loss.data_ptr(), redp, gp, workspace.data_ptr(), workspace.numel(), stream,
+                            fastemit_lambda)
     return loss, (loss_reduced if reduction != "none" else None), grad, workspace
 
 
@@ -122,11 +125,13 @@ def device_flags(workspace: torch.Tensor) -> int:
 
 class _RNNTLossFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, logits, targets, logit_lengths, target_lengths, blank, clamp, reduction, fused_log_softmax):
+    def forward(ctx, logits, targets, logit_lengths, target_lengths, blank, clamp, reduction, fused_log_softmax,
+                fastemit_lambda):
         T = _lib.host_i32(logit_lengths)
         U = _lib.host_i32(target_lengths)
         loss, loss_red, grad, ws = rnnt_loss_fused(logits, targets, T, U, blank, clamp, reduction, fused_log_softmax,
-                                                   compute_grad=logits.requires_grad)
+                                                   compute_grad=logits.requires_grad,
+                                                   fastemit_lambda=fastemit_lambda)
         ctx.meta = (T, U, reduction, logits.shape, logits.dtype)
         ctx.used = False
         if grad is not None:
@@ -137,7 +142,7 @@ class _RNNTLossFunction(torch.autograd.Function):
     def backward(ctx, grad_out):
         T, U, reduction, shape, dtype = ctx.meta
         if not ctx.saved_tensors:
-            return (None,) * 8
+            return (None,) * 9
         if ctx.used:
             raise RuntimeError("rnnt_loss backward was already run for this forward call")
         ctx.used = True
@@ -151,32 +156,37 @@ class _RNNTLossFunction(torch.autograd.Function):
             else:
                 _lib.grad_scale(grad.data_ptr(), _dtype_code(dtype), shape[0], shape[1], T, U, scale.data_ptr(),
                                 reduction == "none", ws.data_ptr(), ws.numel(), stream)
-        return grad, None, None, None, None, None, None, None
+        return grad, None, None, None, None, None, None, None, None
 
 
 def rnnt_loss(logits: torch.Tensor, targets: torch.Tensor, logit_lengths, target_lengths, blank: int = -1,
-              clamp: float = -1.0, reduction: str = "mean", fused_log_softmax: bool = True) -> torch.Tensor:
+              clamp: float = -1.0, reduction: str = "mean", fused_log_softmax: bool = True,
+              fastemit_lambda: float = 0.0) -> torch.Tensor:
     """RNN-T loss over packed (or padded 4-D) logits; differentiable with respect to ``logits``.
 
     ``blank`` in [-V, V-1] (negative counts from the end), ``clamp > 0`` clips
     each gradient element to [-clamp, clamp], ``reduction`` is none (per
     sample, fp32 (B,)), mean (over the batch) or sum.  With
     ``fused_log_softmax=False`` the inputs are taken as log-probabilities.
+    ``fastemit_lambda >= 0`` is the FastEmit regularisation weight: the
+    backward pass weights every label emission's derivative by
+    (1 + fastemit_lambda); the returned loss is the plain one.
     """
     if reduction not in ("none", "mean", "sum"):
         raise ValueError(f"reduction must be none, mean or sum, got {reduction!r}")
     return _RNNTLossFunction.apply(logits, targets, logit_lengths, target_lengths, int(blank), float(clamp),
-                                   reduction, bool(fused_log_softmax))
+                                   reduction, bool(fused_log_softmax), float(fastemit_lambda))
 
 
 class RNNTLoss(torch.nn.Module):
     """Module form of :func:`rnnt_loss` with the attributes fixed at construction."""
 
     def __init__(self, blank: int = -1, clamp: float = -1.0, reduction: str = "mean",
-                 fused_log_softmax: bool = True):
+                 fused_log_softmax: bool = True, fastemit_lambda: float = 0.0):
         super().__init__()
         self.blank, self.clamp, self.reduction, self.fused_log_softmax = blank, clamp, reduction, fused_log_softmax
+        self.fastemit_lambda = fastemit_lambda
 
     def forward(self, logits, targets, logit_lengths, target_lengths):
         return rnnt_loss(logits, targets, logit_lengths, target_lengths, self.blank, self.clamp, self.reduction,
-                         self.fused_log_softmax)
+                         self.fused_log_softmax, self.fastemit_lambda)

@@ -98,6 +98,7 @@ def _call_fused(**over):
     dict(ws_ptr=0x600010),                       # workspace not 256-byte aligned
     dict(logit_lengths=np.array([4, 0], np.int32)),
     dict(target_lengths=np.array([2, -1], np.int32)),
+    dict(fastemit_lambda=-0.5), dict(fastemit_lambda=float("inf")), dict(fastemit_lambda=float("nan")),
 ])
 def test_fused_call_rejects_invalid_arguments_before_any_launch(over):
     with pytest.raises(ValueError):

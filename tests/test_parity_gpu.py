@@ -58,20 +58,21 @@ def _np_rows(t: torch.Tensor) -> np.ndarray:
     return a.numpy()
 
 
-def run(rl, w, reduction=None, inplace=False, compute_grad=True, clamp=None):
+def run(rl, w, reduction=None, inplace=False, compute_grad=True, clamp=None, fastemit=0.0):
     reduction = w.reduction if reduction is None else reduction
     clamp = w.clamp if clamp is None else clamp
     logits = w.logits.clone() if inplace else w.logits
     tg = torch.from_numpy(w.targets).to("cuda")
     loss, red, grad, ws = rl.rnnt_loss_fused(logits, tg, w.logit_lengths, w.target_lengths, blank=w.blank,
                                              clamp=clamp, reduction=reduction, fused_log_softmax=w.fused,
-                                             compute_grad=compute_grad, inplace=inplace)
+                                             compute_grad=compute_grad, inplace=inplace, fastemit_lambda=fastemit)
     flags = rl.device_flags(ws)
     torch.cuda.synchronize()
     return loss, red, grad, flags
 
 
-def check_against_oracle(w, loss, grad, reduction, clamp=None, grad_rows="all", samples=None, seed=0):
+def check_against_oracle(w, loss, grad, reduction, clamp=None, grad_rows="all", samples=None, seed=0,
+                         fastemit=0.0):
     """Compare per-sample loss (all samples) and gradients of selected rows with the oracle."""
     clamp = w.clamp if clamp is None else clamp
     ltol, gtol = TOL[w.dtype]
@@ -93,7 +94,8 @@ def check_against_oracle(w, loss, grad, reduction, clamp=None, grad_rows="all", 
             pick = set([0, 1, U, n - 1, n - 2, max(0, n - U - 1)])
             pick |= set(rng.integers(0, n, size=min(n, grad_rows)).tolist())
             rows = np.array(sorted(r for r in pick if 0 <= r < n), np.int64)
-        r = oracle.sample(x, T, U, w.targets[i], b, w.fused, clamp, want_grad=(i in want_grad), rows=rows)
+        r = oracle.sample(x, T, U, w.targets[i], b, w.fused, clamp, want_grad=(i in want_grad), rows=rows,
+                          fastemit_lambda=fastemit)
         return i, r, rows
 
     errs_loss, errs_grad = [], []
@@ -473,3 +475,71 @@ def test_mixed_domains_in_one_batch(rl):
     w.logits = torch.tensor(x, dtype=torch.float32, device="cuda")
     loss, red, grad, flags = run(rl, w)
     check_against_oracle(w, loss, grad, "none")
+
+
+# ------------------------------------------------------------------- FastEmit
+@pytest.mark.parametrize("V,dtype,fused,lam,clamp", [
+    (29, torch.float32, True, 0.01, -1.0),       # narrow rows (several rows per wave)
+    (1024, torch.float32, True, 0.5, -1.0),      # one 4 KiB row per wave
+    (1000, torch.float32, True, 2.0, 0.1),       # unaligned row length (scalar tail), clamp
+    (4096, torch.float16, True, 0.5, -1.0),      # half rows of 8 KiB
+    (8192, torch.float32, True, 0.3, 0.05),      # rows split over several waves, clamp
+    (2048, torch.float16, False, 0.3, -1.0),     # log-prob inputs: flows only
+    (50, torch.float32, False, 1.0, 0.2),
+])
+def test_fastemit_gradient(rl, V, dtype, fused, lam, clamp):
+    w = _custom([31, 12, 1, 20], [7, 4, 5, 0], V, dtype=dtype, std=2.0, blank=-1, fused=fused,
+                prenormalise=not fused, clamp=clamp, reduction="mean", seed=V + 3)
+    loss, red, grad, flags = run(rl, w, fastemit=lam)
+    assert flags == 0
+    check_against_oracle(w, loss, grad, "mean", fastemit=lam)
+    plain, _, _, _ = run(rl, w)
+    assert torch.equal(loss, plain)   # the loss value does not depend on the FastEmit weight
+
+
+def test_fastemit_log_domain(rl):
+    """Extreme log-prob inputs (the log-domain sweep) with a FastEmit weight."""
+    rng = np.random.default_rng(44)
+    w = _custom([18, 7], [5, 3], 20, std=1.0, blank=0, fused=False, reduction="sum", seed=44)
+    x = np.round(rng.uniform(-250.0, -0.25, size=(w.N, w.V)) * 4) / 4
+    x[::6, 0] = -0.5
+    w.logits = torch.tensor(x, dtype=torch.float32, device="cuda")
+    loss, red, grad, flags = run(rl, w, fastemit=0.7)
+    assert flags == 0
+    check_against_oracle(w, loss, grad, "sum", fastemit=0.7)
+
+
+def test_fastemit_bpe_full_size(rl):
+    """The full bpe batch with lambda = 0.01: every loss, every row of the smallest and largest samples, and
+    rows of a middle one; each fused gradient row still sums to zero."""
+    w = workloads.make("bpe", device="cuda")
+    loss, red, grad, flags = run(rl, w, fastemit=0.01)
+    assert flags == 0
+    order = np.argsort(w.logit_lengths.astype(np.int64) * (w.target_lengths + 1))
+    check_against_oracle(w, loss, grad, w.reduction, grad_rows="all", samples=[int(order[0]), int(order[-1])],
+                         fastemit=0.01)
+    assert grad.double().sum(dim=1).abs().max().item() < 1e-6
+
+
+def test_fastemit_padded_and_autograd(rl):
+    Ts, Us = [26, 9, 14], [6, 2, 11]
+    w = workloads.make_custom(Ts, Us, 96, std=2.0, reduction="none", seed=45, device="cuda")
+    lam = 0.25
+    tg = torch.from_numpy(w.targets).to("cuda")
+    ref_loss, _, ref_grad, _ = run(rl, w, fastemit=lam)
+    check_against_oracle(w, ref_loss, ref_grad, "none", fastemit=lam)
+    max_T, max_U1 = 28, 13
+    xp = _to_padded(w, max_T, max_U1)
+    loss_p, _, grad_p, _ = rl.rnnt_loss_fused(xp, tg, w.logit_lengths, w.target_lengths, blank=w.blank,
+                                              reduction="none", fastemit_lambda=lam)
+    torch.cuda.synchronize()
+    rows, pad = _padded_rows(w, grad_p, max_T, max_U1)
+    assert torch.equal(loss_p, ref_loss) and torch.equal(rows, ref_grad) and bool((pad == 0).all())
+    x = w.logits.clone().requires_grad_(True)
+    out = rl.rnnt_loss(x, tg, w.logit_lengths, w.target_lengths, blank=w.blank, reduction="none",
+                       fastemit_lambda=lam)
+    up = torch.tensor([1.5, -0.5, 2.0], device="cuda")
+    out.backward(up)
+    torch.cuda.synchronize()
+    fac = torch.cat([torch.full((w.rows(i).stop - w.rows(i).start, 1), float(up[i])) for i in range(3)]).cuda()
+    assert torch.allclose(x.grad, ref_grad * fac, rtol=1e-6, atol=0)
