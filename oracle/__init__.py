@@ -63,6 +63,11 @@ def _load():
                 ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double,
                 ctypes.POINTER(ctypes.c_int64), ctypes.c_long, dp, dp, dp, dp, dp]
             lib.rnnt_oracle_sample_ex.restype = ctypes.c_int
+            ip = ctypes.POINTER(ctypes.c_int)
+            lib.rnnt_oracle_multiblank_sample.argtypes = [
+                ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ip, ctypes.c_int,
+                ctypes.c_int, ip, ip, ctypes.c_double, ctypes.c_int, ctypes.c_double, ctypes.c_double, dp, dp, dp]
+            lib.rnnt_oracle_multiblank_sample.restype = ctypes.c_int
             lib.rnnt_oracle_half_to_double.argtypes = [ctypes.c_uint16]
             lib.rnnt_oracle_half_to_double.restype = ctypes.c_double
             _lib = lib
@@ -185,3 +190,79 @@ def batch(logits, targets, logit_lengths, target_lengths, blank: int = -1, clamp
         reduced, scale = losses.sum() / B, 1.0 / B
     grad_reduced = grad * scale if want_grad else None
     return losses, reduced, grad, grad_reduced
+
+
+def multiblank_sample(x, T: int, U: int, y, blank: int, big_blank_ids, big_blank_durations, sigma: float = 0.0,
+                      fused: bool = True, clamp: float = -1.0, fastemit_lambda: float = 0.0,
+                      want_grad: bool = True) -> SampleResult:
+    """Multi-blank transducer loss (and gradient of every row) of one sample.
+
+    Big blank i is class ``big_blank_ids[i]`` and moves t forward by
+    ``big_blank_durations[i]``; every emission's log-probability is lowered
+    by ``sigma`` (logit under-normalisation).  These follow the
+    compute_multiblank_grad_kernel page's parameters; see rnnt_oracle.c for
+    the reading of the alignment rules.  ``loss_alpha`` is the forward
+    recursion's value, ``loss`` the backward one's.
+    """
+    lib = _load()
+    x = np.asarray(x)
+    if x.dtype not in _DT:
+        x = x.astype(np.float64)
+    x = np.ascontiguousarray(x)
+    V = x.shape[1]
+    if x.shape[0] != T * (U + 1):
+        raise ValueError("row count does not match T*(U+1)")
+    ids = np.ascontiguousarray(np.asarray(big_blank_ids, dtype=np.int32).reshape(-1))
+    dur = np.ascontiguousarray(np.asarray(big_blank_durations, dtype=np.int32).reshape(-1))
+    if ids.shape != dur.shape:
+        raise ValueError("big_blank_ids and big_blank_durations must have the same length")
+    nb = len(ids)
+    yy = np.ascontiguousarray(np.asarray(y[:U], dtype=np.int32)) if U > 0 else np.zeros(1, np.int32)
+    ip = ctypes.POINTER(ctypes.c_int)
+    grad = np.empty((T * (U + 1), V), np.float64) if want_grad else None
+    la = ctypes.c_double()
+    lb = ctypes.c_double()
+    rc = lib.rnnt_oracle_multiblank_sample(
+        x.ctypes.data_as(ctypes.c_void_p), _DT[x.dtype], T, U, V, yy.ctypes.data_as(ip), int(blank), nb,
+        (ids if nb else np.zeros(1, np.int32)).ctypes.data_as(ip),
+        (dur if nb else np.zeros(1, np.int32)).ctypes.data_as(ip), float(sigma), int(bool(fused)), float(clamp),
+        float(fastemit_lambda), _ptr(grad), ctypes.byref(la), ctypes.byref(lb))
+    if rc == ORACLE_BAD_TARGET:
+        raise ValueError("target label equal to a blank or outside [0, V)")
+    if rc != ORACLE_OK:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return SampleResult(lb.value, la.value, grad, None, None)
+
+
+def multiblank_batch(logits, targets, logit_lengths, target_lengths, big_blank_ids, big_blank_durations,
+                     blank: int = -1, sigma: float = 0.0, clamp: float = -1.0, reduction: str = "mean",
+                     fused: bool = True, fastemit_lambda: float = 0.0, want_grad: bool = True):
+    """Whole-batch multi-blank oracle over the packed layout; returns as :func:`batch`."""
+    logits = np.asarray(logits)
+    N, V = logits.shape
+    B = len(logit_lengths)
+    b = normalize_blank(int(blank), V)
+    Ts = [int(v) for v in logit_lengths]
+    Us = [int(v) for v in target_lengths]
+    rows = [Ts[i] * (Us[i] + 1) for i in range(B)]
+    if sum(rows) != N:
+        raise ValueError("sum of T_i*(U_i+1) does not equal logits.shape[0]")
+    if reduction not in ("none", "mean", "sum"):
+        raise ValueError(f"unknown reduction {reduction!r}")
+    losses = np.empty(B, np.float64)
+    grad = np.empty((N, V), np.float64) if want_grad else None
+    off = 0
+    for i in range(B):
+        res = multiblank_sample(logits[off:off + rows[i]], Ts[i], Us[i], np.asarray(targets[i]), b, big_blank_ids,
+                                big_blank_durations, sigma, fused, clamp, fastemit_lambda, want_grad)
+        losses[i] = res.loss
+        if want_grad:
+            grad[off:off + rows[i]] = res.grad
+        off += rows[i]
+    if reduction == "none":
+        reduced, scale = losses.copy(), 1.0
+    elif reduction == "sum":
+        reduced, scale = losses.sum(), 1.0
+    else:
+        reduced, scale = losses.sum() / B, 1.0 / B
+    return losses, reduced, grad, (grad * scale if want_grad else None)

@@ -93,3 +93,74 @@ def sample(x, T: int, U: int, y, blank: int, fused: bool = True, fastemit_lambda
 
 def count_paths(T: int, U: int) -> int:
     return math.comb(T - 1 + U, U)
+
+
+def _mb_paths(T: int, U: int, durations):
+    """Yield each multi-blank alignment as (t, u, kind) steps; kind is "blank", "label" or a big-blank index.
+
+    From a node (t, u) with t < T: the standard blank moves to t+1, big blank i to t+durations[i], the next label
+    (u < U) to u+1.  An alignment is complete at exactly (T, U); moves past T or reaching T with u < U are
+    dropped.
+    """
+    def walk(t, u, steps):
+        if t == T:
+            if u == U:
+                yield list(steps)
+            return
+        moves = [("blank", 1)] + [(i, d) for i, d in enumerate(durations)]
+        for kind, d in moves:
+            nt = t + d
+            if nt < T or (nt == T and u == U):
+                steps.append((t, u, kind))
+                yield from walk(nt, u, steps)
+                steps.pop()
+        if u < U:
+            steps.append((t, u, "label"))
+            yield from walk(t, u + 1, steps)
+            steps.pop()
+
+    yield from walk(0, 0, [])
+
+
+def multiblank_sample(x, T: int, U: int, y, blank: int, big_blank_ids, big_blank_durations, sigma: float = 0.0,
+                      fused: bool = True, fastemit_lambda: float = 0.0):
+    """(loss, grad) of the multi-blank transducer by enumerating every alignment (tiny lattices only).
+
+    Each emission's log-probability is lowered by sigma; a label edge's expected uses weigh (1 + lambda).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    V = x.shape[1]
+    U1 = U + 1
+    lp = _log_probs(x, fused) - sigma
+
+    def cls(kind, u):
+        if kind == "blank":
+            return blank
+        if kind == "label":
+            return int(y[u])
+        return int(big_blank_ids[kind])
+
+    path_logp, path_steps = [], []
+    for steps in _mb_paths(T, U, list(big_blank_durations)):
+        path_logp.append(sum(lp[t * U1 + u, cls(k, u)] for (t, u, k) in steps))
+        path_steps.append(steps)
+    m = max(path_logp)
+    Z = sum(math.exp(p - m) for p in path_logp)
+    loss = -(m + math.log(Z))
+    d_lp = np.zeros_like(lp)
+    for p, steps in zip(path_logp, path_steps):
+        w = math.exp(p - m) / Z
+        for (t, u, k) in steps:
+            d_lp[t * U1 + u, cls(k, u)] -= w * (1.0 + fastemit_lambda) if k == "label" else w
+    if not fused:
+        return loss, d_lp
+    grad = np.zeros_like(lp)
+    for r in range(lp.shape[0]):
+        p = np.exp(lp[r] + sigma)
+        J = np.eye(V) - np.outer(np.ones(V), p)
+        grad[r] = d_lp[r] @ J
+    return loss, grad
+
+
+def count_multiblank_paths(T: int, U: int, durations) -> int:
+    return sum(1 for _ in _mb_paths(T, U, list(durations)))

@@ -248,3 +248,154 @@ int rnnt_oracle_sample(const double *x, int T, int U, int V, const int *y, int b
     return rnnt_oracle_sample_ex(x, ORACLE_F64, T, U, V, y, blank, fused, clamp, 0.0, NULL, -1, grad, alpha_out,
                                  beta_out, loss_alpha, loss_beta);
 }
+
+/*
+ * Multi-blank transducer (the ESPnet compute_multiblank_grad_kernel page:
+ * activations over V + 1 + num_big_blanks classes, a list of big-blank
+ * durations, and sigma, the hyper-parameter of logit under-normalisation;
+ * the page defers the mathematics to the multi-blank transducer paper).
+ * Reading taken:
+ *   - besides the standard blank (t,u) -> (t+1,u) and the next label
+ *     (t,u) -> (t,u+1), big blank i, class bb_id[i], moves (t,u) -> (t+d_i,u)
+ *     with d_i = bb_dur[i] >= 1;
+ *   - every emission's log-probability is lowered by sigma:
+ *     lp(t,u,k) = x_k - logsumexp(x) - sigma (fused) or x_k - sigma;
+ *   - an alignment ends when a blank of any kind moves it from (t,U) to
+ *     exactly t = T; blanks that would pass T, or reach T with u < U, are not
+ *     part of any alignment;
+ *   - loss = -log of the summed alignment probability; the gradient is its
+ *     derivative (with the FastEmit weight on the label edges, as above).
+ * nb = 0 and sigma = 0 is the plain transducer loss.
+ */
+int rnnt_oracle_multiblank_sample(const void *x, int dtype, int T, int U, int V, const int *y, int blank, int nb,
+                                  const int *bb_id, const int *bb_dur, double sigma, int fused, double clamp,
+                                  double fastemit_lambda, double *grad, double *loss_alpha, double *loss_beta)
+{
+    if (T < 1 || U < 0 || V < 1 || blank < 0 || blank >= V || nb < 0) return ORACLE_BAD_ARGS;
+    if (dtype != ORACLE_F64 && dtype != ORACLE_F32 && dtype != ORACLE_F16) return ORACLE_BAD_ARGS;
+    if (!(fastemit_lambda >= 0.0) || isinf(fastemit_lambda) || !isfinite(sigma)) return ORACLE_BAD_ARGS;
+    for (int i = 0; i < nb; ++i) {
+        if (bb_id[i] < 0 || bb_id[i] >= V || bb_id[i] == blank || bb_dur[i] < 1) return ORACLE_BAD_ARGS;
+        for (int j = 0; j < i; ++j)
+            if (bb_id[j] == bb_id[i]) return ORACLE_BAD_ARGS;
+    }
+    for (int u = 0; u < U; ++u) {
+        if (y[u] < 0 || y[u] >= V || y[u] == blank) return ORACLE_BAD_TARGET;
+        for (int i = 0; i < nb; ++i)
+            if (y[u] == bb_id[i]) return ORACLE_BAD_TARGET;
+    }
+
+    const int U1 = U + 1;
+    const long cells = (long)T * U1;
+    const int nbb = nb > 0 ? nb : 1;
+    double *lse = malloc(sizeof(double) * cells);
+    double *lpb = malloc(sizeof(double) * cells);
+    double *lpy = malloc(sizeof(double) * cells);
+    double *lpg = malloc(sizeof(double) * cells * nbb);   /* big blanks: lpg[c * nb + i] */
+    double *al = malloc(sizeof(double) * cells);
+    double *be = malloc(sizeof(double) * cells);
+    if (!lse || !lpb || !lpy || !lpg || !al || !be) {
+        free(lse); free(lpb); free(lpy); free(lpg); free(al); free(be);
+        return ORACLE_NO_MEMORY;
+    }
+
+    /* Per-node log-probabilities of the edges the lattice uses. */
+    for (long c = 0; c < cells; ++c) {
+        const int u = (int)(c % U1);
+        lse[c] = fused ? row_logsumexp(x, dtype, c, V) : 0.0;
+        lpb[c] = elem(x, dtype, c, V, blank) - lse[c] - sigma;
+        lpy[c] = (u < U) ? elem(x, dtype, c, V, y[u]) - lse[c] - sigma : -INFINITY;
+        for (int i = 0; i < nb; ++i) lpg[c * nb + i] = elem(x, dtype, c, V, bb_id[i]) - lse[c] - sigma;
+    }
+
+    /* Forward: alpha(t,u) sums the partial alignments that arrive at (t,u). */
+    for (int t = 0; t < T; ++t) {
+        for (int u = 0; u <= U; ++u) {
+            const long c = (long)t * U1 + u;
+            if (t == 0 && u == 0) { al[c] = 0.0; continue; }
+            double a = -INFINITY;
+            if (t > 0) a = log_add(a, al[c - U1] + lpb[c - U1]);
+            if (u > 0) a = log_add(a, al[c - 1] + lpy[c - 1]);
+            for (int i = 0; i < nb; ++i) {
+                const int d = bb_dur[i];
+                if (t >= d) a = log_add(a, al[c - (long)d * U1] + lpg[(c - (long)d * U1) * nb + i]);
+            }
+            al[c] = a;
+        }
+    }
+    double logz_alpha = al[(long)(T - 1) * U1 + U] + lpb[(long)(T - 1) * U1 + U];
+    for (int i = 0; i < nb; ++i) {
+        const int d = bb_dur[i];
+        if (T - d >= 0) {
+            const long c = (long)(T - d) * U1 + U;
+            logz_alpha = log_add(logz_alpha, al[c] + lpg[c * nb + i]);
+        }
+    }
+
+    /* Backward: beta(t,u) sums the alignment suffixes from (t,u), the final
+     * blank included; a blank reaching t = T counts only from u = U. */
+    for (int t = T - 1; t >= 0; --t) {
+        for (int u = U; u >= 0; --u) {
+            const long c = (long)t * U1 + u;
+            double b = -INFINITY;
+            if (t + 1 < T) b = log_add(b, be[c + U1] + lpb[c]);
+            else if (u == U) b = log_add(b, lpb[c]);
+            if (u < U) b = log_add(b, be[c + 1] + lpy[c]);
+            for (int i = 0; i < nb; ++i) {
+                const int d = bb_dur[i];
+                if (t + d < T) b = log_add(b, be[c + (long)d * U1] + lpg[c * nb + i]);
+                else if (t + d == T && u == U) b = log_add(b, lpg[c * nb + i]);
+            }
+            be[c] = b;
+        }
+    }
+    const double logz = be[0];
+    if (loss_alpha) *loss_alpha = -logz_alpha;
+    if (loss_beta) *loss_beta = -logz;
+
+    if (grad) {
+        for (long c = 0; c < cells; ++c) {
+            const int t = (int)(c / U1), u = (int)(c % U1);
+            double *g = grad + c * V;
+            for (int k = 0; k < V; ++k) g[k] = 0.0;
+            double sum_d = 0.0;
+            if (logz != -INFINITY) {
+                /* d loss / d lp of each edge leaving (t,u): minus its posterior. */
+                double nb_blank = -INFINITY;            /* log beta after the standard blank */
+                if (t + 1 < T) nb_blank = be[c + U1];
+                else if (u == U) nb_blank = 0.0;
+                const double d_blank = -exp(al[c] + lpb[c] + nb_blank - logz);
+                g[blank] += d_blank;
+                sum_d += d_blank;
+                if (u < U) {
+                    const double d_label = -(1.0 + fastemit_lambda) * exp(al[c] + lpy[c] + be[c + 1] - logz);
+                    g[y[u]] += d_label;
+                    sum_d += d_label;
+                }
+                for (int i = 0; i < nb; ++i) {
+                    const int d = bb_dur[i];
+                    double nxt = -INFINITY;
+                    if (t + d < T) nxt = be[c + (long)d * U1];
+                    else if (t + d == T && u == U) nxt = 0.0;
+                    const double d_big = -exp(al[c] + lpg[c * nb + i] + nxt - logz);
+                    g[bb_id[i]] += d_big;
+                    sum_d += d_big;
+                }
+            }
+            if (fused) {
+                for (int k = 0; k < V; ++k) {
+                    const double p = (lse[c] == -INFINITY) ? 0.0 : exp(elem(x, dtype, c, V, k) - lse[c]);
+                    g[k] -= p * sum_d;
+                }
+            }
+            if (clamp > 0.0) {
+                for (int k = 0; k < V; ++k) {
+                    if (g[k] > clamp) g[k] = clamp;
+                    if (g[k] < -clamp) g[k] = -clamp;
+                }
+            }
+        }
+    }
+    free(lse); free(lpb); free(lpy); free(lpg); free(al); free(be);
+    return ORACLE_OK;
+}

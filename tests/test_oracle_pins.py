@@ -417,3 +417,94 @@ def test_fastemit_finite_differences():
         fd_full = (loss_full(xp) - loss_full(xm)) / (2 * eps)
         fd_label = (loss_label_only(xp, r) - loss_label_only(xm, r)) / (2 * eps)
         assert abs(fd_full + lam * fd_label - g[r, k]) < 1e-8, (r, k)
+
+
+# Multi-blank transducer (the compute_multiblank_grad_kernel page: big blanks with durations and sigma, the
+# logit under-normalisation).  Reading: big blank i moves (t,u) -> (t+d_i,u); every emission's log-probability is
+# lowered by sigma; an alignment ends when a blank of any kind lands exactly on t = T at u = U.
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("T,U,ids,durs,sigma,lam", [
+    (1, 2, [3], [2], 0.0, 0.0), (2, 1, [3], [2], 0.1, 0.0), (4, 2, [5, 4], [2, 3], 0.3, 0.0),
+    (6, 1, [5, 4, 3], [2, 4, 6], 0.05, 0.2), (5, 3, [1], [1], 0.0, 0.0), (7, 2, [0, 2], [3, 8], -0.2, 0.5)])
+def test_multiblank_bruteforce(T, U, ids, durs, sigma, lam, fused):
+    rng = np.random.default_rng(T * 100 + U * 10 + len(ids) + int(fused))
+    V, blank = 7, 6
+    x = rng.normal(0.0, 1.5, size=(T * (U + 1), V))
+    labels = [k for k in range(V) if k != blank and k not in ids]
+    y = rng.choice(labels, size=U)
+    if not fused:
+        x = sp_log_softmax(x, axis=1) + rng.normal(0, 0.1, size=x.shape)
+    bl, bg = bruteforce.multiblank_sample(x, T, U, y, blank, ids, durs, sigma, fused, lam)
+    r = oracle.multiblank_sample(x, T, U, y, blank, ids, durs, sigma, fused, fastemit_lambda=lam)
+    assert abs(r.loss - bl) <= 1e-12 * max(1.0, abs(bl))
+    assert abs(r.loss_alpha - bl) <= 1e-12 * max(1.0, abs(bl))
+    np.testing.assert_allclose(r.grad, bg, atol=1e-12, rtol=0)
+
+
+def test_multiblank_path_counts():
+    # no big blank: C(T-1+U, U) alignments; durations {2}: compositions of T into parts 1 and 2 (Fibonacci F(T+1))
+    # interleaved with the U labels, which may only come before the last blank
+    assert bruteforce.count_multiblank_paths(6, 0, []) == 1
+    assert bruteforce.count_multiblank_paths(6, 0, [2]) == 13           # F(7)
+    assert bruteforce.count_multiblank_paths(5, 2, []) == math.comb(6, 2)
+
+
+def test_multiblank_reduces_to_the_plain_loss():
+    rng = np.random.default_rng(31)
+    T, U, V, blank = 23, 6, 11, 10
+    x, y = _rand_case(rng, T, U, V, blank, std=2.0)
+    p = oracle.sample(x, T, U, y, blank, True)
+    m = oracle.multiblank_sample(x, T, U, y, blank, [], [], 0.0, True)
+    assert abs(m.loss - p.loss) <= 1e-13 * abs(p.loss)
+    np.testing.assert_allclose(m.grad, p.grad, atol=1e-15, rtol=0)
+    # sigma alone: every alignment makes T + U emissions, so the loss moves by sigma (T + U), the gradient not at all
+    s = oracle.multiblank_sample(x, T, U, y, blank, [], [], 0.37, True)
+    assert abs(s.loss - (p.loss + 0.37 * (T + U))) <= 1e-12 * abs(p.loss)
+    np.testing.assert_allclose(s.grad, p.grad, atol=1e-13, rtol=0)
+    # a big blank longer than T can never be taken: the plain loss and gradient
+    ids = [k for k in range(V) if k != blank and k not in y][:1]
+    z = oracle.multiblank_sample(x, T, U, y, blank, ids, [T + 1], 0.0, True)
+    assert abs(z.loss - p.loss) <= 1e-13 * abs(p.loss)
+    np.testing.assert_allclose(z.grad, p.grad, atol=1e-15, rtol=0)
+
+
+def test_multiblank_invariants():
+    """Fused rows sum to zero; non-fused flows: the blanks of all kinds advance t by exactly T in total, the
+    labels are emitted U times; alpha and beta agree."""
+    rng = np.random.default_rng(32)
+    T, U, V, blank = 40, 9, 13, 0
+    ids, durs = [12, 11], [2, 4]
+    labels = [k for k in range(V) if k not in (blank, 12, 11)]
+    x = rng.normal(0.0, 2.0, size=(T * (U + 1), V))
+    y = rng.choice(labels, size=U)
+    f = oracle.multiblank_sample(x, T, U, y, blank, ids, durs, 0.25, True)
+    assert abs(f.loss - f.loss_alpha) <= 1e-12 * abs(f.loss)
+    assert np.abs(f.grad.sum(axis=1)).max() < 1e-13
+    lp = sp_log_softmax(x, axis=1)
+    n = oracle.multiblank_sample(lp, T, U, y, blank, ids, durs, 0.25, False)
+    advance = -(n.grad[:, blank].sum() + 2 * n.grad[:, 12].sum() + 4 * n.grad[:, 11].sum())
+    assert abs(advance - T) < 1e-10
+    assert abs(-n.grad[:, labels].sum() - U) < 1e-10
+    with pytest.raises(ValueError):
+        oracle.multiblank_sample(x, T, U, y, blank, [blank], [2], 0.0, True)       # big blank equal to blank
+    with pytest.raises(ValueError):
+        oracle.multiblank_sample(x, T, U, [12] * U, blank, ids, durs, 0.0, True)  # label equal to a big blank
+
+
+def test_multiblank_finite_differences():
+    rng = np.random.default_rng(33)
+    T, U, V, blank = 9, 3, 8, 7
+    ids, durs = [6, 5], [2, 3]
+    x = rng.normal(0.0, 1.0, size=(T * (U + 1), V))
+    y = rng.choice([0, 1, 2, 3, 4], size=U)
+    g = oracle.multiblank_sample(x, T, U, y, blank, ids, durs, 0.2, True).grad
+    eps = 1e-6
+    for _ in range(40):
+        r = int(rng.integers(0, x.shape[0]))
+        k = int(rng.integers(0, V))
+        xp = x.copy(); xp[r, k] += eps
+        xm = x.copy(); xm[r, k] -= eps
+        fd = (oracle.multiblank_sample(xp, T, U, y, blank, ids, durs, 0.2, True, want_grad=False).loss
+              - oracle.multiblank_sample(xm, T, U, y, blank, ids, durs, 0.2, True, want_grad=False).loss) / (2 * eps)
+        assert abs(fd - g[r, k]) < 1e-8, (r, k)
