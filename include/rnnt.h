@@ -202,6 +202,59 @@ rnnt_status rnnt_grad_scale_padded(void *grad, rnnt_dtype dtype, int32_t max_T, 
                                    size_t workspace_bytes, rnnt_stream_t stream);
 
 /*
+ * Multi-blank transducer loss and gradient (the ESPnet
+ * compute_multiblank_grad_kernel page: activations over the labels, the
+ * standard blank and num_big_blanks big blanks; each big blank has a
+ * duration; sigma is the logit under-normalisation hyper-parameter; the page
+ * defers the mathematics to the multi-blank transducer paper).  Reading
+ * taken: from node (t,u) the standard blank moves to (t+1,u), big blank i to
+ * (t + big_blank_durations[i], u) and the next label to (t,u+1); every
+ * emission's log-probability is lowered by sigma; an alignment ends when a
+ * blank of any kind reaches t = T exactly at u = U.  The loss is -log of the
+ * summed alignment probability, the gradient its derivative (with the
+ * FastEmit weight on the label emissions).  With no big blank and sigma = 0
+ * this is rnnt_loss_fused's loss.
+ *
+ *   Packed layout only; logits, targets, S, lengths, blank, clamp,
+ *   fastemit_lambda, fused_log_softmax, reduction, loss, loss_reduced, grad
+ *   (NULL: loss only) and stream as for rnnt_loss_fused.
+ *   num_big_blanks    0..4.
+ *   big_blank_ids     host int32[num_big_blanks]: the class of each big blank,
+ *                     in [0, V), distinct, none equal to the standard blank.
+ *   big_blank_durations  host int32[num_big_blanks], each in [1, 16].
+ *   sigma             finite; subtracted from every emission's log-probability.
+ *   workspace         device, >= rnnt_multiblank_workspace_size bytes, 256-byte
+ *                     aligned.
+ * Returns RNNT_INVALID_VALUE for the conditions of rnnt_loss_fused, a bad big
+ * blank list, a non-finite sigma, or a batch whose widest lattice and longest
+ * duration need more than 64 KiB of ring per sweep, i.e.
+ * (longest duration + 1) * (U1p * 8 + 4) bytes > 64 KiB, U1p = the widest
+ * U_i + 1 rounded up to 64 times a power of two (at U1p = 1024 the longest
+ * duration is 6).  A label equal to blank or to a big
+ * blank sets RNNT_DEV_BAD_TARGET (read with rnnt_loss_fused_check).
+ */
+rnnt_status rnnt_multiblank_workspace_size(int32_t B, int32_t V, int64_t N, rnnt_dtype dtype,
+                                           const int32_t *logit_lengths, const int32_t *target_lengths,
+                                           int32_t num_big_blanks, const int32_t *big_blank_durations,
+                                           size_t *workspace_bytes);
+rnnt_status rnnt_multiblank_loss(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V,
+                                 const int32_t *targets, int32_t S, const int32_t *logit_lengths,
+                                 const int32_t *target_lengths, int32_t B, int64_t blank, int32_t num_big_blanks,
+                                 const int32_t *big_blank_ids, const int32_t *big_blank_durations, float sigma,
+                                 float clamp, float fastemit_lambda, int fused_log_softmax,
+                                 rnnt_reduction reduction, float *loss, float *loss_reduced, void *grad,
+                                 void *workspace, size_t workspace_bytes, rnnt_stream_t stream);
+
+/*
+ * rnnt_grad_scale for a gradient written by rnnt_multiblank_loss (same
+ * arguments; the workspace is that call's).
+ */
+rnnt_status rnnt_multiblank_grad_scale(void *grad, rnnt_dtype dtype, int64_t N, int32_t V,
+                                       const int32_t *logit_lengths, const int32_t *target_lengths, int32_t B,
+                                       const float *scale, int per_sample, const void *workspace,
+                                       size_t workspace_bytes, rnnt_stream_t stream);
+
+/*
  * Synchronises `stream`, then copies into *dev_flags the device status word
  * (RNNT_DEV_* bits) of the most recent rnnt_loss_fused call that used
  * `workspace`; every rnnt_loss_fused call clears it when it starts.

@@ -456,6 +456,141 @@ rnnt_status loss_impl(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V
     return RNNT_SUCCESS;
 }
 
+// ------------------------------------------------- multi-blank transducer
+// Samples in batch order; every sample's diagonals are stored U1p wide, U1p a
+// power-of-two multiple of 64 covering the widest lattice.
+struct MbPlan {
+    std::vector<SampleDesc> desc;
+    MbLayout lay{};
+};
+
+rnnt_status build_mb_plan(int32_t B, int32_t V, int64_t N, const int32_t *T, const int32_t *U, int32_t nb,
+                          const int32_t *dur, MbPlan &p) {
+    rnnt_status st = check_lengths(B, V, T, U);
+    if (st != RNNT_SUCCESS) return st;
+    if (nb < 0 || nb > kMaxBigBlanks || (nb > 0 && !dur)) return RNNT_INVALID_VALUE;
+    int dmax = 1;
+    for (int32_t i = 0; i < nb; ++i) {
+        if (dur[i] < 1 || dur[i] > kMaxBigBlankDuration) return RNNT_INVALID_VALUE;
+        dmax = std::max(dmax, (int)dur[i]);
+    }
+    int max_U1 = 1;
+    for (int32_t i = 0; i < B; ++i) max_U1 = std::max(max_U1, U[i] + 1);
+    int J = 1;
+    while (64 * J < max_U1) J <<= 1;
+    const int U1p = 64 * J;
+    if (mb_ring_bytes(U1p, dmax) > kMbRingBytes) return RNNT_INVALID_VALUE;
+    p.desc.resize(B);
+    int64_t row = 0, slot = 0, diag = 0, ab = 0;
+    for (int32_t i = 0; i < B; ++i) {
+        SampleDesc &d = p.desc[i];
+        d.row_off = row;
+        d.slot_off = slot;
+        d.diag_off = diag;
+        d.ab_off = ab;
+        d.T = T[i];
+        d.U = U[i];
+        d.index = i;
+        d.U1p = U1p;
+        d.tstride = U[i] + 1;
+        d.chunk0 = 0;
+        row += (int64_t)T[i] * (U[i] + 1);
+        slot += ((int64_t)T[i] + U[i]) * (U[i] + 1);
+        diag += (int64_t)T[i] + U[i];
+        ab += ((int64_t)T[i] + U[i]) * U1p;
+    }
+    if (N >= 0 && row != N) return RNNT_INVALID_VALUE;
+    if (row >= ((int64_t)1 << 62) / std::max(1, V)) return RNNT_INVALID_VALUE;
+    MbLayout &L = p.lay;
+    size_t off = 0;
+    L.status = 0;
+    off = 256;
+    L.desc = off;   off = align_up(off + sizeof(SampleDesc) * B);
+    L.den = off;    off = align_up(off + sizeof(float) * (size_t)row);
+    L.lp = off;     off = align_up(off + sizeof(float) * (size_t)(2 + nb) * (size_t)slot);
+    L.alpha = off;  off = align_up(off + sizeof(double) * (size_t)ab);
+    L.beta = off;   off = align_up(off + sizeof(double) * (size_t)ab);
+    L.ealpha = off; off = align_up(off + sizeof(int32_t) * (size_t)(diag + B));
+    L.ebeta = off;  off = align_up(off + sizeof(int32_t) * (size_t)(diag + B));
+    L.log2z = off;  off = align_up(off + sizeof(double) * 2 * (size_t)B);
+    L.total = off;
+    L.n_slots = slot;
+    L.U1p = U1p;
+    return RNNT_SUCCESS;
+}
+
+rnnt_status multiblank_impl(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V, const int32_t *targets,
+                            int32_t S, const int32_t *T, const int32_t *U, int32_t B, int64_t blank, int32_t nb,
+                            const int32_t *ids, const int32_t *dur, float sigma, float clamp, float fastemit,
+                            int fused, rnnt_reduction reduction, float *loss, float *loss_reduced, void *grad,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    const int es = esize_of(dtype);
+    if (!es || V < 1 || B < 1 || N < 0) return RNNT_INVALID_VALUE;
+    if (reduction != RNNT_REDUCTION_NONE && reduction != RNNT_REDUCTION_MEAN && reduction != RNNT_REDUCTION_SUM)
+        return RNNT_INVALID_VALUE;
+    if (blank < -(int64_t)V || blank > (int64_t)V - 1) return RNNT_INVALID_VALUE;
+    const int bn = (int)(blank < 0 ? blank + V : blank);
+    if (!(fastemit >= 0.0f) || std::isinf(fastemit) || !std::isfinite(sigma)) return RNNT_INVALID_VALUE;
+    if (!T || !U || !loss || !workspace) return RNNT_INVALID_VALUE;
+    if (nb < 0 || nb > kMaxBigBlanks || (nb > 0 && (!ids || !dur))) return RNNT_INVALID_VALUE;
+    for (int32_t i = 0; i < nb; ++i) {
+        if (ids[i] < 0 || ids[i] >= V || ids[i] == bn) return RNNT_INVALID_VALUE;
+        for (int32_t j = 0; j < i; ++j)
+            if (ids[j] == ids[i]) return RNNT_INVALID_VALUE;
+    }
+    if (N > 0 && !logits) return RNNT_INVALID_VALUE;
+    int32_t maxU = 0;
+    for (int32_t i = 0; i < B; ++i) maxU = std::max(maxU, U[i]);
+    if (maxU > 0 && (!targets || S < maxU)) return RNNT_INVALID_VALUE;
+    if (S < 0) return RNNT_INVALID_VALUE;
+    const size_t bytes = (size_t)N * (size_t)V * (size_t)es;
+    if (grad && grad != logits && bytes > 0 && ranges_overlap(grad, bytes, logits, bytes)) return RNNT_INVALID_VALUE;
+    MbPlan plan;
+    rnnt_status st = build_mb_plan(B, V, N, T, U, nb, dur, plan);
+    if (st != RNNT_SUCCESS) return st;
+    if (workspace_bytes < plan.lay.total) return RNNT_WORKSPACE_TOO_SMALL;
+    if ((uintptr_t)workspace % kAlign != 0) return RNNT_INVALID_VALUE;
+
+    // the status word (cleared) and the descriptors go up in one copy
+    std::vector<uint8_t> head(plan.lay.desc + sizeof(SampleDesc) * B, 0);
+    std::memcpy(head.data() + plan.lay.desc, plan.desc.data(), sizeof(SampleDesc) * B);
+    st = upload(workspace, head, stream);
+    if (st != RNNT_SUCCESS) return st;
+
+    MbArgs a{};
+    a.logits = logits;
+    a.grad = grad;
+    a.esize = es;
+    a.N = N;
+    a.V = V;
+    a.B = B;
+    a.S = S;
+    a.blank = bn;
+    a.fused = fused ? 1 : 0;
+    a.clamp = clamp;
+    a.fastemit = fastemit;
+    a.sigma = sigma;
+    a.grad_scale = reduction == RNNT_REDUCTION_MEAN ? 1.0f / (float)B : 1.0f;
+    a.nb = nb;
+    for (int32_t i = 0; i < nb; ++i) {
+        a.ids[i] = ids[i];
+        a.dur[i] = dur[i];
+    }
+    a.targets = targets;
+    a.loss = loss;
+    a.loss_reduced = loss_reduced;
+    a.reduction = reduction;
+    a.ws = static_cast<uint8_t *>(workspace);
+    a.lay = plan.lay;
+    if (N > 0 && timed(0, stream, [&] { return launch_mb_rows(a, stream); }) != hipSuccess)
+        return RNNT_EXECUTION_FAILED;
+    if (timed(1, stream, [&] { return launch_mb_sweep(a, stream); }) != hipSuccess) return RNNT_EXECUTION_FAILED;
+    if (grad && N > 0 && timed(2, stream, [&] { return launch_mb_grad(a, stream); }) != hipSuccess)
+        return RNNT_EXECUTION_FAILED;
+    if (timed(3, stream, [&] { return launch_mb_reduce(a, stream); }) != hipSuccess) return RNNT_EXECUTION_FAILED;
+    return RNNT_SUCCESS;
+}
+
 rnnt_status grad_scale_impl(void *grad, rnnt_dtype dtype, int64_t N, int32_t V, const int32_t *logit_lengths,
                             const int32_t *target_lengths, int32_t B, const float *scale, int per_sample,
                             const void *workspace, size_t workspace_bytes, hipStream_t stream, const Padding &pad) {
@@ -538,6 +673,53 @@ rnnt_status rnnt_grad_scale_padded(void *grad, rnnt_dtype dtype, int32_t max_T, 
     pad.max_U1 = max_U1;
     return grad_scale_impl(grad, dtype, -1, V, logit_lengths, target_lengths, B, scale, per_sample, workspace,
                            workspace_bytes, static_cast<hipStream_t>(stream), pad);
+}
+
+rnnt_status rnnt_multiblank_workspace_size(int32_t B, int32_t V, int64_t N, rnnt_dtype dtype,
+                                           const int32_t *logit_lengths, const int32_t *target_lengths,
+                                           int32_t num_big_blanks, const int32_t *big_blank_durations,
+                                           size_t *workspace_bytes) {
+    if (!esize_of(dtype) || !workspace_bytes || N < 0) return RNNT_INVALID_VALUE;
+    MbPlan p;
+    rnnt_status st = build_mb_plan(B, V, N, logit_lengths, target_lengths, num_big_blanks, big_blank_durations, p);
+    if (st != RNNT_SUCCESS) return st;
+    *workspace_bytes = p.lay.total;
+    return RNNT_SUCCESS;
+}
+
+rnnt_status rnnt_multiblank_loss(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V, const int32_t *targets,
+                                 int32_t S, const int32_t *logit_lengths, const int32_t *target_lengths, int32_t B,
+                                 int64_t blank, int32_t num_big_blanks, const int32_t *big_blank_ids,
+                                 const int32_t *big_blank_durations, float sigma, float clamp,
+                                 float fastemit_lambda, int fused_log_softmax, rnnt_reduction reduction, float *loss,
+                                 float *loss_reduced, void *grad, void *workspace, size_t workspace_bytes,
+                                 rnnt_stream_t stream) {
+    return multiblank_impl(logits, dtype, N, V, targets, S, logit_lengths, target_lengths, B, blank, num_big_blanks,
+                           big_blank_ids, big_blank_durations, sigma, clamp, fastemit_lambda, fused_log_softmax,
+                           reduction, loss, loss_reduced, grad, workspace, workspace_bytes,
+                           static_cast<hipStream_t>(stream));
+}
+
+rnnt_status rnnt_multiblank_grad_scale(void *grad, rnnt_dtype dtype, int64_t N, int32_t V,
+                                       const int32_t *logit_lengths, const int32_t *target_lengths, int32_t B,
+                                       const float *scale, int per_sample, const void *workspace,
+                                       size_t workspace_bytes, rnnt_stream_t stream) {
+    const int es = esize_of(dtype);
+    if (!es || !grad || !scale || !workspace || V < 1 || B < 1 || N < 0) return RNNT_INVALID_VALUE;
+    rnnt_status st = check_lengths(B, V, logit_lengths, target_lengths);
+    if (st != RNNT_SUCCESS) return st;
+    int64_t rows = 0;
+    for (int32_t i = 0; i < B; ++i) rows += (int64_t)logit_lengths[i] * (target_lengths[i] + 1);
+    if (rows != N) return RNNT_INVALID_VALUE;
+    WorkspaceLayout L{};
+    L.desc = 256;  // where build_mb_plan puts the descriptors
+    if (workspace_bytes < L.desc + sizeof(SampleDesc) * (size_t)B) return RNNT_WORKSPACE_TOO_SMALL;
+    if (N == 0) return RNNT_SUCCESS;
+    const bool aligned16 = ((int64_t)V * es) % 16 == 0 && (uintptr_t)grad % 16 == 0;
+    if (launch_grad_scale(grad, es, V, N, B, scale, per_sample, static_cast<const uint8_t *>(workspace), L,
+                          row_geometry(V, es, aligned16), static_cast<hipStream_t>(stream)) != hipSuccess)
+        return RNNT_EXECUTION_FAILED;
+    return RNNT_SUCCESS;
 }
 
 rnnt_status rnnt_timing_enable(int on) {

@@ -187,4 +187,45 @@ hipError_t launch_zero_padding(void *grad, int esize, int V, int B, int max_T, i
 // Largest lattice width (U+1) the alpha/beta kernel supports.
 constexpr int kMaxU1 = 1024;
 
+// ------------------------------------------------- multi-blank transducer
+constexpr int kMaxBigBlanks = 4;
+constexpr int kMaxBigBlankDuration = 16;
+constexpr size_t kMbRingBytes = 64 * 1024;  // LDS of one sweep: the last (longest duration + 1) diagonals
+
+// Workspace of the multi-blank path.  Byte offsets; the status word is at 0
+// and the sample descriptors at 256, as in the plain layout.
+struct MbLayout {
+    size_t status, desc, den, lp, alpha, beta, ealpha, ebeta, log2z, total;
+    int64_t n_slots;    // skewed node slots, sum_i (T_i+U_i)(U_i+1)
+    int U1p;            // columns of one stored diagonal, a multiple of 64 for every sample
+};
+
+struct MbArgs {
+    const void *logits;
+    void *grad;
+    int esize;
+    int64_t N;
+    int V, B, S;
+    int blank;          // normalised
+    int fused;
+    float clamp, fastemit, sigma, grad_scale;
+    int nb;             // number of big blanks
+    int ids[kMaxBigBlanks];
+    int dur[kMaxBigBlanks];
+    const int32_t *targets;
+    float *loss;
+    float *loss_reduced;
+    int reduction;
+    uint8_t *ws;
+    MbLayout lay;
+};
+
+// LDS bytes of one multi-blank sweep: (longest duration + 1) diagonals of U1p
+// fp64 values and their exponents.
+size_t mb_ring_bytes(int U1p, int max_duration);
+hipError_t launch_mb_rows(const MbArgs &a, hipStream_t stream);
+hipError_t launch_mb_sweep(const MbArgs &a, hipStream_t stream);
+hipError_t launch_mb_grad(const MbArgs &a, hipStream_t stream);
+hipError_t launch_mb_reduce(const MbArgs &a, hipStream_t stream);
+
 }  // namespace rnnt

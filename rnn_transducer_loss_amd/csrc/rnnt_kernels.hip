@@ -1462,4 +1462,426 @@ hipError_t launch_zero_padding(void *grad, int esize, int V, int B, int max_T, i
 
 #undef WS
 
+// ====================================================== multi-blank transducer
+// The ESPnet compute_multiblank_grad_kernel page: activations over the labels,
+// the standard blank and num_big_blanks big blanks, each big blank with a
+// duration, and sigma, the logit under-normalisation hyper-parameter.  From
+// node (t,u) the standard blank moves to (t+1,u), big blank i to (t+d_i,u)
+// and the next label to (t,u+1); every edge's log-probability is lowered by
+// sigma; an alignment ends when a blank of any kind reaches t = T exactly at
+// u = U.  The sweeps treat that end as a virtual node (T,U) on anti-diagonal
+// T+U, with beta(T,U) = 1, so the ends need no special case.
+//
+// Three passes of their own: per row, the log-normaliser and the edges'
+// log-probabilities (fp32 planes in the skewed slots); one wave per sample
+// and direction sweeping anti-diagonals in fp64 probabilities renormalised by
+// a power of two on every diagonal, with the last (longest duration + 1)
+// diagonals in an LDS ring for the big blanks' jumps; and per row, the
+// gradient.  The loss check and reduction are k_reduce's.
+namespace {
+
+struct MbParams {
+    int nb;
+    int ids[kMaxBigBlanks];
+    int dur[kMaxBigBlanks];
+    int R;        // ring depth: the longest duration + 1
+    float sigma;
+};
+
+__device__ __forceinline__ const SampleDesc &mb_sample_of_row(const SampleDesc *__restrict__ desc, int B,
+                                                              int64_t r) {
+    int lo = 0, hi = B - 1;  // last sample whose first row is <= r (every sample has a row)
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (desc[mid].row_off <= r) lo = mid;
+        else hi = mid - 1;
+    }
+    return desc[lo];
+}
+
+// exp(lp) in fp64 for an fp32 log-prob, the exponent split off exactly, so
+// a weight far below fp32's range keeps its value.
+__device__ __forceinline__ double prob_d(float lp) {
+    constexpr float kHi = 1.44269502162933349609375f;
+    constexpr float kLo = 1.925963033500011079e-8f;
+    const float k = rintf(lp * kLog2e);
+    const float f = fmaf(lp, kHi, -k) + lp * kLo;
+    const double p = __builtin_amdgcn_ldexp((double)exp2_fast(f), (int)k);
+    return (lp < -1100.f) ? 0.0 : p;
+}
+
+__device__ __forceinline__ double readlane_d(double v, int l) {
+    const int lo = __builtin_amdgcn_readlane(__double2loint(v), l);
+    const int hi = __builtin_amdgcn_readlane(__double2hiint(v), l);
+    return __hiloint2double(hi, lo);
+}
+
+// One wave per packed row, four per workgroup: the row's log-normaliser
+// (fused) and the log-probabilities, less sigma, of the edges leaving the
+// node, at its skewed slot: plane 0 the standard blank, plane 1 the next label
+// (-inf at u = U or for a label outside [0,V)), plane 2+i big blank i.
+template <typename T>
+__global__ __launch_bounds__(256) void k_mb_rows(const T *__restrict__ logits, int64_t N, int V, int blank,
+                                                 int fused, MbParams mp, const SampleDesc *__restrict__ desc,
+                                                 int B, const int32_t *__restrict__ targets, int S,
+                                                 float *__restrict__ den, float *__restrict__ lp, int64_t n_slots,
+                                                 uint32_t *status, int64_t row_base) {
+    const int lane = threadIdx.x & 63;
+    const int64_t r = row_base + (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= N) return;
+    const SampleDesc d = mb_sample_of_row(desc, B, r);
+    const int U1 = d.U + 1;
+    const int64_t lr = r - d.row_off;
+    const int t = (int)(lr / U1);
+    const int u = (int)(lr - (int64_t)t * U1);
+    const T *x = logits + r * (int64_t)V;
+    float dn = 0.f;
+    if (fused) {
+        float m = kNegInf;
+        for (int k = lane; k < V; k += 64) m = fmaxf(m, Elem<T>::load1(x + k));
+        m = wave_max_f(m);
+        float sum = 0.f;
+        if (m != kNegInf)
+            for (int k = lane; k < V; k += 64) sum += exp2_fast((Elem<T>::load1(x + k) - m) * kLog2e);
+        sum = wave_sum_f(sum);
+        dn = (m == kNegInf) ? kNegInf : m + log2_fast(sum) * kLn2;
+    }
+    if (lane == 0) den[r] = dn;
+    if (lane < 2 + mp.nb) {
+        int k = blank;
+        if (lane == 1) {
+            k = -1;
+            if (u < d.U) {
+                const int y = targets[(int64_t)d.index * S + u];
+                bool bad = y < 0 || y >= V || y == blank;
+#pragma unroll
+                for (int i = 0; i < kMaxBigBlanks; ++i) bad = bad || (i < mp.nb && y == mp.ids[i]);
+                if (bad) atomicOr(status, (uint32_t)RNNT_DEV_BAD_TARGET);
+                k = (y >= 0 && y < V) ? y : -1;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kMaxBigBlanks; ++i)
+            if (lane == 2 + i) k = mp.ids[i];
+        const float v = (k >= 0 && dn != kNegInf) ? Elem<T>::load1(x + k) - dn - mp.sigma : kNegInf;
+        lp[(int64_t)lane * n_slots + d.slot_off + (int64_t)(t + u) * U1 + u] = v;
+    }
+}
+
+// One wave per (sample, direction): blockIdx 2i runs alpha of sample i,
+// 2i+1 beta.  Lane l holds columns l + 64j, j < J.  `cur` is the diagonal
+// just finished, scaled by 2^-E; the ring keeps the last R diagonals (and
+// their exponents) for the big blanks, whose sources lie d_i diagonals away.
+// Every weight is masked where its edge does not exist, so unwritten slots
+// are never used.  Stored: every real diagonal of alpha or beta (scaled) and
+// its exponent; log2 P(y|x) and, from beta, the loss.
+template <int J>
+__global__ __launch_bounds__(64) void k_mb_sweep(const SampleDesc *__restrict__ desc, int B, MbParams mp,
+                                                 const float *__restrict__ lp, int64_t n_slots,
+                                                 double *__restrict__ alpha, double *__restrict__ beta,
+                                                 int *__restrict__ ealpha, int *__restrict__ ebeta,
+                                                 double *__restrict__ log2z, float *__restrict__ loss) {
+    extern __shared__ double mb_ring[];  // R * J * 64 values, then R exponents
+    constexpr int U1p = 64 * J;
+    const int lane = threadIdx.x;
+    const SampleDesc d = desc[blockIdx.x >> 1];
+    const bool bw = (blockIdx.x & 1) != 0;
+    const int T = d.T, U = d.U, U1 = U + 1, nd = T + U, R = mp.R;
+    int *ering = reinterpret_cast<int *>(mb_ring + (size_t)R * J * 64);
+    for (int q = lane; q < R * J * 64; q += 64) mb_ring[q] = 0.0;
+    for (int q = lane; q < R; q += 64) ering[q] = 0;
+    const float *lpb = lp + d.slot_off;
+    const float *lpy = lp + n_slots + d.slot_off;
+    const float *lpg = lp + 2 * n_slots + d.slot_off;
+    double *tab = (bw ? beta : alpha) + d.ab_off;
+    int *etab = (bw ? ebeta : ealpha) + d.diag_off + d.index;
+
+    // start: alpha(0,0) = 1 on diagonal 0; beta of the virtual end (T,U) = 1 on diagonal T+U
+    double cur[J];
+    int E = 0;
+    {
+        const int n0 = bw ? nd : 0;
+        const int uc = bw ? U : 0;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            cur[j] = (lane + 64 * j == uc) ? 1.0 : 0.0;
+            mb_ring[((n0 % R) * J + j) * 64 + lane] = cur[j];
+        }
+        if (!bw) {
+#pragma unroll
+            for (int j = 0; j < J; ++j) tab[j * 64 + lane] = cur[j];
+            if (lane == 0) etab[0] = 0;
+        }
+    }
+
+    for (int step = 1; step <= nd; ++step) {
+        const int n = bw ? nd - step : step;
+        // the neighbouring column of the finished diagonal: u-1 (forward) or u+1 (backward)
+        double rot[J], side[J];
+#pragma unroll
+        for (int j = 0; j < J; ++j) rot[j] = bw ? rotate_down(cur[j]) : rotate_up(cur[j]);
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            if (bw) side[j] = (lane == 63) ? (j + 1 < J ? rot[j + 1] : 0.0) : rot[j];
+            else side[j] = (lane == 0) ? (j > 0 ? rot[j - 1] : 0.0) : rot[j];
+        }
+        // big blanks: source diagonal, whether it exists, its exponent relative to E
+        int ns[kMaxBigBlanks], shg[kMaxBigBlanks];
+        bool okd[kMaxBigBlanks];
+        int64_t pl[kMaxBigBlanks];  // the big blank's plane; an unused slot reads plane 0, masked
+#pragma unroll
+        for (int i = 0; i < kMaxBigBlanks; ++i) {
+            pl[i] = (int64_t)(i < mp.nb ? i : 0) * n_slots;
+            ns[i] = bw ? n + mp.dur[i] : n - mp.dur[i];
+            okd[i] = (i < mp.nb) && (bw ? ns[i] <= nd : ns[i] >= 0);
+            if (!okd[i]) ns[i] = bw ? n : 0;  // an in-range stand-in; its weight is masked
+            shg[i] = okd[i] ? ering[ns[i] % R] - E : 0;
+        }
+        double nx[J];
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int u = lane + 64 * j;
+            const int t = n - u;
+            const int uc = min(u, U);
+            double acc;
+            bool cell;
+            if (!bw) {
+                cell = (u <= U) && ((t >= 0 && t <= T - 1) || (t == T && u == U));
+                const int64_t sp = (int64_t)(n - 1) * U1;
+                const float b = lpb[sp + uc];
+                const float y = lpy[sp + max(uc - 1, 0)];
+                const bool okb = (t >= 1) && (t <= T);            // from (t-1,u)
+                const bool oky = (u >= 1) && (t >= 0) && (t <= T - 1);  // from (t,u-1)
+                acc = (okb ? prob_d(b) : 0.0) * cur[j] + (oky ? prob_d(y) : 0.0) * side[j];
+#pragma unroll
+                for (int i = 0; i < kMaxBigBlanks; ++i) {
+                    const int ts = t - mp.dur[i];                   // from (t-d_i,u)
+                    const bool ok = okd[i] && ts >= 0 && ts <= T - 1;
+                    const float g = lpg[pl[i] + (int64_t)ns[i] * U1 + uc];
+                    const double src = mb_ring[((ns[i] % R) * J + j) * 64 + lane];
+                    acc += ok ? prob_d(g) * __builtin_amdgcn_ldexp(src, shg[i]) : 0.0;
+                }
+            } else {
+                cell = (u <= U) && (t >= 0) && (t <= T - 1);
+                const int64_t sc = (int64_t)n * U1 + uc;
+                const float b = lpb[sc];
+                const float y = lpy[sc];
+                acc = (cell ? prob_d(b) : 0.0) * cur[j] + ((cell && u < U) ? prob_d(y) : 0.0) * side[j];
+#pragma unroll
+                for (int i = 0; i < kMaxBigBlanks; ++i) {
+                    const bool ok = okd[i] && cell;                 // to (t+d_i,u); zero where that is no node
+                    const float g = lpg[pl[i] + sc];
+                    const double src = mb_ring[((ns[i] % R) * J + j) * 64 + lane];
+                    acc += ok ? prob_d(g) * __builtin_amdgcn_ldexp(src, shg[i]) : 0.0;
+                }
+            }
+            nx[j] = cell ? acc : 0.0;
+        }
+        // renormalise by a power of two (a diagonal of zeros keeps its exponent)
+        int eb = 0;
+#pragma unroll
+        for (int j = 0; j < J; ++j) eb = max(eb, (__double2hiint(nx[j]) >> 20) & 0x7ff);
+        eb = wave_max_i(eb);
+        const int sh = eb == 0 ? 0 : eb - 1023;
+        E += sh;
+        const int slot = n % R;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            cur[j] = __builtin_amdgcn_ldexp(nx[j], -sh);
+            mb_ring[(slot * J + j) * 64 + lane] = cur[j];
+        }
+        if (lane == 0) ering[slot] = E;
+        if (n < nd) {
+#pragma unroll
+            for (int j = 0; j < J; ++j) tab[(int64_t)n * U1p + j * 64 + lane] = cur[j];
+            if (lane == 0) etab[n] = E;
+        }
+    }
+
+    // log2 P(y|x): alpha of the virtual end (T,U), or beta(0,0)
+    const int ue = bw ? 0 : U;
+    double v = 0.0;
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+        if (j == (ue >> 6)) v = cur[j];
+    v = readlane_d(v, ue & 63);
+    const double l2 = (v > 0.0) ? log2_d(v) + (double)E : kNegInfD;
+    if (lane == 0) {
+        if (bw) {
+            log2z[d.index] = l2;
+            loss[d.index] = (float)(-l2 * kLn2D);
+        } else {
+            log2z[B + d.index] = l2;
+        }
+    }
+}
+
+// One wave per packed row, four per workgroup: g_k = P(k) (occ + lambda
+// flow_y) - the flows of the edges leaving the node, each at its class
+// (standard blank, label weighted by 1 + lambda, big blanks), clamped,
+// times the reduction scale.  P(k) is the softmax without sigma (sigma is a
+// constant of every log-probability, so it leaves the log_softmax Jacobian
+// as it is); without fused log_softmax only the flows remain.
+template <typename T>
+__global__ __launch_bounds__(256) void k_mb_grad(const T *__restrict__ logits, T *__restrict__ grad, int64_t N,
+                                                 int V, int blank, int fused, MbParams mp, int U1p,
+                                                 const SampleDesc *__restrict__ desc, int B,
+                                                 const int32_t *__restrict__ targets, int S,
+                                                 const float *__restrict__ den, const float *__restrict__ lp,
+                                                 int64_t n_slots, const double *__restrict__ alpha,
+                                                 const double *__restrict__ beta, const int *__restrict__ ealpha,
+                                                 const int *__restrict__ ebeta, const double *__restrict__ log2z,
+                                                 float clamp, float scale, float fastemit, int64_t row_base) {
+    const int lane = threadIdx.x & 63;
+    const int64_t r = row_base + (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= N) return;
+    const SampleDesc d = mb_sample_of_row(desc, B, r);
+    const int U1 = d.U + 1;
+    const int64_t lr = r - d.row_off;
+    const int t = (int)(lr / U1);
+    const int u = (int)(lr - (int64_t)t * U1);
+    const int n = t + u;
+    const int64_t s = d.slot_off + (int64_t)n * U1 + u;
+    const int64_t eo = d.diag_off + d.index;
+    const double lz = log2z[d.index];
+    // log2 beta of node (t2,u2): the virtual end (T,U) is 1, anything outside the lattice 0
+    auto lbeta = [&](int t2, int u2) -> double {
+        if (t2 == d.T && u2 == d.U) return 0.0;
+        if (t2 >= d.T || u2 > d.U) return kNegInfD;
+        const int n2 = t2 + u2;
+        return log2_d(beta[d.ab_off + (int64_t)n2 * U1p + u2]) + (double)ebeta[eo + n2];
+    };
+    double lo = kNegInfD, lb = kNegInfD, ly = kNegInfD;
+    double lg[kMaxBigBlanks];
+#pragma unroll
+    for (int i = 0; i < kMaxBigBlanks; ++i) lg[i] = kNegInfD;
+    if (lz != kNegInfD) {
+        const double la = log2_d(alpha[d.ab_off + (int64_t)n * U1p + u]) + (double)ealpha[eo + n] - lz;
+        lo = la + lbeta(t, u);
+        lb = la + (double)lp[s] * kLog2eD + lbeta(t + 1, u);
+        if (u < d.U) ly = la + (double)lp[n_slots + s] * kLog2eD + lbeta(t, u + 1);
+#pragma unroll
+        for (int i = 0; i < kMaxBigBlanks; ++i)
+            if (i < mp.nb) lg[i] = la + (double)lp[(int64_t)(2 + i) * n_slots + s] * kLog2eD + lbeta(t + mp.dur[i], u);
+    }
+    if (fastemit > 0.f && ly != kNegInfD && lo != kNegInfD)
+        lo += (double)log2f(1.f + fastemit * exp2_fast((float)(ly - lo)));
+    int y = -1;
+    if (u < d.U) {
+        const int yy = targets[(int64_t)d.index * S + u];
+        y = (yy >= 0 && yy < V) ? yy : -1;
+    }
+    const float fb = exp2_fast((float)lb) * scale;
+    const float fy = exp2_fast((float)ly) * scale * (1.f + fastemit);
+    float fg[kMaxBigBlanks];
+#pragma unroll
+    for (int i = 0; i < kMaxBigBlanks; ++i) fg[i] = exp2_fast((float)lg[i]) * scale;
+    const float dn = den[r];
+    const float shift2 = (fused && dn != kNegInf) ? (float)(lo - (double)dn * kLog2eD) + log2_fast(scale) : kNegInf;
+    const bool do_clamp = clamp > 0.f;
+    const float cl = clamp * scale;
+    const T *x = logits + r * (int64_t)V;
+    T *g = grad + r * (int64_t)V;
+    for (int k = lane; k < V; k += 64) {
+        float v = 0.f;
+        if (fused) v = exp2_fast(fmaf(Elem<T>::load1(x + k), kLog2e, shift2));
+        v -= (k == blank) ? fb : 0.f;
+        v -= (k == y) ? fy : 0.f;
+#pragma unroll
+        for (int i = 0; i < kMaxBigBlanks; ++i) v -= (i < mp.nb && k == mp.ids[i]) ? fg[i] : 0.f;
+        Elem<T>::store1(g + k, clamp_to(v, cl, do_clamp));
+    }
+}
+
+MbParams mb_params(const MbArgs &a) {
+    MbParams p{};
+    p.nb = a.nb;
+    int dmax = 1;
+    for (int i = 0; i < kMaxBigBlanks; ++i) {
+        p.ids[i] = i < a.nb ? a.ids[i] : -1;
+        p.dur[i] = i < a.nb ? a.dur[i] : 1;
+        if (i < a.nb) dmax = std::max(dmax, a.dur[i]);
+    }
+    p.R = dmax + 1;
+    p.sigma = a.sigma;
+    return p;
+}
+
+template <typename Fn> hipError_t with_esize(int esize, Fn &&fn) {
+    if (esize == 4) return fn(float{});
+    return fn(_Float16{});
+}
+
+}  // namespace
+
+#define MBWS(type, field) reinterpret_cast<type>(a.ws + a.lay.field)
+
+size_t mb_ring_bytes(int U1p, int max_duration) {
+    return (size_t)(max_duration + 1) * (size_t)U1p * sizeof(double) + (size_t)(max_duration + 1) * sizeof(int);
+}
+
+hipError_t launch_mb_rows(const MbArgs &a, hipStream_t stream) {
+    const MbParams mp = mb_params(a);
+    return with_esize(a.esize, [&](auto tag) {
+        using T = decltype(tag);
+        const int64_t blocks = (a.N + 3) / 4;
+        constexpr int64_t kMaxBlocks = (int64_t)1 << 24;
+        for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocks) {
+            const unsigned nb = (unsigned)std::min<int64_t>(kMaxBlocks, blocks - b0);
+            hipLaunchKernelGGL(k_mb_rows<T>, dim3(nb), dim3(256), 0, stream, static_cast<const T *>(a.logits), a.N,
+                               a.V, a.blank, a.fused, mp, MBWS(const SampleDesc *, desc), a.B, a.targets, a.S,
+                               MBWS(float *, den), MBWS(float *, lp), a.lay.n_slots, MBWS(uint32_t *, status),
+                               b0 * 4);
+        }
+        return hipGetLastError();
+    });
+}
+
+hipError_t launch_mb_sweep(const MbArgs &a, hipStream_t stream) {
+    const MbParams mp = mb_params(a);
+    const size_t lds = mb_ring_bytes(a.lay.U1p, mp.R - 1);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(2 * a.B), dim3(64), lds, stream, MBWS(const SampleDesc *, desc), a.B, mp,
+                           MBWS(const float *, lp), a.lay.n_slots, MBWS(double *, alpha), MBWS(double *, beta),
+                           MBWS(int *, ealpha), MBWS(int *, ebeta), MBWS(double *, log2z), a.loss);
+        return hipGetLastError();
+    };
+    switch (a.lay.U1p / 64) {
+    case 1: return go(k_mb_sweep<1>);
+    case 2: return go(k_mb_sweep<2>);
+    case 4: return go(k_mb_sweep<4>);
+    case 8: return go(k_mb_sweep<8>);
+    case 16: return go(k_mb_sweep<16>);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_mb_grad(const MbArgs &a, hipStream_t stream) {
+    const MbParams mp = mb_params(a);
+    return with_esize(a.esize, [&](auto tag) {
+        using T = decltype(tag);
+        const int64_t blocks = (a.N + 3) / 4;
+        constexpr int64_t kMaxBlocks = (int64_t)1 << 24;
+        for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocks) {
+            const unsigned nb = (unsigned)std::min<int64_t>(kMaxBlocks, blocks - b0);
+            hipLaunchKernelGGL(k_mb_grad<T>, dim3(nb), dim3(256), 0, stream, static_cast<const T *>(a.logits),
+                               static_cast<T *>(a.grad), a.N, a.V, a.blank, a.fused, mp, a.lay.U1p,
+                               MBWS(const SampleDesc *, desc), a.B, a.targets, a.S, MBWS(const float *, den),
+                               MBWS(const float *, lp), a.lay.n_slots, MBWS(const double *, alpha),
+                               MBWS(const double *, beta), MBWS(const int *, ealpha), MBWS(const int *, ebeta),
+                               MBWS(const double *, log2z), a.clamp, a.grad_scale, a.fastemit, b0 * 4);
+        }
+        return hipGetLastError();
+    });
+}
+
+hipError_t launch_mb_reduce(const MbArgs &a, hipStream_t stream) {
+    float *out = (a.reduction != RNNT_REDUCTION_NONE) ? a.loss_reduced : nullptr;
+    hipLaunchKernelGGL(k_reduce, dim3(1), dim3(64), 0, stream, a.loss, MBWS(const double *, log2z), a.B,
+                       a.reduction == RNNT_REDUCTION_MEAN, out, MBWS(uint32_t *, status));
+    return hipGetLastError();
+}
+
+#undef MBWS
+
 }  // namespace rnnt

@@ -190,3 +190,102 @@ class RNNTLoss(torch.nn.Module):
     def forward(self, logits, targets, logit_lengths, target_lengths):
         return rnnt_loss(logits, targets, logit_lengths, target_lengths, self.blank, self.clamp, self.reduction,
                          self.fused_log_softmax, self.fastemit_lambda)
+
+
+# ------------------------------------------------------ multi-blank transducer
+def rnnt_multiblank_fused(logits: torch.Tensor, targets: torch.Tensor, logit_lengths, target_lengths,
+                          big_blank_ids, big_blank_durations, blank: int = -1, sigma: float = 0.0,
+                          clamp: float = -1.0, reduction: str = "mean", fused_log_softmax: bool = True,
+                          fastemit_lambda: float = 0.0, compute_grad: bool = True,
+                          grad: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                          loss: Optional[torch.Tensor] = None, loss_reduced: Optional[torch.Tensor] = None):
+    """One multi-blank librnnt call over packed logits.  Returns ``(loss, loss_reduced, grad, workspace)``.
+
+    Big blank i is class ``big_blank_ids[i]`` and advances t by ``big_blank_durations[i]`` frames; ``sigma`` is
+    subtracted from every emission's log-probability (logit under-normalisation).  The rest is as for
+    :func:`rnnt_loss_fused`.
+    """
+    tg = _prepare(logits, targets)
+    if logits.dim() != 2:
+        raise ValueError("the multi-blank loss takes packed 2-D (sum_i T_i*(U_i+1), V) logits")
+    T = _lib.host_i32(logit_lengths)
+    U = _lib.host_i32(target_lengths)
+    B = len(T)
+    if len(U) != B:
+        raise ValueError("logit_lengths and target_lengths must have the same length")
+    dev = logits.device
+    code = _dtype_code(logits.dtype)
+    N, V = logits.shape
+    need = _lib.workspace_size_multiblank(B, V, N, code, T, U, big_blank_durations)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if loss is None:
+        loss = torch.empty(B, dtype=torch.float32, device=dev)
+    if reduction != "none" and loss_reduced is None:
+        loss_reduced = torch.empty(1, dtype=torch.float32, device=dev)
+    if compute_grad:
+        if grad is None:
+            grad = torch.empty_like(logits)
+        elif grad.shape != logits.shape or grad.dtype != logits.dtype or not grad.is_contiguous():
+            raise ValueError("grad must match logits in shape and dtype and be contiguous")
+    else:
+        grad = None
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        _lib.loss_multiblank(logits.data_ptr(), code, N, V, tg.data_ptr() if tg.numel() else 0, tg.shape[1], T, U,
+                             blank, big_blank_ids, big_blank_durations, sigma, clamp, fastemit_lambda,
+                             fused_log_softmax, reduction, loss.data_ptr(),
+                             loss_reduced.data_ptr() if reduction != "none" else 0,
+                             grad.data_ptr() if grad is not None else 0, workspace.data_ptr(), workspace.numel(),
+                             stream)
+    return loss, (loss_reduced if reduction != "none" else None), grad, workspace
+
+
+class _MultiblankFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, logits, targets, logit_lengths, target_lengths, big_blank_ids, big_blank_durations, blank,
+                sigma, clamp, reduction, fused_log_softmax, fastemit_lambda):
+        T = _lib.host_i32(logit_lengths)
+        U = _lib.host_i32(target_lengths)
+        loss, loss_red, grad, ws = rnnt_multiblank_fused(
+            logits, targets, T, U, big_blank_ids, big_blank_durations, blank, sigma, clamp, reduction,
+            fused_log_softmax, fastemit_lambda, compute_grad=logits.requires_grad)
+        ctx.meta = (T, U, reduction, logits.shape, logits.dtype)
+        ctx.used = False
+        if grad is not None:
+            ctx.save_for_backward(grad, ws)
+        return loss if reduction == "none" else loss_red.reshape(())
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        none = (None,) * 11
+        T, U, reduction, shape, dtype = ctx.meta
+        if not ctx.saved_tensors:
+            return (None,) + none
+        if ctx.used:
+            raise RuntimeError("rnnt_loss_multiblank backward was already run for this forward call")
+        ctx.used = True
+        grad, ws = ctx.saved_tensors
+        scale = grad_out.detach().to(device=grad.device, dtype=torch.float32).contiguous().reshape(-1)
+        with torch.cuda.device(grad.device):
+            stream = torch.cuda.current_stream(grad.device).cuda_stream
+            _lib.grad_scale_multiblank(grad.data_ptr(), _dtype_code(dtype), shape[0], shape[1], T, U,
+                                       scale.data_ptr(), reduction == "none", ws.data_ptr(), ws.numel(), stream)
+        return (grad,) + none
+
+
+def rnnt_loss_multiblank(logits: torch.Tensor, targets: torch.Tensor, logit_lengths, target_lengths,
+                         big_blank_durations, big_blank_ids, blank: int = -1, sigma: float = 0.0,
+                         clamp: float = -1.0, reduction: str = "mean", fused_log_softmax: bool = True,
+                         fastemit_lambda: float = 0.0) -> torch.Tensor:
+    """Multi-blank transducer loss over packed logits, differentiable with respect to ``logits``.
+
+    ``big_blank_durations[i]`` is the number of frames big blank i (class ``big_blank_ids[i]``) advances;
+    ``sigma`` lowers every emission's log-probability (logit under-normalisation).  With no big blank and
+    ``sigma = 0`` this is :func:`rnnt_loss`.
+    """
+    if reduction not in ("none", "mean", "sum"):
+        raise ValueError(f"reduction must be none, mean or sum, got {reduction!r}")
+    return _MultiblankFunction.apply(logits, targets, logit_lengths, target_lengths, list(big_blank_ids),
+                                     list(big_blank_durations), int(blank), float(sigma), float(clamp), reduction,
+                                     bool(fused_log_softmax), float(fastemit_lambda))

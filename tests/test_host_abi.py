@@ -192,3 +192,40 @@ def test_schedule_chunk_sizes_follow_row_bytes():
     # about 256 KiB of logits per chunk, in multiples of 64 rows
     assert c32[0, 2] == 64 and c16[0, 2] == 64
     assert (c32[:, 2] % 64 == 0).sum() >= len(c32) - 8
+
+
+def _call_multiblank(**over):
+    """rnnt_multiblank_loss with fake (never dereferenced) device pointers; only host checks can run."""
+    T = np.array([4, 6], np.int32)
+    U = np.array([2, 1], np.int32)
+    args = dict(logits_ptr=0x100000, dtype_code=0, N=24, V=8, targets_ptr=0x200000, S=2, logit_lengths=T,
+                target_lengths=U, blank=-1, big_blank_ids=[6, 5], big_blank_durations=[2, 3], sigma=0.0, clamp=-1.0,
+                fastemit_lambda=0.0, fused=True, reduction="mean", loss_ptr=0x300000, loss_reduced_ptr=0x400000,
+                grad_ptr=0x500000, ws_ptr=0x600000, ws_bytes=1 << 20, stream=0)
+    args.update(over)
+    _lib.loss_multiblank(**args)
+
+
+@pytest.mark.parametrize("over", [
+    dict(big_blank_ids=[7, 5]),                       # equal to the standard blank (V-1)
+    dict(big_blank_ids=[6, 6]),                       # duplicate
+    dict(big_blank_ids=[8, 5]),                       # outside [0, V)
+    dict(big_blank_durations=[0, 3]), dict(big_blank_durations=[2, 17]),
+    dict(big_blank_ids=[1, 2, 3, 4, 5], big_blank_durations=[2, 2, 2, 2, 2]),   # more than four
+    dict(sigma=float("nan")), dict(fastemit_lambda=-1.0), dict(blank=8), dict(N=25), dict(S=1),
+    dict(ws_bytes=64), dict(ws_ptr=0x600010), dict(loss_ptr=0),
+])
+def test_multiblank_call_rejects_invalid_arguments_before_any_launch(over):
+    with pytest.raises(ValueError):
+        _call_multiblank(**over)
+
+
+def test_multiblank_ring_limit():
+    # (longest duration + 1) diagonals of the widest lattice (8 bytes a column plus a 4-byte exponent each) must
+    # fit 64 KiB of LDS: U+1 = 1000 pads to 1024 columns, so durations up to 6 fit and 7 does not
+    T, U = np.array([3], np.int32), np.array([999], np.int32)
+    N = 3 * 1000
+    assert _lib.workspace_size_multiblank(1, 8, N, 0, T, U, [6]) > 0
+    with pytest.raises(ValueError):
+        _lib.workspace_size_multiblank(1, 8, N, 0, T, U, [7])
+    assert _lib.workspace_size_multiblank(1, 8, 3 * 200, 0, T, np.array([199], np.int32), [16]) > 0

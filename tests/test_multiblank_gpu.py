@@ -1,0 +1,202 @@
+"""GPU parity of the multi-blank transducer path against the fp64 oracle (run on an MI355X).
+
+The path (the ESPnet compute_multiblank_grad_kernel page: big blanks with durations and sigma, the logit
+under-normalisation) runs through the C ABI (``rnnt_multiblank_loss``) on seeded inputs and is compared element
+by element with ``oracle.multiblank_sample`` on the same inputs, to the same gates as the plain path:
+
+    fp32 inputs: loss relative error <= 1e-5, gradient absolute error <= 1e-5
+    fp16 inputs: loss relative error <= 2e-3, gradient absolute error <= 3e-3
+
+The per-sample gradient (the output divided by the reduction scale) is held to the gate.
+"""
+import concurrent.futures as cf
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: (1e-5, 1e-5), torch.float16: (2e-3, 3e-3)}
+
+
+@pytest.fixture(scope="module")
+def rl():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rnn_transducer_loss_amd as rl
+    rl._lib.load()
+    return rl
+
+
+def _threads():
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:  # pragma: no cover
+        return 4
+
+
+def run_mb(rl, w, reduction=None, clamp=None, fastemit=0.0, compute_grad=True):
+    reduction = w.reduction if reduction is None else reduction
+    clamp = w.clamp if clamp is None else clamp
+    tg = torch.from_numpy(w.targets).to("cuda")
+    loss, red, grad, ws = rl.rnnt_multiblank_fused(w.logits, tg, w.logit_lengths, w.target_lengths,
+                                                   w.big_blank_ids, w.big_blank_durations, blank=w.blank,
+                                                   sigma=w.sigma, clamp=clamp, reduction=reduction,
+                                                   fused_log_softmax=w.fused, fastemit_lambda=fastemit,
+                                                   compute_grad=compute_grad)
+    flags = rl.device_flags(ws)
+    torch.cuda.synchronize()
+    return loss, red, grad, flags
+
+
+def check_mb(w, loss, grad, reduction, clamp=None, fastemit=0.0, grad_samples=None):
+    clamp = w.clamp if clamp is None else clamp
+    ltol, gtol = TOL[w.dtype]
+    b = w.blank + w.V if w.blank < 0 else w.blank
+    scale = 1.0 / w.B if reduction == "mean" else 1.0
+    loss_h = loss.detach().cpu().numpy().astype(np.float64)
+    want = set(range(w.B) if grad_samples is None else grad_samples) if grad is not None else set()
+
+    def one(i):
+        T, U = int(w.logit_lengths[i]), int(w.target_lengths[i])
+        x = w.logits[w.rows(i)].detach().cpu().numpy()
+        r = oracle.multiblank_sample(x, T, U, w.targets[i], b, w.big_blank_ids, w.big_blank_durations, w.sigma,
+                                     w.fused, clamp, fastemit, want_grad=(i in want))
+        return i, r
+
+    worst_l, worst_g = 0.0, 0.0
+    with cf.ThreadPoolExecutor(_threads()) as ex:
+        for i, r in ex.map(one, range(w.B)):
+            rel = abs(loss_h[i] - r.loss) / max(1.0, abs(r.loss))
+            worst_l = max(worst_l, rel)
+            assert rel <= ltol, f"sample {i}: loss {loss_h[i]} vs oracle {r.loss} (rel {rel:.3g})"
+            if r.grad is not None:
+                g = grad[w.rows(i)].detach().double().cpu().numpy() / scale
+                err = np.abs(g - r.grad).max()
+                worst_g = max(worst_g, err)
+                assert err <= gtol, f"sample {i}: grad max abs err {err:.3g}"
+    return worst_l, worst_g
+
+
+def _mb(Ts, Us, V, ids, durs, sigma=0.0, **kw):
+    return workloads.make_custom(Ts, Us, V, device="cuda", big_blank_ids=ids, big_blank_durations=durs, sigma=sigma,
+                                 **kw)
+
+
+@pytest.mark.parametrize("V,dtype,fused,ids,durs,sigma,lam,clamp", [
+    (16, torch.float32, True, [14, 13], [2, 3], 0.1, 0.0, -1.0),
+    (50, torch.float32, True, [46, 47, 48], [2, 4, 8], 0.05, 0.3, 0.2),
+    (1024, torch.float32, True, [1022, 1021, 1020], [2, 4, 8], 0.05, 0.0, -1.0),
+    (300, torch.float16, True, [1, 2], [3, 6], 0.0, 0.0, -1.0),
+    (64, torch.float32, False, [62], [5], 0.2, 0.0, -1.0),
+    (2048, torch.float16, False, [2046, 2045], [2, 4], 0.0, 0.1, -1.0),
+    (33, torch.float32, True, [0, 5, 9, 31], [1, 16, 7, 2], -0.1, 0.0, 0.05),
+])
+def test_multiblank_against_oracle(rl, V, dtype, fused, ids, durs, sigma, lam, clamp):
+    # samples shorter than some durations, U = 0, T = 1 and ordinary ones in one batch
+    blank = 0 if 0 not in ids and V == 300 else -1
+    w = _mb([40, 12, 3, 1, 25], [9, 4, 2, 3, 0], V, ids, durs, sigma, dtype=dtype, std=2.0 if fused else 1.5,
+            blank=blank, clamp=clamp, fused=fused, prenormalise=not fused, reduction="mean", seed=V + len(ids))
+    loss, red, grad, flags = run_mb(rl, w, fastemit=lam)
+    assert flags == 0
+    check_mb(w, loss, grad, "mean", fastemit=lam)
+    assert abs(red.item() - loss.double().mean().item()) <= 1e-6 * max(1.0, abs(red.item()))
+
+
+@pytest.mark.parametrize("U,durs", [(63, [2, 8]), (64, [2, 8]), (127, [3]), (128, [3]), (255, [2, 16]),
+                                    (256, [2, 14]), (511, [4]), (512, [6]), (700, [2, 6]), (1023, [2, 6])])
+def test_multiblank_lattice_widths(rl, U, durs):
+    # U+1 across every column width of the sweep (64, 128, 256, 512, 1024 columns) and ring depths up to the
+    # 64 KiB limit: (longest duration + 1) * (columns * 8 + 4) bytes
+    ids = [7, 6][:len(durs)]
+    w = _mb([3, 30], [U, min(U, 20)], 9, ids, durs, 0.05, std=1.0, blank=0, reduction="none", seed=U)
+    loss, red, grad, flags = run_mb(rl, w)
+    assert flags == 0
+    check_mb(w, loss, grad, "none")
+
+
+def test_multiblank_without_big_blanks(rl):
+    """No big blank and sigma = 0: the plain loss and gradient; sigma alone shifts each loss by sigma (T+U)."""
+    w = _mb([30, 17, 8], [7, 5, 0], 40, [], [], 0.0, std=2.0, blank=-1, reduction="none", seed=3)
+    loss, _, grad, flags = run_mb(rl, w)
+    assert flags == 0
+    check_mb(w, loss, grad, "none")
+    tg = torch.from_numpy(w.targets).to("cuda")
+    ploss, _, pgrad, _ = rl.rnnt_loss_fused(w.logits, tg, w.logit_lengths, w.target_lengths, blank=-1,
+                                            reduction="none")
+    torch.cuda.synchronize()
+    assert torch.allclose(loss, ploss, rtol=2e-6, atol=0)
+    assert (grad - pgrad).abs().max().item() <= 2e-6
+    w.sigma = 0.4
+    sloss, _, sgrad, _ = run_mb(rl, w)
+    shift = torch.tensor([0.4 * float(T + U) for T, U in zip(w.logit_lengths, w.target_lengths)],
+                         dtype=torch.float32, device="cuda")
+    assert torch.allclose(sloss, loss + shift, rtol=2e-6, atol=0)
+    assert (sgrad - grad).abs().max().item() <= 2e-6
+
+
+@pytest.mark.parametrize("reduction", ["none", "mean", "sum"])
+def test_multiblank_autograd(rl, reduction):
+    w = _mb([26, 19, 11], [6, 8, 3], 48, [45, 46], [2, 4], 0.1, std=2.0, blank=-1, reduction=reduction, seed=21)
+    x = w.logits.clone().requires_grad_(True)
+    tg = torch.from_numpy(w.targets).cuda()
+    out = rl.rnnt_loss_multiblank(x, tg, torch.from_numpy(w.logit_lengths).cuda(),
+                                  torch.from_numpy(w.target_lengths).cuda(), w.big_blank_durations, w.big_blank_ids,
+                                  blank=-1, sigma=w.sigma, reduction=reduction)
+    if reduction == "none":
+        up = torch.tensor([0.5, 2.0, -1.0], device="cuda")
+        (out * up).sum().backward()
+        fac = np.repeat(up.cpu().numpy(), [w.rows(i).stop - w.rows(i).start for i in range(3)])[:, None]
+    else:
+        (out * 3.5).backward()
+        fac = 3.5 / w.B if reduction == "mean" else 3.5
+    _, red, gref, _ = oracle.multiblank_batch(x.detach().cpu().numpy(), w.targets, w.logit_lengths,
+                                              w.target_lengths, w.big_blank_ids, w.big_blank_durations, blank=-1,
+                                              sigma=w.sigma, reduction="none")
+    err = np.abs(x.grad.double().cpu().numpy() - gref * fac).max()
+    assert err <= 1e-5 * 3.5
+    if reduction != "none":
+        expect = red.sum() / (w.B if reduction == "mean" else 1)
+        assert abs(out.item() - expect) <= 1e-5 * abs(expect)
+
+
+def test_multiblank_bad_targets_are_flagged(rl):
+    w = _mb([8, 6], [3, 2], 12, [10, 9], [2, 3], 0.0, std=1.0, blank=-1, reduction="none", seed=8)
+    tg = w.targets.copy()
+    tg[0, 1] = 10         # a big blank's class
+    w.targets = tg
+    loss, red, grad, flags = run_mb(rl, w)
+    assert flags & 2
+    assert math.isfinite(loss[0].item()) and math.isfinite(loss[1].item())
+    # the other sample is unaffected (the oracle refuses the flagged one)
+    T, U = int(w.logit_lengths[1]), int(w.target_lengths[1])
+    r = oracle.multiblank_sample(w.logits[w.rows(1)].cpu().numpy(), T, U, w.targets[1], w.V - 1, w.big_blank_ids,
+                                 w.big_blank_durations, w.sigma)
+    assert abs(loss[1].item() - r.loss) <= 1e-5 * max(1.0, abs(r.loss))
+    assert np.abs(grad[w.rows(1)].double().cpu().numpy() - r.grad).max() <= 1e-5
+
+
+def test_multiblank_score_only_and_deterministic(rl):
+    w = _mb([50, 31], [12, 7], 200, [198, 197], [2, 4], 0.05, std=2.0, blank=-1, reduction="sum", seed=4)
+    a = run_mb(rl, w)
+    b = run_mb(rl, w)
+    c = run_mb(rl, w, compute_grad=False)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[2], b[2]) and torch.equal(a[0], c[0])
+    assert c[2] is None
+
+
+def test_multiblank_workload_full_size(rl):
+    """The multi-blank workload (bpe shapes, big blanks of 2, 4 and 8 frames, sigma 0.05): every loss, and
+    every gradient row of the smallest and the largest sample; fused rows sum to zero."""
+    w = workloads.make("multiblank", device="cuda")
+    loss, red, grad, flags = run_mb(rl, w)
+    assert flags == 0
+    area = w.logit_lengths.astype(np.int64) * (w.target_lengths + 1)
+    check_mb(w, loss, grad, w.reduction, grad_samples=[int(np.argmin(area)), int(np.argmax(area))])
+    assert grad.double().sum(dim=1).abs().max().item() < 1e-6

@@ -13,9 +13,15 @@ precision / skewed long-form):
     skewed   64   lognormal(ln 300, 0.6)    round(T/5*U(0.6,1.0))     2048     fp16   log_softmax(N(0,1.5^2)) -1 off no sum
                   clipped to [50, 1600]
 
+plus one multi-blank workload, the bpe shapes with three big blanks (classes
+1022, 1021, 1020 of durations 2, 4, 8 frames) beside the standard blank 1023
+and sigma 0.05 (the logit under-normalisation):
+
+    multiblank 32 U{200..400}               U{40..100}                1024     fp32   N(0,2^2)    -1     off    yes    mean
+
 Draw order (numpy ``default_rng(seed)``): T[B], then U[B], then the padded
-targets (B, max U) uniform over the non-blank ids (padding is 0 and never
-read), all on the host.  Logits are drawn per sample with torch's Philox
+targets (B, max U) uniform over the non-blank ids (the big blanks excluded;
+padding is 0 and never read), all on the host.  Logits are drawn per sample with torch's Philox
 generator on the requested device, seeded with ``seed * 1000003 + i``, as
 fp32 and rounded to fp16 (round-to-nearest-even) where the workload is fp16.
 The skewed workload's inputs are log-probabilities: each sample's fp32 draw
@@ -30,8 +36,10 @@ from typing import List, Optional
 import numpy as np
 import torch
 
-NAMES = ("tiny", "char", "bpe", "half", "skewed")
-DEFAULT_SEEDS = {"tiny": 1, "char": 2, "bpe": 3, "half": 4, "skewed": 5}
+NAMES = ("tiny", "char", "bpe", "half", "skewed", "multiblank")
+DEFAULT_SEEDS = {"tiny": 1, "char": 2, "bpe": 3, "half": 4, "skewed": 5, "multiblank": 6}
+# big-blank classes, durations and sigma of the multi-blank workload
+MULTIBLANK = {"big_blank_ids": (1022, 1021, 1020), "big_blank_durations": (2, 4, 8), "sigma": 0.05}
 
 
 @dataclasses.dataclass
@@ -47,6 +55,9 @@ class Workload:
     targets: np.ndarray        # int32 (B, S), zero padded
     logits: torch.Tensor       # (N, V) fp32/fp16, packed t-major per sample
     offsets: np.ndarray        # int64 (B+1,), row offset of each sample
+    big_blank_ids: tuple = ()  # multi-blank workloads only
+    big_blank_durations: tuple = ()
+    sigma: float = 0.0
 
     @property
     def B(self) -> int:
@@ -70,9 +81,9 @@ def _offsets(T: np.ndarray, U: np.ndarray) -> np.ndarray:
     return off
 
 
-def _draw_targets(rng: np.random.Generator, U: np.ndarray, V: int, blank_norm: int) -> np.ndarray:
+def _draw_targets(rng: np.random.Generator, U: np.ndarray, V: int, blank_norm: int, exclude=()) -> np.ndarray:
     S = max(1, int(U.max()) if len(U) else 1)
-    ids = np.array([k for k in range(V) if k != blank_norm], np.int64)
+    ids = np.array([k for k in range(V) if k != blank_norm and k not in exclude], np.int64)
     tg = np.zeros((len(U), S), np.int32)
     for i, u in enumerate(U):
         if u > 0:
@@ -102,15 +113,19 @@ def _draw_logits(T, U, V, std, dtype, seed, device, prenormalise=False) -> torch
 def make_custom(T: List[int], U: List[int], V: int, *, dtype=torch.float32, std: float = 1.0,
                 blank: int = -1, clamp: float = -1.0, fused: bool = True, reduction: str = "mean",
                 seed: int = 0, device="cpu", prenormalise: bool = False, name: str = "custom",
-                targets: Optional[np.ndarray] = None) -> Workload:
-    """A workload with explicit per-sample lengths (edge cases, small parity cases)."""
+                targets: Optional[np.ndarray] = None, big_blank_ids=(), big_blank_durations=(),
+                sigma: float = 0.0) -> Workload:
+    """A workload with explicit per-sample lengths (edge cases, small parity cases); targets avoid the blank
+    and any big blank."""
     T = np.asarray(T, np.int32)
     U = np.asarray(U, np.int32)
     bn = blank + V if blank < 0 else blank
     rng = np.random.default_rng(seed)
-    tg = _draw_targets(rng, U, V, bn) if targets is None else np.asarray(targets, np.int32)
+    tg = (_draw_targets(rng, U, V, bn, tuple(big_blank_ids)) if targets is None
+          else np.asarray(targets, np.int32))
     logits = _draw_logits(T, U, V, std, dtype, seed, device, prenormalise)
-    return Workload(name, V, blank, clamp, fused, reduction, T, U, tg, logits, _offsets(T, U))
+    return Workload(name, V, blank, clamp, fused, reduction, T, U, tg, logits, _offsets(T, U),
+                    tuple(big_blank_ids), tuple(big_blank_durations), float(sigma))
 
 
 def lengths(name: str, seed: Optional[int] = None):
@@ -125,7 +140,7 @@ def lengths(name: str, seed: Optional[int] = None):
         T = rng.integers(50, 101, size=8).astype(np.int32)
         U = rng.integers(10, 31, size=8).astype(np.int32)
         V, blank = 29, 0
-    elif name == "bpe":
+    elif name in ("bpe", "multiblank"):
         T = rng.integers(200, 401, size=32).astype(np.int32)
         U = rng.integers(40, 101, size=32).astype(np.int32)
         V, blank = 1024, -1
@@ -140,7 +155,7 @@ def lengths(name: str, seed: Optional[int] = None):
     else:
         raise KeyError(name)
     bn = blank + V if blank < 0 else blank
-    tg = _draw_targets(rng, U, V, bn)
+    tg = _draw_targets(rng, U, V, bn, MULTIBLANK["big_blank_ids"] if name == "multiblank" else ())
     return T, U, tg, V, blank
 
 
@@ -151,6 +166,7 @@ _PARAMS = {
     "bpe": (torch.float32, 2.0, -1.0, True, "mean", False),
     "half": (torch.float16, 2.0, 1.0, True, "mean", False),
     "skewed": (torch.float16, 1.5, -1.0, False, "sum", True),
+    "multiblank": (torch.float32, 2.0, -1.0, True, "mean", False),
 }
 
 
@@ -160,7 +176,12 @@ def make(name: str, seed: Optional[int] = None, device="cpu") -> Workload:
     T, U, tg, V, blank = lengths(name, seed)
     dtype, std, clamp, fused, reduction, pre = _PARAMS[name]
     logits = _draw_logits(T, U, V, std, dtype, seed, device, pre)
-    return Workload(name, V, blank, clamp, fused, reduction, T, U, tg, logits, _offsets(T, U))
+    w = Workload(name, V, blank, clamp, fused, reduction, T, U, tg, logits, _offsets(T, U))
+    if name == "multiblank":
+        w.big_blank_ids = MULTIBLANK["big_blank_ids"]
+        w.big_blank_durations = MULTIBLANK["big_blank_durations"]
+        w.sigma = MULTIBLANK["sigma"]
+    return w
 
 
 def describe(name: str, seed: Optional[int] = None) -> dict:
