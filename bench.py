@@ -5,6 +5,8 @@ One step is one ``rnnt_loss_fused`` call over one seeded synthetic batch: the
 host schedule upload, the row-statistics pass, the alpha/beta recursions, the
 gradient pass and the loss reduction -- every step of the hot path.  Inputs,
 outputs and workspace are resident in HBM before the timed region starts.
+``--workload multiblank`` times ``rnnt_multiblank_loss`` (big blanks of 2, 4
+and 8 frames on the bpe shapes) the same way.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload bpe]
 
@@ -36,6 +38,8 @@ METRIC = "packed logits elements/s (fwd+bwd) & effective HBM GB/s vs peak, 1 MI3
 PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E, AMD published peak
 KERNEL_SOURCE = os.path.join(ROOT, "rnn_transducer_loss_amd", "csrc", "rnnt_kernels.hip")
 KERNEL_SYMBOLS = {"rowstats": "k_rowstats", "alpha_beta": "k_alpha_beta", "grad": "k_grad", "reduce": "k_reduce"}
+# the multi-blank path's own passes (rnnt_multiblank_loss)
+MB_KERNEL_SYMBOLS = {"rowstats": "k_mb_rows", "alpha_beta": "k_mb_sweep", "grad": "k_mb_grad", "reduce": "k_reduce"}
 
 
 def esize(dtype) -> int:
@@ -108,8 +112,13 @@ def cpu_baseline(w, budget_s: float = 12.0, min_wall_s: float = 1.5, fastemit_la
     host = {}
 
     def one(i):
-        r = oracle.sample(host[i], int(w.logit_lengths[i]), int(w.target_lengths[i]), w.targets[i], b, w.fused,
-                          w.clamp, want_grad=True, fastemit_lambda=fastemit_lambda)
+        T, U = int(w.logit_lengths[i]), int(w.target_lengths[i])
+        if w.big_blank_durations:
+            r = oracle.multiblank_sample(host[i], T, U, w.targets[i], b, w.big_blank_ids, w.big_blank_durations,
+                                         w.sigma, w.fused, w.clamp, fastemit_lambda, want_grad=True)
+        else:
+            r = oracle.sample(host[i], T, U, w.targets[i], b, w.fused, w.clamp, want_grad=True,
+                              fastemit_lambda=fastemit_lambda)
         return int(rows[i]) * w.V, r.loss
 
     done_elems, done_samples, passes = 0, 0, 0
@@ -165,7 +174,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="bpe", choices=["tiny", "char", "bpe", "half", "skewed"])
+    ap.add_argument("--workload", default="bpe", choices=["tiny", "char", "bpe", "half", "skewed", "multiblank"])
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--fastemit-lambda", type=float, default=0.0,
                     help="FastEmit weight on the label-emission gradient (0: the plain loss)")
@@ -198,12 +207,25 @@ def main():
     loss = torch.empty(w.B, dtype=torch.float32, device=dev)
     red = torch.empty(1, dtype=torch.float32, device=dev)
     grad = torch.empty_like(w.logits)
-    ws = torch.empty(rl.workspace_bytes(w.logits, T, U), dtype=torch.uint8, device=dev)
+    multiblank = bool(w.big_blank_durations)
+    if multiblank:
+        nbytes = rl._lib.workspace_size_multiblank(w.B, w.V, w.N, rl._lib.RNNT_F32 if esize(w.dtype) == 4
+                                                   else rl._lib.RNNT_F16, T, U, w.big_blank_durations)
+    else:
+        nbytes = rl.workspace_bytes(w.logits, T, U)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    symbols = MB_KERNEL_SYMBOLS if multiblank else KERNEL_SYMBOLS
 
     def step():
-        rl.rnnt_loss_fused(w.logits, tg, T, U, blank=w.blank, clamp=w.clamp, reduction=w.reduction,
-                           fused_log_softmax=w.fused, grad=grad, workspace=ws, loss=loss, loss_reduced=red,
-                           fastemit_lambda=args.fastemit_lambda)
+        if multiblank:
+            rl.rnnt_multiblank_fused(w.logits, tg, T, U, w.big_blank_ids, w.big_blank_durations, blank=w.blank,
+                                     sigma=w.sigma, clamp=w.clamp, reduction=w.reduction,
+                                     fused_log_softmax=w.fused, fastemit_lambda=args.fastemit_lambda, grad=grad,
+                                     workspace=ws, loss=loss, loss_reduced=red)
+        else:
+            rl.rnnt_loss_fused(w.logits, tg, T, U, blank=w.blank, clamp=w.clamp, reduction=w.reduction,
+                               fused_log_softmax=w.fused, grad=grad, workspace=ws, loss=loss, loss_reduced=red,
+                               fastemit_lambda=args.fastemit_lambda)
 
     print(f"bench: N={w.N} V={w.V} B={w.B}; warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -243,8 +265,8 @@ def main():
     roofline = None
     if dom_bytes is not None:
         ach = dom_bytes / (per_kernel[dominant] * 1e-3) / 1e9
-        traffic = committed_traffic(KERNEL_SYMBOLS[dominant], w.name)
-        roofline = {"bound": "hbm", "kernel": KERNEL_SYMBOLS[dominant], "achieved": round(ach, 1),
+        traffic = committed_traffic(symbols[dominant], w.name)
+        roofline = {"bound": "hbm", "kernel": symbols[dominant], "achieved": round(ach, 1),
                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4),
                     "traffic": traffic, "algorithmic_bytes_per_step": dom_bytes,
                     "kernel_ms_per_step": round(per_kernel[dominant], 5),
@@ -272,6 +294,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "V": w.V, "rows": w.N, "elements": w.N * w.V,
                    "io_dtype": "fp16" if esize(w.dtype) == 2 else "fp32", "fused_log_softmax": w.fused,
                    "reduction": w.reduction, "clamp": w.clamp, "fastemit_lambda": args.fastemit_lambda,
+                   **({"big_blank_durations": list(w.big_blank_durations), "sigma": w.sigma} if multiblank else {}),
                    "T_max": int(T.max()), "U_max": int(U.max()), "recursion_dtype": "f64"},
         "effective_GBps": round(eff, 1),
         "effective_frac_of_peak": round(eff / PEAK_HBM_GBPS, 4),

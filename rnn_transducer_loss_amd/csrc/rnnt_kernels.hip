@@ -1570,22 +1570,26 @@ __global__ __launch_bounds__(256) void k_mb_rows(const T *__restrict__ logits, i
 
 // One wave per (sample, direction): blockIdx 2i runs alpha of sample i,
 // 2i+1 beta.  Lane l holds columns l + 64j, j < J.  `cur` is the diagonal
-// just finished, scaled by 2^-E; the ring keeps the last R diagonals (and
-// their exponents) for the big blanks, whose sources lie d_i diagonals away.
-// Every weight is masked where its edge does not exist, so unwritten slots
-// are never used.  Stored: every real diagonal of alpha or beta (scaled) and
-// its exponent; log2 P(y|x) and, from beta, the loss.
-template <int J>
-__global__ __launch_bounds__(64) void k_mb_sweep(const SampleDesc *__restrict__ desc, int B, MbParams mp,
-                                                 const float *__restrict__ lp, int64_t n_slots,
-                                                 double *__restrict__ alpha, double *__restrict__ beta,
-                                                 int *__restrict__ ealpha, int *__restrict__ ebeta,
-                                                 double *__restrict__ log2z, float *__restrict__ loss) {
+// just finished, scaled by 2^-E; the LDS ring keeps the last R diagonals
+// (and their exponents) for the big blanks, whose sources lie d_i diagonals
+// away.  The edges' log-probabilities do not depend on the recursion, so
+// those of the next P diagonals are in flight while a diagonal is computed
+// (a register ring, one slot per step mod P; every slot holds all
+// kMaxBigBlanks big-blank planes, unused ones reading plane 0, so the loads
+// and their waits are the same every step).  Every weight is masked where its
+// edge does not exist, so unwritten slots are never used.  Stored: every real
+// diagonal of alpha or beta (scaled) and its exponent; log2 P(y|x) and, from
+// beta, the loss.
+template <int J, int P, bool bw>
+__device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const MbParams &mp,
+                                             const float *__restrict__ lp, int64_t n_slots,
+                                             double *__restrict__ alpha, double *__restrict__ beta,
+                                             int *__restrict__ ealpha, int *__restrict__ ebeta,
+                                             double *__restrict__ log2z, float *__restrict__ loss) {
     extern __shared__ double mb_ring[];  // R * J * 64 values, then R exponents
     constexpr int U1p = 64 * J;
+    constexpr int NW = 2 + kMaxBigBlanks;  // blank, label, big blanks
     const int lane = threadIdx.x;
-    const SampleDesc d = desc[blockIdx.x >> 1];
-    const bool bw = (blockIdx.x & 1) != 0;
     const int T = d.T, U = d.U, U1 = U + 1, nd = T + U, R = mp.R;
     int *ering = reinterpret_cast<int *>(mb_ring + (size_t)R * J * 64);
     for (int q = lane; q < R * J * 64; q += 64) mb_ring[q] = 0.0;
@@ -1593,19 +1597,48 @@ __global__ __launch_bounds__(64) void k_mb_sweep(const SampleDesc *__restrict__ 
     const float *lpb = lp + d.slot_off;
     const float *lpy = lp + n_slots + d.slot_off;
     const float *lpg = lp + 2 * n_slots + d.slot_off;
+    int64_t pl[kMaxBigBlanks];  // each big blank's plane; an unused slot reads plane 0 (masked)
+#pragma unroll
+    for (int i = 0; i < kMaxBigBlanks; ++i) pl[i] = (int64_t)(i < mp.nb ? i : 0) * n_slots;
     double *tab = (bw ? beta : alpha) + d.ab_off;
     int *etab = (bw ? ebeta : ealpha) + d.diag_off + d.index;
+
+    // The raw log-probabilities step `step` uses (steps past the end load the
+    // last step's again; their values are never used).  Forward, diagonal n
+    // pulls from n-1 (blank at column u, label at u-1) and n-d_i; backward,
+    // every edge leaves the node itself.
+    auto load_w = [&](int step, float (&w)[J][NW]) {
+        const int n = bw ? nd - min(step, nd) : min(step, nd);
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int uc = min(lane + 64 * j, U);
+            if (!bw) {
+                const int64_t sp = (int64_t)(n - 1) * U1;
+                w[j][0] = lpb[sp + uc];
+                w[j][1] = lpy[sp + max(uc - 1, 0)];
+#pragma unroll
+                for (int i = 0; i < kMaxBigBlanks; ++i)
+                    w[j][2 + i] = lpg[pl[i] + (int64_t)max(n - mp.dur[i], 0) * U1 + uc];
+            } else {
+                const int64_t sc = (int64_t)n * U1 + uc;
+                w[j][0] = lpb[sc];
+                w[j][1] = lpy[sc];
+#pragma unroll
+                for (int i = 0; i < kMaxBigBlanks; ++i) w[j][2 + i] = lpg[pl[i] + sc];
+            }
+        }
+    };
 
     // start: alpha(0,0) = 1 on diagonal 0; beta of the virtual end (T,U) = 1 on diagonal T+U
     double cur[J];
     int E = 0;
+    int slot = (bw ? nd : 0) % R;  // ring slot of the diagonal last written (n mod R, kept incrementally)
     {
-        const int n0 = bw ? nd : 0;
         const int uc = bw ? U : 0;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             cur[j] = (lane + 64 * j == uc) ? 1.0 : 0.0;
-            mb_ring[((n0 % R) * J + j) * 64 + lane] = cur[j];
+            mb_ring[(slot * J + j) * 64 + lane] = cur[j];
         }
         if (!bw) {
 #pragma unroll
@@ -1614,8 +1647,24 @@ __global__ __launch_bounds__(64) void k_mb_sweep(const SampleDesc *__restrict__ 
         }
     }
 
-    for (int step = 1; step <= nd; ++step) {
+    // One step: diagonal n from the finished one (`cur`), the ring and the
+    // weights w.  Branch-free: an edge that does not exist gets its weight
+    // replaced by -inf (probability 0) before use, and every ring read is
+    // issued, so the LDS reads of a step go out together.
+    auto step_once = [&](int step, const float (&w)[J][NW]) {
         const int n = bw ? nd - step : step;
+        slot = bw ? (slot == 0 ? R - 1 : slot - 1) : (slot + 1 == R ? 0 : slot + 1);
+        // big blanks: source diagonal, its ring slot and exponent relative to E
+        int sl[kMaxBigBlanks], shg[kMaxBigBlanks];
+        bool okd[kMaxBigBlanks];
+#pragma unroll
+        for (int i = 0; i < kMaxBigBlanks; ++i) {
+            const int dd = mp.dur[i];  // 1 <= dd < R
+            okd[i] = (i < mp.nb) && (bw ? n + dd <= nd : n - dd >= 0);
+            const int q = bw ? slot + dd : slot - dd;
+            sl[i] = bw ? (q >= R ? q - R : q) : (q < 0 ? q + R : q);
+            shg[i] = (ering[sl[i]] - E) * (int)okd[i];  // arithmetic, so the read is never skipped
+        }
         // the neighbouring column of the finished diagonal: u-1 (forward) or u+1 (backward)
         double rot[J], side[J];
 #pragma unroll
@@ -1625,55 +1674,30 @@ __global__ __launch_bounds__(64) void k_mb_sweep(const SampleDesc *__restrict__ 
             if (bw) side[j] = (lane == 63) ? (j + 1 < J ? rot[j + 1] : 0.0) : rot[j];
             else side[j] = (lane == 0) ? (j > 0 ? rot[j - 1] : 0.0) : rot[j];
         }
-        // big blanks: source diagonal, whether it exists, its exponent relative to E
-        int ns[kMaxBigBlanks], shg[kMaxBigBlanks];
-        bool okd[kMaxBigBlanks];
-        int64_t pl[kMaxBigBlanks];  // the big blank's plane; an unused slot reads plane 0, masked
-#pragma unroll
-        for (int i = 0; i < kMaxBigBlanks; ++i) {
-            pl[i] = (int64_t)(i < mp.nb ? i : 0) * n_slots;
-            ns[i] = bw ? n + mp.dur[i] : n - mp.dur[i];
-            okd[i] = (i < mp.nb) && (bw ? ns[i] <= nd : ns[i] >= 0);
-            if (!okd[i]) ns[i] = bw ? n : 0;  // an in-range stand-in; its weight is masked
-            shg[i] = okd[i] ? ering[ns[i] % R] - E : 0;
-        }
         double nx[J];
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             const int u = lane + 64 * j;
             const int t = n - u;
-            const int uc = min(u, U);
-            double acc;
-            bool cell;
+            bool cell, okb, oky;
             if (!bw) {
                 cell = (u <= U) && ((t >= 0 && t <= T - 1) || (t == T && u == U));
-                const int64_t sp = (int64_t)(n - 1) * U1;
-                const float b = lpb[sp + uc];
-                const float y = lpy[sp + max(uc - 1, 0)];
-                const bool okb = (t >= 1) && (t <= T);            // from (t-1,u)
-                const bool oky = (u >= 1) && (t >= 0) && (t <= T - 1);  // from (t,u-1)
-                acc = (okb ? prob_d(b) : 0.0) * cur[j] + (oky ? prob_d(y) : 0.0) * side[j];
-#pragma unroll
-                for (int i = 0; i < kMaxBigBlanks; ++i) {
-                    const int ts = t - mp.dur[i];                   // from (t-d_i,u)
-                    const bool ok = okd[i] && ts >= 0 && ts <= T - 1;
-                    const float g = lpg[pl[i] + (int64_t)ns[i] * U1 + uc];
-                    const double src = mb_ring[((ns[i] % R) * J + j) * 64 + lane];
-                    acc += ok ? prob_d(g) * __builtin_amdgcn_ldexp(src, shg[i]) : 0.0;
-                }
+                okb = (t >= 1) && (t <= T);                  // from (t-1,u)
+                oky = (u >= 1) && (t >= 0) && (t <= T - 1);  // from (t,u-1)
             } else {
                 cell = (u <= U) && (t >= 0) && (t <= T - 1);
-                const int64_t sc = (int64_t)n * U1 + uc;
-                const float b = lpb[sc];
-                const float y = lpy[sc];
-                acc = (cell ? prob_d(b) : 0.0) * cur[j] + ((cell && u < U) ? prob_d(y) : 0.0) * side[j];
+                okb = cell;                                  // to (t+1,u)
+                oky = cell && (u < U);                       // to (t,u+1)
+            }
+            double acc = prob_d(okb ? w[j][0] : kNegInf) * cur[j];
+            acc = fma(prob_d(oky ? w[j][1] : kNegInf), side[j], acc);
 #pragma unroll
-                for (int i = 0; i < kMaxBigBlanks; ++i) {
-                    const bool ok = okd[i] && cell;                 // to (t+d_i,u); zero where that is no node
-                    const float g = lpg[pl[i] + sc];
-                    const double src = mb_ring[((ns[i] % R) * J + j) * 64 + lane];
-                    acc += ok ? prob_d(g) * __builtin_amdgcn_ldexp(src, shg[i]) : 0.0;
-                }
+            for (int i = 0; i < kMaxBigBlanks; ++i) {
+                // forward from (t-d_i,u); backward to (t+d_i,u), zero where that is no node
+                const int ts = t - mp.dur[i];
+                const bool ok = okd[i] && (bw ? cell : (ts >= 0 && ts <= T - 1));
+                const double src = mb_ring[(sl[i] * J + j) * 64 + lane];
+                acc = fma(prob_d(ok ? w[j][2 + i] : kNegInf), __builtin_amdgcn_ldexp(src, shg[i]), acc);
             }
             nx[j] = cell ? acc : 0.0;
         }
@@ -1684,7 +1708,6 @@ __global__ __launch_bounds__(64) void k_mb_sweep(const SampleDesc *__restrict__ 
         eb = wave_max_i(eb);
         const int sh = eb == 0 ? 0 : eb - 1023;
         E += sh;
-        const int slot = n % R;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             cur[j] = __builtin_amdgcn_ldexp(nx[j], -sh);
@@ -1695,6 +1718,19 @@ __global__ __launch_bounds__(64) void k_mb_sweep(const SampleDesc *__restrict__ 
 #pragma unroll
             for (int j = 0; j < J; ++j) tab[(int64_t)n * U1p + j * 64 + lane] = cur[j];
             if (lane == 0) etab[n] = E;
+        }
+    };
+
+    float w[P][J][NW];
+#pragma unroll
+    for (int q = 0; q < P; ++q) load_w(1 + q, w[q]);
+    for (int s0 = 1; s0 <= nd; s0 += P) {
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            if (s0 + q <= nd) {
+                step_once(s0 + q, w[q]);
+                load_w(s0 + q + P, w[q]);
+            }
         }
     }
 
@@ -1722,20 +1758,35 @@ __global__ __launch_bounds__(64) void k_mb_sweep(const SampleDesc *__restrict__ 
 // times the reduction scale.  P(k) is the softmax without sigma (sigma is a
 // constant of every log-probability, so it leaves the log_softmax Jacobian
 // as it is); without fused log_softmax only the flows remain.
-template <typename T>
-__global__ __launch_bounds__(256) void k_mb_grad(const T *__restrict__ logits, T *__restrict__ grad, int64_t N,
-                                                 int V, int blank, int fused, MbParams mp, int U1p,
-                                                 const SampleDesc *__restrict__ desc, int B,
-                                                 const int32_t *__restrict__ targets, int S,
-                                                 const float *__restrict__ den, const float *__restrict__ lp,
-                                                 int64_t n_slots, const double *__restrict__ alpha,
-                                                 const double *__restrict__ beta, const int *__restrict__ ealpha,
-                                                 const int *__restrict__ ebeta, const double *__restrict__ log2z,
-                                                 float clamp, float scale, float fastemit, int64_t row_base) {
-    const int lane = threadIdx.x & 63;
-    const int64_t r = row_base + (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (r >= N) return;
-    const SampleDesc d = mb_sample_of_row(desc, B, r);
+template <int J, int P>
+__global__ __launch_bounds__(64) void k_mb_sweep(const SampleDesc *__restrict__ desc, int B, MbParams mp,
+                                                 const float *__restrict__ lp, int64_t n_slots,
+                                                 double *__restrict__ alpha, double *__restrict__ beta,
+                                                 int *__restrict__ ealpha, int *__restrict__ ebeta,
+                                                 double *__restrict__ log2z, float *__restrict__ loss) {
+    const SampleDesc d = desc[blockIdx.x >> 1];
+    if (blockIdx.x & 1) mb_sweep_dir<J, P, true>(d, B, mp, lp, n_slots, alpha, beta, ealpha, ebeta, log2z, loss);
+    else mb_sweep_dir<J, P, false>(d, B, mp, lp, n_slots, alpha, beta, ealpha, ebeta, log2z, loss);
+}
+
+// The gradient terms of packed row r: the softmax shift (occupancy with the
+// FastEmit term, log2 domain, minus the row's normaliser) and the scaled
+// flows of the edges leaving the node, with the label class.
+struct MbRowTerms {
+    float shift2;
+    float fb, fy;
+    float fg[kMaxBigBlanks];
+    int y;
+};
+
+__device__ __forceinline__ MbRowTerms mb_row_terms(const SampleDesc &d, int64_t r, int V, int fused,
+                                                   const MbParams &mp, int U1p, const int32_t *__restrict__ targets,
+                                                   int S, const float *__restrict__ den,
+                                                   const float *__restrict__ lp, int64_t n_slots,
+                                                   const double *__restrict__ alpha,
+                                                   const double *__restrict__ beta, const int *__restrict__ ealpha,
+                                                   const int *__restrict__ ebeta, const double *__restrict__ log2z,
+                                                   float scale, float fastemit) {
     const int U1 = d.U + 1;
     const int64_t lr = r - d.row_off;
     const int t = (int)(lr / U1);
@@ -1766,30 +1817,170 @@ __global__ __launch_bounds__(256) void k_mb_grad(const T *__restrict__ logits, T
     }
     if (fastemit > 0.f && ly != kNegInfD && lo != kNegInfD)
         lo += (double)log2f(1.f + fastemit * exp2_fast((float)(ly - lo)));
-    int y = -1;
+    MbRowTerms rt;
+    rt.y = -1;
     if (u < d.U) {
         const int yy = targets[(int64_t)d.index * S + u];
-        y = (yy >= 0 && yy < V) ? yy : -1;
+        rt.y = (yy >= 0 && yy < V) ? yy : -1;
     }
-    const float fb = exp2_fast((float)lb) * scale;
-    const float fy = exp2_fast((float)ly) * scale * (1.f + fastemit);
-    float fg[kMaxBigBlanks];
+    rt.fb = exp2_fast((float)lb) * scale;
+    rt.fy = exp2_fast((float)ly) * scale * (1.f + fastemit);
 #pragma unroll
-    for (int i = 0; i < kMaxBigBlanks; ++i) fg[i] = exp2_fast((float)lg[i]) * scale;
+    for (int i = 0; i < kMaxBigBlanks; ++i) rt.fg[i] = exp2_fast((float)lg[i]) * scale;
     const float dn = den[r];
-    const float shift2 = (fused && dn != kNegInf) ? (float)(lo - (double)dn * kLog2eD) + log2_fast(scale) : kNegInf;
+    rt.shift2 = (fused && dn != kNegInf) ? (float)(lo - (double)dn * kLog2eD) + log2_fast(scale) : kNegInf;
+    return rt;
+}
+
+// The gradient for rows the vector form does not take (unaligned, or wider
+// than 16 vectors per lane): one wave per row, four per workgroup, scalar
+// elements.
+template <typename T>
+__global__ __launch_bounds__(256) void k_mb_grad(const T *__restrict__ logits, T *__restrict__ grad, int64_t N,
+                                                 int V, int blank, int fused, MbParams mp, int U1p,
+                                                 const SampleDesc *__restrict__ desc, int B,
+                                                 const int32_t *__restrict__ targets, int S,
+                                                 const float *__restrict__ den, const float *__restrict__ lp,
+                                                 int64_t n_slots, const double *__restrict__ alpha,
+                                                 const double *__restrict__ beta, const int *__restrict__ ealpha,
+                                                 const int *__restrict__ ebeta, const double *__restrict__ log2z,
+                                                 float clamp, float scale, float fastemit, int64_t row_base) {
+    const int lane = threadIdx.x & 63;
+    const int64_t r = row_base + (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= N) return;
+    const SampleDesc d = mb_sample_of_row(desc, B, r);
+    const MbRowTerms rt = mb_row_terms(d, r, V, fused, mp, U1p, targets, S, den, lp, n_slots, alpha, beta, ealpha,
+                                       ebeta, log2z, scale, fastemit);
     const bool do_clamp = clamp > 0.f;
     const float cl = clamp * scale;
     const T *x = logits + r * (int64_t)V;
     T *g = grad + r * (int64_t)V;
     for (int k = lane; k < V; k += 64) {
         float v = 0.f;
-        if (fused) v = exp2_fast(fmaf(Elem<T>::load1(x + k), kLog2e, shift2));
-        v -= (k == blank) ? fb : 0.f;
-        v -= (k == y) ? fy : 0.f;
+        if (fused) v = exp2_fast(fmaf(Elem<T>::load1(x + k), kLog2e, rt.shift2));
+        v -= (k == blank) ? rt.fb : 0.f;
+        v -= (k == rt.y) ? rt.fy : 0.f;
 #pragma unroll
-        for (int i = 0; i < kMaxBigBlanks; ++i) v -= (i < mp.nb && k == mp.ids[i]) ? fg[i] : 0.f;
+        for (int i = 0; i < kMaxBigBlanks; ++i) v -= (i < mp.nb && k == mp.ids[i]) ? rt.fg[i] : 0.f;
         Elem<T>::store1(g + k, clamp_to(v, cl, do_clamp));
+    }
+}
+
+// The row passes with the row held in 16-byte vectors, lane l holding
+// vectors l + 64i, i < NV (16-byte aligned rows of at most NV KiB), one row
+// per single-wave workgroup: the shape that streams fastest here.
+template <typename T, int NV>
+__global__ __launch_bounds__(64) void k_mb_rows_v(const T *__restrict__ logits, int64_t N, int V, int blank,
+                                                  int fused, MbParams mp, const SampleDesc *__restrict__ desc,
+                                                  int B, const int32_t *__restrict__ targets, int S,
+                                                  float *__restrict__ den, float *__restrict__ lp,
+                                                  int64_t n_slots, uint32_t *status, int64_t row_base) {
+    using Vec = typename Raw<T>::vec;
+    constexpr int VEC = Raw<T>::kVec;
+    const int lane = threadIdx.x;
+    const int64_t r = row_base + (int64_t)blockIdx.x;
+    if (r >= N) return;
+    const SampleDesc d = mb_sample_of_row(desc, B, r);
+    const int U1 = d.U + 1;
+    const int64_t lr = r - d.row_off;
+    const int t = (int)(lr / U1);
+    const int u = (int)(lr - (int64_t)t * U1);
+    const T *x = logits + r * (int64_t)V;
+    const int nvec = V / VEC;
+    float dn = 0.f;
+    if (fused) {
+        Vec xv[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            if (i * 64 + lane < nvec) xv[i] = load_raw<T, false>(x + (int64_t)(i * 64 + lane) * VEC);
+        float m = wave_max_f(row_max<T, NV, false>(xv, nvec));
+        const float nm = (m == kNegInf) ? 0.f : -m * kLog2e;
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            if (i * 64 + lane < nvec)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) sum += exp2_fast(fmaf(Raw<T>::get(xv[i], e), kLog2e, nm));
+        sum = wave_sum_f(sum);
+        dn = (m == kNegInf) ? kNegInf : m + log2_fast(sum) * kLn2;
+    }
+    if (lane == 0) den[r] = dn;
+    if (lane < 2 + mp.nb) {
+        int k = blank;
+        if (lane == 1) {
+            k = -1;
+            if (u < d.U) {
+                const int y = targets[(int64_t)d.index * S + u];
+                bool bad = y < 0 || y >= V || y == blank;
+#pragma unroll
+                for (int i = 0; i < kMaxBigBlanks; ++i) bad = bad || (i < mp.nb && y == mp.ids[i]);
+                if (bad) atomicOr(status, (uint32_t)RNNT_DEV_BAD_TARGET);
+                k = (y >= 0 && y < V) ? y : -1;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kMaxBigBlanks; ++i)
+            if (lane == 2 + i) k = mp.ids[i];
+        const float v = (k >= 0 && dn != kNegInf) ? Elem<T>::load1(x + k) - dn - mp.sigma : kNegInf;
+        lp[(int64_t)lane * n_slots + d.slot_off + (int64_t)(t + u) * U1 + u] = v;
+    }
+}
+
+// Subtracts f from element c of the row in the vector of lane
+// (c / VEC) % 64, number (c / VEC) / 64 == i (c < 0: nothing).
+template <int VEC>
+__device__ __forceinline__ void mb_sub_at(float (&gv)[VEC], int vi, int i, int c, float f) {
+    if (c >= 0 && ((c / VEC) >> 6) == i) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) gv[e] -= (vi * VEC + e == c) ? f : 0.f;
+    }
+}
+
+template <typename T, int NV>
+__global__ __launch_bounds__(64) void k_mb_grad_v(const T *__restrict__ logits, T *__restrict__ grad, int64_t N,
+                                                  int V, int blank, int fused, MbParams mp, int U1p,
+                                                  const SampleDesc *__restrict__ desc, int B,
+                                                  const int32_t *__restrict__ targets, int S,
+                                                  const float *__restrict__ den, const float *__restrict__ lp,
+                                                  int64_t n_slots, const double *__restrict__ alpha,
+                                                  const double *__restrict__ beta, const int *__restrict__ ealpha,
+                                                  const int *__restrict__ ebeta, const double *__restrict__ log2z,
+                                                  float clamp, float scale, float fastemit, int64_t row_base) {
+    using Vec = typename Raw<T>::vec;
+    constexpr int VEC = Raw<T>::kVec;
+    const int lane = threadIdx.x;
+    const int64_t r = row_base + (int64_t)blockIdx.x;
+    if (r >= N) return;
+    const SampleDesc d = mb_sample_of_row(desc, B, r);
+    const int nvec = V / VEC;
+    Vec xv[NV];
+    if (fused) {
+        const T *x = logits + r * (int64_t)V;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            if (i * 64 + lane < nvec) xv[i] = load_raw<T, true>(x + (int64_t)(i * 64 + lane) * VEC);
+    }
+    MbRowTerms rt = mb_row_terms(d, r, V, fused, mp, U1p, targets, S, den, lp, n_slots, alpha, beta, ealpha, ebeta,
+                                 log2z, scale, fastemit);
+    const bool do_clamp = clamp > 0.f;
+    const float cl = clamp * scale;
+    T *g = grad + r * (int64_t)V;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int vi = i * 64 + lane;
+        if (vi < nvec) {
+            float gv[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                gv[e] = fused ? exp2_fast(fmaf(Raw<T>::get(xv[i], e), kLog2e, rt.shift2)) : 0.f;
+            mb_sub_at<VEC>(gv, vi, i, blank, rt.fb);
+            mb_sub_at<VEC>(gv, vi, i, rt.y, rt.fy);
+#pragma unroll
+            for (int k = 0; k < kMaxBigBlanks; ++k) mb_sub_at<VEC>(gv, vi, i, k < mp.nb ? mp.ids[k] : -1, rt.fg[k]);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) gv[e] = clamp_to(gv[e], cl, do_clamp);
+            store_raw<T, true>(g + (int64_t)vi * VEC, Raw<T>::put(gv));
+        }
     }
 }
 
@@ -1820,12 +2011,53 @@ size_t mb_ring_bytes(int U1p, int max_duration) {
     return (size_t)(max_duration + 1) * (size_t)U1p * sizeof(double) + (size_t)(max_duration + 1) * sizeof(int);
 }
 
+// Vectors per lane of the vector row forms (0: the scalar forms): 16-byte
+// aligned rows of at most 16 KiB.
+static int mb_row_nv(const MbArgs &a) {
+    const bool aligned = ((int64_t)a.V * a.esize) % 16 == 0 && (uintptr_t)a.logits % 16 == 0 &&
+                         (!a.grad || (uintptr_t)a.grad % 16 == 0);
+    if (!aligned) return 0;
+    const int nvec = a.V * a.esize / 16;
+    int nv = 1;
+    while (nv * 64 < nvec) nv <<= 1;
+    return nv <= 16 ? nv : 0;
+}
+
+template <typename Fn> static hipError_t with_mb_nv(int esize, int nv, Fn &&fn) {
+    auto go = [&](auto tag) -> hipError_t {
+        using T = decltype(tag);
+        switch (nv) {
+        case 1: return fn(T{}, std::integral_constant<int, 1>{});
+        case 2: return fn(T{}, std::integral_constant<int, 2>{});
+        case 4: return fn(T{}, std::integral_constant<int, 4>{});
+        case 8: return fn(T{}, std::integral_constant<int, 8>{});
+        default: return fn(T{}, std::integral_constant<int, 16>{});
+        }
+    };
+    if (esize == 4) return go(float{});
+    return go(_Float16{});
+}
+
 hipError_t launch_mb_rows(const MbArgs &a, hipStream_t stream) {
     const MbParams mp = mb_params(a);
+    constexpr int64_t kMaxBlocks = (int64_t)1 << 24;
+    const int nv = mb_row_nv(a);
+    if (nv > 0)
+        return with_mb_nv(a.esize, nv, [&](auto tag, auto nvc) {
+            using T = decltype(tag);
+            constexpr int NV = decltype(nvc)::value;
+            for (int64_t b0 = 0; b0 < a.N; b0 += kMaxBlocks) {
+                const unsigned nb = (unsigned)std::min<int64_t>(kMaxBlocks, a.N - b0);
+                hipLaunchKernelGGL((k_mb_rows_v<T, NV>), dim3(nb), dim3(64), 0, stream,
+                                   static_cast<const T *>(a.logits), a.N, a.V, a.blank, a.fused, mp,
+                                   MBWS(const SampleDesc *, desc), a.B, a.targets, a.S, MBWS(float *, den),
+                                   MBWS(float *, lp), a.lay.n_slots, MBWS(uint32_t *, status), b0);
+            }
+            return hipGetLastError();
+        });
     return with_esize(a.esize, [&](auto tag) {
         using T = decltype(tag);
         const int64_t blocks = (a.N + 3) / 4;
-        constexpr int64_t kMaxBlocks = (int64_t)1 << 24;
         for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocks) {
             const unsigned nb = (unsigned)std::min<int64_t>(kMaxBlocks, blocks - b0);
             hipLaunchKernelGGL(k_mb_rows<T>, dim3(nb), dim3(256), 0, stream, static_cast<const T *>(a.logits), a.N,
@@ -1846,22 +2078,40 @@ hipError_t launch_mb_sweep(const MbArgs &a, hipStream_t stream) {
                            MBWS(int *, ealpha), MBWS(int *, ebeta), MBWS(double *, log2z), a.loss);
         return hipGetLastError();
     };
+    // prefetch depth: the loads of P steps (6 per column) stay within the wait counter's 63
     switch (a.lay.U1p / 64) {
-    case 1: return go(k_mb_sweep<1>);
-    case 2: return go(k_mb_sweep<2>);
-    case 4: return go(k_mb_sweep<4>);
-    case 8: return go(k_mb_sweep<8>);
-    case 16: return go(k_mb_sweep<16>);
+    case 1: return go(k_mb_sweep<1, 4>);
+    case 2: return go(k_mb_sweep<2, 4>);
+    case 4: return go(k_mb_sweep<4, 2>);
+    case 8: return go(k_mb_sweep<8, 1>);
+    case 16: return go(k_mb_sweep<16, 1>);
     }
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_mb_grad(const MbArgs &a, hipStream_t stream) {
     const MbParams mp = mb_params(a);
+    constexpr int64_t kMaxBlocks = (int64_t)1 << 24;
+    const int nv = mb_row_nv(a);
+    if (nv > 0)
+        return with_mb_nv(a.esize, nv, [&](auto tag, auto nvc) {
+            using T = decltype(tag);
+            constexpr int NV = decltype(nvc)::value;
+            for (int64_t b0 = 0; b0 < a.N; b0 += kMaxBlocks) {
+                const unsigned nb = (unsigned)std::min<int64_t>(kMaxBlocks, a.N - b0);
+                hipLaunchKernelGGL((k_mb_grad_v<T, NV>), dim3(nb), dim3(64), 0, stream,
+                                   static_cast<const T *>(a.logits), static_cast<T *>(a.grad), a.N, a.V, a.blank,
+                                   a.fused, mp, a.lay.U1p, MBWS(const SampleDesc *, desc), a.B, a.targets, a.S,
+                                   MBWS(const float *, den), MBWS(const float *, lp), a.lay.n_slots,
+                                   MBWS(const double *, alpha), MBWS(const double *, beta),
+                                   MBWS(const int *, ealpha), MBWS(const int *, ebeta), MBWS(const double *, log2z),
+                                   a.clamp, a.grad_scale, a.fastemit, b0);
+            }
+            return hipGetLastError();
+        });
     return with_esize(a.esize, [&](auto tag) {
         using T = decltype(tag);
         const int64_t blocks = (a.N + 3) / 4;
-        constexpr int64_t kMaxBlocks = (int64_t)1 << 24;
         for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocks) {
             const unsigned nb = (unsigned)std::min<int64_t>(kMaxBlocks, blocks - b0);
             hipLaunchKernelGGL(k_mb_grad<T>, dim3(nb), dim3(256), 0, stream, static_cast<const T *>(a.logits),
