@@ -475,7 +475,11 @@ rnnt_status build_mb_plan(int32_t B, int32_t V, int64_t N, const int32_t *T, con
         dmax = std::max(dmax, (int)dur[i]);
     }
     int max_U1 = 1;
-    for (int32_t i = 0; i < B; ++i) max_U1 = std::max(max_U1, U[i] + 1);
+    for (int32_t i = 0; i < B; ++i) {
+        max_U1 = std::max(max_U1, U[i] + 1);
+        // the sweep addresses a sample's slots with 32-bit byte offsets
+        if (((int64_t)T[i] + U[i]) * (U[i] + 1) * 8 >= ((int64_t)1 << 31)) return RNNT_INVALID_VALUE;
+    }
     int J = 1;
     while (64 * J < max_U1) J <<= 1;
     const int U1p = 64 * J;
@@ -507,7 +511,7 @@ rnnt_status build_mb_plan(int32_t B, int32_t V, int64_t N, const int32_t *T, con
     off = 256;
     L.desc = off;   off = align_up(off + sizeof(SampleDesc) * B);
     L.den = off;    off = align_up(off + sizeof(float) * (size_t)row);
-    L.lp = off;     off = align_up(off + sizeof(float) * (size_t)(2 + nb) * (size_t)slot);
+    L.wp = off;     off = align_up(off + sizeof(double) * (size_t)(2 + nb) * (size_t)slot);
     L.alpha = off;  off = align_up(off + sizeof(double) * (size_t)ab);
     L.beta = off;   off = align_up(off + sizeof(double) * (size_t)ab);
     L.ealpha = off; off = align_up(off + sizeof(int32_t) * (size_t)(diag + B));

@@ -195,7 +195,7 @@ constexpr size_t kMbRingBytes = 64 * 1024;  // LDS of one sweep: the last (longe
 // Workspace of the multi-blank path.  Byte offsets; the status word is at 0
 // and the sample descriptors at 256, as in the plain layout.
 struct MbLayout {
-    size_t status, desc, den, lp, alpha, beta, ealpha, ebeta, log2z, total;
+    size_t status, desc, den, wp, alpha, beta, ealpha, ebeta, log2z, total;
     int64_t n_slots;    // skewed node slots, sum_i (T_i+U_i)(U_i+1)
     int U1p;            // columns of one stored diagonal, a multiple of 64 for every sample
 };

@@ -1510,6 +1510,12 @@ __device__ __forceinline__ double prob_d(float lp) {
     return (lp < -1100.f) ? 0.0 : p;
 }
 
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+    const int lo = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uint64_t)v);
+    const int hi = __builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
+}
+
 __device__ __forceinline__ double readlane_d(double v, int l) {
     const int lo = __builtin_amdgcn_readlane(__double2loint(v), l);
     const int hi = __builtin_amdgcn_readlane(__double2hiint(v), l);
@@ -1517,14 +1523,15 @@ __device__ __forceinline__ double readlane_d(double v, int l) {
 }
 
 // One wave per packed row, four per workgroup: the row's log-normaliser
-// (fused) and the log-probabilities, less sigma, of the edges leaving the
-// node, at its skewed slot: plane 0 the standard blank, plane 1 the next label
-// (-inf at u = U or for a label outside [0,V)), plane 2+i big blank i.
+// (fused) and the probabilities, in fp64, of the edges leaving the node
+// (their log-probabilities less sigma, exponentiated), at its skewed slot:
+// plane 0 the standard blank, plane 1 the next label (0 at u = U or for a
+// label outside [0,V)), plane 2+i big blank i.
 template <typename T>
 __global__ __launch_bounds__(256) void k_mb_rows(const T *__restrict__ logits, int64_t N, int V, int blank,
                                                  int fused, MbParams mp, const SampleDesc *__restrict__ desc,
                                                  int B, const int32_t *__restrict__ targets, int S,
-                                                 float *__restrict__ den, float *__restrict__ lp, int64_t n_slots,
+                                                 float *__restrict__ den, double *__restrict__ wp, int64_t n_slots,
                                                  uint32_t *status, int64_t row_base) {
     const int lane = threadIdx.x & 63;
     const int64_t r = row_base + (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -1564,67 +1571,85 @@ __global__ __launch_bounds__(256) void k_mb_rows(const T *__restrict__ logits, i
         for (int i = 0; i < kMaxBigBlanks; ++i)
             if (lane == 2 + i) k = mp.ids[i];
         const float v = (k >= 0 && dn != kNegInf) ? Elem<T>::load1(x + k) - dn - mp.sigma : kNegInf;
-        lp[(int64_t)lane * n_slots + d.slot_off + (int64_t)(t + u) * U1 + u] = v;
+        wp[(int64_t)lane * n_slots + d.slot_off + (int64_t)(t + u) * U1 + u] = prob_d(v);
     }
 }
 
 // One wave per (sample, direction): blockIdx 2i runs alpha of sample i,
 // 2i+1 beta.  Lane l holds columns l + 64j, j < J.  `cur` is the diagonal
 // just finished, scaled by 2^-E; the LDS ring keeps the last R diagonals
-// (and their exponents) for the big blanks, whose sources lie d_i diagonals
-// away.  The edges' log-probabilities do not depend on the recursion, so
-// those of the next P diagonals are in flight while a diagonal is computed
-// (a register ring, one slot per step mod P; every slot holds all
-// kMaxBigBlanks big-blank planes, unused ones reading plane 0, so the loads
-// and their waits are the same every step).  Every weight is masked where its
-// edge does not exist, so unwritten slots are never used.  Stored: every real
-// diagonal of alpha or beta (scaled) and its exponent; log2 P(y|x) and, from
-// beta, the loss.
-template <int J, int P, bool bw>
+// (and their exponents) for the NB big blanks, whose sources lie d_i
+// diagonals away.  The edges' probabilities do not depend on the recursion,
+// so those of the next P diagonals are in flight while a diagonal is
+// computed (a register ring, one slot per step mod P), loaded through buffer
+// resources with the diagonal's offset in a scalar register and the lane's
+// column offset fixed, so a step does no address arithmetic.  Missing edges
+// are masked through their weights and every LDS read is issued, so a step
+// has no branches around its reads.  Stored: every real diagonal of alpha or
+// beta (scaled) and its exponent; log2 P(y|x) and, from beta, the loss.
+template <int J, int NB> struct MbSweepShape {
+    static constexpr int NW = 2 + NB;  // blank, label, big blanks
+    // steps in flight: their loads and stores stay within the wait counter's 63
+    static constexpr int P0 = 56 / (NW * J + J + 1);
+    static constexpr int P = P0 < 1 ? 1 : (P0 > 8 ? 8 : P0);
+};
+
+template <int J, int NB, bool bw>
 __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const MbParams &mp,
-                                             const float *__restrict__ lp, int64_t n_slots,
+                                             const double *__restrict__ wp, int64_t n_slots,
                                              double *__restrict__ alpha, double *__restrict__ beta,
                                              int *__restrict__ ealpha, int *__restrict__ ebeta,
                                              double *__restrict__ log2z, float *__restrict__ loss) {
     extern __shared__ double mb_ring[];  // R * J * 64 values, then R exponents
     constexpr int U1p = 64 * J;
-    constexpr int NW = 2 + kMaxBigBlanks;  // blank, label, big blanks
+    constexpr int NW = MbSweepShape<J, NB>::NW;
+    constexpr int P = MbSweepShape<J, NB>::P;
     const int lane = threadIdx.x;
     const int T = d.T, U = d.U, U1 = U + 1, nd = T + U, R = mp.R;
     int *ering = reinterpret_cast<int *>(mb_ring + (size_t)R * J * 64);
     for (int q = lane; q < R * J * 64; q += 64) mb_ring[q] = 0.0;
     for (int q = lane; q < R; q += 64) ering[q] = 0;
-    const float *lpb = lp + d.slot_off;
-    const float *lpy = lp + n_slots + d.slot_off;
-    const float *lpg = lp + 2 * n_slots + d.slot_off;
-    int64_t pl[kMaxBigBlanks];  // each big blank's plane; an unused slot reads plane 0 (masked)
+    // one resource per plane over the sample's slots (nd diagonals of U1)
+    const uint32_t span = (uint32_t)nd * (uint32_t)U1 * 8u;
+    Rsrc rs[NW];
 #pragma unroll
-    for (int i = 0; i < kMaxBigBlanks; ++i) pl[i] = (int64_t)(i < mp.nb ? i : 0) * n_slots;
+    for (int k = 0; k < NW; ++k) rs[k] = buffer_at(wp + (int64_t)k * n_slots + d.slot_off, span);
+    uint32_t vo[J], vo_left[J];  // byte offsets of the lane's columns u and u-1 (clamped into the lattice)
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int uc = min(lane + 64 * j, U);
+        vo[j] = (uint32_t)uc * 8u;
+        vo_left[j] = (uint32_t)max(uc - 1, 0) * 8u;
+    }
     double *tab = (bw ? beta : alpha) + d.ab_off;
     int *etab = (bw ? ebeta : ealpha) + d.diag_off + d.index;
 
-    // The raw log-probabilities step `step` uses (steps past the end load the
-    // last step's again; their values are never used).  Forward, diagonal n
-    // pulls from n-1 (blank at column u, label at u-1) and n-d_i; backward,
-    // every edge leaves the node itself.
-    auto load_w = [&](int step, float (&w)[J][NW]) {
+    // soff is wave-uniform; readfirstlane keeps it in a scalar register even where the compiler
+    // computes it with vector instructions (a saturating subtract has no scalar form), which would
+    // otherwise wrap every load in a loop over the distinct values
+    auto ld = [&](int k, uint32_t voff, uint32_t soff) -> double {
+        const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane((int)soff);
+        return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(rs[k], voff, so, 0));
+    };
+    // The probabilities step `step` uses (steps past the end load the last
+    // step's again; never used).  Forward, diagonal n pulls from n-1 (blank
+    // at column u, label at u-1) and n-d_i; backward, every edge leaves the
+    // node itself.
+    auto load_w = [&](int step, double (&w)[J][NW]) {
         const int n = bw ? nd - min(step, nd) : min(step, nd);
+        const uint32_t row = 8u * (uint32_t)U1;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            const int uc = min(lane + 64 * j, U);
             if (!bw) {
-                const int64_t sp = (int64_t)(n - 1) * U1;
-                w[j][0] = lpb[sp + uc];
-                w[j][1] = lpy[sp + max(uc - 1, 0)];
+                const uint32_t sp = (uint32_t)(n - 1) * row;
+                w[j][0] = ld(0, vo[j], sp);
+                w[j][1] = ld(1, vo_left[j], sp);
 #pragma unroll
-                for (int i = 0; i < kMaxBigBlanks; ++i)
-                    w[j][2 + i] = lpg[pl[i] + (int64_t)max(n - mp.dur[i], 0) * U1 + uc];
+                for (int i = 0; i < NB; ++i) w[j][2 + i] = ld(2 + i, vo[j], (uint32_t)max(n - mp.dur[i], 0) * row);
             } else {
-                const int64_t sc = (int64_t)n * U1 + uc;
-                w[j][0] = lpb[sc];
-                w[j][1] = lpy[sc];
+                const uint32_t sc = (uint32_t)n * row;
 #pragma unroll
-                for (int i = 0; i < kMaxBigBlanks; ++i) w[j][2 + i] = lpg[pl[i] + sc];
+                for (int k = 0; k < NW; ++k) w[j][k] = ld(k, vo[j], sc);
             }
         }
     };
@@ -1647,20 +1672,16 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
         }
     }
 
-    // One step: diagonal n from the finished one (`cur`), the ring and the
-    // weights w.  Branch-free: an edge that does not exist gets its weight
-    // replaced by -inf (probability 0) before use, and every ring read is
-    // issued, so the LDS reads of a step go out together.
-    auto step_once = [&](int step, const float (&w)[J][NW]) {
+    auto step_once = [&](int step, const double (&w)[J][NW]) {
         const int n = bw ? nd - step : step;
         slot = bw ? (slot == 0 ? R - 1 : slot - 1) : (slot + 1 == R ? 0 : slot + 1);
-        // big blanks: source diagonal, its ring slot and exponent relative to E
-        int sl[kMaxBigBlanks], shg[kMaxBigBlanks];
-        bool okd[kMaxBigBlanks];
+        // big blanks: source diagonal's ring slot and exponent relative to E
+        int sl[NB > 0 ? NB : 1], shg[NB > 0 ? NB : 1];
+        bool okd[NB > 0 ? NB : 1];
 #pragma unroll
-        for (int i = 0; i < kMaxBigBlanks; ++i) {
+        for (int i = 0; i < NB; ++i) {
             const int dd = mp.dur[i];  // 1 <= dd < R
-            okd[i] = (i < mp.nb) && (bw ? n + dd <= nd : n - dd >= 0);
+            okd[i] = bw ? n + dd <= nd : n - dd >= 0;
             const int q = bw ? slot + dd : slot - dd;
             sl[i] = bw ? (q >= R ? q - R : q) : (q < 0 ? q + R : q);
             shg[i] = (ering[sl[i]] - E) * (int)okd[i];  // arithmetic, so the read is never skipped
@@ -1689,15 +1710,15 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
                 okb = cell;                                  // to (t+1,u)
                 oky = cell && (u < U);                       // to (t,u+1)
             }
-            double acc = prob_d(okb ? w[j][0] : kNegInf) * cur[j];
-            acc = fma(prob_d(oky ? w[j][1] : kNegInf), side[j], acc);
+            double acc = (okb ? w[j][0] : 0.0) * cur[j];
+            acc = fma(oky ? w[j][1] : 0.0, side[j], acc);
 #pragma unroll
-            for (int i = 0; i < kMaxBigBlanks; ++i) {
+            for (int i = 0; i < NB; ++i) {
                 // forward from (t-d_i,u); backward to (t+d_i,u), zero where that is no node
                 const int ts = t - mp.dur[i];
                 const bool ok = okd[i] && (bw ? cell : (ts >= 0 && ts <= T - 1));
                 const double src = mb_ring[(sl[i] * J + j) * 64 + lane];
-                acc = fma(prob_d(ok ? w[j][2 + i] : kNegInf), __builtin_amdgcn_ldexp(src, shg[i]), acc);
+                acc = fma(ok ? w[j][2 + i] : 0.0, __builtin_amdgcn_ldexp(src, shg[i]), acc);
             }
             nx[j] = cell ? acc : 0.0;
         }
@@ -1721,7 +1742,7 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
         }
     };
 
-    float w[P][J][NW];
+    double w[P][J][NW];
 #pragma unroll
     for (int q = 0; q < P; ++q) load_w(1 + q, w[q]);
     for (int s0 = 1; s0 <= nd; s0 += P) {
@@ -1752,21 +1773,23 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
     }
 }
 
-// One wave per packed row, four per workgroup: g_k = P(k) (occ + lambda
-// flow_y) - the flows of the edges leaving the node, each at its class
-// (standard blank, label weighted by 1 + lambda, big blanks), clamped,
-// times the reduction scale.  P(k) is the softmax without sigma (sigma is a
-// constant of every log-probability, so it leaves the log_softmax Jacobian
-// as it is); without fused log_softmax only the flows remain.
-template <int J, int P>
+template <int J, int NB>
 __global__ __launch_bounds__(64) void k_mb_sweep(const SampleDesc *__restrict__ desc, int B, MbParams mp,
-                                                 const float *__restrict__ lp, int64_t n_slots,
+                                                 const double *__restrict__ wp, int64_t n_slots,
                                                  double *__restrict__ alpha, double *__restrict__ beta,
                                                  int *__restrict__ ealpha, int *__restrict__ ebeta,
                                                  double *__restrict__ log2z, float *__restrict__ loss) {
-    const SampleDesc d = desc[blockIdx.x >> 1];
-    if (blockIdx.x & 1) mb_sweep_dir<J, P, true>(d, B, mp, lp, n_slots, alpha, beta, ealpha, ebeta, log2z, loss);
-    else mb_sweep_dir<J, P, false>(d, B, mp, lp, n_slots, alpha, beta, ealpha, ebeta, log2z, loss);
+    // the descriptor is the same for the whole wave: say so, so that every
+    // offset derived from it (the buffer loads' scalar offsets) stays scalar
+    SampleDesc d = desc[blockIdx.x >> 1];
+    d.T = __builtin_amdgcn_readfirstlane(d.T);
+    d.U = __builtin_amdgcn_readfirstlane(d.U);
+    d.index = __builtin_amdgcn_readfirstlane(d.index);
+    d.slot_off = uniform_i64(d.slot_off);
+    d.diag_off = uniform_i64(d.diag_off);
+    d.ab_off = uniform_i64(d.ab_off);
+    if (blockIdx.x & 1) mb_sweep_dir<J, NB, true>(d, B, mp, wp, n_slots, alpha, beta, ealpha, ebeta, log2z, loss);
+    else mb_sweep_dir<J, NB, false>(d, B, mp, wp, n_slots, alpha, beta, ealpha, ebeta, log2z, loss);
 }
 
 // The gradient terms of packed row r: the softmax shift (occupancy with the
@@ -1782,7 +1805,7 @@ struct MbRowTerms {
 __device__ __forceinline__ MbRowTerms mb_row_terms(const SampleDesc &d, int64_t r, int V, int fused,
                                                    const MbParams &mp, int U1p, const int32_t *__restrict__ targets,
                                                    int S, const float *__restrict__ den,
-                                                   const float *__restrict__ lp, int64_t n_slots,
+                                                   const double *__restrict__ wp, int64_t n_slots,
                                                    const double *__restrict__ alpha,
                                                    const double *__restrict__ beta, const int *__restrict__ ealpha,
                                                    const int *__restrict__ ebeta, const double *__restrict__ log2z,
@@ -1809,11 +1832,11 @@ __device__ __forceinline__ MbRowTerms mb_row_terms(const SampleDesc &d, int64_t 
     if (lz != kNegInfD) {
         const double la = log2_d(alpha[d.ab_off + (int64_t)n * U1p + u]) + (double)ealpha[eo + n] - lz;
         lo = la + lbeta(t, u);
-        lb = la + (double)lp[s] * kLog2eD + lbeta(t + 1, u);
-        if (u < d.U) ly = la + (double)lp[n_slots + s] * kLog2eD + lbeta(t, u + 1);
+        lb = la + log2_d(wp[s]) + lbeta(t + 1, u);
+        if (u < d.U) ly = la + log2_d(wp[n_slots + s]) + lbeta(t, u + 1);
 #pragma unroll
         for (int i = 0; i < kMaxBigBlanks; ++i)
-            if (i < mp.nb) lg[i] = la + (double)lp[(int64_t)(2 + i) * n_slots + s] * kLog2eD + lbeta(t + mp.dur[i], u);
+            if (i < mp.nb) lg[i] = la + log2_d(wp[(int64_t)(2 + i) * n_slots + s]) + lbeta(t + mp.dur[i], u);
     }
     if (fastemit > 0.f && ly != kNegInfD && lo != kNegInfD)
         lo += (double)log2f(1.f + fastemit * exp2_fast((float)(ly - lo)));
@@ -1840,7 +1863,7 @@ __global__ __launch_bounds__(256) void k_mb_grad(const T *__restrict__ logits, T
                                                  int V, int blank, int fused, MbParams mp, int U1p,
                                                  const SampleDesc *__restrict__ desc, int B,
                                                  const int32_t *__restrict__ targets, int S,
-                                                 const float *__restrict__ den, const float *__restrict__ lp,
+                                                 const float *__restrict__ den, const double *__restrict__ wp,
                                                  int64_t n_slots, const double *__restrict__ alpha,
                                                  const double *__restrict__ beta, const int *__restrict__ ealpha,
                                                  const int *__restrict__ ebeta, const double *__restrict__ log2z,
@@ -1849,7 +1872,7 @@ __global__ __launch_bounds__(256) void k_mb_grad(const T *__restrict__ logits, T
     const int64_t r = row_base + (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (r >= N) return;
     const SampleDesc d = mb_sample_of_row(desc, B, r);
-    const MbRowTerms rt = mb_row_terms(d, r, V, fused, mp, U1p, targets, S, den, lp, n_slots, alpha, beta, ealpha,
+    const MbRowTerms rt = mb_row_terms(d, r, V, fused, mp, U1p, targets, S, den, wp, n_slots, alpha, beta, ealpha,
                                        ebeta, log2z, scale, fastemit);
     const bool do_clamp = clamp > 0.f;
     const float cl = clamp * scale;
@@ -1873,7 +1896,7 @@ template <typename T, int NV>
 __global__ __launch_bounds__(64) void k_mb_rows_v(const T *__restrict__ logits, int64_t N, int V, int blank,
                                                   int fused, MbParams mp, const SampleDesc *__restrict__ desc,
                                                   int B, const int32_t *__restrict__ targets, int S,
-                                                  float *__restrict__ den, float *__restrict__ lp,
+                                                  float *__restrict__ den, double *__restrict__ wp,
                                                   int64_t n_slots, uint32_t *status, int64_t row_base) {
     using Vec = typename Raw<T>::vec;
     constexpr int VEC = Raw<T>::kVec;
@@ -1922,7 +1945,7 @@ __global__ __launch_bounds__(64) void k_mb_rows_v(const T *__restrict__ logits, 
         for (int i = 0; i < kMaxBigBlanks; ++i)
             if (lane == 2 + i) k = mp.ids[i];
         const float v = (k >= 0 && dn != kNegInf) ? Elem<T>::load1(x + k) - dn - mp.sigma : kNegInf;
-        lp[(int64_t)lane * n_slots + d.slot_off + (int64_t)(t + u) * U1 + u] = v;
+        wp[(int64_t)lane * n_slots + d.slot_off + (int64_t)(t + u) * U1 + u] = prob_d(v);
     }
 }
 
@@ -1941,7 +1964,7 @@ __global__ __launch_bounds__(64) void k_mb_grad_v(const T *__restrict__ logits, 
                                                   int V, int blank, int fused, MbParams mp, int U1p,
                                                   const SampleDesc *__restrict__ desc, int B,
                                                   const int32_t *__restrict__ targets, int S,
-                                                  const float *__restrict__ den, const float *__restrict__ lp,
+                                                  const float *__restrict__ den, const double *__restrict__ wp,
                                                   int64_t n_slots, const double *__restrict__ alpha,
                                                   const double *__restrict__ beta, const int *__restrict__ ealpha,
                                                   const int *__restrict__ ebeta, const double *__restrict__ log2z,
@@ -1960,7 +1983,7 @@ __global__ __launch_bounds__(64) void k_mb_grad_v(const T *__restrict__ logits, 
         for (int i = 0; i < NV; ++i)
             if (i * 64 + lane < nvec) xv[i] = load_raw<T, true>(x + (int64_t)(i * 64 + lane) * VEC);
     }
-    MbRowTerms rt = mb_row_terms(d, r, V, fused, mp, U1p, targets, S, den, lp, n_slots, alpha, beta, ealpha, ebeta,
+    MbRowTerms rt = mb_row_terms(d, r, V, fused, mp, U1p, targets, S, den, wp, n_slots, alpha, beta, ealpha, ebeta,
                                  log2z, scale, fastemit);
     const bool do_clamp = clamp > 0.f;
     const float cl = clamp * scale;
@@ -2051,7 +2074,7 @@ hipError_t launch_mb_rows(const MbArgs &a, hipStream_t stream) {
                 hipLaunchKernelGGL((k_mb_rows_v<T, NV>), dim3(nb), dim3(64), 0, stream,
                                    static_cast<const T *>(a.logits), a.N, a.V, a.blank, a.fused, mp,
                                    MBWS(const SampleDesc *, desc), a.B, a.targets, a.S, MBWS(float *, den),
-                                   MBWS(float *, lp), a.lay.n_slots, MBWS(uint32_t *, status), b0);
+                                   MBWS(double *, wp), a.lay.n_slots, MBWS(uint32_t *, status), b0);
             }
             return hipGetLastError();
         });
@@ -2062,7 +2085,7 @@ hipError_t launch_mb_rows(const MbArgs &a, hipStream_t stream) {
             const unsigned nb = (unsigned)std::min<int64_t>(kMaxBlocks, blocks - b0);
             hipLaunchKernelGGL(k_mb_rows<T>, dim3(nb), dim3(256), 0, stream, static_cast<const T *>(a.logits), a.N,
                                a.V, a.blank, a.fused, mp, MBWS(const SampleDesc *, desc), a.B, a.targets, a.S,
-                               MBWS(float *, den), MBWS(float *, lp), a.lay.n_slots, MBWS(uint32_t *, status),
+                               MBWS(float *, den), MBWS(double *, wp), a.lay.n_slots, MBWS(uint32_t *, status),
                                b0 * 4);
         }
         return hipGetLastError();
@@ -2074,17 +2097,27 @@ hipError_t launch_mb_sweep(const MbArgs &a, hipStream_t stream) {
     const size_t lds = mb_ring_bytes(a.lay.U1p, mp.R - 1);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, dim3(2 * a.B), dim3(64), lds, stream, MBWS(const SampleDesc *, desc), a.B, mp,
-                           MBWS(const float *, lp), a.lay.n_slots, MBWS(double *, alpha), MBWS(double *, beta),
+                           MBWS(const double *, wp), a.lay.n_slots, MBWS(double *, alpha), MBWS(double *, beta),
                            MBWS(int *, ealpha), MBWS(int *, ebeta), MBWS(double *, log2z), a.loss);
         return hipGetLastError();
     };
-    // prefetch depth: the loads of P steps (6 per column) stay within the wait counter's 63
+    auto by_nb = [&](auto jc) -> hipError_t {
+        constexpr int J = decltype(jc)::value;
+        switch (a.nb) {
+        case 0: return go(k_mb_sweep<J, 0>);
+        case 1: return go(k_mb_sweep<J, 1>);
+        case 2: return go(k_mb_sweep<J, 2>);
+        case 3: return go(k_mb_sweep<J, 3>);
+        case 4: return go(k_mb_sweep<J, 4>);
+        }
+        return hipErrorInvalidValue;
+    };
     switch (a.lay.U1p / 64) {
-    case 1: return go(k_mb_sweep<1, 4>);
-    case 2: return go(k_mb_sweep<2, 4>);
-    case 4: return go(k_mb_sweep<4, 2>);
-    case 8: return go(k_mb_sweep<8, 1>);
-    case 16: return go(k_mb_sweep<16, 1>);
+    case 1: return by_nb(std::integral_constant<int, 1>{});
+    case 2: return by_nb(std::integral_constant<int, 2>{});
+    case 4: return by_nb(std::integral_constant<int, 4>{});
+    case 8: return by_nb(std::integral_constant<int, 8>{});
+    case 16: return by_nb(std::integral_constant<int, 16>{});
     }
     return hipErrorInvalidValue;
 }
@@ -2102,7 +2135,7 @@ hipError_t launch_mb_grad(const MbArgs &a, hipStream_t stream) {
                 hipLaunchKernelGGL((k_mb_grad_v<T, NV>), dim3(nb), dim3(64), 0, stream,
                                    static_cast<const T *>(a.logits), static_cast<T *>(a.grad), a.N, a.V, a.blank,
                                    a.fused, mp, a.lay.U1p, MBWS(const SampleDesc *, desc), a.B, a.targets, a.S,
-                                   MBWS(const float *, den), MBWS(const float *, lp), a.lay.n_slots,
+                                   MBWS(const float *, den), MBWS(const double *, wp), a.lay.n_slots,
                                    MBWS(const double *, alpha), MBWS(const double *, beta),
                                    MBWS(const int *, ealpha), MBWS(const int *, ebeta), MBWS(const double *, log2z),
                                    a.clamp, a.grad_scale, a.fastemit, b0);
@@ -2117,7 +2150,7 @@ hipError_t launch_mb_grad(const MbArgs &a, hipStream_t stream) {
             hipLaunchKernelGGL(k_mb_grad<T>, dim3(nb), dim3(256), 0, stream, static_cast<const T *>(a.logits),
                                static_cast<T *>(a.grad), a.N, a.V, a.blank, a.fused, mp, a.lay.U1p,
                                MBWS(const SampleDesc *, desc), a.B, a.targets, a.S, MBWS(const float *, den),
-                               MBWS(const float *, lp), a.lay.n_slots, MBWS(const double *, alpha),
+                               MBWS(const double *, wp), a.lay.n_slots, MBWS(const double *, alpha),
                                MBWS(const double *, beta), MBWS(const int *, ealpha), MBWS(const int *, ebeta),
                                MBWS(const double *, log2z), a.clamp, a.grad_scale, a.fastemit, b0 * 4);
         }
