@@ -36,6 +36,14 @@
  *     device for uploading the per-call schedule.
  *   - All device work is enqueued on `stream` (a hipStream_t; NULL means the
  *     default stream); calls return before it completes.
+ *   - HIP graph capture: an rnnt_loss_fused / rnnt_loss_padded call with
+ *     B <= 64 enqueues kernels only (its schedule travels as kernel
+ *     arguments), so it can be captured and replayed; a replay recomputes
+ *     the same lengths, pointers and sizes it was captured with.  Calls that
+ *     copy their schedule from the host (B > 64, and every
+ *     rnnt_multiblank_loss call) return RNNT_INVALID_VALUE on a capturing
+ *     stream, before enqueuing anything.  Kernel timing must be off while
+ *     capturing.
  *   - Host-detectable argument errors return a non-zero rnnt_status before
  *     anything is enqueued; outputs are then untouched.  Problems only the
  *     device can see set bits in a status word kept in the workspace (see

@@ -186,6 +186,10 @@ std::mutex g_mu;
 std::map<int, StagingRing> g_rings;
 
 rnnt_status upload(void *dst, const std::vector<uint8_t> &src, hipStream_t stream) {
+    // A captured copy would replay from a staging slot that later calls reuse.
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return RNNT_MEMOPS_FAILED;
+    if (cap != hipStreamCaptureStatusNone) return RNNT_INVALID_VALUE;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return RNNT_MEMOPS_FAILED;
     std::lock_guard<std::mutex> lk(g_mu);

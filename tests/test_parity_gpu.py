@@ -543,3 +543,69 @@ def test_fastemit_padded_and_autograd(rl):
     torch.cuda.synchronize()
     fac = torch.cat([torch.full((w.rows(i).stop - w.rows(i).start, 1), float(up[i])) for i in range(3)]).cuda()
     assert torch.allclose(x.grad, ref_grad * fac, rtol=1e-6, atol=0)
+
+
+# ------------------------------------------------------------ HIP graph capture
+def test_graph_capture_and_replay(rl):
+    """A batch of up to 64 samples enqueues kernels only: capture one call, replay it several times with eager
+    calls and synchronisations in between, and check every replay bit for bit against the eager result."""
+    w = workloads.make("char", seed=2, device="cuda")
+    tg = torch.from_numpy(w.targets).to("cuda")
+    T, U = w.logit_lengths, w.target_lengths
+    loss = torch.empty(w.B, dtype=torch.float32, device="cuda")
+    red = torch.empty(1, dtype=torch.float32, device="cuda")
+    grad = torch.empty_like(w.logits)
+    ws = torch.empty(rl.workspace_bytes(w.logits, T, U), dtype=torch.uint8, device="cuda")
+
+    def call():
+        rl.rnnt_loss_fused(w.logits, tg, T, U, blank=w.blank, reduction=w.reduction, fused_log_softmax=w.fused,
+                           grad=grad, workspace=ws, loss=loss, loss_reduced=red)
+
+    call()
+    torch.cuda.synchronize()
+    ref = (loss.clone(), red.clone(), grad.clone())
+    check_against_oracle(w, ref[0], ref[2], w.reduction)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()                      # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    other = workloads.make_custom([30, 12], [6, 3], 40, std=2.0, seed=9, device="cuda")
+    for k in range(3):
+        loss.zero_()
+        red.zero_()
+        grad.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(loss, ref[0]) and torch.equal(red, ref[1]) and torch.equal(grad, ref[2]), k
+        run(rl, other)              # eager work of another batch in between
+        torch.cuda.synchronize()
+
+
+@pytest.mark.filterwarnings("ignore:The CUDA Graph is empty")  # nothing is captured: both calls are refused
+def test_graph_capture_refuses_host_copies(rl):
+    """More than 64 samples (and the multi-blank path) copy their schedule from the host: refused under capture."""
+    Ts, Us = [5] * 70, [2] * 70
+    w = workloads.make_custom(Ts, Us, 16, std=1.0, seed=10, device="cuda")
+    tg = torch.from_numpy(w.targets).to("cuda")
+    loss = torch.empty(w.B, dtype=torch.float32, device="cuda")
+    ws = torch.empty(rl.workspace_bytes(w.logits, w.logit_lengths, w.target_lengths), dtype=torch.uint8,
+                     device="cuda")
+    grad = torch.empty_like(w.logits)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        with pytest.raises(ValueError):
+            rl.rnnt_loss_fused(w.logits, tg, w.logit_lengths, w.target_lengths, reduction="none", grad=grad,
+                               workspace=ws, loss=loss)
+        with pytest.raises(ValueError):
+            rl.rnnt_multiblank_fused(w.logits, tg, w.logit_lengths, w.target_lengths, [13], [2], reduction="none",
+                                     grad=grad, loss=loss)
+    torch.cuda.synchronize()
+    loss2, _, _, _ = rl.rnnt_loss_fused(w.logits, tg, w.logit_lengths, w.target_lengths, reduction="none")
+    torch.cuda.synchronize()
+    assert torch.isfinite(loss2).all()
