@@ -609,3 +609,59 @@ def test_graph_capture_refuses_host_copies(rl):
     loss2, _, _, _ = rl.rnnt_loss_fused(w.logits, tg, w.logit_lengths, w.target_lengths, reduction="none")
     torch.cuda.synchronize()
     assert torch.isfinite(loss2).all()
+
+
+def test_concurrent_calls_from_two_threads(rl):
+    """Two host threads, each on its own stream with its own batch and buffers, alternate calls: one batch of
+    more than 64 samples (schedule through the pinned staging ring), one of 8 (schedule as kernel arguments),
+    so the plan cache is replaced on nearly every call.  Every result equals its sequential reference."""
+    import threading
+    rng = np.random.default_rng(91)
+    big = workloads.make_custom(rng.integers(5, 40, size=80).tolist(), rng.integers(0, 12, size=80).tolist(), 64,
+                                std=2.0, seed=91, reduction="sum", device="cuda")
+    small = workloads.make("char", seed=101, device="cuda")
+
+    def buffers(w):
+        return dict(loss=torch.empty(w.B, dtype=torch.float32, device="cuda"),
+                    loss_reduced=torch.empty(1, dtype=torch.float32, device="cuda"),
+                    grad=torch.empty_like(w.logits),
+                    workspace=torch.empty(rl.workspace_bytes(w.logits, w.logit_lengths, w.target_lengths),
+                                          dtype=torch.uint8, device="cuda"))
+
+    def call(w, buf):
+        tg = torch.from_numpy(w.targets).to("cuda")
+        rl.rnnt_loss_fused(w.logits, tg, w.logit_lengths, w.target_lengths, blank=w.blank, reduction=w.reduction,
+                           fused_log_softmax=w.fused, **buf)
+
+    refs = {}
+    for name, w in (("big", big), ("small", small)):
+        b = buffers(w)
+        call(w, b)
+        torch.cuda.synchronize()
+        refs[name] = (b["loss"].clone(), b["loss_reduced"].clone(), b["grad"].clone())
+    check_against_oracle(big, refs["big"][0], refs["big"][2], "sum")
+    errors = []
+
+    def worker(name, w):
+        try:
+            stream = torch.cuda.Stream()
+            b = buffers(w)
+            with torch.cuda.stream(stream):
+                for _ in range(25):
+                    call(w, b)
+                    stream.synchronize()
+                    ok = (torch.equal(b["loss"], refs[name][0]) and torch.equal(b["loss_reduced"], refs[name][1])
+                          and torch.equal(b["grad"], refs[name][2]))
+                    if not ok:
+                        errors.append(name)
+                        return
+        except Exception as e:  # pragma: no cover - reported below
+            errors.append(f"{name}: {e!r}")
+
+    threads = [threading.Thread(target=worker, args=(n, w)) for n, w in (("big", big), ("small", small))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads)
+    assert not errors, errors
