@@ -237,7 +237,7 @@ rnnt_status rnnt_grad_scale_padded(void *grad, rnnt_dtype dtype, int32_t max_T, 
  * blank list, a non-finite sigma, or a batch whose widest lattice and longest
  * duration need more than 64 KiB of ring per sweep, i.e.
  * (longest duration + 1) * (U1p * 8 + 4) bytes > 64 KiB, U1p = the widest
- * U_i + 1 rounded up to 64 times a power of two (at U1p = 1024 the longest
+ * U_i + 1 rounded up to 128 times a power of two (at U1p = 1024 the longest
  * duration is 6).  A label equal to blank or to a big
  * blank sets RNNT_DEV_BAD_TARGET (read with rnnt_loss_fused_check).
  */

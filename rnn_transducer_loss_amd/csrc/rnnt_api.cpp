@@ -484,9 +484,9 @@ rnnt_status build_mb_plan(int32_t B, int32_t V, int64_t N, const int32_t *T, con
         // the sweep addresses a sample's slots with 32-bit byte offsets
         if (((int64_t)T[i] + U[i]) * (U[i] + 1) * 8 >= ((int64_t)1 << 31)) return RNNT_INVALID_VALUE;
     }
-    int J = 1;
-    while (64 * J < max_U1) J <<= 1;
-    const int U1p = 64 * J;
+    int G = 1;  // groups of 128 columns (two per lane) in the sweep
+    while (128 * G < max_U1) G <<= 1;
+    const int U1p = 128 * G;
     if (mb_ring_bytes(U1p, dmax) > kMbRingBytes) return RNNT_INVALID_VALUE;
     p.desc.resize(B);
     int64_t row = 0, slot = 0, diag = 0, ab = 0;
@@ -515,7 +515,8 @@ rnnt_status build_mb_plan(int32_t B, int32_t V, int64_t N, const int32_t *T, con
     off = 256;
     L.desc = off;   off = align_up(off + sizeof(SampleDesc) * B);
     L.den = off;    off = align_up(off + sizeof(float) * (size_t)row);
-    L.wp = off;     off = align_up(off + sizeof(double) * (size_t)(2 + nb) * (size_t)slot);
+    // the sweep's 16-byte loads of a lane's column pair may reach one slot past a plane's last
+    L.wp = off;     off = align_up(off + sizeof(double) * ((size_t)(2 + nb) * (size_t)slot + 2));
     L.alpha = off;  off = align_up(off + sizeof(double) * (size_t)ab);
     L.beta = off;   off = align_up(off + sizeof(double) * (size_t)ab);
     L.ealpha = off; off = align_up(off + sizeof(int32_t) * (size_t)(diag + B));

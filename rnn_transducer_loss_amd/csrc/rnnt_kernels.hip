@@ -1576,103 +1576,119 @@ __global__ __launch_bounds__(256) void k_mb_rows(const T *__restrict__ logits, i
 }
 
 // One wave per (sample, direction): blockIdx 2i runs alpha of sample i,
-// 2i+1 beta.  Lane l holds columns l + 64j, j < J.  `cur` is the diagonal
-// just finished, scaled by 2^-E; the LDS ring keeps the last R diagonals
-// (and their exponents) for the NB big blanks, whose sources lie d_i
-// diagonals away.  The edges' probabilities do not depend on the recursion,
-// so those of the next P diagonals are in flight while a diagonal is
-// computed (a register ring, one slot per step mod P), loaded through buffer
-// resources with the diagonal's offset in a scalar register and the lane's
-// column offset fixed, so a step does no address arithmetic.  Missing edges
+// 2i+1 beta.  Lane l holds the two adjacent columns 128g + 2l and
+// 128g + 2l + 1 of each group g < G, so every edge's weights for its two
+// columns arrive in one 16-byte load and its two values leave in one 16-byte
+// store; only one neighbour per group and step crosses lanes (a DPP move).
+// `cur` is the diagonal just finished, scaled by 2^-E; the LDS ring keeps the
+// last R diagonals (and their exponents) for the NB big blanks, whose sources
+// lie d_i diagonals away.  The edges' probabilities do not depend on the
+// recursion, so those of the next P diagonals are in flight while a diagonal
+// is computed (a register ring, one slot per step mod P), loaded through
+// buffer resources with the diagonal's offset in a scalar register and the
+// lane's offset fixed, so a step does no address arithmetic.  Missing edges
 // are masked through their weights and every LDS read is issued, so a step
 // has no branches around its reads.  Stored: every real diagonal of alpha or
 // beta (scaled) and its exponent; log2 P(y|x) and, from beta, the loss.
-template <int J, int NB> struct MbSweepShape {
+template <int G, int NB> struct MbSweepShape {
     static constexpr int NW = 2 + NB;  // blank, label, big blanks
-    // steps in flight: their loads and stores stay within the wait counter's 63
-    static constexpr int P0 = 56 / (NW * J + J + 1);
+    // steps in flight: their loads and stores stay within the wait counter's
+    // 63, and the ring within 128 registers (160 measured slower)
+    static constexpr int P_ops = 56 / (NW * G + G + 1);
+    static constexpr int P_regs = 128 / (4 * NW * G);
+    static constexpr int P0 = P_ops < P_regs ? P_ops : P_regs;
     static constexpr int P = P0 < 1 ? 1 : (P0 > 8 ? 8 : P0);
 };
 
-template <int J, int NB, bool bw>
+struct D2 {
+    double a, b;  // columns 2l and 2l+1 of a group
+};
+
+__device__ __forceinline__ D2 as_d2(u32x4 v) {
+    return {__hiloint2double((int)v[1], (int)v[0]), __hiloint2double((int)v[3], (int)v[2])};
+}
+
+template <int G, int NB, bool bw>
 __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const MbParams &mp,
                                              const double *__restrict__ wp, int64_t n_slots,
                                              double *__restrict__ alpha, double *__restrict__ beta,
                                              int *__restrict__ ealpha, int *__restrict__ ebeta,
                                              double *__restrict__ log2z, float *__restrict__ loss) {
-    extern __shared__ double mb_ring[];  // R * J * 64 values, then R exponents
-    constexpr int U1p = 64 * J;
-    constexpr int NW = MbSweepShape<J, NB>::NW;
-    constexpr int P = MbSweepShape<J, NB>::P;
+    extern __shared__ double mb_ring[];  // R diagonals of G groups of 64 lanes x 2 values, then R exponents
+    constexpr int U1p = 128 * G;
+    constexpr int NW = MbSweepShape<G, NB>::NW;
+    constexpr int P = MbSweepShape<G, NB>::P;
     const int lane = threadIdx.x;
     const int T = d.T, U = d.U, U1 = U + 1, nd = T + U, R = mp.R;
-    int *ering = reinterpret_cast<int *>(mb_ring + (size_t)R * J * 64);
-    for (int q = lane; q < R * J * 64; q += 64) mb_ring[q] = 0.0;
+    int *ering = reinterpret_cast<int *>(mb_ring + (size_t)R * U1p);
+    for (int q = lane; q < R * U1p; q += 64) mb_ring[q] = 0.0;
     for (int q = lane; q < R; q += 64) ering[q] = 0;
-    // one resource per plane over the sample's slots (nd diagonals of U1)
+    // ring entry of (diagonal slot s, group g): this lane's pair at 16-byte stride
+    auto ring_at = [&](int sslot, int g) -> D2 * {
+        return reinterpret_cast<D2 *>(mb_ring + (size_t)(sslot * G + g) * 128) + lane;
+    };
+    // one resource per plane over the sample's slots (nd diagonals of U1), so
+    // the 16-byte loads of the last pair of the last diagonal stay in range
     const uint32_t span = (uint32_t)nd * (uint32_t)U1 * 8u;
     Rsrc rs[NW];
 #pragma unroll
     for (int k = 0; k < NW; ++k) rs[k] = buffer_at(wp + (int64_t)k * n_slots + d.slot_off, span);
-    uint32_t vo[J], vo_left[J];  // byte offsets of the lane's columns u and u-1 (clamped into the lattice)
+    uint32_t vo[G];  // byte offset of the lane's first column, clamped into the lattice
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-        const int uc = min(lane + 64 * j, U);
-        vo[j] = (uint32_t)uc * 8u;
-        vo_left[j] = (uint32_t)max(uc - 1, 0) * 8u;
-    }
+    for (int g = 0; g < G; ++g) vo[g] = (uint32_t)min(128 * g + 2 * lane, U) * 8u;
     double *tab = (bw ? beta : alpha) + d.ab_off;
     int *etab = (bw ? ebeta : ealpha) + d.diag_off + d.index;
 
-    // soff is wave-uniform; readfirstlane keeps it in a scalar register even where the compiler
-    // computes it with vector instructions (a saturating subtract has no scalar form), which would
-    // otherwise wrap every load in a loop over the distinct values
-    auto ld = [&](int k, uint32_t voff, uint32_t soff) -> double {
+    // soff is wave-uniform; readfirstlane keeps it in a scalar register even
+    // where the compiler computes it with vector instructions
+    auto ld = [&](int k, uint32_t voff, uint32_t soff) -> D2 {
         const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane((int)soff);
-        return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(rs[k], voff, so, 0));
+        return as_d2(__builtin_amdgcn_raw_buffer_load_b128(rs[k], voff, so, 0));
     };
-    // The probabilities step `step` uses (steps past the end load the last
-    // step's again; never used).  Forward, diagonal n pulls from n-1 (blank
-    // at column u, label at u-1) and n-d_i; backward, every edge leaves the
+    // The probabilities step `step` uses, for the lane's two columns (steps
+    // past the end load the last step's again; never used).  Forward,
+    // diagonal n pulls from n-1 (blank at column u; the label from u-1, moved
+    // over by one column below) and n-d_i; backward, every edge leaves the
     // node itself.
-    auto load_w = [&](int step, double (&w)[J][NW]) {
+    auto load_w = [&](int step, D2 (&w)[G][NW]) {
         const int n = bw ? nd - min(step, nd) : min(step, nd);
         const uint32_t row = 8u * (uint32_t)U1;
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
+        for (int g = 0; g < G; ++g) {
             if (!bw) {
                 const uint32_t sp = (uint32_t)(n - 1) * row;
-                w[j][0] = ld(0, vo[j], sp);
-                w[j][1] = ld(1, vo_left[j], sp);
+                w[g][0] = ld(0, vo[g], sp);
+                w[g][1] = ld(1, vo[g], sp);
 #pragma unroll
-                for (int i = 0; i < NB; ++i) w[j][2 + i] = ld(2 + i, vo[j], (uint32_t)max(n - mp.dur[i], 0) * row);
+                for (int i = 0; i < NB; ++i) w[g][2 + i] = ld(2 + i, vo[g], (uint32_t)max(n - mp.dur[i], 0) * row);
             } else {
                 const uint32_t sc = (uint32_t)n * row;
 #pragma unroll
-                for (int k = 0; k < NW; ++k) w[j][k] = ld(k, vo[j], sc);
+                for (int k = 0; k < NW; ++k) w[g][k] = ld(k, vo[g], sc);
             }
         }
     };
 
     // start: alpha(0,0) = 1 on diagonal 0; beta of the virtual end (T,U) = 1 on diagonal T+U
-    double cur[J];
+    D2 cur[G];
     int E = 0;
     int slot = (bw ? nd : 0) % R;  // ring slot of the diagonal last written (n mod R, kept incrementally)
     {
-        const int uc = bw ? U : 0;
+        const int ue = bw ? U : 0;
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
-            cur[j] = (lane + 64 * j == uc) ? 1.0 : 0.0;
-            mb_ring[(slot * J + j) * 64 + lane] = cur[j];
+        for (int g = 0; g < G; ++g) {
+            const int c0 = 128 * g + 2 * lane;
+            cur[g] = {c0 == ue ? 1.0 : 0.0, c0 + 1 == ue ? 1.0 : 0.0};
+            *ring_at(slot, g) = cur[g];
         }
         if (!bw) {
 #pragma unroll
-            for (int j = 0; j < J; ++j) tab[j * 64 + lane] = cur[j];
+            for (int g = 0; g < G; ++g) reinterpret_cast<D2 *>(tab + 128 * g)[lane] = cur[g];
             if (lane == 0) etab[0] = 0;
         }
     }
 
-    auto step_once = [&](int step, const double (&w)[J][NW]) {
+    auto step_once = [&](int step, const D2 (&w)[G][NW]) {
         const int n = bw ? nd - step : step;
         slot = bw ? (slot == 0 ? R - 1 : slot - 1) : (slot + 1 == R ? 0 : slot + 1);
         // big blanks: source diagonal's ring slot and exponent relative to E
@@ -1686,63 +1702,90 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
             sl[i] = bw ? (q >= R ? q - R : q) : (q < 0 ? q + R : q);
             shg[i] = (ering[sl[i]] - E) * (int)okd[i];  // arithmetic, so the read is never skipped
         }
-        // the neighbouring column of the finished diagonal: u-1 (forward) or u+1 (backward)
-        double rot[J], side[J];
+        // Cross-lane neighbours.  Forward: column 2l-1 of the finished
+        // diagonal and the label weight of column 2l-1 come from lane l-1's
+        // second value (lane 0 of group g: lane 63 of group g-1).  Backward:
+        // column 2l+2 of the finished diagonal from lane l+1's first value
+        // (lane 63 of group g: lane 0 of group g+1).
+        double nb_v[G], nb_w[G];
 #pragma unroll
-        for (int j = 0; j < J; ++j) rot[j] = bw ? rotate_down(cur[j]) : rotate_up(cur[j]);
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            if (bw) side[j] = (lane == 63) ? (j + 1 < J ? rot[j + 1] : 0.0) : rot[j];
-            else side[j] = (lane == 0) ? (j > 0 ? rot[j - 1] : 0.0) : rot[j];
+        for (int g = 0; g < G; ++g) {
+            nb_v[g] = bw ? rotate_down(cur[g].a) : rotate_up(cur[g].b);
+            nb_w[g] = bw ? 0.0 : rotate_up(w[g][1].b);
         }
-        double nx[J];
+        double side_v[G], side_w[G];
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const int u = lane + 64 * j;
-            const int t = n - u;
-            bool cell, okb, oky;
-            if (!bw) {
-                cell = (u <= U) && ((t >= 0 && t <= T - 1) || (t == T && u == U));
-                okb = (t >= 1) && (t <= T);                  // from (t-1,u)
-                oky = (u >= 1) && (t >= 0) && (t <= T - 1);  // from (t,u-1)
+        for (int g = 0; g < G; ++g) {
+            if (bw) {
+                side_v[g] = (lane == 63) ? (g + 1 < G ? nb_v[g + 1] : 0.0) : nb_v[g];
+                side_w[g] = 0.0;
             } else {
-                cell = (u <= U) && (t >= 0) && (t <= T - 1);
-                okb = cell;                                  // to (t+1,u)
-                oky = cell && (u < U);                       // to (t,u+1)
+                side_v[g] = (lane == 0) ? (g > 0 ? nb_v[g - 1] : 0.0) : nb_v[g];
+                side_w[g] = (lane == 0) ? (g > 0 ? nb_w[g - 1] : 0.0) : nb_w[g];
             }
-            double acc = (okb ? w[j][0] : 0.0) * cur[j];
-            acc = fma(oky ? w[j][1] : 0.0, side[j], acc);
+        }
+        D2 nx[G];
 #pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                // forward from (t-d_i,u); backward to (t+d_i,u), zero where that is no node
-                const int ts = t - mp.dur[i];
-                const bool ok = okd[i] && (bw ? cell : (ts >= 0 && ts <= T - 1));
-                const double src = mb_ring[(sl[i] * J + j) * 64 + lane];
-                acc = fma(ok ? w[j][2 + i] : 0.0, __builtin_amdgcn_ldexp(src, shg[i]), acc);
+        for (int g = 0; g < G; ++g) {
+            D2 src[NB > 0 ? NB : 1];
+#pragma unroll
+            for (int i = 0; i < NB; ++i) src[i] = *ring_at(sl[i], g);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int u = 128 * g + 2 * lane + h;
+                const int t = n - u;
+                bool cell, okb, oky;
+                if (!bw) {
+                    cell = (u <= U) && ((t >= 0 && t <= T - 1) || (t == T && u == U));
+                    okb = (t >= 1) && (t <= T);                  // from (t-1,u)
+                    oky = (u >= 1) && (t >= 0) && (t <= T - 1);  // from (t,u-1)
+                } else {
+                    cell = (u <= U) && (t >= 0) && (t <= T - 1);
+                    okb = cell;                                  // to (t+1,u)
+                    oky = cell && (u < U);                       // to (t,u+1)
+                }
+                const double wb = h ? w[g][0].b : w[g][0].a;
+                const double cv = h ? cur[g].b : cur[g].a;
+                // label: forward, weight of column u-1 and value of column u-1; backward, own weight and u+1
+                const double wy = bw ? (h ? w[g][1].b : w[g][1].a) : (h ? w[g][1].a : side_w[g]);
+                const double sv = bw ? (h ? side_v[g] : cur[g].b) : (h ? cur[g].a : side_v[g]);
+                double acc = (okb ? wb : 0.0) * cv;
+                acc = fma(oky ? wy : 0.0, sv, acc);
+#pragma unroll
+                for (int i = 0; i < NB; ++i) {
+                    // forward from (t-d_i,u); backward to (t+d_i,u), zero where that is no node
+                    const int ts = t - mp.dur[i];
+                    const bool ok = okd[i] && (bw ? cell : (ts >= 0 && ts <= T - 1));
+                    const double wg = h ? w[g][2 + i].b : w[g][2 + i].a;
+                    const double sr = h ? src[i].b : src[i].a;
+                    acc = fma(ok ? wg : 0.0, __builtin_amdgcn_ldexp(sr, shg[i]), acc);
+                }
+                if (h) nx[g].b = cell ? acc : 0.0;
+                else nx[g].a = cell ? acc : 0.0;
             }
-            nx[j] = cell ? acc : 0.0;
         }
         // renormalise by a power of two (a diagonal of zeros keeps its exponent)
         int eb = 0;
 #pragma unroll
-        for (int j = 0; j < J; ++j) eb = max(eb, (__double2hiint(nx[j]) >> 20) & 0x7ff);
+        for (int g = 0; g < G; ++g)
+            eb = max(eb, max((__double2hiint(nx[g].a) >> 20) & 0x7ff, (__double2hiint(nx[g].b) >> 20) & 0x7ff));
         eb = wave_max_i(eb);
         const int sh = eb == 0 ? 0 : eb - 1023;
         E += sh;
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
-            cur[j] = __builtin_amdgcn_ldexp(nx[j], -sh);
-            mb_ring[(slot * J + j) * 64 + lane] = cur[j];
+        for (int g = 0; g < G; ++g) {
+            cur[g] = {__builtin_amdgcn_ldexp(nx[g].a, -sh), __builtin_amdgcn_ldexp(nx[g].b, -sh)};
+            *ring_at(slot, g) = cur[g];
         }
         if (lane == 0) ering[slot] = E;
         if (n < nd) {
 #pragma unroll
-            for (int j = 0; j < J; ++j) tab[(int64_t)n * U1p + j * 64 + lane] = cur[j];
+            for (int g = 0; g < G; ++g) reinterpret_cast<D2 *>(tab + (int64_t)n * U1p + 128 * g)[lane] = cur[g];
             if (lane == 0) etab[n] = E;
         }
     };
 
-    double w[P][J][NW];
+    D2 w[P][G][NW];
 #pragma unroll
     for (int q = 0; q < P; ++q) load_w(1 + q, w[q]);
     for (int s0 = 1; s0 <= nd; s0 += P) {
@@ -1755,13 +1798,12 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
         }
     }
 
-    // log2 P(y|x): alpha of the virtual end (T,U), or beta(0,0)
+    // log2 P(y|x): alpha of the virtual end (T,U), or beta(0,0), read back
+    // from the ring slot the last diagonal went to (a register array indexed
+    // by the column's group would be kept in scratch)
     const int ue = bw ? 0 : U;
-    double v = 0.0;
-#pragma unroll
-    for (int j = 0; j < J; ++j)
-        if (j == (ue >> 6)) v = cur[j];
-    v = readlane_d(v, ue & 63);
+    const D2 mine = *ring_at(slot, ue >> 7);
+    const double v = readlane_d((ue & 1) ? mine.b : mine.a, (ue & 127) >> 1);
     const double l2 = (v > 0.0) ? log2_d(v) + (double)E : kNegInfD;
     if (lane == 0) {
         if (bw) {
@@ -1773,23 +1815,15 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
     }
 }
 
-template <int J, int NB>
+template <int G, int NB>
 __global__ __launch_bounds__(64) void k_mb_sweep(const SampleDesc *__restrict__ desc, int B, MbParams mp,
                                                  const double *__restrict__ wp, int64_t n_slots,
                                                  double *__restrict__ alpha, double *__restrict__ beta,
                                                  int *__restrict__ ealpha, int *__restrict__ ebeta,
                                                  double *__restrict__ log2z, float *__restrict__ loss) {
-    // the descriptor is the same for the whole wave: say so, so that every
-    // offset derived from it (the buffer loads' scalar offsets) stays scalar
-    SampleDesc d = desc[blockIdx.x >> 1];
-    d.T = __builtin_amdgcn_readfirstlane(d.T);
-    d.U = __builtin_amdgcn_readfirstlane(d.U);
-    d.index = __builtin_amdgcn_readfirstlane(d.index);
-    d.slot_off = uniform_i64(d.slot_off);
-    d.diag_off = uniform_i64(d.diag_off);
-    d.ab_off = uniform_i64(d.ab_off);
-    if (blockIdx.x & 1) mb_sweep_dir<J, NB, true>(d, B, mp, wp, n_slots, alpha, beta, ealpha, ebeta, log2z, loss);
-    else mb_sweep_dir<J, NB, false>(d, B, mp, wp, n_slots, alpha, beta, ealpha, ebeta, log2z, loss);
+    const SampleDesc d = desc[blockIdx.x >> 1];
+    if (blockIdx.x & 1) mb_sweep_dir<G, NB, true>(d, B, mp, wp, n_slots, alpha, beta, ealpha, ebeta, log2z, loss);
+    else mb_sweep_dir<G, NB, false>(d, B, mp, wp, n_slots, alpha, beta, ealpha, ebeta, log2z, loss);
 }
 
 // The gradient terms of packed row r: the softmax shift (occupancy with the
@@ -2102,22 +2136,21 @@ hipError_t launch_mb_sweep(const MbArgs &a, hipStream_t stream) {
         return hipGetLastError();
     };
     auto by_nb = [&](auto jc) -> hipError_t {
-        constexpr int J = decltype(jc)::value;
+        constexpr int G = decltype(jc)::value;
         switch (a.nb) {
-        case 0: return go(k_mb_sweep<J, 0>);
-        case 1: return go(k_mb_sweep<J, 1>);
-        case 2: return go(k_mb_sweep<J, 2>);
-        case 3: return go(k_mb_sweep<J, 3>);
-        case 4: return go(k_mb_sweep<J, 4>);
+        case 0: return go(k_mb_sweep<G, 0>);
+        case 1: return go(k_mb_sweep<G, 1>);
+        case 2: return go(k_mb_sweep<G, 2>);
+        case 3: return go(k_mb_sweep<G, 3>);
+        case 4: return go(k_mb_sweep<G, 4>);
         }
         return hipErrorInvalidValue;
     };
-    switch (a.lay.U1p / 64) {
+    switch (a.lay.U1p / 128) {
     case 1: return by_nb(std::integral_constant<int, 1>{});
     case 2: return by_nb(std::integral_constant<int, 2>{});
     case 4: return by_nb(std::integral_constant<int, 4>{});
     case 8: return by_nb(std::integral_constant<int, 8>{});
-    case 16: return by_nb(std::integral_constant<int, 16>{});
     }
     return hipErrorInvalidValue;
 }
