@@ -1516,6 +1516,15 @@ __device__ __forceinline__ int64_t uniform_i64(int64_t v) {
     return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
 }
 
+// Workgroups are dispatched to the 8 XCDs in turn (workgroup b to XCD b % 8),
+// each XCD with its own L2.  Logical block of workgroup b when the grid
+// (a multiple of 8 workgroups, `per` for each XCD) gives XCD x the
+// contiguous blocks [x * per, (x + 1) * per): the per-node records a row
+// pass writes near its rows then fill their lines in one L2, not eight.
+__device__ __forceinline__ int64_t xcd_block(int64_t b, int64_t per) {
+    return (b & 7) * per + (b >> 3);
+}
+
 __device__ __forceinline__ double readlane_d(double v, int l) {
     const int lo = __builtin_amdgcn_readlane(__double2loint(v), l);
     const int hi = __builtin_amdgcn_readlane(__double2hiint(v), l);
@@ -1935,7 +1944,7 @@ __global__ __launch_bounds__(64) void k_mb_rows_v(const T *__restrict__ logits, 
     using Vec = typename Raw<T>::vec;
     constexpr int VEC = Raw<T>::kVec;
     const int lane = threadIdx.x;
-    const int64_t r = row_base + (int64_t)blockIdx.x;
+    const int64_t r = row_base + xcd_block(blockIdx.x, gridDim.x >> 3);
     if (r >= N) return;
     const SampleDesc d = mb_sample_of_row(desc, B, r);
     const int U1 = d.U + 1;
@@ -2006,6 +2015,7 @@ __global__ __launch_bounds__(64) void k_mb_grad_v(const T *__restrict__ logits, 
     using Vec = typename Raw<T>::vec;
     constexpr int VEC = Raw<T>::kVec;
     const int lane = threadIdx.x;
+    // plain order: the XCD-contiguous order of the row pass made this pass slower (0.88 -> 0.94 ms)
     const int64_t r = row_base + (int64_t)blockIdx.x;
     if (r >= N) return;
     const SampleDesc d = mb_sample_of_row(desc, B, r);
@@ -2104,7 +2114,8 @@ hipError_t launch_mb_rows(const MbArgs &a, hipStream_t stream) {
             using T = decltype(tag);
             constexpr int NV = decltype(nvc)::value;
             for (int64_t b0 = 0; b0 < a.N; b0 += kMaxBlocks) {
-                const unsigned nb = (unsigned)std::min<int64_t>(kMaxBlocks, a.N - b0);
+                // a multiple of 8 workgroups, so each XCD takes a contiguous range of rows
+                const unsigned nb = (unsigned)((std::min<int64_t>(kMaxBlocks, a.N - b0) + 7) & ~(int64_t)7);
                 hipLaunchKernelGGL((k_mb_rows_v<T, NV>), dim3(nb), dim3(64), 0, stream,
                                    static_cast<const T *>(a.logits), a.N, a.V, a.blank, a.fused, mp,
                                    MBWS(const SampleDesc *, desc), a.B, a.targets, a.S, MBWS(float *, den),
