@@ -240,6 +240,10 @@ rnnt_status rnnt_grad_scale_padded(void *grad, rnnt_dtype dtype, int32_t max_T, 
  * U_i + 1 rounded up to 128 times a power of two (at U1p = 1024 the longest
  * duration is 6).  A label equal to blank or to a big
  * blank sets RNNT_DEV_BAD_TARGET (read with rnnt_loss_fused_check).
+ * The recursion runs in fp64 probabilities renormalised per anti-diagonal:
+ * an edge whose log-probability (less sigma) is below about -745 counts as
+ * probability zero (rnnt_loss_fused has a log-domain fallback for such
+ * inputs; this path does not).
  */
 rnnt_status rnnt_multiblank_workspace_size(int32_t B, int32_t V, int64_t N, rnnt_dtype dtype,
                                            const int32_t *logit_lengths, const int32_t *target_lengths,

@@ -200,3 +200,18 @@ def test_multiblank_workload_full_size(rl):
     area = w.logit_lengths.astype(np.int64) * (w.target_lengths + 1)
     check_mb(w, loss, grad, w.reduction, grad_samples=[int(np.argmin(area)), int(np.argmax(area))])
     assert grad.double().sum(dim=1).abs().max().item() < 1e-6
+
+
+def test_multiblank_extreme_fused_logits(rl):
+    """Fused logits of spread N(0, 40^2): edge log-probabilities reach about -300, far outside fp32's exponent
+    range, inside fp64's (the sweep works in fp64 probabilities).  Tolerance as for the plain path's extreme case:
+    the fp32 inputs themselves carry ~1.5e-5 rounding at |x| ~ 160, so the gradient is held to 2e-4 and the loss
+    to 1e-5 relative."""
+    w = _mb([25, 11, 7], [5, 4, 0], 64, [60, 61], [2, 3], 0.1, std=40.0, blank=-1, reduction="sum", seed=43)
+    loss, red, grad, flags = run_mb(rl, w)
+    assert flags == 0
+    ref_l, _, ref_g, _ = oracle.multiblank_batch(w.logits.cpu().numpy(), w.targets, w.logit_lengths,
+                                                 w.target_lengths, w.big_blank_ids, w.big_blank_durations,
+                                                 blank=-1, sigma=w.sigma, reduction="none")
+    np.testing.assert_allclose(loss.double().cpu().numpy(), ref_l, rtol=1e-5, atol=0)
+    assert np.abs(grad.double().cpu().numpy() - ref_g).max() <= 2e-4
