@@ -215,3 +215,12 @@ def test_multiblank_extreme_fused_logits(rl):
                                                  blank=-1, sigma=w.sigma, reduction="none")
     np.testing.assert_allclose(loss.double().cpu().numpy(), ref_l, rtol=1e-5, atol=0)
     assert np.abs(grad.double().cpu().numpy() - ref_g).max() <= 2e-4
+
+
+def test_multiblank_very_long_lattices(rl):
+    """T = 20000 frames with big blanks of 2 and 8 frames: ~20000 diagonal steps through the LDS ring, every loss
+    and the whole gradient."""
+    w = _mb([20000, 9000], [3, 0], 16, [14, 13], [2, 8], 0.05, std=1.0, blank=-1, reduction="none", seed=18)
+    loss, red, grad, flags = run_mb(rl, w)
+    assert flags == 0
+    check_mb(w, loss, grad, "none")

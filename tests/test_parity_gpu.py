@@ -665,3 +665,12 @@ def test_concurrent_calls_from_two_threads(rl):
         t.join(timeout=120)
     assert not any(t.is_alive() for t in threads)
     assert not errors, errors
+
+
+def test_very_long_lattices(rl):
+    """T = 20000 frames (about 20000 dependent diagonal steps, total probabilities near e^-55000, far below fp64's
+    range, carried by the sweeps' exponents), with U = 3 and U = 0, fused fp32: every loss and the whole gradient."""
+    w = _custom([20000, 12000], [3, 0], 16, std=1.0, blank=-1, reduction="none", seed=17)
+    loss, red, grad, flags = run(rl, w)
+    assert flags == 0
+    check_against_oracle(w, loss, grad, "none")
