@@ -224,3 +224,30 @@ def test_multiblank_very_long_lattices(rl):
     loss, red, grad, flags = run_mb(rl, w)
     assert flags == 0
     check_mb(w, loss, grad, "none")
+
+
+@pytest.mark.parametrize("seed", range(2000, 2016))
+def test_multiblank_random_option_sweep(rl, seed):
+    """Seeded draws over the multi-blank option space: batch shape, vocabulary, dtype, fused or not, the big
+    blanks (count, classes, durations), sigma, clamp, FastEmit and reduction."""
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 10))
+    V = int(rng.choice([8, 16, 33, 64, 200, 1024]))
+    nb = int(rng.integers(0, 5))
+    blank = int(rng.integers(-V, V))
+    bn = blank + V if blank < 0 else blank
+    ids = [int(k) for k in rng.choice([k for k in range(V) if k != bn], size=nb, replace=False)]
+    durs = [int(d) for d in rng.integers(1, 17, size=nb)]
+    Ts = rng.integers(1, 60, size=B).tolist()
+    Us = rng.integers(0, 25, size=B).tolist()
+    fused = bool(rng.random() < 0.7)
+    dtype = torch.float16 if rng.random() < 0.3 else torch.float32
+    reduction = str(rng.choice(["none", "mean", "sum"]))
+    clamp = float(rng.choice([-1.0, -1.0, 0.1]))
+    lam = float(rng.choice([0.0, 0.0, 0.2]))
+    sigma = float(rng.choice([0.0, 0.05, -0.1]))
+    w = _mb(Ts, Us, V, ids, durs, sigma, dtype=dtype, std=2.0 if fused else 1.5, blank=blank, clamp=clamp,
+            fused=fused, prenormalise=not fused, reduction=reduction, seed=seed)
+    loss, red, grad, flags = run_mb(rl, w, fastemit=lam)
+    assert flags == 0
+    check_mb(w, loss, grad, reduction, fastemit=lam)

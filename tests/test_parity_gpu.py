@@ -674,3 +674,47 @@ def test_very_long_lattices(rl):
     loss, red, grad, flags = run(rl, w)
     assert flags == 0
     check_against_oracle(w, loss, grad, "none")
+
+
+# ------------------------------------------------------ randomized option sweep
+def _random_case(seed):
+    """One seeded draw over the option space: batch shape, vocabulary, dtype, fused or not, blank position,
+    clamp, FastEmit, reduction and logits alignment."""
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 12))
+    V = int(rng.choice([1, 2, 7, 16, 29, 64, 100, 257, 512, 1000, 1024, 2048]))
+    Ts = rng.integers(1, 70, size=B).tolist()
+    Us = (rng.integers(0, 30, size=B) if V > 1 else np.zeros(B, np.int64)).tolist()
+    dtype = torch.float16 if rng.random() < 0.4 else torch.float32
+    fused = bool(rng.random() < 0.7)
+    blank = int(rng.integers(-V, V))
+    clamp = float(rng.choice([-1.0, -1.0, 0.05, 0.3]))
+    lam = float(rng.choice([0.0, 0.0, 0.01, 0.5]))
+    reduction = str(rng.choice(["none", "mean", "sum"]))
+    return dict(Ts=Ts, Us=Us, V=V, dtype=dtype, fused=fused, blank=blank, clamp=clamp, lam=lam,
+                reduction=reduction, unaligned=bool(rng.random() < 0.2), padded=bool(rng.random() < 0.2))
+
+
+@pytest.mark.parametrize("seed", range(1000, 1024))
+def test_random_option_sweep(rl, seed):
+    c = _random_case(seed)
+    w = _custom(c["Ts"], c["Us"], c["V"], dtype=c["dtype"], std=2.0 if c["fused"] else 1.5, blank=c["blank"],
+                clamp=c["clamp"], fused=c["fused"], prenormalise=not c["fused"], reduction=c["reduction"], seed=seed)
+    if c["unaligned"]:
+        buf = torch.empty(w.logits.numel() + 1, dtype=w.logits.dtype, device="cuda")
+        buf[1:].copy_(w.logits.reshape(-1))
+        w.logits = buf[1:].view(w.N, w.V)
+    loss, red, grad, flags = run(rl, w, fastemit=c["lam"])
+    assert flags == 0, c
+    check_against_oracle(w, loss, grad, c["reduction"], fastemit=c["lam"])
+    _reduced_ok(w, loss, red, c["reduction"])
+    if c["padded"]:
+        max_T, max_U1 = max(c["Ts"]) + 2, max(c["Us"]) + 3
+        xp = _to_padded(w, max_T, max_U1)
+        tg = torch.from_numpy(w.targets).to("cuda")
+        lp_, _, gp_, _ = rl.rnnt_loss_fused(xp, tg, w.logit_lengths, w.target_lengths, blank=w.blank,
+                                            clamp=c["clamp"], reduction=c["reduction"], fused_log_softmax=w.fused,
+                                            fastemit_lambda=c["lam"])
+        torch.cuda.synchronize()
+        rows, pad = _padded_rows(w, gp_, max_T, max_U1)
+        assert torch.equal(lp_, loss) and torch.equal(rows, grad) and bool((pad == 0).all())
