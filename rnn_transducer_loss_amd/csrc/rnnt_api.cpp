@@ -69,11 +69,18 @@ std::vector<int32_t> lpt_order(int32_t B, const int32_t *T, const int32_t *U) {
 // Rows per chunk: about 256 KiB of logits per workgroup, but at least ~1024
 // chunks when the batch is small, rounded to a multiple of 64 rows (the most
 // rows any row geometry's workgroup takes per iteration), so the chunk table
-// does not depend on the geometry.
+// does not depend on the geometry.  Below 64 K rows that rounding would
+// leave most CUs idle and each workgroup walking its chunk in several
+// dependent iterations, so small batches take chunks of a multiple of 8
+// rows, ~2048 of them: one iteration each for rows of more than 16 classes.
 int32_t rows_per_chunk(int64_t N, int32_t V, int esize) {
     const int64_t row_bytes = (int64_t)V * esize;
     const int64_t by_bytes = std::max<int64_t>(1, (256 * 1024) / std::max<int64_t>(1, row_bytes));
     const int64_t by_count = std::max<int64_t>(1, (N + 1023) / 1024);
+    if (by_count < 64) {
+        const int64_t small = std::max<int64_t>(1, (N + 2047) / 2048);
+        return (int32_t)std::min<int64_t>((std::min(by_bytes, small) + 7) / 8 * 8, 64);
+    }
     int64_t r = std::min(by_bytes, by_count);
     r = (r + 63) / 64 * 64;
     return (int32_t)std::min<int64_t>(r, 1 << 16);

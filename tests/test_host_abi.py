@@ -194,6 +194,19 @@ def test_schedule_chunk_sizes_follow_row_bytes():
     assert (c32[:, 2] % 64 == 0).sum() >= len(c32) - 8
 
 
+def test_small_batches_get_fine_chunks():
+    # a character-vocabulary batch (~13 K rows of 29 classes): chunks of 8 rows, so ~1600 workgroups each take
+    # one iteration instead of 200 walking 64 rows
+    rng = np.random.default_rng(2)
+    T = rng.integers(50, 101, size=8).astype(np.int32)
+    U = rng.integers(10, 31, size=8).astype(np.int32)
+    _, c = _lib.plan_describe(29, _lib.RNNT_F32, T, U)
+    N = int((T.astype(np.int64) * (U + 1)).sum())
+    assert c[:, 2].max() == 8 and len(c) >= N // 8
+    _, tiny = _lib.plan_describe(16, _lib.RNNT_F32, np.array([12, 9], np.int32), np.array([4, 3], np.int32))
+    assert tiny[:, 2].max() == 8 and tiny[:, 2].sum() == 12 * 5 + 9 * 4
+
+
 def _call_multiblank(**over):
     """rnnt_multiblank_loss with fake (never dereferenced) device pointers; only host checks can run."""
     T = np.array([4, 6], np.int32)
