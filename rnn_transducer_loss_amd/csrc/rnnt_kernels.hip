@@ -27,6 +27,9 @@
 // by HBM bandwidth (coalesced 16-byte accesses, one row per wave with the next
 // row's loads in flight, DPP wave reductions) and the recursion by the latency
 // of its T+U dependent steps.
+//
+// The multi-blank transducer (big blanks with durations) has passes of its
+// own, at the end of this file.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -1473,7 +1476,7 @@ hipError_t launch_zero_padding(void *grad, int esize, int V, int B, int max_T, i
 // T+U, with beta(T,U) = 1, so the ends need no special case.
 //
 // Three passes of their own: per row, the log-normaliser and the edges'
-// log-probabilities (fp32 planes in the skewed slots); one wave per sample
+// probabilities (fp64 planes in the skewed slots); one wave per sample
 // and direction sweeping anti-diagonals in fp64 probabilities renormalised by
 // a power of two on every diagonal, with the last (longest duration + 1)
 // diagonals in an LDS ring for the big blanks' jumps; and per row, the
@@ -1508,12 +1511,6 @@ __device__ __forceinline__ double prob_d(float lp) {
     const float f = fmaf(lp, kHi, -k) + lp * kLo;
     const double p = __builtin_amdgcn_ldexp((double)exp2_fast(f), (int)k);
     return (lp < -1100.f) ? 0.0 : p;
-}
-
-__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
-    const int lo = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uint64_t)v);
-    const int hi = __builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
-    return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
 }
 
 // Workgroups are dispatched to the 8 XCDs in turn (workgroup b to XCD b % 8),
