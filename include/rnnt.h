@@ -258,13 +258,42 @@ rnnt_status rnnt_multiblank_loss(const void *logits, rnnt_dtype dtype, int64_t N
                                  void *workspace, size_t workspace_bytes, rnnt_stream_t stream);
 
 /*
+ * The multi-blank loss for logits in the padded (B, max_T, max_U1, V) layout
+ * (the compute_multiblank_grad_kernel page's activations [B, T, U, V + 1 +
+ * num_big_blanks]): node (t, u) of sample i is row (i*max_T + t)*max_U1 + u;
+ * padding rows of logits are never read and get a zero gradient (written by
+ * the gradient pass itself).  Arguments and limits as for
+ * rnnt_multiblank_loss, with max_T >= T_i and max_U1 >= U_i + 1 for every
+ * sample, and the workspace sized by rnnt_multiblank_padded_workspace_size.
+ */
+rnnt_status rnnt_multiblank_padded_workspace_size(int32_t B, int32_t V, int32_t max_T, int32_t max_U1,
+                                                  rnnt_dtype dtype, const int32_t *logit_lengths,
+                                                  const int32_t *target_lengths, int32_t num_big_blanks,
+                                                  const int32_t *big_blank_durations, size_t *workspace_bytes);
+rnnt_status rnnt_multiblank_loss_padded(const void *logits, rnnt_dtype dtype, int32_t max_T, int32_t max_U1,
+                                        int32_t V, const int32_t *targets, int32_t S,
+                                        const int32_t *logit_lengths, const int32_t *target_lengths, int32_t B,
+                                        int64_t blank, int32_t num_big_blanks, const int32_t *big_blank_ids,
+                                        const int32_t *big_blank_durations, float sigma, float clamp,
+                                        float fastemit_lambda, int fused_log_softmax, rnnt_reduction reduction,
+                                        float *loss, float *loss_reduced, void *grad, void *workspace,
+                                        size_t workspace_bytes, rnnt_stream_t stream);
+
+/*
  * rnnt_grad_scale for a gradient written by rnnt_multiblank_loss (same
- * arguments; the workspace is that call's).
+ * arguments; the workspace is that call's), and for one written by
+ * rnnt_multiblank_loss_padded (all B*max_T*max_U1 rows are scaled; padding
+ * rows stay zero).
  */
 rnnt_status rnnt_multiblank_grad_scale(void *grad, rnnt_dtype dtype, int64_t N, int32_t V,
                                        const int32_t *logit_lengths, const int32_t *target_lengths, int32_t B,
                                        const float *scale, int per_sample, const void *workspace,
                                        size_t workspace_bytes, rnnt_stream_t stream);
+rnnt_status rnnt_multiblank_grad_scale_padded(void *grad, rnnt_dtype dtype, int32_t max_T, int32_t max_U1,
+                                              int32_t V, const int32_t *logit_lengths,
+                                              const int32_t *target_lengths, int32_t B, const float *scale,
+                                              int per_sample, const void *workspace, size_t workspace_bytes,
+                                              rnnt_stream_t stream);
 
 /*
  * Synchronises `stream`, then copies into *dev_flags the device status word

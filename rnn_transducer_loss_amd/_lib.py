@@ -26,7 +26,8 @@ RNNT_DEV_BAD_TARGET = 2
 EXPORTS = ("rnnt_loss_fused_workspace_size", "rnnt_loss_fused", "rnnt_grad_scale", "rnnt_loss_fused_check",
            "rnnt_status_string", "rnnt_plan_describe", "rnnt_timing_enable", "rnnt_timing_read",
            "rnnt_loss_padded_workspace_size", "rnnt_loss_padded", "rnnt_grad_scale_padded",
-           "rnnt_multiblank_workspace_size", "rnnt_multiblank_loss", "rnnt_multiblank_grad_scale")
+           "rnnt_multiblank_workspace_size", "rnnt_multiblank_loss", "rnnt_multiblank_grad_scale",
+           "rnnt_multiblank_padded_workspace_size", "rnnt_multiblank_loss_padded", "rnnt_multiblank_grad_scale_padded")
 KERNELS = ("rowstats", "alpha_beta", "grad", "reduce")
 
 _lib = None
@@ -92,6 +93,20 @@ def load():
         lib.rnnt_multiblank_grad_scale.argtypes = [_vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, _i32p, _i32p,
                                                    ctypes.c_int32, _vp, ctypes.c_int, _vp, ctypes.c_size_t, _vp]
         lib.rnnt_multiblank_grad_scale.restype = ctypes.c_int
+        lib.rnnt_multiblank_padded_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                              ctypes.c_int32, ctypes.c_int, _i32p, _i32p,
+                                                              ctypes.c_int32, _i32p, ctypes.POINTER(ctypes.c_size_t)]
+        lib.rnnt_multiblank_padded_workspace_size.restype = ctypes.c_int
+        lib.rnnt_multiblank_loss_padded.argtypes = [_vp, ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                    _vp, ctypes.c_int32, _i32p, _i32p, ctypes.c_int32,
+                                                    ctypes.c_int64, ctypes.c_int32, _i32p, _i32p, ctypes.c_float,
+                                                    ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp,
+                                                    _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        lib.rnnt_multiblank_loss_padded.restype = ctypes.c_int
+        lib.rnnt_multiblank_grad_scale_padded.argtypes = [_vp, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
+                                                          ctypes.c_int32, _i32p, _i32p, ctypes.c_int32, _vp,
+                                                          ctypes.c_int, _vp, ctypes.c_size_t, _vp]
+        lib.rnnt_multiblank_grad_scale_padded.restype = ctypes.c_int
         lib.rnnt_timing_enable.argtypes = [ctypes.c_int]
         lib.rnnt_timing_enable.restype = ctypes.c_int
         lib.rnnt_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), _i32p]
@@ -302,3 +317,50 @@ def grad_scale_multiblank(grad_ptr: int, dtype_code: int, N: int, V: int, logit_
                                            scale_ptr or None, int(bool(per_sample)), ws_ptr or None, ws_bytes,
                                            stream or None)
     check(rc, "rnnt_multiblank_grad_scale")
+
+
+def workspace_size_multiblank_padded(B: int, V: int, max_T: int, max_U1: int, dtype_code: int, logit_lengths,
+                                     target_lengths, big_blank_durations) -> int:
+    T = host_i32(logit_lengths)
+    U = host_i32(target_lengths)
+    if len(T) != B or len(U) != B:
+        raise ValueError("length vectors must have B entries")
+    dur = host_i32(big_blank_durations).reshape(-1)
+    nb = len(dur)
+    out = ctypes.c_size_t()
+    check(load().rnnt_multiblank_padded_workspace_size(B, V, max_T, max_U1, dtype_code, _p(T), _p(U), nb,
+                                                       _p(dur if nb else np.zeros(1, np.int32)), ctypes.byref(out)),
+          "rnnt_multiblank_padded_workspace_size")
+    return int(out.value)
+
+
+def loss_multiblank_padded(logits_ptr: int, dtype_code: int, max_T: int, max_U1: int, V: int, targets_ptr: int,
+                           S: int, logit_lengths, target_lengths, blank: int, big_blank_ids, big_blank_durations,
+                           sigma: float, clamp: float, fastemit_lambda: float, fused: bool, reduction: str,
+                           loss_ptr: int, loss_reduced_ptr: int, grad_ptr: int, ws_ptr: int, ws_bytes: int,
+                           stream: int):
+    T = host_i32(logit_lengths)
+    U = host_i32(target_lengths)
+    B = len(T)
+    if len(U) != B:
+        raise ValueError("length vectors must have B entries")
+    if reduction not in REDUCTIONS:
+        raise ValueError(f"reduction must be one of {sorted(REDUCTIONS)}")
+    nb, ids, dur = _big_blanks(big_blank_ids, big_blank_durations)
+    rc = load().rnnt_multiblank_loss_padded(logits_ptr or None, dtype_code, max_T, max_U1, V, targets_ptr or None, S,
+                                            _p(T), _p(U), B, int(blank), nb, _p(ids), _p(dur), float(sigma),
+                                            float(clamp), float(fastemit_lambda), int(bool(fused)),
+                                            REDUCTIONS[reduction], loss_ptr or None, loss_reduced_ptr or None,
+                                            grad_ptr or None, ws_ptr or None, ws_bytes, stream or None)
+    check(rc, "rnnt_multiblank_loss_padded")
+
+
+def grad_scale_multiblank_padded(grad_ptr: int, dtype_code: int, max_T: int, max_U1: int, V: int, logit_lengths,
+                                 target_lengths, scale_ptr: int, per_sample: bool, ws_ptr: int, ws_bytes: int,
+                                 stream: int):
+    T = host_i32(logit_lengths)
+    U = host_i32(target_lengths)
+    rc = load().rnnt_multiblank_grad_scale_padded(grad_ptr or None, dtype_code, max_T, max_U1, V, _p(T), _p(U),
+                                                  len(T), scale_ptr or None, int(bool(per_sample)), ws_ptr or None,
+                                                  ws_bytes, stream or None)
+    check(rc, "rnnt_multiblank_grad_scale_padded")

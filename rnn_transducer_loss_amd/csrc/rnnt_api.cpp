@@ -476,9 +476,15 @@ struct MbPlan {
 };
 
 rnnt_status build_mb_plan(int32_t B, int32_t V, int64_t N, const int32_t *T, const int32_t *U, int32_t nb,
-                          const int32_t *dur, MbPlan &p) {
+                          const int32_t *dur, MbPlan &p, const Padding &pad = Padding()) {
     rnnt_status st = check_lengths(B, V, T, U);
     if (st != RNNT_SUCCESS) return st;
+    if (pad.on()) {
+        if (pad.max_U1 < 1) return RNNT_INVALID_VALUE;
+        for (int32_t i = 0; i < B; ++i)
+            if (T[i] > pad.max_T || U[i] + 1 > pad.max_U1) return RNNT_INVALID_VALUE;
+        if ((int64_t)B * pad.max_T * pad.max_U1 >= ((int64_t)1 << 62) / std::max(1, V)) return RNNT_INVALID_VALUE;
+    }
     if (nb < 0 || nb > kMaxBigBlanks || (nb > 0 && !dur)) return RNNT_INVALID_VALUE;
     int dmax = 1;
     for (int32_t i = 0; i < nb; ++i) {
@@ -499,7 +505,9 @@ rnnt_status build_mb_plan(int32_t B, int32_t V, int64_t N, const int32_t *T, con
     int64_t row = 0, slot = 0, diag = 0, ab = 0;
     for (int32_t i = 0; i < B; ++i) {
         SampleDesc &d = p.desc[i];
-        d.row_off = row;
+        // packed: rows follow each other; padded: sample i's block starts at i * max_T * max_U1 and a frame
+        // is max_U1 rows
+        d.row_off = pad.on() ? (int64_t)i * pad.max_T * pad.max_U1 : row;
         d.slot_off = slot;
         d.diag_off = diag;
         d.ab_off = ab;
@@ -507,7 +515,7 @@ rnnt_status build_mb_plan(int32_t B, int32_t V, int64_t N, const int32_t *T, con
         d.U = U[i];
         d.index = i;
         d.U1p = U1p;
-        d.tstride = U[i] + 1;
+        d.tstride = pad.on() ? pad.max_U1 : U[i] + 1;
         d.chunk0 = 0;
         row += (int64_t)T[i] * (U[i] + 1);
         slot += ((int64_t)T[i] + U[i]) * (U[i] + 1);
@@ -516,12 +524,13 @@ rnnt_status build_mb_plan(int32_t B, int32_t V, int64_t N, const int32_t *T, con
     }
     if (N >= 0 && row != N) return RNNT_INVALID_VALUE;
     if (row >= ((int64_t)1 << 62) / std::max(1, V)) return RNNT_INVALID_VALUE;
+    const int64_t phys = pad.on() ? (int64_t)B * pad.max_T * pad.max_U1 : row;  // rows of logits and grad
     MbLayout &L = p.lay;
     size_t off = 0;
     L.status = 0;
     off = 256;
     L.desc = off;   off = align_up(off + sizeof(SampleDesc) * B);
-    L.den = off;    off = align_up(off + sizeof(float) * (size_t)row);
+    L.den = off;    off = align_up(off + sizeof(float) * (size_t)phys);
     // the sweep's 16-byte loads of a lane's column pair may reach one slot past a plane's last
     L.wp = off;     off = align_up(off + sizeof(double) * ((size_t)(2 + nb) * (size_t)slot + 2));
     L.alpha = off;  off = align_up(off + sizeof(double) * (size_t)ab);
@@ -532,6 +541,7 @@ rnnt_status build_mb_plan(int32_t B, int32_t V, int64_t N, const int32_t *T, con
     L.total = off;
     L.n_slots = slot;
     L.U1p = U1p;
+    L.rows = phys;
     return RNNT_SUCCESS;
 }
 
@@ -539,9 +549,11 @@ rnnt_status multiblank_impl(const void *logits, rnnt_dtype dtype, int64_t N, int
                             int32_t S, const int32_t *T, const int32_t *U, int32_t B, int64_t blank, int32_t nb,
                             const int32_t *ids, const int32_t *dur, float sigma, float clamp, float fastemit,
                             int fused, rnnt_reduction reduction, float *loss, float *loss_reduced, void *grad,
-                            void *workspace, size_t workspace_bytes, hipStream_t stream) {
+                            void *workspace, size_t workspace_bytes, hipStream_t stream,
+                            const Padding &pad = Padding()) {
     const int es = esize_of(dtype);
-    if (!es || V < 1 || B < 1 || N < 0) return RNNT_INVALID_VALUE;
+    if (!es || V < 1 || B < 1) return RNNT_INVALID_VALUE;
+    if (pad.on() ? (pad.max_U1 < 1) : (N < 0)) return RNNT_INVALID_VALUE;
     if (reduction != RNNT_REDUCTION_NONE && reduction != RNNT_REDUCTION_MEAN && reduction != RNNT_REDUCTION_SUM)
         return RNNT_INVALID_VALUE;
     if (blank < -(int64_t)V || blank > (int64_t)V - 1) return RNNT_INVALID_VALUE;
@@ -554,15 +566,16 @@ rnnt_status multiblank_impl(const void *logits, rnnt_dtype dtype, int64_t N, int
         for (int32_t j = 0; j < i; ++j)
             if (ids[j] == ids[i]) return RNNT_INVALID_VALUE;
     }
-    if (N > 0 && !logits) return RNNT_INVALID_VALUE;
+    const int64_t rows = pad.on() ? (int64_t)B * pad.max_T * pad.max_U1 : N;
+    if (rows > 0 && !logits) return RNNT_INVALID_VALUE;
     int32_t maxU = 0;
     for (int32_t i = 0; i < B; ++i) maxU = std::max(maxU, U[i]);
     if (maxU > 0 && (!targets || S < maxU)) return RNNT_INVALID_VALUE;
     if (S < 0) return RNNT_INVALID_VALUE;
-    const size_t bytes = (size_t)N * (size_t)V * (size_t)es;
+    const size_t bytes = (size_t)rows * (size_t)V * (size_t)es;
     if (grad && grad != logits && bytes > 0 && ranges_overlap(grad, bytes, logits, bytes)) return RNNT_INVALID_VALUE;
     MbPlan plan;
-    rnnt_status st = build_mb_plan(B, V, N, T, U, nb, dur, plan);
+    rnnt_status st = build_mb_plan(B, V, pad.on() ? -1 : N, T, U, nb, dur, plan, pad);
     if (st != RNNT_SUCCESS) return st;
     if (workspace_bytes < plan.lay.total) return RNNT_WORKSPACE_TOO_SMALL;
     if ((uintptr_t)workspace % kAlign != 0) return RNNT_INVALID_VALUE;
@@ -577,7 +590,7 @@ rnnt_status multiblank_impl(const void *logits, rnnt_dtype dtype, int64_t N, int
     a.logits = logits;
     a.grad = grad;
     a.esize = es;
-    a.N = N;
+    a.N = plan.lay.rows;
     a.V = V;
     a.B = B;
     a.S = S;
@@ -598,12 +611,43 @@ rnnt_status multiblank_impl(const void *logits, rnnt_dtype dtype, int64_t N, int
     a.reduction = reduction;
     a.ws = static_cast<uint8_t *>(workspace);
     a.lay = plan.lay;
-    if (N > 0 && timed(0, stream, [&] { return launch_mb_rows(a, stream); }) != hipSuccess)
+    if (a.N > 0 && timed(0, stream, [&] { return launch_mb_rows(a, stream); }) != hipSuccess)
         return RNNT_EXECUTION_FAILED;
     if (timed(1, stream, [&] { return launch_mb_sweep(a, stream); }) != hipSuccess) return RNNT_EXECUTION_FAILED;
-    if (grad && N > 0 && timed(2, stream, [&] { return launch_mb_grad(a, stream); }) != hipSuccess)
+    if (grad && a.N > 0 && timed(2, stream, [&] { return launch_mb_grad(a, stream); }) != hipSuccess)
         return RNNT_EXECUTION_FAILED;
     if (timed(3, stream, [&] { return launch_mb_reduce(a, stream); }) != hipSuccess) return RNNT_EXECUTION_FAILED;
+    return RNNT_SUCCESS;
+}
+
+// The multi-blank gradient's upstream scaling: the descriptors the loss call
+// left at byte 256 of its workspace give each sample's first row (packed, or
+// its padded block), which is all k_grad_scale reads.
+rnnt_status mb_grad_scale_impl(void *grad, rnnt_dtype dtype, int64_t N, int32_t V, const int32_t *T,
+                               const int32_t *U, int32_t B, const float *scale, int per_sample,
+                               const void *workspace, size_t workspace_bytes, hipStream_t stream,
+                               const Padding &pad) {
+    const int es = esize_of(dtype);
+    if (!es || !grad || !scale || !workspace || V < 1 || B < 1) return RNNT_INVALID_VALUE;
+    rnnt_status st = check_lengths(B, V, T, U);
+    if (st != RNNT_SUCCESS) return st;
+    int64_t rows = 0;
+    if (pad.on()) {
+        for (int32_t i = 0; i < B; ++i)
+            if (T[i] > pad.max_T || U[i] + 1 > pad.max_U1) return RNNT_INVALID_VALUE;
+        rows = (int64_t)B * pad.max_T * pad.max_U1;
+    } else {
+        for (int32_t i = 0; i < B; ++i) rows += (int64_t)T[i] * (U[i] + 1);
+        if (rows != N) return RNNT_INVALID_VALUE;
+    }
+    WorkspaceLayout L{};
+    L.desc = 256;  // where build_mb_plan puts the descriptors
+    if (workspace_bytes < L.desc + sizeof(SampleDesc) * (size_t)B) return RNNT_WORKSPACE_TOO_SMALL;
+    if (rows == 0) return RNNT_SUCCESS;
+    const bool aligned16 = ((int64_t)V * es) % 16 == 0 && (uintptr_t)grad % 16 == 0;
+    if (launch_grad_scale(grad, es, V, rows, B, scale, per_sample, static_cast<const uint8_t *>(workspace), L,
+                          row_geometry(V, es, aligned16), stream) != hipSuccess)
+        return RNNT_EXECUTION_FAILED;
     return RNNT_SUCCESS;
 }
 
@@ -716,26 +760,59 @@ rnnt_status rnnt_multiblank_loss(const void *logits, rnnt_dtype dtype, int64_t N
                            static_cast<hipStream_t>(stream));
 }
 
+rnnt_status rnnt_multiblank_padded_workspace_size(int32_t B, int32_t V, int32_t max_T, int32_t max_U1,
+                                                  rnnt_dtype dtype, const int32_t *logit_lengths,
+                                                  const int32_t *target_lengths, int32_t num_big_blanks,
+                                                  const int32_t *big_blank_durations, size_t *workspace_bytes) {
+    if (!esize_of(dtype) || !workspace_bytes || max_T < 1 || max_U1 < 1) return RNNT_INVALID_VALUE;
+    Padding pad;
+    pad.max_T = max_T;
+    pad.max_U1 = max_U1;
+    MbPlan p;
+    rnnt_status st = build_mb_plan(B, V, -1, logit_lengths, target_lengths, num_big_blanks, big_blank_durations, p,
+                                   pad);
+    if (st != RNNT_SUCCESS) return st;
+    *workspace_bytes = p.lay.total;
+    return RNNT_SUCCESS;
+}
+
+rnnt_status rnnt_multiblank_loss_padded(const void *logits, rnnt_dtype dtype, int32_t max_T, int32_t max_U1,
+                                        int32_t V, const int32_t *targets, int32_t S, const int32_t *logit_lengths,
+                                        const int32_t *target_lengths, int32_t B, int64_t blank,
+                                        int32_t num_big_blanks, const int32_t *big_blank_ids,
+                                        const int32_t *big_blank_durations, float sigma, float clamp,
+                                        float fastemit_lambda, int fused_log_softmax, rnnt_reduction reduction,
+                                        float *loss, float *loss_reduced, void *grad, void *workspace,
+                                        size_t workspace_bytes, rnnt_stream_t stream) {
+    if (max_T < 1 || max_U1 < 1) return RNNT_INVALID_VALUE;
+    Padding pad;
+    pad.max_T = max_T;
+    pad.max_U1 = max_U1;
+    return multiblank_impl(logits, dtype, -1, V, targets, S, logit_lengths, target_lengths, B, blank, num_big_blanks,
+                           big_blank_ids, big_blank_durations, sigma, clamp, fastemit_lambda, fused_log_softmax,
+                           reduction, loss, loss_reduced, grad, workspace, workspace_bytes,
+                           static_cast<hipStream_t>(stream), pad);
+}
+
 rnnt_status rnnt_multiblank_grad_scale(void *grad, rnnt_dtype dtype, int64_t N, int32_t V,
                                        const int32_t *logit_lengths, const int32_t *target_lengths, int32_t B,
                                        const float *scale, int per_sample, const void *workspace,
                                        size_t workspace_bytes, rnnt_stream_t stream) {
-    const int es = esize_of(dtype);
-    if (!es || !grad || !scale || !workspace || V < 1 || B < 1 || N < 0) return RNNT_INVALID_VALUE;
-    rnnt_status st = check_lengths(B, V, logit_lengths, target_lengths);
-    if (st != RNNT_SUCCESS) return st;
-    int64_t rows = 0;
-    for (int32_t i = 0; i < B; ++i) rows += (int64_t)logit_lengths[i] * (target_lengths[i] + 1);
-    if (rows != N) return RNNT_INVALID_VALUE;
-    WorkspaceLayout L{};
-    L.desc = 256;  // where build_mb_plan puts the descriptors
-    if (workspace_bytes < L.desc + sizeof(SampleDesc) * (size_t)B) return RNNT_WORKSPACE_TOO_SMALL;
-    if (N == 0) return RNNT_SUCCESS;
-    const bool aligned16 = ((int64_t)V * es) % 16 == 0 && (uintptr_t)grad % 16 == 0;
-    if (launch_grad_scale(grad, es, V, N, B, scale, per_sample, static_cast<const uint8_t *>(workspace), L,
-                          row_geometry(V, es, aligned16), static_cast<hipStream_t>(stream)) != hipSuccess)
-        return RNNT_EXECUTION_FAILED;
-    return RNNT_SUCCESS;
+    return mb_grad_scale_impl(grad, dtype, N, V, logit_lengths, target_lengths, B, scale, per_sample, workspace,
+                              workspace_bytes, static_cast<hipStream_t>(stream), Padding());
+}
+
+rnnt_status rnnt_multiblank_grad_scale_padded(void *grad, rnnt_dtype dtype, int32_t max_T, int32_t max_U1,
+                                              int32_t V, const int32_t *logit_lengths,
+                                              const int32_t *target_lengths, int32_t B, const float *scale,
+                                              int per_sample, const void *workspace, size_t workspace_bytes,
+                                              rnnt_stream_t stream) {
+    if (max_T < 1 || max_U1 < 1) return RNNT_INVALID_VALUE;
+    Padding pad;
+    pad.max_T = max_T;
+    pad.max_U1 = max_U1;
+    return mb_grad_scale_impl(grad, dtype, -1, V, logit_lengths, target_lengths, B, scale, per_sample, workspace,
+                              workspace_bytes, static_cast<hipStream_t>(stream), pad);
 }
 
 rnnt_status rnnt_timing_enable(int on) {

@@ -197,6 +197,7 @@ constexpr size_t kMbRingBytes = 64 * 1024;  // LDS of one sweep: the last (longe
 struct MbLayout {
     size_t status, desc, den, wp, alpha, beta, ealpha, ebeta, log2z, total;
     int64_t n_slots;    // skewed node slots, sum_i (T_i+U_i)(U_i+1)
+    int64_t rows;       // rows of logits and grad: sum_i T_i(U_i+1) packed, B * max_T * max_U1 padded
     int U1p;            // columns of one stored diagonal: 128 times a power of two, for every sample
 };
 

@@ -1545,8 +1545,9 @@ __global__ __launch_bounds__(256) void k_mb_rows(const T *__restrict__ logits, i
     const SampleDesc d = mb_sample_of_row(desc, B, r);
     const int U1 = d.U + 1;
     const int64_t lr = r - d.row_off;
-    const int t = (int)(lr / U1);
-    const int u = (int)(lr - (int64_t)t * U1);
+    const int t = (int)(lr / d.tstride);
+    const int u = (int)(lr - (int64_t)t * d.tstride);
+    if (t >= d.T || u > d.U) return;  // a padding row of the padded layout
     const T *x = logits + r * (int64_t)V;
     float dn = 0.f;
     if (fused) {
@@ -1842,7 +1843,7 @@ struct MbRowTerms {
     int y;
 };
 
-__device__ __forceinline__ MbRowTerms mb_row_terms(const SampleDesc &d, int64_t r, int V, int fused,
+__device__ __forceinline__ MbRowTerms mb_row_terms(const SampleDesc &d, int64_t r, int t, int u, int V, int fused,
                                                    const MbParams &mp, int U1p, const int32_t *__restrict__ targets,
                                                    int S, const float *__restrict__ den,
                                                    const double *__restrict__ wp, int64_t n_slots,
@@ -1851,9 +1852,6 @@ __device__ __forceinline__ MbRowTerms mb_row_terms(const SampleDesc &d, int64_t 
                                                    const int *__restrict__ ebeta, const double *__restrict__ log2z,
                                                    float scale, float fastemit) {
     const int U1 = d.U + 1;
-    const int64_t lr = r - d.row_off;
-    const int t = (int)(lr / U1);
-    const int u = (int)(lr - (int64_t)t * U1);
     const int n = t + u;
     const int64_t s = d.slot_off + (int64_t)n * U1 + u;
     const int64_t eo = d.diag_off + d.index;
@@ -1912,12 +1910,19 @@ __global__ __launch_bounds__(256) void k_mb_grad(const T *__restrict__ logits, T
     const int64_t r = row_base + (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (r >= N) return;
     const SampleDesc d = mb_sample_of_row(desc, B, r);
-    const MbRowTerms rt = mb_row_terms(d, r, V, fused, mp, U1p, targets, S, den, wp, n_slots, alpha, beta, ealpha,
-                                       ebeta, log2z, scale, fastemit);
+    const int64_t lr = r - d.row_off;
+    const int t = (int)(lr / d.tstride);
+    const int u = (int)(lr - (int64_t)t * d.tstride);
+    T *g = grad + r * (int64_t)V;
+    if (t >= d.T || u > d.U) {  // a padding row of the padded layout: zero gradient
+        for (int k = lane; k < V; k += 64) Elem<T>::store1(g + k, 0.f);
+        return;
+    }
+    const MbRowTerms rt = mb_row_terms(d, r, t, u, V, fused, mp, U1p, targets, S, den, wp, n_slots, alpha, beta,
+                                       ealpha, ebeta, log2z, scale, fastemit);
     const bool do_clamp = clamp > 0.f;
     const float cl = clamp * scale;
     const T *x = logits + r * (int64_t)V;
-    T *g = grad + r * (int64_t)V;
     for (int k = lane; k < V; k += 64) {
         float v = 0.f;
         if (fused) v = exp2_fast(fmaf(Elem<T>::load1(x + k), kLog2e, rt.shift2));
@@ -1946,8 +1951,9 @@ __global__ __launch_bounds__(64) void k_mb_rows_v(const T *__restrict__ logits, 
     const SampleDesc d = mb_sample_of_row(desc, B, r);
     const int U1 = d.U + 1;
     const int64_t lr = r - d.row_off;
-    const int t = (int)(lr / U1);
-    const int u = (int)(lr - (int64_t)t * U1);
+    const int t = (int)(lr / d.tstride);
+    const int u = (int)(lr - (int64_t)t * d.tstride);
+    if (t >= d.T || u > d.U) return;  // a padding row of the padded layout
     const T *x = logits + r * (int64_t)V;
     const int nvec = V / VEC;
     float dn = 0.f;
@@ -2017,6 +2023,17 @@ __global__ __launch_bounds__(64) void k_mb_grad_v(const T *__restrict__ logits, 
     if (r >= N) return;
     const SampleDesc d = mb_sample_of_row(desc, B, r);
     const int nvec = V / VEC;
+    const int64_t lr = r - d.row_off;
+    const int t = (int)(lr / d.tstride);
+    const int u = (int)(lr - (int64_t)t * d.tstride);
+    T *g = grad + r * (int64_t)V;
+    if (t >= d.T || u > d.U) {  // a padding row of the padded layout: zero gradient
+        float z[VEC] = {};
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            if (i * 64 + lane < nvec) store_raw<T, true>(g + (int64_t)(i * 64 + lane) * VEC, Raw<T>::put(z));
+        return;
+    }
     Vec xv[NV];
     if (fused) {
         const T *x = logits + r * (int64_t)V;
@@ -2024,11 +2041,10 @@ __global__ __launch_bounds__(64) void k_mb_grad_v(const T *__restrict__ logits, 
         for (int i = 0; i < NV; ++i)
             if (i * 64 + lane < nvec) xv[i] = load_raw<T, true>(x + (int64_t)(i * 64 + lane) * VEC);
     }
-    MbRowTerms rt = mb_row_terms(d, r, V, fused, mp, U1p, targets, S, den, wp, n_slots, alpha, beta, ealpha, ebeta,
-                                 log2z, scale, fastemit);
+    MbRowTerms rt = mb_row_terms(d, r, t, u, V, fused, mp, U1p, targets, S, den, wp, n_slots, alpha, beta, ealpha,
+                                 ebeta, log2z, scale, fastemit);
     const bool do_clamp = clamp > 0.f;
     const float cl = clamp * scale;
-    T *g = grad + r * (int64_t)V;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int vi = i * 64 + lane;

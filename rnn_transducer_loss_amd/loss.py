@@ -199,15 +199,13 @@ def rnnt_multiblank_fused(logits: torch.Tensor, targets: torch.Tensor, logit_len
                           fastemit_lambda: float = 0.0, compute_grad: bool = True,
                           grad: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                           loss: Optional[torch.Tensor] = None, loss_reduced: Optional[torch.Tensor] = None):
-    """One multi-blank librnnt call over packed logits.  Returns ``(loss, loss_reduced, grad, workspace)``.
+    """One multi-blank librnnt call.  Returns ``(loss, loss_reduced, grad, workspace)``.
 
     Big blank i is class ``big_blank_ids[i]`` and advances t by ``big_blank_durations[i]`` frames; ``sigma`` is
-    subtracted from every emission's log-probability (logit under-normalisation).  The rest is as for
-    :func:`rnnt_loss_fused`.
+    subtracted from every emission's log-probability (logit under-normalisation).  Packed 2-D or padded 4-D
+    logits, the rest as for :func:`rnnt_loss_fused`.
     """
     tg = _prepare(logits, targets)
-    if logits.dim() != 2:
-        raise ValueError("the multi-blank loss takes packed 2-D (sum_i T_i*(U_i+1), V) logits")
     T = _lib.host_i32(logit_lengths)
     U = _lib.host_i32(target_lengths)
     B = len(T)
@@ -215,8 +213,15 @@ def rnnt_multiblank_fused(logits: torch.Tensor, targets: torch.Tensor, logit_len
         raise ValueError("logit_lengths and target_lengths must have the same length")
     dev = logits.device
     code = _dtype_code(logits.dtype)
-    N, V = logits.shape
-    need = _lib.workspace_size_multiblank(B, V, N, code, T, U, big_blank_durations)
+    padded = logits.dim() == 4
+    if padded:
+        if logits.shape[0] != B:
+            raise ValueError("padded logits must have one (max_T, max_U+1, V) block per sample")
+        max_T, max_U1, V = logits.shape[1], logits.shape[2], logits.shape[3]
+        need = _lib.workspace_size_multiblank_padded(B, V, max_T, max_U1, code, T, U, big_blank_durations)
+    else:
+        N, V = logits.shape
+        need = _lib.workspace_size_multiblank(B, V, N, code, T, U, big_blank_durations)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     if loss is None:
@@ -232,12 +237,18 @@ def rnnt_multiblank_fused(logits: torch.Tensor, targets: torch.Tensor, logit_len
         grad = None
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        _lib.loss_multiblank(logits.data_ptr(), code, N, V, tg.data_ptr() if tg.numel() else 0, tg.shape[1], T, U,
-                             blank, big_blank_ids, big_blank_durations, sigma, clamp, fastemit_lambda,
-                             fused_log_softmax, reduction, loss.data_ptr(),
-                             loss_reduced.data_ptr() if reduction != "none" else 0,
-                             grad.data_ptr() if grad is not None else 0, workspace.data_ptr(), workspace.numel(),
-                             stream)
+        tgp = tg.data_ptr() if tg.numel() else 0
+        redp = loss_reduced.data_ptr() if reduction != "none" else 0
+        gp = grad.data_ptr() if grad is not None else 0
+        if padded:
+            _lib.loss_multiblank_padded(logits.data_ptr(), code, max_T, max_U1, V, tgp, tg.shape[1], T, U, blank,
+                                        big_blank_ids, big_blank_durations, sigma, clamp, fastemit_lambda,
+                                        fused_log_softmax, reduction, loss.data_ptr(), redp, gp,
+                                        workspace.data_ptr(), workspace.numel(), stream)
+        else:
+            _lib.loss_multiblank(logits.data_ptr(), code, N, V, tgp, tg.shape[1], T, U, blank, big_blank_ids,
+                                 big_blank_durations, sigma, clamp, fastemit_lambda, fused_log_softmax, reduction,
+                                 loss.data_ptr(), redp, gp, workspace.data_ptr(), workspace.numel(), stream)
     return loss, (loss_reduced if reduction != "none" else None), grad, workspace
 
 
@@ -269,8 +280,13 @@ class _MultiblankFunction(torch.autograd.Function):
         scale = grad_out.detach().to(device=grad.device, dtype=torch.float32).contiguous().reshape(-1)
         with torch.cuda.device(grad.device):
             stream = torch.cuda.current_stream(grad.device).cuda_stream
-            _lib.grad_scale_multiblank(grad.data_ptr(), _dtype_code(dtype), shape[0], shape[1], T, U,
-                                       scale.data_ptr(), reduction == "none", ws.data_ptr(), ws.numel(), stream)
+            if len(shape) == 4:
+                _lib.grad_scale_multiblank_padded(grad.data_ptr(), _dtype_code(dtype), shape[1], shape[2], shape[3],
+                                                  T, U, scale.data_ptr(), reduction == "none", ws.data_ptr(),
+                                                  ws.numel(), stream)
+            else:
+                _lib.grad_scale_multiblank(grad.data_ptr(), _dtype_code(dtype), shape[0], shape[1], T, U,
+                                           scale.data_ptr(), reduction == "none", ws.data_ptr(), ws.numel(), stream)
         return (grad,) + none
 
 
@@ -278,7 +294,7 @@ def rnnt_loss_multiblank(logits: torch.Tensor, targets: torch.Tensor, logit_leng
                          big_blank_durations, big_blank_ids, blank: int = -1, sigma: float = 0.0,
                          clamp: float = -1.0, reduction: str = "mean", fused_log_softmax: bool = True,
                          fastemit_lambda: float = 0.0) -> torch.Tensor:
-    """Multi-blank transducer loss over packed logits, differentiable with respect to ``logits``.
+    """Multi-blank transducer loss over packed (or padded 4-D) logits, differentiable with respect to ``logits``.
 
     ``big_blank_durations[i]`` is the number of frames big blank i (class ``big_blank_ids[i]``) advances;
     ``sigma`` lowers every emission's log-probability (logit under-normalisation).  With no big blank and

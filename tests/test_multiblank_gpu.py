@@ -251,3 +251,63 @@ def test_multiblank_random_option_sweep(rl, seed):
     loss, red, grad, flags = run_mb(rl, w, fastemit=lam)
     assert flags == 0
     check_mb(w, loss, grad, reduction, fastemit=lam)
+
+
+def _padded(w, max_T, max_U1, fill=float("nan")):
+    x = torch.full((w.B, max_T, max_U1, w.V), fill, dtype=w.logits.dtype, device=w.logits.device)
+    for i in range(w.B):
+        T, U = int(w.logit_lengths[i]), int(w.target_lengths[i])
+        x[i, :T, :U + 1] = w.logits[w.rows(i)].reshape(T, U + 1, w.V)
+    return x
+
+
+def _unpad(w, g, max_T, max_U1):
+    valid = torch.zeros((w.B, max_T, max_U1), dtype=torch.bool, device=g.device)
+    parts = []
+    for i in range(w.B):
+        T, U = int(w.logit_lengths[i]), int(w.target_lengths[i])
+        valid[i, :T, :U + 1] = True
+        parts.append(g[i, :T, :U + 1].reshape(-1, w.V))
+    return torch.cat(parts), g[~valid]
+
+
+@pytest.mark.parametrize("V,dtype,fused", [(64, torch.float32, True), (33, torch.float32, True),
+                                           (256, torch.float16, False)])
+def test_multiblank_padded_matches_packed(rl, V, dtype, fused):
+    # padded (B, max_T, max_U+1, V) logits (NaN padding, never read): the packed call's losses and, row for row,
+    # its gradient bits; the padding rows get a zero gradient
+    Ts, Us = [30, 12, 1, 19], [6, 0, 4, 9]
+    w = _mb(Ts, Us, V, [V - 2, V - 3], [2, 5], 0.05, dtype=dtype, std=2.0 if fused else 1.5, blank=-1, fused=fused,
+            prenormalise=not fused, reduction="sum", seed=V + 7)
+    max_T, max_U1 = max(Ts) + 2, max(Us) + 3
+    xp = _padded(w, max_T, max_U1)
+    tg = torch.from_numpy(w.targets).to("cuda")
+    loss_p, red_p, grad_p, ws = rl.rnnt_multiblank_fused(xp, tg, w.logit_lengths, w.target_lengths, w.big_blank_ids,
+                                                         w.big_blank_durations, blank=w.blank, sigma=w.sigma,
+                                                         reduction="sum", fused_log_softmax=fused)
+    assert rl.device_flags(ws) == 0
+    loss, red, grad, _ = run_mb(rl, w)
+    torch.cuda.synchronize()
+    assert torch.equal(loss_p, loss) and torch.equal(red_p, red)
+    rows, pad = _unpad(w, grad_p, max_T, max_U1)
+    assert torch.equal(rows, grad)
+    assert pad.numel() > 0 and bool((pad == 0).all())
+    check_mb(w, loss, grad, "sum")
+
+
+def test_multiblank_padded_autograd(rl):
+    Ts, Us = [22, 9, 15], [5, 2, 7]
+    w = _mb(Ts, Us, 48, [45, 46], [3, 2], 0.1, std=2.0, blank=-1, reduction="none", seed=47)
+    tg = torch.from_numpy(w.targets).to("cuda")
+    xp = _padded(w, 24, 9, fill=0.0)
+    ref_loss, _, ref_grad, _ = rl.rnnt_multiblank_fused(xp, tg, w.logit_lengths, w.target_lengths, w.big_blank_ids,
+                                                        w.big_blank_durations, blank=-1, sigma=w.sigma,
+                                                        reduction="none")
+    x = xp.clone().requires_grad_(True)
+    out = rl.rnnt_loss_multiblank(x, tg, w.logit_lengths, w.target_lengths, w.big_blank_durations, w.big_blank_ids,
+                                  blank=-1, sigma=w.sigma, reduction="none")
+    up = torch.tensor([0.5, -2.0, 3.0], device="cuda")
+    out.backward(up)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach(), ref_loss)
+    assert torch.allclose(x.grad, ref_grad * up.view(-1, 1, 1, 1), rtol=1e-6, atol=0)
