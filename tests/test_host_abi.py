@@ -242,3 +242,20 @@ def test_multiblank_ring_limit():
     with pytest.raises(ValueError):
         _lib.workspace_size_multiblank(1, 8, N, 0, T, U, [7])
     assert _lib.workspace_size_multiblank(1, 8, 3 * 200, 0, T, np.array([199], np.int32), [16]) > 0
+
+
+def test_multiblank_padded_sizes_and_limits():
+    T = np.array([4, 6, 3], np.int32)
+    U = np.array([2, 1, 5], np.int32)
+    N = int((T * (U + 1)).sum())
+    packed = _lib.workspace_size_multiblank(3, 32, N, _lib.RNNT_F32, T, U, [2, 3])
+    padded = _lib.workspace_size_multiblank_padded(3, 32, 6, 6, _lib.RNNT_F32, T, U, [2, 3])
+    # the padded layout only adds the per-row normalisers of its padding rows
+    assert padded - packed == (lambda b: (b + 255) // 256 * 256)(4 * 3 * 6 * 6) - \
+        (lambda b: (b + 255) // 256 * 256)(4 * N)
+    for max_T, max_U1 in ((5, 6), (6, 5), (0, 6)):   # a sample does not fit, or an empty extent
+        with pytest.raises(ValueError):
+            _lib.workspace_size_multiblank_padded(3, 32, max_T, max_U1, _lib.RNNT_F32, T, U, [2, 3])
+    with pytest.raises(ValueError):
+        _lib.loss_multiblank_padded(0x100000, 0, 6, 5, 32, 0x200000, 5, T, U, -1, [30], [2], 0.0, -1.0, 0.0, True,
+                                    "sum", 0x300000, 0x400000, 0x500000, 0x600000, 1 << 20, 0)
