@@ -1528,6 +1528,39 @@ __device__ __forceinline__ double readlane_d(double v, int l) {
     return __hiloint2double(hi, lo);
 }
 
+// The 2 + nb weights of node (t,u): lane k < 2 + nb stores plane k's, `v`
+// its log-probability (less sigma).  Edges that leave the lattice are stored
+// as probability zero — the blank out of the last frame below column U, a
+// big blank that passes T or reaches it below column U (the label at
+// column U arrives as -inf) — and the slots outside the lattice are zeroed,
+// one contiguous run per anti-diagonal: node (0,u) zeroes columns u+1..U of
+// diagonal u (t < 0), node (T-1,u) columns 0..u of diagonal T+u (t >= T).
+// So the sweep reads no slot it must mask.
+__device__ __forceinline__ void mb_store_node(const SampleDesc &d, int t, int u, const MbParams &mp, int lane,
+                                              float v, double *__restrict__ wp, int64_t n_slots) {
+    const int U1 = d.U + 1;
+    const int np = 2 + mp.nb;
+    if (lane < np) {
+        bool gone = (lane == 0) && (t == d.T - 1) && (u < d.U);
+#pragma unroll
+        for (int i = 0; i < kMaxBigBlanks; ++i) {
+            const int te = t + mp.dur[i];
+            if (lane == 2 + i) gone = te > d.T || (te == d.T && u < d.U);
+        }
+        wp[(int64_t)lane * n_slots + d.slot_off + (int64_t)(t + u) * U1 + u] = gone ? 0.0 : prob_d(v);
+    }
+    if (t == 0 && u < d.U) {
+        const int len = d.U - u;  // columns u+1 .. U of anti-diagonal u
+        for (int q = lane; q < len * np; q += 64)
+            wp[(int64_t)(q / len) * n_slots + d.slot_off + (int64_t)u * U1 + u + 1 + q % len] = 0.0;
+    }
+    if (t == d.T - 1 && u < d.U) {
+        const int len = u + 1;  // columns 0 .. u of anti-diagonal T+u
+        for (int q = lane; q < len * np; q += 64)
+            wp[(int64_t)(q / len) * n_slots + d.slot_off + (int64_t)(d.T + u) * U1 + q % len] = 0.0;
+    }
+}
+
 // One wave per packed row, four per workgroup: the row's log-normaliser
 // (fused) and the probabilities, in fp64, of the edges leaving the node
 // (their log-probabilities less sigma, exponentiated), at its skewed slot:
@@ -1561,6 +1594,7 @@ __global__ __launch_bounds__(256) void k_mb_rows(const T *__restrict__ logits, i
         dn = (m == kNegInf) ? kNegInf : m + log2_fast(sum) * kLn2;
     }
     if (lane == 0) den[r] = dn;
+    float v = kNegInf;
     if (lane < 2 + mp.nb) {
         int k = blank;
         if (lane == 1) {
@@ -1577,9 +1611,9 @@ __global__ __launch_bounds__(256) void k_mb_rows(const T *__restrict__ logits, i
 #pragma unroll
         for (int i = 0; i < kMaxBigBlanks; ++i)
             if (lane == 2 + i) k = mp.ids[i];
-        const float v = (k >= 0 && dn != kNegInf) ? Elem<T>::load1(x + k) - dn - mp.sigma : kNegInf;
-        wp[(int64_t)lane * n_slots + d.slot_off + (int64_t)(t + u) * U1 + u] = prob_d(v);
+        v = (k >= 0 && dn != kNegInf) ? Elem<T>::load1(x + k) - dn - mp.sigma : kNegInf;
     }
+    mb_store_node(d, t, u, mp, lane, v, wp, n_slots);
 }
 
 // One wave per (sample, direction): blockIdx 2i runs alpha of sample i,
@@ -1634,44 +1668,39 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
     auto ring_at = [&](int sslot, int g) -> D2 * {
         return reinterpret_cast<D2 *>(mb_ring + (size_t)(sslot * G + g) * 128) + lane;
     };
-    // one resource per plane over the sample's slots (nd diagonals of U1), so
-    // the 16-byte loads of the last pair of the last diagonal stay in range
-    const uint32_t span = (uint32_t)nd * (uint32_t)U1 * 8u;
-    Rsrc rs[NW];
+    uint32_t vo[G];  // byte offset of the lane's first column in a diagonal
 #pragma unroll
-    for (int k = 0; k < NW; ++k) rs[k] = buffer_at(wp + (int64_t)k * n_slots + d.slot_off, span);
-    uint32_t vo[G];  // byte offset of the lane's first column, clamped into the lattice
-#pragma unroll
-    for (int g = 0; g < G; ++g) vo[g] = (uint32_t)min(128 * g + 2 * lane, U) * 8u;
+    for (int g = 0; g < G; ++g) vo[g] = (uint32_t)(128 * g + 2 * lane) * 8u;
     double *tab = (bw ? beta : alpha) + d.ab_off;
     int *etab = (bw ? ebeta : ealpha) + d.diag_off + d.index;
 
-    // soff is wave-uniform; readfirstlane keeps it in a scalar register even
-    // where the compiler computes it with vector instructions
-    auto ld = [&](int k, uint32_t voff, uint32_t soff) -> D2 {
-        const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane((int)soff);
-        return as_d2(__builtin_amdgcn_raw_buffer_load_b128(rs[k], voff, so, 0));
+    // One buffer resource per plane and diagonal, U1 slots long: its range
+    // check returns zero for the columns past U, so those lanes' weights are
+    // zero without a test.  The diagonal index is wave-uniform (readfirstlane
+    // keeps it scalar where the compiler forms it with vector instructions).
+    auto ld = [&](int k, int diag, uint32_t voff) -> D2 {
+        const int dg = __builtin_amdgcn_readfirstlane(diag);
+        const Rsrc r = buffer_at(wp + (int64_t)k * n_slots + d.slot_off + (int64_t)dg * U1, (uint32_t)U1 * 8u);
+        return as_d2(__builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
     };
     // The probabilities step `step` uses, for the lane's two columns (steps
     // past the end load the last step's again; never used).  Forward,
     // diagonal n pulls from n-1 (blank at column u; the label from u-1, moved
     // over by one column below) and n-d_i; backward, every edge leaves the
-    // node itself.
+    // node itself.  A big blank's source diagonal before 0 reads diagonal 0;
+    // its term is cancelled through the exponent.
     auto load_w = [&](int step, D2 (&w)[G][NW]) {
         const int n = bw ? nd - min(step, nd) : min(step, nd);
-        const uint32_t row = 8u * (uint32_t)U1;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             if (!bw) {
-                const uint32_t sp = (uint32_t)(n - 1) * row;
-                w[g][0] = ld(0, vo[g], sp);
-                w[g][1] = ld(1, vo[g], sp);
+                w[g][0] = ld(0, n - 1, vo[g]);
+                w[g][1] = ld(1, n - 1, vo[g]);
 #pragma unroll
-                for (int i = 0; i < NB; ++i) w[g][2 + i] = ld(2 + i, vo[g], (uint32_t)max(n - mp.dur[i], 0) * row);
+                for (int i = 0; i < NB; ++i) w[g][2 + i] = ld(2 + i, max(n - mp.dur[i], 0), vo[g]);
             } else {
-                const uint32_t sc = (uint32_t)n * row;
 #pragma unroll
-                for (int k = 0; k < NW; ++k) w[g][k] = ld(k, vo[g], sc);
+                for (int k = 0; k < NW; ++k) w[g][k] = ld(k, n, vo[g]);
             }
         }
     };
@@ -1698,16 +1727,18 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
     auto step_once = [&](int step, const D2 (&w)[G][NW]) {
         const int n = bw ? nd - step : step;
         slot = bw ? (slot == 0 ? R - 1 : slot - 1) : (slot + 1 == R ? 0 : slot + 1);
-        // big blanks: source diagonal's ring slot and exponent relative to E
+        // big blanks: source diagonal's ring slot and exponent relative to E;
+        // a source diagonal outside [0, nd] gets an exponent that scales its
+        // term to zero (its ring slot holds zeros or an older diagonal)
         int sl[NB > 0 ? NB : 1], shg[NB > 0 ? NB : 1];
-        bool okd[NB > 0 ? NB : 1];
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             const int dd = mp.dur[i];  // 1 <= dd < R
-            okd[i] = bw ? n + dd <= nd : n - dd >= 0;
+            const bool okd = bw ? n + dd <= nd : n - dd >= 0;
             const int q = bw ? slot + dd : slot - dd;
             sl[i] = bw ? (q >= R ? q - R : q) : (q < 0 ? q + R : q);
-            shg[i] = (ering[sl[i]] - E) * (int)okd[i];  // arithmetic, so the read is never skipped
+            const int eg = ering[sl[i]] - E;
+            shg[i] = okd ? eg : -4096;
         }
         // Cross-lane neighbours.  Forward: column 2l-1 of the finished
         // diagonal and the label weight of column 2l-1 come from lane l-1's
@@ -1737,38 +1768,27 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
             D2 src[NB > 0 ? NB : 1];
 #pragma unroll
             for (int i = 0; i < NB; ++i) src[i] = *ring_at(sl[i], g);
+            // No masks: every weight of an edge that does not exist is zero
+            // (outside-lattice slots and lattice-leaving edges stored as zero
+            // by the row pass, columns past U zeroed by the range check), so
+            // nodes outside the lattice come out zero by themselves.
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int u = 128 * g + 2 * lane + h;
-                const int t = n - u;
-                bool cell, okb, oky;
-                if (!bw) {
-                    cell = (u <= U) && ((t >= 0 && t <= T - 1) || (t == T && u == U));
-                    okb = (t >= 1) && (t <= T);                  // from (t-1,u)
-                    oky = (u >= 1) && (t >= 0) && (t <= T - 1);  // from (t,u-1)
-                } else {
-                    cell = (u <= U) && (t >= 0) && (t <= T - 1);
-                    okb = cell;                                  // to (t+1,u)
-                    oky = cell && (u < U);                       // to (t,u+1)
-                }
                 const double wb = h ? w[g][0].b : w[g][0].a;
                 const double cv = h ? cur[g].b : cur[g].a;
                 // label: forward, weight of column u-1 and value of column u-1; backward, own weight and u+1
                 const double wy = bw ? (h ? w[g][1].b : w[g][1].a) : (h ? w[g][1].a : side_w[g]);
                 const double sv = bw ? (h ? side_v[g] : cur[g].b) : (h ? cur[g].a : side_v[g]);
-                double acc = (okb ? wb : 0.0) * cv;
-                acc = fma(oky ? wy : 0.0, sv, acc);
+                double acc = fma(wy, sv, wb * cv);
 #pragma unroll
                 for (int i = 0; i < NB; ++i) {
-                    // forward from (t-d_i,u); backward to (t+d_i,u), zero where that is no node
-                    const int ts = t - mp.dur[i];
-                    const bool ok = okd[i] && (bw ? cell : (ts >= 0 && ts <= T - 1));
+                    // forward from (t-d_i,u); backward to (t+d_i,u)
                     const double wg = h ? w[g][2 + i].b : w[g][2 + i].a;
                     const double sr = h ? src[i].b : src[i].a;
-                    acc = fma(ok ? wg : 0.0, __builtin_amdgcn_ldexp(sr, shg[i]), acc);
+                    acc = fma(wg, __builtin_amdgcn_ldexp(sr, shg[i]), acc);
                 }
-                if (h) nx[g].b = cell ? acc : 0.0;
-                else nx[g].a = cell ? acc : 0.0;
+                if (h) nx[g].b = acc;
+                else nx[g].a = acc;
             }
         }
         // renormalise by a power of two (a diagonal of zeros keeps its exponent)
@@ -1937,7 +1957,7 @@ __global__ __launch_bounds__(256) void k_mb_grad(const T *__restrict__ logits, T
 // The row passes with the row held in 16-byte vectors, lane l holding
 // vectors l + 64i, i < NV (16-byte aligned rows of at most NV KiB), one row
 // per single-wave workgroup: the shape that streams fastest here.
-template <typename T, int NV>
+template <typename T, int NV, bool FULL>
 __global__ __launch_bounds__(64) void k_mb_rows_v(const T *__restrict__ logits, int64_t N, int V, int blank,
                                                   int fused, MbParams mp, const SampleDesc *__restrict__ desc,
                                                   int B, const int32_t *__restrict__ targets, int S,
@@ -1961,19 +1981,20 @@ __global__ __launch_bounds__(64) void k_mb_rows_v(const T *__restrict__ logits, 
         Vec xv[NV];
 #pragma unroll
         for (int i = 0; i < NV; ++i)
-            if (i * 64 + lane < nvec) xv[i] = load_raw<T, false>(x + (int64_t)(i * 64 + lane) * VEC);
-        float m = wave_max_f(row_max<T, NV, false>(xv, nvec));
+            if (FULL || i * 64 + lane < nvec) xv[i] = load_raw<T, false>(x + (int64_t)(i * 64 + lane) * VEC);
+        float m = wave_max_f(row_max<T, NV, FULL>(xv, nvec));
         const float nm = (m == kNegInf) ? 0.f : -m * kLog2e;
         float sum = 0.f;
 #pragma unroll
         for (int i = 0; i < NV; ++i)
-            if (i * 64 + lane < nvec)
+            if (FULL || i * 64 + lane < nvec)
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) sum += exp2_fast(fmaf(Raw<T>::get(xv[i], e), kLog2e, nm));
         sum = wave_sum_f(sum);
         dn = (m == kNegInf) ? kNegInf : m + log2_fast(sum) * kLn2;
     }
     if (lane == 0) den[r] = dn;
+    float v = kNegInf;
     if (lane < 2 + mp.nb) {
         int k = blank;
         if (lane == 1) {
@@ -1990,9 +2011,9 @@ __global__ __launch_bounds__(64) void k_mb_rows_v(const T *__restrict__ logits, 
 #pragma unroll
         for (int i = 0; i < kMaxBigBlanks; ++i)
             if (lane == 2 + i) k = mp.ids[i];
-        const float v = (k >= 0 && dn != kNegInf) ? Elem<T>::load1(x + k) - dn - mp.sigma : kNegInf;
-        wp[(int64_t)lane * n_slots + d.slot_off + (int64_t)(t + u) * U1 + u] = prob_d(v);
+        v = (k >= 0 && dn != kNegInf) ? Elem<T>::load1(x + k) - dn - mp.sigma : kNegInf;
     }
+    mb_store_node(d, t, u, mp, lane, v, wp, n_slots);
 }
 
 // Subtracts f from element c of the row in the vector of lane
@@ -2005,7 +2026,7 @@ __device__ __forceinline__ void mb_sub_at(float (&gv)[VEC], int vi, int i, int c
     }
 }
 
-template <typename T, int NV>
+template <typename T, int NV, bool FULL>
 __global__ __launch_bounds__(64) void k_mb_grad_v(const T *__restrict__ logits, T *__restrict__ grad, int64_t N,
                                                   int V, int blank, int fused, MbParams mp, int U1p,
                                                   const SampleDesc *__restrict__ desc, int B,
@@ -2031,7 +2052,7 @@ __global__ __launch_bounds__(64) void k_mb_grad_v(const T *__restrict__ logits, 
         float z[VEC] = {};
 #pragma unroll
         for (int i = 0; i < NV; ++i)
-            if (i * 64 + lane < nvec) store_raw<T, true>(g + (int64_t)(i * 64 + lane) * VEC, Raw<T>::put(z));
+            if (FULL || i * 64 + lane < nvec) store_raw<T, true>(g + (int64_t)(i * 64 + lane) * VEC, Raw<T>::put(z));
         return;
     }
     Vec xv[NV];
@@ -2039,7 +2060,7 @@ __global__ __launch_bounds__(64) void k_mb_grad_v(const T *__restrict__ logits, 
         const T *x = logits + r * (int64_t)V;
 #pragma unroll
         for (int i = 0; i < NV; ++i)
-            if (i * 64 + lane < nvec) xv[i] = load_raw<T, true>(x + (int64_t)(i * 64 + lane) * VEC);
+            if (FULL || i * 64 + lane < nvec) xv[i] = load_raw<T, true>(x + (int64_t)(i * 64 + lane) * VEC);
     }
     MbRowTerms rt = mb_row_terms(d, r, t, u, V, fused, mp, U1p, targets, S, den, wp, n_slots, alpha, beta, ealpha,
                                  ebeta, log2z, scale, fastemit);
@@ -2048,7 +2069,7 @@ __global__ __launch_bounds__(64) void k_mb_grad_v(const T *__restrict__ logits, 
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int vi = i * 64 + lane;
-        if (vi < nvec) {
+        if (FULL || vi < nvec) {
             float gv[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; ++e)
@@ -2103,19 +2124,21 @@ static int mb_row_nv(const MbArgs &a) {
     return nv <= 16 ? nv : 0;
 }
 
-template <typename Fn> static hipError_t with_mb_nv(int esize, int nv, Fn &&fn) {
-    auto go = [&](auto tag) -> hipError_t {
+// full: the row fills all nv vectors of every lane (no tail test).
+template <typename Fn> static hipError_t with_mb_nv(int esize, int nv, bool full, Fn &&fn) {
+    auto go = [&](auto tag, auto fc) -> hipError_t {
         using T = decltype(tag);
         switch (nv) {
-        case 1: return fn(T{}, std::integral_constant<int, 1>{});
-        case 2: return fn(T{}, std::integral_constant<int, 2>{});
-        case 4: return fn(T{}, std::integral_constant<int, 4>{});
-        case 8: return fn(T{}, std::integral_constant<int, 8>{});
-        default: return fn(T{}, std::integral_constant<int, 16>{});
+        case 1: return fn(T{}, std::integral_constant<int, 1>{}, fc);
+        case 2: return fn(T{}, std::integral_constant<int, 2>{}, fc);
+        case 4: return fn(T{}, std::integral_constant<int, 4>{}, fc);
+        case 8: return fn(T{}, std::integral_constant<int, 8>{}, fc);
+        default: return fn(T{}, std::integral_constant<int, 16>{}, fc);
         }
     };
-    if (esize == 4) return go(float{});
-    return go(_Float16{});
+    if (esize == 4)
+        return full ? go(float{}, std::true_type{}) : go(float{}, std::false_type{});
+    return full ? go(_Float16{}, std::true_type{}) : go(_Float16{}, std::false_type{});
 }
 
 hipError_t launch_mb_rows(const MbArgs &a, hipStream_t stream) {
@@ -2123,13 +2146,14 @@ hipError_t launch_mb_rows(const MbArgs &a, hipStream_t stream) {
     constexpr int64_t kMaxBlocks = (int64_t)1 << 24;
     const int nv = mb_row_nv(a);
     if (nv > 0)
-        return with_mb_nv(a.esize, nv, [&](auto tag, auto nvc) {
+        return with_mb_nv(a.esize, nv, a.V * a.esize == nv * 1024, [&](auto tag, auto nvc, auto fc) {
             using T = decltype(tag);
             constexpr int NV = decltype(nvc)::value;
+            constexpr bool FULL = decltype(fc)::value;
             for (int64_t b0 = 0; b0 < a.N; b0 += kMaxBlocks) {
                 // a multiple of 8 workgroups, so each XCD takes a contiguous range of rows
                 const unsigned nb = (unsigned)((std::min<int64_t>(kMaxBlocks, a.N - b0) + 7) & ~(int64_t)7);
-                hipLaunchKernelGGL((k_mb_rows_v<T, NV>), dim3(nb), dim3(64), 0, stream,
+                hipLaunchKernelGGL((k_mb_rows_v<T, NV, FULL>), dim3(nb), dim3(64), 0, stream,
                                    static_cast<const T *>(a.logits), a.N, a.V, a.blank, a.fused, mp,
                                    MBWS(const SampleDesc *, desc), a.B, a.targets, a.S, MBWS(float *, den),
                                    MBWS(double *, wp), a.lay.n_slots, MBWS(uint32_t *, status), b0);
@@ -2184,12 +2208,13 @@ hipError_t launch_mb_grad(const MbArgs &a, hipStream_t stream) {
     constexpr int64_t kMaxBlocks = (int64_t)1 << 24;
     const int nv = mb_row_nv(a);
     if (nv > 0)
-        return with_mb_nv(a.esize, nv, [&](auto tag, auto nvc) {
+        return with_mb_nv(a.esize, nv, a.V * a.esize == nv * 1024, [&](auto tag, auto nvc, auto fc) {
             using T = decltype(tag);
             constexpr int NV = decltype(nvc)::value;
+            constexpr bool FULL = decltype(fc)::value;
             for (int64_t b0 = 0; b0 < a.N; b0 += kMaxBlocks) {
                 const unsigned nb = (unsigned)std::min<int64_t>(kMaxBlocks, a.N - b0);
-                hipLaunchKernelGGL((k_mb_grad_v<T, NV>), dim3(nb), dim3(64), 0, stream,
+                hipLaunchKernelGGL((k_mb_grad_v<T, NV, FULL>), dim3(nb), dim3(64), 0, stream,
                                    static_cast<const T *>(a.logits), static_cast<T *>(a.grad), a.N, a.V, a.blank,
                                    a.fused, mp, a.lay.U1p, MBWS(const SampleDesc *, desc), a.B, a.targets, a.S,
                                    MBWS(const float *, den), MBWS(const double *, wp), a.lay.n_slots,
