@@ -1626,11 +1626,13 @@ __global__ __launch_bounds__(256) void k_mb_rows(const T *__restrict__ logits, i
 // lie d_i diagonals away.  The edges' probabilities do not depend on the
 // recursion, so those of the next P diagonals are in flight while a diagonal
 // is computed (a register ring, one slot per step mod P), loaded through
-// buffer resources with the diagonal's offset in a scalar register and the
-// lane's offset fixed, so a step does no address arithmetic.  Missing edges
-// are masked through their weights and every LDS read is issued, so a step
-// has no branches around its reads.  Stored: every real diagonal of alpha or
-// beta (scaled) and its exponent; log2 P(y|x) and, from beta, the loss.
+// buffer resources one diagonal long with the lane's offset fixed.  No edge
+// is masked: the row pass stores zero weights for edges that leave the
+// lattice and for slots outside it, the range check zeroes columns past U,
+// and a big blank whose source diagonal does not exist is scaled to zero
+// through its exponent, so nodes outside the lattice stay zero by
+// themselves.  Stored: every real diagonal of alpha or beta (scaled) and its
+// exponent; log2 P(y|x) and, from beta, the loss.
 template <int G, int NB> struct MbSweepShape {
     static constexpr int NW = 2 + NB;  // blank, label, big blanks
     // steps in flight: their loads and stores stay within the wait counter's
