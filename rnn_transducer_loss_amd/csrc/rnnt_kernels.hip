@@ -182,13 +182,16 @@ __device__ __forceinline__ float wave_sum_f(float v) {
     v += dpp_f<0x143, 0xc>(0.f, v);
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
-__device__ __forceinline__ int wave_max_i(int v) {
-    v = max(v, dpp_i<0xb1, 0xf>(v, v));
-    v = max(v, dpp_i<0x4e, 0xf>(v, v));
-    v = max(v, dpp_i<0x124, 0xf>(v, v));
-    v = max(v, dpp_i<0x128, 0xf>(v, v));
-    v = max(v, dpp_i<0x142, 0xa>(v, v));
-    v = max(v, dpp_i<0x143, 0xc>(v, v));
+// Maximum of non-negative values (floating-point exponent fields): lanes a
+// stage does not reach read 0, the identity, so each move folds into the
+// maximum instruction.
+__device__ __forceinline__ int wave_max_nonneg(int v) {
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0xb1, 0xf, 0xf, true));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x4e, 0xf, 0xf, true));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x124, 0xf, 0xf, true));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x128, 0xf, 0xf, true));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, true));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, true));
     return __builtin_amdgcn_readlane(v, 63);
 }
 
@@ -660,7 +663,7 @@ template <int K, int G> __device__ __forceinline__ int renorm(double (&a)[G][K])
     for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int k = 0; k < K; ++k) eb = max(eb, (__double2hiint(a[g][k]) >> 20) & 0x7ff);
-    eb = wave_max_i(eb);
+    eb = wave_max_nonneg(eb);
     const int sh = eb - 1023;
 #pragma unroll
     for (int g = 0; g < G; ++g)
@@ -1622,16 +1625,17 @@ __global__ __launch_bounds__(256) void k_mb_rows(const T *__restrict__ logits, i
 // columns arrive in one 16-byte load and its two values leave in one 16-byte
 // store; only one neighbour per group and step crosses lanes (a DPP move).
 // `cur` is the diagonal just finished, scaled by 2^-E; the LDS ring keeps the
-// last R diagonals (and their exponents) for the NB big blanks, whose sources
-// lie d_i diagonals away.  The edges' probabilities do not depend on the
-// recursion, so those of the next P diagonals are in flight while a diagonal
-// is computed (a register ring, one slot per step mod P), loaded through
-// buffer resources one diagonal long with the lane's offset fixed.  No edge
-// is masked: the row pass stores zero weights for edges that leave the
-// lattice and for slots outside it, the range check zeroes columns past U,
-// and a big blank whose source diagonal does not exist is scaled to zero
-// through its exponent, so nodes outside the lattice stay zero by
-// themselves.  Stored: every real diagonal of alpha or beta (scaled) and its
+// last R diagonals for the NB big blanks, whose sources lie d_i diagonals
+// away, and the lanes of one register their exponents.  The edges'
+// probabilities do not depend on the recursion, so those of the next P
+// diagonals are in flight while a diagonal is computed (a register ring, one
+// slot per step mod P).  No edge is masked: the row pass stores zero weights
+// for edges that leave the lattice and for slots outside it, the range check
+// zeroes columns past U, and a big blank whose source diagonal does not
+// exist reads a ring slot still holding zeros, so nodes outside the lattice
+// stay zero by themselves.  One wave issues one instruction at a time here,
+// so the step is written for few instructions: no per-lane masks, scalar
+// diagonal offsets, exponents moved by lane index.  Stored: every real diagonal of alpha or beta (scaled) and its
 // exponent; log2 P(y|x) and, from beta, the loss.
 template <int G, int NB> struct MbSweepShape {
     static constexpr int NW = 2 + NB;  // blank, label, big blanks
@@ -1657,19 +1661,21 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
                                              double *__restrict__ alpha, double *__restrict__ beta,
                                              int *__restrict__ ealpha, int *__restrict__ ebeta,
                                              double *__restrict__ log2z, float *__restrict__ loss) {
-    extern __shared__ double mb_ring[];  // R diagonals of G groups of 64 lanes x 2 values, then R exponents
+    extern __shared__ double mb_ring[];  // R diagonals of G groups of 64 lanes x 2 values
     constexpr int U1p = 128 * G;
     constexpr int NW = MbSweepShape<G, NB>::NW;
     constexpr int P = MbSweepShape<G, NB>::P;
     const int lane = threadIdx.x;
     const int T = d.T, U = d.U, U1 = U + 1, nd = T + U, R = mp.R;
-    int *ering = reinterpret_cast<int *>(mb_ring + (size_t)R * U1p);
     for (int q = lane; q < R * U1p; q += 64) mb_ring[q] = 0.0;
-    for (int q = lane; q < R; q += 64) ering[q] = 0;
     // ring entry of (diagonal slot s, group g): this lane's pair at 16-byte stride
     auto ring_at = [&](int sslot, int g) -> D2 * {
         return reinterpret_cast<D2 *>(mb_ring + (size_t)(sslot * G + g) * 128) + lane;
     };
+    // Lane s holds the exponent of the diagonal in ring slot s (R <= 17 lanes
+    // used): written by a select on the lane index and read with readlane,
+    // without LDS or lane masks.
+    int eh = 0;
     uint32_t vo[G];  // byte offset of the lane's first column in a diagonal
 #pragma unroll
     for (int g = 0; g < G; ++g) vo[g] = (uint32_t)(128 * g + 2 * lane) * 8u;
@@ -1678,19 +1684,23 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
 
     // One buffer resource per plane and diagonal, U1 slots long: its range
     // check returns zero for the columns past U, so those lanes' weights are
-    // zero without a test.  The diagonal index is wave-uniform (readfirstlane
-    // keeps it scalar where the compiler forms it with vector instructions).
+    // zero without a test.  The diagonal's byte offset is formed in 32 bits
+    // (a sample's span is below 2^31 bytes) and kept scalar with readfirstlane
+    // where the compiler would form it with vector instructions.
+    const char *pb[NW];
+#pragma unroll
+    for (int k = 0; k < NW; ++k) pb[k] = reinterpret_cast<const char *>(wp + (int64_t)k * n_slots + d.slot_off);
+    const uint32_t dbytes = (uint32_t)U1 * 8u;
     auto ld = [&](int k, int diag, uint32_t voff) -> D2 {
-        const int dg = __builtin_amdgcn_readfirstlane(diag);
-        const Rsrc r = buffer_at(wp + (int64_t)k * n_slots + d.slot_off + (int64_t)dg * U1, (uint32_t)U1 * 8u);
-        return as_d2(__builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+        const uint32_t off = (uint32_t)__builtin_amdgcn_readfirstlane(diag) * dbytes;
+        return as_d2(__builtin_amdgcn_raw_buffer_load_b128(buffer_at(pb[k] + off, dbytes), voff, 0, 0));
     };
     // The probabilities step `step` uses, for the lane's two columns (steps
     // past the end load the last step's again; never used).  Forward,
     // diagonal n pulls from n-1 (blank at column u; the label from u-1, moved
     // over by one column below) and n-d_i; backward, every edge leaves the
     // node itself.  A big blank's source diagonal before 0 reads diagonal 0;
-    // its term is cancelled through the exponent.
+    // its source value is zero (below).
     auto load_w = [&](int step, D2 (&w)[G][NW]) {
         const int n = bw ? nd - min(step, nd) : min(step, nd);
 #pragma unroll
@@ -1710,7 +1720,19 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
     // start: alpha(0,0) = 1 on diagonal 0; beta of the virtual end (T,U) = 1 on diagonal T+U
     D2 cur[G];
     int E = 0;
-    int slot = (bw ? nd : 0) % R;  // ring slot of the diagonal last written (n mod R, kept incrementally)
+    // Ring slots, advanced with the diagonal: `slot` holds the diagonal last
+    // written (n mod R), sl[i] the source diagonal of big blank i for the
+    // next step (n - d_i forward, n + d_i backward, mod R).  A source
+    // diagonal outside [0, T+U] maps to a slot no diagonal has been written
+    // to yet (1 <= d_i < R), which still holds the zeros it started with.
+    int slot = bw ? nd % R : 0;
+    int sl[NB > 0 ? NB : 1];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int q = bw ? slot + mp.dur[i] : R - mp.dur[i];
+        sl[i] = q >= R ? q - R : q;
+    }
+    auto advance = [&](int &s) { s = bw ? (s == 0 ? R - 1 : s - 1) : (s + 1 == R ? 0 : s + 1); };
     {
         const int ue = bw ? U : 0;
 #pragma unroll
@@ -1722,46 +1744,45 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
         if (!bw) {
 #pragma unroll
             for (int g = 0; g < G; ++g) reinterpret_cast<D2 *>(tab + 128 * g)[lane] = cur[g];
-            if (lane == 0) etab[0] = 0;
+            etab[0] = 0;
         }
     }
 
     auto step_once = [&](int step, const D2 (&w)[G][NW]) {
         const int n = bw ? nd - step : step;
-        slot = bw ? (slot == 0 ? R - 1 : slot - 1) : (slot + 1 == R ? 0 : slot + 1);
-        // big blanks: source diagonal's ring slot and exponent relative to E;
-        // a source diagonal outside [0, nd] gets an exponent that scales its
-        // term to zero (its ring slot holds zeros or an older diagonal)
-        int sl[NB > 0 ? NB : 1], shg[NB > 0 ? NB : 1];
+        advance(slot);
+        // big blanks: the source's ring slot and its exponent relative to E
+        int shg[NB > 0 ? NB : 1];
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-            const int dd = mp.dur[i];  // 1 <= dd < R
-            const bool okd = bw ? n + dd <= nd : n - dd >= 0;
-            const int q = bw ? slot + dd : slot - dd;
-            sl[i] = bw ? (q >= R ? q - R : q) : (q < 0 ? q + R : q);
-            const int eg = ering[sl[i]] - E;
-            shg[i] = okd ? eg : -4096;
+            advance(sl[i]);
+            shg[i] = __builtin_amdgcn_readlane(eh, sl[i]) - E;
         }
         // Cross-lane neighbours.  Forward: column 2l-1 of the finished
         // diagonal and the label weight of column 2l-1 come from lane l-1's
-        // second value (lane 0 of group g: lane 63 of group g-1).  Backward:
-        // column 2l+2 of the finished diagonal from lane l+1's first value
-        // (lane 63 of group g: lane 0 of group g+1).
-        double nb_v[G], nb_w[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            nb_v[g] = bw ? rotate_down(cur[g].a) : rotate_up(cur[g].b);
-            nb_w[g] = bw ? 0.0 : rotate_up(w[g][1].b);
-        }
+        // second value (lane 0 of group g: lane 63 of group g-1, or zero).
+        // Backward: column 2l+2 of the finished diagonal from lane l+1's
+        // first value (lane 63 of group g: lane 0 of group g+1, or zero).
         double side_v[G], side_w[G];
+        if constexpr (G == 1) {
+            side_v[0] = bw ? shift_down_zero(cur[0].a) : shift_up_zero(cur[0].b);
+            side_w[0] = bw ? 0.0 : shift_up_zero(w[0][1].b);
+        } else {
+            double nb_v[G], nb_w[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            if (bw) {
-                side_v[g] = (lane == 63) ? (g + 1 < G ? nb_v[g + 1] : 0.0) : nb_v[g];
-                side_w[g] = 0.0;
-            } else {
-                side_v[g] = (lane == 0) ? (g > 0 ? nb_v[g - 1] : 0.0) : nb_v[g];
-                side_w[g] = (lane == 0) ? (g > 0 ? nb_w[g - 1] : 0.0) : nb_w[g];
+            for (int g = 0; g < G; ++g) {
+                nb_v[g] = bw ? rotate_down(cur[g].a) : rotate_up(cur[g].b);
+                nb_w[g] = bw ? 0.0 : rotate_up(w[g][1].b);
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                if (bw) {
+                    side_v[g] = (lane == 63) ? (g + 1 < G ? nb_v[g + 1] : 0.0) : nb_v[g];
+                    side_w[g] = 0.0;
+                } else {
+                    side_v[g] = (lane == 0) ? (g > 0 ? nb_v[g - 1] : 0.0) : nb_v[g];
+                    side_w[g] = (lane == 0) ? (g > 0 ? nb_w[g - 1] : 0.0) : nb_w[g];
+                }
             }
         }
         D2 nx[G];
@@ -1798,7 +1819,7 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
 #pragma unroll
         for (int g = 0; g < G; ++g)
             eb = max(eb, max((__double2hiint(nx[g].a) >> 20) & 0x7ff, (__double2hiint(nx[g].b) >> 20) & 0x7ff));
-        eb = wave_max_i(eb);
+        eb = wave_max_nonneg(eb);
         const int sh = eb == 0 ? 0 : eb - 1023;
         E += sh;
 #pragma unroll
@@ -1806,11 +1827,11 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
             cur[g] = {__builtin_amdgcn_ldexp(nx[g].a, -sh), __builtin_amdgcn_ldexp(nx[g].b, -sh)};
             *ring_at(slot, g) = cur[g];
         }
-        if (lane == 0) ering[slot] = E;
-        if (n < nd) {
+        eh = (lane == slot) ? E : eh;
+        if (bw || n < nd) {
 #pragma unroll
             for (int g = 0; g < G; ++g) reinterpret_cast<D2 *>(tab + (int64_t)n * U1p + 128 * g)[lane] = cur[g];
-            if (lane == 0) etab[n] = E;
+            etab[n] = E;  // every lane stores the same value: no lane mask
         }
     };
 
