@@ -234,11 +234,12 @@ rnnt_status rnnt_grad_scale_padded(void *grad, rnnt_dtype dtype, int32_t max_T, 
  *   workspace         device, >= rnnt_multiblank_workspace_size bytes, 256-byte
  *                     aligned.
  * Returns RNNT_INVALID_VALUE for the conditions of rnnt_loss_fused, a bad big
- * blank list, a non-finite sigma, or a batch whose widest lattice and longest
- * duration need more than 64 KiB of ring per sweep, i.e.
- * (longest duration + 1) * (U1p * 8 + 4) bytes > 64 KiB, U1p = the widest
- * U_i + 1 rounded up to 128 times a power of two (at U1p = 1024 the longest
- * duration is 6).  A label equal to blank or to a big
+ * blank list, a non-finite sigma, a batch whose widest lattice and longest
+ * duration need more than 64 KiB of ring per sweep, i.e. R * U1p * 8 bytes
+ * > 64 KiB with R the power of two above the longest duration and U1p the
+ * widest U_i + 1 rounded up to 128 times a power of two (at U1p = 1024 the
+ * longest duration is 7, at 512 it is 15), or a sample with
+ * (T_i + U_i) * U1p * 8 >= 2^31.  A label equal to blank or to a big
  * blank sets RNNT_DEV_BAD_TARGET (read with rnnt_loss_fused_check).
  * The recursion runs in fp64 probabilities renormalised per anti-diagonal:
  * an edge whose log-probability (less sigma) is below about -745 counts as

@@ -492,14 +492,14 @@ rnnt_status build_mb_plan(int32_t B, int32_t V, int64_t N, const int32_t *T, con
         dmax = std::max(dmax, (int)dur[i]);
     }
     int max_U1 = 1;
-    for (int32_t i = 0; i < B; ++i) {
-        max_U1 = std::max(max_U1, U[i] + 1);
-        // the sweep addresses a sample's slots with 32-bit byte offsets
-        if (((int64_t)T[i] + U[i]) * (U[i] + 1) * 8 >= ((int64_t)1 << 31)) return RNNT_INVALID_VALUE;
-    }
+    for (int32_t i = 0; i < B; ++i) max_U1 = std::max(max_U1, U[i] + 1);
     int G = 1;  // groups of 128 columns (two per lane) in the sweep
     while (128 * G < max_U1) G <<= 1;
     const int U1p = 128 * G;
+    // the sweep addresses a sample's weights and its alpha/beta table (T+U
+    // diagonals of U1p slots) with 32-bit byte offsets
+    for (int32_t i = 0; i < B; ++i)
+        if (((int64_t)T[i] + U[i]) * U1p * 8 >= ((int64_t)1 << 31)) return RNNT_INVALID_VALUE;
     if (mb_ring_bytes(U1p, dmax) > kMbRingBytes) return RNNT_INVALID_VALUE;
     p.desc.resize(B);
     int64_t row = 0, slot = 0, diag = 0, ab = 0;

@@ -190,7 +190,7 @@ constexpr int kMaxU1 = 1024;
 // ------------------------------------------------- multi-blank transducer
 constexpr int kMaxBigBlanks = 4;
 constexpr int kMaxBigBlankDuration = 16;
-constexpr size_t kMbRingBytes = 64 * 1024;  // LDS of one sweep: the last (longest duration + 1) diagonals
+constexpr size_t kMbRingBytes = 64 * 1024;  // LDS of one sweep: the ring of recent diagonals
 
 // Workspace of the multi-blank path.  Byte offsets; the status word is at 0
 // and the sample descriptors at 256, as in the plain layout.
@@ -221,8 +221,8 @@ struct MbArgs {
     MbLayout lay;
 };
 
-// LDS bytes of one multi-blank sweep: (longest duration + 1) diagonals of U1p
-// fp64 values and their exponents.
+// LDS bytes of one multi-blank sweep: a ring of R diagonals of U1p fp64
+// values, R the power of two above the longest duration.
 size_t mb_ring_bytes(int U1p, int max_duration);
 hipError_t launch_mb_rows(const MbArgs &a, hipStream_t stream);
 hipError_t launch_mb_sweep(const MbArgs &a, hipStream_t stream);

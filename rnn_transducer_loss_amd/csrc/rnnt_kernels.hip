@@ -1490,7 +1490,7 @@ struct MbParams {
     int nb;
     int ids[kMaxBigBlanks];
     int dur[kMaxBigBlanks];
-    int R;        // ring depth: the longest duration + 1
+    int R;        // ring depth: the power of two above the longest duration
     float sigma;
 };
 
@@ -1666,13 +1666,13 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
     constexpr int NW = MbSweepShape<G, NB>::NW;
     constexpr int P = MbSweepShape<G, NB>::P;
     const int lane = threadIdx.x;
-    const int T = d.T, U = d.U, U1 = U + 1, nd = T + U, R = mp.R;
+    const int T = d.T, U = d.U, U1 = U + 1, nd = T + U, R = mp.R, M = R - 1;
     for (int q = lane; q < R * U1p; q += 64) mb_ring[q] = 0.0;
     // ring entry of (diagonal slot s, group g): this lane's pair at 16-byte stride
     auto ring_at = [&](int sslot, int g) -> D2 * {
         return reinterpret_cast<D2 *>(mb_ring + (size_t)(sslot * G + g) * 128) + lane;
     };
-    // Lane s holds the exponent of the diagonal in ring slot s (R <= 17 lanes
+    // Lane s holds the exponent of the diagonal in ring slot s (R <= 32 lanes
     // used): written by a select on the lane index and read with readlane,
     // without LDS or lane masks.
     int eh = 0;
@@ -1681,19 +1681,28 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
     for (int g = 0; g < G; ++g) vo[g] = (uint32_t)(128 * g + 2 * lane) * 8u;
     double *tab = (bw ? beta : alpha) + d.ab_off;
     int *etab = (bw ? ebeta : ealpha) + d.diag_off + d.index;
+    // Stores through resources over diagonals 0 .. T+U-1 of the table (the
+    // diagonal offset is scalar): the forward sweep's last diagonal, the
+    // virtual end's, falls outside and its store is dropped.  A table spans
+    // less than 2^31 bytes (checked on the host).
+    const Rsrc rtab = buffer_at(tab, (uint32_t)nd * (uint32_t)U1p * 8u);
+    const Rsrc retab = buffer_at(etab, (uint32_t)nd * 4u);
 
-    // One buffer resource per plane and diagonal, U1 slots long: its range
-    // check returns zero for the columns past U, so those lanes' weights are
-    // zero without a test.  The diagonal's byte offset is formed in 32 bits
-    // (a sample's span is below 2^31 bytes) and kept scalar with readfirstlane
-    // where the compiler would form it with vector instructions.
+    // One buffer resource per plane over the sample's slots, the diagonal
+    // chosen by the scalar offset.  The range check covers the scalar offset
+    // too, so a record count of (that offset + U1 slots) checks the lane's
+    // columns against U: the columns past U read zero without a test.  All
+    // planes at one diagonal share the offset and the count; offsets are
+    // 32-bit (a sample's span is below 2^31 bytes) and kept scalar with
+    // readfirstlane where the compiler would form them with vector
+    // instructions.
     const char *pb[NW];
 #pragma unroll
     for (int k = 0; k < NW; ++k) pb[k] = reinterpret_cast<const char *>(wp + (int64_t)k * n_slots + d.slot_off);
     const uint32_t dbytes = (uint32_t)U1 * 8u;
     auto ld = [&](int k, int diag, uint32_t voff) -> D2 {
         const uint32_t off = (uint32_t)__builtin_amdgcn_readfirstlane(diag) * dbytes;
-        return as_d2(__builtin_amdgcn_raw_buffer_load_b128(buffer_at(pb[k] + off, dbytes), voff, 0, 0));
+        return as_d2(__builtin_amdgcn_raw_buffer_load_b128(buffer_at(pb[k], off + dbytes), voff, off, 0));
     };
     // The probabilities step `step` uses, for the lane's two columns (steps
     // past the end load the last step's again; never used).  Forward,
@@ -1720,19 +1729,11 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
     // start: alpha(0,0) = 1 on diagonal 0; beta of the virtual end (T,U) = 1 on diagonal T+U
     D2 cur[G];
     int E = 0;
-    // Ring slots, advanced with the diagonal: `slot` holds the diagonal last
-    // written (n mod R), sl[i] the source diagonal of big blank i for the
-    // next step (n - d_i forward, n + d_i backward, mod R).  A source
-    // diagonal outside [0, T+U] maps to a slot no diagonal has been written
-    // to yet (1 <= d_i < R), which still holds the zeros it started with.
-    int slot = bw ? nd % R : 0;
-    int sl[NB > 0 ? NB : 1];
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        const int q = bw ? slot + mp.dur[i] : R - mp.dur[i];
-        sl[i] = q >= R ? q - R : q;
-    }
-    auto advance = [&](int &s) { s = bw ? (s == 0 ? R - 1 : s - 1) : (s + 1 == R ? 0 : s + 1); };
+    // Diagonal n lives in ring slot n mod R (R a power of two).  A big
+    // blank's source diagonal outside [0, T+U] maps to a slot no diagonal has
+    // been written to yet (1 <= d_i < R), which still holds the zeros it
+    // started with.
+    int slot = (bw ? nd : 0) & M;
     {
         const int ue = bw ? U : 0;
 #pragma unroll
@@ -1750,12 +1751,12 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
 
     auto step_once = [&](int step, const D2 (&w)[G][NW]) {
         const int n = bw ? nd - step : step;
-        advance(slot);
+        slot = n & M;
         // big blanks: the source's ring slot and its exponent relative to E
-        int shg[NB > 0 ? NB : 1];
+        int sl[NB > 0 ? NB : 1], shg[NB > 0 ? NB : 1];
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-            advance(sl[i]);
+            sl[i] = (bw ? n + mp.dur[i] : n - mp.dur[i]) & M;
             shg[i] = __builtin_amdgcn_readlane(eh, sl[i]) - E;
         }
         // Cross-lane neighbours.  Forward: column 2l-1 of the finished
@@ -1828,11 +1829,15 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
             *ring_at(slot, g) = cur[g];
         }
         eh = (lane == slot) ? E : eh;
-        if (bw || n < nd) {
+        const uint32_t so = (uint32_t)n * (uint32_t)U1p * 8u;
 #pragma unroll
-            for (int g = 0; g < G; ++g) reinterpret_cast<D2 *>(tab + (int64_t)n * U1p + 128 * g)[lane] = cur[g];
-            etab[n] = E;  // every lane stores the same value: no lane mask
+        for (int g = 0; g < G; ++g) {
+            const u32x4 v = {(uint32_t)__double2loint(cur[g].a), (uint32_t)__double2hiint(cur[g].a),
+                             (uint32_t)__double2loint(cur[g].b), (uint32_t)__double2hiint(cur[g].b)};
+            __builtin_amdgcn_raw_buffer_store_b128(v, rtab, vo[g], so, 0);
         }
+        // every lane stores the same value: no lane mask
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)E, retab, 0, (uint32_t)n * 4u, 0);
     };
 
     D2 w[P][G][NW];
@@ -2117,7 +2122,8 @@ MbParams mb_params(const MbArgs &a) {
         p.dur[i] = i < a.nb ? a.dur[i] : 1;
         if (i < a.nb) dmax = std::max(dmax, a.dur[i]);
     }
-    p.R = dmax + 1;
+    p.R = 1;
+    while (p.R < dmax + 1) p.R <<= 1;
     p.sigma = a.sigma;
     return p;
 }
@@ -2132,7 +2138,9 @@ template <typename Fn> hipError_t with_esize(int esize, Fn &&fn) {
 #define MBWS(type, field) reinterpret_cast<type>(a.ws + a.lay.field)
 
 size_t mb_ring_bytes(int U1p, int max_duration) {
-    return (size_t)(max_duration + 1) * (size_t)U1p * sizeof(double) + (size_t)(max_duration + 1) * sizeof(int);
+    size_t r = 1;
+    while (r < (size_t)max_duration + 1) r <<= 1;
+    return r * (size_t)U1p * sizeof(double);
 }
 
 // Vectors per lane of the vector row forms (0: the scalar forms): 16-byte

@@ -234,14 +234,29 @@ def test_multiblank_call_rejects_invalid_arguments_before_any_launch(over):
 
 
 def test_multiblank_ring_limit():
-    # (longest duration + 1) diagonals of the widest lattice (8 bytes a column plus a 4-byte exponent each) must
-    # fit 64 KiB of LDS: U+1 = 1000 pads to 1024 columns, so durations up to 6 fit and 7 does not
+    # R diagonals of the widest lattice (8 bytes a column), R the power of two above the longest duration, must fit
+    # 64 KiB of LDS: U+1 = 1000 pads to 1024 columns, so durations up to 7 fit and 8 does not; U+1 = 401 pads to
+    # 512, durations up to 15 fit
     T, U = np.array([3], np.int32), np.array([999], np.int32)
     N = 3 * 1000
-    assert _lib.workspace_size_multiblank(1, 8, N, 0, T, U, [6]) > 0
+    assert _lib.workspace_size_multiblank(1, 8, N, 0, T, U, [7]) > 0
     with pytest.raises(ValueError):
-        _lib.workspace_size_multiblank(1, 8, N, 0, T, U, [7])
+        _lib.workspace_size_multiblank(1, 8, N, 0, T, U, [8])
+    U4 = np.array([400], np.int32)
+    assert _lib.workspace_size_multiblank(1, 8, 3 * 401, 0, T, U4, [2, 15]) > 0
+    with pytest.raises(ValueError):
+        _lib.workspace_size_multiblank(1, 8, 3 * 401, 0, T, U4, [16])
     assert _lib.workspace_size_multiblank(1, 8, 3 * 200, 0, T, np.array([199], np.int32), [16]) > 0
+
+
+def test_multiblank_table_span_limit():
+    # the sweep addresses a sample's T+U diagonals of 128 (padded) columns of fp64 with 32-bit byte offsets:
+    # (T+U) * 128 * 8 must stay below 2^31
+    U = np.array([0], np.int32)
+    ok, bad = 2 ** 31 // 1024 - 1, 2 ** 31 // 1024
+    assert _lib.workspace_size_multiblank(1, 8, ok, 0, np.array([ok], np.int32), U, [2]) > 0
+    with pytest.raises(ValueError):
+        _lib.workspace_size_multiblank(1, 8, bad, 0, np.array([bad], np.int32), U, [2])
 
 
 def test_multiblank_padded_sizes_and_limits():

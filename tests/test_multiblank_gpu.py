@@ -110,10 +110,10 @@ def test_multiblank_against_oracle(rl, V, dtype, fused, ids, durs, sigma, lam, c
 
 
 @pytest.mark.parametrize("U,durs", [(63, [2, 8]), (64, [2, 8]), (127, [3]), (128, [3]), (255, [2, 16]),
-                                    (256, [2, 14]), (511, [4]), (512, [6]), (700, [2, 6]), (1023, [2, 6])])
+                                    (256, [2, 15]), (511, [4]), (512, [7]), (700, [2, 6]), (1023, [2, 7])])
 def test_multiblank_lattice_widths(rl, U, durs):
     # U+1 across every column width of the sweep (64, 128, 256, 512, 1024 columns) and ring depths up to the
-    # 64 KiB limit: (longest duration + 1) * (columns * 8 + 4) bytes
+    # 64 KiB limit: R * columns * 8 bytes, R the power of two above the longest duration
     ids = [7, 6][:len(durs)]
     w = _mb([3, 30], [U, min(U, 20)], 9, ids, durs, 0.05, std=1.0, blank=0, reduction="none", seed=U)
     loss, red, grad, flags = run_mb(rl, w)
