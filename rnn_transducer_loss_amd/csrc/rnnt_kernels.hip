@@ -701,13 +701,15 @@ template <typename D, int K, int G> struct SweepIO {
             wout[g] = c * 8u;
         }
     }
+    // n >= 0 at every call: an unsigned 32 x 32 -> 64-bit product needs no
+    // sign extension (fewer scalar instructions per diagonal).
     __device__ void load(Wts<K> (&r)[G], int n) const {
-        const Rsrc rs = buffer_at(w + (int64_t)n * w_bytes, w_bytes);
+        const Rsrc rs = buffer_at(w + (uint64_t)(uint32_t)n * w_bytes, w_bytes);
 #pragma unroll
         for (int g = 0; g < G; ++g) D::template load<K>(r[g], rs, win[g]);
     }
     __device__ void store(int n, const double (&a)[G][K]) const {
-        const Rsrc rs = buffer_at(out + (int64_t)n * out_bytes, out_bytes);
+        const Rsrc rs = buffer_at(out + (uint64_t)(uint32_t)n * out_bytes, out_bytes);
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
