@@ -24,7 +24,6 @@ namespace rnnt {
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int64_t kCachedTailBytes = 160ll << 20;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Padded (B, max_T, max_U1, V) layout, or packed when max_T == 0.
@@ -155,20 +154,6 @@ rnnt_status build_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t
     L.n_chunks = (int32_t)p.chunks.size();
     L.rows_per_chunk = rpc;
     L.max_sample_chunks = (int32_t)max_sample_chunks;
-    // The gradient pass walks the chunks in reverse, so the rows the
-    // rowstats pass reads last are read again first: those last ~160 MB
-    // (within the 256 MB memory-side cache) are read with caching loads,
-    // everything before them with non-temporal loads.
-    {
-        const int64_t row_bytes = (int64_t)V * esize;
-        int64_t tail = 0;
-        int32_t k = L.n_chunks;
-        while (k > 0 && tail < kCachedTailBytes) {
-            --k;
-            tail += (int64_t)p.chunks[k].count * row_bytes;
-        }
-        L.first_cached_chunk = k;
-    }
     return RNNT_SUCCESS;
 }
 

@@ -118,7 +118,6 @@ struct WorkspaceLayout {
     int64_t n_diags;
     int32_t n_chunks;
     int32_t rows_per_chunk;
-    int32_t first_cached_chunk;  // rowstats: chunks from here on use caching loads
     int32_t max_sample_chunks;   // most chunks of any one sample
 };
 
