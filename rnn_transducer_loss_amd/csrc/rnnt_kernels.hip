@@ -1480,9 +1480,9 @@ hipError_t launch_zero_padding(void *grad, int esize, int V, int B, int max_T, i
 // Three passes of their own: per row, the log-normaliser and the edges'
 // probabilities (fp64 planes in the skewed slots); one wave per sample
 // and direction sweeping anti-diagonals in fp64 probabilities renormalised by
-// a power of two on every diagonal, with the last (longest duration + 1)
-// diagonals in an LDS ring for the big blanks' jumps; and per row, the
-// gradient.  The loss check and reduction are k_reduce's.
+// a power of two on every diagonal, with the recent diagonals in an LDS
+// ring (a power of two deep, above the longest duration) for the big
+// blanks' jumps; and per row, the gradient.  The loss check and reduction are k_reduce's.
 namespace {
 
 struct MbParams {
