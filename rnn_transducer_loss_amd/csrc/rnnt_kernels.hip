@@ -50,6 +50,12 @@ constexpr double kLn2D = 0.69314718055994530942;
 constexpr double kNegInfD = -__builtin_inf();
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kProbRange = 80.f;  // |log-prob| bound of the probability-domain sweep
+// Per-sample mode word (zeroed by k_plan): the row pass sets kModeLog when a
+// log-probability leaves that bound, k_check_ab sets kModeRerun when the
+// probability-domain sweeps lost alignment mass; either sends the sample's
+// recursions, and the gradient's reads of them, to the log domain.
+constexpr int kModeLog = 1;
+constexpr int kModeRerun = 2;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
@@ -213,7 +219,7 @@ __device__ __forceinline__ void emit_node(const SampleDesc &d, int t, int u, flo
     node[slot] = make_float4(lpb, lpy, dn, __int_as_float(y));
     prob[slot] = make_float2(prob_of(lpb), prob_of(lpy));
     const bool wide = (lpb != kNegInf && fabsf(lpb) > kProbRange) || (lpy != kNegInf && fabsf(lpy) > kProbRange);
-    if (wide) atomicOr(&mode[d.index], 1);
+    if (wide) atomicOr(&mode[d.index], kModeLog);
 }
 
 // Slots u0 .. u1-1 of diagonal n hold no lattice node: give them impossible
@@ -911,10 +917,12 @@ __global__ __launch_bounds__(64) void k_alpha_beta(const SampleDesc *__restrict_
                                                    const float2 *__restrict__ prob, double *__restrict__ alpha,
                                                    double *__restrict__ beta, int *__restrict__ ealpha,
                                                    int *__restrict__ ebeta, double *__restrict__ log2z,
-                                                   float *__restrict__ loss) {
+                                                   float *__restrict__ loss, int rerun) {
     const SampleDesc d = desc[order[blockIdx.x >> 1]];
+    const int md = mode[d.index];
+    if (rerun && !(md & kModeRerun)) return;  // the rerun takes only the samples k_check_ab marked
     const bool bw = (blockIdx.x & 1) != 0;
-    const bool lm = mode[d.index] != 0;
+    const bool lm = md != 0;
     double *z = bw ? &log2z[d.index] : &log2z[B + d.index];
     // PF: diagonals per prefetch block.  A ring holds G*K/2*PF 16-byte loads
     // (the log domain: twice as many 8-byte ones); when a ring is first read,
@@ -928,6 +936,49 @@ __global__ __launch_bounds__(64) void k_alpha_beta(const SampleDesc *__restrict_
     default: run_sweep<4, 4, 2>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z); break;
     }
     if (bw && threadIdx.x == 0) loss[d.index] = (float)(-log2z[d.index] * kLn2D);
+}
+
+// Forward-backward check of the probability-domain recursions.  Every
+// alignment passes exactly one node of each anti-diagonal, so the sum over an
+// anti-diagonal of alpha * beta is P(y|x) on every diagonal.  The scaled
+// sweeps keep one exponent per block of diagonals, so a node far below its
+// diagonal's largest value can fall out of fp64's range; that is harmless
+// where the node carries no alignment mass (the far corners of long
+// diagonals), and it is what a sum off P reveals where it does (a lattice
+// whose paths favour one kind of edge by many nats per step, for example).
+// Mass lost at a node is missing from every later diagonal's sum (alpha) or
+// every earlier one's (beta), so a few diagonals spread over the lattice
+// reveal it: one wave for each of 16 per sample (bin midpoints, the last
+// being the last diagonal, compared with the backward P).  A sum that
+// differs from P by more than 4e-6 in log2 (fp64 sums, log2 to ~1e-7), or P
+// itself zero, marks the sample for the log-domain rerun of both its
+// recursions.
+constexpr int kCheckDiagonals = 16;
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__global__ __launch_bounds__(64) void k_check_ab(const SampleDesc *__restrict__ desc, int *__restrict__ mode,
+                                                 const double *__restrict__ alpha, const double *__restrict__ beta,
+                                                 const int *__restrict__ ealpha, const int *__restrict__ ebeta,
+                                                 const double *__restrict__ log2z) {
+    const SampleDesc d = desc[blockIdx.x / kCheckDiagonals];
+    const int j = blockIdx.x % kCheckDiagonals;
+    if (mode[d.index] != 0) return;  // already in the log domain, or marked
+    const int lane = threadIdx.x;
+    const int T = d.T, U = d.U, nd = T + U;
+    const double lz = log2z[d.index];
+    const int n = (j + 1 < kCheckDiagonals) ? (int)(((int64_t)(2 * j + 1) * nd) / (2 * kCheckDiagonals)) : nd - 1;
+    const int64_t q = d.ab_off + (int64_t)n * d.U1p;
+    double s = 0.0;
+    for (int u = max(0, n - T + 1) + lane; u <= min(n, U); u += 64) s += alpha[q + u] * beta[q + u];
+    s = wave_sum_d(s);
+    const double ls = log2_d(s) + (double)(ealpha[d.diag_off + ((n + 1) >> 3)] + ebeta[d.diag_off + ((nd - n) >> 3)]);
+    const bool bad = !(lz > kNegInfD) || !(s > 0.0) || !(fabs(ls - lz) <= 4e-6);
+    if (bad && lane == 0) atomicOr(&mode[d.index], kModeRerun);
 }
 
 // ------------------------------------------------------------ K3: gradient
@@ -1355,11 +1406,21 @@ hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream) {
     });
 }
 
+// The recursions, the forward-backward check of the probability-domain
+// samples, and the log-domain rerun of the samples the check marked (a
+// launch whose workgroups exit at once when none is).
 hipError_t launch_alpha_beta(const LaunchArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL(k_alpha_beta, dim3(2 * a.B), dim3(64), 0, stream, WS(const SampleDesc *, desc),
-                       WS(const int32_t *, order), a.B, WS(const int *, mode), WS(const float4 *, node),
-                       WS(const float2 *, prob), WS(double *, alpha), WS(double *, beta), WS(int *, ealpha),
-                       WS(int *, ebeta), WS(double *, log2z), a.loss);
+    for (int rerun = 0; rerun < 2; ++rerun) {
+        if (rerun) {
+            hipLaunchKernelGGL(k_check_ab, dim3(kCheckDiagonals * a.B), dim3(64), 0, stream, WS(const SampleDesc *, desc),
+                               WS(int *, mode), WS(const double *, alpha), WS(const double *, beta),
+                               WS(const int *, ealpha), WS(const int *, ebeta), WS(const double *, log2z));
+        }
+        hipLaunchKernelGGL(k_alpha_beta, dim3(2 * a.B), dim3(64), 0, stream, WS(const SampleDesc *, desc),
+                           WS(const int32_t *, order), a.B, WS(const int *, mode), WS(const float4 *, node),
+                           WS(const float2 *, prob), WS(double *, alpha), WS(double *, beta), WS(int *, ealpha),
+                           WS(int *, ebeta), WS(double *, log2z), a.loss, rerun);
+    }
     return hipGetLastError();
 }
 

@@ -676,6 +676,25 @@ def test_very_long_lattices(rl):
     check_against_oracle(w, loss, grad, "none")
 
 
+@pytest.mark.parametrize("gap,jitter", [(15.0, 0.0), (20.0, 0.0), (15.0, 1.0), (25.0, 2.0)])
+def test_peaked_blank_lattices(rl, gap, jitter):
+    """The blank logit `gap` nats above every label on every row (a model that favours blank everywhere): each
+    label costs ~gap nats, so along an anti-diagonal alpha falls by ~gap per label while the nodes that carry the
+    alignment mass sit hundreds of nats below the diagonal's largest value.  The probability-domain sweeps lose
+    them (fp64 range); the forward-backward check catches it and reruns the sample in the log domain.  Every loss
+    and the whole gradient against the oracle."""
+    Ts, Us, V = [300, 40, 120], [100, 39, 30], 8
+    w = _custom(Ts, Us, V, std=1.0, blank=0, reduction="none", seed=int(gap * 10 + jitter))
+    rng = np.random.default_rng(int(gap))
+    x = np.zeros(tuple(w.logits.shape), np.float32)
+    x[:, 0] = gap
+    x += (jitter * rng.standard_normal(x.shape)).astype(np.float32)
+    w.logits = torch.from_numpy(x).to("cuda")
+    loss, red, grad, flags = run(rl, w)
+    assert flags == 0
+    check_against_oracle(w, loss, grad, "none")
+
+
 # ------------------------------------------------------ randomized option sweep
 def _random_case(seed):
     """One seeded draw over the option space: batch shape, vocabulary, dtype, fused or not, blank position,
