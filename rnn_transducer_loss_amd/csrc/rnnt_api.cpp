@@ -515,6 +515,7 @@ rnnt_status build_mb_plan(int32_t B, int32_t V, int64_t N, const int32_t *T, con
     L.status = 0;
     off = 256;
     L.desc = off;   off = align_up(off + sizeof(SampleDesc) * B);
+    L.mode = off;   off = align_up(off + sizeof(int32_t) * B);  // per sample: 1 = recursions in the log domain
     L.den = off;    off = align_up(off + sizeof(float) * (size_t)phys);
     // the sweep's 16-byte loads of a lane's column pair may reach one slot past a plane's last
     L.wp = off;     off = align_up(off + sizeof(double) * ((size_t)(2 + nb) * (size_t)slot + 2));
@@ -565,8 +566,8 @@ rnnt_status multiblank_impl(const void *logits, rnnt_dtype dtype, int64_t N, int
     if (workspace_bytes < plan.lay.total) return RNNT_WORKSPACE_TOO_SMALL;
     if ((uintptr_t)workspace % kAlign != 0) return RNNT_INVALID_VALUE;
 
-    // the status word (cleared) and the descriptors go up in one copy
-    std::vector<uint8_t> head(plan.lay.desc + sizeof(SampleDesc) * B, 0);
+    // the status word (cleared), the descriptors and the mode words (cleared) go up in one copy
+    std::vector<uint8_t> head(plan.lay.mode + sizeof(int32_t) * B, 0);
     std::memcpy(head.data() + plan.lay.desc, plan.desc.data(), sizeof(SampleDesc) * B);
     st = upload(workspace, head, stream);
     if (st != RNNT_SUCCESS) return st;

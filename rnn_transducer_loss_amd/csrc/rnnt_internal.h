@@ -194,7 +194,7 @@ constexpr size_t kMbRingBytes = 64 * 1024;  // LDS of one sweep: the ring of rec
 // Workspace of the multi-blank path.  Byte offsets; the status word is at 0
 // and the sample descriptors at 256, as in the plain layout.
 struct MbLayout {
-    size_t status, desc, den, wp, alpha, beta, ealpha, ebeta, log2z, total;
+    size_t status, desc, mode, den, wp, alpha, beta, ealpha, ebeta, log2z, total;
     int64_t n_slots;    // skewed node slots, sum_i (T_i+U_i)(U_i+1)
     int64_t rows;       // rows of logits and grad: sum_i T_i(U_i+1) packed, B * max_T * max_U1 padded
     int U1p;            // columns of one stored diagonal: 128 times a power of two, for every sample

@@ -1715,7 +1715,7 @@ __device__ __forceinline__ D2 as_d2(u32x4 v) {
     return {__hiloint2double((int)v[1], (int)v[0]), __hiloint2double((int)v[3], (int)v[2])};
 }
 
-template <int G, int NB, bool bw>
+template <int G, int NB, bool bw, bool LOG>
 __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const MbParams &mp,
                                              const double *__restrict__ wp, int64_t n_slots,
                                              double *__restrict__ alpha, double *__restrict__ beta,
@@ -1727,7 +1727,7 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
     constexpr int P = MbSweepShape<G, NB>::P;
     const int lane = threadIdx.x;
     const int T = d.T, U = d.U, U1 = U + 1, nd = T + U, R = mp.R, M = R - 1;
-    for (int q = lane; q < R * U1p; q += 64) mb_ring[q] = 0.0;
+    for (int q = lane; q < R * U1p; q += 64) mb_ring[q] = LOG ? kNegInfD : 0.0;
     // ring entry of (diagonal slot s, group g): this lane's pair at 16-byte stride
     auto ring_at = [&](int sslot, int g) -> D2 * {
         return reinterpret_cast<D2 *>(mb_ring + (size_t)(sslot * G + g) * 128) + lane;
@@ -1799,7 +1799,8 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int c0 = 128 * g + 2 * lane;
-            cur[g] = {c0 == ue ? 1.0 : 0.0, c0 + 1 == ue ? 1.0 : 0.0};
+            const double one = LOG ? 0.0 : 1.0, zero = LOG ? kNegInfD : 0.0;
+            cur[g] = {c0 == ue ? one : zero, c0 + 1 == ue ? one : zero};
             *ring_at(slot, g) = cur[g];
         }
         if (!bw) {
@@ -1817,7 +1818,7 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             sl[i] = (bw ? n + mp.dur[i] : n - mp.dur[i]) & M;
-            shg[i] = __builtin_amdgcn_readlane(eh, sl[i]) - E;
+            shg[i] = LOG ? 0 : __builtin_amdgcn_readlane(eh, sl[i]) - E;
         }
         // Cross-lane neighbours.  Forward: column 2l-1 of the finished
         // diagonal and the label weight of column 2l-1 come from lane l-1's
@@ -1825,10 +1826,11 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
         // Backward: column 2l+2 of the finished diagonal from lane l+1's
         // first value (lane 63 of group g: lane 0 of group g+1, or zero).
         double side_v[G], side_w[G];
-        if constexpr (G == 1) {
+        if constexpr (G == 1 && !LOG) {
             side_v[0] = bw ? shift_down_zero(cur[0].a) : shift_up_zero(cur[0].b);
             side_w[0] = bw ? 0.0 : shift_up_zero(w[0][1].b);
         } else {
+            const double zv = LOG ? kNegInfD : 0.0;  // an edge lane's missing neighbour
             double nb_v[G], nb_w[G];
 #pragma unroll
             for (int g = 0; g < G; ++g) {
@@ -1838,10 +1840,10 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 if (bw) {
-                    side_v[g] = (lane == 63) ? (g + 1 < G ? nb_v[g + 1] : 0.0) : nb_v[g];
+                    side_v[g] = (lane == 63) ? (g + 1 < G ? nb_v[g + 1] : zv) : nb_v[g];
                     side_w[g] = 0.0;
                 } else {
-                    side_v[g] = (lane == 0) ? (g > 0 ? nb_v[g - 1] : 0.0) : nb_v[g];
+                    side_v[g] = (lane == 0) ? (g > 0 ? nb_v[g - 1] : zv) : nb_v[g];
                     side_w[g] = (lane == 0) ? (g > 0 ? nb_w[g - 1] : 0.0) : nb_w[g];
                 }
             }
@@ -1863,26 +1865,47 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
                 // label: forward, weight of column u-1 and value of column u-1; backward, own weight and u+1
                 const double wy = bw ? (h ? w[g][1].b : w[g][1].a) : (h ? w[g][1].a : side_w[g]);
                 const double sv = bw ? (h ? side_v[g] : cur[g].b) : (h ? cur[g].a : side_v[g]);
-                double acc = fma(wy, sv, wb * cv);
+                double acc;
+                if constexpr (LOG) {
+                    // log2 values: the weights' logs, then a log-sum-exp of the 2 + NB terms
+                    double tm[2 + NB];
+                    tm[0] = log2_d(wb) + cv;
+                    tm[1] = log2_d(wy) + sv;
 #pragma unroll
-                for (int i = 0; i < NB; ++i) {
-                    // forward from (t-d_i,u); backward to (t+d_i,u)
-                    const double wg = h ? w[g][2 + i].b : w[g][2 + i].a;
-                    const double sr = h ? src[i].b : src[i].a;
-                    acc = fma(wg, __builtin_amdgcn_ldexp(sr, shg[i]), acc);
+                    for (int i = 0; i < NB; ++i)
+                        tm[2 + i] = log2_d(h ? w[g][2 + i].b : w[g][2 + i].a) + (h ? src[i].b : src[i].a);
+                    double m = tm[0];
+#pragma unroll
+                    for (int k = 1; k < 2 + NB; ++k) m = fmax(m, tm[k]);
+                    float sum = 0.f;
+#pragma unroll
+                    for (int k = 0; k < 2 + NB; ++k) sum += exp2_fast((float)(tm[k] - m));
+                    acc = (m == kNegInfD) ? kNegInfD : m + (double)log2_fast(sum);
+                } else {
+                    acc = fma(wy, sv, wb * cv);
+#pragma unroll
+                    for (int i = 0; i < NB; ++i) {
+                        // forward from (t-d_i,u); backward to (t+d_i,u)
+                        const double wg = h ? w[g][2 + i].b : w[g][2 + i].a;
+                        const double sr = h ? src[i].b : src[i].a;
+                        acc = fma(wg, __builtin_amdgcn_ldexp(sr, shg[i]), acc);
+                    }
                 }
                 if (h) nx[g].b = acc;
                 else nx[g].a = acc;
             }
         }
         // renormalise by a power of two (a diagonal of zeros keeps its exponent)
-        int eb = 0;
+        int sh = 0;
+        if constexpr (!LOG) {
+            int eb = 0;
 #pragma unroll
-        for (int g = 0; g < G; ++g)
-            eb = max(eb, max((__double2hiint(nx[g].a) >> 20) & 0x7ff, (__double2hiint(nx[g].b) >> 20) & 0x7ff));
-        eb = wave_max_nonneg(eb);
-        const int sh = eb == 0 ? 0 : eb - 1023;
-        E += sh;
+            for (int g = 0; g < G; ++g)
+                eb = max(eb, max((__double2hiint(nx[g].a) >> 20) & 0x7ff, (__double2hiint(nx[g].b) >> 20) & 0x7ff));
+            eb = wave_max_nonneg(eb);
+            sh = eb == 0 ? 0 : eb - 1023;
+            E += sh;
+        }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             cur[g] = {__builtin_amdgcn_ldexp(nx[g].a, -sh), __builtin_amdgcn_ldexp(nx[g].b, -sh)};
@@ -1919,7 +1942,7 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
     const int ue = bw ? 0 : U;
     const D2 mine = *ring_at(slot, ue >> 7);
     const double v = readlane_d((ue & 1) ? mine.b : mine.a, (ue & 127) >> 1);
-    const double l2 = (v > 0.0) ? log2_d(v) + (double)E : kNegInfD;
+    const double l2 = LOG ? v : ((v > 0.0) ? log2_d(v) + (double)E : kNegInfD);
     if (lane == 0) {
         if (bw) {
             log2z[d.index] = l2;
@@ -1930,15 +1953,75 @@ __device__ __forceinline__ void mb_sweep_dir(const SampleDesc &d, int B, const M
     }
 }
 
-template <int G, int NB>
+// LOG: the log-domain rerun, of the samples k_mb_check marked only.
+template <int G, int NB, bool LOG>
 __global__ __launch_bounds__(64) void k_mb_sweep(const SampleDesc *__restrict__ desc, int B, MbParams mp,
                                                  const double *__restrict__ wp, int64_t n_slots,
                                                  double *__restrict__ alpha, double *__restrict__ beta,
                                                  int *__restrict__ ealpha, int *__restrict__ ebeta,
-                                                 double *__restrict__ log2z, float *__restrict__ loss) {
+                                                 double *__restrict__ log2z, float *__restrict__ loss,
+                                                 const int *__restrict__ mode) {
     const SampleDesc d = desc[blockIdx.x >> 1];
-    if (blockIdx.x & 1) mb_sweep_dir<G, NB, true>(d, B, mp, wp, n_slots, alpha, beta, ealpha, ebeta, log2z, loss);
-    else mb_sweep_dir<G, NB, false>(d, B, mp, wp, n_slots, alpha, beta, ealpha, ebeta, log2z, loss);
+    if (LOG && mode[d.index] == 0) return;
+    if (blockIdx.x & 1)
+        mb_sweep_dir<G, NB, true, LOG>(d, B, mp, wp, n_slots, alpha, beta, ealpha, ebeta, log2z, loss);
+    else
+        mb_sweep_dir<G, NB, false, LOG>(d, B, mp, wp, n_slots, alpha, beta, ealpha, ebeta, log2z, loss);
+}
+
+// Forward-backward check of the probability-domain sweeps.  Every alignment
+// emits label u exactly once, so the sum over t of alpha(t,u) P(label)
+// beta(t,u+1) is P(y|x) for every u < U.  Renormalising each diagonal by its
+// largest value loses the nodes far below it (fp64's range); harmless where
+// they carry no alignment mass, wrong where they do (big blanks make
+// advancing in t cheap, so on a long lattice the nodes with more frames done
+// can lie hundreds of nats above those with more labels done, which finish
+// more cheaply).  One wave for each of 16 columns spread over [0, U) per
+// sample (bin midpoints, the last column U-1); the terms, on different
+// diagonals, are summed as log2 values.  A sum that differs from the
+// backward P by more than 4e-6 in log2, or P itself zero, marks the sample
+// for the log-domain rerun.  Lattices without labels have one node per
+// diagonal and need no check.
+__global__ __launch_bounds__(64) void k_mb_check(const SampleDesc *__restrict__ desc, int *__restrict__ mode,
+                                                 const double *__restrict__ wp, int64_t n_slots, int U1p,
+                                                 const double *__restrict__ alpha, const double *__restrict__ beta,
+                                                 const int *__restrict__ ealpha, const int *__restrict__ ebeta,
+                                                 const double *__restrict__ log2z) {
+    constexpr int J = 16;
+    const SampleDesc d = desc[blockIdx.x / J];
+    const int j = blockIdx.x % J;
+    const int T = d.T, U = d.U, U1 = U + 1;
+    if (U == 0 || mode[d.index] != 0) return;
+    const int lane = threadIdx.x;
+    const double lz = log2z[d.index];
+    const int u = (j + 1 < J) ? (int)(((int64_t)(2 * j + 1) * U) / (2 * J)) : U - 1;
+    const int64_t eo = d.diag_off + d.index;
+    double m = kNegInfD, s = 0.0;
+    for (int t = lane; t < T; t += 64) {
+        const int n = t + u;
+        const double la = log2_d(alpha[d.ab_off + (int64_t)n * U1p + u]) + (double)ealpha[eo + n];
+        const double lw = log2_d(wp[n_slots + d.slot_off + (int64_t)n * U1 + u]);
+        const double lb = log2_d(beta[d.ab_off + (int64_t)(n + 1) * U1p + u + 1]) + (double)ebeta[eo + n + 1];
+        const double l = la + lw + lb;
+        if (l > m) {
+            s = s * (double)exp2_fast((float)(m - l)) + 1.0;
+            m = l;
+        } else if (l > kNegInfD) {
+            s += (double)exp2_fast((float)(l - m));
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const double m2 = __shfl_xor(m, off, 64);
+        const double s2 = __shfl_xor(s, off, 64);
+        const double mm = fmax(m, m2);
+        s = (mm == kNegInfD) ? 0.0
+                             : s * (double)exp2_fast((float)(m - mm)) + s2 * (double)exp2_fast((float)(m2 - mm));
+        m = mm;
+    }
+    const double ls = m + log2_d(s);
+    const bool bad = !(lz > kNegInfD) || !(m > kNegInfD) || !(fabs(ls - lz) <= 4e-6);
+    if (bad && lane == 0) atomicOr(&mode[d.index], 1);
 }
 
 // The gradient terms of packed row r: the softmax shift (occupancy with the
@@ -1958,7 +2041,7 @@ __device__ __forceinline__ MbRowTerms mb_row_terms(const SampleDesc &d, int64_t 
                                                    const double *__restrict__ alpha,
                                                    const double *__restrict__ beta, const int *__restrict__ ealpha,
                                                    const int *__restrict__ ebeta, const double *__restrict__ log2z,
-                                                   float scale, float fastemit) {
+                                                   float scale, float fastemit, bool lm) {
     const int U1 = d.U + 1;
     const int n = t + u;
     const int64_t s = d.slot_off + (int64_t)n * U1 + u;
@@ -1969,14 +2052,16 @@ __device__ __forceinline__ MbRowTerms mb_row_terms(const SampleDesc &d, int64_t 
         if (t2 == d.T && u2 == d.U) return 0.0;
         if (t2 >= d.T || u2 > d.U) return kNegInfD;
         const int n2 = t2 + u2;
-        return log2_d(beta[d.ab_off + (int64_t)n2 * U1p + u2]) + (double)ebeta[eo + n2];
+        const double v = beta[d.ab_off + (int64_t)n2 * U1p + u2];
+        return lm ? v : log2_d(v) + (double)ebeta[eo + n2];
     };
     double lo = kNegInfD, lb = kNegInfD, ly = kNegInfD;
     double lg[kMaxBigBlanks];
 #pragma unroll
     for (int i = 0; i < kMaxBigBlanks; ++i) lg[i] = kNegInfD;
     if (lz != kNegInfD) {
-        const double la = log2_d(alpha[d.ab_off + (int64_t)n * U1p + u]) + (double)ealpha[eo + n] - lz;
+        const double av = alpha[d.ab_off + (int64_t)n * U1p + u];
+        const double la = (lm ? av : log2_d(av) + (double)ealpha[eo + n]) - lz;
         lo = la + lbeta(t, u);
         lb = la + log2_d(wp[s]) + lbeta(t + 1, u);
         if (u < d.U) ly = la + log2_d(wp[n_slots + s]) + lbeta(t, u + 1);
@@ -2013,7 +2098,8 @@ __global__ __launch_bounds__(256) void k_mb_grad(const T *__restrict__ logits, T
                                                  int64_t n_slots, const double *__restrict__ alpha,
                                                  const double *__restrict__ beta, const int *__restrict__ ealpha,
                                                  const int *__restrict__ ebeta, const double *__restrict__ log2z,
-                                                 float clamp, float scale, float fastemit, int64_t row_base) {
+                                                 const int *__restrict__ mode, float clamp, float scale,
+                                                 float fastemit, int64_t row_base) {
     const int lane = threadIdx.x & 63;
     const int64_t r = row_base + (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (r >= N) return;
@@ -2027,7 +2113,7 @@ __global__ __launch_bounds__(256) void k_mb_grad(const T *__restrict__ logits, T
         return;
     }
     const MbRowTerms rt = mb_row_terms(d, r, t, u, V, fused, mp, U1p, targets, S, den, wp, n_slots, alpha, beta,
-                                       ealpha, ebeta, log2z, scale, fastemit);
+                                       ealpha, ebeta, log2z, scale, fastemit, mode[d.index] != 0);
     const bool do_clamp = clamp > 0.f;
     const float cl = clamp * scale;
     const T *x = logits + r * (int64_t)V;
@@ -2125,7 +2211,8 @@ __global__ __launch_bounds__(64) void k_mb_grad_v(const T *__restrict__ logits, 
                                                   int64_t n_slots, const double *__restrict__ alpha,
                                                   const double *__restrict__ beta, const int *__restrict__ ealpha,
                                                   const int *__restrict__ ebeta, const double *__restrict__ log2z,
-                                                  float clamp, float scale, float fastemit, int64_t row_base) {
+                                                  const int *__restrict__ mode, float clamp, float scale,
+                                                  float fastemit, int64_t row_base) {
     using Vec = typename Raw<T>::vec;
     constexpr int VEC = Raw<T>::kVec;
     const int lane = threadIdx.x;
@@ -2153,7 +2240,7 @@ __global__ __launch_bounds__(64) void k_mb_grad_v(const T *__restrict__ logits, 
             if (FULL || i * 64 + lane < nvec) xv[i] = load_raw<T, true>(x + (int64_t)(i * 64 + lane) * VEC);
     }
     MbRowTerms rt = mb_row_terms(d, r, t, u, V, fused, mp, U1p, targets, S, den, wp, n_slots, alpha, beta, ealpha,
-                                 ebeta, log2z, scale, fastemit);
+                                 ebeta, log2z, scale, fastemit, mode[d.index] != 0);
     const bool do_clamp = clamp > 0.f;
     const float cl = clamp * scale;
 #pragma unroll
@@ -2270,20 +2357,32 @@ hipError_t launch_mb_rows(const MbArgs &a, hipStream_t stream) {
 hipError_t launch_mb_sweep(const MbArgs &a, hipStream_t stream) {
     const MbParams mp = mb_params(a);
     const size_t lds = mb_ring_bytes(a.lay.U1p, mp.R - 1);
-    auto go = [&](auto kern) {
+    // The probability-domain sweeps, the forward-backward check, and the
+    // log-domain rerun of the samples it marked (a launch whose workgroups
+    // exit at once when none is).
+    auto go = [&](auto kern, auto klog) {
         hipLaunchKernelGGL(kern, dim3(2 * a.B), dim3(64), lds, stream, MBWS(const SampleDesc *, desc), a.B, mp,
                            MBWS(const double *, wp), a.lay.n_slots, MBWS(double *, alpha), MBWS(double *, beta),
-                           MBWS(int *, ealpha), MBWS(int *, ebeta), MBWS(double *, log2z), a.loss);
+                           MBWS(int *, ealpha), MBWS(int *, ebeta), MBWS(double *, log2z), a.loss,
+                           MBWS(const int *, mode));
+        hipLaunchKernelGGL(k_mb_check, dim3(16 * a.B), dim3(64), 0, stream, MBWS(const SampleDesc *, desc),
+                           MBWS(int *, mode), MBWS(const double *, wp), a.lay.n_slots, a.lay.U1p,
+                           MBWS(const double *, alpha), MBWS(const double *, beta), MBWS(const int *, ealpha),
+                           MBWS(const int *, ebeta), MBWS(const double *, log2z));
+        hipLaunchKernelGGL(klog, dim3(2 * a.B), dim3(64), lds, stream, MBWS(const SampleDesc *, desc), a.B, mp,
+                           MBWS(const double *, wp), a.lay.n_slots, MBWS(double *, alpha), MBWS(double *, beta),
+                           MBWS(int *, ealpha), MBWS(int *, ebeta), MBWS(double *, log2z), a.loss,
+                           MBWS(const int *, mode));
         return hipGetLastError();
     };
     auto by_nb = [&](auto jc) -> hipError_t {
         constexpr int G = decltype(jc)::value;
         switch (a.nb) {
-        case 0: return go(k_mb_sweep<G, 0>);
-        case 1: return go(k_mb_sweep<G, 1>);
-        case 2: return go(k_mb_sweep<G, 2>);
-        case 3: return go(k_mb_sweep<G, 3>);
-        case 4: return go(k_mb_sweep<G, 4>);
+        case 0: return go(k_mb_sweep<G, 0, false>, k_mb_sweep<G, 0, true>);
+        case 1: return go(k_mb_sweep<G, 1, false>, k_mb_sweep<G, 1, true>);
+        case 2: return go(k_mb_sweep<G, 2, false>, k_mb_sweep<G, 2, true>);
+        case 3: return go(k_mb_sweep<G, 3, false>, k_mb_sweep<G, 3, true>);
+        case 4: return go(k_mb_sweep<G, 4, false>, k_mb_sweep<G, 4, true>);
         }
         return hipErrorInvalidValue;
     };
@@ -2313,7 +2412,7 @@ hipError_t launch_mb_grad(const MbArgs &a, hipStream_t stream) {
                                    MBWS(const float *, den), MBWS(const double *, wp), a.lay.n_slots,
                                    MBWS(const double *, alpha), MBWS(const double *, beta),
                                    MBWS(const int *, ealpha), MBWS(const int *, ebeta), MBWS(const double *, log2z),
-                                   a.clamp, a.grad_scale, a.fastemit, b0);
+                                   MBWS(const int *, mode), a.clamp, a.grad_scale, a.fastemit, b0);
             }
             return hipGetLastError();
         });
@@ -2327,7 +2426,8 @@ hipError_t launch_mb_grad(const MbArgs &a, hipStream_t stream) {
                                MBWS(const SampleDesc *, desc), a.B, a.targets, a.S, MBWS(const float *, den),
                                MBWS(const double *, wp), a.lay.n_slots, MBWS(const double *, alpha),
                                MBWS(const double *, beta), MBWS(const int *, ealpha), MBWS(const int *, ebeta),
-                               MBWS(const double *, log2z), a.clamp, a.grad_scale, a.fastemit, b0 * 4);
+                               MBWS(const double *, log2z), MBWS(const int *, mode), a.clamp, a.grad_scale,
+                               a.fastemit, b0 * 4);
         }
         return hipGetLastError();
     });

@@ -226,6 +226,32 @@ def test_multiblank_very_long_lattices(rl):
     check_mb(w, loss, grad, "none")
 
 
+def test_multiblank_wide_alpha_range(rl):
+    """A big blank of 12 frames on a lattice with twice as many labels as frames (T=116, U=238): advancing in t
+    is so cheap that on late anti-diagonals the nodes with more frames done lie ~e^745 above those with more labels
+    done, which carry alignment mass because they finish cheaply.  The probability-domain sweep loses them; the
+    label-count check catches it and the sample is rerun in the log domain.  Every loss and the whole gradient."""
+    w = _mb([116, 8], [238, 119], 1024, [352], [12], 0.05, dtype=torch.float32, std=2.0, blank=675, clamp=-1.0,
+            fused=True, prenormalise=False, reduction="mean", seed=3001)
+    loss, red, grad, flags = run_mb(rl, w, fastemit=0.2)
+    assert flags == 0
+    check_mb(w, loss, grad, "mean", fastemit=0.2)
+
+
+@pytest.mark.parametrize("gap", [15.0, 25.0])
+def test_multiblank_peaked_blank(rl, gap):
+    """The blank logit `gap` nats above every other class (labels and the big blanks alike): alpha falls by ~gap
+    per label along an anti-diagonal, so the probability-domain sweep loses the nodes that carry the mass and the
+    sample is rerun in the log domain.  Every loss and the whole gradient."""
+    w = _mb([300, 60], [100, 50], 8, [7, 6], [4, 8], 0.0, std=1.0, blank=0, reduction="none", seed=int(gap))
+    x = np.zeros(tuple(w.logits.shape), np.float32)
+    x[:, 0] = gap
+    w.logits = torch.from_numpy(x).to("cuda")
+    loss, red, grad, flags = run_mb(rl, w)
+    assert flags == 0
+    check_mb(w, loss, grad, "none")
+
+
 @pytest.mark.parametrize("seed", range(2000, 2016))
 def test_multiblank_random_option_sweep(rl, seed):
     """Seeded draws over the multi-blank option space: batch shape, vocabulary, dtype, fused or not, the big
