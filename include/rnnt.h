@@ -144,6 +144,13 @@ rnnt_status rnnt_loss_fused_workspace_size(int32_t B, int32_t V, int64_t N, rnnt
  * Invalid label values are only visible on the device: they set
  * RNNT_DEV_BAD_TARGET, and a label outside [0, V) makes its sample's
  * alignment impossible (loss +inf, gradient 0 for that sample).
+ * Numerics: the recursions run in fp64 probabilities scaled by a power of
+ * two per block of anti-diagonals.  A sample takes the log domain instead
+ * when one of its edge log-probabilities lies outside [-80, 80], or when
+ * the forward-backward identity (alpha * beta summed over an anti-diagonal
+ * is P(y|x)) fails by more than 4e-6 in log2 on one of 16 checked
+ * diagonals: nodes carrying alignment mass fell out of fp64's range; the
+ * sample is then recomputed in the log domain within the same call.
  */
 rnnt_status rnnt_loss_fused(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V,
                             const int32_t *targets, int32_t S,
@@ -241,10 +248,14 @@ rnnt_status rnnt_grad_scale_padded(void *grad, rnnt_dtype dtype, int32_t max_T, 
  * longest duration is 7, at 512 it is 15), or a sample with
  * (T_i + U_i) * U1p * 8 >= 2^31.  A label equal to blank or to a big
  * blank sets RNNT_DEV_BAD_TARGET (read with rnnt_loss_fused_check).
- * The recursion runs in fp64 probabilities renormalised per anti-diagonal:
- * an edge whose log-probability (less sigma) is below about -745 counts as
- * probability zero (rnnt_loss_fused has a log-domain fallback for such
- * inputs; this path does not).
+ * The recursion runs in fp64 probabilities renormalised per anti-diagonal;
+ * when the identity that every alignment emits each label once (the sum
+ * over t of alpha(t,u) P(label) beta(t,u+1) is P(y|x)) fails by more than
+ * 4e-6 in log2 on one of 16 checked columns, nodes carrying alignment mass
+ * fell out of fp64's range and the sample is recomputed in the log domain
+ * within the same call.  The edge weights are kept as fp64 probabilities,
+ * so an edge whose log-probability (less sigma) is below about -745 counts
+ * as probability zero in either domain.
  */
 rnnt_status rnnt_multiblank_workspace_size(int32_t B, int32_t V, int64_t N, rnnt_dtype dtype,
                                            const int32_t *logit_lengths, const int32_t *target_lengths,
