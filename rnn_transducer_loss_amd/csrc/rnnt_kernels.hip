@@ -1034,8 +1034,11 @@ __device__ __forceinline__ RowTerms row_terms(const SampleDesc &d, const SampleT
         if (u < d.U) ly = a2 + (double)l.y * kLog2eD + node_log2(beta, eb, q + U1p + 1, gnext, st.log_mode);
     }
     // occ + lambda flow_y = occ (1 + lambda 2^(ly - lo)); flow_y <= occ, so
-    // the exponent is at most about zero.
-    if (fastemit > 0.f && ly != kNegInfD) lo += (double)log2f(1.f + fastemit * exp2_fast((float)(ly - lo)));
+    // the exponent is at most about zero.  A node whose occupancy underflowed
+    // (a far corner of the lattice in the probability domain) keeps it at
+    // zero: -inf + inf would be NaN.
+    if (fastemit > 0.f && ly != kNegInfD && lo != kNegInfD)
+        lo += (double)log2f(1.f + fastemit * exp2_fast((float)(ly - lo)));
     RowTerms r;
     r.shift2 = fused ? (float)(lo - (double)l.z * kLog2eD) + log2_scale : kNegInf;
     r.fb = exp2_fast((float)lb) * scale;

@@ -695,6 +695,20 @@ def test_peaked_blank_lattices(rl, gap, jitter):
     check_against_oracle(w, loss, grad, "none")
 
 
+@pytest.mark.parametrize("Ts,Us,V,blank,std,clamp,reduction,seed", [
+    ([131], [537], 2, 1, 8.0, -1.0, "none", 5091),
+    ([299, 247, 131], [152, 121, 472], 8, 7, 2.0, 0.1, "sum", 5113),
+])
+def test_fastemit_on_lattices_with_underflowing_corners(rl, Ts, Us, V, blank, std, clamp, reduction, seed):
+    """Wide lattices (U up to 537) whose far corners underflow in the probability domain while carrying no
+    alignment mass: the FastEmit term must leave those nodes' zero occupancy alone (it produced NaN gradients
+    there).  Every loss and the whole gradient against the oracle."""
+    w = _custom(Ts, Us, V, std=std, blank=blank, clamp=clamp, reduction=reduction, seed=seed)
+    loss, red, grad, flags = run(rl, w, fastemit=0.3)
+    assert flags == 0
+    check_against_oracle(w, loss, grad, reduction, fastemit=0.3)
+
+
 # ------------------------------------------------------ randomized option sweep
 def _random_case(seed):
     """One seeded draw over the option space: batch shape, vocabulary, dtype, fused or not, blank position,
