@@ -750,4 +750,9 @@ def test_random_option_sweep(rl, seed):
                                             fastemit_lambda=c["lam"])
         torch.cuda.synchronize()
         rows, pad = _padded_rows(w, gp_, max_T, max_U1)
+        if c["unaligned"]:
+            # unaligned rows take the scalar row kernels, the padded copy the vector ones: the bitwise reference
+            # is the same packed logits, aligned
+            w.logits = w.logits.contiguous().clone()
+            loss, red, grad, flags = run(rl, w, fastemit=c["lam"])
         assert torch.equal(lp_, loss) and torch.equal(rows, grad) and bool((pad == 0).all())
