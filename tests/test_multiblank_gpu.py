@@ -252,6 +252,22 @@ def test_multiblank_peaked_blank(rl, gap):
     check_mb(w, loss, grad, "none")
 
 
+def test_multiblank_cheap_big_blank_expensive_blank(rl):
+    """Logits of 0 for a 16-frame big blank, -80 for the standard blank, small for the labels: with five labels, ten
+    of every sixteen diagonals are reached only through standard blanks, so the diagonal where the next big blank
+    lands sits ~e^800 above the one before it, past fp64's range in the probability-domain sweep; the check sends
+    the sample to the log domain.  Every loss and the whole gradient."""
+    w = _mb([100, 33], [5, 3], 12, [11], [16], 0.0, std=1.0, blank=0, reduction="none", seed=77)
+    rng = np.random.default_rng(77)
+    x = (0.5 * rng.standard_normal(tuple(w.logits.shape))).astype(np.float32)
+    x[:, 0] = -80.0
+    x[:, 11] = 0.0
+    w.logits = torch.from_numpy(x).to("cuda")
+    loss, red, grad, flags = run_mb(rl, w)
+    assert flags == 0
+    check_mb(w, loss, grad, "none")
+
+
 @pytest.mark.parametrize("seed", range(2000, 2016))
 def test_multiblank_random_option_sweep(rl, seed):
     """Seeded draws over the multi-blank option space: batch shape, vocabulary, dtype, fused or not, the big
