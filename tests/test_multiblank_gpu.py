@@ -268,6 +268,34 @@ def test_multiblank_cheap_big_blank_expensive_blank(rl):
     check_mb(w, loss, grad, "none")
 
 
+@pytest.mark.parametrize("fused,frac", [(True, 0.3), (False, 0.7)])
+def test_multiblank_masked_vocabulary(rl, fused, frac):
+    """-inf logits (or log-probs) on a random share of the classes other than the standard blank, big blanks
+    included: exactly impossible edges, and samples with no possible alignment (loss +inf, zero gradient)."""
+    Ts, Us, V = [40, 25, 60, 9], [30, 12, 45, 0], 29
+    ids, durs = [28, 27], [2, 5]
+    w = _mb(Ts, Us, V, ids, durs, 0.0, std=2.0 if fused else 1.5, blank=0, fused=fused, prenormalise=not fused,
+            reduction="none", seed=int(frac * 100))
+    rng = np.random.default_rng(int(frac * 100) + 1)
+    x = w.logits.float().cpu().numpy()
+    m = rng.random(x.shape) < frac
+    m[:, 0] = False
+    x[m] = -np.inf
+    w.logits = torch.from_numpy(x).to("cuda")
+    loss, red, grad, flags = run_mb(rl, w, fastemit=0.1)
+    for i in range(w.B):
+        T, U = int(w.logit_lengths[i]), int(w.target_lengths[i])
+        r = oracle.multiblank_sample(x[w.rows(i)], T, U, w.targets[i], 0, ids, durs, 0.0, fused, -1.0, 0.1,
+                                     want_grad=True)
+        g = grad[w.rows(i)].detach().double().cpu().numpy()
+        lg = float(loss[i].item())
+        if np.isinf(r.loss):
+            assert np.isinf(lg) and lg > 0 and np.all(g == 0), f"sample {i}"
+        else:
+            assert abs(lg - r.loss) <= 1e-5 * max(1.0, abs(r.loss)), f"sample {i}: loss {lg} vs oracle {r.loss}"
+            assert np.isfinite(g).all() and np.abs(g - r.grad).max() <= 1e-5, f"sample {i}: gradient"
+
+
 @pytest.mark.parametrize("seed", range(2000, 2016))
 def test_multiblank_random_option_sweep(rl, seed):
     """Seeded draws over the multi-blank option space: batch shape, vocabulary, dtype, fused or not, the big

@@ -709,6 +709,43 @@ def test_fastemit_on_lattices_with_underflowing_corners(rl, Ts, Us, V, blank, st
     check_against_oracle(w, loss, grad, reduction, fastemit=0.3)
 
 
+def check_masked(w, loss, grad, oracle_fn, gtol=1e-5):
+    """Per-sample comparison that admits impossible alignments: an infinite oracle loss must come back as +inf
+    with a zero gradient, a finite one to the fp32 tolerances."""
+    for i in range(w.B):
+        r = oracle_fn(i)
+        g = grad[w.rows(i)].detach().double().cpu().numpy()
+        lg = float(loss[i].item())
+        if np.isinf(r.loss):
+            assert np.isinf(lg) and lg > 0, f"sample {i}: loss {lg}, oracle +inf"
+            assert np.all(g == 0), f"sample {i}: impossible alignment with a non-zero gradient"
+        else:
+            assert abs(lg - r.loss) <= 1e-5 * max(1.0, abs(r.loss)), f"sample {i}: loss {lg} vs oracle {r.loss}"
+            assert np.isfinite(g).all() and np.abs(g - r.grad).max() <= gtol, f"sample {i}: gradient"
+
+
+@pytest.mark.parametrize("fused,frac,lam", [(True, 0.3, 0.0), (True, 0.7, 0.2), (False, 0.3, 0.2), (False, 0.7, 0.0)])
+def test_masked_vocabulary(rl, fused, frac, lam, oracle_mod):
+    """-inf logits (or log-probs) on a random share of the non-blank classes of every row: edges that are exactly
+    impossible, and samples whose every alignment is (loss +inf, zero gradient).  Every loss and gradient."""
+    Ts, Us, V = [40, 25, 60, 7, 33], [30, 12, 45, 6, 0], 29
+    w = _custom(Ts, Us, V, std=2.0 if fused else 1.5, blank=0, fused=fused, prenormalise=not fused,
+                reduction="none", seed=int(frac * 100) + fused)
+    rng = np.random.default_rng(int(frac * 100))
+    x = w.logits.float().cpu().numpy()
+    m = rng.random(x.shape) < frac
+    m[:, 0] = False
+    x[m] = -np.inf
+    w.logits = torch.from_numpy(x).to("cuda")
+    loss, red, grad, flags = run(rl, w, fastemit=lam)
+
+    def ref(i):
+        T, U = int(w.logit_lengths[i]), int(w.target_lengths[i])
+        return oracle_mod.sample(x[w.rows(i)], T, U, w.targets[i], 0, fused, -1.0, want_grad=True,
+                                 fastemit_lambda=lam)
+    check_masked(w, loss, grad, ref)
+
+
 # ------------------------------------------------------ randomized option sweep
 def _random_case(seed):
     """One seeded draw over the option space: batch shape, vocabulary, dtype, fused or not, blank position,
