@@ -88,14 +88,15 @@ def normalize_blank(blank: int, V: int) -> int:
 
 
 class SampleResult:
-    __slots__ = ("loss", "loss_alpha", "grad", "alpha", "beta")
+    __slots__ = ("loss", "loss_alpha", "grad", "alpha", "beta", "bad_target")
 
-    def __init__(self, loss, loss_alpha, grad, alpha, beta):
+    def __init__(self, loss, loss_alpha, grad, alpha, beta, bad_target=False):
         self.loss = loss
         self.loss_alpha = loss_alpha
         self.grad = grad
         self.alpha = alpha
         self.beta = beta
+        self.bad_target = bad_target
 
 
 _DT = {np.dtype(np.float64): 0, np.dtype(np.float32): 1, np.dtype(np.float16): 2}
@@ -108,7 +109,7 @@ def half_to_double(h: int) -> float:
 
 def sample(x, T: int, U: int, y, blank: int, fused: bool = True, clamp: float = -1.0,
            want_grad: bool = True, want_tables: bool = False, rows=None,
-           fastemit_lambda: float = 0.0) -> SampleResult:
+           fastemit_lambda: float = 0.0, allow_bad_targets: bool = False) -> SampleResult:
     """Loss (and optionally gradient / alpha / beta tables) of one sample.
 
     ``x`` holds the sample's T*(U+1) rows of V values as float64, float32 or
@@ -117,6 +118,11 @@ def sample(x, T: int, U: int, y, blank: int, fused: bool = True, clamp: float = 
     restricts the gradient to those rows, returned in that order; by default
     every row.  The loss is the beta-path value -beta(0,0); ``loss_alpha`` is
     the alpha-path value kept for the cross-check.
+
+    A label equal to blank or outside [0, V) (the build post's section 5.2
+    rules blank out of the labels) leaves the sample without any alignment:
+    loss +inf and a zero gradient.  Such a sample raises ValueError unless
+    ``allow_bad_targets`` is set; then the result carries ``bad_target``.
     """
     lib = _load()
     x = np.asarray(x)
@@ -144,11 +150,11 @@ def sample(x, T: int, U: int, y, blank: int, fused: bool = True, clamp: float = 
         int(blank), int(bool(fused)), float(clamp), float(fastemit_lambda),
         rr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)) if rr is not None else None, nr,
         _ptr(grad), _ptr(al), _ptr(be), ctypes.byref(la), ctypes.byref(lb))
-    if rc == ORACLE_BAD_TARGET:
+    if rc == ORACLE_BAD_TARGET and not allow_bad_targets:
         raise ValueError("target label equal to blank or outside [0, V)")
-    if rc != ORACLE_OK:
+    if rc not in (ORACLE_OK, ORACLE_BAD_TARGET):
         raise ValueError(f"oracle rejected the arguments (code {rc})")
-    return SampleResult(lb.value, la.value, grad, al, be)
+    return SampleResult(lb.value, la.value, grad, al, be, rc == ORACLE_BAD_TARGET)
 
 
 def batch(logits, targets, logit_lengths, target_lengths, blank: int = -1, clamp: float = -1.0,
@@ -194,7 +200,7 @@ def batch(logits, targets, logit_lengths, target_lengths, blank: int = -1, clamp
 
 def multiblank_sample(x, T: int, U: int, y, blank: int, big_blank_ids, big_blank_durations, sigma: float = 0.0,
                       fused: bool = True, clamp: float = -1.0, fastemit_lambda: float = 0.0,
-                      want_grad: bool = True) -> SampleResult:
+                      want_grad: bool = True, allow_bad_targets: bool = False) -> SampleResult:
     """Multi-blank transducer loss (and gradient of every row) of one sample.
 
     Big blank i is class ``big_blank_ids[i]`` and moves t forward by
@@ -202,7 +208,9 @@ def multiblank_sample(x, T: int, U: int, y, blank: int, big_blank_ids, big_blank
     by ``sigma`` (logit under-normalisation).  These follow the
     compute_multiblank_grad_kernel page's parameters; see rnnt_oracle.c for
     the reading of the alignment rules.  ``loss_alpha`` is the forward
-    recursion's value, ``loss`` the backward one's.
+    recursion's value, ``loss`` the backward one's.  A label that is a blank
+    of either kind or outside [0, V) leaves no alignment (loss +inf, zero
+    gradient); it raises ValueError unless ``allow_bad_targets`` is set.
     """
     lib = _load()
     x = np.asarray(x)
@@ -227,11 +235,11 @@ def multiblank_sample(x, T: int, U: int, y, blank: int, big_blank_ids, big_blank
         (ids if nb else np.zeros(1, np.int32)).ctypes.data_as(ip),
         (dur if nb else np.zeros(1, np.int32)).ctypes.data_as(ip), float(sigma), int(bool(fused)), float(clamp),
         float(fastemit_lambda), _ptr(grad), ctypes.byref(la), ctypes.byref(lb))
-    if rc == ORACLE_BAD_TARGET:
+    if rc == ORACLE_BAD_TARGET and not allow_bad_targets:
         raise ValueError("target label equal to a blank or outside [0, V)")
-    if rc != ORACLE_OK:
+    if rc not in (ORACLE_OK, ORACLE_BAD_TARGET):
         raise ValueError(f"oracle rejected the arguments (code {rc})")
-    return SampleResult(lb.value, la.value, grad, None, None)
+    return SampleResult(lb.value, la.value, grad, None, None, rc == ORACLE_BAD_TARGET)
 
 
 def multiblank_batch(logits, targets, logit_lengths, target_lengths, big_blank_ids, big_blank_durations,

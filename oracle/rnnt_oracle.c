@@ -34,6 +34,13 @@
  *    log_softmax is fused, the log_softmax Jacobian
  *        dL/dx_k = dL/dlp_k - softmax_k * sum_j dL/dlp_j.
  *
+ *  - Labels (warp-transducer build post, section 5.2: the labels must not
+ *    contain blank).  Reading taken: a target that is not a non-blank class
+ *    (equal to blank, or outside [0,V)) is a symbol no alignment can emit, so
+ *    the sample has no legal alignment: P(y|x) = 0, loss = +inf and every
+ *    gradient element 0 (there is nothing to differentiate).  The result is
+ *    computed that way and the call reports ORACLE_BAD_TARGET beside it.
+ *
  *  - Clamp (README "Operator features": for clamp > 0 every gradient element
  *    is clipped to [-clamp, clamp]; clamp <= 0 disables it).
  *
@@ -114,7 +121,8 @@ static double row_logsumexp(const void *x, int dtype, long r, int V)
  *   x        T*(U+1) rows of V values, row-major, of type dtype (ORACLE_F64,
  *            _F32 or _F16); logits, or log-probs when fused == 0.  Values are
  *            converted exactly to fp64 as they are read.
- *   y        U target labels; each must lie in [0,V) and differ from blank.
+ *   y        U target labels; one outside [0,V) or equal to blank makes the
+ *            sample impossible (see "Labels" above).
  *   blank    already normalised to [0,V).
  *   grad_rows, n_grad_rows   sample-local rows whose gradient is wanted
  *            (NULL with n_grad_rows < 0 means every row, in order).
@@ -126,7 +134,8 @@ static double row_logsumexp(const void *x, int dtype, long r, int V)
  *            variables (beta(t,u) includes the emissions at (t,u) onwards,
  *            so beta(0,0) = log P(y|x)).
  *   loss_alpha, loss_beta  -log P(y|x) from each recursion.
- * Returns ORACLE_OK or an error code.
+ * Returns ORACLE_OK, ORACLE_BAD_TARGET (outputs computed, the sample has no
+ * alignment because of a label) or an error code (outputs untouched).
  */
 int rnnt_oracle_sample_ex(const void *x, int dtype, int T, int U, int V, const int *y, int blank, int fused,
                           double clamp, double fastemit_lambda, const int64_t *grad_rows, long n_grad_rows,
@@ -136,8 +145,9 @@ int rnnt_oracle_sample_ex(const void *x, int dtype, int T, int U, int V, const i
     if (T < 1 || U < 0 || V < 1 || blank < 0 || blank >= V) return ORACLE_BAD_ARGS;
     if (!(fastemit_lambda >= 0.0) || isinf(fastemit_lambda)) return ORACLE_BAD_ARGS;
     if (dtype != ORACLE_F64 && dtype != ORACLE_F32 && dtype != ORACLE_F16) return ORACLE_BAD_ARGS;
+    int bad_target = 0;
     for (int u = 0; u < U; ++u)
-        if (y[u] < 0 || y[u] >= V || y[u] == blank) return ORACLE_BAD_TARGET;
+        if (y[u] < 0 || y[u] >= V || y[u] == blank) bad_target = 1;
 
     const int U1 = U + 1;
     const long cells = (long)T * U1;
@@ -157,7 +167,8 @@ int rnnt_oracle_sample_ex(const void *x, int dtype, int T, int U, int V, const i
             long c = (long)t * U1 + u;
             lse[c] = fused ? row_logsumexp(x, dtype, c, V) : 0.0;
             lpb[c] = elem(x, dtype, c, V, blank) - lse[c];
-            lpy[c] = (u < U) ? elem(x, dtype, c, V, y[u]) - lse[c] : -INFINITY;
+            const int label_ok = (u < U) && y[u] >= 0 && y[u] < V && y[u] != blank;
+            lpy[c] = label_ok ? elem(x, dtype, c, V, y[u]) - lse[c] : -INFINITY;
         }
     }
 
@@ -220,7 +231,7 @@ int rnnt_oracle_sample_ex(const void *x, int dtype, int T, int U, int V, const i
             d_label *= 1.0 + fastemit_lambda;
             for (int k = 0; k < V; ++k) g[k] = 0.0;
             g[blank] += d_blank;
-            if (u < U) g[y[u]] += d_label;
+            if (u < U && d_label != 0.0) g[y[u]] += d_label;   /* non-zero only for a valid label */
             if (fused) {
                 double sum_d = d_blank + d_label;
                 for (int k = 0; k < V; ++k) {
@@ -238,7 +249,7 @@ int rnnt_oracle_sample_ex(const void *x, int dtype, int T, int U, int V, const i
     }
 
     free(lse); free(lpb); free(lpy); free(al); free(be);
-    return ORACLE_OK;
+    return bad_target ? ORACLE_BAD_TARGET : ORACLE_OK;
 }
 
 /* fp64 input, gradient of every row (the form the pins use). */
@@ -264,7 +275,9 @@ int rnnt_oracle_sample(const double *x, int T, int U, int V, const int *y, int b
  *     exactly t = T; blanks that would pass T, or reach T with u < U, are not
  *     part of any alignment;
  *   - loss = -log of the summed alignment probability; the gradient is its
- *     derivative (with the FastEmit weight on the label edges, as above).
+ *     derivative (with the FastEmit weight on the label edges, as above);
+ *   - a label that is a blank of either kind or outside [0,V) admits no
+ *     alignment (as above): loss +inf, gradient 0, ORACLE_BAD_TARGET.
  * nb = 0 and sigma = 0 is the plain transducer loss.
  */
 int rnnt_oracle_multiblank_sample(const void *x, int dtype, int T, int U, int V, const int *y, int blank, int nb,
@@ -279,10 +292,11 @@ int rnnt_oracle_multiblank_sample(const void *x, int dtype, int T, int U, int V,
         for (int j = 0; j < i; ++j)
             if (bb_id[j] == bb_id[i]) return ORACLE_BAD_ARGS;
     }
+    int bad_target = 0;
     for (int u = 0; u < U; ++u) {
-        if (y[u] < 0 || y[u] >= V || y[u] == blank) return ORACLE_BAD_TARGET;
+        if (y[u] < 0 || y[u] >= V || y[u] == blank) bad_target = 1;
         for (int i = 0; i < nb; ++i)
-            if (y[u] == bb_id[i]) return ORACLE_BAD_TARGET;
+            if (y[u] == bb_id[i]) bad_target = 1;
     }
 
     const int U1 = U + 1;
@@ -304,7 +318,9 @@ int rnnt_oracle_multiblank_sample(const void *x, int dtype, int T, int U, int V,
         const int u = (int)(c % U1);
         lse[c] = fused ? row_logsumexp(x, dtype, c, V) : 0.0;
         lpb[c] = elem(x, dtype, c, V, blank) - lse[c] - sigma;
-        lpy[c] = (u < U) ? elem(x, dtype, c, V, y[u]) - lse[c] - sigma : -INFINITY;
+        int label_ok = (u < U) && y[u] >= 0 && y[u] < V && y[u] != blank;
+        for (int i = 0; i < nb; ++i) label_ok = label_ok && y[u] != bb_id[i];
+        lpy[c] = label_ok ? elem(x, dtype, c, V, y[u]) - lse[c] - sigma : -INFINITY;
         for (int i = 0; i < nb; ++i) lpg[c * nb + i] = elem(x, dtype, c, V, bb_id[i]) - lse[c] - sigma;
     }
 
@@ -369,7 +385,7 @@ int rnnt_oracle_multiblank_sample(const void *x, int dtype, int T, int U, int V,
                 sum_d += d_blank;
                 if (u < U) {
                     const double d_label = -(1.0 + fastemit_lambda) * exp(al[c] + lpy[c] + be[c + 1] - logz);
-                    g[y[u]] += d_label;
+                    if (d_label != 0.0) g[y[u]] += d_label;   /* non-zero only for a valid label */
                     sum_d += d_label;
                 }
                 for (int i = 0; i < nb; ++i) {
@@ -397,5 +413,5 @@ int rnnt_oracle_multiblank_sample(const void *x, int dtype, int T, int U, int V,
         }
     }
     free(lse); free(lpb); free(lpy); free(lpg); free(al); free(be);
-    return ORACLE_OK;
+    return bad_target ? ORACLE_BAD_TARGET : ORACLE_OK;
 }

@@ -272,6 +272,35 @@ def test_blank_normalisation_and_bad_targets():
         oracle.sample(x, 3, 1, [5], 4)   # label outside [0, V)
 
 
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("bad", [4, 5, -1])
+def test_label_that_is_not_a_symbol_leaves_no_alignment(fused, bad):
+    """The build post's section 5.2 rules blank out of the labels; a label equal to blank (4 here) or outside
+    [0, V) is a symbol no alignment can emit.  Every alignment emits every label exactly once, so the set of
+    alignments is empty: P(y|x) = 0, loss +inf, and the gradient of every row is exactly zero (also through the
+    log_softmax chain rule).  The same sample with that label replaced by a valid one is finite, so the
+    infinity comes from the label alone."""
+    rng = np.random.default_rng(7)
+    T, U, V = 4, 3, 5
+    x = rng.normal(size=(T * (U + 1), V))
+    if not fused:
+        x = x - np.log(np.exp(x).sum(axis=1, keepdims=True))
+    y = [1, bad, 2]
+    r = oracle.sample(x, T, U, y, 4, fused=fused, allow_bad_targets=True)
+    assert r.bad_target
+    assert np.isinf(r.loss) and r.loss > 0 and np.isinf(r.loss_alpha)
+    assert np.all(r.grad == 0.0)
+    ok = oracle.sample(x, T, U, [1, 3, 2], 4, fused=fused)
+    assert np.isfinite(ok.loss) and not ok.bad_target
+    # the multi-blank oracle: a label equal to a big blank's class is no symbol either
+    m = oracle.multiblank_sample(x, T, U, [1, 3, 2], 4, [3], [2], 0.1, fused=fused, allow_bad_targets=True)
+    assert m.bad_target and np.isinf(m.loss) and np.all(m.grad == 0.0)
+    m2 = oracle.multiblank_sample(x, T, U, y, 4, [0], [2], 0.1, fused=fused, allow_bad_targets=True)
+    assert m2.bad_target and np.isinf(m2.loss) and np.all(m2.grad == 0.0)
+    with pytest.raises(ValueError):
+        oracle.multiblank_sample(x, T, U, [1, 3, 2], 4, [3], [2], 0.1, fused=fused)
+
+
 def test_golden_readme_example():
     """The README usage-example layout (24 packed rows, V=8), values stored by tests/golden/make_golden.py."""
     import json
