@@ -218,7 +218,8 @@ def main():
 
     def step():
         if multiblank:
-            rl.rnnt_multiblank_fused(w.logits, tg, T, U, w.big_blank_ids, w.big_blank_durations, blank=w.blank,
+            rl.rnnt_multiblank_fused(w.logits, tg, T, U, big_blank_ids=w.big_blank_ids,
+                                     big_blank_durations=w.big_blank_durations, blank=w.blank,
                                      sigma=w.sigma, clamp=w.clamp, reduction=w.reduction,
                                      fused_log_softmax=w.fused, fastemit_lambda=args.fastemit_lambda, grad=grad,
                                      workspace=ws, loss=loss, loss_reduced=red)

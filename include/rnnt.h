@@ -78,7 +78,7 @@ typedef enum {
 /* Bits of the device status word (read back by rnnt_loss_fused_check). */
 enum {
     RNNT_DEV_LOSS_MISMATCH = 1u, /* |L_alpha - L_beta| > 1e-4 * max(1, |L_beta|) for some sample */
-    RNNT_DEV_BAD_TARGET = 2u     /* a label y_u lies outside [0, V) or equals blank */
+    RNNT_DEV_BAD_TARGET = 2u     /* a label y_u lies outside [0, V) or equals a blank */
 };
 
 /*
@@ -142,8 +142,10 @@ rnnt_status rnnt_loss_fused_workspace_size(int32_t B, int32_t V, int64_t N, rnnt
  * sum_i T_i*(U_i+1) != N or partial overlap of grad and logits;
  * RNNT_WORKSPACE_TOO_SMALL; RNNT_MEMOPS_FAILED; RNNT_EXECUTION_FAILED.
  * Invalid label values are only visible on the device: they set
- * RNNT_DEV_BAD_TARGET, and a label outside [0, V) makes its sample's
- * alignment impossible (loss +inf, gradient 0 for that sample).
+ * RNNT_DEV_BAD_TARGET.  A label outside [0, V) or equal to blank is no
+ * symbol an alignment can emit (warp-transducer build post, section 5.2:
+ * the labels exclude blank), so its sample has no alignment: loss +inf and
+ * a zero gradient for that sample; the other samples are unaffected.
  * Numerics: the recursions run in fp64 probabilities scaled by a power of
  * two per block of anti-diagonals.  A sample takes the log domain instead
  * when one of its edge log-probabilities lies outside [-80, 80], or when
@@ -247,7 +249,9 @@ rnnt_status rnnt_grad_scale_padded(void *grad, rnnt_dtype dtype, int32_t max_T, 
  * widest U_i + 1 rounded up to 128 times a power of two (at U1p = 1024 the
  * longest duration is 7, at 512 it is 15), or a sample with
  * (T_i + U_i) * U1p * 8 >= 2^31.  A label equal to blank or to a big
- * blank sets RNNT_DEV_BAD_TARGET (read with rnnt_loss_fused_check).
+ * blank, or outside [0, V), sets RNNT_DEV_BAD_TARGET (read with
+ * rnnt_loss_fused_check) and leaves its sample without an alignment (loss
+ * +inf, zero gradient), as in rnnt_loss_fused.
  * The recursion runs in fp64 probabilities renormalised per anti-diagonal;
  * when the identity that every alignment emits each label once (the sum
  * over t of alpha(t,u) P(label) beta(t,u+1) is P(y|x)) fails by more than

@@ -516,7 +516,8 @@ rnnt_status build_mb_plan(int32_t B, int32_t V, int64_t N, const int32_t *T, con
     off = 256;
     L.desc = off;   off = align_up(off + sizeof(SampleDesc) * B);
     L.mode = off;   off = align_up(off + sizeof(int32_t) * B);  // per sample: 1 = recursions in the log domain
-    L.den = off;    off = align_up(off + sizeof(float) * (size_t)phys);
+    // per row: the maximum and log2 of the sum of exp(x - maximum), fp32
+    L.den = off;    off = align_up(off + 2 * sizeof(float) * (size_t)phys);
     // the sweep's 16-byte loads of a lane's column pair may reach one slot past a plane's last
     L.wp = off;     off = align_up(off + sizeof(double) * ((size_t)(2 + nb) * (size_t)slot + 2));
     L.alpha = off;  off = align_up(off + sizeof(double) * (size_t)ab);

@@ -96,8 +96,8 @@ __host__ __device__ inline ChunkDesc make_chunk(const SampleDesc &d, int32_t sam
 // Byte offsets of the workspace regions (each 256-byte aligned).  Everything
 // before `chunks` is written by the per-call upload; the chunk table is built
 // on the device from the sample descriptors (launch_plan).  Per skewed slot:
-//   node  {log P(blank), log P(next label), log-sum-exp of the row (fused) or
-//         0, the next label as int bits (-1 if none)};
+//   node  {log P(blank), log P(next label), the row's maximum m and log2 of
+//         its sum of exp(x - m) (fused; 0 and 0 for log-prob inputs)};
 //   prob  {P(blank), P(next label)} in fp32.
 struct WorkspaceLayout {
     size_t status;      // uint32 status word

@@ -1,17 +1,23 @@
 // gfx950 kernels of librnnt: the fused RNN-T loss, forward and backward.
 //
 // Pass structure (rnnt-loss-ascend README, "Architecture", kernel steps 1-5):
-//   rowstats    step 1    per packed row: log-sum-exp over V (fused) and the
-//                         two log-probs the lattice uses, log P(blank) and
+//   rowstats    step 1    per packed row: the row maximum m and log2 of the
+//                         sum of exp(x - m) over V (fused), and the two
+//                         log-probs the lattice uses, log P(blank) and
 //                         log P(y_{u+1}), stored per node in a skewed layout
 //                         (one contiguous run per anti-diagonal) both as fp32
-//                         log-probs and as fp32 probabilities.
-//   alpha_beta  steps 2-4 one workgroup per sample; wave 0 runs the forward
-//                         (alpha) recursion and wave 1 the backward (beta)
-//                         recursion, one anti-diagonal per step (README
-//                         "Operator features": every node of an anti-diagonal
-//                         has its inputs ready); the two losses are
-//                         cross-checked.
+//                         log-probs and as fp32 probabilities.  The maximum
+//                         is kept apart from the log-sum so that every later
+//                         fp32 step works on x - m, which does not depend on
+//                         a common offset of the row (log_softmax is
+//                         shift-invariant; README parameter table,
+//                         fused_log_softmax, and "Value" section 3).
+//   alpha_beta  steps 2-4 two single-wave workgroups per sample, one running
+//                         the forward (alpha) recursion and the other the
+//                         backward (beta) recursion, one anti-diagonal per
+//                         step (README "Operator features": every node of an
+//                         anti-diagonal has its inputs ready); the two
+//                         losses are cross-checked.
 //   grad        step 5    per packed row: the fused gradient (README "Value"
 //                         section 2), clamp, reduction scale, one write.
 //   reduce                none / mean / sum of the per-sample losses.
@@ -76,6 +82,16 @@ __device__ __forceinline__ float prob_of(float lp) {
     const float f = fmaf(lp, kHi, -k) + lp * kLo;
     const float p = __builtin_amdgcn_ldexpf(exp2_fast(f), (int)k);
     return (lp == kNegInf) ? 0.f : p;
+}
+
+// log2 of sum_k exp(x_k - m) from s = sum_k exp2(fma(x_k, log2(e), nm)),
+// nm = -m * log2(e) rounded to fp32.  Each term is exp2((x_k - m) log2(e)
+// + eps) with eps = m log2(e) + nm, the rounding error of nm (up to
+// ulp(m log2(e)) / 2, ~6e-5 at m ~ 1000), common to the whole row; fma
+// computes eps exactly, so it is taken back out here and the result does not
+// depend on the size of m (with log2(e) the same fp32 constant throughout).
+__device__ __forceinline__ float log2_sum_shifted(float s, float m, float nm) {
+    return log2_fast(s) - fmaf(m, kLog2e, nm);
 }
 
 // ------------------------------------------------------------ element I/O
@@ -203,20 +219,21 @@ __device__ __forceinline__ int wave_max_nonneg(int v) {
 
 // ---------------------------------------------------- row statistics output
 // Writes what the recursions and the gradient need about node (t,u), at its
-// skewed slot: node = {log P(blank), log P(y_{u+1}), log-sum-exp of the row
-// (fused) or 0, the label (-1 if none)} and prob = the two probabilities in
-// fp32.  The blank edge leaving t = T-1 below u = U
+// skewed slot: node = {log P(blank), log P(y_{u+1}), the row's reference
+// value m, log2 of the row's sum of exp(x - m)} (fused; m is the row maximum,
+// or 0 for a row of -inf; both 0 for log-prob inputs) and prob = the two
+// probabilities in fp32.  The blank edge leaving t = T-1 below u = U
 // leaves the lattice and the label edge at u = U does not exist, so both are
 // stored as impossible.  The wide kernel calls it from every lane with
 // wave-uniform values (the stores are then unconditional and the compiler's
 // wait counts stay exact); the others from one lane per row.
-__device__ __forceinline__ void emit_node(const SampleDesc &d, int t, int u, float dn, int y, float lpb, float lpy,
-                                          float4 *__restrict__ node, float2 *__restrict__ prob,
+__device__ __forceinline__ void emit_node(const SampleDesc &d, int t, int u, float m, float ls2, float lpb,
+                                          float lpy, float4 *__restrict__ node, float2 *__restrict__ prob,
                                           int *__restrict__ mode) {
     if (t == d.T - 1 && u < d.U) lpb = kNegInf;
     if (u == d.U) lpy = kNegInf;
     const int64_t slot = d.slot_off + (int64_t)(t + u) * (d.U + 1) + u;
-    node[slot] = make_float4(lpb, lpy, dn, __int_as_float(y));
+    node[slot] = make_float4(lpb, lpy, m, ls2);
     prob[slot] = make_float2(prob_of(lpb), prob_of(lpy));
     const bool wide = (lpb != kNegInf && fabsf(lpb) > kProbRange) || (lpy != kNegInf && fabsf(lpy) > kProbRange);
     if (wide) atomicOr(&mode[d.index], kModeLog);
@@ -229,7 +246,7 @@ __device__ __forceinline__ void fill_slots(const SampleDesc &d, int n, int u0, i
                                            float4 *__restrict__ node, float2 *__restrict__ prob) {
     const int64_t base = d.slot_off + (int64_t)n * (d.U + 1);
     for (int u = u0 + lane; u < u1; u += nl) {
-        node[base + u] = make_float4(kNegInf, kNegInf, 0.f, __int_as_float(-1));
+        node[base + u] = make_float4(kNegInf, kNegInf, 0.f, 0.f);
         prob[base + u] = make_float2(0.f, 0.f);
     }
 }
@@ -251,13 +268,13 @@ __device__ __forceinline__ void fill_columns(const SampleDesc &d, int t, int u, 
     if (t == 0)
         for (int n = lane; n < u; n += nl) {
             const int64_t s = d.slot_off + (int64_t)n * U1 + u;
-            node[s] = make_float4(kNegInf, kNegInf, 0.f, __int_as_float(-1));
+            node[s] = make_float4(kNegInf, kNegInf, 0.f, 0.f);
             prob[s] = make_float2(0.f, 0.f);
         }
     if (t == d.T - 1)
         for (int n = d.T + u + lane; n < d.T + d.U; n += nl) {
             const int64_t s = d.slot_off + (int64_t)n * U1 + u;
-            node[s] = make_float4(kNegInf, kNegInf, 0.f, __int_as_float(-1));
+            node[s] = make_float4(kNegInf, kNegInf, 0.f, 0.f);
             prob[s] = make_float2(0.f, 0.f);
         }
 }
@@ -267,13 +284,21 @@ __device__ __forceinline__ int64_t row_of(const SampleDesc &d, int t, int u) {
     return d.row_off + (int64_t)t * d.tstride + u;
 }
 
-__device__ __forceinline__ int read_label(const SampleDesc &d, int u, int V, int blank,
-                                          const int32_t *__restrict__ targets, int S, uint32_t *status) {
+// The label y_{u+1} of node (t,u), or -1 at u = U.  A label that is not a
+// non-blank class (outside [0, V), or equal to blank: the build post's
+// section 5.2 rules blank out of the labels) admits no alignment: its edge
+// is read as impossible (-1), and the status word is flagged.
+__device__ __forceinline__ int label_of(const SampleDesc &d, int u, int V, int blank,
+                                        const int32_t *__restrict__ targets, int S) {
     if (u >= d.U) return -1;
     const int y = targets[(int64_t)d.index * S + u];
-    const bool in_range = (y >= 0) && (y < V);
-    if (!in_range || y == blank) atomicOr(status, (uint32_t)RNNT_DEV_BAD_TARGET);
-    return in_range ? y : -1;
+    return (y >= 0 && y < V && y != blank) ? y : -1;
+}
+__device__ __forceinline__ int read_label(const SampleDesc &d, int u, int V, int blank,
+                                          const int32_t *__restrict__ targets, int S, uint32_t *status) {
+    const int y = label_of(d, u, V, blank, targets, S);
+    if (u < d.U && y < 0) atomicOr(status, (uint32_t)RNNT_DEV_BAD_TARGET);
+    return y;
 }
 
 // Lane-local maximum of a row held the way the wide kernels hold it.  fp16
@@ -373,7 +398,6 @@ __device__ __forceinline__ void rowstats_wide_chunk(const T *__restrict__ logits
     // wave-uniform, so per-row scalars stay in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nvec = V / VEC;
-    const int U1 = d.U + 1;
     auto load_row = [&](int n, int u, Vec (&x)[NV]) {
         const T *p = logits + row_of(d, n - u, u) * (int64_t)V;
 #pragma unroll
@@ -412,7 +436,8 @@ __device__ __forceinline__ void rowstats_wide_chunk(const T *__restrict__ logits
         const float hyn = (yn >= 0) ? elem(nn, un, yn) : 0.f;
         float m = row_max<T, NV, FULL>(xc, nvec);
         m = wave_max_f(m);
-        const float mr = (m == kNegInf) ? 0.f : m;
+        const bool dead = (m == kNegInf);
+        const float mr = dead ? 0.f : m;
         const float nm = -mr * kLog2e;
         float s = 0.f;
 #pragma unroll
@@ -421,11 +446,11 @@ __device__ __forceinline__ void rowstats_wide_chunk(const T *__restrict__ logits
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) s += exp2_fast(fmaf(Raw<T>::get(xc[i], e), kLog2e, nm));
         s = wave_sum_f(s);
-        const float dn = (m == kNegInf) ? kNegInf : m + log2_fast(s) * kLn2;
-        const bool dead = (dn == kNegInf);
-        const float lpb = dead ? kNegInf : hb - dn;
-        const float lpy = (dead || y < 0) ? kNegInf : hy - dn;
-        emit_node(d, n - u, u, dn, y, lpb, lpy, node, prob, mode);
+        // s >= 1 (the maximum contributes exp(0)); log P = (x - m) - ln s
+        const float ls2 = dead ? 0.f : log2_sum_shifted(s, mr, nm);
+        const float lpb = dead ? kNegInf : (hb - mr) - ls2 * kLn2;
+        const float lpy = (dead || y < 0) ? kNegInf : (hy - mr) - ls2 * kLn2;
+        emit_node(d, n - u, u, mr, ls2, lpb, lpy, node, prob, mode);
         fill_diagonal_ends(d, n, u, lane, 64, node, prob);
         n = nn;
         u = un;
@@ -489,10 +514,11 @@ __global__ __launch_bounds__(256) void k_rowstats_narrow(const T *__restrict__ l
                 for (int e = 1; e < VEC; ++e) vm = fmaxf(vm, x[e]);
                 const float mn = fmaxf(m, vm);
                 const float mr = (mn == kNegInf) ? 0.f : mn;
-                const float nm = -mr * kLog2e;
                 float acc = s * exp2_fast((m - mr) * kLog2e);
+                // each lane keeps its own running maximum, so the terms are
+                // formed from x - max directly (exact for the terms that matter)
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) acc += exp2_fast(fmaf(x[e], kLog2e, nm));
+                for (int e = 0; e < VEC; ++e) acc += exp2_fast((x[e] - mr) * kLog2e);
                 s = acc;
                 m = mn;
             }
@@ -508,14 +534,15 @@ __global__ __launch_bounds__(256) void k_rowstats_narrow(const T *__restrict__ l
         }
         if (!active) continue;
         if (sub == 0) {
-            const float dn = (m == kNegInf) ? kNegInf : m + log2_fast(s) * kLn2;
+            const bool dead = (m == kNegInf);
+            const float mr = dead ? 0.f : m;
+            const float ls2 = dead ? 0.f : log2_fast(s);
             const int y = read_label(d, u, V, blank, targets, S, status);
-            const bool dead = (dn == kNegInf);
             const float hb = Elem<T>::load1(p + blank);
             const float hy = (y >= 0) ? Elem<T>::load1(p + y) : 0.f;
-            const float lpb = dead ? kNegInf : hb - dn;
-            const float lpy = (dead || y < 0) ? kNegInf : hy - dn;
-            emit_node(d, t, u, dn, y, lpb, lpy, node, prob, mode);
+            const float lpb = dead ? kNegInf : (hb - mr) - ls2 * kLn2;
+            const float lpy = (dead || y < 0) ? kNegInf : (hy - mr) - ls2 * kLn2;
+            emit_node(d, t, u, mr, ls2, lpb, lpy, node, prob, mode);
         }
         if (t == 0 || t == d.T - 1) fill_columns(d, t, u, sub, G, node, prob);
     }
@@ -551,7 +578,7 @@ __global__ __launch_bounds__(256) void k_gather(const T *__restrict__ logits, in
         const int y = read_label(d, u, V, blank, targets, S, status);
         const float lpb = Elem<T>::load1(p + blank);
         const float lpy = (y < 0) ? kNegInf : Elem<T>::load1(p + y);
-        emit_node(d, t, u, 0.f, y, lpb, lpy, node, prob, mode);
+        emit_node(d, t, u, 0.f, 0.f, lpb, lpy, node, prob, mode);
     }
 }
 
@@ -985,15 +1012,20 @@ __global__ __launch_bounds__(64) void k_check_ab(const SampleDesc *__restrict__ 
 // g_k = P(k|t,u) * occ(t,u) - [k = blank] flow_b - [k = y_{u+1}] flow_y, where
 // occ = alpha*beta/P(y|x) and the flows are the posterior probabilities of
 // leaving (t,u) by blank or by the next label.  P * occ is evaluated as
-// exp2(x * log2(e) + shift) with one per-row shift.  With a FastEmit weight
-// lambda (the FastEmit paper's rule: the label-emission derivatives times
-// 1 + lambda) the label flow is (1 + lambda) flow_y and, through the
-// log_softmax chain rule, the softmax term carries occ + lambda flow_y.
+// exp2((x - m) * log2(e) + shift) with the row's maximum m and one per-row
+// shift log2(occ * scale) - log2(sum of exp(x - m)): every term is of the
+// size of x - m and the shift, never of x itself, so a common offset of the
+// row's logits changes nothing (the fp32 rounding of x * log2(e) at large |x|
+// would).  With a FastEmit weight lambda (the FastEmit paper's rule: the
+// label-emission derivatives times 1 + lambda) the label flow is
+// (1 + lambda) flow_y and, through the log_softmax chain rule, the softmax
+// term carries occ + lambda flow_y.
 struct RowTerms {
-    float shift2;  // log2(occ * scale) - den * log2(e), or -inf
+    float m;       // the row's reference value (its maximum), 0 if not fused
+    float shift2;  // log2(occ * scale) - log2(sum of exp(x - m)), or -inf
     float fb;      // scaled blank flow
     float fy;      // scaled label flow
-    int y;         // next label, -1 at u = U or when invalid
+    int y;         // next label, -1 at u = U or when not a non-blank class
 };
 
 struct SampleTerms {
@@ -1008,13 +1040,15 @@ __device__ __forceinline__ double node_log2(const double *__restrict__ v, const 
     return log_mode ? v[s] : log2_d(v[s]) + (double)e[ge];
 }
 
-// Terms of node (t, u) from its skewed slots: the row's log-sum-exp, label
-// and log-probs (node), alpha, beta and beta of the two successors.
+// Terms of node (t, u) from its skewed slots: the row's maximum, log-sum and
+// log-probs (node), alpha, beta and beta of the two successors; the label
+// from the targets.
 __device__ __forceinline__ RowTerms row_terms(const SampleDesc &d, const SampleTerms &st, int t, int u,
                                               const float4 *__restrict__ node, const double *__restrict__ alpha,
                                               const double *__restrict__ beta, const int *__restrict__ ealpha,
                                               const int *__restrict__ ebeta, float log2_scale, float scale,
-                                              float fastemit, float scale_y, bool fused) {
+                                              float fastemit, float scale_y, bool fused, int V, int blank,
+                                              const int32_t *__restrict__ targets, int S) {
     const int U1 = d.U + 1;
     const int n = t + u;
     const int64_t s = d.slot_off + (int64_t)n * U1 + u;      // node slot
@@ -1040,17 +1074,19 @@ __device__ __forceinline__ RowTerms row_terms(const SampleDesc &d, const SampleT
     if (fastemit > 0.f && ly != kNegInfD && lo != kNegInfD)
         lo += (double)log2f(1.f + fastemit * exp2_fast((float)(ly - lo)));
     RowTerms r;
-    r.shift2 = fused ? (float)(lo - (double)l.z * kLog2eD) + log2_scale : kNegInf;
+    r.m = l.z;
+    r.shift2 = fused ? (float)(lo - (double)l.w) + log2_scale : kNegInf;
     r.fb = exp2_fast((float)lb) * scale;
     r.fy = exp2_fast((float)ly) * scale_y;
-    r.y = __float_as_int(l.w);
+    r.y = label_of(d, u, V, blank, targets, S);
     return r;
 }
 
 struct GradArgs {
-    int V, blank, n_chunks;
+    int V, blank, n_chunks, S;
     float clamp, scale, log2_scale;
     float fastemit, scale_y;  // FastEmit weight; scale * (1 + fastemit)
+    const int32_t *targets;
     const SampleDesc *desc;
     const ChunkDesc *chunks;
     const int *mode;
@@ -1066,13 +1102,14 @@ struct GradArgs {
 // parameters, so the compiler knows the gradient stores cannot clobber them
 // and reads their wave-uniform elements through the scalar cache.
 #define RNNT_GRAD_PARAMS                                                                                      \
-    int V, int blank, int n_chunks, float clamp, float scale, float log2_scale, float fastemit, float scale_y, \
-        const SampleDesc *__restrict__ desc, const ChunkDesc *__restrict__ chunks, const int *__restrict__ mode, \
-        const double *__restrict__ log2z, const float4 *__restrict__ node, const double *__restrict__ alpha,   \
-        const double *__restrict__ beta, const int *__restrict__ ealpha, const int *__restrict__ ebeta
-#define RNNT_GRAD_ARGS(g)                                                                                  \
-    g.V, g.blank, g.n_chunks, g.clamp, g.scale, g.log2_scale, g.fastemit, g.scale_y, g.desc, g.chunks, g.mode, \
-        g.log2z, g.node, g.alpha, g.beta, g.ealpha, g.ebeta
+    int V, int blank, int n_chunks, int S, float clamp, float scale, float log2_scale, float fastemit,          \
+        float scale_y, const int32_t *__restrict__ targets, const SampleDesc *__restrict__ desc,                \
+        const ChunkDesc *__restrict__ chunks, const int *__restrict__ mode, const double *__restrict__ log2z,   \
+        const float4 *__restrict__ node, const double *__restrict__ alpha, const double *__restrict__ beta,     \
+        const int *__restrict__ ealpha, const int *__restrict__ ebeta
+#define RNNT_GRAD_ARGS(g)                                                                                    \
+    g.V, g.blank, g.n_chunks, g.S, g.clamp, g.scale, g.log2_scale, g.fastemit, g.scale_y, g.targets, g.desc,   \
+        g.chunks, g.mode, g.log2z, g.node, g.alpha, g.beta, g.ealpha, g.ebeta
 
 __device__ __forceinline__ float clamp_to(float v, float cl, bool do_clamp) {
     return do_clamp ? fminf(fmaxf(v, -cl), cl) : v;
@@ -1100,7 +1137,7 @@ __device__ __forceinline__ void grad_row(typename Raw<T>::vec (&xc)[NV], T *dst,
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
                 float v = 0.f;
-                if constexpr (FUSED) v = exp2_fast(fmaf(Raw<T>::get(xc[j], e), kLog2e, rt.shift2));
+                if constexpr (FUSED) v = exp2_fast(fmaf(Raw<T>::get(xc[j], e) - rt.m, kLog2e, rt.shift2));
                 gv[e] = v;
             }
             if ((vb >> 6) == i) {
@@ -1119,16 +1156,16 @@ __device__ __forceinline__ void grad_row(typename Raw<T>::vec (&xc)[NV], T *dst,
     }
 }
 
-// The gradient, one wave per workgroup and S workgroups per row (each NV
+// The gradient, one wave per workgroup and SPLIT workgroups per row (each NV
 // vectors per lane: rows of up to 4 KiB take one): each wave loads its part
 // of the row, computes and stores it, and exits.  Many single-wave
 // workgroups of 4 KiB keep enough rows in flight without a prefetch ring
 // (and run faster than four-wave workgroups over four rows).  Workgroup b
-// takes part (b % PB) % S of row (b % PB) / S of chunk n_chunks-1-b/PB
-// (PB = rows per chunk * S, row order), so the chunks run in the reverse of
+// takes part (b % PB) % SPLIT of row (b % PB) / SPLIT of chunk n_chunks-1-b/PB
+// (PB = rows per chunk * SPLIT, row order), so the chunks run in the reverse of
 // the row pass's order, which starts where that pass ended (measured 6%
 // faster than the forward order for a write-only gradient, 0.5% otherwise).
-template <typename T, int NV, int S, bool FULL, bool FUSED, bool CLAMP>
+template <typename T, int NV, int SPLIT, bool FULL, bool FUSED, bool CLAMP>
 __global__ __launch_bounds__(64) void k_grad_rows(const T *logits, T *grad, int blocks_per_chunk,
                                                   int64_t block_base, RNNT_GRAD_PARAMS) {
     constexpr int VEC = Raw<T>::kVec;
@@ -1136,9 +1173,9 @@ __global__ __launch_bounds__(64) void k_grad_rows(const T *logits, T *grad, int 
     const int64_t b = block_base + blockIdx.x;
     const ChunkDesc c = chunks[n_chunks - 1 - (int)(b / bpc)];
     const int part = (int)(b % bpc);
-    const int r = part / S;
+    const int r = part / SPLIT;
     if (r >= c.count) return;
-    const int i0 = (part % S) * NV;  // first vector number of this wave's part
+    const int i0 = (part % SPLIT) * NV;  // first vector number of this wave's part
     const SampleDesc d = desc[c.sample];
     const int lane = threadIdx.x & 63;
     const int nvec = V / VEC;
@@ -1157,8 +1194,8 @@ __global__ __launch_bounds__(64) void k_grad_rows(const T *logits, T *grad, int 
         }
     }
     const SampleTerms st{log2z[d.index], mode[d.index] != 0};
-    const RowTerms rt =
-        row_terms(d, st, t, u, node, alpha, beta, ealpha, ebeta, log2_scale, scale, fastemit, scale_y, FUSED);
+    const RowTerms rt = row_terms(d, st, t, u, node, alpha, beta, ealpha, ebeta, log2_scale, scale, fastemit,
+                                  scale_y, FUSED, V, blank, targets, S);
     grad_row<T, NV, FULL, FUSED, CLAMP>(x, grad + row * (int64_t)V, rt, blank, nvec, clamp * scale, i0);
 }
 
@@ -1183,8 +1220,8 @@ __global__ __launch_bounds__(256) void k_grad_narrow(const T *logits, T *grad, R
         const int t = lr / U1;
         const int u = lr - t * U1;
         const int64_t row = row_of(d, t, u);
-        const RowTerms rt =
-        row_terms(d, st, t, u, node, alpha, beta, ealpha, ebeta, log2_scale, scale, fastemit, scale_y, FUSED);
+        const RowTerms rt = row_terms(d, st, t, u, node, alpha, beta, ealpha, ebeta, log2_scale, scale, fastemit,
+                                      scale_y, FUSED, V, blank, targets, S);
         const T *src = logits + row * (int64_t)V;
         T *dst = grad + row * (int64_t)V;
         const int vb = blank / VEC, vy = rt.y >= 0 ? rt.y / VEC : -1;
@@ -1196,7 +1233,7 @@ __global__ __launch_bounds__(256) void k_grad_narrow(const T *logits, T *grad, R
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
                 float v = 0.f;
-                if constexpr (FUSED) v = exp2_fast(fmaf(x[e], kLog2e, rt.shift2));
+                if constexpr (FUSED) v = exp2_fast(fmaf(x[e] - rt.m, kLog2e, rt.shift2));
                 v -= (i == vb && e == eb) ? rt.fb : 0.f;
                 v -= (i == vy && e == ey) ? rt.fy : 0.f;
                 gv[e] = clamp_to(v, cl, do_clamp);
@@ -1433,6 +1470,8 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
     g.V = a.V;
     g.blank = a.blank;
     g.n_chunks = a.lay.n_chunks;
+    g.S = a.S;
+    g.targets = a.targets;
     g.clamp = a.clamp;
     g.scale = a.grad_scale;
     g.log2_scale = log2f(a.grad_scale);
@@ -1458,10 +1497,9 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
             // waves per row: rows of up to 4 KiB (four vectors per lane) take one
             constexpr int S = Tg::n > 4 ? Tg::n / 4 : 1;
             constexpr int NVW = Tg::n / S;
-            void (*kern)(const T *, T *, int, int64_t, int, int, int, float, float, float, float, float,
-                         const SampleDesc *,
-                         const ChunkDesc *, const int *, const double *, const float4 *, const double *,
-                         const double *, const int *, const int *);
+            void (*kern)(const T *, T *, int, int64_t, int, int, int, int, float, float, float, float, float,
+                         const int32_t *, const SampleDesc *, const ChunkDesc *, const int *, const double *,
+                         const float4 *, const double *, const double *, const int *, const int *);
             if (a.fused) {
                 if (cl) kern = fu ? k_grad_rows<T, NVW, S, true, true, true> : k_grad_rows<T, NVW, S, false, true, true>;
                 else kern = fu ? k_grad_rows<T, NVW, S, true, true, false> : k_grad_rows<T, NVW, S, false, true, false>;
@@ -1541,8 +1579,9 @@ hipError_t launch_zero_padding(void *grad, int esize, int V, int B, int max_T, i
 // u = U.  The sweeps treat that end as a virtual node (T,U) on anti-diagonal
 // T+U, with beta(T,U) = 1, so the ends need no special case.
 //
-// Three passes of their own: per row, the log-normaliser and the edges'
-// probabilities (fp64 planes in the skewed slots); one wave per sample
+// Three passes of their own: per row, the log-normaliser (the row maximum and
+// log2 of the sum of exp(x - max), kept apart as in the plain path) and the
+// edges' probabilities (fp64 planes in the skewed slots); one wave per sample
 // and direction sweeping anti-diagonals in fp64 probabilities renormalised by
 // a power of two on every diagonal, with the recent diagonals in an LDS
 // ring (a power of two deep, above the longest duration) for the big
@@ -1556,6 +1595,15 @@ struct MbParams {
     int R;        // ring depth: the power of two above the longest duration
     float sigma;
 };
+
+// A label must be a class that is neither the standard blank nor a big
+// blank; any other value admits no alignment (its edge is impossible).
+__device__ __forceinline__ bool mb_label_ok(int y, int V, int blank, const MbParams &mp) {
+    bool ok = y >= 0 && y < V && y != blank;
+#pragma unroll
+    for (int i = 0; i < kMaxBigBlanks; ++i) ok = ok && !(i < mp.nb && y == mp.ids[i]);
+    return ok;
+}
 
 __device__ __forceinline__ const SampleDesc &mb_sample_of_row(const SampleDesc *__restrict__ desc, int B,
                                                               int64_t r) {
@@ -1628,7 +1676,8 @@ __device__ __forceinline__ void mb_store_node(const SampleDesc &d, int t, int u,
 }
 
 // One wave per packed row, four per workgroup: the row's log-normaliser
-// (fused) and the probabilities, in fp64, of the edges leaving the node
+// (fused: {maximum, log2 sum of exp(x - maximum)}; {0, 0} for log-prob inputs
+// and rows of -inf) and the probabilities, in fp64, of the edges leaving the node
 // (their log-probabilities less sigma, exponentiated), at its skewed slot:
 // plane 0 the standard blank, plane 1 the next label (0 at u = U or for a
 // label outside [0,V)), plane 2+i big blank i.
@@ -1636,30 +1685,32 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_mb_rows(const T *__restrict__ logits, int64_t N, int V, int blank,
                                                  int fused, MbParams mp, const SampleDesc *__restrict__ desc,
                                                  int B, const int32_t *__restrict__ targets, int S,
-                                                 float *__restrict__ den, double *__restrict__ wp, int64_t n_slots,
-                                                 uint32_t *status, int64_t row_base) {
+                                                 float2 *__restrict__ den, double *__restrict__ wp,
+                                                 int64_t n_slots, uint32_t *status, int64_t row_base) {
     const int lane = threadIdx.x & 63;
     const int64_t r = row_base + (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (r >= N) return;
     const SampleDesc d = mb_sample_of_row(desc, B, r);
-    const int U1 = d.U + 1;
     const int64_t lr = r - d.row_off;
     const int t = (int)(lr / d.tstride);
     const int u = (int)(lr - (int64_t)t * d.tstride);
     if (t >= d.T || u > d.U) return;  // a padding row of the padded layout
     const T *x = logits + r * (int64_t)V;
-    float dn = 0.f;
+    float mr = 0.f, ls2 = 0.f;
+    bool dead = false;
     if (fused) {
         float m = kNegInf;
         for (int k = lane; k < V; k += 64) m = fmaxf(m, Elem<T>::load1(x + k));
         m = wave_max_f(m);
+        dead = (m == kNegInf);
         float sum = 0.f;
-        if (m != kNegInf)
+        if (!dead)
             for (int k = lane; k < V; k += 64) sum += exp2_fast((Elem<T>::load1(x + k) - m) * kLog2e);
         sum = wave_sum_f(sum);
-        dn = (m == kNegInf) ? kNegInf : m + log2_fast(sum) * kLn2;
+        mr = dead ? 0.f : m;
+        ls2 = dead ? 0.f : log2_fast(sum);
     }
-    if (lane == 0) den[r] = dn;
+    if (lane == 0) den[r] = make_float2(mr, ls2);
     float v = kNegInf;
     if (lane < 2 + mp.nb) {
         int k = blank;
@@ -1667,17 +1718,15 @@ __global__ __launch_bounds__(256) void k_mb_rows(const T *__restrict__ logits, i
             k = -1;
             if (u < d.U) {
                 const int y = targets[(int64_t)d.index * S + u];
-                bool bad = y < 0 || y >= V || y == blank;
-#pragma unroll
-                for (int i = 0; i < kMaxBigBlanks; ++i) bad = bad || (i < mp.nb && y == mp.ids[i]);
+                const bool bad = !mb_label_ok(y, V, blank, mp);
                 if (bad) atomicOr(status, (uint32_t)RNNT_DEV_BAD_TARGET);
-                k = (y >= 0 && y < V) ? y : -1;
+                k = bad ? -1 : y;
             }
         }
 #pragma unroll
         for (int i = 0; i < kMaxBigBlanks; ++i)
             if (lane == 2 + i) k = mp.ids[i];
-        v = (k >= 0 && dn != kNegInf) ? Elem<T>::load1(x + k) - dn - mp.sigma : kNegInf;
+        v = (k >= 0 && !dead) ? (Elem<T>::load1(x + k) - mr) - ls2 * kLn2 - mp.sigma : kNegInf;
     }
     mb_store_node(d, t, u, mp, lane, v, wp, n_slots);
 }
@@ -2031,15 +2080,17 @@ __global__ __launch_bounds__(64) void k_mb_check(const SampleDesc *__restrict__ 
 // FastEmit term, log2 domain, minus the row's normaliser) and the scaled
 // flows of the edges leaving the node, with the label class.
 struct MbRowTerms {
-    float shift2;
+    float m;       // the row's maximum (0 if not fused)
+    float shift2;  // log2(occ * scale) - log2(sum of exp(x - m)), or -inf
     float fb, fy;
     float fg[kMaxBigBlanks];
     int y;
 };
 
-__device__ __forceinline__ MbRowTerms mb_row_terms(const SampleDesc &d, int64_t r, int t, int u, int V, int fused,
+__device__ __forceinline__ MbRowTerms mb_row_terms(const SampleDesc &d, int64_t r, int t, int u, int V, int blank,
+                                                   int fused,
                                                    const MbParams &mp, int U1p, const int32_t *__restrict__ targets,
-                                                   int S, const float *__restrict__ den,
+                                                   int S, const float2 *__restrict__ den,
                                                    const double *__restrict__ wp, int64_t n_slots,
                                                    const double *__restrict__ alpha,
                                                    const double *__restrict__ beta, const int *__restrict__ ealpha,
@@ -2078,14 +2129,15 @@ __device__ __forceinline__ MbRowTerms mb_row_terms(const SampleDesc &d, int64_t 
     rt.y = -1;
     if (u < d.U) {
         const int yy = targets[(int64_t)d.index * S + u];
-        rt.y = (yy >= 0 && yy < V) ? yy : -1;
+        rt.y = mb_label_ok(yy, V, blank, mp) ? yy : -1;
     }
     rt.fb = exp2_fast((float)lb) * scale;
     rt.fy = exp2_fast((float)ly) * scale * (1.f + fastemit);
 #pragma unroll
     for (int i = 0; i < kMaxBigBlanks; ++i) rt.fg[i] = exp2_fast((float)lg[i]) * scale;
-    const float dn = den[r];
-    rt.shift2 = (fused && dn != kNegInf) ? (float)(lo - (double)dn * kLog2eD) + log2_fast(scale) : kNegInf;
+    const float2 dn = den[r];
+    rt.m = dn.x;
+    rt.shift2 = (fused && lo != kNegInfD) ? (float)(lo - (double)dn.y) + log2_fast(scale) : kNegInf;
     return rt;
 }
 
@@ -2097,7 +2149,7 @@ __global__ __launch_bounds__(256) void k_mb_grad(const T *__restrict__ logits, T
                                                  int V, int blank, int fused, MbParams mp, int U1p,
                                                  const SampleDesc *__restrict__ desc, int B,
                                                  const int32_t *__restrict__ targets, int S,
-                                                 const float *__restrict__ den, const double *__restrict__ wp,
+                                                 const float2 *__restrict__ den, const double *__restrict__ wp,
                                                  int64_t n_slots, const double *__restrict__ alpha,
                                                  const double *__restrict__ beta, const int *__restrict__ ealpha,
                                                  const int *__restrict__ ebeta, const double *__restrict__ log2z,
@@ -2115,14 +2167,14 @@ __global__ __launch_bounds__(256) void k_mb_grad(const T *__restrict__ logits, T
         for (int k = lane; k < V; k += 64) Elem<T>::store1(g + k, 0.f);
         return;
     }
-    const MbRowTerms rt = mb_row_terms(d, r, t, u, V, fused, mp, U1p, targets, S, den, wp, n_slots, alpha, beta,
+    const MbRowTerms rt = mb_row_terms(d, r, t, u, V, blank, fused, mp, U1p, targets, S, den, wp, n_slots, alpha, beta,
                                        ealpha, ebeta, log2z, scale, fastemit, mode[d.index] != 0);
     const bool do_clamp = clamp > 0.f;
     const float cl = clamp * scale;
     const T *x = logits + r * (int64_t)V;
     for (int k = lane; k < V; k += 64) {
         float v = 0.f;
-        if (fused) v = exp2_fast(fmaf(Elem<T>::load1(x + k), kLog2e, rt.shift2));
+        if (fused) v = exp2_fast(fmaf(Elem<T>::load1(x + k) - rt.m, kLog2e, rt.shift2));
         v -= (k == blank) ? rt.fb : 0.f;
         v -= (k == rt.y) ? rt.fy : 0.f;
 #pragma unroll
@@ -2140,7 +2192,7 @@ template <typename T, int NV, bool FULL>
 __global__ __launch_bounds__(64) void k_mb_rows_v(const T *__restrict__ logits, int64_t N, int V, int blank,
                                                   int fused, MbParams mp, const SampleDesc *__restrict__ desc,
                                                   int B, const int32_t *__restrict__ targets, int S,
-                                                  float *__restrict__ den, double *__restrict__ wp,
+                                                  float2 *__restrict__ den, double *__restrict__ wp,
                                                   int64_t n_slots, uint32_t *status, int64_t row_base) {
     using Vec = typename Raw<T>::vec;
     constexpr int VEC = Raw<T>::kVec;
@@ -2148,21 +2200,23 @@ __global__ __launch_bounds__(64) void k_mb_rows_v(const T *__restrict__ logits, 
     const int64_t r = row_base + xcd_block(blockIdx.x, gridDim.x >> 3);
     if (r >= N) return;
     const SampleDesc d = mb_sample_of_row(desc, B, r);
-    const int U1 = d.U + 1;
     const int64_t lr = r - d.row_off;
     const int t = (int)(lr / d.tstride);
     const int u = (int)(lr - (int64_t)t * d.tstride);
     if (t >= d.T || u > d.U) return;  // a padding row of the padded layout
     const T *x = logits + r * (int64_t)V;
     const int nvec = V / VEC;
-    float dn = 0.f;
+    float mr = 0.f, ls2 = 0.f;
+    bool dead = false;
     if (fused) {
         Vec xv[NV];
 #pragma unroll
         for (int i = 0; i < NV; ++i)
             if (FULL || i * 64 + lane < nvec) xv[i] = load_raw<T, true>(x + (int64_t)(i * 64 + lane) * VEC);
-        float m = wave_max_f(row_max<T, NV, FULL>(xv, nvec));
-        const float nm = (m == kNegInf) ? 0.f : -m * kLog2e;
+        const float m = wave_max_f(row_max<T, NV, FULL>(xv, nvec));
+        dead = (m == kNegInf);
+        mr = dead ? 0.f : m;
+        const float nm = -mr * kLog2e;
         float sum = 0.f;
 #pragma unroll
         for (int i = 0; i < NV; ++i)
@@ -2170,9 +2224,9 @@ __global__ __launch_bounds__(64) void k_mb_rows_v(const T *__restrict__ logits, 
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) sum += exp2_fast(fmaf(Raw<T>::get(xv[i], e), kLog2e, nm));
         sum = wave_sum_f(sum);
-        dn = (m == kNegInf) ? kNegInf : m + log2_fast(sum) * kLn2;
+        ls2 = dead ? 0.f : log2_sum_shifted(sum, mr, nm);
     }
-    if (lane == 0) den[r] = dn;
+    if (lane == 0) den[r] = make_float2(mr, ls2);
     float v = kNegInf;
     if (lane < 2 + mp.nb) {
         int k = blank;
@@ -2180,17 +2234,15 @@ __global__ __launch_bounds__(64) void k_mb_rows_v(const T *__restrict__ logits, 
             k = -1;
             if (u < d.U) {
                 const int y = targets[(int64_t)d.index * S + u];
-                bool bad = y < 0 || y >= V || y == blank;
-#pragma unroll
-                for (int i = 0; i < kMaxBigBlanks; ++i) bad = bad || (i < mp.nb && y == mp.ids[i]);
+                const bool bad = !mb_label_ok(y, V, blank, mp);
                 if (bad) atomicOr(status, (uint32_t)RNNT_DEV_BAD_TARGET);
-                k = (y >= 0 && y < V) ? y : -1;
+                k = bad ? -1 : y;
             }
         }
 #pragma unroll
         for (int i = 0; i < kMaxBigBlanks; ++i)
             if (lane == 2 + i) k = mp.ids[i];
-        v = (k >= 0 && dn != kNegInf) ? Elem<T>::load1(x + k) - dn - mp.sigma : kNegInf;
+        v = (k >= 0 && !dead) ? (Elem<T>::load1(x + k) - mr) - ls2 * kLn2 - mp.sigma : kNegInf;
     }
     mb_store_node(d, t, u, mp, lane, v, wp, n_slots);
 }
@@ -2210,7 +2262,7 @@ __global__ __launch_bounds__(64) void k_mb_grad_v(const T *__restrict__ logits, 
                                                   int V, int blank, int fused, MbParams mp, int U1p,
                                                   const SampleDesc *__restrict__ desc, int B,
                                                   const int32_t *__restrict__ targets, int S,
-                                                  const float *__restrict__ den, const double *__restrict__ wp,
+                                                  const float2 *__restrict__ den, const double *__restrict__ wp,
                                                   int64_t n_slots, const double *__restrict__ alpha,
                                                   const double *__restrict__ beta, const int *__restrict__ ealpha,
                                                   const int *__restrict__ ebeta, const double *__restrict__ log2z,
@@ -2242,7 +2294,7 @@ __global__ __launch_bounds__(64) void k_mb_grad_v(const T *__restrict__ logits, 
         for (int i = 0; i < NV; ++i)
             if (FULL || i * 64 + lane < nvec) xv[i] = load_raw<T, true>(x + (int64_t)(i * 64 + lane) * VEC);
     }
-    MbRowTerms rt = mb_row_terms(d, r, t, u, V, fused, mp, U1p, targets, S, den, wp, n_slots, alpha, beta, ealpha,
+    MbRowTerms rt = mb_row_terms(d, r, t, u, V, blank, fused, mp, U1p, targets, S, den, wp, n_slots, alpha, beta, ealpha,
                                  ebeta, log2z, scale, fastemit, mode[d.index] != 0);
     const bool do_clamp = clamp > 0.f;
     const float cl = clamp * scale;
@@ -2253,7 +2305,7 @@ __global__ __launch_bounds__(64) void k_mb_grad_v(const T *__restrict__ logits, 
             float gv[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; ++e)
-                gv[e] = fused ? exp2_fast(fmaf(Raw<T>::get(xv[i], e), kLog2e, rt.shift2)) : 0.f;
+                gv[e] = fused ? exp2_fast(fmaf(Raw<T>::get(xv[i], e) - rt.m, kLog2e, rt.shift2)) : 0.f;
             mb_sub_at<VEC>(gv, vi, i, blank, rt.fb);
             mb_sub_at<VEC>(gv, vi, i, rt.y, rt.fy);
 #pragma unroll
@@ -2338,7 +2390,7 @@ hipError_t launch_mb_rows(const MbArgs &a, hipStream_t stream) {
                 const unsigned nb = (unsigned)((std::min<int64_t>(kMaxBlocks, a.N - b0) + 7) & ~(int64_t)7);
                 hipLaunchKernelGGL((k_mb_rows_v<T, NV, FULL>), dim3(nb), dim3(64), 0, stream,
                                    static_cast<const T *>(a.logits), a.N, a.V, a.blank, a.fused, mp,
-                                   MBWS(const SampleDesc *, desc), a.B, a.targets, a.S, MBWS(float *, den),
+                                   MBWS(const SampleDesc *, desc), a.B, a.targets, a.S, MBWS(float2 *, den),
                                    MBWS(double *, wp), a.lay.n_slots, MBWS(uint32_t *, status), b0);
             }
             return hipGetLastError();
@@ -2350,7 +2402,7 @@ hipError_t launch_mb_rows(const MbArgs &a, hipStream_t stream) {
             const unsigned nb = (unsigned)std::min<int64_t>(kMaxBlocks, blocks - b0);
             hipLaunchKernelGGL(k_mb_rows<T>, dim3(nb), dim3(256), 0, stream, static_cast<const T *>(a.logits), a.N,
                                a.V, a.blank, a.fused, mp, MBWS(const SampleDesc *, desc), a.B, a.targets, a.S,
-                               MBWS(float *, den), MBWS(double *, wp), a.lay.n_slots, MBWS(uint32_t *, status),
+                               MBWS(float2 *, den), MBWS(double *, wp), a.lay.n_slots, MBWS(uint32_t *, status),
                                b0 * 4);
         }
         return hipGetLastError();
@@ -2412,7 +2464,7 @@ hipError_t launch_mb_grad(const MbArgs &a, hipStream_t stream) {
                 hipLaunchKernelGGL((k_mb_grad_v<T, NV, FULL>), dim3(nb), dim3(64), 0, stream,
                                    static_cast<const T *>(a.logits), static_cast<T *>(a.grad), a.N, a.V, a.blank,
                                    a.fused, mp, a.lay.U1p, MBWS(const SampleDesc *, desc), a.B, a.targets, a.S,
-                                   MBWS(const float *, den), MBWS(const double *, wp), a.lay.n_slots,
+                                   MBWS(const float2 *, den), MBWS(const double *, wp), a.lay.n_slots,
                                    MBWS(const double *, alpha), MBWS(const double *, beta),
                                    MBWS(const int *, ealpha), MBWS(const int *, ebeta), MBWS(const double *, log2z),
                                    MBWS(const int *, mode), a.clamp, a.grad_scale, a.fastemit, b0);
@@ -2426,7 +2478,7 @@ hipError_t launch_mb_grad(const MbArgs &a, hipStream_t stream) {
             const unsigned nb = (unsigned)std::min<int64_t>(kMaxBlocks, blocks - b0);
             hipLaunchKernelGGL(k_mb_grad<T>, dim3(nb), dim3(256), 0, stream, static_cast<const T *>(a.logits),
                                static_cast<T *>(a.grad), a.N, a.V, a.blank, a.fused, mp, a.lay.U1p,
-                               MBWS(const SampleDesc *, desc), a.B, a.targets, a.S, MBWS(const float *, den),
+                               MBWS(const SampleDesc *, desc), a.B, a.targets, a.S, MBWS(const float2 *, den),
                                MBWS(const double *, wp), a.lay.n_slots, MBWS(const double *, alpha),
                                MBWS(const double *, beta), MBWS(const int *, ealpha), MBWS(const int *, ebeta),
                                MBWS(const double *, log2z), MBWS(const int *, mode), a.clamp, a.grad_scale,

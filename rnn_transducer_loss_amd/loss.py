@@ -193,7 +193,18 @@ class RNNTLoss(torch.nn.Module):
 
 
 # ------------------------------------------------------ multi-blank transducer
-def rnnt_multiblank_fused(logits: torch.Tensor, targets: torch.Tensor, logit_lengths, target_lengths,
+def _big_blanks(big_blank_ids, big_blank_durations):
+    """Validated lists of the big blanks' classes and durations (same length; ids distinct)."""
+    ids = [int(v) for v in big_blank_ids]
+    durs = [int(v) for v in big_blank_durations]
+    if len(ids) != len(durs):
+        raise ValueError("big_blank_ids and big_blank_durations must have the same length")
+    if len(set(ids)) != len(ids):
+        raise ValueError("big_blank_ids must be distinct classes")
+    return ids, durs
+
+
+def rnnt_multiblank_fused(logits: torch.Tensor, targets: torch.Tensor, logit_lengths, target_lengths, *,
                           big_blank_ids, big_blank_durations, blank: int = -1, sigma: float = 0.0,
                           clamp: float = -1.0, reduction: str = "mean", fused_log_softmax: bool = True,
                           fastemit_lambda: float = 0.0, compute_grad: bool = True,
@@ -202,9 +213,12 @@ def rnnt_multiblank_fused(logits: torch.Tensor, targets: torch.Tensor, logit_len
     """One multi-blank librnnt call.  Returns ``(loss, loss_reduced, grad, workspace)``.
 
     Big blank i is class ``big_blank_ids[i]`` and advances t by ``big_blank_durations[i]`` frames; ``sigma`` is
-    subtracted from every emission's log-probability (logit under-normalisation).  Packed 2-D or padded 4-D
-    logits, the rest as for :func:`rnnt_loss_fused`.
+    subtracted from every emission's log-probability (logit under-normalisation).  Both lists are keyword-only
+    (two integer lists in swapped order would otherwise be accepted silently); the classes must be distinct,
+    in [0, V) and not the blank (the library refuses others).  Packed 2-D or padded 4-D logits, the rest as for
+    :func:`rnnt_loss_fused`.
     """
+    big_blank_ids, big_blank_durations = _big_blanks(big_blank_ids, big_blank_durations)
     tg = _prepare(logits, targets)
     T = _lib.host_i32(logit_lengths)
     U = _lib.host_i32(target_lengths)
@@ -259,8 +273,9 @@ class _MultiblankFunction(torch.autograd.Function):
         T = _lib.host_i32(logit_lengths)
         U = _lib.host_i32(target_lengths)
         loss, loss_red, grad, ws = rnnt_multiblank_fused(
-            logits, targets, T, U, big_blank_ids, big_blank_durations, blank, sigma, clamp, reduction,
-            fused_log_softmax, fastemit_lambda, compute_grad=logits.requires_grad)
+            logits, targets, T, U, big_blank_ids=big_blank_ids, big_blank_durations=big_blank_durations,
+            blank=blank, sigma=sigma, clamp=clamp, reduction=reduction, fused_log_softmax=fused_log_softmax,
+            fastemit_lambda=fastemit_lambda, compute_grad=logits.requires_grad)
         ctx.meta = (T, U, reduction, logits.shape, logits.dtype)
         ctx.used = False
         if grad is not None:
@@ -290,18 +305,20 @@ class _MultiblankFunction(torch.autograd.Function):
         return (grad,) + none
 
 
-def rnnt_loss_multiblank(logits: torch.Tensor, targets: torch.Tensor, logit_lengths, target_lengths,
-                         big_blank_durations, big_blank_ids, blank: int = -1, sigma: float = 0.0,
+def rnnt_loss_multiblank(logits: torch.Tensor, targets: torch.Tensor, logit_lengths, target_lengths, *,
+                         big_blank_ids, big_blank_durations, blank: int = -1, sigma: float = 0.0,
                          clamp: float = -1.0, reduction: str = "mean", fused_log_softmax: bool = True,
                          fastemit_lambda: float = 0.0) -> torch.Tensor:
     """Multi-blank transducer loss over packed (or padded 4-D) logits, differentiable with respect to ``logits``.
 
     ``big_blank_durations[i]`` is the number of frames big blank i (class ``big_blank_ids[i]``) advances;
     ``sigma`` lowers every emission's log-probability (logit under-normalisation).  With no big blank and
-    ``sigma = 0`` this is :func:`rnnt_loss`.
+    ``sigma = 0`` this is :func:`rnnt_loss`.  The big-blank lists are keyword-only, as in
+    :func:`rnnt_multiblank_fused`.
     """
     if reduction not in ("none", "mean", "sum"):
         raise ValueError(f"reduction must be none, mean or sum, got {reduction!r}")
-    return _MultiblankFunction.apply(logits, targets, logit_lengths, target_lengths, list(big_blank_ids),
-                                     list(big_blank_durations), int(blank), float(sigma), float(clamp), reduction,
+    big_blank_ids, big_blank_durations = _big_blanks(big_blank_ids, big_blank_durations)
+    return _MultiblankFunction.apply(logits, targets, logit_lengths, target_lengths, big_blank_ids,
+                                     big_blank_durations, int(blank), float(sigma), float(clamp), reduction,
                                      bool(fused_log_softmax), float(fastemit_lambda))

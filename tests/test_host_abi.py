@@ -265,9 +265,10 @@ def test_multiblank_padded_sizes_and_limits():
     N = int((T * (U + 1)).sum())
     packed = _lib.workspace_size_multiblank(3, 32, N, _lib.RNNT_F32, T, U, [2, 3])
     padded = _lib.workspace_size_multiblank_padded(3, 32, 6, 6, _lib.RNNT_F32, T, U, [2, 3])
-    # the padded layout only adds the per-row normalisers of its padding rows
-    assert padded - packed == (lambda b: (b + 255) // 256 * 256)(4 * 3 * 6 * 6) - \
-        (lambda b: (b + 255) // 256 * 256)(4 * N)
+    # the padded layout only adds the per-row normalisers (two fp32 values: the row maximum and log2 of the
+    # sum of exp(x - maximum)) of its padding rows
+    assert padded - packed == (lambda b: (b + 255) // 256 * 256)(8 * 3 * 6 * 6) - \
+        (lambda b: (b + 255) // 256 * 256)(8 * N)
     for max_T, max_U1 in ((5, 6), (6, 5), (0, 6)):   # a sample does not fit, or an empty extent
         with pytest.raises(ValueError):
             _lib.workspace_size_multiblank_padded(3, 32, max_T, max_U1, _lib.RNNT_F32, T, U, [2, 3])

@@ -46,7 +46,8 @@ def run_mb(rl, w, reduction=None, clamp=None, fastemit=0.0, compute_grad=True):
     clamp = w.clamp if clamp is None else clamp
     tg = torch.from_numpy(w.targets).to("cuda")
     loss, red, grad, ws = rl.rnnt_multiblank_fused(w.logits, tg, w.logit_lengths, w.target_lengths,
-                                                   w.big_blank_ids, w.big_blank_durations, blank=w.blank,
+                                                   big_blank_ids=w.big_blank_ids,
+                                                   big_blank_durations=w.big_blank_durations, blank=w.blank,
                                                    sigma=w.sigma, clamp=clamp, reduction=reduction,
                                                    fused_log_softmax=w.fused, fastemit_lambda=fastemit,
                                                    compute_grad=compute_grad)
@@ -147,7 +148,8 @@ def test_multiblank_autograd(rl, reduction):
     x = w.logits.clone().requires_grad_(True)
     tg = torch.from_numpy(w.targets).cuda()
     out = rl.rnnt_loss_multiblank(x, tg, torch.from_numpy(w.logit_lengths).cuda(),
-                                  torch.from_numpy(w.target_lengths).cuda(), w.big_blank_durations, w.big_blank_ids,
+                                  torch.from_numpy(w.target_lengths).cuda(), big_blank_ids=w.big_blank_ids,
+                                  big_blank_durations=w.big_blank_durations,
                                   blank=-1, sigma=w.sigma, reduction=reduction)
     if reduction == "none":
         up = torch.tensor([0.5, 2.0, -1.0], device="cuda")
@@ -166,29 +168,45 @@ def test_multiblank_autograd(rl, reduction):
         assert abs(out.item() - expect) <= 1e-5 * abs(expect)
 
 
-def test_multiblank_bad_targets_are_flagged(rl):
-    w = _mb([8, 6], [3, 2], 12, [10, 9], [2, 3], 0.0, std=1.0, blank=-1, reduction="none", seed=8)
+@pytest.mark.parametrize("fused", [True, False])
+def test_multiblank_bad_targets_are_flagged(rl, fused):
+    """Labels equal to a big blank's class, to the standard blank or outside [0, V) are no symbols: those samples
+    have no alignment (loss +inf, zero gradient) on both sides, the status word is flagged, and the other
+    samples match the oracle."""
+    w = _mb([8, 6, 7, 9], [3, 2, 3, 4], 12, [10, 9], [2, 3], 0.05, std=1.0, blank=-1, fused=fused,
+            prenormalise=not fused, reduction="none", seed=8)
     tg = w.targets.copy()
     tg[0, 1] = 10         # a big blank's class
+    tg[2, 0] = 11         # the standard blank
+    tg[3, 3] = 12         # outside [0, V)
     w.targets = tg
     loss, red, grad, flags = run_mb(rl, w)
     assert flags & 2
-    assert math.isfinite(loss[0].item()) and math.isfinite(loss[1].item())
-    # the other sample is unaffected (the oracle refuses the flagged one)
-    T, U = int(w.logit_lengths[1]), int(w.target_lengths[1])
-    r = oracle.multiblank_sample(w.logits[w.rows(1)].cpu().numpy(), T, U, w.targets[1], w.V - 1, w.big_blank_ids,
-                                 w.big_blank_durations, w.sigma)
-    assert abs(loss[1].item() - r.loss) <= 1e-5 * max(1.0, abs(r.loss))
-    assert np.abs(grad[w.rows(1)].double().cpu().numpy() - r.grad).max() <= 1e-5
+    x = w.logits.float().cpu().numpy()
+    for i in range(w.B):
+        T, U = int(w.logit_lengths[i]), int(w.target_lengths[i])
+        r = oracle.multiblank_sample(x[w.rows(i)], T, U, w.targets[i], w.V - 1, w.big_blank_ids,
+                                     w.big_blank_durations, w.sigma, fused=fused, allow_bad_targets=True)
+        g = grad[w.rows(i)].double().cpu().numpy()
+        if i == 1:
+            assert not r.bad_target
+            assert abs(loss[i].item() - r.loss) <= 1e-5 * max(1.0, abs(r.loss))
+            assert np.abs(g - r.grad).max() <= 1e-5
+        else:
+            assert r.bad_target and np.isinf(r.loss) and np.all(r.grad == 0)
+            assert math.isinf(loss[i].item()) and loss[i].item() > 0 and np.all(g == 0), i
 
 
 def test_multiblank_score_only_and_deterministic(rl):
+    """grad = NULL: every loss against the oracle and bit for bit equal to the full call's; repeated calls
+    are bitwise identical."""
     w = _mb([50, 31], [12, 7], 200, [198, 197], [2, 4], 0.05, std=2.0, blank=-1, reduction="sum", seed=4)
     a = run_mb(rl, w)
     b = run_mb(rl, w)
     c = run_mb(rl, w, compute_grad=False)
     assert torch.equal(a[0], b[0]) and torch.equal(a[2], b[2]) and torch.equal(a[0], c[0])
     assert c[2] is None
+    check_mb(w, c[0], None, "sum")
 
 
 def test_multiblank_workload_full_size(rl):
@@ -204,17 +222,31 @@ def test_multiblank_workload_full_size(rl):
 
 def test_multiblank_extreme_fused_logits(rl):
     """Fused logits of spread N(0, 40^2): edge log-probabilities reach about -300, far outside fp32's exponent
-    range, inside fp64's (the sweep works in fp64 probabilities).  Tolerance as for the plain path's extreme case:
-    the fp32 inputs themselves carry ~1.5e-5 rounding at |x| ~ 160, so the gradient is held to 2e-4 and the loss
-    to 1e-5 relative."""
+    range, inside fp64's (the sweep works in fp64 probabilities).  The fp32 row steps work on x - max, so the
+    fp32 gate holds: loss 1e-5 relative, gradient 1e-5."""
     w = _mb([25, 11, 7], [5, 4, 0], 64, [60, 61], [2, 3], 0.1, std=40.0, blank=-1, reduction="sum", seed=43)
     loss, red, grad, flags = run_mb(rl, w)
     assert flags == 0
-    ref_l, _, ref_g, _ = oracle.multiblank_batch(w.logits.cpu().numpy(), w.targets, w.logit_lengths,
-                                                 w.target_lengths, w.big_blank_ids, w.big_blank_durations,
-                                                 blank=-1, sigma=w.sigma, reduction="none")
-    np.testing.assert_allclose(loss.double().cpu().numpy(), ref_l, rtol=1e-5, atol=0)
-    assert np.abs(grad.double().cpu().numpy() - ref_g).max() <= 2e-4
+    check_mb(w, loss, grad, "sum")
+
+
+@pytest.mark.parametrize("offset", [100.0, 1000.0, "random"])
+@pytest.mark.parametrize("V,dtype", [(1024, torch.float32), (50, torch.float32), (4096, torch.float16)])
+def test_multiblank_fused_logit_offsets(rl, V, dtype, offset):
+    """A constant added to each row's logits (100, 1000, or a per-row constant from [-1000, 1000]) leaves the
+    multi-blank loss and gradient at the gates (log_softmax is shift-invariant)."""
+    ids = [V - 2, V - 3, V - 4]
+    w = _mb([40, 23, 31], [12, 7, 0], V, ids, [2, 4, 8], 0.05, dtype=dtype, std=2.0, blank=-1, reduction="mean",
+            seed=V)
+    if offset == "random":
+        g = torch.Generator(device="cuda").manual_seed(V)
+        c = torch.rand(w.N, 1, generator=g, device="cuda", dtype=torch.float64) * 2000.0 - 1000.0
+    else:
+        c = torch.full((w.N, 1), float(offset), device="cuda", dtype=torch.float64)
+    w.logits = (w.logits.double() + c).to(dtype)
+    loss, red, grad, flags = run_mb(rl, w)
+    assert flags == 0
+    check_mb(w, loss, grad, "mean")
 
 
 def test_multiblank_very_long_lattices(rl):
@@ -352,8 +384,9 @@ def test_multiblank_padded_matches_packed(rl, V, dtype, fused):
     max_T, max_U1 = max(Ts) + 2, max(Us) + 3
     xp = _padded(w, max_T, max_U1)
     tg = torch.from_numpy(w.targets).to("cuda")
-    loss_p, red_p, grad_p, ws = rl.rnnt_multiblank_fused(xp, tg, w.logit_lengths, w.target_lengths, w.big_blank_ids,
-                                                         w.big_blank_durations, blank=w.blank, sigma=w.sigma,
+    loss_p, red_p, grad_p, ws = rl.rnnt_multiblank_fused(xp, tg, w.logit_lengths, w.target_lengths,
+                                                         big_blank_ids=w.big_blank_ids,
+                                                         big_blank_durations=w.big_blank_durations, blank=w.blank, sigma=w.sigma,
                                                          reduction="sum", fused_log_softmax=fused)
     assert rl.device_flags(ws) == 0
     loss, red, grad, _ = run_mb(rl, w)
@@ -370,11 +403,13 @@ def test_multiblank_padded_autograd(rl):
     w = _mb(Ts, Us, 48, [45, 46], [3, 2], 0.1, std=2.0, blank=-1, reduction="none", seed=47)
     tg = torch.from_numpy(w.targets).to("cuda")
     xp = _padded(w, 24, 9, fill=0.0)
-    ref_loss, _, ref_grad, _ = rl.rnnt_multiblank_fused(xp, tg, w.logit_lengths, w.target_lengths, w.big_blank_ids,
-                                                        w.big_blank_durations, blank=-1, sigma=w.sigma,
+    ref_loss, _, ref_grad, _ = rl.rnnt_multiblank_fused(xp, tg, w.logit_lengths, w.target_lengths,
+                                                        big_blank_ids=w.big_blank_ids,
+                                                        big_blank_durations=w.big_blank_durations, blank=-1, sigma=w.sigma,
                                                         reduction="none")
     x = xp.clone().requires_grad_(True)
-    out = rl.rnnt_loss_multiblank(x, tg, w.logit_lengths, w.target_lengths, w.big_blank_durations, w.big_blank_ids,
+    out = rl.rnnt_loss_multiblank(x, tg, w.logit_lengths, w.target_lengths, big_blank_ids=w.big_blank_ids,
+                                  big_blank_durations=w.big_blank_durations,
                                   blank=-1, sigma=w.sigma, reduction="none")
     up = torch.tensor([0.5, -2.0, 3.0], device="cuda")
     out.backward(up)

@@ -159,23 +159,24 @@ def test_bpe_workload_full_size(rl):
 
 
 def test_half_workload_full_size(rl):
+    """The fp16 workload at full size (16 samples, V = 4096): every loss, and in every sample the gradient of
+    rows (0,0), (0,1), (0,U), (T-1,U), the two rows before it and 200 random rows."""
     w = workloads.make("half", device="cuda")
     loss, red, grad, flags = run(rl, w)
     assert flags == 0
-    order = np.argsort(w.logit_lengths.astype(np.int64) * (w.target_lengths + 1))
-    picks = [int(order[0]), int(order[-1])]
-    check_against_oracle(w, loss, grad, w.reduction, grad_rows=3000, samples=picks)
+    check_against_oracle(w, loss, grad, w.reduction, grad_rows=200)
     _reduced_ok(w, loss, red, w.reduction)
     assert torch.isfinite(grad).all()
 
 
 def test_skewed_workload_full_size(rl):
+    """The skewed log-prob workload at full size (64 samples): every loss, and in every sample the gradient of
+    the corner rows and 200 random rows."""
     w = workloads.make("skewed", device="cuda")
     loss, red, grad, flags = run(rl, w)
     assert flags == 0
     order = np.argsort(w.logit_lengths.astype(np.int64) * (w.target_lengths + 1))
-    picks = [int(order[0]), int(order[-1]), int(order[len(order) // 2])]
-    check_against_oracle(w, loss, grad, w.reduction, grad_rows=4000, samples=picks)
+    check_against_oracle(w, loss, grad, w.reduction, grad_rows=200)
     _reduced_ok(w, loss, red, w.reduction)
     # non-fused: at most two non-zeros per row; per sample the entries sum to -(T+U)
     nnz = (grad != 0).sum(dim=1)
@@ -336,10 +337,17 @@ def test_inplace_gradient_over_logits(rl):
     assert torch.equal(grad, ref_grad)
 
 
-def test_score_only(rl):
-    w = _custom([40, 20], [10, 7], 64, std=2.0, blank=-1, reduction="sum", seed=4)
+@pytest.mark.parametrize("V,dtype,fused", [(64, torch.float32, True), (1024, torch.float32, True),
+                                           (29, torch.float32, True), (2048, torch.float16, False)])
+def test_score_only(rl, V, dtype, fused):
+    """grad = NULL (the GPURNNT page's score_forward: costs without gradients): every loss against the oracle,
+    and bit for bit equal to the loss of the full call."""
+    w = _custom([40, 20, 33], [10, 7, 0], V, dtype=dtype, std=2.0 if fused else 1.5, blank=-1, fused=fused,
+                prenormalise=not fused, reduction="sum", seed=4)
     loss, red, grad, flags = run(rl, w, compute_grad=False)
-    assert grad is None
+    assert grad is None and flags == 0
+    check_against_oracle(w, loss, None, "sum")
+    _reduced_ok(w, loss, red, "sum")
     ref, _, _, _ = run(rl, w)
     assert torch.equal(loss, ref)
 
@@ -362,17 +370,26 @@ def test_deterministic_bitwise(rl):
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
 
 
-def test_bad_targets_are_flagged(rl):
-    w = _custom([6, 5], [3, 2], 10, std=1.0, blank=-1, reduction="none", seed=8)
+@pytest.mark.parametrize("fused", [True, False])
+def test_bad_targets_are_flagged(rl, fused):
+    """A label equal to blank or outside [0, V) is no symbol an alignment can emit (the build post's section 5.2
+    rules blank out of the labels): that sample has no alignment, loss +inf and a zero gradient, on both sides;
+    the status word is flagged and the other samples are unaffected."""
+    w = _custom([6, 5, 9], [3, 2, 4], 10, std=1.0, blank=-1, fused=fused, prenormalise=not fused,
+                reduction="none", seed=8)
     tg = w.targets.copy()
     tg[0, 1] = 9          # equals blank (V-1)
     tg[1, 0] = 12         # outside [0, V)
     w.targets = tg
     loss, red, grad, flags = run(rl, w)
     assert flags & 2
-    assert math.isinf(loss[1].item()) and loss[1].item() > 0
-    assert grad[w.rows(1)].abs().max().item() == 0.0
-    assert math.isfinite(loss[0].item())
+    x = w.logits.float().cpu().numpy()
+
+    def ref(i):
+        T, U = int(w.logit_lengths[i]), int(w.target_lengths[i])
+        return oracle.sample(x[w.rows(i)], T, U, w.targets[i], 9, fused, -1.0, allow_bad_targets=True)
+    check_masked(w, loss, grad, ref)
+    assert math.isinf(loss[0].item()) and math.isinf(loss[1].item()) and math.isfinite(loss[2].item())
 
 
 # ------------------------------------------------------------------- autograd
@@ -450,19 +467,60 @@ def test_log_domain_across_register_tiles(rl, U):
 
 
 def test_extreme_fused_logits(rl):
-    """Fused logits of spread ~N(0, 40^2): log-probs reach -300, the sample takes the log-domain sweep.
-
-    Tolerance derived from fp32 input rounding: |logit| ~ 160 has ulp 1.5e-5, so each
-    log-prob carries up to ~2e-5 absolute error; the loss stays within 1e-5 relative
-    (it is ~1e3-1e4) and the gradient within 2e-4 absolute.
-    """
+    """Fused logits of spread ~N(0, 40^2): log-probs reach -300, the sample takes the log-domain sweep.  The
+    fp32 steps work on x - max, never on x, so the fp32 gate holds: loss 1e-5 relative, gradient 1e-5."""
     w = _custom([25, 11], [5, 4], 64, std=40.0, blank=-1, reduction="sum", seed=42)
     loss, red, grad, flags = run(rl, w)
     assert flags == 0
-    ref = oracle.batch(w.logits.cpu().numpy(), w.targets, w.logit_lengths, w.target_lengths, blank=-1,
-                       reduction="sum")
-    np.testing.assert_allclose(loss.double().cpu().numpy(), ref[0], rtol=1e-5, atol=0)
-    assert np.abs(grad.double().cpu().numpy() - ref[2]).max() <= 2e-4
+    check_against_oracle(w, loss, grad, "sum")
+
+
+def _offset_rows(w, offset, seed):
+    """The logits of w with a constant added to every row: `offset` itself, or (offset "random") a per-row
+    constant drawn uniformly from [-1000, 1000].  The sum is rounded to the logits' dtype; the oracle reads the
+    rounded values."""
+    if offset == "random":
+        g = torch.Generator(device="cuda").manual_seed(seed)
+        c = (torch.rand(w.N, 1, generator=g, device="cuda", dtype=torch.float64) * 2000.0 - 1000.0)
+    else:
+        c = torch.full((w.N, 1), float(offset), device="cuda", dtype=torch.float64)
+    return (w.logits.double() + c).to(w.logits.dtype)
+
+
+@pytest.mark.parametrize("offset", [50.0, 100.0, 300.0, 1000.0, -1000.0, "random"])
+@pytest.mark.parametrize("case", ["tiny", "char", "bpe_shaped", "wide_fp32", "half_fp16"])
+def test_fused_logit_offsets(rl, case, offset):
+    """log_softmax is shift-invariant (README parameter table, fused_log_softmax; "Value" section 3), so a
+    constant added to a row's logits must leave the fused path within the parity gates: fp32 loss 1e-5
+    relative and gradient 1e-5 absolute (fp16: 2e-3 / 3e-3).  Offsets of 50 to 1000 (and random per-row
+    ones) on the tiny and char workloads, a bpe-shaped batch (V = 1024, one 4 KiB row per wave), rows of
+    16 KiB split over four gradient waves, and fp16 rows of V = 4096."""
+    if case in ("tiny", "char"):
+        w = workloads.make(case, device="cuda")
+    elif case == "bpe_shaped":
+        w = _custom([60, 37, 81], [20, 9, 31], 1024, std=2.0, blank=-1, reduction="mean", seed=31)
+    elif case == "wide_fp32":
+        w = _custom([9, 14], [6, 3], 4096, std=2.0, blank=-1, reduction="sum", seed=32)
+    else:
+        w = _custom([30, 21], [8, 12], 4096, dtype=torch.float16, std=2.0, blank=-1, clamp=1.0,
+                    reduction="mean", seed=33)
+    w.logits = _offset_rows(w, offset, seed=len(case))
+    loss, red, grad, flags = run(rl, w)
+    assert flags == 0
+    check_against_oracle(w, loss, grad, w.reduction)
+
+
+def test_bpe_workload_random_row_offsets(rl):
+    """The full bpe batch with a per-row offset drawn from [-1000, 1000]: every loss at 1e-5, every gradient
+    row of the smallest and the largest sample at 1e-5, 200 rows of every other sample; fused rows sum to 0."""
+    w = workloads.make("bpe", device="cuda")
+    w.logits = _offset_rows(w, "random", seed=3)
+    loss, red, grad, flags = run(rl, w)
+    assert flags == 0
+    order = np.argsort(w.logit_lengths.astype(np.int64) * (w.target_lengths + 1))
+    check_against_oracle(w, loss, grad, w.reduction, grad_rows="all", samples=[int(order[0]), int(order[-1])])
+    check_against_oracle(w, loss, grad, w.reduction, grad_rows=200, samples=[int(i) for i in order[1:-1]], seed=1)
+    assert grad.double().sum(dim=1).abs().max().item() < 1e-6
 
 
 def test_mixed_domains_in_one_batch(rl):
@@ -603,7 +661,8 @@ def test_graph_capture_refuses_host_copies(rl):
             rl.rnnt_loss_fused(w.logits, tg, w.logit_lengths, w.target_lengths, reduction="none", grad=grad,
                                workspace=ws, loss=loss)
         with pytest.raises(ValueError):
-            rl.rnnt_multiblank_fused(w.logits, tg, w.logit_lengths, w.target_lengths, [13], [2], reduction="none",
+            rl.rnnt_multiblank_fused(w.logits, tg, w.logit_lengths, w.target_lengths, big_blank_ids=[13],
+                                     big_blank_durations=[2], reduction="none",
                                      grad=grad, loss=loss)
     torch.cuda.synchronize()
     loss2, _, _, _ = rl.rnnt_loss_fused(w.logits, tg, w.logit_lengths, w.target_lengths, reduction="none")
