@@ -219,6 +219,41 @@ rnnt_status rnnt_grad_scale_padded(void *grad, rnnt_dtype dtype, int32_t max_T, 
                                    size_t workspace_bytes, rnnt_stream_t stream);
 
 /*
+ * rnnt_loss_fused without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory during the call: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The workspace is a fixed device array inside the library, 128 MiB
+ * (RNNT_NOALLOC_SCRATCH_BYTES) per device, held by every device that loads
+ * the library until the process ends.  The call makes no device, pinned or
+ * host heap allocation and uses no plan cache; its address is looked up
+ * once per device on the first call made with that device current.
+ *
+ *   Arguments as for rnnt_loss_fused (packed layout), minus the workspace,
+ *   plus:
+ *   dev_status        device uint32, or NULL: receives the device status
+ *                     word of this call (RNNT_DEV_* bits), which
+ *                     rnnt_loss_fused_check would read from a workspace.
+ * Returns what rnnt_loss_fused returns, and RNNT_INVALID_VALUE for B > 64
+ * (the schedule travels as kernel arguments; larger batches would need the
+ * host staging copy, which allocates), RNNT_WORKSPACE_TOO_SMALL when the
+ * batch needs more than RNNT_NOALLOC_SCRATCH_BYTES of workspace (the size
+ * rnnt_loss_fused_workspace_size reports), RNNT_MEMOPS_FAILED when the
+ * scratch address cannot be obtained.
+ * Every call on one device shares that device's scratch and leaves its
+ * contents behind (the next call rewrites what it reads; the status word is
+ * cleared at the start of each call): calls that overlap in time on one
+ * device, from several streams or threads, race and give undefined
+ * results.  Serialise them (one stream, or events between streams).
+ */
+#define RNNT_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+rnnt_status rnnt_loss_fused_noalloc(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V,
+                                    const int32_t *targets, int32_t S, const int32_t *logit_lengths,
+                                    const int32_t *target_lengths, int32_t B, int64_t blank, float clamp,
+                                    float fastemit_lambda, int fused_log_softmax, rnnt_reduction reduction,
+                                    float *loss, float *loss_reduced, void *grad, uint32_t *dev_status,
+                                    rnnt_stream_t stream);
+
+/*
  * Multi-blank transducer loss and gradient (the ESPnet
  * compute_multiblank_grad_kernel page: activations over the labels, the
  * standard blank and num_big_blanks big blanks; each big blank has a

@@ -27,7 +27,9 @@ EXPORTS = ("rnnt_loss_fused_workspace_size", "rnnt_loss_fused", "rnnt_grad_scale
            "rnnt_status_string", "rnnt_plan_describe", "rnnt_timing_enable", "rnnt_timing_read",
            "rnnt_loss_padded_workspace_size", "rnnt_loss_padded", "rnnt_grad_scale_padded",
            "rnnt_multiblank_workspace_size", "rnnt_multiblank_loss", "rnnt_multiblank_grad_scale",
-           "rnnt_multiblank_padded_workspace_size", "rnnt_multiblank_loss_padded", "rnnt_multiblank_grad_scale_padded")
+           "rnnt_multiblank_padded_workspace_size", "rnnt_multiblank_loss_padded", "rnnt_multiblank_grad_scale_padded",
+           "rnnt_loss_fused_noalloc")
+NOALLOC_SCRATCH_BYTES = 128 << 20   # RNNT_NOALLOC_SCRATCH_BYTES
 KERNELS = ("rowstats", "alpha_beta", "grad", "reduce")
 
 _lib = None
@@ -60,6 +62,11 @@ def load():
                                         ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp,
                                         ctypes.c_size_t, _vp]
         lib.rnnt_loss_fused.restype = ctypes.c_int
+        lib.rnnt_loss_fused_noalloc.argtypes = [_vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, _vp,
+                                                ctypes.c_int32, _i32p, _i32p, ctypes.c_int32, ctypes.c_int64,
+                                                ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, _vp,
+                                                _vp, _vp, _vp]
+        lib.rnnt_loss_fused_noalloc.restype = ctypes.c_int
         lib.rnnt_grad_scale.argtypes = [_vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, _i32p, _i32p,
                                         ctypes.c_int32, _vp, ctypes.c_int, _vp, ctypes.c_size_t, _vp]
         lib.rnnt_grad_scale.restype = ctypes.c_int
@@ -172,6 +179,25 @@ def loss_fused(logits_ptr: int, dtype_code: int, N: int, V: int, targets_ptr: in
                                 loss_reduced_ptr or None, grad_ptr or None, ws_ptr or None, ws_bytes,
                                 stream or None)
     check(rc, "rnnt_loss_fused")
+
+
+def loss_fused_noalloc(logits_ptr: int, dtype_code: int, N: int, V: int, targets_ptr: int, S: int, logit_lengths,
+                       target_lengths, blank: int, clamp: float, fused: bool, reduction: str, loss_ptr: int,
+                       loss_reduced_ptr: int, grad_ptr: int, status_ptr: int, stream: int,
+                       fastemit_lambda: float = 0.0):
+    """rnnt_loss_fused_noalloc: the workspace is the library's fixed device scratch (no allocation)."""
+    T = host_i32(logit_lengths)
+    U = host_i32(target_lengths)
+    B = len(T)
+    if len(U) != B:
+        raise ValueError("length vectors must have B entries")
+    if reduction not in REDUCTIONS:
+        raise ValueError(f"reduction must be one of {sorted(REDUCTIONS)}")
+    rc = load().rnnt_loss_fused_noalloc(logits_ptr or None, dtype_code, N, V, targets_ptr or None, S, _p(T), _p(U),
+                                        B, int(blank), float(clamp), float(fastemit_lambda), int(bool(fused)),
+                                        REDUCTIONS[reduction], loss_ptr or None, loss_reduced_ptr or None,
+                                        grad_ptr or None, status_ptr or None, stream or None)
+    check(rc, "rnnt_loss_fused_noalloc")
 
 
 def grad_scale(grad_ptr: int, dtype_code: int, N: int, V: int, logit_lengths, target_lengths, scale_ptr: int,

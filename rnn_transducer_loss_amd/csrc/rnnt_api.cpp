@@ -36,7 +36,6 @@ struct Padding {
 struct Plan {
     std::vector<SampleDesc> desc;
     std::vector<int32_t> order;
-    std::vector<ChunkDesc> chunks;
     WorkspaceLayout lay{};
     int max_U1 = 1;
 };
@@ -51,18 +50,29 @@ rnnt_status check_lengths(int32_t B, int32_t V, const int32_t *T, const int32_t 
 }
 
 // Samples by decreasing cost: lattice area T*(U+1) (the README's balancing
-// key), then the length T+U of the recursion's critical path, then index.
-std::vector<int32_t> lpt_order(int32_t B, const int32_t *T, const int32_t *U) {
-    std::vector<int32_t> ord(B);
-    std::iota(ord.begin(), ord.end(), 0);
-    std::stable_sort(ord.begin(), ord.end(), [&](int32_t a, int32_t b) {
+// key), then the length T+U of the recursion's critical path, then index,
+// into ord[B].  The key is a strict total order, so every sorting method
+// gives the same result; batches of up to kArgSamples samples take an
+// insertion sort, which allocates nothing.
+void lpt_order_into(int32_t B, const int32_t *T, const int32_t *U, int32_t *ord) {
+    auto before = [&](int32_t a, int32_t b) {
         const int64_t aa = (int64_t)T[a] * (U[a] + 1), ab = (int64_t)T[b] * (U[b] + 1);
         if (aa != ab) return aa > ab;
         const int64_t la = (int64_t)T[a] + U[a], lb = (int64_t)T[b] + U[b];
         if (la != lb) return la > lb;
         return a < b;
-    });
-    return ord;
+    };
+    for (int32_t i = 0; i < B; ++i) ord[i] = i;
+    if (B <= kArgSamples) {
+        for (int32_t i = 1; i < B; ++i) {
+            const int32_t v = ord[i];
+            int32_t j = i;
+            for (; j > 0 && before(v, ord[j - 1]); --j) ord[j] = ord[j - 1];
+            ord[j] = v;
+        }
+    } else {
+        std::sort(ord, ord + B, before);
+    }
 }
 
 // Rows per chunk: about 256 KiB of logits per workgroup, but at least ~1024
@@ -85,8 +95,13 @@ int32_t rows_per_chunk(int64_t N, int32_t V, int esize) {
     return (int32_t)std::min<int64_t>(r, 1 << 16);
 }
 
-rnnt_status build_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t *T, const int32_t *U,
-                       Plan &p, const Padding &pad = Padding()) {
+// The sample descriptors (desc[B]), the longest-first order (order[B]) and
+// the workspace layout of a batch, in caller storage; allocates nothing.
+// Every sample's rows are cut into chunks of `rows_per_chunk` rows, numbered
+// in longest-first sample order (the chunk table itself is built on the
+// device from the descriptors, and by make_chunk on the host when asked for).
+rnnt_status plan_into(int32_t B, int32_t V, int64_t N, int esize, const int32_t *T, const int32_t *U,
+                      const Padding &pad, SampleDesc *desc, int32_t *order, WorkspaceLayout &L, int32_t &max_U1) {
     rnnt_status st = check_lengths(B, V, T, U);
     if (st != RNNT_SUCCESS) return st;
     if (pad.on()) {
@@ -95,11 +110,10 @@ rnnt_status build_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t
             if (T[i] > pad.max_T || U[i] + 1 > pad.max_U1) return RNNT_INVALID_VALUE;
         if ((int64_t)B * pad.max_T * pad.max_U1 >= ((int64_t)1 << 62) / std::max(1, V)) return RNNT_INVALID_VALUE;
     }
-    p.desc.resize(B);
     int64_t row = 0, slot = 0, diag = 0, ab = 0;
-    p.max_U1 = 1;
+    max_U1 = 1;
     for (int32_t i = 0; i < B; ++i) {
-        SampleDesc &d = p.desc[i];
+        SampleDesc &d = desc[i];
         d.row_off = pad.on() ? (int64_t)i * pad.max_T * pad.max_U1 : row;
         d.tstride = pad.on() ? pad.max_U1 : U[i] + 1;
         d.chunk0 = 0;
@@ -114,32 +128,31 @@ rnnt_status build_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t
         slot += ((int64_t)T[i] + U[i]) * (U[i] + 1);
         diag += (int64_t)T[i] + U[i];
         ab += ((int64_t)T[i] + U[i]) * d.U1p;
-        p.max_U1 = std::max(p.max_U1, U[i] + 1);
+        max_U1 = std::max(max_U1, U[i] + 1);
     }
     if (N >= 0 && row != N) return RNNT_INVALID_VALUE;
     if (row >= ((int64_t)1 << 62) / std::max(1, V)) return RNNT_INVALID_VALUE;
-    p.order = lpt_order(B, T, U);
+    lpt_order_into(B, T, U, order);
     const int32_t rpc = rows_per_chunk(row, V, esize);
-    p.chunks.clear();
-    int64_t max_sample_chunks = 0;
+    int64_t n_chunks = 0, max_sample_chunks = 0;
     for (int32_t k = 0; k < B; ++k) {
-        const int32_t i = p.order[k];
+        const int32_t i = order[k];
         const int64_t rows = (int64_t)T[i] * (U[i] + 1);
         if (rows > INT32_MAX) return RNNT_INVALID_VALUE;
-        p.desc[i].chunk0 = (int32_t)std::min<size_t>(p.chunks.size(), INT32_MAX);
+        desc[i].chunk0 = (int32_t)std::min<int64_t>(n_chunks, INT32_MAX);
         const int64_t n = (rows + rpc - 1) / rpc;
         max_sample_chunks = std::max(max_sample_chunks, n);
-        for (int64_t j = 0; j < n; ++j) p.chunks.push_back(make_chunk(p.desc[i], i, (int32_t)j, rpc));
+        n_chunks += n;
     }
-    if (p.chunks.size() > (size_t)INT32_MAX) return RNNT_INVALID_VALUE;
-    WorkspaceLayout &L = p.lay;
+    if (n_chunks > INT32_MAX) return RNNT_INVALID_VALUE;
     size_t off = 0;
+    L = WorkspaceLayout{};
     L.status = 0;
     off = 256;
     L.mode = off;   off = align_up(off + sizeof(int32_t) * B);
     L.desc = off;   off = align_up(off + sizeof(SampleDesc) * B);
     L.order = off;  off = align_up(off + sizeof(int32_t) * B);
-    L.chunks = off; off = align_up(off + sizeof(ChunkDesc) * p.chunks.size());
+    L.chunks = off; off = align_up(off + sizeof(ChunkDesc) * (size_t)n_chunks);
     L.node = off;   off = align_up(off + 4 * sizeof(float) * (size_t)slot);
     L.prob = off;   off = align_up(off + 2 * sizeof(float) * (size_t)slot);
     L.alpha = off;  off = align_up(off + sizeof(double) * (size_t)ab);
@@ -151,10 +164,19 @@ rnnt_status build_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t
     L.n_slots = slot;
     L.n_ab_slots = ab;
     L.n_diags = diag;
-    L.n_chunks = (int32_t)p.chunks.size();
+    L.n_chunks = (int32_t)n_chunks;
     L.rows_per_chunk = rpc;
     L.max_sample_chunks = (int32_t)max_sample_chunks;
     return RNNT_SUCCESS;
+}
+
+rnnt_status build_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t *T, const int32_t *U,
+                       Plan &p, const Padding &pad = Padding()) {
+    rnnt_status st = check_lengths(B, V, T, U);
+    if (st != RNNT_SUCCESS) return st;
+    p.desc.resize(B);
+    p.order.resize(B);
+    return plan_into(B, V, N, esize, T, U, pad, p.desc.data(), p.order.data(), p.lay, p.max_U1);
 }
 
 int esize_of(rnnt_dtype dt) { return dt == RNNT_F32 ? 4 : (dt == RNNT_F16 ? 2 : 0); }
@@ -360,13 +382,23 @@ rnnt_status rnnt_plan_describe(int32_t B, int32_t V, rnnt_dtype dtype, const int
     if (st != RNNT_SUCCESS) return st;
     if (sample_order)
         for (int32_t k = 0; k < B && k < cap; ++k) sample_order[k] = p.order[k];
-    const int32_t nc = (int32_t)p.chunks.size();
-    for (int32_t k = 0; k < nc && k < cap; ++k) {
-        if (chunk_sample) chunk_sample[k] = p.chunks[k].sample;
-        if (chunk_row_begin) chunk_row_begin[k] = p.chunks[k].row_begin;
-        if (chunk_row_count) chunk_row_count[k] = p.chunks[k].count;
-        if (chunk_diag) chunk_diag[k] = p.chunks[k].diag;
-        if (chunk_col) chunk_col[k] = p.chunks[k].col;
+    const int32_t nc = p.lay.n_chunks;
+    const int32_t rpc = p.lay.rows_per_chunk;
+    for (int32_t o = 0; o < B; ++o) {  // chunks of the samples in longest-first order
+        const int32_t i = p.order[o];
+        const SampleDesc &d = p.desc[i];
+        const int64_t rows = (int64_t)d.T * (d.U + 1);
+        const int32_t n = (int32_t)((rows + rpc - 1) / rpc);
+        for (int32_t j = 0; j < n; ++j) {
+            const int32_t k = d.chunk0 + j;
+            if (k >= cap) break;
+            const ChunkDesc c = make_chunk(d, i, j, rpc);
+            if (chunk_sample) chunk_sample[k] = c.sample;
+            if (chunk_row_begin) chunk_row_begin[k] = c.row_begin;
+            if (chunk_row_count) chunk_row_count[k] = c.count;
+            if (chunk_diag) chunk_diag[k] = c.diag;
+            if (chunk_col) chunk_col[k] = c.col;
+        }
     }
     if (n_chunks) *n_chunks = nc;
     return RNNT_SUCCESS;
@@ -377,21 +409,21 @@ rnnt_status rnnt_plan_describe(int32_t B, int32_t V, rnnt_dtype dtype, const int
 namespace rnnt {
 namespace {
 
-// The loss and gradient for the packed layout (pad off, N rows) or the
-// padded (B, max_T, max_U1, V) layout (pad on, N ignored).
-rnnt_status loss_impl(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V, const int32_t *targets, int32_t S,
-                      const int32_t *logit_lengths, const int32_t *target_lengths, int32_t B, int64_t blank,
-                      float clamp, float fastemit_lambda, int fused_log_softmax, rnnt_reduction reduction,
-                      float *loss, float *loss_reduced, void *grad, void *workspace, size_t workspace_bytes,
-                      hipStream_t stream, const Padding &pad) {
-    const int es = esize_of(dtype);
+// Host checks of one call, before anything is enqueued; `aligned16` tells
+// whether the rows can be moved in 16-byte vectors.
+rnnt_status check_call(const void *logits, int es, int64_t N, int32_t V, const int32_t *targets, int32_t S,
+                       const int32_t *logit_lengths, const int32_t *target_lengths, int32_t B, int64_t blank,
+                       float fastemit_lambda, rnnt_reduction reduction, const float *loss, const void *grad,
+                       const Padding &pad, bool &aligned16) {
     if (!es || V < 1 || B < 1) return RNNT_INVALID_VALUE;
     if (pad.on() ? (pad.max_U1 < 1) : (N < 0)) return RNNT_INVALID_VALUE;
     if (reduction != RNNT_REDUCTION_NONE && reduction != RNNT_REDUCTION_MEAN && reduction != RNNT_REDUCTION_SUM)
         return RNNT_INVALID_VALUE;
     if (blank < -(int64_t)V || blank > (int64_t)V - 1) return RNNT_INVALID_VALUE;
     if (!(fastemit_lambda >= 0.0f) || std::isinf(fastemit_lambda)) return RNNT_INVALID_VALUE;
-    if (!logit_lengths || !target_lengths || !loss || !workspace) return RNNT_INVALID_VALUE;
+    if (!logit_lengths || !target_lengths || !loss) return RNNT_INVALID_VALUE;
+    rnnt_status st = check_lengths(B, V, logit_lengths, target_lengths);
+    if (st != RNNT_SUCCESS) return st;
     const int64_t rows = pad.on() ? (int64_t)B * pad.max_T * pad.max_U1 : N;
     if (rows > 0 && !logits) return RNNT_INVALID_VALUE;
     int32_t maxU = 0;
@@ -400,21 +432,14 @@ rnnt_status loss_impl(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V
     if (S < 0) return RNNT_INVALID_VALUE;
     const size_t bytes = (size_t)rows * (size_t)V * (size_t)es;
     if (grad && grad != logits && bytes > 0 && ranges_overlap(grad, bytes, logits, bytes)) return RNNT_INVALID_VALUE;
-    const bool aligned16 = ((int64_t)V * es) % 16 == 0 && ((uintptr_t)logits % 16 == 0) &&
-                           (!grad || (uintptr_t)grad % 16 == 0);
-    std::shared_ptr<const PlanEntry> e;
-    rnnt_status st = get_plan(B, V, pad.on() ? -1 : N, es, logit_lengths, target_lengths, e, pad);
-    if (st != RNNT_SUCCESS) return st;
-    const Plan &plan = e->plan;
-    if (workspace_bytes < plan.lay.total) return RNNT_WORKSPACE_TOO_SMALL;
-    if ((uintptr_t)workspace % kAlign != 0) return RNNT_INVALID_VALUE;
+    aligned16 = ((int64_t)V * es) % 16 == 0 && ((uintptr_t)logits % 16 == 0) && (!grad || (uintptr_t)grad % 16 == 0);
+    return RNNT_SUCCESS;
+}
 
-    const RowGeom geom = row_geometry(V, es, aligned16);
-    if (!e->args) {
-        st = upload(workspace, e->packed, stream);
-        if (st != RNNT_SUCCESS) return st;
-    }
-
+LaunchArgs launch_args(const void *logits, int es, int64_t rows, int32_t V, const int32_t *targets, int32_t S,
+                       int32_t B, int64_t blank, float clamp, float fastemit_lambda, int fused_log_softmax,
+                       rnnt_reduction reduction, float *loss, float *loss_reduced, void *grad, void *ws,
+                       const WorkspaceLayout &lay, int32_t max_U1, bool aligned16) {
     LaunchArgs a{};
     a.logits = logits;
     a.grad = grad;
@@ -432,24 +457,64 @@ rnnt_status loss_impl(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V
     a.loss = loss;
     a.loss_reduced = loss_reduced;
     a.reduction = reduction;
-    a.ws = static_cast<uint8_t *>(workspace);
-    a.lay = plan.lay;
-    a.geom = geom;
-    a.max_U1 = plan.max_U1;
+    a.ws = static_cast<uint8_t *>(ws);
+    a.lay = lay;
+    a.geom = row_geometry(V, es, aligned16);
+    a.max_U1 = max_U1;
     a.aligned16 = aligned16;
+    a.status_out = nullptr;
+    return a;
+}
 
-    if (launch_plan(a, e->args.get(), stream) != hipSuccess) return RNNT_EXECUTION_FAILED;
-    if (plan.lay.n_chunks > 0 && timed(0, stream, [&] { return launch_rowstats(a, stream); }) != hipSuccess)
+// The kernels of one call, in order, on `stream`: the chunk table (and, with
+// `pa`, the descriptors it carries as kernel arguments), row statistics, the
+// recursions, the gradient (unless score-only), the padding rows' zeros, the
+// reduction.  `timing`: bracket the passes with the bench's timing events.
+rnnt_status enqueue_path(const LaunchArgs &a, const PlanArgs *pa, const Padding &pad, bool timing,
+                         hipStream_t stream) {
+    auto run = [&](int k, auto &&fn) { return timing ? timed(k, stream, fn) : fn(); };
+    if (launch_plan(a, pa, stream) != hipSuccess) return RNNT_EXECUTION_FAILED;
+    if (a.lay.n_chunks > 0 && run(0, [&] { return launch_rowstats(a, stream); }) != hipSuccess)
         return RNNT_EXECUTION_FAILED;
-    if (timed(1, stream, [&] { return launch_alpha_beta(a, stream); }) != hipSuccess) return RNNT_EXECUTION_FAILED;
-    if (grad && plan.lay.n_chunks > 0 && timed(2, stream, [&] { return launch_grad(a, stream); }) != hipSuccess)
+    if (run(1, [&] { return launch_alpha_beta(a, stream); }) != hipSuccess) return RNNT_EXECUTION_FAILED;
+    if (a.grad && a.lay.n_chunks > 0 && run(2, [&] { return launch_grad(a, stream); }) != hipSuccess)
         return RNNT_EXECUTION_FAILED;
-    if (grad && pad.on() &&
-        launch_zero_padding(grad, es, V, B, pad.max_T, pad.max_U1, a.ws, plan.lay, geom, stream) != hipSuccess)
+    if (a.grad && pad.on() &&
+        launch_zero_padding(a.grad, a.esize, a.V, a.B, pad.max_T, pad.max_U1, a.ws, a.lay, a.geom, stream) !=
+            hipSuccess)
         return RNNT_EXECUTION_FAILED;
-    if (timed(3, stream, [&] { return launch_reduce(a, stream); }) != hipSuccess)
-        return RNNT_EXECUTION_FAILED;
+    if (run(3, [&] { return launch_reduce(a, stream); }) != hipSuccess) return RNNT_EXECUTION_FAILED;
     return RNNT_SUCCESS;
+}
+
+// The loss and gradient for the packed layout (pad off, N rows) or the
+// padded (B, max_T, max_U1, V) layout (pad on, N ignored).
+rnnt_status loss_impl(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V, const int32_t *targets, int32_t S,
+                      const int32_t *logit_lengths, const int32_t *target_lengths, int32_t B, int64_t blank,
+                      float clamp, float fastemit_lambda, int fused_log_softmax, rnnt_reduction reduction,
+                      float *loss, float *loss_reduced, void *grad, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream, const Padding &pad) {
+    const int es = esize_of(dtype);
+    bool aligned16 = false;
+    rnnt_status st = check_call(logits, es, N, V, targets, S, logit_lengths, target_lengths, B, blank,
+                                fastemit_lambda, reduction, loss, grad, pad, aligned16);
+    if (st != RNNT_SUCCESS) return st;
+    if (!workspace) return RNNT_INVALID_VALUE;
+    std::shared_ptr<const PlanEntry> e;
+    st = get_plan(B, V, pad.on() ? -1 : N, es, logit_lengths, target_lengths, e, pad);
+    if (st != RNNT_SUCCESS) return st;
+    const Plan &plan = e->plan;
+    if (workspace_bytes < plan.lay.total) return RNNT_WORKSPACE_TOO_SMALL;
+    if ((uintptr_t)workspace % kAlign != 0) return RNNT_INVALID_VALUE;
+    if (!e->args) {
+        st = upload(workspace, e->packed, stream);
+        if (st != RNNT_SUCCESS) return st;
+    }
+    const int64_t rows = pad.on() ? (int64_t)B * pad.max_T * pad.max_U1 : N;
+    const LaunchArgs a = launch_args(logits, es, rows, V, targets, S, B, blank, clamp, fastemit_lambda,
+                                     fused_log_softmax, reduction, loss, loss_reduced, grad, workspace, plan.lay,
+                                     plan.max_U1, aligned16);
+    return enqueue_path(a, e->args.get(), pad, true, stream);
 }
 
 // ------------------------------------------------- multi-blank transducer
@@ -671,6 +736,37 @@ rnnt_status rnnt_loss_fused(const void *logits, rnnt_dtype dtype, int64_t N, int
     return loss_impl(logits, dtype, N, V, targets, S, logit_lengths, target_lengths, B, blank, clamp,
                      fastemit_lambda, fused_log_softmax, reduction, loss, loss_reduced, grad, workspace, workspace_bytes,
                      static_cast<hipStream_t>(stream), Padding());
+}
+
+rnnt_status rnnt_loss_fused_noalloc(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V,
+                                    const int32_t *targets, int32_t S, const int32_t *logit_lengths,
+                                    const int32_t *target_lengths, int32_t B, int64_t blank, float clamp,
+                                    float fastemit_lambda, int fused_log_softmax, rnnt_reduction reduction,
+                                    float *loss, float *loss_reduced, void *grad, uint32_t *dev_status,
+                                    rnnt_stream_t stream_) {
+    // Everything below lives on the stack or in the device's fixed scratch:
+    // no device, pinned or host heap allocation, no plan cache, no timing
+    // events.  The schedule travels as kernel arguments, hence B <= 64.
+    const hipStream_t stream = static_cast<hipStream_t>(stream_);
+    const int es = esize_of(dtype);
+    bool aligned16 = false;
+    rnnt_status st = check_call(logits, es, N, V, targets, S, logit_lengths, target_lengths, B, blank,
+                                fastemit_lambda, reduction, loss, grad, Padding(), aligned16);
+    if (st != RNNT_SUCCESS) return st;
+    if (B > kArgSamples) return RNNT_INVALID_VALUE;
+    PlanArgs pa{};
+    pa.B = B;
+    WorkspaceLayout lay{};
+    int32_t max_U1 = 1;
+    st = plan_into(B, V, N, es, logit_lengths, target_lengths, Padding(), pa.desc, pa.order, lay, max_U1);
+    if (st != RNNT_SUCCESS) return st;
+    if (lay.total > kScratchBytes) return RNNT_WORKSPACE_TOO_SMALL;
+    void *ws = nullptr;
+    if (scratch_address(&ws) != hipSuccess) return RNNT_MEMOPS_FAILED;
+    LaunchArgs a = launch_args(logits, es, N, V, targets, S, B, blank, clamp, fastemit_lambda, fused_log_softmax,
+                               reduction, loss, loss_reduced, grad, ws, lay, max_U1, aligned16);
+    a.status_out = dev_status;
+    return enqueue_path(a, &pa, Padding(), false, stream);
 }
 
 rnnt_status rnnt_loss_padded_workspace_size(int32_t B, int32_t V, int32_t max_T, int32_t max_U1, rnnt_dtype dtype,

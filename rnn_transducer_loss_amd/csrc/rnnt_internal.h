@@ -156,6 +156,7 @@ struct LaunchArgs {
     RowGeom geom;
     int max_U1;          // max_i (U_i + 1)
     bool aligned16;
+    uint32_t *status_out;  // device; if set, the reduction kernel copies the final status word there
 };
 
 // Batches of up to kArgSamples samples pass their descriptors and order to
@@ -182,6 +183,13 @@ hipError_t launch_grad_scale(void *grad, int esize, int V, int64_t N, int B, con
 // Padded layout: zero the gradient rows outside every sample's lattice.
 hipError_t launch_zero_padding(void *grad, int esize, int V, int B, int max_T, int max_U1, const uint8_t *ws,
                                const WorkspaceLayout &lay, const RowGeom &geom, hipStream_t stream);
+
+// The fixed device scratch used as the workspace of rnnt_loss_fused_noalloc:
+// its size, and its address on the current device (hipGetSymbolAddress,
+// taken once per device and kept).
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+static_assert(kScratchBytes == RNNT_NOALLOC_SCRATCH_BYTES, "the header states the scratch size");
+hipError_t scratch_address(void **ptr);
 
 // Largest lattice width (U+1) the alpha/beta kernel supports.
 constexpr int kMaxU1 = 1024;

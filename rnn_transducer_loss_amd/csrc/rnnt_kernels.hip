@@ -41,6 +41,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "rnnt_internal.h"
@@ -1245,9 +1246,12 @@ __global__ __launch_bounds__(256) void k_grad_narrow(const T *logits, T *grad, R
 
 // --------------------------------------------------------------- reduction
 // Cross-checks the two sweeps' log2 P(y|x) of every sample, then (out
-// non-null) reduces the per-sample losses: sum, or mean over B.
+// non-null) reduces the per-sample losses: sum, or mean over B.  With
+// status_out set, the final status word (every earlier kernel's bits and
+// this one's) is copied there.
 __global__ __launch_bounds__(64) void k_reduce(const float *__restrict__ loss, const double *__restrict__ log2z,
-                                               int B, int mean, float *__restrict__ out, uint32_t *status) {
+                                               int B, int mean, float *__restrict__ out, uint32_t *status,
+                                               uint32_t *status_out) {
     double s = 0.0;
     bool agree = true;
     for (int i = threadIdx.x; i < B; i += 64) {
@@ -1256,7 +1260,11 @@ __global__ __launch_bounds__(64) void k_reduce(const float *__restrict__ loss, c
         const double la = -log2z[B + i] * kLn2D;
         agree = agree && ((la == lb) || (fabs(la - lb) <= 1e-4 * fmax(1.0, fabs(lb))));
     }
-    if (__any(!agree) && threadIdx.x == 0) atomicOr(status, (uint32_t)RNNT_DEV_LOSS_MISMATCH);
+    const uint32_t bit = __any(!agree) ? (uint32_t)RNNT_DEV_LOSS_MISMATCH : 0u;
+    if (threadIdx.x == 0) {
+        const uint32_t word = atomicOr(status, bit) | bit;
+        if (status_out) *status_out = word;
+    }
     if (!out) return;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
@@ -1533,7 +1541,7 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
 hipError_t launch_reduce(const LaunchArgs &a, hipStream_t stream) {
     float *out = (a.reduction != RNNT_REDUCTION_NONE) ? a.loss_reduced : nullptr;
     hipLaunchKernelGGL(k_reduce, dim3(1), dim3(64), 0, stream, a.loss, WS(const double *, log2z), a.B,
-                       a.reduction == RNNT_REDUCTION_MEAN, out, WS(uint32_t *, status));
+                       a.reduction == RNNT_REDUCTION_MEAN, out, WS(uint32_t *, status), a.status_out);
     return hipGetLastError();
 }
 
@@ -2491,10 +2499,43 @@ hipError_t launch_mb_grad(const MbArgs &a, hipStream_t stream) {
 hipError_t launch_mb_reduce(const MbArgs &a, hipStream_t stream) {
     float *out = (a.reduction != RNNT_REDUCTION_NONE) ? a.loss_reduced : nullptr;
     hipLaunchKernelGGL(k_reduce, dim3(1), dim3(64), 0, stream, a.loss, MBWS(const double *, log2z), a.B,
-                       a.reduction == RNNT_REDUCTION_MEAN, out, MBWS(uint32_t *, status));
+                       a.reduction == RNNT_REDUCTION_MEAN, out, MBWS(uint32_t *, status), nullptr);
     return hipGetLastError();
 }
 
 #undef MBWS
+
+}  // namespace rnnt
+
+// ========================================= scratch of the allocation-free call
+// rnnt_loss_fused_noalloc takes its workspace from this fixed array instead of
+// a caller allocation, for callers that cannot allocate device memory.  Each
+// device that loads the library holds its own copy until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory: the
+// device address comes from hipGetSymbolAddress, once per device with that
+// device current, and only that address is ever passed to a kernel.
+static __device__ __align__(256) uint8_t scratch[rnnt::kScratchBytes];
+
+namespace rnnt {
+
+hipError_t scratch_address(void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 }  // namespace rnnt

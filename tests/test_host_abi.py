@@ -275,3 +275,27 @@ def test_multiblank_padded_sizes_and_limits():
     with pytest.raises(ValueError):
         _lib.loss_multiblank_padded(0x100000, 0, 6, 5, 32, 0x200000, 5, T, U, -1, [30], [2], 0.0, -1.0, 0.0, True,
                                     "sum", 0x300000, 0x400000, 0x500000, 0x600000, 1 << 20, 0)
+
+
+def test_noalloc_refusals_before_any_device_work():
+    """rnnt_loss_fused_noalloc refuses on the host, before enqueuing anything: more than 64 samples (its schedule
+    travels as kernel arguments), and a batch whose workspace exceeds the fixed scratch of 128 MiB.  The device
+    pointers are never dereferenced on these paths."""
+    T = np.full(65, 3, np.int32)
+    U = np.full(65, 1, np.int32)
+    with pytest.raises(ValueError):
+        _lib.loss_fused_noalloc(0x100000, _lib.RNNT_F32, int((T * (U + 1)).sum()), 8, 0x200000, 1, T, U, -1, -1.0,
+                                True, "sum", 0x300000, 0x400000, 0x500000, 0, 0)
+    # one lattice of 20000 x 1001 nodes: ~40 bytes of workspace per node, far beyond 128 MiB
+    T1 = np.array([20000], np.int32)
+    U1 = np.array([1000], np.int32)
+    need = _lib.workspace_size(1, 8, 20000 * 1001, _lib.RNNT_F32, T1, U1)
+    assert need > _lib.NOALLOC_SCRATCH_BYTES
+    with pytest.raises(ValueError, match="workspace too small"):
+        _lib.loss_fused_noalloc(1 << 40, _lib.RNNT_F32, 20000 * 1001, 8, 0x200000, 1000, T1, U1, -1, -1.0, True,
+                                "sum", 0x300000, 0x400000, 2 << 40, 0, 0)
+    # the skewed workload's batch (the largest of the named ones, 64 samples) fits
+    import workloads
+    Ts, Us = workloads.lengths("skewed")[:2]
+    assert _lib.workspace_size(len(Ts), 2048, int((Ts.astype(np.int64) * (Us + 1)).sum()), _lib.RNNT_F16, Ts,
+                               Us) <= _lib.NOALLOC_SCRATCH_BYTES
