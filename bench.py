@@ -8,15 +8,19 @@ outputs and workspace are resident in HBM before the timed region starts.
 ``--workload multiblank`` times ``rnnt_multiblank_loss`` (big blanks of 2, 4
 and 8 frames on the bpe shapes) the same way.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload bpe]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload half]
 
-Prints one JSON line.  ``value`` is packed logits elements per second
-(N*V per step / time per step); the line also carries the effective HBM
-bandwidth of the whole step, the roofline of the dominant kernel (its
-algorithmic bytes per step over its device time per step, measured with HIP
-events around each of its launches on the stream the launch runs on; a step
-makes one or two launches of each pass) and the fp64 CPU oracle timed on a
-bounded sample of the same batch on this host's cores.
+The default workload is ``half``, the largest named batch (16 samples, V =
+4096, fp16 logits with fp32 arithmetic: 3.56e9 packed elements, 14.2 GB of
+one-read-one-write traffic per step).  Prints one JSON line.  ``value`` is
+packed logits elements per second (N*V per step / time per step); the line
+also carries the effective HBM bandwidth of the whole step, the roofline of
+the dominant kernel (its algorithmic bytes per step over its device time per
+step, measured with HIP events around each of its launches on the stream the
+launch runs on), the host time to schedule a batch whose plan is not cached,
+and the fp64 CPU oracle timed on a bounded sample of the same batch on every
+core available to this process, plus one-thread oracle rates on the tiny,
+char and bpe workloads.
 
 ``--copy-calibration`` instead runs a plain device-to-device copy of known
 size, so that rocprofv3's FETCH_SIZE / WRITE_SIZE can be scaled to bytes.
@@ -89,8 +93,25 @@ def committed_traffic(kernel: str, workload: str):
     return None
 
 
-def cpu_baseline(w, budget_s: float = 12.0, min_wall_s: float = 1.5, fastemit_lambda: float = 0.0):
-    """The fp64 oracle on this host's cores over a bounded set of the batch's samples.
+def host_cores() -> dict:
+    """The cores this process may run on (its affinity mask), the machine's count, and the cgroup CPU quota."""
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count() or 1
+    quota = None
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            q, period = f.read().split()[:2]
+            if q != "max":
+                quota = float(q) / float(period)
+    except (OSError, ValueError):
+        pass
+    return {"affinity": affinity, "machine": os.cpu_count(), "cgroup_quota": quota}
+
+
+def cpu_baseline(w, threads: int, budget_s: float = 12.0, min_wall_s: float = 1.5, fastemit_lambda: float = 0.0):
+    """The fp64 oracle with ``threads`` threads over a bounded set of the batch's samples.
 
     Samples go out one per thread in batch order until ``budget_s`` of wall time is spent; when the whole batch
     takes less than ``min_wall_s`` it is run again (whole passes) until that much time has passed, so the rate
@@ -100,15 +121,12 @@ def cpu_baseline(w, budget_s: float = 12.0, min_wall_s: float = 1.5, fastemit_la
     import numpy as np
     import oracle
 
-    try:
-        avail = len(os.sched_getaffinity(0))
-    except AttributeError:  # pragma: no cover
-        avail = os.cpu_count() or 1
-    threads = max(1, min(16, avail))
+    threads = max(1, int(threads))
     b = w.blank + w.V if w.blank < 0 else w.blank
     rows = (w.logit_lengths.astype(np.int64) * (w.target_lengths + 1))
-    # batch order, skipping samples whose fp64 gradient would exceed 1 GiB per thread
-    cand = [i for i in range(w.B) if rows[i] * w.V * 8 <= (1 << 30)]
+    # batch order, skipping samples whose fp64 gradient would exceed 4 GiB per thread (none of the named
+    # workloads has one: half's largest is ~2.9 GB)
+    cand = [i for i in range(w.B) if rows[i] * w.V * 8 <= (4 << 30)]
     host = {}
 
     def one(i):
@@ -150,6 +168,58 @@ def cpu_baseline(w, budget_s: float = 12.0, min_wall_s: float = 1.5, fastemit_la
                       f"fp64, one sample per thread, {elapsed:.2f} s wall"}
 
 
+def single_thread_oracle(names=("tiny", "char", "bpe"), budget_s: float = 4.0) -> dict:
+    """The fp64 oracle on one thread (loss and full gradient) on the small named workloads: the whole batch for
+    tiny and char, the samples in batch order until ``budget_s`` for bpe.  Elements/s and the sample timed."""
+    import oracle
+    import workloads
+    out = {}
+    for name in names:
+        w = workloads.make(name, device="cuda")
+        b = w.blank + w.V if w.blank < 0 else w.blank
+        done, n_samples, t = 0, 0, 0.0
+        passes = 0
+        while True:
+            for i in range(w.B):
+                x = w.logits[w.rows(i)].cpu().numpy()
+                T, U = int(w.logit_lengths[i]), int(w.target_lengths[i])
+                t0 = time.perf_counter()
+                oracle.sample(x, T, U, w.targets[i], b, w.fused, w.clamp, want_grad=True)
+                t += time.perf_counter() - t0
+                done += T * (U + 1) * w.V
+                n_samples += 1
+                if t >= budget_s:
+                    break
+            passes += 1
+            if t >= 0.5 or n_samples < w.B * passes:
+                break
+        out[name] = {"value": done / t, "unit": "elements/s", "threads": 1,
+                     "sample": f"{n_samples} sample(s) of the {name} batch in {passes} pass(es), "
+                               f"{done} packed elements, {t:.2f} s"}
+        del w
+    return out
+
+
+def host_schedule_us(rl, w, reps: int = 20) -> dict:
+    """Host time to validate and schedule a batch whose plan is not cached (the longest-first order, the
+    descriptors, the workspace layout), in microseconds: the median over ``reps`` workspace queries of this
+    batch's lengths, each after a query with other lengths that replaces the cached plan.  Also the host time
+    of one call whose plan is cached (validation and kernel launches)."""
+    import numpy as np
+    T, U = w.logit_lengths, w.target_lengths
+    T2 = T.copy()
+    T2[0] += 1
+    N2 = int((T2.astype(np.int64) * (U + 1)).sum())
+    code = rl._lib.RNNT_F16 if w.logits.dtype.itemsize == 2 else rl._lib.RNNT_F32
+    fresh = []
+    for _ in range(reps):
+        rl._lib.workspace_size(w.B, w.V, N2, code, T2, U)
+        t0 = time.perf_counter()
+        rl._lib.workspace_size(w.B, w.V, w.N, code, T, U)
+        fresh.append((time.perf_counter() - t0) * 1e6)
+    return {"fresh_plan_us": round(float(np.median(fresh)), 2)}
+
+
 def copy_calibration(steps: int):
     import torch
     n = 1 << 30
@@ -174,7 +244,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="bpe", choices=["tiny", "char", "bpe", "half", "skewed", "multiblank"])
+    ap.add_argument("--workload", default="half", choices=["tiny", "char", "bpe", "half", "skewed", "multiblank"])
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--fastemit-lambda", type=float, default=0.0,
                     help="FastEmit weight on the label-emission gradient (0: the plain loss)")
@@ -248,6 +318,17 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     print(f"bench: {ms:.4f} ms/step (host wall {wall_ms:.4f})", file=sys.stderr, flush=True)
 
+    # host side: the call's own host time with its plan cached (validation and launches, no synchronisation),
+    # then the scheduling of a batch whose plan is not cached
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    call_us = (time.perf_counter() - t0) * 1e6 / args.steps
+    torch.cuda.synchronize()
+    sched = None if multiblank else host_schedule_us(rl, w)
+    if sched is not None:
+        sched["cached_call_us"] = round(call_us, 2)
+
     # per-kernel timing: HIP events around each launch, on the stream the
     # launch runs on (a step makes one or two launches of each pass, see
     # launches_per_step); times are summed per step
@@ -276,8 +357,17 @@ def main():
     eff = ab["path"] / (ms * 1e-3) / 1e9
     cpu = None
     if not args.no_cpu_baseline:
-        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, fastemit_lambda=args.fastemit_lambda)
+        cores = host_cores()
+        # every core of the affinity mask, unless a cgroup quota allows fewer (then more threads only share them)
+        threads = cores["affinity"]
+        if cores["cgroup_quota"]:
+            threads = max(1, min(threads, int(cores["cgroup_quota"])))
+        print(f"bench: timing the CPU oracle on {threads} threads ({cores})", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, threads, fastemit_lambda=args.fastemit_lambda)
+        if cpu is not None:
+            cpu["host_cores"] = cores
+            print("bench: timing the CPU oracle on one thread (tiny, char, bpe)", file=sys.stderr, flush=True)
+            cpu["single_thread"] = single_thread_oracle()
 
     out = {
         "metric": METRIC,
@@ -290,7 +380,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32",   # the arithmetic of the row passes; the recursion accumulates in f64
+
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "V": w.V, "rows": w.N, "elements": w.N * w.V,
                    "io_dtype": "fp16" if esize(w.dtype) == 2 else "fp32", "fused_log_softmax": w.fused,
@@ -303,6 +394,7 @@ def main():
         "kernel_ms": {k: (round(v, 5) if v is not None else None) for k, v in per_kernel.items()},
         "launches_per_step": launches,
         "host_wall_ms_per_step": round(wall_ms, 4),
+        "host_schedule": sched,
         "device_flags": flags,
         "roofline": roofline,
         "cpu_baseline": cpu,
