@@ -61,18 +61,40 @@ extern "C" {
 
 typedef void *rnnt_stream_t; /* a hipStream_t */
 
+/*
+ * Each enum below carries two reserved enumerators at the ends of the int32
+ * range, so that every int32 value is a valid value of the type: a code the
+ * library does not know is refused with RNNT_INVALID_VALUE (or described as
+ * "unknown status") instead of being undefined in the C++ implementation.
+ */
+
 /* Element type of logits and grad (README parameter table: float32 / float16). */
-typedef enum { RNNT_F32 = 0, RNNT_F16 = 1 } rnnt_dtype;
+typedef enum {
+    RNNT_F32 = 0,
+    RNNT_F16 = 1,
+    RNNT_DTYPE_RESERVED_MIN_ = -0x7fffffff - 1,
+    RNNT_DTYPE_RESERVED_MAX_ = 0x7fffffff
+} rnnt_dtype;
 
 /* Reduction of the per-sample losses (README usage example). */
-typedef enum { RNNT_REDUCTION_NONE = 0, RNNT_REDUCTION_MEAN = 1, RNNT_REDUCTION_SUM = 2 } rnnt_reduction;
+typedef enum {
+    RNNT_REDUCTION_NONE = 0,
+    RNNT_REDUCTION_MEAN = 1,
+    RNNT_REDUCTION_SUM = 2,
+    RNNT_REDUCTION_RESERVED_MIN_ = -0x7fffffff - 1,
+    RNNT_REDUCTION_RESERVED_MAX_ = 0x7fffffff
+} rnnt_reduction;
 
+/* Return status of every entry point (the ESPnet GPURNNT page's RNNTStatus:
+ * success or a failure code; its RNNT_STATUS_INVALID_VALUE for bad inputs). */
 typedef enum {
     RNNT_SUCCESS = 0,
     RNNT_INVALID_VALUE = 1,       /* an argument violates the constraints below */
     RNNT_WORKSPACE_TOO_SMALL = 2, /* workspace_bytes below what _workspace_size reported */
     RNNT_MEMOPS_FAILED = 3,       /* a HIP copy or host staging allocation failed */
-    RNNT_EXECUTION_FAILED = 4     /* a kernel launch failed */
+    RNNT_EXECUTION_FAILED = 4,    /* a kernel launch failed */
+    RNNT_STATUS_RESERVED_MIN_ = -0x7fffffff - 1,
+    RNNT_STATUS_RESERVED_MAX_ = 0x7fffffff
 } rnnt_status;
 
 /* Bits of the device status word (read back by rnnt_loss_fused_check). */

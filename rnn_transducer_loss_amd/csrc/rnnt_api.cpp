@@ -355,6 +355,7 @@ const char *rnnt_status_string(rnnt_status s) {
     case RNNT_WORKSPACE_TOO_SMALL: return "workspace too small";
     case RNNT_MEMOPS_FAILED: return "HIP memory operation failed";
     case RNNT_EXECUTION_FAILED: return "kernel launch failed";
+    default: break;
     }
     return "unknown status";
 }
