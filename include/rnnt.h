@@ -18,8 +18,14 @@
  *   node (0,0) that emit blank to advance t and emit y_{u+1} to advance u, and
  *   end by emitting blank at (T_i-1, U_i) (warp-transducer build post,
  *   section 1.1; README "Value" section 2 gives the gradient of it).  The
- *   forward (alpha) and backward (beta) log-space recursions are both run and
- *   their two losses cross-checked (README "Value" section 3).
+ *   forward (alpha) and backward (beta) recursions are both run and their
+ *   two losses cross-checked (README "Value" section 3).  The README fixes
+ *   the log domain for stability; here the recursions carry fp64
+ *   probabilities rescaled by a power of two per block of anti-diagonals
+ *   (exact up to fp64 rounding while the nodes that carry alignment mass
+ *   stay in fp64's range, which a per-sample check verifies), and a sample
+ *   that leaves that range is recomputed in the log domain (see the
+ *   numerics note under rnnt_loss_fused).
  *
  *   The gradient is with respect to the packed input (logits, or the given
  *   log-probabilities when fused_log_softmax is 0).  With clamp > 0 every
@@ -371,11 +377,19 @@ rnnt_status rnnt_multiblank_grad_scale_padded(void *grad, rnnt_dtype dtype, int3
 /*
  * Synchronises `stream`, then copies into *dev_flags the device status word
  * (RNNT_DEV_* bits) of the most recent rnnt_loss_fused call that used
- * `workspace`; every rnnt_loss_fused call clears it when it starts.
+ * `workspace`; every rnnt_loss_fused call clears it when it starts.  The
+ * status codes follow the ESPnet GPURNNT page's RNNTStatus (success, or a
+ * failure such as RNNT_STATUS_INVALID_VALUE); the per-sample problems only
+ * the device can see (README "Value" section 3: the alpha and beta losses
+ * must agree; the build post's section 5.2: labels exclude blank) come back
+ * as these bits.  RNNT_INVALID_VALUE for a NULL workspace or dev_flags;
+ * RNNT_MEMOPS_FAILED if the copy or the synchronisation fails.
  */
 rnnt_status rnnt_loss_fused_check(void *workspace, rnnt_stream_t stream, uint32_t *dev_flags);
 
-/* Static English description of a status code. */
+/* Static English description of a status code (the ESPnet GPURNNT page's
+ * RNNTStatus codes as numbered above); "unknown status" for any other value.
+ * Never NULL; the string is owned by the library. */
 const char *rnnt_status_string(rnnt_status s);
 
 /*
