@@ -249,6 +249,9 @@ def main():
     ap.add_argument("--fastemit-lambda", type=float, default=0.0,
                     help="FastEmit weight on the label-emission gradient (0: the plain loss)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one captured call (a HIP graph) instead of eager calls: the same kernels "
+                         "without the per-call host work; batches of up to 64 samples, not the multi-blank path")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -304,6 +307,24 @@ def main():
     flags = rl.device_flags(ws)
     torch.cuda.synchronize()
 
+    run = step
+    if args.graph:
+        if multiblank or w.B > 64:
+            print("bench: --graph needs a plain batch of at most 64 samples", file=sys.stderr)
+            sys.exit(2)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        run = graph.replay
+
     # whole-step timing: K steps bracketed by synchronisation on both sides
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -311,7 +332,7 @@ def main():
     w0 = time.perf_counter()
     e0.record()
     for _ in range(args.steps):
-        step()
+        run()
     e1.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - w0) * 1e3 / args.steps
@@ -387,7 +408,8 @@ def main():
                    "io_dtype": "fp16" if esize(w.dtype) == 2 else "fp32", "fused_log_softmax": w.fused,
                    "reduction": w.reduction, "clamp": w.clamp, "fastemit_lambda": args.fastemit_lambda,
                    **({"big_blank_durations": list(w.big_blank_durations), "sigma": w.sigma} if multiblank else {}),
-                   "T_max": int(T.max()), "U_max": int(U.max()), "recursion_dtype": "f64"},
+                   "T_max": int(T.max()), "U_max": int(U.max()), "recursion_dtype": "f64",
+                   "launch": "hip_graph_replay" if args.graph else "eager"},
         "effective_GBps": round(eff, 1),
         "effective_frac_of_peak": round(eff / PEAK_HBM_GBPS, 4),
         "algorithmic_bytes_per_step": ab["path"],

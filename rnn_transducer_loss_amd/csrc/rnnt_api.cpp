@@ -469,8 +469,9 @@ LaunchArgs launch_args(const void *logits, int es, int64_t rows, int32_t V, cons
 
 // The kernels of one call, in order, on `stream`: the chunk table (and, with
 // `pa`, the descriptors it carries as kernel arguments), row statistics, the
-// recursions, the gradient (unless score-only), the padding rows' zeros, the
-// reduction.  `timing`: bracket the passes with the bench's timing events.
+// recursions and their check, the gradient with the loss reduction in its
+// first workgroup (score-only: the reduction alone), the padding rows' zeros.
+// `timing`: bracket the passes with the bench's timing events.
 rnnt_status enqueue_path(const LaunchArgs &a, const PlanArgs *pa, const Padding &pad, bool timing,
                          hipStream_t stream) {
     auto run = [&](int k, auto &&fn) { return timing ? timed(k, stream, fn) : fn(); };
@@ -484,7 +485,9 @@ rnnt_status enqueue_path(const LaunchArgs &a, const PlanArgs *pa, const Padding 
         launch_zero_padding(a.grad, a.esize, a.V, a.B, pad.max_T, pad.max_U1, a.ws, a.lay, a.geom, stream) !=
             hipSuccess)
         return RNNT_EXECUTION_FAILED;
-    if (run(3, [&] { return launch_reduce(a, stream); }) != hipSuccess) return RNNT_EXECUTION_FAILED;
+    // with a gradient pass its first workgroup has reduced the losses; without one, a launch of its own
+    if (!(a.grad && a.lay.n_chunks > 0) && run(3, [&] { return launch_reduce(a, stream); }) != hipSuccess)
+        return RNNT_EXECUTION_FAILED;
     return RNNT_SUCCESS;
 }
 

@@ -205,6 +205,11 @@ __device__ __forceinline__ float wave_sum_f(float v) {
     v += dpp_f<0x143, 0xc>(0.f, v);
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
+__device__ __forceinline__ double readlane_d(double v, int l) {
+    const int lo = __builtin_amdgcn_readlane(__double2loint(v), l);
+    const int hi = __builtin_amdgcn_readlane(__double2hiint(v), l);
+    return __hiloint2double(hi, lo);
+}
 // Maximum of non-negative values (floating-point exponent fields): lanes a
 // stage does not reach read 0, the identity, so each move folds into the
 // maximum instruction.
@@ -938,7 +943,7 @@ __device__ void run_sweep(const SampleDesc &d, bool backward, bool log_mode, con
 // sample run on different compute units and do not share one unit's vector
 // memory path.  The backward sweep writes the loss and log2 P(y|x) at
 // log2z[i], the forward sweep its own log2 P(y|x) at log2z[B + i]; the
-// reduction kernel compares the two.
+// reduction (reduce_losses) compares the two.
 __global__ __launch_bounds__(64) void k_alpha_beta(const SampleDesc *__restrict__ desc,
                                                    const int32_t *__restrict__ order, int B,
                                                    const int *__restrict__ mode, const float4 *__restrict__ node,
@@ -1007,6 +1012,33 @@ __global__ __launch_bounds__(64) void k_check_ab(const SampleDesc *__restrict__ 
     const double ls = log2_d(s) + (double)(ealpha[d.diag_off + ((n + 1) >> 3)] + ebeta[d.diag_off + ((nd - n) >> 3)]);
     const bool bad = !(lz > kNegInfD) || !(s > 0.0) || !(fabs(ls - lz) <= 4e-6);
     if (bad && lane == 0) atomicOr(&mode[d.index], kModeRerun);
+}
+
+// --------------------------------------------------------------- reduction
+// One wave: cross-checks the two sweeps' log2 P(y|x) of every sample
+// (README "Value" section 3), then (out non-null) reduces the per-sample
+// losses: sum, or mean over B, in a fixed order.  With status_out set, the
+// final status word (every earlier kernel's bits and this one's) is copied
+// there.  Run by the first workgroup of the gradient launch, or on its own
+// (k_reduce) when there is no gradient pass.
+__device__ void reduce_losses(const float *__restrict__ loss, const double *__restrict__ log2z, int B, int mean,
+                              float *__restrict__ out, uint32_t *status, uint32_t *status_out) {
+    double s = 0.0;
+    bool agree = true;
+    for (int i = threadIdx.x; i < B; i += 64) {
+        s += (double)loss[i];
+        const double lb = -log2z[i] * kLn2D;
+        const double la = -log2z[B + i] * kLn2D;
+        agree = agree && ((la == lb) || (fabs(la - lb) <= 1e-4 * fmax(1.0, fabs(lb))));
+    }
+    const uint32_t bit = __any(!agree) ? (uint32_t)RNNT_DEV_LOSS_MISMATCH : 0u;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+    if (threadIdx.x == 0) {
+        const uint32_t word = atomicOr(status, bit) | bit;
+        if (status_out) *status_out = word;
+        if (out) out[0] = (float)(mean ? s / (double)B : s);
+    }
 }
 
 // ------------------------------------------------------------ K3: gradient
@@ -1083,7 +1115,17 @@ __device__ __forceinline__ RowTerms row_terms(const SampleDesc &d, const SampleT
     return r;
 }
 
+// The reduction the gradient launch's first workgroup performs (on = 0: none).
+struct ReduceArgs {
+    const float *loss;
+    float *out;
+    uint32_t *status;
+    uint32_t *status_out;
+    int B, mean, on;
+};
+
 struct GradArgs {
+    ReduceArgs red;
     int V, blank, n_chunks, S;
     float clamp, scale, log2_scale;
     float fastemit, scale_y;  // FastEmit weight; scale * (1 + fastemit)
@@ -1107,10 +1149,10 @@ struct GradArgs {
         float scale_y, const int32_t *__restrict__ targets, const SampleDesc *__restrict__ desc,                \
         const ChunkDesc *__restrict__ chunks, const int *__restrict__ mode, const double *__restrict__ log2z,   \
         const float4 *__restrict__ node, const double *__restrict__ alpha, const double *__restrict__ beta,     \
-        const int *__restrict__ ealpha, const int *__restrict__ ebeta
+        const int *__restrict__ ealpha, const int *__restrict__ ebeta, ReduceArgs red
 #define RNNT_GRAD_ARGS(g)                                                                                    \
     g.V, g.blank, g.n_chunks, g.S, g.clamp, g.scale, g.log2_scale, g.fastemit, g.scale_y, g.targets, g.desc,   \
-        g.chunks, g.mode, g.log2z, g.node, g.alpha, g.beta, g.ealpha, g.ebeta
+        g.chunks, g.mode, g.log2z, g.node, g.alpha, g.beta, g.ealpha, g.ebeta, g.red
 
 __device__ __forceinline__ float clamp_to(float v, float cl, bool do_clamp) {
     return do_clamp ? fminf(fmaxf(v, -cl), cl) : v;
@@ -1170,6 +1212,8 @@ template <typename T, int NV, int SPLIT, bool FULL, bool FUSED, bool CLAMP>
 __global__ __launch_bounds__(64) void k_grad_rows(const T *logits, T *grad, int blocks_per_chunk,
                                                   int64_t block_base, RNNT_GRAD_PARAMS) {
     constexpr int VEC = Raw<T>::kVec;
+    if (red.on && blockIdx.x == 0)
+        reduce_losses(red.loss, log2z, red.B, red.mean, red.out, red.status, red.status_out);
     const int bpc = blocks_per_chunk;
     const int64_t b = block_base + blockIdx.x;
     const ChunkDesc c = chunks[n_chunks - 1 - (int)(b / bpc)];
@@ -1203,6 +1247,8 @@ __global__ __launch_bounds__(64) void k_grad_rows(const T *logits, T *grad, int 
 template <typename T, int VEC, int G, bool FUSED>
 __global__ __launch_bounds__(256) void k_grad_narrow(const T *logits, T *grad, RNNT_GRAD_PARAMS) {
     constexpr int RPW = 64 / G;
+    if (red.on && blockIdx.x == 0 && threadIdx.x < 64)
+        reduce_losses(red.loss, log2z, red.B, red.mean, red.out, red.status, red.status_out);
     const ChunkDesc c = chunks[n_chunks - 1 - blockIdx.x];
     const SampleDesc d = desc[c.sample];
     const SampleTerms st{log2z[d.index], mode[d.index] != 0};
@@ -1244,31 +1290,10 @@ __global__ __launch_bounds__(256) void k_grad_narrow(const T *logits, T *grad, R
     }
 }
 
-// --------------------------------------------------------------- reduction
-// Cross-checks the two sweeps' log2 P(y|x) of every sample, then (out
-// non-null) reduces the per-sample losses: sum, or mean over B.  With
-// status_out set, the final status word (every earlier kernel's bits and
-// this one's) is copied there.
 __global__ __launch_bounds__(64) void k_reduce(const float *__restrict__ loss, const double *__restrict__ log2z,
                                                int B, int mean, float *__restrict__ out, uint32_t *status,
                                                uint32_t *status_out) {
-    double s = 0.0;
-    bool agree = true;
-    for (int i = threadIdx.x; i < B; i += 64) {
-        s += (double)loss[i];
-        const double lb = -log2z[i] * kLn2D;
-        const double la = -log2z[B + i] * kLn2D;
-        agree = agree && ((la == lb) || (fabs(la - lb) <= 1e-4 * fmax(1.0, fabs(lb))));
-    }
-    const uint32_t bit = __any(!agree) ? (uint32_t)RNNT_DEV_LOSS_MISMATCH : 0u;
-    if (threadIdx.x == 0) {
-        const uint32_t word = atomicOr(status, bit) | bit;
-        if (status_out) *status_out = word;
-    }
-    if (!out) return;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-    if (threadIdx.x == 0) out[0] = (float)(mean ? s / (double)B : s);
+    reduce_losses(loss, log2z, B, mean, out, status, status_out);
 }
 
 // Upstream-gradient scaling of an already written gradient: each workgroup
@@ -1472,9 +1497,17 @@ hipError_t launch_alpha_beta(const LaunchArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// The gradient, and in its first workgroup the loss check and reduction.
 hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
     const dim3 grid(a.lay.n_chunks), block(256);
     GradArgs g;
+    g.red.loss = a.loss;
+    g.red.out = (a.reduction != RNNT_REDUCTION_NONE) ? a.loss_reduced : nullptr;
+    g.red.status = WS(uint32_t *, status);
+    g.red.status_out = a.status_out;
+    g.red.B = a.B;
+    g.red.mean = a.reduction == RNNT_REDUCTION_MEAN;
+    g.red.on = 1;
     g.V = a.V;
     g.blank = a.blank;
     g.n_chunks = a.lay.n_chunks;
@@ -1507,7 +1540,7 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
             constexpr int NVW = Tg::n / S;
             void (*kern)(const T *, T *, int, int64_t, int, int, int, int, float, float, float, float, float,
                          const int32_t *, const SampleDesc *, const ChunkDesc *, const int *, const double *,
-                         const float4 *, const double *, const double *, const int *, const int *);
+                         const float4 *, const double *, const double *, const int *, const int *, ReduceArgs);
             if (a.fused) {
                 if (cl) kern = fu ? k_grad_rows<T, NVW, S, true, true, true> : k_grad_rows<T, NVW, S, false, true, true>;
                 else kern = fu ? k_grad_rows<T, NVW, S, true, true, false> : k_grad_rows<T, NVW, S, false, true, false>;
@@ -1522,6 +1555,7 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
             for (int64_t base = 0; base < total; base += kMaxBlocks) {
                 const unsigned nb = (unsigned)std::min<int64_t>(kMaxBlocks, total - base);
                 hipLaunchKernelGGL(kern, dim3(nb), dim3(64), 0, stream, in, out, bpc, base, RNNT_GRAD_ARGS(g));
+                g.red.on = 0;  // the first launch's first workgroup reduces
             }
             return hipGetLastError();
         });
@@ -1644,11 +1678,6 @@ __device__ __forceinline__ int64_t xcd_block(int64_t b, int64_t per) {
     return (b & 7) * per + (b >> 3);
 }
 
-__device__ __forceinline__ double readlane_d(double v, int l) {
-    const int lo = __builtin_amdgcn_readlane(__double2loint(v), l);
-    const int hi = __builtin_amdgcn_readlane(__double2hiint(v), l);
-    return __hiloint2double(hi, lo);
-}
 
 // The 2 + nb weights of node (t,u): lane k < 2 + nb stores plane k's, `v`
 // its log-probability (less sigma).  Edges that leave the lattice are stored

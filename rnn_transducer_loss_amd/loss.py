@@ -45,6 +45,24 @@ def _prepare(logits: torch.Tensor, targets: torch.Tensor):
     return tg
 
 
+class _on_device:
+    """Makes ``dev`` the current device for the block, unless it already is (the common case costs nothing)."""
+    __slots__ = ("ctx",)
+
+    def __init__(self, dev: torch.device):
+        idx = dev.index if dev.index is not None else torch.cuda.current_device()
+        self.ctx = None if idx == torch.cuda.current_device() else torch.cuda.device(idx)
+
+    def __enter__(self):
+        if self.ctx is not None:
+            self.ctx.__enter__()
+
+    def __exit__(self, *exc):
+        if self.ctx is not None:
+            self.ctx.__exit__(*exc)
+        return False
+
+
 def workspace_bytes(logits: torch.Tensor, logit_lengths, target_lengths) -> int:
     T = _lib.host_i32(logit_lengths)
     U = _lib.host_i32(target_lengths)
@@ -82,11 +100,11 @@ def rnnt_loss_fused(logits: torch.Tensor, targets: torch.Tensor, logit_lengths, 
         if logits.shape[0] != B:
             raise ValueError("padded logits must have one (max_T, max_U+1, V) block per sample")
         max_T, max_U1, V = logits.shape[1], logits.shape[2], logits.shape[3]
-        need = _lib.workspace_size_padded(B, V, max_T, max_U1, code, T, U)
     else:
         N, V = logits.shape
-        need = _lib.workspace_size(B, V, N, code, T, U)
-    if workspace is None or workspace.numel() < need:
+    if workspace is None:  # a caller's workspace is checked by the library itself
+        need = (_lib.workspace_size_padded(B, V, max_T, max_U1, code, T, U) if padded
+                else _lib.workspace_size(B, V, N, code, T, U))
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     if loss is None:
         loss = torch.empty(B, dtype=torch.float32, device=dev)
@@ -101,7 +119,7 @@ def rnnt_loss_fused(logits: torch.Tensor, targets: torch.Tensor, logit_lengths, 
             raise ValueError("grad must match logits in shape and dtype and be contiguous")
     else:
         grad = None
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         tgp = tg.data_ptr() if tg.numel() else 0
         redp = loss_reduced.data_ptr() if reduction != "none" else 0
