@@ -244,7 +244,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="half", choices=["tiny", "char", "bpe", "half", "skewed", "multiblank"])
+    ap.add_argument("--workload", default="half", choices=["tiny", "char", "bpe", "half", "skewed", "multiblank", "vocab5k"])
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--fastemit-lambda", type=float, default=0.0,
                     help="FastEmit weight on the label-emission gradient (0: the plain loss)")

@@ -128,6 +128,8 @@ struct RowGeom {
     int rows_per_block_iter;
     int wide_nv;        // > 0: one row per wave, wide_nv vectors per lane
     bool wide_full;     // V is exactly 64 * wide_nv vectors (no tail lanes)
+    int stream_parts;   // > 0: rows wider than 16 KiB (16-byte vectors): the row pass streams each row in 4 KiB
+                        // segments, the gradient pass splits it over stream_parts waves of 4 KiB
 };
 
 RowGeom row_geometry(int V, int esize, bool aligned16);

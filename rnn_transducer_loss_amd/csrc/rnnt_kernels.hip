@@ -484,6 +484,84 @@ __global__ __launch_bounds__(256) void k_rowstats_wide(const T *__restrict__ log
     rowstats_wide_chunk<T, NV, FULL>(logits, V, blank, d, c, targets, S, node, prob, mode, status);
 }
 
+// ----------------------------------- K1 rowstats, rows wider than 16 KiB
+// One row per wave (four waves, a chunk's nodes in diagonal order), the row
+// walked in segments of 4 KiB (four 16-byte vectors per lane) with the next
+// segment's loads in flight.  Each lane keeps a running maximum of its
+// elements and the sum of exp(x - that maximum), rescaled when it grows; at
+// the end of the row the lanes' sums are rescaled to the row maximum and
+// added.  Every term is formed from x - maximum, as in the other row passes.
+template <typename T>
+__global__ __launch_bounds__(256) void k_rowstats_stream(const T *__restrict__ logits, int V, int blank,
+                                                         const SampleDesc *__restrict__ desc,
+                                                         const ChunkDesc *__restrict__ chunks,
+                                                         const int32_t *__restrict__ targets, int S,
+                                                         float4 *__restrict__ node, float2 *__restrict__ prob,
+                                                         int *__restrict__ mode, uint32_t *status) {
+    constexpr int VEC = Raw<T>::kVec;
+    constexpr int NS = 4;  // vectors per lane per segment
+    using Vec = typename Raw<T>::vec;
+    const ChunkDesc c = chunks[blockIdx.x];
+    const SampleDesc d = desc[c.sample];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nvec = V / VEC;
+    const int nseg = (nvec + 64 * NS - 1) / (64 * NS);
+    int n = c.diag, u = c.col;
+    advance_diag(n, u, wave, d.T, d.U);
+    for (int r = wave; r < c.count; r += 4) {
+        const T *p = logits + row_of(d, n - u, u) * (int64_t)V;
+        const int y = __builtin_amdgcn_readfirstlane(read_label(d, u, V, blank, targets, S, status));
+        const float hb = Elem<T>::load1(p + blank);
+        const float hy = (y >= 0) ? Elem<T>::load1(p + y) : 0.f;
+        auto load_seg = [&](int sg, Vec (&x)[NS]) {
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                const int vi = (sg * NS + i) * 64 + lane;
+                if (vi < nvec) x[i] = load_raw<T, true>(p + (int64_t)vi * VEC);
+            }
+        };
+        float m = kNegInf, s = 0.f;
+        auto take_seg = [&](int sg, const Vec (&x)[NS]) {
+            float sm = kNegInf;
+#pragma unroll
+            for (int i = 0; i < NS; ++i)
+                if ((sg * NS + i) * 64 + lane < nvec)
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) sm = fmaxf(sm, Raw<T>::get(x[i], e));
+            const float mn = fmaxf(m, sm);
+            const float mr = (mn == kNegInf) ? 0.f : mn;
+            float acc = s * exp2_fast((m - mr) * kLog2e);
+#pragma unroll
+            for (int i = 0; i < NS; ++i)
+                if ((sg * NS + i) * 64 + lane < nvec)
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) acc += exp2_fast((Raw<T>::get(x[i], e) - mr) * kLog2e);
+            s = acc;
+            m = mn;
+        };
+        Vec xa[NS], xb[NS];
+        load_seg(0, xa);
+        for (int sg = 0; sg < nseg; sg += 2) {
+            if (sg + 1 < nseg) load_seg(sg + 1, xb);
+            take_seg(sg, xa);
+            if (sg + 1 < nseg) {
+                if (sg + 2 < nseg) load_seg(sg + 2, xa);
+                take_seg(sg + 1, xb);
+            }
+        }
+        const float M = wave_max_f(m);
+        const bool dead = (M == kNegInf);
+        const float mr = dead ? 0.f : M;
+        const float ls2 = dead ? 0.f : log2_fast(wave_sum_f(s * exp2_fast((m - mr) * kLog2e)));
+        const float lpb = dead ? kNegInf : (hb - mr) - ls2 * kLn2;
+        const float lpy = (dead || y < 0) ? kNegInf : (hy - mr) - ls2 * kLn2;
+        emit_node(d, n - u, u, mr, ls2, lpb, lpy, node, prob, mode);
+        fill_diagonal_ends(d, n, u, lane, 64, node, prob);
+        advance_diag(n, u, 4, d.T, d.U);
+    }
+}
+
 // --------------------------------- K1 rowstats, G < 64 lanes per row (small V)
 // Rows in row order (several short rows per wave); each row's outputs go to
 // its skewed slot.
@@ -1200,7 +1278,8 @@ __device__ __forceinline__ void grad_row(typename Raw<T>::vec (&xc)[NV], T *dst,
 }
 
 // The gradient, one wave per workgroup and SPLIT workgroups per row (each NV
-// vectors per lane: rows of up to 4 KiB take one): each wave loads its part
+// vectors per lane: rows of up to 4 KiB take one; SPLIT = 0: split_rt
+// workgroups, for rows wider than 16 KiB): each wave loads its part
 // of the row, computes and stores it, and exits.  Many single-wave
 // workgroups of 4 KiB keep enough rows in flight without a prefetch ring
 // (and run faster than four-wave workgroups over four rows).  Workgroup b
@@ -1210,7 +1289,7 @@ __device__ __forceinline__ void grad_row(typename Raw<T>::vec (&xc)[NV], T *dst,
 // faster than the forward order for a write-only gradient, 0.5% otherwise).
 template <typename T, int NV, int SPLIT, bool FULL, bool FUSED, bool CLAMP>
 __global__ __launch_bounds__(64) void k_grad_rows(const T *logits, T *grad, int blocks_per_chunk,
-                                                  int64_t block_base, RNNT_GRAD_PARAMS) {
+                                                  int64_t block_base, int split_rt, RNNT_GRAD_PARAMS) {
     constexpr int VEC = Raw<T>::kVec;
     if (red.on && blockIdx.x == 0)
         reduce_losses(red.loss, log2z, red.B, red.mean, red.out, red.status, red.status_out);
@@ -1218,9 +1297,10 @@ __global__ __launch_bounds__(64) void k_grad_rows(const T *logits, T *grad, int 
     const int64_t b = block_base + blockIdx.x;
     const ChunkDesc c = chunks[n_chunks - 1 - (int)(b / bpc)];
     const int part = (int)(b % bpc);
-    const int r = part / SPLIT;
+    const int split = SPLIT > 0 ? SPLIT : split_rt;  // 0: rows of any width, split_rt waves each
+    const int r = part / split;
     if (r >= c.count) return;
-    const int i0 = (part % SPLIT) * NV;  // first vector number of this wave's part
+    const int i0 = (part % split) * NV;  // first vector number of this wave's part
     const SampleDesc d = desc[c.sample];
     const int lane = threadIdx.x & 63;
     const int nvec = V / VEC;
@@ -1415,12 +1495,15 @@ RowGeom row_geometry(int V, int esize, bool aligned16) {
     // most 16 of them per lane.
     g.wide_nv = 0;
     g.wide_full = false;
+    g.stream_parts = 0;
     if (aligned16 && G == 64 && nvec > 64) {
         int nv = 1;
         while (nv * 64 < nvec) nv <<= 1;
         if (nv <= 16) {
             g.wide_nv = nv;
             g.wide_full = (nvec == nv * 64);
+        } else {
+            g.stream_parts = (nvec + 255) / 256;  // 4 KiB parts
         }
     }
     return g;
@@ -1443,7 +1526,8 @@ hipError_t launch_plan(const LaunchArgs &a, const PlanArgs *pa, hipStream_t stre
 
 hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream) {
     const dim3 grid(a.lay.n_chunks), block(256);
-    const bool diag = a.geom.wide_nv > 0;  // the uploaded chunk table is in diagonal order
+    // one row per wave: the chunks are walked in diagonal order
+    const bool diag = a.geom.wide_nv > 0 || a.geom.stream_parts > 0;
     if (!a.fused) {
         auto go = [&](auto tag, auto dtag) {
             using T = decltype(tag);
@@ -1456,6 +1540,16 @@ hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream) {
         if (a.esize == 4)
             return diag ? go(float{}, std::true_type{}) : go(float{}, std::false_type{});
         return diag ? go(_Float16{}, std::true_type{}) : go(_Float16{}, std::false_type{});
+    }
+    if (a.geom.stream_parts > 0) {
+        auto go = [&](auto tag) {
+            using T = decltype(tag);
+            hipLaunchKernelGGL(k_rowstats_stream<T>, grid, block, 0, stream, static_cast<const T *>(a.logits), a.V,
+                               a.blank, WS(const SampleDesc *, desc), WS(const ChunkDesc *, chunks), a.targets, a.S,
+                               WS(float4 *, node), WS(float2 *, prob), WS(int *, mode), WS(uint32_t *, status));
+            return hipGetLastError();
+        };
+        return a.esize == 4 ? go(float{}) : go(_Float16{});
     }
     if (diag)
         return with_wide(a.esize, a.geom.wide_nv, [&](auto tag) {
@@ -1527,37 +1621,50 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
     g.beta = WS(const double *, beta);
     g.ealpha = WS(const int *, ealpha);
     g.ebeta = WS(const int *, ebeta);
+    // One wave per workgroup, SPLIT (0: split_rt) waves per row, NVW vectors per lane each.
+    auto rows = [&](auto ttag, auto nvw, auto spl, bool full, int split_rt) -> hipError_t {
+        using T = decltype(ttag);
+        constexpr int NVW = decltype(nvw)::value;
+        constexpr int SPLIT = decltype(spl)::value;
+        const T *in = static_cast<const T *>(a.logits);
+        T *out = static_cast<T *>(a.grad);
+        const bool cl = a.clamp > 0.f;
+        void (*kern)(const T *, T *, int, int64_t, int, int, int, int, int, float, float, float, float, float,
+                     const int32_t *, const SampleDesc *, const ChunkDesc *, const int *, const double *,
+                     const float4 *, const double *, const double *, const int *, const int *, ReduceArgs);
+        if (a.fused) {
+            if (cl) kern = full ? k_grad_rows<T, NVW, SPLIT, true, true, true> : k_grad_rows<T, NVW, SPLIT, false, true, true>;
+            else kern = full ? k_grad_rows<T, NVW, SPLIT, true, true, false> : k_grad_rows<T, NVW, SPLIT, false, true, false>;
+        } else {
+            if (cl) kern = full ? k_grad_rows<T, NVW, SPLIT, true, false, true> : k_grad_rows<T, NVW, SPLIT, false, false, true>;
+            else kern = full ? k_grad_rows<T, NVW, SPLIT, true, false, false> : k_grad_rows<T, NVW, SPLIT, false, false, false>;
+        }
+        // one launch per 2^24 workgroups, so no launch exceeds 32-bit work-item counts
+        const int bpc = a.lay.rows_per_chunk * (SPLIT > 0 ? SPLIT : split_rt);
+        const int64_t total = (int64_t)a.lay.n_chunks * bpc;
+        constexpr int64_t kMaxBlocks = (int64_t)1 << 24;
+        for (int64_t base = 0; base < total; base += kMaxBlocks) {
+            const unsigned nb = (unsigned)std::min<int64_t>(kMaxBlocks, total - base);
+            hipLaunchKernelGGL(kern, dim3(nb), dim3(64), 0, stream, in, out, bpc, base, split_rt, RNNT_GRAD_ARGS(g));
+            g.red.on = 0;  // the first launch's first workgroup reduces
+        }
+        return hipGetLastError();
+    };
+    if (a.geom.stream_parts > 0) {
+        using C4 = std::integral_constant<int, 4>;
+        using C0 = std::integral_constant<int, 0>;
+        return a.esize == 4 ? rows(float{}, C4{}, C0{}, false, a.geom.stream_parts)
+                            : rows(_Float16{}, C4{}, C0{}, false, a.geom.stream_parts);
+    }
     if (a.geom.wide_nv > 0)
         return with_wide(a.esize, a.geom.wide_nv, [&](auto tag) {
             using Tg = decltype(tag);
             using T = typename Tg::type;
-            const T *in = static_cast<const T *>(a.logits);
-            T *out = static_cast<T *>(a.grad);
-            const bool cl = a.clamp > 0.f;
-            const bool fu = a.geom.wide_full;
             // waves per row: rows of up to 4 KiB (four vectors per lane) take one
             constexpr int S = Tg::n > 4 ? Tg::n / 4 : 1;
             constexpr int NVW = Tg::n / S;
-            void (*kern)(const T *, T *, int, int64_t, int, int, int, int, float, float, float, float, float,
-                         const int32_t *, const SampleDesc *, const ChunkDesc *, const int *, const double *,
-                         const float4 *, const double *, const double *, const int *, const int *, ReduceArgs);
-            if (a.fused) {
-                if (cl) kern = fu ? k_grad_rows<T, NVW, S, true, true, true> : k_grad_rows<T, NVW, S, false, true, true>;
-                else kern = fu ? k_grad_rows<T, NVW, S, true, true, false> : k_grad_rows<T, NVW, S, false, true, false>;
-            } else {
-                if (cl) kern = fu ? k_grad_rows<T, NVW, S, true, false, true> : k_grad_rows<T, NVW, S, false, false, true>;
-                else kern = fu ? k_grad_rows<T, NVW, S, true, false, false> : k_grad_rows<T, NVW, S, false, false, false>;
-            }
-            // one launch per 2^24 workgroups, so no launch exceeds 32-bit work-item counts
-            const int bpc = a.lay.rows_per_chunk * S;
-            const int64_t total = (int64_t)a.lay.n_chunks * bpc;
-            constexpr int64_t kMaxBlocks = (int64_t)1 << 24;
-            for (int64_t base = 0; base < total; base += kMaxBlocks) {
-                const unsigned nb = (unsigned)std::min<int64_t>(kMaxBlocks, total - base);
-                hipLaunchKernelGGL(kern, dim3(nb), dim3(64), 0, stream, in, out, bpc, base, RNNT_GRAD_ARGS(g));
-                g.red.on = 0;  // the first launch's first workgroup reduces
-            }
-            return hipGetLastError();
+            return rows(T{}, std::integral_constant<int, NVW>{}, std::integral_constant<int, S>{},
+                        a.geom.wide_full, S);
         });
     return with_narrow(a.esize, a.geom.vec, a.geom.lanes_per_row, [&](auto tag) {
         using Tg = decltype(tag);

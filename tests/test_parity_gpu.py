@@ -270,7 +270,7 @@ def test_single_path_and_degenerate_lattices(rl, dtype):
     check_against_oracle(w, loss, grad, "sum")
 
 
-@pytest.mark.parametrize("V", [1, 2, 3, 5, 31, 64, 65, 100, 257, 1000, 1023, 2049])
+@pytest.mark.parametrize("V", [1, 2, 3, 5, 31, 64, 65, 100, 257, 1000, 1023, 2049, 5001])
 def test_vocab_sizes(rl, V):
     # V = 1 only admits U = 0; odd V exercises the scalar (unvectorised) row path
     Us = [0, 0] if V == 1 else [3, min(9, 5)]
@@ -289,6 +289,36 @@ def test_wide_rows_split_over_waves(rl, V, dtype, clamp):
     loss, red, grad, flags = run(rl, w)
     assert flags == 0
     check_against_oracle(w, loss, grad, "mean")
+
+
+@pytest.mark.parametrize("V,dtype,clamp,fused,lam", [
+    (5000, torch.float32, -1.0, True, 0.0),      # 20000-byte rows: five 4 KiB segments, the last partial
+    (8192, torch.float32, 0.05, True, 0.3),      # 32 KiB rows, clamp, FastEmit
+    (50000, torch.float32, -1.0, True, 0.0),     # 200 KB rows (the README's largest vocabulary)
+    (16384, torch.float16, -1.0, True, 0.0),     # fp16 rows of 32 KiB
+    (20000, torch.float16, 1.0, True, 0.1),
+    (12000, torch.float32, -1.0, False, 0.2),    # log-prob inputs: flows only
+])
+def test_rows_wider_than_16k(rl, V, dtype, clamp, fused, lam):
+    """Rows wider than the 16 KiB a wave holds in registers: the row pass streams each row in 4 KiB segments
+    (running maximum and rescaled sum per lane), the gradient pass splits it over one wave per 4 KiB."""
+    w = _custom([7, 5, 1], [6, 9, 3], V, dtype=dtype, std=2.0 if fused else 1.5, blank=-1, clamp=clamp,
+                fused=fused, prenormalise=not fused, reduction="mean", seed=V % 1000)
+    loss, red, grad, flags = run(rl, w, fastemit=lam)
+    assert flags == 0
+    check_against_oracle(w, loss, grad, "mean", fastemit=lam)
+    if fused and clamp <= 0:  # unclamped fused rows sum to zero
+        assert grad.double().sum(dim=1).abs().max().item() < (1e-6 if dtype == torch.float32 else 2e-2)
+
+
+def test_vocab5k_workload_full_size(rl):
+    """The vocab5k workload (4 samples, V = 5000: 20000-byte rows, the README's V = 5000 shape): every loss and,
+    in every sample, the corner rows and 200 random rows of the gradient."""
+    w = workloads.make("vocab5k", device="cuda")
+    loss, red, grad, flags = run(rl, w)
+    assert flags == 0
+    check_against_oracle(w, loss, grad, w.reduction, grad_rows=200)
+    _reduced_ok(w, loss, red, w.reduction)
 
 
 @pytest.mark.parametrize("U", [63, 64, 127, 128, 255, 256, 511, 512, 700, 767, 768, 1023])
@@ -488,7 +518,7 @@ def _offset_rows(w, offset, seed):
 
 
 @pytest.mark.parametrize("offset", [50.0, 100.0, 300.0, 1000.0, -1000.0, "random"])
-@pytest.mark.parametrize("case", ["tiny", "char", "bpe_shaped", "wide_fp32", "half_fp16"])
+@pytest.mark.parametrize("case", ["tiny", "char", "bpe_shaped", "wide_fp32", "half_fp16", "stream_fp32"])
 def test_fused_logit_offsets(rl, case, offset):
     """log_softmax is shift-invariant (README parameter table, fused_log_softmax; "Value" section 3), so a
     constant added to a row's logits must leave the fused path within the parity gates: fp32 loss 1e-5
@@ -501,6 +531,8 @@ def test_fused_logit_offsets(rl, case, offset):
         w = _custom([60, 37, 81], [20, 9, 31], 1024, std=2.0, blank=-1, reduction="mean", seed=31)
     elif case == "wide_fp32":
         w = _custom([9, 14], [6, 3], 4096, std=2.0, blank=-1, reduction="sum", seed=32)
+    elif case == "stream_fp32":
+        w = _custom([8, 11], [5, 4], 5000, std=2.0, blank=-1, reduction="sum", seed=34)
     else:
         w = _custom([30, 21], [8, 12], 4096, dtype=torch.float16, std=2.0, blank=-1, clamp=1.0,
                     reduction="mean", seed=33)

@@ -12,6 +12,11 @@ precision / skewed long-form):
     half     16   U{300..600}               U{50..150}                4096     fp16   N(0,2^2)    -1     1.0    yes    mean
     skewed   64   lognormal(ln 300, 0.6)    round(T/5*U(0.6,1.0))     2048     fp16   log_softmax(N(0,1.5^2)) -1 off no sum
                   clipped to [50, 1600]
+    vocab5k   4   U{800..1000}              U{150..200}               5000     fp32   N(0,2^2)    -1     off    yes    mean
+
+(vocab5k: rows of 20000 bytes, wider than the 16 KiB a wave holds in registers; the rnnt-loss-ascend
+README's "Performance data" shape B=16, T=1000, U=200, V=5000, with four samples so that the logits
+and the gradient, 16 GB each, fit beside each other on one GPU)
 
 plus one multi-blank workload, the bpe shapes with three big blanks (classes
 1022, 1021, 1020 of durations 2, 4, 8 frames) beside the standard blank 1023
@@ -36,8 +41,8 @@ from typing import List, Optional
 import numpy as np
 import torch
 
-NAMES = ("tiny", "char", "bpe", "half", "skewed", "multiblank")
-DEFAULT_SEEDS = {"tiny": 1, "char": 2, "bpe": 3, "half": 4, "skewed": 5, "multiblank": 6}
+NAMES = ("tiny", "char", "bpe", "half", "skewed", "multiblank", "vocab5k")
+DEFAULT_SEEDS = {"tiny": 1, "char": 2, "bpe": 3, "half": 4, "skewed": 5, "multiblank": 6, "vocab5k": 7}
 # big-blank classes, durations and sigma of the multi-blank workload
 MULTIBLANK = {"big_blank_ids": (1022, 1021, 1020), "big_blank_durations": (2, 4, 8), "sigma": 0.05}
 
@@ -148,6 +153,10 @@ def lengths(name: str, seed: Optional[int] = None):
         T = rng.integers(300, 601, size=16).astype(np.int32)
         U = rng.integers(50, 151, size=16).astype(np.int32)
         V, blank = 4096, -1
+    elif name == "vocab5k":
+        T = rng.integers(800, 1001, size=4).astype(np.int32)
+        U = rng.integers(150, 201, size=4).astype(np.int32)
+        V, blank = 5000, -1
     elif name == "skewed":
         T = np.clip(np.round(np.exp(rng.normal(np.log(300.0), 0.6, size=64))), 50, 1600).astype(np.int32)
         U = np.round(T / 5.0 * rng.uniform(0.6, 1.0, size=64)).astype(np.int32)
@@ -167,6 +176,7 @@ _PARAMS = {
     "half": (torch.float16, 2.0, 1.0, True, "mean", False),
     "skewed": (torch.float16, 1.5, -1.0, False, "sum", True),
     "multiblank": (torch.float32, 2.0, -1.0, True, "mean", False),
+    "vocab5k": (torch.float32, 2.0, -1.0, True, "mean", False),
 }
 
 
