@@ -126,10 +126,8 @@ struct RowGeom {
     int lanes_per_row;  // G: 1..64 lanes cooperate on one row (power of two)
     int vec;            // elements per vector access (1 when rows are not 16-byte aligned)
     int rows_per_block_iter;
-    int wide_nv;        // > 0: one row per wave, wide_nv vectors per lane
-    bool wide_full;     // V is exactly 64 * wide_nv vectors (no tail lanes)
-    int stream_parts;   // > 0: rows wider than 16 KiB (16-byte vectors): the row pass streams each row in 4 KiB
-                        // segments, the gradient pass splits it over stream_parts waves of 4 KiB
+    int stream_parts;   // > 0: rows of more than 1 KiB in 16-byte vectors: the row pass takes one row per wave
+                        // in 4 KiB segments, the gradient pass splits each row over stream_parts waves of 4 KiB
 };
 
 RowGeom row_geometry(int V, int esize, bool aligned16);

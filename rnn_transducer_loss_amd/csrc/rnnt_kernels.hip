@@ -385,109 +385,15 @@ __global__ __launch_bounds__(256) void k_plan(const SampleDesc *__restrict__ des
     if (j < n) chunks[d.chunk0 + j] = make_chunk(d, i, j, rpc);
 }
 
-// --------------------------------------------- K1 rowstats, one row per wave
-// Lane l holds elements (i*64 + l)*VEC .. +VEC-1 of a row, i < NV.  The
-// chunk's nodes are walked in diagonal order, so the per-node outputs of the
-// four waves land in consecutive slots, and each node's row is one
-// contiguous read, with non-temporal loads (ordinary loads made this pass
-// ~10% slower, and keeping the last rows cached for the gradient pass gained
-// nothing measurable).
-template <typename T, int NV, bool FULL>
-__device__ __forceinline__ void rowstats_wide_chunk(const T *__restrict__ logits, int V, int blank,
-                                                    const SampleDesc &d, const ChunkDesc &c,
-                                                    const int32_t *__restrict__ targets, int S,
-                                                    float4 *__restrict__ node, float2 *__restrict__ prob,
-                                                    int *__restrict__ mode, uint32_t *status) {
-    constexpr int VEC = Raw<T>::kVec;
-    using Vec = typename Raw<T>::vec;
-    const int lane = threadIdx.x & 63;
-    // wave-uniform, so per-row scalars stay in scalar registers
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int nvec = V / VEC;
-    auto load_row = [&](int n, int u, Vec (&x)[NV]) {
-        const T *p = logits + row_of(d, n - u, u) * (int64_t)V;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int vi = i * 64 + lane;
-            if (FULL || vi < nvec) x[i] = load_raw<T, true>(p + (int64_t)vi * VEC);
-        }
-    };
-    int r = wave;
-    if (r >= c.count) return;
-    int n = c.diag, u = c.col;
-    advance_diag(n, u, r, d.T, d.U);
-    int y = __builtin_amdgcn_readfirstlane(read_label(d, u, V, blank, targets, S, status));
-    auto elem = [&](int nn, int uu, int k) -> float {
-        return Elem<T>::load1(logits + row_of(d, nn - uu, uu) * (int64_t)V + k);
-    };
-    float hb = elem(n, u, blank);
-    float hy = (y >= 0) ? elem(n, u, y) : 0.f;
-    // One row: the next row's logits, its label and its blank and label
-    // logits (two wave-uniform loads, cheaper than selecting them out of the
-    // row's registers) are requested first, the logits into the next of
-    // three buffers used in turn, then this row is reduced.  With
-    // three buffers a buffer is reloaded two rows after the stores issued
-    // while it was current, so the loads never wait for those stores to
-    // release their registers, and every wait covers exactly the buffer about
-    // to be used.  The last row of the wave loads itself again (a cache hit)
-    // to keep the wait counts static.
-    auto row_step = [&](Vec (&xc)[NV], Vec (&xn)[NV]) -> bool {
-        const bool more = r + 4 < c.count;
-        int nn = n, un = u;
-        advance_diag(nn, un, 4, d.T, d.U);
-        if (more) load_row(nn, un, xn);
-        else load_row(n, u, xn);
-        const int yn = more ? __builtin_amdgcn_readfirstlane(read_label(d, un, V, blank, targets, S, status)) : -1;
-        const float hbn = more ? elem(nn, un, blank) : 0.f;
-        const float hyn = (yn >= 0) ? elem(nn, un, yn) : 0.f;
-        float m = row_max<T, NV, FULL>(xc, nvec);
-        m = wave_max_f(m);
-        const bool dead = (m == kNegInf);
-        const float mr = dead ? 0.f : m;
-        const float nm = -mr * kLog2e;
-        float s = 0.f;
-#pragma unroll
-        for (int i = 0; i < NV; ++i)
-            if (FULL || i * 64 + lane < nvec)
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) s += exp2_fast(fmaf(Raw<T>::get(xc[i], e), kLog2e, nm));
-        s = wave_sum_f(s);
-        // s >= 1 (the maximum contributes exp(0)); log P = (x - m) - ln s
-        const float ls2 = dead ? 0.f : log2_sum_shifted(s, mr, nm);
-        const float lpb = dead ? kNegInf : (hb - mr) - ls2 * kLn2;
-        const float lpy = (dead || y < 0) ? kNegInf : (hy - mr) - ls2 * kLn2;
-        emit_node(d, n - u, u, mr, ls2, lpb, lpy, node, prob, mode);
-        fill_diagonal_ends(d, n, u, lane, 64, node, prob);
-        n = nn;
-        u = un;
-        y = yn;
-        hb = hbn;
-        hy = hyn;
-        r += 4;
-        return more;
-    };
-    Vec x0[NV], x1[NV], x2[NV];
-    load_row(n, u, x0);
-    while (row_step(x0, x1) && row_step(x1, x2) && row_step(x2, x0)) {
-    }
-}
-
-template <typename T, int NV, bool FULL>
-__global__ __launch_bounds__(256) void k_rowstats_wide(const T *__restrict__ logits, int V, int blank,
-                                                       const SampleDesc *__restrict__ desc,
-                                                       const ChunkDesc *__restrict__ chunks,
-                                                       const int32_t *__restrict__ targets, int S,
-                                                       float4 *__restrict__ node, float2 *__restrict__ prob,
-                                                       int *__restrict__ mode, uint32_t *status) {
-    const ChunkDesc c = chunks[blockIdx.x];
-    const SampleDesc d = desc[c.sample];
-    rowstats_wide_chunk<T, NV, FULL>(logits, V, blank, d, c, targets, S, node, prob, mode, status);
-}
-
-// ----------------------------------- K1 rowstats, rows wider than 16 KiB
-// One row per wave (four waves, a chunk's nodes in diagonal order), the row
-// walked in segments of 4 KiB (four 16-byte vectors per lane) with the next
-// segment's loads in flight.  Each lane keeps a running maximum of its
+// ------------------------------------ K1 rowstats, rows wider than 1 KiB
+// One row per wave (four waves, a chunk's nodes in diagonal order, so the
+// four waves' per-node records land in consecutive slots), the row walked in
+// segments of 4 KiB (four 16-byte vectors per lane, non-temporal loads) with
+// the next segment's loads in flight.  Holding only two segments, a wave
+// needs few registers, so many waves (rows) are in flight per compute unit:
+// measured faster than holding whole rows in registers (three row buffers
+// of up to 16 vectors per lane) on 4 KiB and 8 KiB rows, and the only form
+// for rows beyond 16 KiB.  Each lane keeps a running maximum of its
 // elements and the sum of exp(x - that maximum), rescaled when it grows; at
 // the end of the row the lanes' sums are rescaled to the row maximum and
 // added.  Every term is formed from x - maximum, as in the other row passes.
@@ -1277,27 +1183,34 @@ __device__ __forceinline__ void grad_row(typename Raw<T>::vec (&xc)[NV], T *dst,
     }
 }
 
-// The gradient, one wave per workgroup and SPLIT workgroups per row (each NV
-// vectors per lane: rows of up to 4 KiB take one; SPLIT = 0: split_rt
-// workgroups, for rows wider than 16 KiB): each wave loads its part
+// The gradient, one wave per workgroup and `split` workgroups per row (SPLIT,
+// when the launch fixes it at compile time), each taking a 4 KiB part (four
+// 16-byte vectors per lane; the last part may be partial unless FULL): each
+// wave loads its part
 // of the row, computes and stores it, and exits.  Many single-wave
 // workgroups of 4 KiB keep enough rows in flight without a prefetch ring
 // (and run faster than four-wave workgroups over four rows).  Workgroup b
-// takes part (b % PB) % SPLIT of row (b % PB) / SPLIT of chunk n_chunks-1-b/PB
-// (PB = rows per chunk * SPLIT, row order), so the chunks run in the reverse of
+// takes part (b % PB) % split of row (b % PB) / split of chunk n_chunks-1-b/PB
+// (PB = rows per chunk * split, row order), so the chunks run in the reverse of
 // the row pass's order, which starts where that pass ended (measured 6%
 // faster than the forward order for a write-only gradient, 0.5% otherwise).
-template <typename T, int NV, int SPLIT, bool FULL, bool FUSED, bool CLAMP>
+// Forms, as measured on MI355X: fused rows take the masked form with the
+// split at run time (8 KiB fp16 rows: 2.19 ms against 2.30 ms unmasked);
+// log-prob inputs (a write-only pass) take the unmasked form, with the split
+// fixed when it is one (4 KiB rows: 0.995 ms against 1.016 at run time and
+// 1.045 masked).
+template <typename T, bool FUSED, bool CLAMP, int SPLIT, bool FULL>
 __global__ __launch_bounds__(64) void k_grad_rows(const T *logits, T *grad, int blocks_per_chunk,
                                                   int64_t block_base, int split_rt, RNNT_GRAD_PARAMS) {
     constexpr int VEC = Raw<T>::kVec;
+    constexpr int NV = 4;
     if (red.on && blockIdx.x == 0)
         reduce_losses(red.loss, log2z, red.B, red.mean, red.out, red.status, red.status_out);
     const int bpc = blocks_per_chunk;
     const int64_t b = block_base + blockIdx.x;
     const ChunkDesc c = chunks[n_chunks - 1 - (int)(b / bpc)];
     const int part = (int)(b % bpc);
-    const int split = SPLIT > 0 ? SPLIT : split_rt;  // 0: rows of any width, split_rt waves each
+    const int split = SPLIT > 0 ? SPLIT : split_rt;
     const int r = part / split;
     if (r >= c.count) return;
     const int i0 = (part % split) * NV;  // first vector number of this wave's part
@@ -1467,19 +1380,6 @@ template <typename Fn> hipError_t with_narrow(int esize, int vec, int G, Fn &&fn
 #undef RNNT_CASE_G
 }
 
-template <typename Fn> hipError_t with_wide(int esize, int nv, Fn &&fn) {
-#define RNNT_CASE_NV(T, VEC)                                  \
-    switch (nv) {                                             \
-    case 1: return fn(Tag<T, VEC, 1>{});                      \
-    case 2: return fn(Tag<T, VEC, 2>{});                      \
-    case 4: return fn(Tag<T, VEC, 4>{});                      \
-    case 8: return fn(Tag<T, VEC, 8>{});                      \
-    default: return fn(Tag<T, VEC, 16>{});                    \
-    }
-    if (esize == 4) { RNNT_CASE_NV(float, 4) }
-    RNNT_CASE_NV(_Float16, 8)
-#undef RNNT_CASE_NV
-}
 
 }  // namespace
 
@@ -1491,21 +1391,9 @@ RowGeom row_geometry(int V, int esize, bool aligned16) {
     while (G < 64 && G < nvec) G <<= 1;
     g.lanes_per_row = G;
     g.rows_per_block_iter = 4 * (64 / G);
-    // One row per wave with the row held in registers: 16-byte vectors and at
-    // most 16 of them per lane.
-    g.wide_nv = 0;
-    g.wide_full = false;
-    g.stream_parts = 0;
-    if (aligned16 && G == 64 && nvec > 64) {
-        int nv = 1;
-        while (nv * 64 < nvec) nv <<= 1;
-        if (nv <= 16) {
-            g.wide_nv = nv;
-            g.wide_full = (nvec == nv * 64);
-        } else {
-            g.stream_parts = (nvec + 255) / 256;  // 4 KiB parts
-        }
-    }
+    // Rows of more than 64 16-byte vectors (1 KiB): one row per wave in the
+    // row pass, one wave per 4 KiB part in the gradient pass.
+    g.stream_parts = (aligned16 && G == 64 && nvec > 64) ? (nvec + 255) / 256 : 0;
     return g;
 }
 
@@ -1527,7 +1415,7 @@ hipError_t launch_plan(const LaunchArgs &a, const PlanArgs *pa, hipStream_t stre
 hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream) {
     const dim3 grid(a.lay.n_chunks), block(256);
     // one row per wave: the chunks are walked in diagonal order
-    const bool diag = a.geom.wide_nv > 0 || a.geom.stream_parts > 0;
+    const bool diag = a.geom.stream_parts > 0;
     if (!a.fused) {
         auto go = [&](auto tag, auto dtag) {
             using T = decltype(tag);
@@ -1551,17 +1439,6 @@ hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream) {
         };
         return a.esize == 4 ? go(float{}) : go(_Float16{});
     }
-    if (diag)
-        return with_wide(a.esize, a.geom.wide_nv, [&](auto tag) {
-            using Tg = decltype(tag);
-            using T = typename Tg::type;
-            auto kern = a.geom.wide_full ? k_rowstats_wide<T, Tg::n, true> : k_rowstats_wide<T, Tg::n, false>;
-            hipLaunchKernelGGL(kern, grid, block, 0, stream, static_cast<const T *>(a.logits), a.V, a.blank,
-                               WS(const SampleDesc *, desc), WS(const ChunkDesc *, chunks),
-                               a.targets, a.S, WS(float4 *, node), WS(float2 *, prob), WS(int *, mode),
-                               WS(uint32_t *, status));
-            return hipGetLastError();
-        });
     return with_narrow(a.esize, a.geom.vec, a.geom.lanes_per_row, [&](auto tag) {
         using Tg = decltype(tag);
         using T = typename Tg::type;
@@ -1621,51 +1498,37 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
     g.beta = WS(const double *, beta);
     g.ealpha = WS(const int *, ealpha);
     g.ebeta = WS(const int *, ebeta);
-    // One wave per workgroup, SPLIT (0: split_rt) waves per row, NVW vectors per lane each.
-    auto rows = [&](auto ttag, auto nvw, auto spl, bool full, int split_rt) -> hipError_t {
-        using T = decltype(ttag);
-        constexpr int NVW = decltype(nvw)::value;
-        constexpr int SPLIT = decltype(spl)::value;
-        const T *in = static_cast<const T *>(a.logits);
-        T *out = static_cast<T *>(a.grad);
-        const bool cl = a.clamp > 0.f;
-        void (*kern)(const T *, T *, int, int64_t, int, int, int, int, int, float, float, float, float, float,
-                     const int32_t *, const SampleDesc *, const ChunkDesc *, const int *, const double *,
-                     const float4 *, const double *, const double *, const int *, const int *, ReduceArgs);
-        if (a.fused) {
-            if (cl) kern = full ? k_grad_rows<T, NVW, SPLIT, true, true, true> : k_grad_rows<T, NVW, SPLIT, false, true, true>;
-            else kern = full ? k_grad_rows<T, NVW, SPLIT, true, true, false> : k_grad_rows<T, NVW, SPLIT, false, true, false>;
-        } else {
-            if (cl) kern = full ? k_grad_rows<T, NVW, SPLIT, true, false, true> : k_grad_rows<T, NVW, SPLIT, false, false, true>;
-            else kern = full ? k_grad_rows<T, NVW, SPLIT, true, false, false> : k_grad_rows<T, NVW, SPLIT, false, false, false>;
-        }
-        // one launch per 2^24 workgroups, so no launch exceeds 32-bit work-item counts
-        const int bpc = a.lay.rows_per_chunk * (SPLIT > 0 ? SPLIT : split_rt);
-        const int64_t total = (int64_t)a.lay.n_chunks * bpc;
-        constexpr int64_t kMaxBlocks = (int64_t)1 << 24;
-        for (int64_t base = 0; base < total; base += kMaxBlocks) {
-            const unsigned nb = (unsigned)std::min<int64_t>(kMaxBlocks, total - base);
-            hipLaunchKernelGGL(kern, dim3(nb), dim3(64), 0, stream, in, out, bpc, base, split_rt, RNNT_GRAD_ARGS(g));
-            g.red.on = 0;  // the first launch's first workgroup reduces
-        }
-        return hipGetLastError();
-    };
+    // Rows of more than 1 KiB: one single-wave workgroup per 4 KiB part of a row.
     if (a.geom.stream_parts > 0) {
-        using C4 = std::integral_constant<int, 4>;
-        using C0 = std::integral_constant<int, 0>;
-        return a.esize == 4 ? rows(float{}, C4{}, C0{}, false, a.geom.stream_parts)
-                            : rows(_Float16{}, C4{}, C0{}, false, a.geom.stream_parts);
+        auto rows = [&](auto ttag) -> hipError_t {
+            using T = decltype(ttag);
+            const T *in = static_cast<const T *>(a.logits);
+            T *out = static_cast<T *>(a.grad);
+            const bool cl = a.clamp > 0.f;
+            void (*kern)(const T *, T *, int, int64_t, int, int, int, int, int, float, float, float, float, float,
+                         const int32_t *, const SampleDesc *, const ChunkDesc *, const int *, const double *,
+                         const float4 *, const double *, const double *, const int *, const int *, ReduceArgs);
+            const bool full = (int64_t)a.V * a.esize % 4096 == 0;  // every part a whole 4 KiB
+            if (a.fused) kern = cl ? k_grad_rows<T, true, true, 0, false> : k_grad_rows<T, true, false, 0, false>;
+            else if (full && a.geom.stream_parts == 1)
+                kern = cl ? k_grad_rows<T, false, true, 1, true> : k_grad_rows<T, false, false, 1, true>;
+            else if (full)
+                kern = cl ? k_grad_rows<T, false, true, 0, true> : k_grad_rows<T, false, false, 0, true>;
+            else kern = cl ? k_grad_rows<T, false, true, 0, false> : k_grad_rows<T, false, false, 0, false>;
+            // one launch per 2^24 workgroups, so no launch exceeds 32-bit work-item counts
+            const int split = a.geom.stream_parts;
+            const int bpc = a.lay.rows_per_chunk * split;
+            const int64_t total = (int64_t)a.lay.n_chunks * bpc;
+            constexpr int64_t kMaxBlocks = (int64_t)1 << 24;
+            for (int64_t base = 0; base < total; base += kMaxBlocks) {
+                const unsigned nb = (unsigned)std::min<int64_t>(kMaxBlocks, total - base);
+                hipLaunchKernelGGL(kern, dim3(nb), dim3(64), 0, stream, in, out, bpc, base, split, RNNT_GRAD_ARGS(g));
+                g.red.on = 0;  // the first launch's first workgroup reduces
+            }
+            return hipGetLastError();
+        };
+        return a.esize == 4 ? rows(float{}) : rows(_Float16{});
     }
-    if (a.geom.wide_nv > 0)
-        return with_wide(a.esize, a.geom.wide_nv, [&](auto tag) {
-            using Tg = decltype(tag);
-            using T = typename Tg::type;
-            // waves per row: rows of up to 4 KiB (four vectors per lane) take one
-            constexpr int S = Tg::n > 4 ? Tg::n / 4 : 1;
-            constexpr int NVW = Tg::n / S;
-            return rows(T{}, std::integral_constant<int, NVW>{}, std::integral_constant<int, S>{},
-                        a.geom.wide_full, S);
-        });
     return with_narrow(a.esize, a.geom.vec, a.geom.lanes_per_row, [&](auto tag) {
         using Tg = decltype(tag);
         using T = typename Tg::type;
