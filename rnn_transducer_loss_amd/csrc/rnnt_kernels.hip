@@ -386,19 +386,33 @@ __global__ __launch_bounds__(256) void k_plan(const SampleDesc *__restrict__ des
 }
 
 // ------------------------------------ K1 rowstats, rows wider than 1 KiB
-// One row per wave (four waves, a chunk's nodes in diagonal order, so the
-// four waves' per-node records land in consecutive slots), the row walked in
+// One row per wave (W waves per workgroup: eight for rows of up to 4 KiB,
+// sixteen above, each measured fastest there: 8 against 4 waves 2% faster
+// on 4 KiB and 8 KiB rows, 16 against 8 another 1.3% on 8 KiB and 2.4% on
+// 20 KB rows but 9% slower on 4 KiB ones; a chunk's nodes in diagonal order,
+// so the waves' per-node records land in consecutive slots), the row walked in
 // segments of 4 KiB (four 16-byte vectors per lane, non-temporal loads) with
 // the next segment's loads in flight.  Holding only two segments, a wave
 // needs few registers, so many waves (rows) are in flight per compute unit:
 // measured faster than holding whole rows in registers (three row buffers
 // of up to 16 vectors per lane) on 4 KiB and 8 KiB rows, and the only form
-// for rows beyond 16 KiB.  Each lane keeps a running maximum of its
+// for rows beyond 16 KiB.
+//
+// Each lane keeps a running maximum m of its elements, nm = -m log2(e)
+// rounded to fp32, and s = the sum of exp2(fma(x, log2(e), nm)) over its
+// elements: one fused multiply-add, one exp2 and one add per element.  When
+// m grows, s is multiplied by exp2(nm' - nm), which is exact in this form:
+// every term carries the same factor 2^(m log2(e) + nm), the rounding of nm,
+// and that factor changes by exactly nm' - nm.  At the end of the row the
+// lane's sum, rescaled to the row maximum M, is s exp2(-fma(M, log2(e), nm)):
+// the rounding of nm cancels, so no step depends on the size of x, only on
+// x - M (an fp32 emulation against exact sums: 2.4e-7 in log2 of the sum at
+// offsets from 0 to 30000).  Each lane keeps a running maximum of its
 // elements and the sum of exp(x - that maximum), rescaled when it grows; at
 // the end of the row the lanes' sums are rescaled to the row maximum and
 // added.  Every term is formed from x - maximum, as in the other row passes.
-template <typename T>
-__global__ __launch_bounds__(256) void k_rowstats_stream(const T *__restrict__ logits, int V, int blank,
+template <typename T, int W>
+__global__ __launch_bounds__(64 * W) void k_rowstats_stream(const T *__restrict__ logits, int V, int blank,
                                                          const SampleDesc *__restrict__ desc,
                                                          const ChunkDesc *__restrict__ chunks,
                                                          const int32_t *__restrict__ targets, int S,
@@ -415,7 +429,7 @@ __global__ __launch_bounds__(256) void k_rowstats_stream(const T *__restrict__ l
     const int nseg = (nvec + 64 * NS - 1) / (64 * NS);
     int n = c.diag, u = c.col;
     advance_diag(n, u, wave, d.T, d.U);
-    for (int r = wave; r < c.count; r += 4) {
+    for (int r = wave; r < c.count; r += W) {
         const T *p = logits + row_of(d, n - u, u) * (int64_t)V;
         const int y = __builtin_amdgcn_readfirstlane(read_label(d, u, V, blank, targets, S, status));
         const float hb = Elem<T>::load1(p + blank);
@@ -427,24 +441,19 @@ __global__ __launch_bounds__(256) void k_rowstats_stream(const T *__restrict__ l
                 if (vi < nvec) x[i] = load_raw<T, true>(p + (int64_t)vi * VEC);
             }
         };
-        float m = kNegInf, s = 0.f;
+        float m = kNegInf, nm = 0.f, s = 0.f;
         auto take_seg = [&](int sg, const Vec (&x)[NS]) {
-            float sm = kNegInf;
+            const float mn = fmaxf(m, row_max<T, NS, false>(x, nvec - sg * NS * 64));
+            const float nmn = (mn == kNegInf) ? 0.f : -mn * kLog2e;
+            float acc = (m == kNegInf) ? 0.f : s * exp2_fast(nmn - nm);
 #pragma unroll
             for (int i = 0; i < NS; ++i)
                 if ((sg * NS + i) * 64 + lane < nvec)
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) sm = fmaxf(sm, Raw<T>::get(x[i], e));
-            const float mn = fmaxf(m, sm);
-            const float mr = (mn == kNegInf) ? 0.f : mn;
-            float acc = s * exp2_fast((m - mr) * kLog2e);
-#pragma unroll
-            for (int i = 0; i < NS; ++i)
-                if ((sg * NS + i) * 64 + lane < nvec)
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) acc += exp2_fast((Raw<T>::get(x[i], e) - mr) * kLog2e);
+                    for (int e = 0; e < VEC; ++e) acc += exp2_fast(fmaf(Raw<T>::get(x[i], e), kLog2e, nmn));
             s = acc;
             m = mn;
+            nm = nmn;
         };
         Vec xa[NS], xb[NS];
         load_seg(0, xa);
@@ -459,12 +468,13 @@ __global__ __launch_bounds__(256) void k_rowstats_stream(const T *__restrict__ l
         const float M = wave_max_f(m);
         const bool dead = (M == kNegInf);
         const float mr = dead ? 0.f : M;
-        const float ls2 = dead ? 0.f : log2_fast(wave_sum_f(s * exp2_fast((m - mr) * kLog2e)));
+        const float part = (s == 0.f) ? 0.f : s * exp2_fast(-fmaf(mr, kLog2e, nm));
+        const float ls2 = dead ? 0.f : log2_fast(wave_sum_f(part));
         const float lpb = dead ? kNegInf : (hb - mr) - ls2 * kLn2;
         const float lpy = (dead || y < 0) ? kNegInf : (hy - mr) - ls2 * kLn2;
         emit_node(d, n - u, u, mr, ls2, lpb, lpy, node, prob, mode);
         fill_diagonal_ends(d, n, u, lane, 64, node, prob);
-        advance_diag(n, u, 4, d.T, d.U);
+        advance_diag(n, u, W, d.T, d.U);
     }
 }
 
@@ -1432,7 +1442,9 @@ hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream) {
     if (a.geom.stream_parts > 0) {
         auto go = [&](auto tag) {
             using T = decltype(tag);
-            hipLaunchKernelGGL(k_rowstats_stream<T>, grid, block, 0, stream, static_cast<const T *>(a.logits), a.V,
+            auto kern = a.geom.stream_parts == 1 ? k_rowstats_stream<T, 8> : k_rowstats_stream<T, 16>;
+            const dim3 wblock(a.geom.stream_parts == 1 ? 512 : 1024);
+            hipLaunchKernelGGL(kern, grid, wblock, 0, stream, static_cast<const T *>(a.logits), a.V,
                                a.blank, WS(const SampleDesc *, desc), WS(const ChunkDesc *, chunks), a.targets, a.S,
                                WS(float4 *, node), WS(float2 *, prob), WS(int *, mode), WS(uint32_t *, status));
             return hipGetLastError();
