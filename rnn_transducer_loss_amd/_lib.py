@@ -36,6 +36,7 @@ _lib = None
 _lock = threading.Lock()
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
+_i32in = ctypes.c_char_p  # a host int32 input array, passed as the bytes of a contiguous copy
 _vp = ctypes.c_void_p
 
 
@@ -55,63 +56,63 @@ def load():
         lib.rnnt_status_string.argtypes = [ctypes.c_int]
         lib.rnnt_status_string.restype = ctypes.c_char_p
         lib.rnnt_loss_fused_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int,
-                                                       _i32p, _i32p, ctypes.POINTER(ctypes.c_size_t)]
+                                                       _i32in, _i32in, ctypes.POINTER(ctypes.c_size_t)]
         lib.rnnt_loss_fused_workspace_size.restype = ctypes.c_int
         lib.rnnt_loss_fused.argtypes = [_vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, _vp, ctypes.c_int32,
-                                        _i32p, _i32p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                                        _i32in, _i32in, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                                         ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp,
                                         ctypes.c_size_t, _vp]
         lib.rnnt_loss_fused.restype = ctypes.c_int
         lib.rnnt_loss_fused_noalloc.argtypes = [_vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, _vp,
-                                                ctypes.c_int32, _i32p, _i32p, ctypes.c_int32, ctypes.c_int64,
+                                                ctypes.c_int32, _i32in, _i32in, ctypes.c_int32, ctypes.c_int64,
                                                 ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, _vp,
                                                 _vp, _vp, _vp]
         lib.rnnt_loss_fused_noalloc.restype = ctypes.c_int
-        lib.rnnt_grad_scale.argtypes = [_vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, _i32p, _i32p,
+        lib.rnnt_grad_scale.argtypes = [_vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, _i32in, _i32in,
                                         ctypes.c_int32, _vp, ctypes.c_int, _vp, ctypes.c_size_t, _vp]
         lib.rnnt_grad_scale.restype = ctypes.c_int
         lib.rnnt_loss_padded_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                                         ctypes.c_int32, ctypes.c_int, _i32p, _i32p,
+                                                         ctypes.c_int32, ctypes.c_int, _i32in, _i32in,
                                                          ctypes.POINTER(ctypes.c_size_t)]
         lib.rnnt_loss_padded_workspace_size.restype = ctypes.c_int
         lib.rnnt_loss_padded.argtypes = [_vp, ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp,
-                                         ctypes.c_int32, _i32p, _i32p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                                         ctypes.c_int32, _i32in, _i32in, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                                          ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp,
                                          ctypes.c_size_t, _vp]
         lib.rnnt_loss_padded.restype = ctypes.c_int
         lib.rnnt_grad_scale_padded.argtypes = [_vp, ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                               _i32p, _i32p, ctypes.c_int32, _vp, ctypes.c_int, _vp, ctypes.c_size_t,
+                                               _i32in, _i32in, ctypes.c_int32, _vp, ctypes.c_int, _vp, ctypes.c_size_t,
                                                _vp]
         lib.rnnt_grad_scale_padded.restype = ctypes.c_int
         lib.rnnt_loss_fused_check.argtypes = [_vp, _vp, ctypes.POINTER(ctypes.c_uint32)]
         lib.rnnt_loss_fused_check.restype = ctypes.c_int
-        lib.rnnt_plan_describe.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int, _i32p, _i32p, ctypes.c_int32,
+        lib.rnnt_plan_describe.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int, _i32in, _i32in, ctypes.c_int32,
                                            _i32p, _i32p, _i32p, _i32p, _i32p, _i32p, _i32p]
         lib.rnnt_plan_describe.restype = ctypes.c_int
         lib.rnnt_multiblank_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int,
-                                                       _i32p, _i32p, ctypes.c_int32, _i32p,
+                                                       _i32in, _i32in, ctypes.c_int32, _i32in,
                                                        ctypes.POINTER(ctypes.c_size_t)]
         lib.rnnt_multiblank_workspace_size.restype = ctypes.c_int
         lib.rnnt_multiblank_loss.argtypes = [_vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, _vp, ctypes.c_int32,
-                                             _i32p, _i32p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _i32p,
-                                             _i32p, ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_int,
+                                             _i32in, _i32in, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _i32in,
+                                             _i32in, ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_int,
                                              ctypes.c_int, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         lib.rnnt_multiblank_loss.restype = ctypes.c_int
-        lib.rnnt_multiblank_grad_scale.argtypes = [_vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, _i32p, _i32p,
+        lib.rnnt_multiblank_grad_scale.argtypes = [_vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, _i32in, _i32in,
                                                    ctypes.c_int32, _vp, ctypes.c_int, _vp, ctypes.c_size_t, _vp]
         lib.rnnt_multiblank_grad_scale.restype = ctypes.c_int
         lib.rnnt_multiblank_padded_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                                              ctypes.c_int32, ctypes.c_int, _i32p, _i32p,
-                                                              ctypes.c_int32, _i32p, ctypes.POINTER(ctypes.c_size_t)]
+                                                              ctypes.c_int32, ctypes.c_int, _i32in, _i32in,
+                                                              ctypes.c_int32, _i32in, ctypes.POINTER(ctypes.c_size_t)]
         lib.rnnt_multiblank_padded_workspace_size.restype = ctypes.c_int
         lib.rnnt_multiblank_loss_padded.argtypes = [_vp, ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                                    _vp, ctypes.c_int32, _i32p, _i32p, ctypes.c_int32,
-                                                    ctypes.c_int64, ctypes.c_int32, _i32p, _i32p, ctypes.c_float,
+                                                    _vp, ctypes.c_int32, _i32in, _i32in, ctypes.c_int32,
+                                                    ctypes.c_int64, ctypes.c_int32, _i32in, _i32in, ctypes.c_float,
                                                     ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp,
                                                     _vp, _vp, _vp, ctypes.c_size_t, _vp]
         lib.rnnt_multiblank_loss_padded.restype = ctypes.c_int
         lib.rnnt_multiblank_grad_scale_padded.argtypes = [_vp, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
-                                                          ctypes.c_int32, _i32p, _i32p, ctypes.c_int32, _vp,
+                                                          ctypes.c_int32, _i32in, _i32in, ctypes.c_int32, _vp,
                                                           ctypes.c_int, _vp, ctypes.c_size_t, _vp]
         lib.rnnt_multiblank_grad_scale_padded.restype = ctypes.c_int
         lib.rnnt_timing_enable.argtypes = [ctypes.c_int]
@@ -137,6 +138,8 @@ def check(code: int, what: str):
 
 def host_i32(a) -> np.ndarray:
     """A contiguous host int32 copy of a length vector (tensor on any device, list or array)."""
+    if type(a) is np.ndarray and a.dtype == np.int32 and a.flags.c_contiguous:
+        return a
     try:
         import torch
         if isinstance(a, torch.Tensor):
@@ -148,7 +151,14 @@ def host_i32(a) -> np.ndarray:
 
 
 def _p(a: np.ndarray):
+    """Pointer to an int32 array the library writes (an output)."""
     return a.ctypes.data_as(_i32p)
+
+
+def _b(a: np.ndarray) -> bytes:
+    """An int32 input array for the library: the bytes of a contiguous host int32 array (read during the call
+    only).  Faster to pass than an array pointer."""
+    return a.tobytes()
 
 
 def workspace_size(B: int, V: int, N: int, dtype_code: int, logit_lengths, target_lengths) -> int:
@@ -157,7 +167,7 @@ def workspace_size(B: int, V: int, N: int, dtype_code: int, logit_lengths, targe
     if len(T) != B or len(U) != B:
         raise ValueError("length vectors must have B entries")
     out = ctypes.c_size_t()
-    check(load().rnnt_loss_fused_workspace_size(B, V, N, dtype_code, _p(T), _p(U), ctypes.byref(out)),
+    check(load().rnnt_loss_fused_workspace_size(B, V, N, dtype_code, _b(T), _b(U), ctypes.byref(out)),
           "rnnt_loss_fused_workspace_size")
     return int(out.value)
 
@@ -173,7 +183,7 @@ def loss_fused(logits_ptr: int, dtype_code: int, N: int, V: int, targets_ptr: in
         raise ValueError("length vectors must have B entries")
     if reduction not in REDUCTIONS:
         raise ValueError(f"reduction must be one of {sorted(REDUCTIONS)}")
-    rc = load().rnnt_loss_fused(logits_ptr or None, dtype_code, N, V, targets_ptr or None, S, _p(T), _p(U), B,
+    rc = load().rnnt_loss_fused(logits_ptr or None, dtype_code, N, V, targets_ptr or None, S, _b(T), _b(U), B,
                                 int(blank), float(clamp), float(fastemit_lambda), int(bool(fused)),
                                 REDUCTIONS[reduction], loss_ptr or None,
                                 loss_reduced_ptr or None, grad_ptr or None, ws_ptr or None, ws_bytes,
@@ -193,7 +203,7 @@ def loss_fused_noalloc(logits_ptr: int, dtype_code: int, N: int, V: int, targets
         raise ValueError("length vectors must have B entries")
     if reduction not in REDUCTIONS:
         raise ValueError(f"reduction must be one of {sorted(REDUCTIONS)}")
-    rc = load().rnnt_loss_fused_noalloc(logits_ptr or None, dtype_code, N, V, targets_ptr or None, S, _p(T), _p(U),
+    rc = load().rnnt_loss_fused_noalloc(logits_ptr or None, dtype_code, N, V, targets_ptr or None, S, _b(T), _b(U),
                                         B, int(blank), float(clamp), float(fastemit_lambda), int(bool(fused)),
                                         REDUCTIONS[reduction], loss_ptr or None, loss_reduced_ptr or None,
                                         grad_ptr or None, status_ptr or None, stream or None)
@@ -204,7 +214,7 @@ def grad_scale(grad_ptr: int, dtype_code: int, N: int, V: int, logit_lengths, ta
                per_sample: bool, ws_ptr: int, ws_bytes: int, stream: int):
     T = host_i32(logit_lengths)
     U = host_i32(target_lengths)
-    rc = load().rnnt_grad_scale(grad_ptr or None, dtype_code, N, V, _p(T), _p(U), len(T), scale_ptr or None,
+    rc = load().rnnt_grad_scale(grad_ptr or None, dtype_code, N, V, _b(T), _b(U), len(T), scale_ptr or None,
                                 int(bool(per_sample)), ws_ptr or None, ws_bytes, stream or None)
     check(rc, "rnnt_grad_scale")
 
@@ -216,7 +226,7 @@ def workspace_size_padded(B: int, V: int, max_T: int, max_U1: int, dtype_code: i
     if len(T) != B or len(U) != B:
         raise ValueError("length vectors must have B entries")
     out = ctypes.c_size_t()
-    check(load().rnnt_loss_padded_workspace_size(B, V, max_T, max_U1, dtype_code, _p(T), _p(U), ctypes.byref(out)),
+    check(load().rnnt_loss_padded_workspace_size(B, V, max_T, max_U1, dtype_code, _b(T), _b(U), ctypes.byref(out)),
           "rnnt_loss_padded_workspace_size")
     return int(out.value)
 
@@ -232,8 +242,8 @@ def loss_padded(logits_ptr: int, dtype_code: int, max_T: int, max_U1: int, V: in
         raise ValueError("length vectors must have B entries")
     if reduction not in REDUCTIONS:
         raise ValueError(f"reduction must be one of {sorted(REDUCTIONS)}")
-    rc = load().rnnt_loss_padded(logits_ptr or None, dtype_code, max_T, max_U1, V, targets_ptr or None, S, _p(T),
-                                 _p(U), B, int(blank), float(clamp), float(fastemit_lambda), int(bool(fused)),
+    rc = load().rnnt_loss_padded(logits_ptr or None, dtype_code, max_T, max_U1, V, targets_ptr or None, S, _b(T),
+                                 _b(U), B, int(blank), float(clamp), float(fastemit_lambda), int(bool(fused)),
                                  REDUCTIONS[reduction],
                                  loss_ptr or None, loss_reduced_ptr or None, grad_ptr or None, ws_ptr or None,
                                  ws_bytes, stream or None)
@@ -244,7 +254,7 @@ def grad_scale_padded(grad_ptr: int, dtype_code: int, max_T: int, max_U1: int, V
                       target_lengths, scale_ptr: int, per_sample: bool, ws_ptr: int, ws_bytes: int, stream: int):
     T = host_i32(logit_lengths)
     U = host_i32(target_lengths)
-    rc = load().rnnt_grad_scale_padded(grad_ptr or None, dtype_code, max_T, max_U1, V, _p(T), _p(U), len(T),
+    rc = load().rnnt_grad_scale_padded(grad_ptr or None, dtype_code, max_T, max_U1, V, _b(T), _b(U), len(T),
                                        scale_ptr or None, int(bool(per_sample)), ws_ptr or None, ws_bytes,
                                        stream or None)
     check(rc, "rnnt_grad_scale_padded")
@@ -268,12 +278,12 @@ def plan_describe(V: int, dtype_code: int, logit_lengths, target_lengths, diagon
     B = len(T)
     n = ctypes.c_int32()
     lib = load()
-    check(lib.rnnt_plan_describe(B, V, dtype_code, _p(T), _p(U), 0, None, None, None, None, None, None,
+    check(lib.rnnt_plan_describe(B, V, dtype_code, _b(T), _b(U), 0, None, None, None, None, None, None,
                                  ctypes.byref(n)), "rnnt_plan_describe")
     cap = max(B, n.value)
     order = np.zeros(cap, np.int32)
     cs, cb, cc, cd, cu = (np.zeros(cap, np.int32) for _ in range(5))
-    check(lib.rnnt_plan_describe(B, V, dtype_code, _p(T), _p(U), cap, _p(order), _p(cs), _p(cb), _p(cc), _p(cd),
+    check(lib.rnnt_plan_describe(B, V, dtype_code, _b(T), _b(U), cap, _p(order), _p(cs), _p(cb), _p(cc), _p(cd),
                                  _p(cu), ctypes.byref(n)), "rnnt_plan_describe")
     k = n.value
     if diagonal:
@@ -310,7 +320,7 @@ def workspace_size_multiblank(B: int, V: int, N: int, dtype_code: int, logit_len
         raise ValueError("length vectors must have B entries")
     nb, _, dur = _big_blanks(np.zeros(len(host_i32(big_blank_durations).reshape(-1)), np.int32), big_blank_durations)
     out = ctypes.c_size_t()
-    check(load().rnnt_multiblank_workspace_size(B, V, N, dtype_code, _p(T), _p(U), nb, _p(dur), ctypes.byref(out)),
+    check(load().rnnt_multiblank_workspace_size(B, V, N, dtype_code, _b(T), _b(U), nb, _b(dur), ctypes.byref(out)),
           "rnnt_multiblank_workspace_size")
     return int(out.value)
 
@@ -327,8 +337,8 @@ def loss_multiblank(logits_ptr: int, dtype_code: int, N: int, V: int, targets_pt
     if reduction not in REDUCTIONS:
         raise ValueError(f"reduction must be one of {sorted(REDUCTIONS)}")
     nb, ids, dur = _big_blanks(big_blank_ids, big_blank_durations)
-    rc = load().rnnt_multiblank_loss(logits_ptr or None, dtype_code, N, V, targets_ptr or None, S, _p(T), _p(U), B,
-                                     int(blank), nb, _p(ids), _p(dur), float(sigma), float(clamp),
+    rc = load().rnnt_multiblank_loss(logits_ptr or None, dtype_code, N, V, targets_ptr or None, S, _b(T), _b(U), B,
+                                     int(blank), nb, _b(ids), _b(dur), float(sigma), float(clamp),
                                      float(fastemit_lambda), int(bool(fused)), REDUCTIONS[reduction],
                                      loss_ptr or None, loss_reduced_ptr or None, grad_ptr or None, ws_ptr or None,
                                      ws_bytes, stream or None)
@@ -339,7 +349,7 @@ def grad_scale_multiblank(grad_ptr: int, dtype_code: int, N: int, V: int, logit_
                           scale_ptr: int, per_sample: bool, ws_ptr: int, ws_bytes: int, stream: int):
     T = host_i32(logit_lengths)
     U = host_i32(target_lengths)
-    rc = load().rnnt_multiblank_grad_scale(grad_ptr or None, dtype_code, N, V, _p(T), _p(U), len(T),
+    rc = load().rnnt_multiblank_grad_scale(grad_ptr or None, dtype_code, N, V, _b(T), _b(U), len(T),
                                            scale_ptr or None, int(bool(per_sample)), ws_ptr or None, ws_bytes,
                                            stream or None)
     check(rc, "rnnt_multiblank_grad_scale")
@@ -354,8 +364,8 @@ def workspace_size_multiblank_padded(B: int, V: int, max_T: int, max_U1: int, dt
     dur = host_i32(big_blank_durations).reshape(-1)
     nb = len(dur)
     out = ctypes.c_size_t()
-    check(load().rnnt_multiblank_padded_workspace_size(B, V, max_T, max_U1, dtype_code, _p(T), _p(U), nb,
-                                                       _p(dur if nb else np.zeros(1, np.int32)), ctypes.byref(out)),
+    check(load().rnnt_multiblank_padded_workspace_size(B, V, max_T, max_U1, dtype_code, _b(T), _b(U), nb,
+                                                       _b(dur if nb else np.zeros(1, np.int32)), ctypes.byref(out)),
           "rnnt_multiblank_padded_workspace_size")
     return int(out.value)
 
@@ -374,7 +384,7 @@ def loss_multiblank_padded(logits_ptr: int, dtype_code: int, max_T: int, max_U1:
         raise ValueError(f"reduction must be one of {sorted(REDUCTIONS)}")
     nb, ids, dur = _big_blanks(big_blank_ids, big_blank_durations)
     rc = load().rnnt_multiblank_loss_padded(logits_ptr or None, dtype_code, max_T, max_U1, V, targets_ptr or None, S,
-                                            _p(T), _p(U), B, int(blank), nb, _p(ids), _p(dur), float(sigma),
+                                            _b(T), _b(U), B, int(blank), nb, _b(ids), _b(dur), float(sigma),
                                             float(clamp), float(fastemit_lambda), int(bool(fused)),
                                             REDUCTIONS[reduction], loss_ptr or None, loss_reduced_ptr or None,
                                             grad_ptr or None, ws_ptr or None, ws_bytes, stream or None)
@@ -386,7 +396,7 @@ def grad_scale_multiblank_padded(grad_ptr: int, dtype_code: int, max_T: int, max
                                  stream: int):
     T = host_i32(logit_lengths)
     U = host_i32(target_lengths)
-    rc = load().rnnt_multiblank_grad_scale_padded(grad_ptr or None, dtype_code, max_T, max_U1, V, _p(T), _p(U),
+    rc = load().rnnt_multiblank_grad_scale_padded(grad_ptr or None, dtype_code, max_T, max_U1, V, _b(T), _b(U),
                                                   len(T), scale_ptr or None, int(bool(per_sample)), ws_ptr or None,
                                                   ws_bytes, stream or None)
     check(rc, "rnnt_multiblank_grad_scale_padded")

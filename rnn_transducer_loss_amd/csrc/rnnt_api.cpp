@@ -124,6 +124,11 @@ rnnt_status plan_into(int32_t B, int32_t V, int64_t N, int esize, const int32_t 
         d.U = U[i];
         d.index = i;
         d.U1p = padded_width(U[i] + 1);
+        // the sweeps address a sample's alpha/beta table (T+U diagonals of
+        // U1p fp64 values) and its log-domain weights (T+U diagonals of U+1
+        // 16-byte slots) with 32-bit byte offsets
+        if (((int64_t)T[i] + U[i]) * std::max<int64_t>(8 * d.U1p, 16 * (U[i] + 1)) >= ((int64_t)1 << 31))
+            return RNNT_INVALID_VALUE;
         row += (int64_t)T[i] * (U[i] + 1);
         slot += ((int64_t)T[i] + U[i]) * (U[i] + 1);
         diag += (int64_t)T[i] + U[i];
@@ -153,6 +158,8 @@ rnnt_status plan_into(int32_t B, int32_t V, int64_t N, int esize, const int32_t 
     L.desc = off;   off = align_up(off + sizeof(SampleDesc) * B);
     L.order = off;  off = align_up(off + sizeof(int32_t) * B);
     L.chunks = off; off = align_up(off + sizeof(ChunkDesc) * (size_t)n_chunks);
+    L.cflags = off; off = align_up(off + sizeof(uint32_t) * (size_t)n_chunks);
+    L.sflags = off; off = align_up(off + sizeof(uint32_t) * (size_t)B);
     L.node = off;   off = align_up(off + 4 * sizeof(float) * (size_t)slot);
     L.prob = off;   off = align_up(off + 2 * sizeof(float) * (size_t)slot);
     L.alpha = off;  off = align_up(off + sizeof(double) * (size_t)ab);
@@ -165,6 +172,7 @@ rnnt_status plan_into(int32_t B, int32_t V, int64_t N, int esize, const int32_t 
     L.n_ab_slots = ab;
     L.n_diags = diag;
     L.n_chunks = (int32_t)n_chunks;
+    L.n_rows = row;
     L.rows_per_chunk = rpc;
     L.max_sample_chunks = (int32_t)max_sample_chunks;
     return RNNT_SUCCESS;
@@ -291,10 +299,7 @@ rnnt_status get_plan(int32_t B, int32_t V, int64_t N, int esize, const int32_t *
         if (B <= kArgSamples) {
             e->args.reset(new PlanArgs{});
             e->args->B = B;
-            for (int32_t i = 0; i < B; ++i) {
-                e->args->desc[i] = e->plan.desc[i];
-                e->args->order[i] = e->plan.order[i];
-            }
+            for (int32_t k = 0; k < B; ++k) e->args->desc[k] = e->plan.desc[e->plan.order[k]];
         }
         std::lock_guard<std::mutex> lk(g_plan_mu);
         g_plan_cache = e;
@@ -475,8 +480,8 @@ LaunchArgs launch_args(const void *logits, int es, int64_t rows, int32_t V, cons
 rnnt_status enqueue_path(const LaunchArgs &a, const PlanArgs *pa, const Padding &pad, bool timing,
                          hipStream_t stream) {
     auto run = [&](int k, auto &&fn) { return timing ? timed(k, stream, fn) : fn(); };
-    if (launch_plan(a, pa, stream) != hipSuccess) return RNNT_EXECUTION_FAILED;
-    if (a.lay.n_chunks > 0 && run(0, [&] { return launch_rowstats(a, stream); }) != hipSuccess)
+    if (!a.small && launch_plan(a, pa, stream) != hipSuccess) return RNNT_EXECUTION_FAILED;
+    if (a.lay.n_chunks > 0 && run(0, [&] { return launch_rowstats(a, pa, stream); }) != hipSuccess)
         return RNNT_EXECUTION_FAILED;
     if (run(1, [&] { return launch_alpha_beta(a, stream); }) != hipSuccess) return RNNT_EXECUTION_FAILED;
     if (a.grad && a.lay.n_chunks > 0 && run(2, [&] { return launch_grad(a, stream); }) != hipSuccess)
@@ -515,9 +520,10 @@ rnnt_status loss_impl(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V
         if (st != RNNT_SUCCESS) return st;
     }
     const int64_t rows = pad.on() ? (int64_t)B * pad.max_T * pad.max_U1 : N;
-    const LaunchArgs a = launch_args(logits, es, rows, V, targets, S, B, blank, clamp, fastemit_lambda,
-                                     fused_log_softmax, reduction, loss, loss_reduced, grad, workspace, plan.lay,
-                                     plan.max_U1, aligned16);
+    LaunchArgs a = launch_args(logits, es, rows, V, targets, S, B, blank, clamp, fastemit_lambda,
+                               fused_log_softmax, reduction, loss, loss_reduced, grad, workspace, plan.lay,
+                               plan.max_U1, aligned16);
+    a.small = e->args && plan.lay.n_rows <= kSmallRows;
     return enqueue_path(a, e->args.get(), pad, true, stream);
 }
 
@@ -758,18 +764,22 @@ rnnt_status rnnt_loss_fused_noalloc(const void *logits, rnnt_dtype dtype, int64_
                                 fastemit_lambda, reduction, loss, grad, Padding(), aligned16);
     if (st != RNNT_SUCCESS) return st;
     if (B > kArgSamples) return RNNT_INVALID_VALUE;
-    PlanArgs pa{};
-    pa.B = B;
+    SampleDesc desc[kArgSamples];
+    int32_t order[kArgSamples];
     WorkspaceLayout lay{};
     int32_t max_U1 = 1;
-    st = plan_into(B, V, N, es, logit_lengths, target_lengths, Padding(), pa.desc, pa.order, lay, max_U1);
+    st = plan_into(B, V, N, es, logit_lengths, target_lengths, Padding(), desc, order, lay, max_U1);
     if (st != RNNT_SUCCESS) return st;
+    PlanArgs pa{};
+    pa.B = B;
+    for (int32_t k = 0; k < B; ++k) pa.desc[k] = desc[order[k]];
     if (lay.total > kScratchBytes) return RNNT_WORKSPACE_TOO_SMALL;
     void *ws = nullptr;
     if (scratch_address(&ws) != hipSuccess) return RNNT_MEMOPS_FAILED;
     LaunchArgs a = launch_args(logits, es, N, V, targets, S, B, blank, clamp, fastemit_lambda, fused_log_softmax,
                                reduction, loss, loss_reduced, grad, ws, lay, max_U1, aligned16);
     a.status_out = dev_status;
+    a.small = lay.n_rows <= kSmallRows;
     return enqueue_path(a, &pa, Padding(), false, stream);
 }
 

@@ -105,6 +105,8 @@ struct WorkspaceLayout {
     size_t desc;        // SampleDesc[B]
     size_t order;       // int32[B], samples by decreasing cost
     size_t chunks;      // ChunkDesc[n_chunks]
+    size_t cflags;      // uint32[n_chunks]: small batches, the row pass's flag word of each chunk
+    size_t sflags;      // uint32[B]: small batches, each sample's status bits (from its chunks' flags)
     size_t node;        // float4[S]
     size_t prob;        // float2[S]
     size_t alpha;       // double[S_ab], padded diagonals
@@ -116,6 +118,7 @@ struct WorkspaceLayout {
     int64_t n_slots;
     int64_t n_ab_slots;
     int64_t n_diags;
+    int64_t n_rows;              // lattice rows, sum_i T_i (U_i + 1)
     int32_t n_chunks;
     int32_t rows_per_chunk;
     int32_t max_sample_chunks;   // most chunks of any one sample
@@ -157,23 +160,31 @@ struct LaunchArgs {
     int max_U1;          // max_i (U_i + 1)
     bool aligned16;
     uint32_t *status_out;  // device; if set, the reduction kernel copies the final status word there
+    bool small;          // a batch below kSmallRows rows with its descriptors in PlanArgs: three launches
 };
 
-// Batches of up to kArgSamples samples pass their descriptors and order to
-// the chunk-table kernel as kernel arguments; it writes them, clears the
-// status word and the mode flags, and no host-to-device copy is needed.
+// Batches below this many rows (and of at most kArgSamples samples) take
+// three launches instead of six: the row pass derives its chunks from the
+// descriptors passed as kernel arguments (no chunk-table launch), and one
+// two-wave workgroup per sample runs both recursions, their check and the
+// log-domain rerun.
+constexpr int64_t kSmallRows = 64 * 1024 - 1024;
+
+// Batches of up to kArgSamples samples pass their descriptors, in cost
+// order, as kernel arguments to the chunk-table kernel (or, for batches
+// below kSmallRows rows, to the row pass), which writes them and the order
+// to the workspace, so no host-to-device copy is needed.
 constexpr int kArgSamples = 64;
 struct PlanArgs {
     int32_t B;
     int32_t pad;
-    SampleDesc desc[kArgSamples];
-    int32_t order[kArgSamples];
+    SampleDesc desc[kArgSamples];  // in cost order: desc[k].index is the k-th sample of the longest-first order
 };
 static_assert(sizeof(PlanArgs) <= 3900, "kernel arguments are limited to 4 KiB");
 
 // `pa` null: the descriptors were uploaded with the workspace header.
 hipError_t launch_plan(const LaunchArgs &a, const PlanArgs *pa, hipStream_t stream);
-hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream);
+hipError_t launch_rowstats(const LaunchArgs &a, const PlanArgs *pa, hipStream_t stream);
 hipError_t launch_alpha_beta(const LaunchArgs &a, hipStream_t stream);
 hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream);
 hipError_t launch_reduce(const LaunchArgs &a, hipStream_t stream);

@@ -22,6 +22,12 @@
 //                         section 2), clamp, reduction scale, one write.
 //   reduce                none / mean / sum of the per-sample losses.
 //
+// Batches below 64512 lattice rows, where every launch is mostly fixed cost,
+// take three launches instead of six: no chunk-table launch (the row pass
+// derives its chunks from descriptors passed as kernel arguments), and one
+// two-wave workgroup per sample runs both recursions, their check and the
+// log-domain rerun (k_ab_small).
+//
 // The recursions run in a scaled probability domain: node values are fp64
 // mantissas with one power-of-two exponent per group of eight anti-diagonals,
 // renormalised exactly (by a power of two).  A step is then one multiply and
@@ -60,7 +66,9 @@ constexpr float kProbRange = 80.f;  // |log-prob| bound of the probability-domai
 // Per-sample mode word (zeroed by k_plan): the row pass sets kModeLog when a
 // log-probability leaves that bound, k_check_ab sets kModeRerun when the
 // probability-domain sweeps lost alignment mass; either sends the sample's
-// recursions, and the gradient's reads of them, to the log domain.
+// recursions, and the gradient's reads of them, to the log domain.  (Small
+// batches: k_ab_small writes the word whole, from the row pass's per-chunk
+// flags and its own check.)
 constexpr int kModeLog = 1;
 constexpr int kModeRerun = 2;
 
@@ -235,14 +243,14 @@ __device__ __forceinline__ int wave_max_nonneg(int v) {
 // wait counts stay exact); the others from one lane per row.
 __device__ __forceinline__ void emit_node(const SampleDesc &d, int t, int u, float m, float ls2, float lpb,
                                           float lpy, float4 *__restrict__ node, float2 *__restrict__ prob,
-                                          int *__restrict__ mode) {
+                                          int *mode_word) {
     if (t == d.T - 1 && u < d.U) lpb = kNegInf;
     if (u == d.U) lpy = kNegInf;
     const int64_t slot = d.slot_off + (int64_t)(t + u) * (d.U + 1) + u;
     node[slot] = make_float4(lpb, lpy, m, ls2);
     prob[slot] = make_float2(prob_of(lpb), prob_of(lpy));
     const bool wide = (lpb != kNegInf && fabsf(lpb) > kProbRange) || (lpy != kNegInf && fabsf(lpy) > kProbRange);
-    if (wide) atomicOr(&mode[d.index], kModeLog);
+    if (wide) atomicOr(mode_word, kModeLog);
 }
 
 // Slots u0 .. u1-1 of diagonal n hold no lattice node: give them impossible
@@ -358,31 +366,139 @@ __device__ __forceinline__ void advance_diag(int &n, int &u, int step, int T, in
     }
 }
 
+// ------------------------------------------------ row-pass work sources
+// Where a row-pass workgroup finds its chunk and its sample, and where it
+// reports a sample's log-domain flag and a bad label.
+//   TableSrc: the chunk table and descriptors in the workspace (written by
+//     k_plan, which also cleared the mode words and the status word that the
+//     row pass sets bits in).
+//   ArgSrc (batches below 64 K rows, whose every launch is mostly fixed
+//     cost): no chunk-table launch.  The descriptors come as kernel
+//     arguments, in cost order (kernel arguments may live in host memory, so
+//     each workgroup reads them in one round trip: lane k the descriptor of
+//     the k-th sample), each workgroup derives its chunk itself and writes
+//     it to the chunk table for the gradient pass, and ORs its bits
+//     (kModeLog, RNNT_DEV_BAD_TARGET) into a word in LDS that it stores as
+//     its own flag word, so nothing needs clearing first; workgroup 0 also
+//     stores the descriptors and the order.  The recursion kernel ORs a
+//     sample's flag words into its mode and its status bits, the reduction
+//     the samples' status bits into the status word.
+struct TableSrc {
+    const SampleDesc *__restrict__ desc;
+    const ChunkDesc *__restrict__ chunks;
+    int *__restrict__ mode;
+    uint32_t *status;
+};
+struct ArgSrc {
+    PlanArgs pa;  // pa.desc[k]: the k-th sample in cost order (pa.order[k] is its index)
+    int rpc;
+    ChunkDesc *ws_chunks;
+    SampleDesc *ws_desc;
+    int32_t *ws_order;
+    uint32_t *cflags;
+};
+
+// A row-pass workgroup's chunk and sample, and the words its flags go to.
+struct RowWork {
+    ChunkDesc c;
+    SampleDesc d;
+    int *mode_word;
+    uint32_t *status_word;
+};
+
+template <bool DIAG> __device__ __forceinline__ RowWork row_work(const TableSrc &s, uint32_t *) {
+    RowWork w;
+    w.c = s.chunks[blockIdx.x];
+    w.d = s.desc[w.c.sample];
+    w.mode_word = &s.mode[w.d.index];
+    w.status_word = s.status;
+    return w;
+}
+__device__ __forceinline__ void row_work_end(const TableSrc &, uint32_t *) {}
+
+__device__ __forceinline__ int readlane_i(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ int64_t readlane_l(int64_t v, int l) {
+    const int lo = __builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const int hi = __builtin_amdgcn_readlane((int)(v >> 32), l);
+    return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// DIAG: the pass walks its chunk in diagonal order (the chunk's first node
+// is found by bisection); a row-order pass needs only its rows.
+template <bool DIAG> __device__ __forceinline__ RowWork row_work(const ArgSrc &s, uint32_t *flags) {
+    const int x = (int)blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    if (threadIdx.x == 0) *flags = 0u;
+    // Chunks are numbered in cost order, so x belongs to the last sample in
+    // that order whose first chunk is at most x (every sample has a chunk).
+    SampleDesc mine{};
+    if (lane < s.pa.B) mine = s.pa.desc[lane];
+    const uint64_t hit = __ballot(lane < s.pa.B && mine.chunk0 <= x);
+    const int k = 63 - __builtin_clzll(hit);
+    RowWork w;
+    w.d.row_off = readlane_l(mine.row_off, k);
+    w.d.slot_off = readlane_l(mine.slot_off, k);
+    w.d.diag_off = readlane_l(mine.diag_off, k);
+    w.d.ab_off = readlane_l(mine.ab_off, k);
+    w.d.T = readlane_i(mine.T, k);
+    w.d.U = readlane_i(mine.U, k);
+    w.d.index = readlane_i(mine.index, k);
+    w.d.U1p = readlane_i(mine.U1p, k);
+    w.d.tstride = readlane_i(mine.tstride, k);
+    w.d.chunk0 = readlane_i(mine.chunk0, k);
+    if (DIAG) {
+        w.c = make_chunk(w.d, w.d.index, x - w.d.chunk0, s.rpc);
+    } else {
+        const int64_t rows = (int64_t)w.d.T * (w.d.U + 1);
+        const int64_t r0 = (int64_t)(x - w.d.chunk0) * s.rpc;
+        w.c.sample = w.d.index;
+        w.c.row_begin = (int32_t)r0;
+        w.c.count = (int32_t)(rows - r0 < s.rpc ? rows - r0 : s.rpc);
+        w.c.diag = 0;  // unused in row order
+        w.c.col = 0;
+    }
+    if (threadIdx.x == 0) s.ws_chunks[x] = w.c;
+    if (x == 0 && threadIdx.x < 64 && lane < s.pa.B) {
+        s.ws_desc[mine.index] = mine;
+        s.ws_order[lane] = mine.index;
+    }
+    w.mode_word = reinterpret_cast<int *>(flags);
+    w.status_word = flags;
+    __syncthreads();
+    return w;
+}
+__device__ __forceinline__ void row_work_end(const ArgSrc &s, uint32_t *flags) {
+    __syncthreads();
+    if (threadIdx.x == 0) s.cflags[blockIdx.x] = *flags;
+}
+
 // ------------------------------------------------------------ chunk table
-// Workgroup i*GX + x writes chunks 256x .. 256x+255 of sample i, with the
-// arithmetic the host uses to describe the schedule (make_chunk), so only
-// the sample descriptors travel from the host each call.  ARGS: the
-// descriptors and order come as kernel arguments; workgroup 0 also writes
-// them to the workspace and clears the status word and the mode flags.
+// Workgroup k*GX + x writes chunks 256x .. 256x+255 of the k-th sample (in
+// cost order with ARGS, else in batch order), with the arithmetic the host
+// uses to describe the schedule (make_chunk), so only the sample
+// descriptors travel from the host each call.  ARGS: the descriptors come
+// as kernel arguments in cost order; workgroup 0 also writes them and the
+// order to the workspace and clears the status word and the mode flags.
 template <bool ARGS>
 __global__ __launch_bounds__(256) void k_plan(const SampleDesc *__restrict__ desc, int rpc, int gx,
                                               ChunkDesc *__restrict__ chunks, PlanArgs pa, SampleDesc *ws_desc,
                                               int32_t *ws_order, int *ws_mode, uint32_t *ws_status) {
-    const int i = (int)(blockIdx.x / (unsigned)gx);
+    const int k = (int)(blockIdx.x / (unsigned)gx);
     const int x = (int)(blockIdx.x % (unsigned)gx);
-    const SampleDesc d = ARGS ? pa.desc[i] : desc[i];
+    const SampleDesc d = ARGS ? pa.desc[k] : desc[k];
     if (ARGS && blockIdx.x == 0) {
-        for (int k = threadIdx.x; k < pa.B; k += blockDim.x) {
-            ws_desc[k] = pa.desc[k];
-            ws_order[k] = pa.order[k];
-            ws_mode[k] = 0;
+        for (int q = threadIdx.x; q < pa.B; q += blockDim.x) {
+            const SampleDesc e = pa.desc[q];
+            ws_desc[e.index] = e;
+            ws_order[q] = e.index;
+            ws_mode[q] = 0;
         }
         if (threadIdx.x == 0) *ws_status = 0u;
     }
     const int64_t rows = (int64_t)d.T * (d.U + 1);
     const int n = (int)((rows + rpc - 1) / rpc);
     const int j = x * 256 + threadIdx.x;
-    if (j < n) chunks[d.chunk0 + j] = make_chunk(d, i, j, rpc);
+    if (j < n) chunks[d.chunk0 + j] = make_chunk(d, d.index, j, rpc);
 }
 
 // ------------------------------------ K1 rowstats, rows wider than 1 KiB
@@ -411,18 +527,17 @@ __global__ __launch_bounds__(256) void k_plan(const SampleDesc *__restrict__ des
 // elements and the sum of exp(x - that maximum), rescaled when it grows; at
 // the end of the row the lanes' sums are rescaled to the row maximum and
 // added.  Every term is formed from x - maximum, as in the other row passes.
-template <typename T, int W>
-__global__ __launch_bounds__(64 * W) void k_rowstats_stream(const T *__restrict__ logits, int V, int blank,
-                                                         const SampleDesc *__restrict__ desc,
-                                                         const ChunkDesc *__restrict__ chunks,
+template <typename T, int W, typename Src>
+__global__ __launch_bounds__(64 * W) void k_rowstats_stream(const T *__restrict__ logits, int V, int blank, Src src,
                                                          const int32_t *__restrict__ targets, int S,
-                                                         float4 *__restrict__ node, float2 *__restrict__ prob,
-                                                         int *__restrict__ mode, uint32_t *status) {
+                                                         float4 *__restrict__ node, float2 *__restrict__ prob) {
     constexpr int VEC = Raw<T>::kVec;
     constexpr int NS = 4;  // vectors per lane per segment
     using Vec = typename Raw<T>::vec;
-    const ChunkDesc c = chunks[blockIdx.x];
-    const SampleDesc d = desc[c.sample];
+    __shared__ uint32_t wg_flags;
+    const RowWork wk = row_work<true>(src, &wg_flags);
+    const ChunkDesc &c = wk.c;
+    const SampleDesc &d = wk.d;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nvec = V / VEC;
@@ -431,7 +546,7 @@ __global__ __launch_bounds__(64 * W) void k_rowstats_stream(const T *__restrict_
     advance_diag(n, u, wave, d.T, d.U);
     for (int r = wave; r < c.count; r += W) {
         const T *p = logits + row_of(d, n - u, u) * (int64_t)V;
-        const int y = __builtin_amdgcn_readfirstlane(read_label(d, u, V, blank, targets, S, status));
+        const int y = __builtin_amdgcn_readfirstlane(read_label(d, u, V, blank, targets, S, wk.status_word));
         const float hb = Elem<T>::load1(p + blank);
         const float hy = (y >= 0) ? Elem<T>::load1(p + y) : 0.f;
         auto load_seg = [&](int sg, Vec (&x)[NS]) {
@@ -472,25 +587,25 @@ __global__ __launch_bounds__(64 * W) void k_rowstats_stream(const T *__restrict_
         const float ls2 = dead ? 0.f : log2_fast(wave_sum_f(part));
         const float lpb = dead ? kNegInf : (hb - mr) - ls2 * kLn2;
         const float lpy = (dead || y < 0) ? kNegInf : (hy - mr) - ls2 * kLn2;
-        emit_node(d, n - u, u, mr, ls2, lpb, lpy, node, prob, mode);
+        emit_node(d, n - u, u, mr, ls2, lpb, lpy, node, prob, wk.mode_word);
         fill_diagonal_ends(d, n, u, lane, 64, node, prob);
         advance_diag(n, u, W, d.T, d.U);
     }
+    row_work_end(src, &wg_flags);
 }
 
 // --------------------------------- K1 rowstats, G < 64 lanes per row (small V)
 // Rows in row order (several short rows per wave); each row's outputs go to
 // its skewed slot.
-template <typename T, int VEC, int G>
-__global__ __launch_bounds__(256) void k_rowstats_narrow(const T *__restrict__ logits, int V, int blank,
-                                                         const SampleDesc *__restrict__ desc,
-                                                         const ChunkDesc *__restrict__ chunks,
+template <typename T, int VEC, int G, typename Src>
+__global__ __launch_bounds__(256) void k_rowstats_narrow(const T *__restrict__ logits, int V, int blank, Src src,
                                                          const int32_t *__restrict__ targets, int S,
-                                                         float4 *__restrict__ node, float2 *__restrict__ prob,
-                                                         int *__restrict__ mode, uint32_t *status) {
+                                                         float4 *__restrict__ node, float2 *__restrict__ prob) {
     constexpr int RPW = 64 / G;
-    const ChunkDesc c = chunks[blockIdx.x];
-    const SampleDesc d = desc[c.sample];
+    __shared__ uint32_t wg_flags;
+    const RowWork wk = row_work<false>(src, &wg_flags);
+    const ChunkDesc &c = wk.c;
+    const SampleDesc &d = wk.d;
     const int U1 = d.U + 1;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -537,28 +652,28 @@ __global__ __launch_bounds__(256) void k_rowstats_narrow(const T *__restrict__ l
             const bool dead = (m == kNegInf);
             const float mr = dead ? 0.f : m;
             const float ls2 = dead ? 0.f : log2_fast(s);
-            const int y = read_label(d, u, V, blank, targets, S, status);
+            const int y = read_label(d, u, V, blank, targets, S, wk.status_word);
             const float hb = Elem<T>::load1(p + blank);
             const float hy = (y >= 0) ? Elem<T>::load1(p + y) : 0.f;
             const float lpb = dead ? kNegInf : (hb - mr) - ls2 * kLn2;
             const float lpy = (dead || y < 0) ? kNegInf : (hy - mr) - ls2 * kLn2;
-            emit_node(d, t, u, mr, ls2, lpb, lpy, node, prob, mode);
+            emit_node(d, t, u, mr, ls2, lpb, lpy, node, prob, wk.mode_word);
         }
         if (t == 0 || t == d.T - 1) fill_columns(d, t, u, sub, G, node, prob);
     }
+    row_work_end(src, &wg_flags);
 }
 
 // Non-fused inputs are already log-probabilities: gather the two values only.
 // One node per thread, in the chunk's order (DIAG: diagonal order).
-template <typename T, bool DIAG>
-__global__ __launch_bounds__(256) void k_gather(const T *__restrict__ logits, int V, int blank,
-                                                const SampleDesc *__restrict__ desc,
-                                                const ChunkDesc *__restrict__ chunks,
+template <typename T, bool DIAG, typename Src>
+__global__ __launch_bounds__(256) void k_gather(const T *__restrict__ logits, int V, int blank, Src src,
                                                 const int32_t *__restrict__ targets, int S,
-                                                float4 *__restrict__ node, float2 *__restrict__ prob,
-                                                int *__restrict__ mode, uint32_t *status) {
-    const ChunkDesc c = chunks[blockIdx.x];
-    const SampleDesc d = desc[c.sample];
+                                                float4 *__restrict__ node, float2 *__restrict__ prob) {
+    __shared__ uint32_t wg_flags;
+    const RowWork wk = row_work<DIAG>(src, &wg_flags);
+    const ChunkDesc &c = wk.c;
+    const SampleDesc &d = wk.d;
     const int U1 = d.U + 1;
     for (int r = threadIdx.x; r < c.count; r += blockDim.x) {
         int t, u;
@@ -575,11 +690,12 @@ __global__ __launch_bounds__(256) void k_gather(const T *__restrict__ logits, in
             if (t == 0 || t == d.T - 1) fill_columns(d, t, u, 0, 1, node, prob);
         }
         const T *p = logits + row_of(d, t, u) * (int64_t)V;
-        const int y = read_label(d, u, V, blank, targets, S, status);
+        const int y = read_label(d, u, V, blank, targets, S, wk.status_word);
         const float lpb = Elem<T>::load1(p + blank);
         const float lpy = (y < 0) ? kNegInf : Elem<T>::load1(p + y);
-        emit_node(d, t, u, 0.f, 0.f, lpb, lpy, node, prob, mode);
+        emit_node(d, t, u, 0.f, 0.f, lpb, lpy, node, prob, wk.mode_word);
     }
+    row_work_end(src, &wg_flags);
 }
 
 // ----------------------------------------------------- K2: alpha/beta sweeps
@@ -643,10 +759,11 @@ struct ProbDomain {
     __device__ static double combine(double a, double b) { return a + b; }
     __device__ static double edge(double a, float w) { return a * (double)w; }
     // voff[k]: byte offset of column k of the lane's group (even k used).
-    template <int K> __device__ static void load(Wts<K> &w, Rsrc r, const uint32_t (&voff)[K]) {
+    template <int K>
+    __device__ static void load(Wts<K> &w, Rsrc r, const uint32_t (&voff)[K], uint32_t soff) {
 #pragma unroll
         for (int h = 0; h < K / 2; ++h)
-            w.q[h] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff[2 * h], 0, 0));
+            w.q[h] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff[2 * h], soff, 0));
     }
 };
 struct LogDomain {
@@ -663,11 +780,12 @@ struct LogDomain {
     __device__ static double edge(double a, float lpv) { return a + (double)lpv * kLog2eD; }
     // The first eight bytes of each column's slot (offsets clamped to column
     // U by the caller: a log-prob of 0 would not be impossible).
-    template <int K> __device__ static void load(Wts<K> &w, Rsrc r, const uint32_t (&voff)[K]) {
+    template <int K>
+    __device__ static void load(Wts<K> &w, Rsrc r, const uint32_t (&voff)[K], uint32_t soff) {
 #pragma unroll
         for (int h = 0; h < K / 2; ++h) {
-            const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, voff[2 * h], 0, 0);
-            const u32x2 y = __builtin_amdgcn_raw_buffer_load_b64(r, voff[2 * h + 1], 0, 0);
+            const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, voff[2 * h], soff, 0);
+            const u32x2 y = __builtin_amdgcn_raw_buffer_load_b64(r, voff[2 * h + 1], soff, 0);
             w.q[h] = make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(y[0]),
                                  __uint_as_float(y[1]));
         }
@@ -708,20 +826,28 @@ template <int K, int G, int PF> struct Ring {
 
 // Where a sweep reads and writes: the sample's first weight slot and first
 // output slot, the byte sizes of one diagonal of each, and the lane's byte
-// offsets inside a diagonal.
+// offsets inside a diagonal.  Diagonal n is addressed by a scalar offset
+// from the sample's base, so one diagonal costs two or three scalar
+// instructions instead of a 64-bit base per access.  The range check of a
+// buffer access covers the scalar offset as well: a weight resource whose
+// record count ends with diagonal n (offset n * w_bytes plus one diagonal)
+// reads zero for the columns past U, as a resource based at the diagonal
+// would.  The output resource spans the sample's nd diagonals.  Offsets are
+// 32-bit: the host keeps a sample's tables below 2^31 bytes.
 template <typename D, int K, int G> struct SweepIO {
     const char *w;
-    char *out;
+    Rsrc rout;
     uint32_t w_bytes;    // U1 * kSlot
     uint32_t out_bytes;  // U1p * 8
     uint32_t win[G][K];
     uint32_t wout[G];
 
-    __device__ SweepIO(const char *w_, double *out_, int U) : w(w_), out(reinterpret_cast<char *>(out_)) {
+    __device__ SweepIO(const char *w_, double *out_, int U, int nd) : w(w_) {
         const uint32_t lane = threadIdx.x & 63;
         const uint32_t U1 = (uint32_t)U + 1;
         w_bytes = U1 * D::kSlot;
         out_bytes = 64u * K * G * 8u;
+        rout = buffer_at(out_, (uint32_t)nd * out_bytes);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const uint32_t c = 64u * K * g + K * lane;
@@ -731,15 +857,17 @@ template <typename D, int K, int G> struct SweepIO {
             wout[g] = c * 8u;
         }
     }
-    // n >= 0 at every call: an unsigned 32 x 32 -> 64-bit product needs no
-    // sign extension (fewer scalar instructions per diagonal).
+    // 0 <= n < nd at every call (n is uniform; readfirstlane keeps it in a
+    // scalar register where the clamp would otherwise be formed with a
+    // vector instruction).
     __device__ void load(Wts<K> (&r)[G], int n) const {
-        const Rsrc rs = buffer_at(w + (uint64_t)(uint32_t)n * w_bytes, w_bytes);
+        const uint32_t off = (uint32_t)__builtin_amdgcn_readfirstlane(n) * w_bytes;
+        const Rsrc rs = buffer_at(w, off + w_bytes);
 #pragma unroll
-        for (int g = 0; g < G; ++g) D::template load<K>(r[g], rs, win[g]);
+        for (int g = 0; g < G; ++g) D::template load<K>(r[g], rs, win[g], off);
     }
     __device__ void store(int n, const double (&a)[G][K]) const {
-        const Rsrc rs = buffer_at(out + (uint64_t)(uint32_t)n * out_bytes, out_bytes);
+        const uint32_t off = (uint32_t)n * out_bytes;
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -747,7 +875,7 @@ template <typename D, int K, int G> struct SweepIO {
                 const u32x4 v = {(uint32_t)__double2loint(a[g][2 * h]), (uint32_t)__double2hiint(a[g][2 * h]),
                                  (uint32_t)__double2loint(a[g][2 * h + 1]),
                                  (uint32_t)__double2hiint(a[g][2 * h + 1])};
-                __builtin_amdgcn_raw_buffer_store_b128(v, rs, wout[g] + 16u * h, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(v, rout, wout[g] + 16u * h, off, 0);
             }
     }
 };
@@ -839,7 +967,7 @@ __device__ void sweep_forward(const SampleDesc &d, const char *__restrict__ w, d
         for (int k = 0; k < K; ++k) a[g][k] = (g == 0 && k == 0 && lane0) ? D::one() : D::zero();
     int E = 0;
     if (lane == 0) eout[0] = 0;
-    const SweepIO<D, K, G> io(w, out, U);
+    const SweepIO<D, K, G> io(w, out, U, nd);
     Ring<K, G, PF> ra, rb;
     load_block<D, K, G, PF>(ra, io, 0, 1, nd);
     int n0 = 0;
@@ -897,7 +1025,7 @@ __device__ void sweep_backward(const SampleDesc &d, const char *__restrict__ w, 
         for (int k = 0; k < K; ++k) b[g][k] = (64 * K * g + K * lane + k == U) ? D::one() : D::zero();
     int E = 0;
     if (lane == 0) eout[0] = 0;
-    const SweepIO<D, K, G> io(w, out, U);
+    const SweepIO<D, K, G> io(w, out, U, nd);
     Ring<K, G, PF> ra, rb;
     load_block<D, K, G, PF>(ra, io, nd - 1, -1, nd);
     int n0 = nd - 1;
@@ -932,6 +1060,23 @@ __device__ void run_sweep(const SampleDesc &d, bool backward, bool log_mode, con
     }
 }
 
+// The sweep of one direction of sample d, at its lattice width: PF
+// diagonals per prefetch block.  A ring holds G*K/2*PF 16-byte loads (the
+// log domain: twice as many 8-byte ones); when a ring is first read, its
+// loads, the other ring's and about one block of stores are in flight,
+// within the 63 vector memory operations the wait counter tracks.
+__device__ __forceinline__ void sweep_sample(const SampleDesc &d, bool bw, bool lm, const float4 *node,
+                                             const float2 *prob, double *alpha, double *beta, int *ealpha,
+                                             int *ebeta, double *z) {
+    switch (d.U1p) {
+    case 128: run_sweep<2, 1, 16>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z); break;
+    case 256: run_sweep<4, 1, 8>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z); break;
+    case 512: run_sweep<4, 2, 4>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z); break;
+    case 768: run_sweep<4, 3, 3>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z); break;
+    default: run_sweep<4, 4, 2>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z); break;
+    }
+}
+
 // One wave per workgroup: workgroup 2k runs the forward sweep and 2k+1 the
 // backward sweep of the k-th sample in cost order, so the two sweeps of a
 // sample run on different compute units and do not share one unit's vector
@@ -951,17 +1096,7 @@ __global__ __launch_bounds__(64) void k_alpha_beta(const SampleDesc *__restrict_
     const bool bw = (blockIdx.x & 1) != 0;
     const bool lm = md != 0;
     double *z = bw ? &log2z[d.index] : &log2z[B + d.index];
-    // PF: diagonals per prefetch block.  A ring holds G*K/2*PF 16-byte loads
-    // (the log domain: twice as many 8-byte ones); when a ring is first read,
-    // its loads, the other ring's and about one block of stores are in
-    // flight, within the 63 vector memory operations the wait counter tracks.
-    switch (d.U1p) {
-    case 128: run_sweep<2, 1, 16>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z); break;
-    case 256: run_sweep<4, 1, 8>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z); break;
-    case 512: run_sweep<4, 2, 4>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z); break;
-    case 768: run_sweep<4, 3, 3>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z); break;
-    default: run_sweep<4, 4, 2>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z); break;
-    }
+    sweep_sample(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z);
     if (bw && threadIdx.x == 0) loss[d.index] = (float)(-log2z[d.index] * kLn2D);
 }
 
@@ -988,6 +1123,22 @@ __device__ __forceinline__ double wave_sum_d(double v) {
     return v;
 }
 
+// Check diagonal j (of kCheckDiagonals) of sample d by one wave: true when
+// the sum of alpha * beta over it is off P(y|x) (2^lz).
+__device__ __forceinline__ bool check_diagonal(const SampleDesc &d, int j, const double *__restrict__ alpha,
+                                               const double *__restrict__ beta, const int *__restrict__ ealpha,
+                                               const int *__restrict__ ebeta, double lz) {
+    const int lane = threadIdx.x & 63;
+    const int T = d.T, U = d.U, nd = T + U;
+    const int n = (j + 1 < kCheckDiagonals) ? (int)(((int64_t)(2 * j + 1) * nd) / (2 * kCheckDiagonals)) : nd - 1;
+    const int64_t q = d.ab_off + (int64_t)n * d.U1p;
+    double s = 0.0;
+    for (int u = max(0, n - T + 1) + lane; u <= min(n, U); u += 64) s += alpha[q + u] * beta[q + u];
+    s = wave_sum_d(s);
+    const double ls = log2_d(s) + (double)(ealpha[d.diag_off + ((n + 1) >> 3)] + ebeta[d.diag_off + ((nd - n) >> 3)]);
+    return !(lz > kNegInfD) || !(s > 0.0) || !(fabs(ls - lz) <= 4e-6);
+}
+
 __global__ __launch_bounds__(64) void k_check_ab(const SampleDesc *__restrict__ desc, int *__restrict__ mode,
                                                  const double *__restrict__ alpha, const double *__restrict__ beta,
                                                  const int *__restrict__ ealpha, const int *__restrict__ ebeta,
@@ -995,17 +1146,94 @@ __global__ __launch_bounds__(64) void k_check_ab(const SampleDesc *__restrict__ 
     const SampleDesc d = desc[blockIdx.x / kCheckDiagonals];
     const int j = blockIdx.x % kCheckDiagonals;
     if (mode[d.index] != 0) return;  // already in the log domain, or marked
-    const int lane = threadIdx.x;
-    const int T = d.T, U = d.U, nd = T + U;
-    const double lz = log2z[d.index];
-    const int n = (j + 1 < kCheckDiagonals) ? (int)(((int64_t)(2 * j + 1) * nd) / (2 * kCheckDiagonals)) : nd - 1;
-    const int64_t q = d.ab_off + (int64_t)n * d.U1p;
-    double s = 0.0;
-    for (int u = max(0, n - T + 1) + lane; u <= min(n, U); u += 64) s += alpha[q + u] * beta[q + u];
-    s = wave_sum_d(s);
-    const double ls = log2_d(s) + (double)(ealpha[d.diag_off + ((n + 1) >> 3)] + ebeta[d.diag_off + ((nd - n) >> 3)]);
-    const bool bad = !(lz > kNegInfD) || !(s > 0.0) || !(fabs(ls - lz) <= 4e-6);
-    if (bad && lane == 0) atomicOr(&mode[d.index], kModeRerun);
+    const bool bad = check_diagonal(d, j, alpha, beta, ealpha, ebeta, log2z[d.index]);
+    if (bad && threadIdx.x == 0) atomicOr(&mode[d.index], kModeRerun);
+}
+
+// Batches below 64 K rows: one two-wave workgroup per sample (wave 0 the
+// forward sweep, wave 1 the backward sweep) that also takes the sample's
+// mode from the row pass's flag words, checks its probability-domain
+// sweeps on the kCheckDiagonals diagonals (eight per wave) and reruns both
+// in the log domain when a check fails: one launch instead of three, the
+// workgroup barrier standing in for the kernel boundaries.  Writes the
+// sample's mode word for the gradient pass and its loss.
+__global__ __launch_bounds__(128) void k_ab_small(const SampleDesc *__restrict__ desc,
+                                                  const int32_t *__restrict__ order, int B, int rpc,
+                                                  const uint32_t *__restrict__ cflags,
+                                                  uint32_t *__restrict__ sflags, int *__restrict__ mode,
+                                                  const float4 *__restrict__ node, const float2 *__restrict__ prob,
+                                                  double *__restrict__ alpha, double *__restrict__ beta,
+                                                  int *__restrict__ ealpha, int *__restrict__ ebeta,
+                                                  double *__restrict__ log2z, float *__restrict__ loss) {
+    __shared__ int bad_any;
+    const SampleDesc d = desc[order[blockIdx.x]];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool bw = wave == 1;
+    if (threadIdx.x == 0) bad_any = 0;
+    // the OR of the sample's chunk flags, four loads per lane in flight
+    const int nch = (int)(((int64_t)d.T * (d.U + 1) + rpc - 1) / rpc);
+    const uint32_t *cf = cflags + d.chunk0;
+    uint32_t f = 0;
+    for (int j = lane; j < nch; j += 256) {
+        uint32_t g[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) g[q] = (j + 64 * q < nch) ? cf[j + 64 * q] : 0u;
+        f |= g[0] | g[1] | g[2] | g[3];
+    }
+    const int md0 = __any((f & (uint32_t)kModeLog) != 0u) ? kModeLog : 0;
+    if (threadIdx.x == 0)
+        sflags[d.index] = __any((f & (uint32_t)RNNT_DEV_BAD_TARGET) != 0u) ? (uint32_t)RNNT_DEV_BAD_TARGET : 0u;
+    double *z = bw ? &log2z[d.index] : &log2z[B + d.index];
+    sweep_sample(d, bw, md0 != 0, node, prob, alpha, beta, ealpha, ebeta, z);
+    __syncthreads();
+    int md = md0;
+    if (md == 0) {
+        // the check of diagonals wave, wave+2, ..., all eight summed together
+        // so that their loads are in flight at once
+        constexpr int NQ = kCheckDiagonals / 2;
+        const int T = d.T, U = d.U, nd = T + U;
+        int n[NQ];
+        double s[NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int j = wave + 2 * q;
+            n[q] = (j + 1 < kCheckDiagonals) ? (int)(((int64_t)(2 * j + 1) * nd) / (2 * kCheckDiagonals)) : nd - 1;
+            s[q] = 0.0;
+        }
+        for (int u = lane; u <= U; u += 64) {
+            double a[NQ], b[NQ];
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const bool in = u >= n[q] - T + 1 && u <= n[q];
+                const int64_t at = d.ab_off + (int64_t)n[q] * d.U1p + u;
+                a[q] = in ? alpha[at] : 0.0;
+                b[q] = in ? beta[at] : 0.0;
+            }
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) s[q] += a[q] * b[q];
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1)
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) s[q] += __shfl_xor(s[q], off, 64);
+        const double lz = log2z[d.index];
+        bool bad = !(lz > kNegInfD);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const double ls =
+                log2_d(s[q]) + (double)(ealpha[d.diag_off + ((n[q] + 1) >> 3)] + ebeta[d.diag_off + ((nd - n[q]) >> 3)]);
+            bad = bad || !(s[q] > 0.0) || !(fabs(ls - lz) <= 4e-6);
+        }
+        if (bad && lane == 0) atomicOr(&bad_any, 1);
+        __syncthreads();
+        if (bad_any) {
+            md = kModeRerun;
+            sweep_sample(d, bw, true, node, prob, alpha, beta, ealpha, ebeta, z);
+        }
+    }
+    if (threadIdx.x == 0) mode[d.index] = md;
+    if (bw && lane == 0) loss[d.index] = (float)(-log2z[d.index] * kLn2D);
 }
 
 // --------------------------------------------------------------- reduction
@@ -1015,8 +1243,12 @@ __global__ __launch_bounds__(64) void k_check_ab(const SampleDesc *__restrict__ 
 // final status word (every earlier kernel's bits and this one's) is copied
 // there.  Run by the first workgroup of the gradient launch, or on its own
 // (k_reduce) when there is no gradient pass.
+// With sflags (a small batch: each sample's status bits, from the row
+// pass's per-chunk flag words) the status word is written whole, their OR
+// and this one's bits, instead of adding bits to a word k_plan cleared.
 __device__ void reduce_losses(const float *__restrict__ loss, const double *__restrict__ log2z, int B, int mean,
-                              float *__restrict__ out, uint32_t *status, uint32_t *status_out) {
+                              float *__restrict__ out, uint32_t *status, uint32_t *status_out,
+                              const uint32_t *__restrict__ sflags) {
     double s = 0.0;
     bool agree = true;
     for (int i = threadIdx.x; i < B; i += 64) {
@@ -1025,11 +1257,21 @@ __device__ void reduce_losses(const float *__restrict__ loss, const double *__re
         const double la = -log2z[B + i] * kLn2D;
         agree = agree && ((la == lb) || (fabs(la - lb) <= 1e-4 * fmax(1.0, fabs(lb))));
     }
+    uint32_t f = 0;
+    if (sflags)
+        for (int i = threadIdx.x; i < B; i += 64) f |= sflags[i];
+    const uint32_t bad_label = __any((f & (uint32_t)RNNT_DEV_BAD_TARGET) != 0u) ? (uint32_t)RNNT_DEV_BAD_TARGET : 0u;
     const uint32_t bit = __any(!agree) ? (uint32_t)RNNT_DEV_LOSS_MISMATCH : 0u;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
     if (threadIdx.x == 0) {
-        const uint32_t word = atomicOr(status, bit) | bit;
+        uint32_t word;
+        if (sflags) {
+            word = bad_label | bit;
+            *status = word;
+        } else {
+            word = atomicOr(status, bit) | bit;
+        }
         if (status_out) *status_out = word;
         if (out) out[0] = (float)(mean ? s / (double)B : s);
     }
@@ -1115,6 +1357,7 @@ struct ReduceArgs {
     float *out;
     uint32_t *status;
     uint32_t *status_out;
+    const uint32_t *sflags;  // small batches: each sample's status bits, else null
     int B, mean, on;
 };
 
@@ -1215,7 +1458,7 @@ __global__ __launch_bounds__(64) void k_grad_rows(const T *logits, T *grad, int 
     constexpr int VEC = Raw<T>::kVec;
     constexpr int NV = 4;
     if (red.on && blockIdx.x == 0)
-        reduce_losses(red.loss, log2z, red.B, red.mean, red.out, red.status, red.status_out);
+        reduce_losses(red.loss, log2z, red.B, red.mean, red.out, red.status, red.status_out, red.sflags);
     const int bpc = blocks_per_chunk;
     const int64_t b = block_base + blockIdx.x;
     const ChunkDesc c = chunks[n_chunks - 1 - (int)(b / bpc)];
@@ -1251,7 +1494,7 @@ template <typename T, int VEC, int G, bool FUSED>
 __global__ __launch_bounds__(256) void k_grad_narrow(const T *logits, T *grad, RNNT_GRAD_PARAMS) {
     constexpr int RPW = 64 / G;
     if (red.on && blockIdx.x == 0 && threadIdx.x < 64)
-        reduce_losses(red.loss, log2z, red.B, red.mean, red.out, red.status, red.status_out);
+        reduce_losses(red.loss, log2z, red.B, red.mean, red.out, red.status, red.status_out, red.sflags);
     const ChunkDesc c = chunks[n_chunks - 1 - blockIdx.x];
     const SampleDesc d = desc[c.sample];
     const SampleTerms st{log2z[d.index], mode[d.index] != 0};
@@ -1270,15 +1513,27 @@ __global__ __launch_bounds__(256) void k_grad_narrow(const T *logits, T *grad, R
         const int t = lr / U1;
         const int u = lr - t * U1;
         const int64_t row = row_of(d, t, u);
+        const T *src = logits + row * (int64_t)V;
+        // the lane's first vector of the row is loaded before the row's terms,
+        // whose loads it does not depend on
+        float x0[VEC] = {};
+        if constexpr (FUSED)
+            if (sub < nvec) load_n<T, VEC>(src + (int64_t)sub * VEC, x0);
         const RowTerms rt = row_terms(d, st, t, u, node, alpha, beta, ealpha, ebeta, log2_scale, scale, fastemit,
                                       scale_y, FUSED, V, blank, targets, S);
-        const T *src = logits + row * (int64_t)V;
         T *dst = grad + row * (int64_t)V;
         const int vb = blank / VEC, vy = rt.y >= 0 ? rt.y / VEC : -1;
         const int eb = blank - vb * VEC, ey = rt.y - vy * VEC;
         for (int i = sub; i < nvec; i += G) {
             float x[VEC];
-            if constexpr (FUSED) load_n<T, VEC>(src + (int64_t)i * VEC, x);
+            if constexpr (FUSED) {
+                if (i == sub) {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) x[e] = x0[e];
+                } else {
+                    load_n<T, VEC>(src + (int64_t)i * VEC, x);
+                }
+            }
             float gv[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
@@ -1295,8 +1550,8 @@ __global__ __launch_bounds__(256) void k_grad_narrow(const T *logits, T *grad, R
 
 __global__ __launch_bounds__(64) void k_reduce(const float *__restrict__ loss, const double *__restrict__ log2z,
                                                int B, int mean, float *__restrict__ out, uint32_t *status,
-                                               uint32_t *status_out) {
-    reduce_losses(loss, log2z, B, mean, out, status, status_out);
+                                               uint32_t *status_out, const uint32_t *__restrict__ sflags) {
+    reduce_losses(loss, log2z, B, mean, out, status, status_out, sflags);
 }
 
 // Upstream-gradient scaling of an already written gradient: each workgroup
@@ -1422,7 +1677,10 @@ hipError_t launch_plan(const LaunchArgs &a, const PlanArgs *pa, hipStream_t stre
     return hipGetLastError();
 }
 
-hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream) {
+// The row pass with its work source: the chunk table (TableSrc), or for a
+// small batch the descriptors in `pa` (ArgSrc).
+template <typename Src>
+hipError_t launch_rowstats_with(const LaunchArgs &a, const Src &src, hipStream_t stream) {
     const dim3 grid(a.lay.n_chunks), block(256);
     // one row per wave: the chunks are walked in diagonal order
     const bool diag = a.geom.stream_parts > 0;
@@ -1430,9 +1688,8 @@ hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream) {
         auto go = [&](auto tag, auto dtag) {
             using T = decltype(tag);
             constexpr bool D = decltype(dtag)::value;
-            hipLaunchKernelGGL((k_gather<T, D>), grid, block, 0, stream, static_cast<const T *>(a.logits), a.V,
-                               a.blank, WS(const SampleDesc *, desc), WS(const ChunkDesc *, chunks), a.targets, a.S,
-                               WS(float4 *, node), WS(float2 *, prob), WS(int *, mode), WS(uint32_t *, status));
+            hipLaunchKernelGGL((k_gather<T, D, Src>), grid, block, 0, stream, static_cast<const T *>(a.logits), a.V,
+                               a.blank, src, a.targets, a.S, WS(float4 *, node), WS(float2 *, prob));
             return hipGetLastError();
         };
         if (a.esize == 4)
@@ -1442,11 +1699,10 @@ hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream) {
     if (a.geom.stream_parts > 0) {
         auto go = [&](auto tag) {
             using T = decltype(tag);
-            auto kern = a.geom.stream_parts == 1 ? k_rowstats_stream<T, 8> : k_rowstats_stream<T, 16>;
+            auto kern = a.geom.stream_parts == 1 ? k_rowstats_stream<T, 8, Src> : k_rowstats_stream<T, 16, Src>;
             const dim3 wblock(a.geom.stream_parts == 1 ? 512 : 1024);
-            hipLaunchKernelGGL(kern, grid, wblock, 0, stream, static_cast<const T *>(a.logits), a.V,
-                               a.blank, WS(const SampleDesc *, desc), WS(const ChunkDesc *, chunks), a.targets, a.S,
-                               WS(float4 *, node), WS(float2 *, prob), WS(int *, mode), WS(uint32_t *, status));
+            hipLaunchKernelGGL(kern, grid, wblock, 0, stream, static_cast<const T *>(a.logits), a.V, a.blank, src,
+                               a.targets, a.S, WS(float4 *, node), WS(float2 *, prob));
             return hipGetLastError();
         };
         return a.esize == 4 ? go(float{}) : go(_Float16{});
@@ -1454,18 +1710,40 @@ hipError_t launch_rowstats(const LaunchArgs &a, hipStream_t stream) {
     return with_narrow(a.esize, a.geom.vec, a.geom.lanes_per_row, [&](auto tag) {
         using Tg = decltype(tag);
         using T = typename Tg::type;
-        hipLaunchKernelGGL((k_rowstats_narrow<T, Tg::vec, Tg::n>), grid, block, 0, stream,
-                           static_cast<const T *>(a.logits), a.V, a.blank, WS(const SampleDesc *, desc),
-                           WS(const ChunkDesc *, chunks), a.targets, a.S, WS(float4 *, node), WS(float2 *, prob),
-                           WS(int *, mode), WS(uint32_t *, status));
+        hipLaunchKernelGGL((k_rowstats_narrow<T, Tg::vec, Tg::n, Src>), grid, block, 0, stream,
+                           static_cast<const T *>(a.logits), a.V, a.blank, src, a.targets, a.S, WS(float4 *, node),
+                           WS(float2 *, prob));
         return hipGetLastError();
     });
+}
+
+hipError_t launch_rowstats(const LaunchArgs &a, const PlanArgs *pa, hipStream_t stream) {
+    if (a.small) {
+        ArgSrc src;
+        src.pa = *pa;
+        src.rpc = a.lay.rows_per_chunk;
+        src.ws_chunks = WS(ChunkDesc *, chunks);
+        src.ws_desc = WS(SampleDesc *, desc);
+        src.ws_order = WS(int32_t *, order);
+        src.cflags = WS(uint32_t *, cflags);
+        return launch_rowstats_with(a, src, stream);
+    }
+    const TableSrc src{WS(const SampleDesc *, desc), WS(const ChunkDesc *, chunks), WS(int *, mode),
+                       WS(uint32_t *, status)};
+    return launch_rowstats_with(a, src, stream);
 }
 
 // The recursions, the forward-backward check of the probability-domain
 // samples, and the log-domain rerun of the samples the check marked (a
 // launch whose workgroups exit at once when none is).
 hipError_t launch_alpha_beta(const LaunchArgs &a, hipStream_t stream) {
+    if (a.small) {
+        hipLaunchKernelGGL(k_ab_small, dim3(a.B), dim3(128), 0, stream, WS(const SampleDesc *, desc),
+                           WS(const int32_t *, order), a.B, a.lay.rows_per_chunk, WS(const uint32_t *, cflags),
+                           WS(uint32_t *, sflags), WS(int *, mode), WS(const float4 *, node), WS(const float2 *, prob), WS(double *, alpha),
+                           WS(double *, beta), WS(int *, ealpha), WS(int *, ebeta), WS(double *, log2z), a.loss);
+        return hipGetLastError();
+    }
     for (int rerun = 0; rerun < 2; ++rerun) {
         if (rerun) {
             hipLaunchKernelGGL(k_check_ab, dim3(kCheckDiagonals * a.B), dim3(64), 0, stream, WS(const SampleDesc *, desc),
@@ -1488,6 +1766,7 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
     g.red.out = (a.reduction != RNNT_REDUCTION_NONE) ? a.loss_reduced : nullptr;
     g.red.status = WS(uint32_t *, status);
     g.red.status_out = a.status_out;
+    g.red.sflags = a.small ? WS(const uint32_t *, sflags) : nullptr;
     g.red.B = a.B;
     g.red.mean = a.reduction == RNNT_REDUCTION_MEAN;
     g.red.on = 1;
@@ -1557,7 +1836,8 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
 hipError_t launch_reduce(const LaunchArgs &a, hipStream_t stream) {
     float *out = (a.reduction != RNNT_REDUCTION_NONE) ? a.loss_reduced : nullptr;
     hipLaunchKernelGGL(k_reduce, dim3(1), dim3(64), 0, stream, a.loss, WS(const double *, log2z), a.B,
-                       a.reduction == RNNT_REDUCTION_MEAN, out, WS(uint32_t *, status), a.status_out);
+                       a.reduction == RNNT_REDUCTION_MEAN, out, WS(uint32_t *, status), a.status_out,
+                       a.small ? WS(const uint32_t *, sflags) : nullptr);
     return hipGetLastError();
 }
 
@@ -2510,7 +2790,7 @@ hipError_t launch_mb_grad(const MbArgs &a, hipStream_t stream) {
 hipError_t launch_mb_reduce(const MbArgs &a, hipStream_t stream) {
     float *out = (a.reduction != RNNT_REDUCTION_NONE) ? a.loss_reduced : nullptr;
     hipLaunchKernelGGL(k_reduce, dim3(1), dim3(64), 0, stream, a.loss, MBWS(const double *, log2z), a.B,
-                       a.reduction == RNNT_REDUCTION_MEAN, out, MBWS(uint32_t *, status), nullptr);
+                       a.reduction == RNNT_REDUCTION_MEAN, out, MBWS(uint32_t *, status), nullptr, nullptr);
     return hipGetLastError();
 }
 

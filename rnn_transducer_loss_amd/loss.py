@@ -29,6 +29,18 @@ def _dtype_code(dt: torch.dtype) -> int:
     return _DTYPES[dt]
 
 
+# The current HIP stream of a device as a raw handle (torch's own accessor
+# where it has one: it skips building a Stream object on every call).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream_handle(dev: torch.device) -> int:
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    if _raw_stream is not None:
+        return _raw_stream(idx)
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
 def _prepare(logits: torch.Tensor, targets: torch.Tensor):
     if not isinstance(logits, torch.Tensor) or logits.dim() not in (2, 4):
         raise ValueError("logits must be a packed 2-D (sum_i T_i*(U_i+1), V) or a padded 4-D "
@@ -41,8 +53,9 @@ def _prepare(logits: torch.Tensor, targets: torch.Tensor):
         targets = targets.unsqueeze(0)
     if targets.dim() != 2:
         raise ValueError("targets must be a 2-D (B, S) tensor")
-    tg = targets.to(device=logits.device, dtype=torch.int32).contiguous()
-    return tg
+    if targets.dtype == torch.int32 and targets.device == logits.device and targets.is_contiguous():
+        return targets
+    return targets.to(device=logits.device, dtype=torch.int32).contiguous()
 
 
 class _on_device:
@@ -120,7 +133,7 @@ def rnnt_loss_fused(logits: torch.Tensor, targets: torch.Tensor, logit_lengths, 
     else:
         grad = None
     with _on_device(dev):
-        stream = torch.cuda.current_stream(dev).cuda_stream
+        stream = _stream_handle(dev)
         tgp = tg.data_ptr() if tg.numel() else 0
         redp = loss_reduced.data_ptr() if reduction != "none" else 0
         gp = grad.data_ptr() if grad is not None else 0
@@ -138,7 +151,7 @@ def rnnt_loss_fused(logits: torch.Tensor, targets: torch.Tensor, logit_lengths, 
 def device_flags(workspace: torch.Tensor) -> int:
     """RNNT_DEV_* bits of the last call on ``workspace`` (synchronises the current stream)."""
     with torch.cuda.device(workspace.device):
-        return _lib.device_flags(workspace.data_ptr(), torch.cuda.current_stream(workspace.device).cuda_stream)
+        return _lib.device_flags(workspace.data_ptr(), _stream_handle(workspace.device))
 
 
 class _RNNTLossFunction(torch.autograd.Function):
@@ -167,7 +180,7 @@ class _RNNTLossFunction(torch.autograd.Function):
         grad, ws = ctx.saved_tensors
         scale = grad_out.detach().to(device=grad.device, dtype=torch.float32).contiguous().reshape(-1)
         with torch.cuda.device(grad.device):
-            stream = torch.cuda.current_stream(grad.device).cuda_stream
+            stream = _stream_handle(grad.device)
             if len(shape) == 4:
                 _lib.grad_scale_padded(grad.data_ptr(), _dtype_code(dtype), shape[1], shape[2], shape[3], T, U,
                                        scale.data_ptr(), reduction == "none", ws.data_ptr(), ws.numel(), stream)
@@ -268,7 +281,7 @@ def rnnt_multiblank_fused(logits: torch.Tensor, targets: torch.Tensor, logit_len
     else:
         grad = None
     with torch.cuda.device(dev):
-        stream = torch.cuda.current_stream(dev).cuda_stream
+        stream = _stream_handle(dev)
         tgp = tg.data_ptr() if tg.numel() else 0
         redp = loss_reduced.data_ptr() if reduction != "none" else 0
         gp = grad.data_ptr() if grad is not None else 0
@@ -312,7 +325,7 @@ class _MultiblankFunction(torch.autograd.Function):
         grad, ws = ctx.saved_tensors
         scale = grad_out.detach().to(device=grad.device, dtype=torch.float32).contiguous().reshape(-1)
         with torch.cuda.device(grad.device):
-            stream = torch.cuda.current_stream(grad.device).cuda_stream
+            stream = _stream_handle(grad.device)
             if len(shape) == 4:
                 _lib.grad_scale_multiblank_padded(grad.data_ptr(), _dtype_code(dtype), shape[1], shape[2], shape[3],
                                                   T, U, scale.data_ptr(), reduction == "none", ws.data_ptr(),

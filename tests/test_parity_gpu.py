@@ -786,6 +786,49 @@ def test_peaked_blank_lattices(rl, gap, jitter):
     check_against_oracle(w, loss, grad, "none")
 
 
+@pytest.mark.parametrize("size", ["small", "large"])
+@pytest.mark.parametrize("reduction", ["none", "sum"])
+def test_launch_paths_on_mixed_batches(rl, size, reduction):
+    """Batches below 64512 lattice rows take three launches (the row pass finds its chunks from descriptors passed
+    as kernel arguments and reports its flags per chunk; one workgroup per sample runs both recursions, their
+    check and the rerun), larger ones six.  On both sides of that line, one batch mixes an ordinary sample, one
+    whose blank logit is 20 nats above every label (its probability-domain sweeps lose the alignment mass, the
+    check sends it to the log domain), one with logits of spread 40 (log-probs beyond -80: the row pass sends it
+    to the log domain) and one with a label outside [0, V) (no alignment, the status word flagged).  Every loss,
+    the whole gradient and the reduction against the oracle."""
+    scale = 1 if size == "small" else 6
+    Ts = [120 * scale, 100 * scale, 80 * scale, 60 * scale]
+    Us, V = [30, 60, 20, 10], 16
+    w = _custom(Ts, Us, V, std=1.0, blank=0, reduction=reduction, seed=77 + scale)
+    rows = sum(t * (u + 1) for t, u in zip(Ts, Us))
+    assert (rows < 64512) == (size == "small")
+    x = w.logits.float().cpu().numpy()
+    peaked = x[w.rows(1)]
+    peaked[:] = 0.25 * np.random.default_rng(5).standard_normal(peaked.shape).astype(np.float32)
+    peaked[:, 0] += 30.0
+    x[w.rows(2)] *= 40.0
+    w.logits = torch.from_numpy(x).to("cuda")
+    tg = w.targets.copy()
+    tg[3, 4] = V + 3
+    w.targets = tg
+    loss, red, grad, ws = rl.rnnt_loss_fused(w.logits, torch.from_numpy(tg).to("cuda"), w.logit_lengths,
+                                             w.target_lengths, blank=0, reduction=reduction)
+    flags = rl.device_flags(ws)
+    assert flags == 2
+    # the per-sample mode words (int32 at byte 256 of the workspace): 0 probability domain, 1 log domain from the
+    # row pass, 2 rerun after a failed check (the peaked sample, and the one without an alignment)
+    mode = ws[256:256 + 4 * w.B].view(torch.int32).tolist()
+    assert mode == [0, 2, 1, 2], mode
+
+    def ref(i):
+        T, U = int(w.logit_lengths[i]), int(w.target_lengths[i])
+        return oracle.sample(x[w.rows(i)], T, U, w.targets[i], 0, True, -1.0, allow_bad_targets=True)
+    check_masked(w, loss, grad, ref)
+    assert math.isinf(loss[3].item()) and all(math.isfinite(loss[i].item()) for i in range(3))
+    if reduction == "sum":
+        assert math.isinf(red.item())
+
+
 @pytest.mark.parametrize("Ts,Us,V,blank,std,clamp,reduction,seed", [
     ([131], [537], 2, 1, 8.0, -1.0, "none", 5091),
     ([299, 247, 131], [152, 121, 472], 8, 7, 2.0, 0.1, "sum", 5113),
