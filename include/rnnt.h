@@ -167,8 +167,9 @@ rnnt_status rnnt_loss_fused_workspace_size(int32_t B, int32_t V, int64_t N, rnnt
  * Returns RNNT_INVALID_VALUE for a NULL required pointer, bad dtype or
  * reduction, V < 1, B < 1, blank out of range, fastemit_lambda negative or not
  * finite, T_i < 1, U_i < 0, U_i > 1023, U_i > S, a sample with
- * (T_i + U_i) * max(8 * U1p_i, 16 * (U_i + 1)) >= 2^31 (U1p_i = 128 for
- * U_i < 128, else U_i + 1 rounded up to a multiple of 256: the recursions
+ * (T_i + U_i) * max(8 * U1p_i, 16 * (U_i + 1)) >= 2^31 (U1p_i = 64 for
+ * U_i < 64, 128 for U_i < 128, else U_i + 1 rounded up to a multiple of
+ * 256: the recursions
  * address one sample's tables with 32-bit offsets; T_i + U_i up to 131071
  * at any width), sum_i T_i*(U_i+1) != N or partial overlap of grad and logits;
  * RNNT_WORKSPACE_TOO_SMALL; RNNT_MEMOPS_FAILED; RNNT_EXECUTION_FAILED.

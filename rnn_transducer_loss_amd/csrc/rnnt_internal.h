@@ -36,9 +36,9 @@ struct SampleDesc {
 };
 
 // Padded width of a lattice of width U1 in the alpha/beta sweeps (a 64-wide
-// wavefront with K columns per lane per group): 128 (K = 2) up to 128
-// columns, else a multiple of 256 (K = 4).
-inline int padded_width(int U1) { return U1 <= 128 ? 128 : (U1 + 255) / 256 * 256; }
+// wavefront with K columns per lane per group): 64 (K = 1) up to 64
+// columns, 128 (K = 2) up to 128, else a multiple of 256 (K = 4).
+inline int padded_width(int U1) { return U1 <= 64 ? 64 : U1 <= 128 ? 128 : (U1 + 255) / 256 * 256; }
 
 // A run of `count` lattice nodes of one sample handed to one workgroup of a
 // row pass, in one of two orders:

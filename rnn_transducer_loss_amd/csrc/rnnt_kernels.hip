@@ -700,10 +700,11 @@ __global__ __launch_bounds__(256) void k_gather(const T *__restrict__ logits, in
 
 // ----------------------------------------------------- K2: alpha/beta sweeps
 // Lane l owns K consecutive lattice columns in each of G column groups,
-// u = 64*K*g + K*l + k (k < K, g < G; U1p = 64*K*G padded columns, K = 2 for
-// lattices up to 128 columns wide, else 4).  A lane's columns move in
-// 16-byte accesses: the fp32 probabilities {P(blank), P(label)} of two
-// columns per load, two fp64 values per store.  Only a lane's first column
+// u = 64*K*g + K*l + k (k < K, g < G; U1p = 64*K*G padded columns, K = 1 for
+// lattices up to 64 columns wide, 2 up to 128, else 4).  A lane's columns
+// move in 16-byte accesses: the fp32 probabilities {P(blank), P(label)} of
+// two columns per load, two fp64 values per store (8-byte accesses of one
+// column when K = 1).  Only a lane's first column
 // needs a value from another lane (the last column of lane l-1, or of lane
 // 63 of the previous group for lane 0): one wave rotation per group and a
 // select on lane 0 (a plain shift when there is one group).  Diagonal n is
@@ -750,6 +751,12 @@ template <int K> struct Wts {
     __device__ float pb(int k) const { return (k & 1) ? q[k >> 1].z : q[k >> 1].x; }
     __device__ float py(int k) const { return (k & 1) ? q[k >> 1].w : q[k >> 1].y; }
 };
+// One column per lane (lattices up to 64 columns wide): {pb, py}.
+template <> struct Wts<1> {
+    float2 q;
+    __device__ float pb(int) const { return q.x; }
+    __device__ float py(int) const { return q.y; }
+};
 
 struct ProbDomain {
     static constexpr bool kLog = false;
@@ -761,9 +768,13 @@ struct ProbDomain {
     // voff[k]: byte offset of column k of the lane's group (even k used).
     template <int K>
     __device__ static void load(Wts<K> &w, Rsrc r, const uint32_t (&voff)[K], uint32_t soff) {
+        if constexpr (K == 1) {
+            w.q = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, voff[0], soff, 0));
+        } else {
 #pragma unroll
-        for (int h = 0; h < K / 2; ++h)
-            w.q[h] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff[2 * h], soff, 0));
+            for (int h = 0; h < K / 2; ++h)
+                w.q[h] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff[2 * h], soff, 0));
+        }
     }
 };
 struct LogDomain {
@@ -782,12 +793,17 @@ struct LogDomain {
     // U by the caller: a log-prob of 0 would not be impossible).
     template <int K>
     __device__ static void load(Wts<K> &w, Rsrc r, const uint32_t (&voff)[K], uint32_t soff) {
+        if constexpr (K == 1) {
+            const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, voff[0], soff, 0);
+            w.q = make_float2(__uint_as_float(x[0]), __uint_as_float(x[1]));
+        } else {
 #pragma unroll
-        for (int h = 0; h < K / 2; ++h) {
-            const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, voff[2 * h], soff, 0);
-            const u32x2 y = __builtin_amdgcn_raw_buffer_load_b64(r, voff[2 * h + 1], soff, 0);
-            w.q[h] = make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(y[0]),
-                                 __uint_as_float(y[1]));
+            for (int h = 0; h < K / 2; ++h) {
+                const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, voff[2 * h], soff, 0);
+                const u32x2 y = __builtin_amdgcn_raw_buffer_load_b64(r, voff[2 * h + 1], soff, 0);
+                w.q[h] = make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(y[0]),
+                                     __uint_as_float(y[1]));
+            }
         }
     }
 };
@@ -868,6 +884,14 @@ template <typename D, int K, int G> struct SweepIO {
     }
     __device__ void store(int n, const double (&a)[G][K]) const {
         const uint32_t off = (uint32_t)n * out_bytes;
+        if constexpr (K == 1) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const u32x2 v = {(uint32_t)__double2loint(a[g][0]), (uint32_t)__double2hiint(a[g][0])};
+                __builtin_amdgcn_raw_buffer_store_b64(v, rout, wout[g], off, 0);
+            }
+            return;
+        }
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -954,9 +978,17 @@ __device__ __forceinline__ void forward_block(const Ring<K, G, PF> &r, const Swe
     }
 }
 
-template <typename D, int K, int G, int PF>
-__device__ void sweep_forward(const SampleDesc &d, const char *__restrict__ w, double *__restrict__ out,
-                              int *__restrict__ eout, double *log2z) {
+// Proceed: called once the first ring's loads are issued; a sweep that
+// returns false there stops (a caller that starts the probability-domain
+// sweep before the sample's domain is known, so that those loads and the
+// ones deciding the domain are in flight together).
+struct AlwaysGo {
+    __device__ bool operator()() const { return true; }
+};
+
+template <typename D, int K, int G, int PF, typename Go = AlwaysGo>
+__device__ __forceinline__ bool sweep_forward(const SampleDesc &d, const char *__restrict__ w, double *__restrict__ out,
+                              int *__restrict__ eout, double *log2z, Go go = Go()) {
     const int lane = threadIdx.x & 63;
     const bool lane0 = lane == 0;
     const int U = d.U, nd = d.T + U;
@@ -970,6 +1002,7 @@ __device__ void sweep_forward(const SampleDesc &d, const char *__restrict__ w, d
     const SweepIO<D, K, G> io(w, out, U, nd);
     Ring<K, G, PF> ra, rb;
     load_block<D, K, G, PF>(ra, io, 0, 1, nd);
+    if (!go()) return false;
     int n0 = 0;
     for (; n0 + 2 * PF <= nd; n0 += 2 * PF) {
         load_block<D, K, G, PF>(rb, io, n0 + PF, 1, nd);
@@ -991,6 +1024,7 @@ __device__ void sweep_forward(const SampleDesc &d, const char *__restrict__ w, d
         for (int k = 0; k < K; ++k) v = (g == gU && k == kU) ? a[g][k] : v;
     const double z = __shfl(v, (U % (64 * K)) / K, 64);
     if (lane == 0) *log2z = D::kLog ? z : log2_d(z) + (double)E;
+    return true;
 }
 
 // One block of PF backward diagonals n0, n0-1, ..., n0-PF+1 from ring r
@@ -1012,9 +1046,9 @@ __device__ __forceinline__ void backward_block(const Ring<K, G, PF> &r, const Sw
     }
 }
 
-template <typename D, int K, int G, int PF>
-__device__ void sweep_backward(const SampleDesc &d, const char *__restrict__ w, double *__restrict__ out,
-                               int *__restrict__ eout, double *log2z) {
+template <typename D, int K, int G, int PF, typename Go = AlwaysGo>
+__device__ __forceinline__ bool sweep_backward(const SampleDesc &d, const char *__restrict__ w, double *__restrict__ out,
+                               int *__restrict__ eout, double *log2z, Go go = Go()) {
     const int lane = threadIdx.x & 63;
     const bool lane63 = lane == 63;
     const int U = d.U, nd = d.T + U;
@@ -1028,6 +1062,7 @@ __device__ void sweep_backward(const SampleDesc &d, const char *__restrict__ w, 
     const SweepIO<D, K, G> io(w, out, U, nd);
     Ring<K, G, PF> ra, rb;
     load_block<D, K, G, PF>(ra, io, nd - 1, -1, nd);
+    if (!go()) return false;
     int n0 = nd - 1;
     for (; n0 - 2 * PF + 1 >= 0; n0 -= 2 * PF) {
         load_block<D, K, G, PF>(rb, io, n0 - PF, -1, nd);
@@ -1041,22 +1076,29 @@ __device__ void sweep_backward(const SampleDesc &d, const char *__restrict__ w, 
         if (n0 - PF >= 0) backward_block<D, K, G, PF, true>(rb, io, n0 - PF, nd, lane63, b, E, eout);
     }
     if (lane == 0) *log2z = D::kLog ? b[0][0] : log2_d(b[0][0]) + (double)E;
+    return true;
 }
 
-template <int K, int G, int PF>
-__device__ void run_sweep(const SampleDesc &d, bool backward, bool log_mode, const float4 *node, const float2 *prob,
-                          double *alpha, double *beta, int *ea, int *eb, double *z) {
+// The sweep of one direction in the domain the sample takes.  With a Go
+// functor the probability-domain sweep starts first and Go, called once
+// its first loads are issued, returns whether the sample stays in that
+// domain; if not, the log-domain sweep runs instead.
+template <int K, int G, int PF, typename Go = AlwaysGo>
+__device__ __forceinline__ void run_sweep(const SampleDesc &d, bool backward, bool log_mode, const float4 *node, const float2 *prob,
+                          double *alpha, double *beta, int *ea, int *eb, double *z, Go go = Go()) {
     const int64_t so = d.slot_off;
     const int64_t ao = d.ab_off;
     const int64_t dof = d.diag_off;
-    if (log_mode) {
+    if (!log_mode) {
+        const char *w = reinterpret_cast<const char *>(prob + so);
+        const bool done = !backward ? sweep_forward<ProbDomain, K, G, PF>(d, w, alpha + ao, ea + dof, z, go)
+                                    : sweep_backward<ProbDomain, K, G, PF>(d, w, beta + ao, eb + dof, z, go);
+        if (done) return;
+    }
+    {
         const char *w = reinterpret_cast<const char *>(node + so);
         if (!backward) sweep_forward<LogDomain, K, G, PF>(d, w, alpha + ao, ea + dof, z);
         else sweep_backward<LogDomain, K, G, PF>(d, w, beta + ao, eb + dof, z);
-    } else {
-        const char *w = reinterpret_cast<const char *>(prob + so);
-        if (!backward) sweep_forward<ProbDomain, K, G, PF>(d, w, alpha + ao, ea + dof, z);
-        else sweep_backward<ProbDomain, K, G, PF>(d, w, beta + ao, eb + dof, z);
     }
 }
 
@@ -1065,15 +1107,17 @@ __device__ void run_sweep(const SampleDesc &d, bool backward, bool log_mode, con
 // log domain: twice as many 8-byte ones); when a ring is first read, its
 // loads, the other ring's and about one block of stores are in flight,
 // within the 63 vector memory operations the wait counter tracks.
+template <typename Go = AlwaysGo>
 __device__ __forceinline__ void sweep_sample(const SampleDesc &d, bool bw, bool lm, const float4 *node,
                                              const float2 *prob, double *alpha, double *beta, int *ealpha,
-                                             int *ebeta, double *z) {
+                                             int *ebeta, double *z, Go go = Go()) {
     switch (d.U1p) {
-    case 128: run_sweep<2, 1, 16>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z); break;
-    case 256: run_sweep<4, 1, 8>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z); break;
-    case 512: run_sweep<4, 2, 4>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z); break;
-    case 768: run_sweep<4, 3, 3>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z); break;
-    default: run_sweep<4, 4, 2>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z); break;
+    case 64: run_sweep<1, 1, 16>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z, go); break;
+    case 128: run_sweep<2, 1, 16>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z, go); break;
+    case 256: run_sweep<4, 1, 8>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z, go); break;
+    case 512: run_sweep<4, 2, 4>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z, go); break;
+    case 768: run_sweep<4, 3, 3>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z, go); break;
+    default: run_sweep<4, 4, 2>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z, go); break;
     }
 }
 
@@ -1171,21 +1215,27 @@ __global__ __launch_bounds__(128) void k_ab_small(const SampleDesc *__restrict__
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const bool bw = wave == 1;
     if (threadIdx.x == 0) bad_any = 0;
-    // the OR of the sample's chunk flags, four loads per lane in flight
-    const int nch = (int)(((int64_t)d.T * (d.U + 1) + rpc - 1) / rpc);
-    const uint32_t *cf = cflags + d.chunk0;
-    uint32_t f = 0;
-    for (int j = lane; j < nch; j += 256) {
-        uint32_t g[4];
+    // The sample's domain is the OR of its chunks' flags (four loads per
+    // lane in flight); the probability-domain sweep's first loads are issued
+    // before it is known.
+    int md0 = 0;
+    auto domain = [&]() {
+        const int nch = (int)(((int64_t)d.T * (d.U + 1) + rpc - 1) / rpc);
+        const uint32_t *cf = cflags + d.chunk0;
+        uint32_t f = 0;
+        for (int j = lane; j < nch; j += 256) {
+            uint32_t g[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) g[q] = (j + 64 * q < nch) ? cf[j + 64 * q] : 0u;
-        f |= g[0] | g[1] | g[2] | g[3];
-    }
-    const int md0 = __any((f & (uint32_t)kModeLog) != 0u) ? kModeLog : 0;
-    if (threadIdx.x == 0)
-        sflags[d.index] = __any((f & (uint32_t)RNNT_DEV_BAD_TARGET) != 0u) ? (uint32_t)RNNT_DEV_BAD_TARGET : 0u;
+            for (int q = 0; q < 4; ++q) g[q] = (j + 64 * q < nch) ? cf[j + 64 * q] : 0u;
+            f |= g[0] | g[1] | g[2] | g[3];
+        }
+        md0 = __any((f & (uint32_t)kModeLog) != 0u) ? kModeLog : 0;
+        if (threadIdx.x == 0)
+            sflags[d.index] = __any((f & (uint32_t)RNNT_DEV_BAD_TARGET) != 0u) ? (uint32_t)RNNT_DEV_BAD_TARGET : 0u;
+        return md0 == 0;
+    };
     double *z = bw ? &log2z[d.index] : &log2z[B + d.index];
-    sweep_sample(d, bw, md0 != 0, node, prob, alpha, beta, ealpha, ebeta, z);
+    sweep_sample(d, bw, false, node, prob, alpha, beta, ealpha, ebeta, z, domain);
     __syncthreads();
     int md = md0;
     if (md == 0) {
@@ -1201,6 +1251,12 @@ __global__ __launch_bounds__(128) void k_ab_small(const SampleDesc *__restrict__
             n[q] = (j + 1 < kCheckDiagonals) ? (int)(((int64_t)(2 * j + 1) * nd) / (2 * kCheckDiagonals)) : nd - 1;
             s[q] = 0.0;
         }
+        // the diagonals' exponents and P(y|x), loaded with the first columns
+        int ex[NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+            ex[q] = ealpha[d.diag_off + ((n[q] + 1) >> 3)] + ebeta[d.diag_off + ((nd - n[q]) >> 3)];
+        const double lz = log2z[d.index];
         for (int u = lane; u <= U; u += 64) {
             double a[NQ], b[NQ];
 #pragma unroll
@@ -1217,12 +1273,10 @@ __global__ __launch_bounds__(128) void k_ab_small(const SampleDesc *__restrict__
         for (int off = 32; off > 0; off >>= 1)
 #pragma unroll
             for (int q = 0; q < NQ; ++q) s[q] += __shfl_xor(s[q], off, 64);
-        const double lz = log2z[d.index];
         bool bad = !(lz > kNegInfD);
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            const double ls =
-                log2_d(s[q]) + (double)(ealpha[d.diag_off + ((n[q] + 1) >> 3)] + ebeta[d.diag_off + ((nd - n[q]) >> 3)]);
+            const double ls = log2_d(s[q]) + (double)ex[q];
             bad = bad || !(s[q] > 0.0) || !(fabs(ls - lz) <= 4e-6);
         }
         if (bad && lane == 0) atomicOr(&bad_any, 1);

@@ -299,3 +299,18 @@ def test_noalloc_refusals_before_any_device_work():
     Ts, Us = workloads.lengths("skewed")[:2]
     assert _lib.workspace_size(len(Ts), 2048, int((Ts.astype(np.int64) * (Us + 1)).sum()), _lib.RNNT_F16, Ts,
                                Us) <= _lib.NOALLOC_SCRATCH_BYTES
+
+
+def test_table_span_limit():
+    """The recursions address one sample's tables with 32-bit offsets: (T+U) * max(8 * U1p, 16 * (U+1)) must stay
+    below 2^31.  At U = 1023 (U1p = 1024) that allows T+U up to 131071; at U = 10 (U1p = 64) up to 2^31 / 512."""
+    for U, limit in ((1023, 2 ** 31 // (16 * 1024)), (10, 2 ** 31 // 512)):
+        ok_T, bad_T = limit - 1 - U, limit - U
+        for T, fine in ((ok_T, True), (bad_T, False)):
+            Ta, Ua = np.array([T], np.int32), np.array([U], np.int32)
+            N = T * (U + 1)
+            if fine:
+                assert _lib.workspace_size(1, 2, N, _lib.RNNT_F32, Ta, Ua) > 0
+            else:
+                with pytest.raises(ValueError):
+                    _lib.workspace_size(1, 2, N, _lib.RNNT_F32, Ta, Ua)

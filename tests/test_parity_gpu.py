@@ -321,10 +321,10 @@ def test_vocab5k_workload_full_size(rl):
     _reduced_ok(w, loss, red, w.reduction)
 
 
-@pytest.mark.parametrize("U", [63, 64, 127, 128, 255, 256, 511, 512, 700, 767, 768, 1023])
+@pytest.mark.parametrize("U", [0, 1, 62, 63, 64, 127, 128, 255, 256, 511, 512, 700, 767, 768, 1023])
 def test_lattice_widths_across_register_tiles(rl, U):
-    # U+1 crosses each width of the alpha/beta sweeps' lane tiles: 128 columns (two per lane), then
-    # groups of 256 (four per lane), up to four groups
+    # U+1 crosses each width of the alpha/beta sweeps' lane tiles: 64 columns (one per lane), 128 (two per
+    # lane), then groups of 256 (four per lane), up to four groups
     w = _custom([3, 40], [U, min(U, 20)], 8, std=1.0, blank=0, reduction="none", seed=U)
     loss, red, grad, flags = run(rl, w)
     assert flags == 0
@@ -478,7 +478,7 @@ def test_extreme_log_probs_take_the_log_domain_path(rl):
     check_against_oracle(w, loss, grad, "sum")
 
 
-@pytest.mark.parametrize("U", [130, 300, 600, 900])
+@pytest.mark.parametrize("U", [40, 63, 100, 130, 300, 600, 900])
 def test_log_domain_across_register_tiles(rl, U):
     """The log-domain sweep on lattices wide enough for one to four column groups per lane.
 
