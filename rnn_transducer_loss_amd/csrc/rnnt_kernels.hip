@@ -2552,20 +2552,25 @@ __global__ __launch_bounds__(64) void k_mb_rows_v(const T *__restrict__ logits, 
     const int lane = threadIdx.x;
     const int64_t r = row_base + xcd_block(blockIdx.x, gridDim.x >> 3);
     if (r >= N) return;
+    const T *x = logits + r * (int64_t)V;
+    const int nvec = V / VEC;
+    // the row's loads go out before the search for its sample, whose
+    // dependent loads they do not need (a padding row of the padded layout
+    // is read and then left)
+    Vec xv[NV];
+    if (fused) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            if (FULL || i * 64 + lane < nvec) xv[i] = load_raw<T, true>(x + (int64_t)(i * 64 + lane) * VEC);
+    }
     const SampleDesc d = mb_sample_of_row(desc, B, r);
     const int64_t lr = r - d.row_off;
     const int t = (int)(lr / d.tstride);
     const int u = (int)(lr - (int64_t)t * d.tstride);
     if (t >= d.T || u > d.U) return;  // a padding row of the padded layout
-    const T *x = logits + r * (int64_t)V;
-    const int nvec = V / VEC;
     float mr = 0.f, ls2 = 0.f;
     bool dead = false;
     if (fused) {
-        Vec xv[NV];
-#pragma unroll
-        for (int i = 0; i < NV; ++i)
-            if (FULL || i * 64 + lane < nvec) xv[i] = load_raw<T, true>(x + (int64_t)(i * 64 + lane) * VEC);
         const float m = wave_max_f(row_max<T, NV, FULL>(xv, nvec));
         dead = (m == kNegInf);
         mr = dead ? 0.f : m;
@@ -2627,8 +2632,17 @@ __global__ __launch_bounds__(64) void k_mb_grad_v(const T *__restrict__ logits, 
     // plain order: the XCD-contiguous order of the row pass made this pass slower (0.88 -> 0.94 ms)
     const int64_t r = row_base + (int64_t)blockIdx.x;
     if (r >= N) return;
-    const SampleDesc d = mb_sample_of_row(desc, B, r);
     const int nvec = V / VEC;
+    // the row's loads go out before the search for its sample (as in the
+    // row pass)
+    Vec xv[NV];
+    if (fused) {
+        const T *x = logits + r * (int64_t)V;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            if (FULL || i * 64 + lane < nvec) xv[i] = load_raw<T, true>(x + (int64_t)(i * 64 + lane) * VEC);
+    }
+    const SampleDesc d = mb_sample_of_row(desc, B, r);
     const int64_t lr = r - d.row_off;
     const int t = (int)(lr / d.tstride);
     const int u = (int)(lr - (int64_t)t * d.tstride);
@@ -2639,13 +2653,6 @@ __global__ __launch_bounds__(64) void k_mb_grad_v(const T *__restrict__ logits, 
         for (int i = 0; i < NV; ++i)
             if (FULL || i * 64 + lane < nvec) store_raw<T, true>(g + (int64_t)(i * 64 + lane) * VEC, Raw<T>::put(z));
         return;
-    }
-    Vec xv[NV];
-    if (fused) {
-        const T *x = logits + r * (int64_t)V;
-#pragma unroll
-        for (int i = 0; i < NV; ++i)
-            if (FULL || i * 64 + lane < nvec) xv[i] = load_raw<T, true>(x + (int64_t)(i * 64 + lane) * VEC);
     }
     MbRowTerms rt = mb_row_terms(d, r, t, u, V, blank, fused, mp, U1p, targets, S, den, wp, n_slots, alpha, beta, ealpha,
                                  ebeta, log2z, scale, fastemit, mode[d.index] != 0);
