@@ -214,11 +214,15 @@ def _padded_rows(w, g, max_T, max_U1):
 
 @pytest.mark.parametrize("V,dtype,fused", [(300, torch.float32, True), (29, torch.float32, True),
                                            (512, torch.float16, True), (256, torch.float16, False)])
-def test_padded_layout_matches_packed(rl, V, dtype, fused):
+@pytest.mark.parametrize("size", ["small", "large"])
+def test_padded_layout_matches_packed(rl, V, dtype, fused, size):
     # padded (B, max_T, max_U+1, V) input: same losses and, row for row, the
     # same gradient bits as the packed call on the same values; the padding
-    # (NaN here, never read) gets a zero gradient
-    Ts, Us = [40, 17, 33, 1, 25], [9, 0, 14, 6, 3]
+    # (NaN here, never read) gets a zero gradient.  "large": above the
+    # 64512-row line below which a batch takes three launches
+    Ts, Us = ([40, 17, 33, 1, 25], [9, 0, 14, 6, 3]) if size == "small" else \
+        ([500, 170, 330, 1, 250], [90, 0, 44, 6, 30])
+    assert (sum(t * (u + 1) for t, u in zip(Ts, Us)) < 64512) == (size == "small")
     w = workloads.make_custom(Ts, Us, V, dtype=dtype, std=2.0 if fused else 1.5, fused=fused, reduction="sum",
                               seed=77, device="cuda", prenormalise=not fused)
     max_T, max_U1 = max(Ts) + 3, max(Us) + 4
@@ -233,7 +237,7 @@ def test_padded_layout_matches_packed(rl, V, dtype, fused):
     rows, pad = _padded_rows(w, grad_p, max_T, max_U1)
     assert torch.equal(rows, grad)
     assert pad.numel() > 0 and bool((pad == 0).all())
-    check_against_oracle(w, loss, grad, "sum", grad_rows="all" if fused else 64)
+    check_against_oracle(w, loss, grad, "sum", grad_rows=("all" if fused else 64) if size == "small" else 300)
 
 
 def test_padded_inplace_and_autograd(rl):
@@ -369,10 +373,13 @@ def test_inplace_gradient_over_logits(rl):
 
 @pytest.mark.parametrize("V,dtype,fused", [(64, torch.float32, True), (1024, torch.float32, True),
                                            (29, torch.float32, True), (2048, torch.float16, False)])
-def test_score_only(rl, V, dtype, fused):
+@pytest.mark.parametrize("size", ["small", "large"])
+def test_score_only(rl, V, dtype, fused, size):
     """grad = NULL (the GPURNNT page's score_forward: costs without gradients): every loss against the oracle,
-    and bit for bit equal to the loss of the full call."""
-    w = _custom([40, 20, 33], [10, 7, 0], V, dtype=dtype, std=2.0 if fused else 1.5, blank=-1, fused=fused,
+    and bit for bit equal to the loss of the full call; on both sides of the 64512-row line."""
+    Ts, Us = ([40, 20, 33], [10, 7, 0]) if size == "small" else ([500, 200, 330], [100, 70, 0])
+    assert (sum(t * (u + 1) for t, u in zip(Ts, Us)) < 64512) == (size == "small")
+    w = _custom(Ts, Us, V, dtype=dtype, std=2.0 if fused else 1.5, blank=-1, fused=fused,
                 prenormalise=not fused, reduction="sum", seed=4)
     loss, red, grad, flags = run(rl, w, compute_grad=False)
     assert grad is None and flags == 0
