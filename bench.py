@@ -362,6 +362,31 @@ def main():
     per_kernel = {k: (v[0] / args.steps if v[1] else None) for k, v in kt.items()}
     launches = {k: v[1] / args.steps for k, v in kt.items()}
 
+    # secondary: the autograd round trip, rnnt_loss forward then loss.backward(), as a training step calls it
+    # (its gradient buffer allocated per call by torch's caching allocator; the upstream gradient is applied by
+    # the library's scaling kernel, which returns at once for a unit factor)
+    autograd_ms = None
+    if not multiblank and not args.graph:
+        x = w.logits.detach().requires_grad_(True)
+
+        def train_step():
+            out = rl.rnnt_loss(x, tg, T, U, blank=w.blank, clamp=w.clamp, reduction=w.reduction,
+                               fused_log_softmax=w.fused, fastemit_lambda=args.fastemit_lambda)
+            (out.sum() if w.reduction == "none" else out).backward()
+            x.grad = None
+        for _ in range(args.warmup):
+            train_step()
+        torch.cuda.synchronize()
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(args.steps):
+            train_step()
+        a1.record()
+        torch.cuda.synchronize()
+        autograd_ms = round(a0.elapsed_time(a1) / args.steps, 5)
+        del x
+
     ab = algorithmic_bytes(w)
     dominant = max((k for k in per_kernel if per_kernel[k] is not None), key=lambda k: per_kernel[k])
     dom_bytes = ab.get(dominant)
@@ -416,6 +441,7 @@ def main():
         "kernel_ms": {k: (round(v, 5) if v is not None else None) for k, v in per_kernel.items()},
         "launches_per_step": launches,
         "host_wall_ms_per_step": round(wall_ms, 4),
+        "autograd_ms_per_step": autograd_ms,
         "host_schedule": sched,
         "device_flags": flags,
         "roofline": roofline,

@@ -178,8 +178,11 @@ class _RNNTLossFunction(torch.autograd.Function):
             raise RuntimeError("rnnt_loss backward was already run for this forward call")
         ctx.used = True
         grad, ws = ctx.saved_tensors
-        scale = grad_out.detach().to(device=grad.device, dtype=torch.float32).contiguous().reshape(-1)
-        with torch.cuda.device(grad.device):
+        scale = grad_out.detach()
+        if scale.dtype != torch.float32 or scale.device != grad.device or not scale.is_contiguous():
+            scale = scale.to(device=grad.device, dtype=torch.float32).contiguous()
+        scale = scale.reshape(-1)
+        with _on_device(grad.device):
             stream = _stream_handle(grad.device)
             if len(shape) == 4:
                 _lib.grad_scale_padded(grad.data_ptr(), _dtype_code(dtype), shape[1], shape[2], shape[3], T, U,
@@ -323,8 +326,11 @@ class _MultiblankFunction(torch.autograd.Function):
             raise RuntimeError("rnnt_loss_multiblank backward was already run for this forward call")
         ctx.used = True
         grad, ws = ctx.saved_tensors
-        scale = grad_out.detach().to(device=grad.device, dtype=torch.float32).contiguous().reshape(-1)
-        with torch.cuda.device(grad.device):
+        scale = grad_out.detach()
+        if scale.dtype != torch.float32 or scale.device != grad.device or not scale.is_contiguous():
+            scale = scale.to(device=grad.device, dtype=torch.float32).contiguous()
+        scale = scale.reshape(-1)
+        with _on_device(grad.device):
             stream = _stream_handle(grad.device)
             if len(shape) == 4:
                 _lib.grad_scale_multiblank_padded(grad.data_ptr(), _dtype_code(dtype), shape[1], shape[2], shape[3],
