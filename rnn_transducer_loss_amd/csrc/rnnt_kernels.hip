@@ -1243,19 +1243,23 @@ __global__ __launch_bounds__(128) void k_ab_small(const SampleDesc *__restrict__
         // so that their loads are in flight at once
         constexpr int NQ = kCheckDiagonals / 2;
         const int T = d.T, U = d.U, nd = T + U;
+        auto diag_of = [&](int q) {
+            const int j = wave + 2 * q;
+            return (j + 1 < kCheckDiagonals) ? (int)(((int64_t)(2 * j + 1) * nd) / (2 * kCheckDiagonals)) : nd - 1;
+        };
         int n[NQ];
         double s[NQ];
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            const int j = wave + 2 * q;
-            n[q] = (j + 1 < kCheckDiagonals) ? (int)(((int64_t)(2 * j + 1) * nd) / (2 * kCheckDiagonals)) : nd - 1;
+            n[q] = diag_of(q);
             s[q] = 0.0;
         }
-        // the diagonals' exponents and P(y|x), loaded with the first columns
-        int ex[NQ];
-#pragma unroll
-        for (int q = 0; q < NQ; ++q)
-            ex[q] = ealpha[d.diag_off + ((n[q] + 1) >> 3)] + ebeta[d.diag_off + ((nd - n[q]) >> 3)];
+        // After the reduction below, lanes 8q .. 8q+7 hold the sum of
+        // diagonal q: each lane loads that diagonal's exponents and P(y|x)
+        // with the first columns.
+        const int ql = (lane >> 3) & (NQ - 1);
+        const int nl = diag_of(ql);
+        const int exl = ealpha[d.diag_off + ((nl + 1) >> 3)] + ebeta[d.diag_off + ((nd - nl) >> 3)];
         const double lz = log2z[d.index];
         for (int u = lane; u <= U; u += 64) {
             double a[NQ], b[NQ];
@@ -1269,16 +1273,32 @@ __global__ __launch_bounds__(128) void k_ab_small(const SampleDesc *__restrict__
 #pragma unroll
             for (int q = 0; q < NQ; ++q) s[q] += a[q] * b[q];
         }
+        // Eight sums over the wave in ten lane exchanges: at offsets 32, 16
+        // and 8 each lane keeps the half of its sums that its lane bit
+        // selects and adds its partner's copy of that half (so afterwards
+        // lane bits 5..3 name the diagonal), then offsets 4, 2, 1 finish it;
+        // one log2 per lane then serves all eight diagonals.
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1)
-#pragma unroll
-            for (int q = 0; q < NQ; ++q) s[q] += __shfl_xor(s[q], off, 64);
-        bool bad = !(lz > kNegInfD);
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const double ls = log2_d(s[q]) + (double)ex[q];
-            bad = bad || !(s[q] > 0.0) || !(fabs(ls - lz) <= 4e-6);
+        for (int q = 0; q < NQ / 2; ++q) {
+            const bool up = (lane & 32) != 0;
+            const double keep = up ? s[q + 4] : s[q], give = up ? s[q] : s[q + 4];
+            s[q] = keep + __shfl_xor(give, 32, 64);
         }
+#pragma unroll
+        for (int q = 0; q < NQ / 4; ++q) {
+            const bool up = (lane & 16) != 0;
+            const double keep = up ? s[q + 2] : s[q], give = up ? s[q] : s[q + 2];
+            s[q] = keep + __shfl_xor(give, 16, 64);
+        }
+        {
+            const bool up = (lane & 8) != 0;
+            const double keep = up ? s[1] : s[0], give = up ? s[0] : s[1];
+            s[0] = keep + __shfl_xor(give, 8, 64);
+        }
+#pragma unroll
+        for (int off = 4; off > 0; off >>= 1) s[0] += __shfl_xor(s[0], off, 64);
+        const double ls = log2_d(s[0]) + (double)exl;
+        const bool bad = !(lz > kNegInfD) || __any(!(s[0] > 0.0) || !(fabs(ls - lz) <= 4e-6));
         if (bad && lane == 0) atomicOr(&bad_any, 1);
         __syncthreads();
         if (bad_any) {
