@@ -1475,13 +1475,17 @@ __device__ __forceinline__ float clamp_to(float v, float cl, bool do_clamp) {
 // of the vector that holds them: element k is element k % VEC of vector
 // k / VEC, held by lane (k / VEC) mod 64 as its vector number (k / VEC) / 64.
 // The registers are overwritten with the stored gradient.
-template <typename T, int NV, bool FULL, bool FUSED, bool CLAMP>
+// With a rotation h (see k_grad_rows), vector number i is the row's vector
+// (i + h) mod nvec.
+template <typename T, int NV, bool FULL, bool FUSED, bool CLAMP, bool ROT = false>
 __device__ __forceinline__ void grad_row(typename Raw<T>::vec (&xc)[NV], T *dst, const RowTerms &rt, int blank,
-                                         int nvec, float cl, int i0 = 0) {
+                                         int nvec, float cl, int i0 = 0, int h = 0) {
     constexpr int VEC = Raw<T>::kVec;
     const int lane = threadIdx.x & 63;
-    const int vb = blank / VEC, vy = rt.y >= 0 ? rt.y / VEC : -1;
-    const int eb = blank - vb * VEC, ey = rt.y - vy * VEC;
+    if constexpr (!ROT) h = 0;
+    auto number_of = [&](int v) { return v >= h ? v - h : v - h + nvec; };  // vector number of row vector v
+    const int vb = number_of(blank / VEC), vy = rt.y >= 0 ? number_of(rt.y / VEC) : -1;
+    const int eb = (int)((unsigned)blank % VEC), ey = (int)((unsigned)rt.y % VEC);
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         const int i = i0 + j;
@@ -1505,7 +1509,8 @@ __device__ __forceinline__ void grad_row(typename Raw<T>::vec (&xc)[NV], T *dst,
 #pragma unroll
             for (int e = 0; e < VEC; ++e) gv[e] = clamp_to(gv[e], cl, CLAMP);
             xc[j] = Raw<T>::put(gv);
-            store_raw<T, true>(dst + (int64_t)vi * VEC, xc[j]);
+            const int v = vi + h;
+            store_raw<T, true>(dst + (int64_t)(ROT && v >= nvec ? v - nvec : v) * VEC, xc[j]);
         }
     }
 }
@@ -1526,7 +1531,7 @@ __device__ __forceinline__ void grad_row(typename Raw<T>::vec (&xc)[NV], T *dst,
 // log-prob inputs (a write-only pass) take the unmasked form, with the split
 // fixed when it is one (4 KiB rows: 0.995 ms against 1.016 at run time and
 // 1.045 masked).
-template <typename T, bool FUSED, bool CLAMP, int SPLIT, bool FULL>
+template <typename T, bool FUSED, bool CLAMP, int SPLIT, bool FULL, bool ROT>
 __global__ __launch_bounds__(64) void k_grad_rows(const T *logits, T *grad, int blocks_per_chunk,
                                                   int64_t block_base, int split_rt, RNNT_GRAD_PARAMS) {
     constexpr int VEC = Raw<T>::kVec;
@@ -1549,19 +1554,31 @@ __global__ __launch_bounds__(64) void k_grad_rows(const T *logits, T *grad, int 
     const int u = (c.row_begin + r) - t * U1;
     const int64_t row = row_of(d, t, u);
     using Vec = typename Raw<T>::vec;
+    // ROT (rows that may start inside a 128-byte line: their length is no
+    // multiple of 128 bytes, or the gradient is not 128-byte aligned): the
+    // row is walked from its first line boundary, vector number i being the
+    // row's vector (i + h) mod nvec, h the vectors before that boundary
+    // (they come last), so each instruction's 64 vectors fill whole lines of
+    // the gradient.  Cut at the row start, every instruction began and ended
+    // mid-line (20000-byte fp32 rows: 5.41 -> 5.13 ms; 20480-byte rows, with
+    // more data, 4.78).  Other rows take the plain form: the index
+    // arithmetic costs 2-3% where there is nothing to gain.
+    T *dst = grad + row * (int64_t)V;
+    const int h = ROT ? (int)(((128u - ((uint32_t)reinterpret_cast<uintptr_t>(dst) & 127u)) & 127u) >> 4) : 0;
     Vec x[NV];
     if constexpr (FUSED) {
         const T *p = logits + row * (int64_t)V;
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
             const int vi = (i0 + j) * 64 + lane;
-            if (FULL || vi < nvec) x[j] = load_raw<T, true>(p + (int64_t)vi * VEC);
+            const int v = vi + h;
+            if (FULL || vi < nvec) x[j] = load_raw<T, true>(p + (int64_t)(ROT && v >= nvec ? v - nvec : v) * VEC);
         }
     }
     const SampleTerms st{log2z[d.index], mode[d.index] != 0};
     const RowTerms rt = row_terms(d, st, t, u, node, alpha, beta, ealpha, ebeta, log2_scale, scale, fastemit,
                                   scale_y, FUSED, V, blank, targets, S);
-    grad_row<T, NV, FULL, FUSED, CLAMP>(x, grad + row * (int64_t)V, rt, blank, nvec, clamp * scale, i0);
+    grad_row<T, NV, FULL, FUSED, CLAMP, ROT>(x, dst, rt, blank, nvec, clamp * scale, i0, h);
 }
 
 template <typename T, int VEC, int G, bool FUSED>
@@ -1874,12 +1891,20 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
                          const int32_t *, const SampleDesc *, const ChunkDesc *, const int *, const double *,
                          const float4 *, const double *, const double *, const int *, const int *, ReduceArgs);
             const bool full = (int64_t)a.V * a.esize % 4096 == 0;  // every part a whole 4 KiB
-            if (a.fused) kern = cl ? k_grad_rows<T, true, true, 0, false> : k_grad_rows<T, true, false, 0, false>;
+            // rows that can start inside a 128-byte line
+            const bool rot = (int64_t)a.V * a.esize % 128 != 0 || reinterpret_cast<uintptr_t>(a.grad) % 128 != 0;
+            if (a.fused && rot)
+                kern = cl ? k_grad_rows<T, true, true, 0, false, true> : k_grad_rows<T, true, false, 0, false, true>;
+            else if (a.fused)
+                kern = cl ? k_grad_rows<T, true, true, 0, false, false> : k_grad_rows<T, true, false, 0, false, false>;
             else if (full && a.geom.stream_parts == 1)
-                kern = cl ? k_grad_rows<T, false, true, 1, true> : k_grad_rows<T, false, false, 1, true>;
+                kern = cl ? k_grad_rows<T, false, true, 1, true, false> : k_grad_rows<T, false, false, 1, true, false>;
             else if (full)
-                kern = cl ? k_grad_rows<T, false, true, 0, true> : k_grad_rows<T, false, false, 0, true>;
-            else kern = cl ? k_grad_rows<T, false, true, 0, false> : k_grad_rows<T, false, false, 0, false>;
+                kern = cl ? k_grad_rows<T, false, true, 0, true, false> : k_grad_rows<T, false, false, 0, true, false>;
+            else if (rot)
+                kern = cl ? k_grad_rows<T, false, true, 0, false, true> : k_grad_rows<T, false, false, 0, false, true>;
+            else
+                kern = cl ? k_grad_rows<T, false, true, 0, false, false> : k_grad_rows<T, false, false, 0, false, false>;
             // one launch per 2^24 workgroups, so no launch exceeds 32-bit work-item counts
             const int split = a.geom.stream_parts;
             const int bpc = a.lay.rows_per_chunk * split;
