@@ -400,6 +400,33 @@ def test_unaligned_logits_pointer(rl):
     check_against_oracle(w, loss, grad, "mean")
 
 
+@pytest.mark.parametrize("V,dtype,fused", [(1024, torch.float32, True), (2048, torch.float16, False),
+                                           (5000, torch.float32, True), (300, torch.float32, True)])
+def test_rows_off_128_byte_lines(rl, V, dtype, fused):
+    """Logits and gradient 16 bytes past a 128-byte boundary: rows of 4 KiB parts start inside a line, so the
+    wide gradient pass walks each row from its first line boundary (as it does for 20000- and 1200-byte rows
+    anywhere).  The row pass reads the same rows in the same lane order, and the gradient is elementwise, so
+    everything is bitwise equal to the aligned call; the aligned call is checked against the oracle."""
+    w = _custom([37, 22], [9, 14], V, dtype=dtype, std=2.0 if fused else 1.5, blank=-1, fused=fused,
+                prenormalise=not fused, reduction="sum", seed=61)
+    tg = torch.from_numpy(w.targets).to("cuda")
+    shift = 16 // w.logits.element_size()
+    xs = torch.empty(w.logits.numel() + 64, dtype=w.logits.dtype, device="cuda")
+    gs = torch.empty_like(xs)
+    assert xs.data_ptr() % 128 == 0 and gs.data_ptr() % 128 == 0
+    x = xs[shift:shift + w.logits.numel()].view(w.N, w.V)
+    x.copy_(w.logits)
+    g = gs[shift:shift + w.logits.numel()].view(w.N, w.V)
+    loss0, red0, grad0, flags = run(rl, w)
+    assert flags == 0
+    check_against_oracle(w, loss0, grad0, "sum", grad_rows=64)
+    loss1, red1, grad1, _ = rl.rnnt_loss_fused(x, tg, w.logit_lengths, w.target_lengths, blank=w.blank,
+                                               reduction="sum", fused_log_softmax=fused, grad=g)
+    torch.cuda.synchronize()
+    assert grad1.data_ptr() == g.data_ptr()
+    assert torch.equal(loss1, loss0) and torch.equal(red1, red0) and torch.equal(grad1, grad0)
+
+
 def test_deterministic_bitwise(rl):
     w = workloads.make("char", seed=7, device="cuda")
     a = run(rl, w)
