@@ -1483,9 +1483,10 @@ __device__ __forceinline__ void grad_row(typename Raw<T>::vec (&xc)[NV], T *dst,
     constexpr int VEC = Raw<T>::kVec;
     const int lane = threadIdx.x & 63;
     if constexpr (!ROT) h = 0;
+    const int pb = blank / VEC, py = rt.y >= 0 ? rt.y / VEC : -1;  // the row vectors holding them
+    const int eb = blank - pb * VEC, ey = rt.y - py * VEC;
     auto number_of = [&](int v) { return v >= h ? v - h : v - h + nvec; };  // vector number of row vector v
-    const int vb = number_of(blank / VEC), vy = rt.y >= 0 ? number_of(rt.y / VEC) : -1;
-    const int eb = (int)((unsigned)blank % VEC), ey = (int)((unsigned)rt.y % VEC);
+    const int vb = ROT ? number_of(pb) : pb, vy = (ROT && py >= 0) ? number_of(py) : py;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         const int i = i0 + j;
