@@ -401,7 +401,8 @@ def test_unaligned_logits_pointer(rl):
 
 
 @pytest.mark.parametrize("V,dtype,fused", [(1024, torch.float32, True), (2048, torch.float16, False),
-                                           (5000, torch.float32, True), (300, torch.float32, True)])
+                                           (5000, torch.float32, True), (300, torch.float32, True),
+                                           (2504, torch.float16, True), (1000, torch.float32, False)])
 def test_rows_off_128_byte_lines(rl, V, dtype, fused):
     """Logits and gradient 16 bytes past a 128-byte boundary: rows of 4 KiB parts start inside a line, so the
     wide gradient pass walks each row from its first line boundary (as it does for 20000- and 1200-byte rows
