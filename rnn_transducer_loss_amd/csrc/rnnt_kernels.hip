@@ -502,11 +502,12 @@ __global__ __launch_bounds__(256) void k_plan(const SampleDesc *__restrict__ des
 }
 
 // ------------------------------------ K1 rowstats, rows wider than 1 KiB
-// One row per wave (W waves per workgroup: eight for rows of up to 4 KiB,
-// sixteen above, each measured fastest there: 8 against 4 waves 2% faster
-// on 4 KiB and 8 KiB rows, 16 against 8 another 1.3% on 8 KiB and 2.4% on
-// 20 KB rows but 9% slower on 4 KiB ones; a chunk's nodes in diagonal order,
-// so the waves' per-node records land in consecutive slots), the row walked in
+// Rows above 4 KiB: one row per wave (sixteen waves per workgroup, measured
+// fastest there: 16 against 8 waves 1.3% faster on 8 KiB and 2.4% on 20 KB
+// rows; rows of 1 to 4 KiB take k_rowstats_multi below, eight waves of two
+// rows at a time, where one row per wave had measured 8 waves 2% faster than
+// 4 and 9% faster than 16; a chunk's nodes in diagonal order, so the waves'
+// per-node records land in consecutive slots), the row walked in
 // segments of 4 KiB (four 16-byte vectors per lane, non-temporal loads) with
 // the next segment's loads in flight.  Holding only two segments, a wave
 // needs few registers, so many waves (rows) are in flight per compute unit:
@@ -590,6 +591,101 @@ __global__ __launch_bounds__(64 * W) void k_rowstats_stream(const T *__restrict_
         emit_node(d, n - u, u, mr, ls2, lpb, lpy, node, prob, wk.mode_word);
         fill_diagonal_ends(d, n, u, lane, 64, node, prob);
         advance_diag(n, u, W, d.T, d.U);
+    }
+    row_work_end(src, &wg_flags);
+}
+
+// Rows of 1 to 4 KiB (one segment, four vectors per lane): each wave takes R
+// of its rows at a time, r, r + W, ..., r + (R-1) W, with the loads of all
+// of them in flight together and their reductions interleaved.  Per row the
+// arithmetic is the streaming kernel's, lane for lane.  Launched with R = 2
+// (4 KiB fp32 rows: 0.438 -> 0.431 ms against one row at a time; four rows
+// 0.442).
+template <typename T, int W, int R, typename Src>
+__global__ __launch_bounds__(64 * W) void k_rowstats_multi(const T *__restrict__ logits, int V, int blank, Src src,
+                                                        const int32_t *__restrict__ targets, int S,
+                                                        float4 *__restrict__ node, float2 *__restrict__ prob) {
+    constexpr int VEC = Raw<T>::kVec;
+    constexpr int NS = 4;
+    using Vec = typename Raw<T>::vec;
+    __shared__ uint32_t wg_flags;
+    const RowWork wk = row_work<true>(src, &wg_flags);
+    const ChunkDesc &c = wk.c;
+    const SampleDesc &d = wk.d;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nvec = V / VEC;
+    int n = c.diag, u = c.col;
+    advance_diag(n, u, wave, d.T, d.U);
+    for (int r = wave; r < c.count; r += R * W) {
+        int nr[R], ur[R];
+        const T *p[R];
+        nr[0] = n;
+        ur[0] = u;
+#pragma unroll
+        for (int k = 1; k < R; ++k) {
+            nr[k] = nr[k - 1];
+            ur[k] = ur[k - 1];
+            advance_diag(nr[k], ur[k], W, d.T, d.U);
+        }
+#pragma unroll
+        for (int k = 0; k < R; ++k)  // rows past the chunk reread its first (in bounds, not stored)
+            p[k] = logits + row_of(d, (r + k * W < c.count ? nr[k] - ur[k] : n - u),
+                                   (r + k * W < c.count ? ur[k] : u)) * (int64_t)V;
+        Vec x[R][NS];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            const int vi = i * 64 + lane;
+            if (vi < nvec)
+#pragma unroll
+                for (int k = 0; k < R; ++k) x[k][i] = load_raw<T, true>(p[k] + (int64_t)vi * VEC);
+        }
+        int y[R];
+        float hb[R], hy[R];
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            y[k] = (r + k * W < c.count)
+                       ? __builtin_amdgcn_readfirstlane(read_label(d, ur[k], V, blank, targets, S, wk.status_word))
+                       : -1;
+            hb[k] = Elem<T>::load1(p[k] + blank);
+            hy[k] = (y[k] >= 0) ? Elem<T>::load1(p[k] + y[k]) : 0.f;
+        }
+        // per row and lane: the maximum m, nm = -m log2(e) and the sum of exp2(fma(x, log2(e), nm))
+        float m[R], nm[R], sm[R];
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            m[k] = row_max<T, NS, false>(x[k], nvec);
+            nm[k] = (m[k] == kNegInf) ? 0.f : -m[k] * kLog2e;
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < NS; ++i)
+                if (i * 64 + lane < nvec)
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) acc += exp2_fast(fmaf(Raw<T>::get(x[k][i], e), kLog2e, nm[k]));
+            sm[k] = acc;
+        }
+        float M[R], part[R];
+#pragma unroll
+        for (int k = 0; k < R; ++k) M[k] = wave_max_f(m[k]);
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            const float mr = (M[k] == kNegInf) ? 0.f : M[k];
+            part[k] = (sm[k] == 0.f) ? 0.f : sm[k] * exp2_fast(-fmaf(mr, kLog2e, nm[k]));
+        }
+#pragma unroll
+        for (int k = 0; k < R; ++k) part[k] = wave_sum_f(part[k]);
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            if (r + k * W >= c.count) break;
+            const bool dead = (M[k] == kNegInf);
+            const float mr = dead ? 0.f : M[k];
+            const float ls2 = dead ? 0.f : log2_fast(part[k]);
+            const float lpb = dead ? kNegInf : (hb[k] - mr) - ls2 * kLn2;
+            const float lpy = (dead || y[k] < 0) ? kNegInf : (hy[k] - mr) - ls2 * kLn2;
+            emit_node(d, nr[k] - ur[k], ur[k], mr, ls2, lpb, lpy, node, prob, wk.mode_word);
+            fill_diagonal_ends(d, nr[k], ur[k], lane, 64, node, prob);
+        }
+        advance_diag(n, u, R * W, d.T, d.U);
     }
     row_work_end(src, &wg_flags);
 }
@@ -1791,7 +1887,7 @@ hipError_t launch_rowstats_with(const LaunchArgs &a, const Src &src, hipStream_t
     if (a.geom.stream_parts > 0) {
         auto go = [&](auto tag) {
             using T = decltype(tag);
-            auto kern = a.geom.stream_parts == 1 ? k_rowstats_stream<T, 8, Src> : k_rowstats_stream<T, 16, Src>;
+            auto kern = a.geom.stream_parts == 1 ? k_rowstats_multi<T, 8, 2, Src> : k_rowstats_stream<T, 16, Src>;
             const dim3 wblock(a.geom.stream_parts == 1 ? 512 : 1024);
             hipLaunchKernelGGL(kern, grid, wblock, 0, stream, static_cast<const T *>(a.logits), a.V, a.blank, src,
                                a.targets, a.S, WS(float4 *, node), WS(float2 *, prob));
