@@ -117,9 +117,9 @@ enum {
  *   N                 rows of the packed logits; must equal sum_i T_i*(U_i+1).
  *   dtype             RNNT_F32 or RNNT_F16.
  *   logit_lengths     host int32[B]: T_i >= 1.
- *   target_lengths    host int32[B]: 0 <= U_i <= 1023 (U_i+1 is the lattice
+ *   target_lengths    host int32[B]: 0 <= U_i <= 2047 (U_i+1 is the lattice
  *                     width; the alpha/beta kernel keeps a whole anti-diagonal
- *                     of up to 1024 nodes in one wavefront's registers).
+ *                     of up to 2048 nodes in one wavefront's registers).
  *   workspace_bytes   out: required size; the caller allocates it (any
  *                     alignment of 256 bytes or more) and passes it back.
  * Runs every host-side check of rnnt_loss_fused that does not need the
@@ -166,7 +166,7 @@ rnnt_status rnnt_loss_fused_workspace_size(int32_t B, int32_t V, int64_t N, rnnt
  *   stream            hipStream_t for all device work.
  * Returns RNNT_INVALID_VALUE for a NULL required pointer, bad dtype or
  * reduction, V < 1, B < 1, blank out of range, fastemit_lambda negative or not
- * finite, T_i < 1, U_i < 0, U_i > 1023, U_i > S, a sample with
+ * finite, T_i < 1, U_i < 0, U_i > 2047, U_i > S, a sample with
  * (T_i + U_i) * max(8 * U1p_i, 16 * (U_i + 1)) >= 2^31 (U1p_i = 64 for
  * U_i < 64, 128 for U_i < 128, else U_i + 1 rounded up to a multiple of
  * 256: the recursions
@@ -309,8 +309,9 @@ rnnt_status rnnt_loss_fused_noalloc(const void *logits, rnnt_dtype dtype, int64_
  *   sigma             finite; subtracted from every emission's log-probability.
  *   workspace         device, >= rnnt_multiblank_workspace_size bytes, 256-byte
  *                     aligned.
- * Returns RNNT_INVALID_VALUE for the conditions of rnnt_loss_fused, a bad big
- * blank list, a non-finite sigma, a batch whose widest lattice and longest
+ * Returns RNNT_INVALID_VALUE for the conditions of rnnt_loss_fused, a U_i
+ * above 1023 (its sweep keeps an anti-diagonal of up to 1024 nodes in one
+ * wavefront), a bad big blank list, a non-finite sigma, a batch whose widest lattice and longest
  * duration need more than 64 KiB of ring per sweep, i.e. R * U1p * 8 bytes
  * > 64 KiB with R the power of two above the longest duration and U1p the
  * widest U_i + 1 rounded up to 128 times a power of two (at U1p = 1024 the

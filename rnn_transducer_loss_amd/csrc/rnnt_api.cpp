@@ -553,6 +553,7 @@ rnnt_status build_mb_plan(int32_t B, int32_t V, int64_t N, const int32_t *T, con
     }
     int max_U1 = 1;
     for (int32_t i = 0; i < B; ++i) max_U1 = std::max(max_U1, U[i] + 1);
+    if (max_U1 > kMaxMbU1) return RNNT_INVALID_VALUE;
     int G = 1;  // groups of 128 columns (two per lane) in the sweep
     while (128 * G < max_U1) G <<= 1;
     const int U1p = 128 * G;

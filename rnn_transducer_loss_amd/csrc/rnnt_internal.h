@@ -203,7 +203,8 @@ static_assert(kScratchBytes == RNNT_NOALLOC_SCRATCH_BYTES, "the header states th
 hipError_t scratch_address(void **ptr);
 
 // Largest lattice width (U+1) the alpha/beta kernel supports.
-constexpr int kMaxU1 = 1024;
+constexpr int kMaxU1 = 2048;
+constexpr int kMaxMbU1 = 1024;  // the multi-blank sweep: up to eight groups of 128 columns
 
 // ------------------------------------------------- multi-blank transducer
 constexpr int kMaxBigBlanks = 4;

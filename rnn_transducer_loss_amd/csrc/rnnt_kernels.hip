@@ -1213,7 +1213,11 @@ __device__ __forceinline__ void sweep_sample(const SampleDesc &d, bool bw, bool 
     case 256: run_sweep<4, 1, 8>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z, go); break;
     case 512: run_sweep<4, 2, 4>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z, go); break;
     case 768: run_sweep<4, 3, 3>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z, go); break;
-    default: run_sweep<4, 4, 2>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z, go); break;
+    case 1024: run_sweep<4, 4, 2>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z, go); break;
+    case 1280: run_sweep<4, 5, 1>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z, go); break;
+    case 1536: run_sweep<4, 6, 1>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z, go); break;
+    case 1792: run_sweep<4, 7, 1>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z, go); break;
+    default: run_sweep<4, 8, 1>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z, go); break;
     }
 }
 

@@ -59,9 +59,9 @@ def test_workspace_size_grows_with_the_batch():
 
 
 @pytest.mark.parametrize("T,U,N", [([0, 3], [1, 1], None), ([3, 3], [-1, 1], None), ([4], [2], 11),
-                                   ([4], [1023], None), ([2], [1024], None)])
+                                   ([4], [2047], None), ([2], [2048], None)])
 def test_workspace_size_rejects_bad_lengths(T, U, N):
-    if U == [1023]:
+    if U == [2047]:
         assert _ws(T, U) > 0      # widest lattice the kernels support
         return
     with pytest.raises(ValueError):
@@ -249,6 +249,15 @@ def test_multiblank_ring_limit():
     assert _lib.workspace_size_multiblank(1, 8, 3 * 200, 0, T, np.array([199], np.int32), [16]) > 0
 
 
+def test_multiblank_width_limit():
+    # the multi-blank sweep keeps an anti-diagonal of up to 1024 columns in one wave (the plain path 2048)
+    T = np.array([3], np.int32)
+    assert _lib.workspace_size_multiblank(1, 8, 3 * 1024, 0, T, np.array([1023], np.int32), [2]) > 0
+    with pytest.raises(ValueError):
+        _lib.workspace_size_multiblank(1, 8, 3 * 1025, 0, T, np.array([1024], np.int32), [2])
+    assert _ws([3], [1024]) > 0
+
+
 def test_multiblank_table_span_limit():
     # the sweep addresses a sample's T+U diagonals of 128 (padded) columns of fp64 with 32-bit byte offsets:
     # (T+U) * 128 * 8 must stay below 2^31
@@ -303,8 +312,9 @@ def test_noalloc_refusals_before_any_device_work():
 
 def test_table_span_limit():
     """The recursions address one sample's tables with 32-bit offsets: (T+U) * max(8 * U1p, 16 * (U+1)) must stay
-    below 2^31.  At U = 1023 (U1p = 1024) that allows T+U up to 131071; at U = 10 (U1p = 64) up to 2^31 / 512."""
-    for U, limit in ((1023, 2 ** 31 // (16 * 1024)), (10, 2 ** 31 // 512)):
+    below 2^31.  At U = 1023 (U1p = 1024) that allows T+U up to 131071, at U = 2047 up to 65535; at U = 10
+    (U1p = 64) up to 2^31 / 512."""
+    for U, limit in ((1023, 2 ** 31 // (16 * 1024)), (2047, 2 ** 31 // (16 * 2048)), (10, 2 ** 31 // 512)):
         ok_T, bad_T = limit - 1 - U, limit - U
         for T, fine in ((ok_T, True), (bad_T, False)):
             Ta, Ua = np.array([T], np.int32), np.array([U], np.int32)

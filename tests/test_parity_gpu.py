@@ -325,14 +325,28 @@ def test_vocab5k_workload_full_size(rl):
     _reduced_ok(w, loss, red, w.reduction)
 
 
-@pytest.mark.parametrize("U", [0, 1, 62, 63, 64, 127, 128, 255, 256, 511, 512, 700, 767, 768, 1023])
+@pytest.mark.parametrize("U", [0, 1, 62, 63, 64, 127, 128, 255, 256, 511, 512, 700, 767, 768, 1023, 1024, 1279,
+                               1280, 1535, 1536, 1791, 1792, 2047])
 def test_lattice_widths_across_register_tiles(rl, U):
     # U+1 crosses each width of the alpha/beta sweeps' lane tiles: 64 columns (one per lane), 128 (two per
-    # lane), then groups of 256 (four per lane), up to four groups
+    # lane), then groups of 256 (four per lane), up to eight groups
     w = _custom([3, 40], [U, min(U, 20)], 8, std=1.0, blank=0, reduction="none", seed=U)
     loss, red, grad, flags = run(rl, w)
     assert flags == 0
     check_against_oracle(w, loss, grad, "none")
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_wide_lattices_in_a_large_batch(rl, fused):
+    """Lattices of 2001 and 1501 columns (eight and six column groups per lane) in a batch above 64 K rows, so
+    the recursions run on the six-launch path; with log-prob inputs, mildly peaked, for the probability domain."""
+    w = _custom([40, 44, 30], [2000, 1500, 700], 8, std=1.0, blank=0, fused=fused, prenormalise=not fused,
+                reduction="mean", seed=71)
+    assert w.N > 64 * 1024
+    loss, red, grad, flags = run(rl, w)
+    assert flags == 0
+    check_against_oracle(w, loss, grad, "mean", grad_rows=300)
+    _reduced_ok(w, loss, red, "mean")
 
 
 def test_ragged_batch_many_samples(rl):
@@ -513,7 +527,7 @@ def test_extreme_log_probs_take_the_log_domain_path(rl):
     check_against_oracle(w, loss, grad, "sum")
 
 
-@pytest.mark.parametrize("U", [40, 63, 100, 130, 300, 600, 900])
+@pytest.mark.parametrize("U", [40, 63, 100, 130, 300, 600, 900, 1100, 1700, 2047])
 def test_log_domain_across_register_tiles(rl, U):
     """The log-domain sweep on lattices wide enough for one to four column groups per lane.
 
