@@ -523,7 +523,7 @@ rnnt_status loss_impl(const void *logits, rnnt_dtype dtype, int64_t N, int32_t V
     LaunchArgs a = launch_args(logits, es, rows, V, targets, S, B, blank, clamp, fastemit_lambda,
                                fused_log_softmax, reduction, loss, loss_reduced, grad, workspace, plan.lay,
                                plan.max_U1, aligned16);
-    a.small = e->args && plan.lay.n_rows <= kSmallRows;
+    a.small = e->args && plan.lay.n_rows <= kSmallRows && a.max_U1 <= kMaxTileU1;
     return enqueue_path(a, e->args.get(), pad, true, stream);
 }
 
@@ -780,7 +780,7 @@ rnnt_status rnnt_loss_fused_noalloc(const void *logits, rnnt_dtype dtype, int64_
     LaunchArgs a = launch_args(logits, es, N, V, targets, S, B, blank, clamp, fastemit_lambda, fused_log_softmax,
                                reduction, loss, loss_reduced, grad, ws, lay, max_U1, aligned16);
     a.status_out = dev_status;
-    a.small = lay.n_rows <= kSmallRows;
+    a.small = lay.n_rows <= kSmallRows && a.max_U1 <= kMaxTileU1;
     return enqueue_path(a, &pa, Padding(), false, stream);
 }
 

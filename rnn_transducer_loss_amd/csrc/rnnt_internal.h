@@ -202,8 +202,12 @@ constexpr size_t kScratchBytes = (size_t)128 << 20;
 static_assert(kScratchBytes == RNNT_NOALLOC_SCRATCH_BYTES, "the header states the scratch size");
 hipError_t scratch_address(void **ptr);
 
-// Largest lattice width (U+1) the alpha/beta kernel supports.
+// Largest lattice width (U+1) the alpha/beta kernels support: up to
+// kMaxTileU1 one wave holds a whole anti-diagonal (k_alpha_beta, k_ab_small),
+// beyond it several waves share one (k_ab_wide; such batches take the
+// six-launch path).
 constexpr int kMaxU1 = 2048;
+constexpr int kMaxTileU1 = 1024;
 constexpr int kMaxMbU1 = 1024;  // the multi-blank sweep: up to eight groups of 128 columns
 
 // ------------------------------------------------- multi-blank transducer

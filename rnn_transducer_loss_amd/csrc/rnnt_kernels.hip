@@ -954,15 +954,18 @@ template <typename D, int K, int G> struct SweepIO {
     uint32_t win[G][K];
     uint32_t wout[G];
 
-    __device__ SweepIO(const char *w_, double *out_, int U, int nd) : w(w_) {
+    // col0: the first column this wave holds; row_bytes: the output's
+    // diagonal stride (U1p * 8), by default the tile's own width.
+    __device__ SweepIO(const char *w_, double *out_, int U, int nd, uint32_t col0 = 0, uint32_t row_bytes = 0)
+        : w(w_) {
         const uint32_t lane = threadIdx.x & 63;
         const uint32_t U1 = (uint32_t)U + 1;
         w_bytes = U1 * D::kSlot;
-        out_bytes = 64u * K * G * 8u;
+        out_bytes = row_bytes ? row_bytes : 64u * K * G * 8u;
         rout = buffer_at(out_, (uint32_t)nd * out_bytes);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            const uint32_t c = 64u * K * g + K * lane;
+            const uint32_t c = col0 + 64u * K * g + K * lane;
 #pragma unroll
             for (int k = 0; k < K; ++k)  // the log domain clamps to U, the probability domain to the range end
                 win[g][k] = (D::kLog ? min(c + k, (uint32_t)U) : min(c + k, U1)) * D::kSlot;
@@ -1213,11 +1216,7 @@ __device__ __forceinline__ void sweep_sample(const SampleDesc &d, bool bw, bool 
     case 256: run_sweep<4, 1, 8>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z, go); break;
     case 512: run_sweep<4, 2, 4>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z, go); break;
     case 768: run_sweep<4, 3, 3>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z, go); break;
-    case 1024: run_sweep<4, 4, 2>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z, go); break;
-    case 1280: run_sweep<4, 5, 1>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z, go); break;
-    case 1536: run_sweep<4, 6, 1>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z, go); break;
-    case 1792: run_sweep<4, 7, 1>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z, go); break;
-    default: run_sweep<4, 8, 1>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z, go); break;
+    default: run_sweep<4, 4, 2>(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z, go); break;  // 1024
     }
 }
 
@@ -1235,12 +1234,172 @@ __global__ __launch_bounds__(64) void k_alpha_beta(const SampleDesc *__restrict_
                                                    int *__restrict__ ebeta, double *__restrict__ log2z,
                                                    float *__restrict__ loss, int rerun) {
     const SampleDesc d = desc[order[blockIdx.x >> 1]];
+    if (d.U1p > kMaxTileU1) return;  // k_ab_wide's
     const int md = mode[d.index];
     if (rerun && !(md & kModeRerun)) return;  // the rerun takes only the samples k_check_ab marked
     const bool bw = (blockIdx.x & 1) != 0;
     const bool lm = md != 0;
     double *z = bw ? &log2z[d.index] : &log2z[B + d.index];
     sweep_sample(d, bw, lm, node, prob, alpha, beta, ealpha, ebeta, z);
+    if (bw && threadIdx.x == 0) loss[d.index] = (float)(-log2z[d.index] * kLn2D);
+}
+
+// ------------------------------------ lattices wider than 1024 columns
+// One workgroup of NW = U1p / 256 waves per sample and direction (a launch
+// for each NW in 5..8), wave w holding columns 256w .. 256w+255 with the
+// four-column tile, so a diagonal's work is spread over NW waves instead of
+// held by one (~600 ns a diagonal at 2048 columns in one wave's registers).
+// Per diagonal the only value crossing waves is the edge column: each wave
+// leaves it in LDS, one workgroup barrier (LDS only: global stores stay in
+// flight), and its neighbour reads it; two slots alternate by diagonal, so a
+// slot is rewritten only after the barrier that follows its read.  The
+// renormalisation every eighth diagonal takes the largest exponent over all
+// waves (LDS and a barrier), so the diagonal keeps one exponent, as in the
+// single-wave sweep, and the check and gradient read the tables unchanged.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+struct WideShared {
+    double edge[2][8];  // per diagonal parity and wave: the value its neighbour needs
+    int emax[8];        // per wave: the largest biased exponent of its columns
+};
+
+template <int NW> __device__ __forceinline__ int wide_renorm(double (&a)[1][4], int wave, WideShared &sh) {
+    int eb = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) eb = max(eb, (__double2hiint(a[0][k]) >> 20) & 0x7ff);
+    eb = wave_max_nonneg(eb);
+    if ((threadIdx.x & 63) == 0) sh.emax[wave] = eb;
+    lds_barrier();
+    int m = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) m = max(m, sh.emax[i]);
+    const int s = m - 1023;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[0][k] = __builtin_amdgcn_ldexp(a[0][k], -s);
+    return s;
+}
+
+// One forward step of wave `wave`: its column 256w takes the previous wave's
+// last column (its value times its label weight) through LDS.
+template <typename D, int NW>
+__device__ __forceinline__ void wide_forward_step(double (&a)[1][4], const Wts<4> &w, int wave, int par,
+                                                  WideShared &sh) {
+    const int lane = threadIdx.x & 63;
+    double my[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) my[k] = D::edge(a[0][k], w.py(k));
+    if (lane == 63) sh.edge[par][wave] = my[3];
+    lds_barrier();
+    double left = rotate_up(my[3]);
+    if (lane == 0) left = wave > 0 ? sh.edge[par][wave > 0 ? wave - 1 : 0] : D::zero();
+    a[0][0] = D::combine(D::edge(a[0][0], w.pb(0)), left);
+#pragma unroll
+    for (int k = 1; k < 4; ++k) a[0][k] = D::combine(D::edge(a[0][k], w.pb(k)), my[k - 1]);
+}
+
+// One backward step: its column 256w+255 takes the next wave's first column
+// (of the diagonal before the step) through LDS.
+template <typename D, int NW>
+__device__ __forceinline__ void wide_backward_step(double (&b)[1][4], const Wts<4> &w, int wave, int par,
+                                                   WideShared &sh) {
+    const int lane = threadIdx.x & 63;
+    if (lane == 0) sh.edge[par][wave] = b[0][0];
+    lds_barrier();
+    double right = rotate_down(b[0][0]);
+    if (lane == 63) right = wave + 1 < NW ? sh.edge[par][wave + 1 < NW ? wave + 1 : wave] : D::zero();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const double nxt = (k + 1 < 4) ? b[0][k + 1 < 4 ? k + 1 : k] : right;
+        b[0][k] = D::combine(D::edge(b[0][k], w.pb(k)), D::edge(nxt, w.py(k)));
+    }
+}
+
+template <typename D, int NW, int PF>
+__device__ __forceinline__ void wide_sweep(const SampleDesc &d, bool bw, const char *__restrict__ w,
+                                           double *__restrict__ out, int *__restrict__ eout, double *z,
+                                           WideShared &sh) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int U = d.U, nd = d.T + U;
+    const int col0 = 256 * wave;
+    double a[1][4];
+    const int start = bw ? U : 0;  // forward from column 0 of diagonal 0, backward from column U past the end
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[0][k] = (col0 + 4 * lane + k == start) ? D::one() : D::zero();
+    int E = 0;
+    if (wave == 0 && lane == 0) eout[0] = 0;
+    const SweepIO<D, 4, 1> io(w, out, U, nd, (uint32_t)col0, (uint32_t)d.U1p * 8u);
+    Ring<4, 1, PF> ra, rb;
+    // every wave walks the same diagonals, so every wave meets every barrier
+    auto block = [&](const Ring<4, 1, PF> &r, int n0) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            const int n = bw ? n0 - p : n0 + p;
+            if (n < 0 || n >= nd) continue;  // uniform
+            if (!bw) {
+                if (!D::kLog && (n & 7) == 7) {
+                    E += wide_renorm<NW>(a, wave, sh);
+                    if (wave == 0 && lane == 0) eout[(n + 1) >> 3] = E;
+                }
+                io.store(n, a);
+                wide_forward_step<D, NW>(a, r.v[p][0], wave, n & 1, sh);
+            } else {
+                wide_backward_step<D, NW>(a, r.v[p][0], wave, n & 1, sh);
+                if (!D::kLog && ((nd - 1 - n) & 7) == 7) {
+                    E += wide_renorm<NW>(a, wave, sh);
+                    if (wave == 0 && lane == 0) eout[(nd - n) >> 3] = E;
+                }
+                io.store(n, a);
+            }
+        }
+    };
+    const int step = bw ? -1 : 1;
+    int n0 = bw ? nd - 1 : 0;
+    load_block<D, 4, 1, PF>(ra, io, n0, step, nd);
+    for (int done = 0; done < nd; done += 2 * PF) {
+        load_block<D, 4, 1, PF>(rb, io, n0 + step * PF, step, nd);
+        block(ra, n0);
+        load_block<D, 4, 1, PF>(ra, io, n0 + 2 * step * PF, step, nd);
+        block(rb, n0 + step * PF);
+        n0 += 2 * step * PF;
+    }
+    // forward: one step past the last diagonal, column U holds P(y|x); backward: column 0 of diagonal 0
+    const int cz = bw ? 0 : U;
+    if ((cz >> 8) == wave) {
+        double v = 0.0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v = (k == (cz & 3)) ? a[0][k] : v;
+        const double zz = __shfl(v, (cz & 255) >> 2, 64);
+        if (lane == 0) *z = D::kLog ? zz : log2_d(zz) + (double)E;
+    }
+}
+
+// Lattices of 256 * NW columns (U1p), one workgroup of NW waves per sample
+// and direction: workgroup 2k the forward and 2k+1 the backward sweep of
+// the k-th sample in cost order; other samples' workgroups return at once.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void k_ab_wide(const SampleDesc *__restrict__ desc,
+                                                     const int32_t *__restrict__ order, int B,
+                                                     const int *__restrict__ mode, const float4 *__restrict__ node,
+                                                     const float2 *__restrict__ prob, double *__restrict__ alpha,
+                                                     double *__restrict__ beta, int *__restrict__ ealpha,
+                                                     int *__restrict__ ebeta, double *__restrict__ log2z,
+                                                     float *__restrict__ loss, int rerun) {
+    __shared__ WideShared sh;
+    const SampleDesc d = desc[order[blockIdx.x >> 1]];
+    if (d.U1p != 256 * NW) return;  // the whole workgroup
+    const int md = mode[d.index];
+    if (rerun && !(md & kModeRerun)) return;
+    const bool bw = (blockIdx.x & 1) != 0;
+    double *z = bw ? &log2z[d.index] : &log2z[B + d.index];
+    double *out = bw ? beta + d.ab_off : alpha + d.ab_off;
+    int *eout = (bw ? ebeta : ealpha) + d.diag_off;
+    if (md == 0) wide_sweep<ProbDomain, NW, 8>(d, bw, reinterpret_cast<const char *>(prob + d.slot_off), out, eout, z, sh);
+    else wide_sweep<LogDomain, NW, 8>(d, bw, reinterpret_cast<const char *>(node + d.slot_off), out, eout, z, sh);
     if (bw && threadIdx.x == 0) loss[d.index] = (float)(-log2z[d.index] * kLn2D);
 }
 
@@ -1946,6 +2105,18 @@ hipError_t launch_alpha_beta(const LaunchArgs &a, hipStream_t stream) {
                            WS(const int32_t *, order), a.B, WS(const int *, mode), WS(const float4 *, node),
                            WS(const float2 *, prob), WS(double *, alpha), WS(double *, beta), WS(int *, ealpha),
                            WS(int *, ebeta), WS(double *, log2z), a.loss, rerun);
+        if (a.max_U1 > kMaxTileU1) {  // lattices of 1280 .. 2048 padded columns: 5 .. 8 waves each
+            auto wide = [&](auto kern, int nw) {
+                hipLaunchKernelGGL(kern, dim3(2 * a.B), dim3(64 * nw), 0, stream, WS(const SampleDesc *, desc),
+                                   WS(const int32_t *, order), a.B, WS(const int *, mode), WS(const float4 *, node),
+                                   WS(const float2 *, prob), WS(double *, alpha), WS(double *, beta),
+                                   WS(int *, ealpha), WS(int *, ebeta), WS(double *, log2z), a.loss, rerun);
+            };
+            wide(k_ab_wide<5>, 5);
+            wide(k_ab_wide<6>, 6);
+            wide(k_ab_wide<7>, 7);
+            wide(k_ab_wide<8>, 8);
+        }
     }
     return hipGetLastError();
 }
