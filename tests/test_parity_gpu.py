@@ -349,6 +349,31 @@ def test_wide_lattices_in_a_large_batch(rl, fused):
     _reduced_ok(w, loss, red, "mean")
 
 
+def test_wide_lattices_with_options(rl):
+    """A 1700-column lattice (the multi-wave recursion) in fp16 with clamp and FastEmit, against the oracle; the
+    same batch in the padded layout bitwise equal to it, and score-only returning the same losses."""
+    w = _custom([30, 12, 25], [1699, 400, 1300], 24, dtype=torch.float16, std=2.0, blank=-1, clamp=0.3,
+                reduction="sum", seed=73)
+    assert w.N > 64 * 1024 or max(w.target_lengths) + 1 > 1024
+    loss, red, grad, flags = run(rl, w, fastemit=0.02)
+    assert flags == 0
+    check_against_oracle(w, loss, grad, "sum", grad_rows=300, fastemit=0.02)
+    _reduced_ok(w, loss, red, "sum")
+    max_T, max_U1 = max(w.logit_lengths) + 1, max(w.target_lengths) + 2
+    xp = _to_padded(w, max_T, max_U1)
+    tg = torch.from_numpy(w.targets).to("cuda")
+    lp_, _, gp_, _ = rl.rnnt_loss_fused(xp, tg, w.logit_lengths, w.target_lengths, blank=w.blank, clamp=0.3,
+                                        reduction="sum", fused_log_softmax=True, fastemit_lambda=0.02)
+    torch.cuda.synchronize()
+    rows, pad = _padded_rows(w, gp_, max_T, max_U1)
+    assert torch.equal(lp_, loss) and torch.equal(rows, grad) and bool((pad == 0).all())
+    ls, _, _, _ = rl.rnnt_loss_fused(w.logits, tg, w.logit_lengths, w.target_lengths, blank=w.blank, clamp=0.3,
+                                     reduction="sum", fused_log_softmax=True, compute_grad=False,
+                                     fastemit_lambda=0.02)
+    torch.cuda.synchronize()
+    assert torch.equal(ls, loss)
+
+
 def test_ragged_batch_many_samples(rl):
     rng = np.random.default_rng(77)
     B = 150
