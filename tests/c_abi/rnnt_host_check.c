@@ -117,9 +117,10 @@ int main(void) {
         EXPECT(rnnt_loss_fused_workspace_size(3, 16, N, (rnnt_dtype)7, T, U, &ws) == RNNT_INVALID_VALUE);
         EXPECT(rnnt_loss_fused_workspace_size(3, 16, N, RNNT_F32, NULL, U, &ws) == RNNT_INVALID_VALUE);
         EXPECT(rnnt_loss_fused_workspace_size(3, 16, N, RNNT_F32, T, U, NULL) == RNNT_INVALID_VALUE);
-        const int32_t Tz[1] = {0}, Uz[1] = {0}, Ub[1] = {1024}, Tb[1] = {2};
+        const int32_t Tz[1] = {0}, Uz[1] = {0}, Ub[1] = {2048}, Uw[1] = {2047}, Tb[1] = {2};
         EXPECT(rnnt_loss_fused_workspace_size(1, 16, 0, RNNT_F32, Tz, Uz, &ws) == RNNT_INVALID_VALUE);
-        EXPECT(rnnt_loss_fused_workspace_size(1, 16, 2 * 1025, RNNT_F32, Tb, Ub, &ws) == RNNT_INVALID_VALUE);
+        EXPECT(rnnt_loss_fused_workspace_size(1, 16, 2 * 2049, RNNT_F32, Tb, Ub, &ws) == RNNT_INVALID_VALUE);
+        EXPECT(rnnt_loss_fused_workspace_size(1, 16, 2 * 2048, RNNT_F32, Tb, Uw, &ws) == RNNT_SUCCESS && ws > 0);
         const int32_t Un[1] = {-1};
         EXPECT(rnnt_loss_fused_workspace_size(1, 16, 0, RNNT_F32, Tb, Un, &ws) == RNNT_INVALID_VALUE);
         size_t wp = 0;
