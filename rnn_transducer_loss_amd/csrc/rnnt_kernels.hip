@@ -1734,18 +1734,13 @@ __device__ __forceinline__ float clamp_to(float v, float cl, bool do_clamp) {
 // of the vector that holds them: element k is element k % VEC of vector
 // k / VEC, held by lane (k / VEC) mod 64 as its vector number (k / VEC) / 64.
 // The registers are overwritten with the stored gradient.
-// With a rotation h (see k_grad_rows), vector number i is the row's vector
-// (i + h) mod nvec.
-template <typename T, int NV, bool FULL, bool FUSED, bool CLAMP, bool ROT = false>
+template <typename T, int NV, bool FULL, bool FUSED, bool CLAMP>
 __device__ __forceinline__ void grad_row(typename Raw<T>::vec (&xc)[NV], T *dst, const RowTerms &rt, int blank,
-                                         int nvec, float cl, int i0 = 0, int h = 0) {
+                                         int nvec, float cl, int i0 = 0) {
     constexpr int VEC = Raw<T>::kVec;
     const int lane = threadIdx.x & 63;
-    if constexpr (!ROT) h = 0;
-    const int pb = blank / VEC, py = rt.y >= 0 ? rt.y / VEC : -1;  // the row vectors holding them
-    const int eb = blank - pb * VEC, ey = rt.y - py * VEC;
-    auto number_of = [&](int v) { return v >= h ? v - h : v - h + nvec; };  // vector number of row vector v
-    const int vb = ROT ? number_of(pb) : pb, vy = (ROT && py >= 0) ? number_of(py) : py;
+    const int vb = blank / VEC, vy = rt.y >= 0 ? rt.y / VEC : -1;  // the vectors holding them
+    const int eb = blank - vb * VEC, ey = rt.y - vy * VEC;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         const int i = i0 + j;
@@ -1769,8 +1764,7 @@ __device__ __forceinline__ void grad_row(typename Raw<T>::vec (&xc)[NV], T *dst,
 #pragma unroll
             for (int e = 0; e < VEC; ++e) gv[e] = clamp_to(gv[e], cl, CLAMP);
             xc[j] = Raw<T>::put(gv);
-            const int v = vi + h;
-            store_raw<T, true>(dst + (int64_t)(ROT && v >= nvec ? v - nvec : v) * VEC, xc[j]);
+            store_raw<T, true>(dst + (int64_t)vi * VEC, xc[j]);
         }
     }
 }
@@ -1791,7 +1785,7 @@ __device__ __forceinline__ void grad_row(typename Raw<T>::vec (&xc)[NV], T *dst,
 // log-prob inputs (a write-only pass) take the unmasked form, with the split
 // fixed when it is one (4 KiB rows: 0.995 ms against 1.016 at run time and
 // 1.045 masked).
-template <typename T, bool FUSED, bool CLAMP, int SPLIT, bool FULL, bool ROT>
+template <typename T, bool FUSED, bool CLAMP, int SPLIT, bool FULL>
 __global__ __launch_bounds__(64) void k_grad_rows(const T *logits, T *grad, int blocks_per_chunk,
                                                   int64_t block_base, int split_rt, RNNT_GRAD_PARAMS) {
     constexpr int VEC = Raw<T>::kVec;
@@ -1814,31 +1808,139 @@ __global__ __launch_bounds__(64) void k_grad_rows(const T *logits, T *grad, int 
     const int u = (c.row_begin + r) - t * U1;
     const int64_t row = row_of(d, t, u);
     using Vec = typename Raw<T>::vec;
-    // ROT (rows that may start inside a 128-byte line: their length is no
-    // multiple of 128 bytes, or the gradient is not 128-byte aligned): the
-    // row is walked from its first line boundary, vector number i being the
-    // row's vector (i + h) mod nvec, h the vectors before that boundary
-    // (they come last), so each instruction's 64 vectors fill whole lines of
-    // the gradient.  Cut at the row start, every instruction began and ended
-    // mid-line (20000-byte fp32 rows: 5.41 -> 5.13 ms; 20480-byte rows, with
-    // more data, 4.78).  Other rows take the plain form: the index
-    // arithmetic costs 2-3% where there is nothing to gain.
-    T *dst = grad + row * (int64_t)V;
-    const int h = ROT ? (int)(((128u - ((uint32_t)reinterpret_cast<uintptr_t>(dst) & 127u)) & 127u) >> 4) : 0;
     Vec x[NV];
     if constexpr (FUSED) {
         const T *p = logits + row * (int64_t)V;
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
             const int vi = (i0 + j) * 64 + lane;
-            const int v = vi + h;
-            if (FULL || vi < nvec) x[j] = load_raw<T, true>(p + (int64_t)(ROT && v >= nvec ? v - nvec : v) * VEC);
+            if (FULL || vi < nvec) x[j] = load_raw<T, true>(p + (int64_t)vi * VEC);
         }
     }
     const SampleTerms st{log2z[d.index], mode[d.index] != 0};
     const RowTerms rt = row_terms(d, st, t, u, node, alpha, beta, ealpha, ebeta, log2_scale, scale, fastemit,
                                   scale_y, FUSED, V, blank, targets, S);
-    grad_row<T, NV, FULL, FUSED, CLAMP, ROT>(x, dst, rt, blank, nvec, clamp * scale, i0, h);
+    grad_row<T, NV, FULL, FUSED, CLAMP>(x, grad + row * (int64_t)V, rt, blank, nvec, clamp * scale, i0);
+}
+
+// The gradient of rows whose boundaries can fall inside a 128-byte line (a
+// row length that is no multiple of 128 bytes, or a gradient that is not
+// 128-byte aligned), one wave per part of at most 4 KiB as in k_grad_rows.
+// A line that holds the end of one row and the start of the next, where the
+// two rows are adjacent in memory and in the lattice ((t, u) and (t, u+1), or
+// (t, U) and (t+1, 0) when the time steps are packed without padding), is
+// written whole by the later row's waves, which compute the earlier row's
+// last vectors with that row's terms: written in two pieces by two
+// workgroups, each such line cost as much as many whole ones (20000-byte fp32
+// rows streamed 7-9% slower than 19968- or 20480-byte ones, 4000-byte rows
+// 12% slower than 3968-byte ones).  The vectors a row's waves take, from
+// position 0: the kp vectors of the previous row in the line holding the
+// row's start (if they are adjacent), then the row's own vectors, except those
+// in the line holding its end when the next row takes that line.  A row
+// whose predecessor is not adjacent starts mid-line, and its walk begins at
+// its first line boundary (vector number i is position (i + h) mod nw, the h
+// vectors before that boundary last), so that each instruction's 64 vectors
+// still fill whole lines.  Every element is computed as k_grad_rows computes
+// it, so both give the same bits.
+template <typename T, bool FUSED, bool CLAMP>
+__global__ __launch_bounds__(64) void k_grad_rows_line(const T *logits, T *grad, int blocks_per_chunk,
+                                                       int64_t block_base, int split, RNNT_GRAD_PARAMS) {
+    constexpr int VEC = Raw<T>::kVec;
+    constexpr int NV = 4;
+    if (red.on && blockIdx.x == 0)
+        reduce_losses(red.loss, log2z, red.B, red.mean, red.out, red.status, red.status_out, red.sflags);
+    const int bpc = blocks_per_chunk;
+    const int64_t b = block_base + blockIdx.x;
+    const ChunkDesc c = chunks[n_chunks - 1 - (int)(b / bpc)];
+    const int part = (int)(b % bpc);
+    const int r = part / split;
+    if (r >= c.count) return;
+    const int i0 = (part % split) * NV;  // first vector number of this wave's part
+    const SampleDesc d = desc[c.sample];
+    const int lane = threadIdx.x & 63;
+    const int nvec = V / VEC;
+    const int U1 = d.U + 1;
+    const int t = (c.row_begin + r) / U1;
+    const int u = (c.row_begin + r) - t * U1;
+    const int64_t row = row_of(d, t, u);
+    // the rows before and after this one in memory, if they are its lattice neighbours
+    const bool packed = d.tstride == U1;
+    const bool adj_prev = u > 0 || (packed && t > 0);
+    const bool adj_next = u < d.U || (packed && t < d.T - 1);
+    const uint32_t so = (uint32_t)reinterpret_cast<uintptr_t>(grad + row * (int64_t)V) & 127u;  // start in its line
+    const uint32_t eo = (so + (uint32_t)V * (uint32_t)sizeof(T)) & 127u;                       // end in its line
+    const int kp = adj_prev ? (int)(so >> 4) : 0;               // the previous row's vectors at the front
+    const int nw = kp + nvec - (adj_next ? (int)(eo >> 4) : 0);  // vectors this row's waves take
+    // (a part past nw exists only where some row of the launch takes nvec + kp
+    // vectors across one more part than the row alone needs)
+    if (i0 * 64 >= nw) return;
+    const int h = adj_prev ? 0 : (int)(((128u - so) & 127u) >> 4);
+    const int64_t e0 = row * (int64_t)V - (int64_t)kp * VEC;  // element offset of position 0
+    auto position = [&](int vi) { const int v = vi + h; return v >= nw ? v - nw : v; };
+    using Vec = typename Raw<T>::vec;
+    Vec x[NV];
+    if constexpr (FUSED) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int vi = (i0 + j) * 64 + lane;
+            if (vi < nw) x[j] = load_raw<T, true>(logits + e0 + (int64_t)position(vi) * VEC);
+        }
+    }
+    const SampleTerms st{log2z[d.index], mode[d.index] != 0};
+    const RowTerms rt = row_terms(d, st, t, u, node, alpha, beta, ealpha, ebeta, log2_scale, scale, fastemit,
+                                  scale_y, FUSED, V, blank, targets, S);
+    // the previous row's terms, for the part that holds its vectors (positions
+    // below kp; h = 0 whenever kp > 0, so these are vector numbers 0 .. kp-1)
+    RowTerms rp = rt;
+    if (kp > 0 && i0 == 0)
+        rp = row_terms(d, st, u > 0 ? t : t - 1, u > 0 ? u - 1 : d.U, node, alpha, beta, ealpha, ebeta, log2_scale,
+                       scale, fastemit, scale_y, FUSED, V, blank, targets, S);
+    // vector numbers of the blank and label elements: this row's vector k at
+    // position kp + k (if this row's waves take it), the previous row's at
+    // k - (nvec - kp) (if among its last kp vectors); -1 where not taken here
+    auto number_of = [&](int pos) { return pos < 0 || pos >= nw ? -1 : (pos >= h ? pos - h : pos - h + nw); };
+    const int pb = blank / VEC, eb = blank - pb * VEC;
+    const int py = rt.y >= 0 ? rt.y / VEC : -1, ey = rt.y - py * VEC;
+    const int pyp = rp.y >= 0 ? rp.y / VEC : -1, eyp = rp.y - pyp * VEC;
+    const int vb = number_of(kp + pb), vy = py >= 0 ? number_of(kp + py) : -1;
+    const int vbp = kp > 0 ? number_of(pb - (nvec - kp)) : -1;
+    const int vyp = (kp > 0 && pyp >= 0) ? number_of(pyp - (nvec - kp)) : -1;
+    const float cl = clamp * scale;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int i = i0 + j;
+        const int vi = i * 64 + lane;
+        if (vi < nw) {
+            const bool prev = vi < kp;
+            const float m = prev ? rp.m : rt.m, shift2 = prev ? rp.shift2 : rt.shift2;
+            float gv[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                float v = 0.f;
+                if constexpr (FUSED) v = exp2_fast(fmaf(Raw<T>::get(x[j], e) - m, kLog2e, shift2));
+                gv[e] = v;
+            }
+            if ((vb >> 6) == i) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) gv[e] -= (vi == vb && e == eb) ? rt.fb : 0.f;
+            }
+            if ((vy >> 6) == i) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) gv[e] -= (vi == vy && e == ey) ? rt.fy : 0.f;
+            }
+            if (i == 0 && kp > 0) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    gv[e] -= (vi == vbp && e == eb) ? rp.fb : 0.f;
+                    gv[e] -= (vi == vyp && e == eyp) ? rp.fy : 0.f;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) gv[e] = clamp_to(gv[e], cl, CLAMP);
+            x[j] = Raw<T>::put(gv);
+            store_raw<T, true>(grad + e0 + (int64_t)position(vi) * VEC, x[j]);
+        }
+    }
 }
 
 template <typename T, int VEC, int G, bool FUSED>
@@ -2162,23 +2264,31 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
             void (*kern)(const T *, T *, int, int64_t, int, int, int, int, int, float, float, float, float, float,
                          const int32_t *, const SampleDesc *, const ChunkDesc *, const int *, const double *,
                          const float4 *, const double *, const double *, const int *, const int *, ReduceArgs);
-            const bool full = (int64_t)a.V * a.esize % 4096 == 0;  // every part a whole 4 KiB
-            // rows that can start inside a 128-byte line
-            const bool rot = (int64_t)a.V * a.esize % 128 != 0 || reinterpret_cast<uintptr_t>(a.grad) % 128 != 0;
-            if (a.fused && rot)
-                kern = cl ? k_grad_rows<T, true, true, 0, false, true> : k_grad_rows<T, true, false, 0, false, true>;
-            else if (a.fused)
-                kern = cl ? k_grad_rows<T, true, true, 0, false, false> : k_grad_rows<T, true, false, 0, false, false>;
+            const uint32_t row_bytes = (uint32_t)a.V * (uint32_t)a.esize;
+            const bool full = row_bytes % 4096 == 0;  // every part a whole 4 KiB
+            // rows that can start inside a 128-byte line: k_grad_rows_line
+            const uint32_t g0 = (uint32_t)(reinterpret_cast<uintptr_t>(a.grad) & 127u);
+            const bool line = row_bytes % 128 != 0 || g0 != 0;
+            int split = a.geom.stream_parts;
+            if (line) {
+                // Row starts fall at g0 + k * row_bytes (mod 128), i.e. on the
+                // multiples of q = gcd(row_bytes, 128) offset by g0 mod q; a row
+                // takes up to (its start's offset) / 16 vectors of the previous row
+                uint32_t q = 128;
+                while (row_bytes % q != 0) q >>= 1;
+                const int kp_max = (int)((g0 % q + 128 - q) >> 4);
+                split = (int)((row_bytes / 16 + kp_max + 255) / 256);
+                kern = a.fused ? (cl ? k_grad_rows_line<T, true, true> : k_grad_rows_line<T, true, false>)
+                               : (cl ? k_grad_rows_line<T, false, true> : k_grad_rows_line<T, false, false>);
+            } else if (a.fused)
+                kern = cl ? k_grad_rows<T, true, true, 0, false> : k_grad_rows<T, true, false, 0, false>;
             else if (full && a.geom.stream_parts == 1)
-                kern = cl ? k_grad_rows<T, false, true, 1, true, false> : k_grad_rows<T, false, false, 1, true, false>;
+                kern = cl ? k_grad_rows<T, false, true, 1, true> : k_grad_rows<T, false, false, 1, true>;
             else if (full)
-                kern = cl ? k_grad_rows<T, false, true, 0, true, false> : k_grad_rows<T, false, false, 0, true, false>;
-            else if (rot)
-                kern = cl ? k_grad_rows<T, false, true, 0, false, true> : k_grad_rows<T, false, false, 0, false, true>;
+                kern = cl ? k_grad_rows<T, false, true, 0, true> : k_grad_rows<T, false, false, 0, true>;
             else
-                kern = cl ? k_grad_rows<T, false, true, 0, false, false> : k_grad_rows<T, false, false, 0, false, false>;
+                kern = cl ? k_grad_rows<T, false, true, 0, false> : k_grad_rows<T, false, false, 0, false>;
             // one launch per 2^24 workgroups, so no launch exceeds 32-bit work-item counts
-            const int split = a.geom.stream_parts;
             const int bpc = a.lay.rows_per_chunk * split;
             const int64_t total = (int64_t)a.lay.n_chunks * bpc;
             constexpr int64_t kMaxBlocks = (int64_t)1 << 24;

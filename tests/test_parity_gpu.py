@@ -240,6 +240,36 @@ def test_padded_layout_matches_packed(rl, V, dtype, fused, size):
     check_against_oracle(w, loss, grad, "sum", grad_rows=("all" if fused else 64) if size == "small" else 300)
 
 
+@pytest.mark.parametrize("V,dtype,fused", [(1000, torch.float32, True), (2504, torch.float16, True),
+                                           (1000, torch.float32, False)])
+def test_padded_rows_sharing_lines(rl, V, dtype, fused):
+    """Rows whose boundaries fall inside 128-byte lines (4000- and 5008-byte rows), in the padded layout with
+    max_U1 = max(U)+1: in the widest sample the time steps follow each other in memory, so its line shared by
+    (t, U) and (t+1, 0) goes whole to the later row's wave, while the other samples' time steps end at padding.
+    Bitwise equal to the packed call, the padding zero, in place equal to out of place, and the packed call
+    against the oracle."""
+    Ts, Us = [23, 9, 30, 1], [11, 4, 11, 0]
+    w = workloads.make_custom(Ts, Us, V, dtype=dtype, std=2.0 if fused else 1.5, fused=fused, reduction="sum",
+                              seed=83, device="cuda", prenormalise=not fused)
+    max_T, max_U1 = max(Ts) + 2, max(Us) + 1
+    xp = _to_padded(w, max_T, max_U1, fill=0.0)
+    tg = torch.from_numpy(w.targets).to("cuda")
+    loss_p, red_p, grad_p, ws = rl.rnnt_loss_fused(xp, tg, w.logit_lengths, w.target_lengths, blank=w.blank,
+                                                   reduction="sum", fused_log_softmax=fused)
+    assert rl.device_flags(ws) == 0
+    loss, red, grad, _ = run(rl, w)
+    y = xp.clone()
+    loss_i, _, grad_i, _ = rl.rnnt_loss_fused(y, tg, w.logit_lengths, w.target_lengths, blank=w.blank,
+                                              reduction="sum", fused_log_softmax=fused, inplace=True)
+    torch.cuda.synchronize()
+    assert torch.equal(loss_p, loss) and torch.equal(red_p, red)
+    rows, pad = _padded_rows(w, grad_p, max_T, max_U1)
+    assert torch.equal(rows, grad)
+    assert pad.numel() > 0 and bool((pad == 0).all())
+    assert grad_i.data_ptr() == y.data_ptr() and torch.equal(loss_i, loss_p) and torch.equal(y, grad_p)
+    check_against_oracle(w, loss, grad, "sum", grad_rows="all")
+
+
 def test_padded_inplace_and_autograd(rl):
     Ts, Us = [30, 12, 21], [7, 3, 10]
     w = workloads.make_custom(Ts, Us, 320, std=2.0, reduction="none", seed=78, device="cuda")
@@ -443,10 +473,12 @@ def test_unaligned_logits_pointer(rl):
                                            (5000, torch.float32, True), (300, torch.float32, True),
                                            (2504, torch.float16, True), (1000, torch.float32, False)])
 def test_rows_off_128_byte_lines(rl, V, dtype, fused):
-    """Logits and gradient 16 bytes past a 128-byte boundary: rows of 4 KiB parts start inside a line, so the
-    wide gradient pass walks each row from its first line boundary (as it does for 20000- and 1200-byte rows
-    anywhere).  The row pass reads the same rows in the same lane order, and the gradient is elementwise, so
-    everything is bitwise equal to the aligned call; the aligned call is checked against the oracle."""
+    """Logits and gradient 16 bytes past a 128-byte boundary: every row starts inside a line, so the gradient
+    pass gives each line shared by two adjacent rows to the later row's wave, which computes the earlier row's
+    last vectors too (as it does for 20000- and 1200-byte rows anywhere); with 4 KiB rows that takes a second,
+    nearly empty part per row.  The row pass reads the same rows in the same lane order, and the gradient is
+    elementwise, so everything is bitwise equal to the aligned call; the aligned call is checked against the
+    oracle."""
     w = _custom([37, 22], [9, 14], V, dtype=dtype, std=2.0 if fused else 1.5, blank=-1, fused=fused,
                 prenormalise=not fused, reduction="sum", seed=61)
     tg = torch.from_numpy(w.targets).to("cuda")
