@@ -502,14 +502,15 @@ __global__ __launch_bounds__(256) void k_plan(const SampleDesc *__restrict__ des
 }
 
 // ------------------------------------ K1 rowstats, rows wider than 1 KiB
-// Rows above 4 KiB: one row per wave (sixteen waves per workgroup, measured
+// Rows above 5 KiB: one row per wave (sixteen waves per workgroup, measured
 // fastest there: 16 against 8 waves 1.3% faster on 8 KiB and 2.4% on 20 KB
-// rows; rows of 1 to 4 KiB take k_rowstats_multi below, eight waves of two
+// rows; rows of 1 to 5 KiB take k_rowstats_multi below, eight waves of two
 // rows at a time, where one row per wave had measured 8 waves 2% faster than
 // 4 and 9% faster than 16; a chunk's nodes in diagonal order, so the waves'
 // per-node records land in consecutive slots), the row walked in
 // segments of 4 KiB (four 16-byte vectors per lane, non-temporal loads) with
-// the next segment's loads in flight.  Holding only two segments, a wave
+// the next segment's loads in flight (segments of five vectors, two instead
+// of three for 8208-byte rows, measured 23% slower).  Holding only two segments, a wave
 // needs few registers, so many waves (rows) are in flight per compute unit:
 // measured faster than holding whole rows in registers (three row buffers
 // of up to 16 vectors per lane) on 4 KiB and 8 KiB rows, and the only form
@@ -595,18 +596,18 @@ __global__ __launch_bounds__(64 * W) void k_rowstats_stream(const T *__restrict_
     row_work_end(src, &wg_flags);
 }
 
-// Rows of 1 to 4 KiB (one segment, four vectors per lane): each wave takes R
+// Rows of 1 to 5 KiB (one segment of NS = 4 vectors per lane up to 4 KiB, 5
+// above, so a row a little over 4 KiB takes one step rather than two): each wave takes R
 // of its rows at a time, r, r + W, ..., r + (R-1) W, with the loads of all
 // of them in flight together and their reductions interleaved.  Per row the
 // arithmetic is the streaming kernel's, lane for lane.  Launched with R = 2
 // (4 KiB fp32 rows: 0.438 -> 0.431 ms against one row at a time; four rows
 // 0.442).
-template <typename T, int W, int R, typename Src>
+template <typename T, int W, int R, int NS, typename Src>
 __global__ __launch_bounds__(64 * W) void k_rowstats_multi(const T *__restrict__ logits, int V, int blank, Src src,
                                                         const int32_t *__restrict__ targets, int S,
                                                         float4 *__restrict__ node, float2 *__restrict__ prob) {
     constexpr int VEC = Raw<T>::kVec;
-    constexpr int NS = 4;
     using Vec = typename Raw<T>::vec;
     __shared__ uint32_t wg_flags;
     const RowWork wk = row_work<true>(src, &wg_flags);
@@ -1770,8 +1771,10 @@ __device__ __forceinline__ void grad_row(typename Raw<T>::vec (&xc)[NV], T *dst,
 }
 
 // The gradient, one wave per workgroup and `split` workgroups per row (SPLIT,
-// when the launch fixes it at compile time), each taking a 4 KiB part (four
-// 16-byte vectors per lane; the last part may be partial unless FULL): each
+// when the launch fixes it at compile time), each taking a part of NV 16-byte
+// vectors per lane (4 KiB at NV = 4; NV = 5 makes a row of 4 to 5 KiB one
+// part instead of a whole one and a nearly empty one; the last part may be
+// partial unless FULL): each
 // wave loads its part
 // of the row, computes and stores it, and exits.  Many single-wave
 // workgroups of 4 KiB keep enough rows in flight without a prefetch ring
@@ -1785,11 +1788,10 @@ __device__ __forceinline__ void grad_row(typename Raw<T>::vec (&xc)[NV], T *dst,
 // log-prob inputs (a write-only pass) take the unmasked form, with the split
 // fixed when it is one (4 KiB rows: 0.995 ms against 1.016 at run time and
 // 1.045 masked).
-template <typename T, bool FUSED, bool CLAMP, int SPLIT, bool FULL>
+template <typename T, bool FUSED, bool CLAMP, int SPLIT, bool FULL, int NV>
 __global__ __launch_bounds__(64) void k_grad_rows(const T *logits, T *grad, int blocks_per_chunk,
                                                   int64_t block_base, int split_rt, RNNT_GRAD_PARAMS) {
     constexpr int VEC = Raw<T>::kVec;
-    constexpr int NV = 4;
     if (red.on && blockIdx.x == 0)
         reduce_losses(red.loss, log2z, red.B, red.mean, red.out, red.status, red.status_out, red.sflags);
     const int bpc = blocks_per_chunk;
@@ -1842,11 +1844,10 @@ __global__ __launch_bounds__(64) void k_grad_rows(const T *logits, T *grad, int 
 // vectors before that boundary last), so that each instruction's 64 vectors
 // still fill whole lines.  Every element is computed as k_grad_rows computes
 // it, so both give the same bits.
-template <typename T, bool FUSED, bool CLAMP>
+template <typename T, bool FUSED, bool CLAMP, int NV>
 __global__ __launch_bounds__(64) void k_grad_rows_line(const T *logits, T *grad, int blocks_per_chunk,
                                                        int64_t block_base, int split, RNNT_GRAD_PARAMS) {
     constexpr int VEC = Raw<T>::kVec;
-    constexpr int NV = 4;
     if (red.on && blockIdx.x == 0)
         reduce_losses(red.loss, log2z, red.B, red.mean, red.out, red.status, red.status_out, red.sflags);
     const int bpc = blocks_per_chunk;
@@ -2152,8 +2153,14 @@ hipError_t launch_rowstats_with(const LaunchArgs &a, const Src &src, hipStream_t
     if (a.geom.stream_parts > 0) {
         auto go = [&](auto tag) {
             using T = decltype(tag);
-            auto kern = a.geom.stream_parts == 1 ? k_rowstats_multi<T, 8, 2, Src> : k_rowstats_stream<T, 16, Src>;
-            const dim3 wblock(a.geom.stream_parts == 1 ? 512 : 1024);
+            // rows of up to 4 KiB in one step of four vectors per lane, up to
+            // 5 KiB in one step of five (4112-byte fp32 rows: 0.791 -> 0.608 ms
+            // against two segments of the streaming kernel), wider rows streamed
+            const int nvec = a.V * a.esize / 16;
+            auto kern = nvec <= 256 ? k_rowstats_multi<T, 8, 2, 4, Src>
+                        : nvec <= 320 ? k_rowstats_multi<T, 8, 2, 5, Src>
+                                      : k_rowstats_stream<T, 16, Src>;
+            const dim3 wblock(nvec <= 320 ? 512 : 1024);
             hipLaunchKernelGGL(kern, grid, wblock, 0, stream, static_cast<const T *>(a.logits), a.V, a.blank, src,
                                a.targets, a.S, WS(float4 *, node), WS(float2 *, prob));
             return hipGetLastError();
@@ -2254,7 +2261,7 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
     g.beta = WS(const double *, beta);
     g.ealpha = WS(const int *, ealpha);
     g.ebeta = WS(const int *, ebeta);
-    // Rows of more than 1 KiB: one single-wave workgroup per 4 KiB part of a row.
+    // Rows of more than 1 KiB: one single-wave workgroup per part of 4 or 5 KiB of a row.
     if (a.geom.stream_parts > 0) {
         auto rows = [&](auto ttag) -> hipError_t {
             using T = decltype(ttag);
@@ -2265,29 +2272,43 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
                          const int32_t *, const SampleDesc *, const ChunkDesc *, const int *, const double *,
                          const float4 *, const double *, const double *, const int *, const int *, ReduceArgs);
             const uint32_t row_bytes = (uint32_t)a.V * (uint32_t)a.esize;
+            const int nvec = (int)(row_bytes / 16);
             const bool full = row_bytes % 4096 == 0;  // every part a whole 4 KiB
             // rows that can start inside a 128-byte line: k_grad_rows_line
             const uint32_t g0 = (uint32_t)(reinterpret_cast<uintptr_t>(a.grad) & 127u);
             const bool line = row_bytes % 128 != 0 || g0 != 0;
-            int split = a.geom.stream_parts;
-            if (line) {
-                // Row starts fall at g0 + k * row_bytes (mod 128), i.e. on the
-                // multiples of q = gcd(row_bytes, 128) offset by g0 mod q; a row
-                // takes up to (its start's offset) / 16 vectors of the previous row
-                uint32_t q = 128;
-                while (row_bytes % q != 0) q >>= 1;
-                const int kp_max = (int)((g0 % q + 128 - q) >> 4);
-                split = (int)((row_bytes / 16 + kp_max + 255) / 256);
-                kern = a.fused ? (cl ? k_grad_rows_line<T, true, true> : k_grad_rows_line<T, true, false>)
-                               : (cl ? k_grad_rows_line<T, false, true> : k_grad_rows_line<T, false, false>);
-            } else if (a.fused)
-                kern = cl ? k_grad_rows<T, true, true, 0, false> : k_grad_rows<T, true, false, 0, false>;
+            // Row starts fall at g0 + k * row_bytes (mod 128), i.e. on the
+            // multiples of q = gcd(row_bytes, 128) offset by g0 mod q; a row
+            // of k_grad_rows_line takes up to (its start's offset) / 16
+            // vectors of the previous row
+            uint32_t q = 128;
+            while (row_bytes % q != 0) q >>= 1;
+            const int span = nvec + (line ? (int)((g0 % q + 128 - q) >> 4) : 0);  // most vectors of a row's waves
+            // One part of five vectors per lane (5 KiB) for a row of 4 to 5 KiB
+            // (4112-byte fp32 rows: 1.640 -> 1.335 ms against a whole part and
+            // one of a single vector); wider rows keep parts of four (two parts
+            // of five instead of three of four measured 9-10% slower on 8208-
+            // and 8704-byte rows)
+            const bool five = span > 256 && span <= 320;
+            const int split = five ? (span + 319) / 320 : (span + 255) / 256;
+            if (line && five)
+                kern = a.fused ? (cl ? k_grad_rows_line<T, true, true, 5> : k_grad_rows_line<T, true, false, 5>)
+                               : (cl ? k_grad_rows_line<T, false, true, 5> : k_grad_rows_line<T, false, false, 5>);
+            else if (line)
+                kern = a.fused ? (cl ? k_grad_rows_line<T, true, true, 4> : k_grad_rows_line<T, true, false, 4>)
+                               : (cl ? k_grad_rows_line<T, false, true, 4> : k_grad_rows_line<T, false, false, 4>);
+            else if (a.fused && five)
+                kern = cl ? k_grad_rows<T, true, true, 0, false, 5> : k_grad_rows<T, true, false, 0, false, 5>;
+            else if (a.fused)
+                kern = cl ? k_grad_rows<T, true, true, 0, false, 4> : k_grad_rows<T, true, false, 0, false, 4>;
             else if (full && a.geom.stream_parts == 1)
-                kern = cl ? k_grad_rows<T, false, true, 1, true> : k_grad_rows<T, false, false, 1, true>;
+                kern = cl ? k_grad_rows<T, false, true, 1, true, 4> : k_grad_rows<T, false, false, 1, true, 4>;
             else if (full)
-                kern = cl ? k_grad_rows<T, false, true, 0, true> : k_grad_rows<T, false, false, 0, true>;
+                kern = cl ? k_grad_rows<T, false, true, 0, true, 4> : k_grad_rows<T, false, false, 0, true, 4>;
+            else if (five)
+                kern = cl ? k_grad_rows<T, false, true, 0, false, 5> : k_grad_rows<T, false, false, 0, false, 5>;
             else
-                kern = cl ? k_grad_rows<T, false, true, 0, false> : k_grad_rows<T, false, false, 0, false>;
+                kern = cl ? k_grad_rows<T, false, true, 0, false, 4> : k_grad_rows<T, false, false, 0, false, 4>;
             // one launch per 2^24 workgroups, so no launch exceeds 32-bit work-item counts
             const int bpc = a.lay.rows_per_chunk * split;
             const int64_t total = (int64_t)a.lay.n_chunks * bpc;

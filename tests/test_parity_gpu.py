@@ -325,6 +325,24 @@ def test_wide_rows_split_over_waves(rl, V, dtype, clamp):
     check_against_oracle(w, loss, grad, "mean")
 
 
+@pytest.mark.parametrize("V,dtype,clamp,fused", [
+    (1028, torch.float32, -1.0, True),    # 4112-byte rows: shared lines, one part of five vectors per lane
+    (1088, torch.float32, 0.3, True),     # 4352-byte rows on line boundaries, clamp
+    (2056, torch.float16, -1.0, True),    # fp16 rows of 4112 bytes
+    (2112, torch.float16, -1.0, False),   # log-prob inputs, 4224-byte rows
+    (1280, torch.float32, -1.0, False),   # 5120-byte rows: the part exactly full
+])
+def test_rows_of_4_to_5_kib(rl, V, dtype, clamp, fused):
+    """Rows a little over 4 KiB: the row pass takes each in one step of five vectors per lane and the gradient
+    in one wave of five vectors per lane (where four would leave a second, nearly empty part); every gradient
+    row against the oracle."""
+    w = _custom([9, 6], [7, 10], V, dtype=dtype, std=2.0 if fused else 1.5, blank=-1, clamp=clamp, fused=fused,
+                prenormalise=not fused, reduction="mean", seed=V + 1)
+    loss, red, grad, flags = run(rl, w)
+    assert flags == 0
+    check_against_oracle(w, loss, grad, "mean")
+
+
 @pytest.mark.parametrize("V,dtype,clamp,fused,lam", [
     (5000, torch.float32, -1.0, True, 0.0),      # 20000-byte rows: five 4 KiB segments, the last partial
     (8192, torch.float32, 0.05, True, 0.3),      # 32 KiB rows, clamp, FastEmit
