@@ -502,6 +502,25 @@ __global__ __launch_bounds__(256) void k_plan(const SampleDesc *__restrict__ des
 }
 
 // ------------------------------------ K1 rowstats, rows wider than 1 KiB
+// Rows that do not all start on a 16-byte boundary (ODD: a row length that is
+// no multiple of 16 bytes, or logits off such a boundary) are read in the
+// 16-byte vectors that cover them, from the one holding the row's first
+// element (`lead` elements before it): slots outside the row read -inf, which
+// the maximum ignores and the sum of exponentials counts as zero.  Such a
+// vector never leaves the 16-byte block, so the page, of the row's first or
+// last element.
+template <typename T>
+__device__ __forceinline__ void mask_outside_row(typename Raw<T>::vec &x, int first, int V) {
+    if (first < 0 || first + Raw<T>::kVec > V) {  // first: the row's index of slot 0
+#pragma unroll
+        for (int e = 0; e < Raw<T>::kVec; ++e)
+            if (first + e < 0 || first + e >= V) x[e] = (T)kNegInf;
+    }
+}
+template <typename T> __device__ __forceinline__ int lead_of(const T *p) {
+    return (int)((reinterpret_cast<uintptr_t>(p) & 15u) / sizeof(T));
+}
+
 // Rows above 5 KiB: one row per wave (sixteen waves per workgroup, measured
 // fastest there: 16 against 8 waves 1.3% faster on 8 KiB and 2.4% on 20 KB
 // rows; rows of 1 to 5 KiB take k_rowstats_multi below, eight waves of two
@@ -529,7 +548,7 @@ __global__ __launch_bounds__(256) void k_plan(const SampleDesc *__restrict__ des
 // elements and the sum of exp(x - that maximum), rescaled when it grows; at
 // the end of the row the lanes' sums are rescaled to the row maximum and
 // added.  Every term is formed from x - maximum, as in the other row passes.
-template <typename T, int W, typename Src>
+template <typename T, int W, bool ODD, typename Src>
 __global__ __launch_bounds__(64 * W) void k_rowstats_stream(const T *__restrict__ logits, int V, int blank, Src src,
                                                          const int32_t *__restrict__ targets, int S,
                                                          float4 *__restrict__ node, float2 *__restrict__ prob) {
@@ -551,21 +570,28 @@ __global__ __launch_bounds__(64 * W) void k_rowstats_stream(const T *__restrict_
         const int y = __builtin_amdgcn_readfirstlane(read_label(d, u, V, blank, targets, S, wk.status_word));
         const float hb = Elem<T>::load1(p + blank);
         const float hy = (y >= 0) ? Elem<T>::load1(p + y) : 0.f;
+        const int lead = ODD ? lead_of(p) : 0;
+        const T *pv = p - lead;
+        const int nvr = ODD ? (lead + V + VEC - 1) / VEC : nvec;  // vectors covering the row
+        const int nsegr = ODD ? (nvr + 64 * NS - 1) / (64 * NS) : nseg;
         auto load_seg = [&](int sg, Vec (&x)[NS]) {
 #pragma unroll
             for (int i = 0; i < NS; ++i) {
                 const int vi = (sg * NS + i) * 64 + lane;
-                if (vi < nvec) x[i] = load_raw<T, true>(p + (int64_t)vi * VEC);
+                if (vi < nvr) {
+                    x[i] = load_raw<T, true>(pv + (int64_t)vi * VEC);
+                    if constexpr (ODD) mask_outside_row<T>(x[i], vi * VEC - lead, V);
+                }
             }
         };
         float m = kNegInf, nm = 0.f, s = 0.f;
         auto take_seg = [&](int sg, const Vec (&x)[NS]) {
-            const float mn = fmaxf(m, row_max<T, NS, false>(x, nvec - sg * NS * 64));
+            const float mn = fmaxf(m, row_max<T, NS, false>(x, nvr - sg * NS * 64));
             const float nmn = (mn == kNegInf) ? 0.f : -mn * kLog2e;
             float acc = (m == kNegInf) ? 0.f : s * exp2_fast(nmn - nm);
 #pragma unroll
             for (int i = 0; i < NS; ++i)
-                if ((sg * NS + i) * 64 + lane < nvec)
+                if ((sg * NS + i) * 64 + lane < nvr)
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) acc += exp2_fast(fmaf(Raw<T>::get(x[i], e), kLog2e, nmn));
             s = acc;
@@ -574,11 +600,11 @@ __global__ __launch_bounds__(64 * W) void k_rowstats_stream(const T *__restrict_
         };
         Vec xa[NS], xb[NS];
         load_seg(0, xa);
-        for (int sg = 0; sg < nseg; sg += 2) {
-            if (sg + 1 < nseg) load_seg(sg + 1, xb);
+        for (int sg = 0; sg < nsegr; sg += 2) {
+            if (sg + 1 < nsegr) load_seg(sg + 1, xb);
             take_seg(sg, xa);
-            if (sg + 1 < nseg) {
-                if (sg + 2 < nseg) load_seg(sg + 2, xa);
+            if (sg + 1 < nsegr) {
+                if (sg + 2 < nsegr) load_seg(sg + 2, xa);
                 take_seg(sg + 1, xb);
             }
         }
@@ -603,7 +629,7 @@ __global__ __launch_bounds__(64 * W) void k_rowstats_stream(const T *__restrict_
 // arithmetic is the streaming kernel's, lane for lane.  Launched with R = 2
 // (4 KiB fp32 rows: 0.438 -> 0.431 ms against one row at a time; four rows
 // 0.442).
-template <typename T, int W, int R, int NS, typename Src>
+template <typename T, int W, int R, int NS, bool ODD, typename Src>
 __global__ __launch_bounds__(64 * W) void k_rowstats_multi(const T *__restrict__ logits, int V, int blank, Src src,
                                                         const int32_t *__restrict__ targets, int S,
                                                         float4 *__restrict__ node, float2 *__restrict__ prob) {
@@ -634,12 +660,31 @@ __global__ __launch_bounds__(64 * W) void k_rowstats_multi(const T *__restrict__
             p[k] = logits + row_of(d, (r + k * W < c.count ? nr[k] - ur[k] : n - u),
                                    (r + k * W < c.count ? ur[k] : u)) * (int64_t)V;
         Vec x[R][NS];
+        int lead[R], nv[R];  // ODD: the row's elements before its first 16-byte boundary; vectors covering it
 #pragma unroll
-        for (int i = 0; i < NS; ++i) {
-            const int vi = i * 64 + lane;
-            if (vi < nvec)
+        for (int k = 0; k < R; ++k) {
+            lead[k] = ODD ? lead_of(p[k]) : 0;
+            nv[k] = ODD ? (lead[k] + V + VEC - 1) / VEC : nvec;
+        }
+        if constexpr (!ODD) {
 #pragma unroll
-                for (int k = 0; k < R; ++k) x[k][i] = load_raw<T, true>(p[k] + (int64_t)vi * VEC);
+            for (int i = 0; i < NS; ++i) {
+                const int vi = i * 64 + lane;
+                if (vi < nvec)
+#pragma unroll
+                    for (int k = 0; k < R; ++k) x[k][i] = load_raw<T, true>(p[k] + (int64_t)vi * VEC);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                const int vi = i * 64 + lane;
+#pragma unroll
+                for (int k = 0; k < R; ++k)
+                    if (vi < nv[k]) {
+                        x[k][i] = load_raw<T, true>(p[k] - lead[k] + (int64_t)vi * VEC);
+                        mask_outside_row<T>(x[k][i], vi * VEC - lead[k], V);
+                    }
+            }
         }
         int y[R];
         float hb[R], hy[R];
@@ -655,12 +700,12 @@ __global__ __launch_bounds__(64 * W) void k_rowstats_multi(const T *__restrict__
         float m[R], nm[R], sm[R];
 #pragma unroll
         for (int k = 0; k < R; ++k) {
-            m[k] = row_max<T, NS, false>(x[k], nvec);
+            m[k] = row_max<T, NS, false>(x[k], nv[k]);
             nm[k] = (m[k] == kNegInf) ? 0.f : -m[k] * kLog2e;
             float acc = 0.f;
 #pragma unroll
             for (int i = 0; i < NS; ++i)
-                if (i * 64 + lane < nvec)
+                if (i * 64 + lane < nv[k])
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) acc += exp2_fast(fmaf(Raw<T>::get(x[k][i], e), kLog2e, nm[k]));
             sm[k] = acc;
@@ -1944,6 +1989,138 @@ __global__ __launch_bounds__(64) void k_grad_rows_line(const T *logits, T *grad,
     }
 }
 
+// The gradient of rows that do not all start on a 16-byte boundary (a row
+// length that is no multiple of 16 bytes, or gradient and logits off such a
+// boundary by the same amount), in the 16-byte vectors that cover them: as in
+// k_grad_rows_line, a row's waves own the bytes from the 128-byte line that
+// holds its start, when the previous row is its lattice neighbour in memory
+// (else from its first element), to the line that holds its end when the next
+// row is (else to its last element), and compute the previous row's elements
+// in that first line with the previous row's terms, element by element in the
+// vector where the two rows meet.  A vector that reaches past owned bytes (at
+// a row edge with no such neighbour) is stored element by element; its load
+// reads the whole vector, which stays in the 16-byte block, so the page, of
+// an element of the row.  Rows that start mid-line after a non-neighbour are
+// walked from their first line boundary.  Each element is computed as in
+// k_grad_rows.
+template <typename T, bool FUSED, bool CLAMP, int NV>
+__global__ __launch_bounds__(64) void k_grad_rows_odd(const T *logits, T *grad, int blocks_per_chunk,
+                                                      int64_t block_base, int split, RNNT_GRAD_PARAMS) {
+    constexpr int VEC = Raw<T>::kVec;
+    constexpr int ES = (int)sizeof(T);
+    if (red.on && blockIdx.x == 0)
+        reduce_losses(red.loss, log2z, red.B, red.mean, red.out, red.status, red.status_out, red.sflags);
+    const int bpc = blocks_per_chunk;
+    const int64_t b = block_base + blockIdx.x;
+    const ChunkDesc c = chunks[n_chunks - 1 - (int)(b / bpc)];
+    const int part = (int)(b % bpc);
+    const int r = part / split;
+    if (r >= c.count) return;
+    const int i0 = (part % split) * NV;  // first vector number of this wave's part
+    const SampleDesc d = desc[c.sample];
+    const int lane = threadIdx.x & 63;
+    const int U1 = d.U + 1;
+    const int t = (c.row_begin + r) / U1;
+    const int u = (c.row_begin + r) - t * U1;
+    const int64_t row = row_of(d, t, u);
+    const bool packed = d.tstride == U1;
+    const bool adj_prev = u > 0 || (packed && t > 0);
+    const bool adj_next = u < d.U || (packed && t < d.T - 1);
+    // byte addresses: the row [rs, re), the owned bytes [a0, a1), the first vector v0
+    const uintptr_t rs = reinterpret_cast<uintptr_t>(grad + row * (int64_t)V);
+    const uintptr_t re = rs + (uintptr_t)V * ES;
+    const uintptr_t a0 = adj_prev ? (rs & ~(uintptr_t)127) : rs;
+    const uintptr_t a1 = adj_next ? (re & ~(uintptr_t)127) : re;
+    const uintptr_t v0 = a0 & ~(uintptr_t)15;
+    const int nw = (int)((((a1 + 15) & ~(uintptr_t)15) - v0) >> 4);  // vectors this row's waves take
+    // (a part past nw exists only where some row of the launch needs one more)
+    if (i0 * 64 >= nw) return;
+    const int h = adj_prev ? 0 : (int)(((128u - (uint32_t)(v0 & 127u)) & 127u) >> 4);
+    // slots (elements from v0): owned [o0, o1), the row's first element at os
+    const int o0 = (int)((a0 - v0) / ES), o1 = (int)((a1 - v0) / ES), os = (int)((rs - v0) / ES);
+    const int64_t e0 = row * (int64_t)V - os;  // tensor element at slot 0
+    auto position = [&](int vi) { const int v = vi + h; return v >= nw ? v - nw : v; };
+    using Vec = typename Raw<T>::vec;
+    Vec x[NV];
+    if constexpr (FUSED) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int vi = (i0 + j) * 64 + lane;
+            if (vi < nw) x[j] = load_raw<T, true>(logits + e0 + (int64_t)position(vi) * VEC);
+        }
+    }
+    const SampleTerms st{log2z[d.index], mode[d.index] != 0};
+    const RowTerms rt = row_terms(d, st, t, u, node, alpha, beta, ealpha, ebeta, log2_scale, scale, fastemit,
+                                  scale_y, FUSED, V, blank, targets, S);
+    // the previous row's last elements, slots o0 .. os-1 (h = 0 here, so
+    // within this row's first eight vectors: vector numbers below 64)
+    const bool has_prev = o0 < os;
+    RowTerms rp = rt;
+    if (has_prev && i0 == 0)
+        rp = row_terms(d, st, u > 0 ? t : t - 1, u > 0 ? u - 1 : d.U, node, alpha, beta, ealpha, ebeta, log2_scale,
+                       scale, fastemit, scale_y, FUSED, V, blank, targets, S);
+    // vector numbers and lanes' slots of the blank and label elements: this
+    // row's element k at slot os + k, the previous row's at os - V + k; -1
+    // where not owned here
+    auto number_of = [&](int slot) {
+        const int q = slot / VEC;
+        return q >= h ? q - h : q - h + nw;
+    };
+    const int sb = os + blank, sy = rt.y >= 0 ? os + rt.y : -1;
+    const int sbp = os - V + blank, syp = rp.y >= 0 ? os - V + rp.y : -1;
+    const int vb = sb < o1 ? number_of(sb) : -1;
+    const int vy = (sy >= 0 && sy < o1) ? number_of(sy) : -1;
+    const int vbp = (has_prev && sbp >= o0) ? number_of(sbp) : -1;
+    const int vyp = (has_prev && syp >= o0) ? number_of(syp) : -1;
+    const int eb = sb % VEC, ey = sy >= 0 ? sy % VEC : 0;
+    const int ebp = sbp >= 0 ? sbp % VEC : 0, eyp = syp >= 0 ? syp % VEC : 0;
+    const float cl = clamp * scale;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int i = i0 + j;
+        const int vi = i * 64 + lane;
+        if (vi < nw) {
+            const int s0 = position(vi) * VEC;  // the vector's first slot
+            float gv[VEC];
+            if (i == 0 && has_prev) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const bool prev = s0 + e < os;
+                    const float m = prev ? rp.m : rt.m, shift2 = prev ? rp.shift2 : rt.shift2;
+                    float v = 0.f;
+                    if constexpr (FUSED) v = exp2_fast(fmaf(Raw<T>::get(x[j], e) - m, kLog2e, shift2));
+                    gv[e] = v - ((vi == vbp && e == ebp) ? rp.fb : 0.f) - ((vi == vyp && e == eyp) ? rp.fy : 0.f);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    float v = 0.f;
+                    if constexpr (FUSED) v = exp2_fast(fmaf(Raw<T>::get(x[j], e) - rt.m, kLog2e, rt.shift2));
+                    gv[e] = v;
+                }
+            }
+            if ((vb >> 6) == i) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) gv[e] -= (vi == vb && e == eb) ? rt.fb : 0.f;
+            }
+            if ((vy >> 6) == i) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) gv[e] -= (vi == vy && e == ey) ? rt.fy : 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) gv[e] = clamp_to(gv[e], cl, CLAMP);
+            T *dst = grad + e0 + s0;
+            if (s0 >= o0 && s0 + VEC <= o1) {
+                store_raw<T, true>(dst, Raw<T>::put(gv));
+            } else {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    if (s0 + e >= o0 && s0 + e < o1) dst[e] = (T)gv[e];
+            }
+        }
+    }
+}
+
 template <typename T, int VEC, int G, bool FUSED>
 __global__ __launch_bounds__(256) void k_grad_narrow(const T *logits, T *grad, RNNT_GRAD_PARAMS) {
     constexpr int RPW = 64 / G;
@@ -2110,9 +2287,12 @@ RowGeom row_geometry(int V, int esize, bool aligned16) {
     while (G < 64 && G < nvec) G <<= 1;
     g.lanes_per_row = G;
     g.rows_per_block_iter = 4 * (64 / G);
-    // Rows of more than 64 16-byte vectors (1 KiB): one row per wave in the
-    // row pass, one wave per 4 KiB part in the gradient pass.
-    g.stream_parts = (aligned16 && G == 64 && nvec > 64) ? (nvec + 255) / 256 : 0;
+    // Rows of more than 1 KiB: one row per wave in the row pass, one wave per
+    // part of 4 or 5 KiB in the gradient pass, in 16-byte vectors (rows not
+    // all on 16-byte boundaries span one vector more).
+    const int64_t row_bytes = (int64_t)V * esize;
+    const int64_t vspan = aligned16 ? row_bytes / 16 : (row_bytes + 30) / 16;
+    g.stream_parts = row_bytes > 1024 ? (int)((vspan + 255) / 256) : 0;
     return g;
 }
 
@@ -2156,10 +2336,17 @@ hipError_t launch_rowstats_with(const LaunchArgs &a, const Src &src, hipStream_t
             // rows of up to 4 KiB in one step of four vectors per lane, up to
             // 5 KiB in one step of five (4112-byte fp32 rows: 0.791 -> 0.608 ms
             // against two segments of the streaming kernel), wider rows streamed
-            const int nvec = a.V * a.esize / 16;
-            auto kern = nvec <= 256 ? k_rowstats_multi<T, 8, 2, 4, Src>
-                        : nvec <= 320 ? k_rowstats_multi<T, 8, 2, 5, Src>
-                                      : k_rowstats_stream<T, 16, Src>;
+            // (rows not all on 16-byte boundaries: the odd forms, over up to
+            // one vector more)
+            constexpr int VEC = 16 / (int)sizeof(T);
+            const bool odd = !a.aligned16;
+            const int nvec = odd ? (a.V + 2 * VEC - 2) / VEC : a.V / VEC;
+            auto kern = odd ? (nvec <= 256   ? k_rowstats_multi<T, 8, 2, 4, true, Src>
+                               : nvec <= 320 ? k_rowstats_multi<T, 8, 2, 5, true, Src>
+                                             : k_rowstats_stream<T, 16, true, Src>)
+                            : (nvec <= 256   ? k_rowstats_multi<T, 8, 2, 4, false, Src>
+                               : nvec <= 320 ? k_rowstats_multi<T, 8, 2, 5, false, Src>
+                                             : k_rowstats_stream<T, 16, false, Src>);
             const dim3 wblock(nvec <= 320 ? 512 : 1024);
             hipLaunchKernelGGL(kern, grid, wblock, 0, stream, static_cast<const T *>(a.logits), a.V, a.blank, src,
                                a.targets, a.S, WS(float4 *, node), WS(float2 *, prob));
@@ -2261,8 +2448,45 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
     g.beta = WS(const double *, beta);
     g.ealpha = WS(const int *, ealpha);
     g.ebeta = WS(const int *, ebeta);
-    // Rows of more than 1 KiB: one single-wave workgroup per part of 4 or 5 KiB of a row.
-    if (a.geom.stream_parts > 0) {
+    // Rows of more than 1 KiB: one single-wave workgroup per part of 4 or 5 KiB
+    // of a row.  Rows not all on 16-byte boundaries take k_grad_rows_odd, if
+    // the logits (when read) sit at the same offset from such a boundary as
+    // the gradient; else the narrow kernels.
+    const bool same16 = ((reinterpret_cast<uintptr_t>(a.logits) ^ reinterpret_cast<uintptr_t>(a.grad)) & 15u) == 0;
+    if (a.geom.stream_parts > 0 && !a.aligned16 && (!a.fused || same16)) {
+        auto rows = [&](auto ttag) -> hipError_t {
+            using T = decltype(ttag);
+            const T *in = static_cast<const T *>(a.logits);
+            T *out = static_cast<T *>(a.grad);
+            const bool cl = a.clamp > 0.f;
+            void (*kern)(const T *, T *, int, int64_t, int, int, int, int, int, float, float, float, float, float,
+                         const int32_t *, const SampleDesc *, const ChunkDesc *, const int *, const double *,
+                         const float4 *, const double *, const double *, const int *, const int *, ReduceArgs);
+            // most vectors a row's waves take: the line before the row's
+            // start, the row, and the vector holding its end
+            const int64_t row_bytes = (int64_t)a.V * a.esize;
+            const int span = (int)((row_bytes + 127 + 15) / 16 + 1);
+            const bool five = span > 256 && span <= 320;
+            const int split = five ? 1 : (span + 255) / 256;
+            if (five)
+                kern = a.fused ? (cl ? k_grad_rows_odd<T, true, true, 5> : k_grad_rows_odd<T, true, false, 5>)
+                               : (cl ? k_grad_rows_odd<T, false, true, 5> : k_grad_rows_odd<T, false, false, 5>);
+            else
+                kern = a.fused ? (cl ? k_grad_rows_odd<T, true, true, 4> : k_grad_rows_odd<T, true, false, 4>)
+                               : (cl ? k_grad_rows_odd<T, false, true, 4> : k_grad_rows_odd<T, false, false, 4>);
+            const int bpc = a.lay.rows_per_chunk * split;
+            const int64_t total = (int64_t)a.lay.n_chunks * bpc;
+            constexpr int64_t kMaxBlocks = (int64_t)1 << 24;
+            for (int64_t base = 0; base < total; base += kMaxBlocks) {
+                const unsigned nb = (unsigned)std::min<int64_t>(kMaxBlocks, total - base);
+                hipLaunchKernelGGL(kern, dim3(nb), dim3(64), 0, stream, in, out, bpc, base, split, RNNT_GRAD_ARGS(g));
+                g.red.on = 0;  // the first launch's first workgroup reduces
+            }
+            return hipGetLastError();
+        };
+        return a.esize == 4 ? rows(float{}) : rows(_Float16{});
+    }
+    if (a.geom.stream_parts > 0 && a.aligned16) {
         auto rows = [&](auto ttag) -> hipError_t {
             using T = decltype(ttag);
             const T *in = static_cast<const T *>(a.logits);

@@ -343,6 +343,70 @@ def test_rows_of_4_to_5_kib(rl, V, dtype, clamp, fused):
     check_against_oracle(w, loss, grad, "mean")
 
 
+@pytest.mark.parametrize("V,dtype,clamp,fused,size", [
+    (1025, torch.float32, -1.0, True, "small"),   # 4100-byte rows: a BPE vocabulary of 1024 and the blank
+    (1025, torch.float32, -1.0, True, "large"),
+    (2049, torch.float16, -1.0, True, "small"),   # fp16, 4098-byte rows
+    (4097, torch.float16, 0.5, True, "large"),    # 8194-byte rows, clamp
+    (5001, torch.float32, -1.0, True, "small"),   # 20004-byte rows over five parts
+    (257, torch.float32, -1.0, True, "small"),    # 1028-byte rows, just over the narrow kernels' 1 KiB
+    (1537, torch.float32, -1.0, False, "small"),  # log-prob inputs, 6148-byte rows
+    (3001, torch.float16, -1.0, False, "large"),
+])
+def test_rows_off_16_byte_boundaries(rl, V, dtype, clamp, fused, size):
+    """Row lengths that are no multiple of 16 bytes: the row pass reads each row in the 16-byte vectors that cover
+    it (slots outside the row masked), the gradient pass owns whole lines and computes the elements of two rows
+    that meet inside a vector each with its own row's terms.  "large": above the 64512-row line below which a
+    batch takes three launches.  Every loss, and every gradient row (small) or corner and random rows (large),
+    against the oracle."""
+    Ts, Us = ([9, 6, 1], [7, 10, 0]) if size == "small" else ([400, 300], [130, 100])
+    assert (sum(t * (u + 1) for t, u in zip(Ts, Us)) < 64512) == (size == "small")
+    w = _custom(Ts, Us, V, dtype=dtype, std=2.0 if fused else 1.5, blank=-1, clamp=clamp, fused=fused,
+                prenormalise=not fused, reduction="sum", seed=V + 3)
+    loss, red, grad, flags = run(rl, w)
+    assert flags == 0
+    check_against_oracle(w, loss, grad, "sum", grad_rows="all" if size == "small" else 300)
+
+
+@pytest.mark.parametrize("V,dtype", [(1025, torch.float32), (2049, torch.float16)])
+def test_odd_rows_padded_inplace_and_offsets(rl, V, dtype):
+    """Rows off 16-byte boundaries in the padded layout (max_U1 = max(U)+1, so one sample's time steps are adjacent
+    in memory; padding zero), in place (bitwise equal to out of place at the same addresses), and with logits and
+    gradient one element past a 16-byte boundary (the same vectors) or at different offsets (the narrow gradient
+    kernels): each against the oracle.  The row pass's lanes take a row's elements by their place in 16-byte
+    blocks, so calls at other addresses agree to rounding, not bit for bit."""
+    Ts, Us = [13, 7, 20], [9, 4, 9]
+    w = _custom(Ts, Us, V, dtype=dtype, std=2.0, blank=-1, reduction="sum", seed=V + 5)
+    tg = torch.from_numpy(w.targets).to("cuda")
+    loss0, red0, grad0, flags = run(rl, w)
+    assert flags == 0
+    check_against_oracle(w, loss0, grad0, "sum")
+    max_T, max_U1 = max(Ts) + 1, max(Us) + 1
+    xp = _to_padded(w, max_T, max_U1, fill=0.0)
+    loss_p, red_p, grad_p, _ = rl.rnnt_loss_fused(xp, tg, w.logit_lengths, w.target_lengths, blank=w.blank,
+                                                  reduction="sum")
+    y = xp.clone()
+    loss_i, _, grad_i, _ = rl.rnnt_loss_fused(y, tg, w.logit_lengths, w.target_lengths, blank=w.blank,
+                                              reduction="sum", inplace=True)
+    torch.cuda.synchronize()
+    rows, pad = _padded_rows(w, grad_p, max_T, max_U1)
+    check_against_oracle(w, loss_p, rows, "sum")
+    assert bool((pad == 0).all())
+    assert grad_i.data_ptr() == y.data_ptr() and torch.equal(loss_i, loss_p) and torch.equal(y, grad_p)
+    n = w.logits.numel()
+    for xo, go in ((1, 1), (1, 3)):
+        xs = torch.empty(n + 16, dtype=dtype, device="cuda")
+        gs = torch.empty(n + 16, dtype=dtype, device="cuda")
+        x = xs[xo:xo + n].view(w.N, w.V)
+        x.copy_(w.logits)
+        g = gs[go:go + n].view(w.N, w.V)
+        loss1, red1, grad1, _ = rl.rnnt_loss_fused(x, tg, w.logit_lengths, w.target_lengths, blank=w.blank,
+                                                   reduction="sum", grad=g)
+        torch.cuda.synchronize()
+        assert grad1.data_ptr() == g.data_ptr()
+        check_against_oracle(w, loss1, grad1, "sum")
+
+
 @pytest.mark.parametrize("V,dtype,clamp,fused,lam", [
     (5000, torch.float32, -1.0, True, 0.0),      # 20000-byte rows: five 4 KiB segments, the last partial
     (8192, torch.float32, 0.05, True, 0.3),      # 32 KiB rows, clamp, FastEmit
@@ -1045,9 +1109,16 @@ def test_random_option_sweep(rl, seed):
                                             fastemit_lambda=c["lam"])
         torch.cuda.synchronize()
         rows, pad = _padded_rows(w, gp_, max_T, max_U1)
-        if c["unaligned"]:
-            # unaligned rows take the scalar row kernels, the padded copy the vector ones: the bitwise reference
-            # is the same packed logits, aligned
-            w.logits = w.logits.contiguous().clone()
-            loss, red, grad, flags = run(rl, w, fastemit=c["lam"])
-        assert torch.equal(lp_, loss) and torch.equal(rows, grad) and bool((pad == 0).all())
+        assert bool((pad == 0).all())
+        row_bytes = c["V"] * w.logits.element_size()
+        if row_bytes > 1024 and row_bytes % 16 != 0:
+            # rows off 16-byte boundaries: the row pass's lanes take a row's elements by their place in 16-byte
+            # blocks, so the padded copy (its rows at other addresses) agrees to rounding: against the oracle
+            check_against_oracle(w, lp_, rows, c["reduction"], fastemit=c["lam"])
+        else:
+            if c["unaligned"]:
+                # the unaligned call's rows sit elsewhere in their 16-byte blocks (or take the scalar kernels):
+                # the bitwise reference is the same packed logits, aligned
+                w.logits = w.logits.contiguous().clone()
+                loss, red, grad, flags = run(rl, w, fastemit=c["lam"])
+            assert torch.equal(lp_, loss) and torch.equal(rows, grad)
