@@ -505,16 +505,31 @@ __global__ __launch_bounds__(256) void k_plan(const SampleDesc *__restrict__ des
 // Rows that do not all start on a 16-byte boundary (ODD: a row length that is
 // no multiple of 16 bytes, or logits off such a boundary) are read in the
 // 16-byte vectors that cover them, from the one holding the row's first
-// element (`lead` elements before it): slots outside the row read -inf, which
-// the maximum ignores and the sum of exponentials counts as zero.  Such a
-// vector never leaves the 16-byte block, so the page, of the row's first or
-// last element.
-template <typename T>
-__device__ __forceinline__ void mask_outside_row(typename Raw<T>::vec &x, int first, int V) {
-    if (first < 0 || first + Raw<T>::kVec > V) {  // first: the row's index of slot 0
+// element (`lead` elements before it): the slots outside the row, in its first
+// and last vectors only, read -inf, which the maximum ignores and the sum of
+// exponentials counts as zero.  Such a vector never leaves the 16-byte block,
+// so the page, of the row's first or last element.  The vectors x[i] are the
+// row's vectors (base + i) * 64 + lane; only the first and the last are
+// touched (a test per element of every vector had cost the fp16 row pass a
+// third of its speed).
+template <typename T, int N>
+__device__ __forceinline__ void mask_row_edges(typename Raw<T>::vec (&x)[N], int base, int lead, int nv, int V) {
+    constexpr int VEC = Raw<T>::kVec;
+    const int lane = threadIdx.x & 63;
+    if (base == 0 && lead > 0 && lane == 0) {
 #pragma unroll
-        for (int e = 0; e < Raw<T>::kVec; ++e)
-            if (first + e < 0 || first + e >= V) x[e] = (T)kNegInf;
+        for (int e = 0; e < VEC; ++e)
+            if (e < lead) x[0][e] = (T)kNegInf;
+    }
+    const int last = nv - 1, tail = V + lead - last * VEC;  // valid slots of the last vector: 0 .. tail-1
+    if (tail < VEC) {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            if ((base + i) == (last >> 6) && lane == (last & 63)) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    if (e >= tail) x[i][e] = (T)kNegInf;
+            }
     }
 }
 template <typename T> __device__ __forceinline__ int lead_of(const T *p) {
@@ -578,11 +593,9 @@ __global__ __launch_bounds__(64 * W) void k_rowstats_stream(const T *__restrict_
 #pragma unroll
             for (int i = 0; i < NS; ++i) {
                 const int vi = (sg * NS + i) * 64 + lane;
-                if (vi < nvr) {
-                    x[i] = load_raw<T, true>(pv + (int64_t)vi * VEC);
-                    if constexpr (ODD) mask_outside_row<T>(x[i], vi * VEC - lead, V);
-                }
+                if (vi < nvr) x[i] = load_raw<T, true>(pv + (int64_t)vi * VEC);
             }
+            if constexpr (ODD) mask_row_edges<T, NS>(x, sg * NS, lead, nvr, V);
         };
         float m = kNegInf, nm = 0.f, s = 0.f;
         auto take_seg = [&](int sg, const Vec (&x)[NS]) {
@@ -680,11 +693,10 @@ __global__ __launch_bounds__(64 * W) void k_rowstats_multi(const T *__restrict__
                 const int vi = i * 64 + lane;
 #pragma unroll
                 for (int k = 0; k < R; ++k)
-                    if (vi < nv[k]) {
-                        x[k][i] = load_raw<T, true>(p[k] - lead[k] + (int64_t)vi * VEC);
-                        mask_outside_row<T>(x[k][i], vi * VEC - lead[k], V);
-                    }
+                    if (vi < nv[k]) x[k][i] = load_raw<T, true>(p[k] - lead[k] + (int64_t)vi * VEC);
             }
+#pragma unroll
+            for (int k = 0; k < R; ++k) mask_row_edges<T, NS>(x[k], 0, lead[k], nv[k], V);
         }
         int y[R];
         float hb[R], hy[R];
