@@ -3221,11 +3221,13 @@ __global__ __launch_bounds__(256) void k_mb_grad(const T *__restrict__ logits, T
 }
 
 // The row passes with the row held in 16-byte vectors, lane l holding
-// vectors l + 64i, i < NV (16-byte aligned rows of at most NV KiB), one row
-// per single-wave workgroup: the shape that streams fastest here.  The row
-// pass reads with non-temporal loads (4% faster than ordinary loads, and
-// the sweep after it finds more of its weights cached).
-template <typename T, int NV, bool FULL>
+// vectors l + 64i, i < NV (rows of at most NV KiB), one row per single-wave
+// workgroup: the shape that streams fastest here.  The row pass reads with
+// non-temporal loads (4% faster than ordinary loads, and the sweep after it
+// finds more of its weights cached).  ODD: rows that do not all start on a
+// 16-byte boundary, read in the vectors that cover them from the one holding
+// the row's first element, as the plain row pass reads them (mask_row_edges).
+template <typename T, int NV, bool FULL, bool ODD>
 __global__ __launch_bounds__(64) void k_mb_rows_v(const T *__restrict__ logits, int64_t N, int V, int blank,
                                                   int fused, MbParams mp, const SampleDesc *__restrict__ desc,
                                                   int B, const int32_t *__restrict__ targets, int S,
@@ -3237,7 +3239,8 @@ __global__ __launch_bounds__(64) void k_mb_rows_v(const T *__restrict__ logits, 
     const int64_t r = row_base + xcd_block(blockIdx.x, gridDim.x >> 3);
     if (r >= N) return;
     const T *x = logits + r * (int64_t)V;
-    const int nvec = V / VEC;
+    const int lead = ODD ? lead_of(x) : 0;
+    const int nvec = ODD ? (lead + V + VEC - 1) / VEC : V / VEC;
     // the row's loads go out before the search for its sample, whose
     // dependent loads they do not need (a padding row of the padded layout
     // is read and then left)
@@ -3245,7 +3248,9 @@ __global__ __launch_bounds__(64) void k_mb_rows_v(const T *__restrict__ logits, 
     if (fused) {
 #pragma unroll
         for (int i = 0; i < NV; ++i)
-            if (FULL || i * 64 + lane < nvec) xv[i] = load_raw<T, true>(x + (int64_t)(i * 64 + lane) * VEC);
+            if (FULL || i * 64 + lane < nvec)
+                xv[i] = load_raw<T, true>(x - lead + (int64_t)(i * 64 + lane) * VEC);
+        if constexpr (ODD) mask_row_edges<T, NV>(xv, 0, lead, nvec, V);
     }
     const SampleDesc d = mb_sample_of_row(desc, B, r);
     const int64_t lr = r - d.row_off;
@@ -3299,7 +3304,11 @@ __device__ __forceinline__ void mb_sub_at(float (&gv)[VEC], int vi, int i, int c
     }
 }
 
-template <typename T, int NV, bool FULL>
+// ODD: rows that do not all start on a 16-byte boundary (gradient and logits
+// at the same offset from one): in the vectors that cover the row, the class
+// k at slot lead + k; the row's first and last vectors are stored element by
+// element within the row.
+template <typename T, int NV, bool FULL, bool ODD>
 __global__ __launch_bounds__(64) void k_mb_grad_v(const T *__restrict__ logits, T *__restrict__ grad, int64_t N,
                                                   int V, int blank, int fused, MbParams mp, int U1p,
                                                   const SampleDesc *__restrict__ desc, int B,
@@ -3316,12 +3325,27 @@ __global__ __launch_bounds__(64) void k_mb_grad_v(const T *__restrict__ logits, 
     // plain order: the XCD-contiguous order of the row pass made this pass slower (0.88 -> 0.94 ms)
     const int64_t r = row_base + (int64_t)blockIdx.x;
     if (r >= N) return;
-    const int nvec = V / VEC;
+    T *g = grad + r * (int64_t)V;
+    const int lead = ODD ? lead_of(g) : 0;
+    const int nvec = ODD ? (lead + V + VEC - 1) / VEC : V / VEC;
+    T *gv0 = g - lead;  // the row's first vector
+    // the vector of lane vi: stored whole, or element by element where it
+    // reaches outside the row (ODD)
+    auto store_vec = [&](int vi, const float (&v)[VEC]) {
+        const int s0 = vi * VEC;
+        if (!ODD || (s0 >= lead && s0 + VEC <= lead + V)) {
+            store_raw<T, true>(gv0 + (int64_t)s0, Raw<T>::put(v));
+        } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                if (s0 + e >= lead && s0 + e < lead + V) gv0[s0 + e] = (T)v[e];
+        }
+    };
     // the row's loads go out before the search for its sample (as in the
     // row pass)
     Vec xv[NV];
     if (fused) {
-        const T *x = logits + r * (int64_t)V;
+        const T *x = logits + r * (int64_t)V - lead;
 #pragma unroll
         for (int i = 0; i < NV; ++i)
             if (FULL || i * 64 + lane < nvec) xv[i] = load_raw<T, true>(x + (int64_t)(i * 64 + lane) * VEC);
@@ -3330,12 +3354,11 @@ __global__ __launch_bounds__(64) void k_mb_grad_v(const T *__restrict__ logits, 
     const int64_t lr = r - d.row_off;
     const int t = (int)(lr / d.tstride);
     const int u = (int)(lr - (int64_t)t * d.tstride);
-    T *g = grad + r * (int64_t)V;
     if (t >= d.T || u > d.U) {  // a padding row of the padded layout: zero gradient
-        float z[VEC] = {};
+        const float z[VEC] = {};
 #pragma unroll
         for (int i = 0; i < NV; ++i)
-            if (FULL || i * 64 + lane < nvec) store_raw<T, true>(g + (int64_t)(i * 64 + lane) * VEC, Raw<T>::put(z));
+            if (FULL || i * 64 + lane < nvec) store_vec(i * 64 + lane, z);
         return;
     }
     MbRowTerms rt = mb_row_terms(d, r, t, u, V, blank, fused, mp, U1p, targets, S, den, wp, n_slots, alpha, beta, ealpha,
@@ -3350,13 +3373,14 @@ __global__ __launch_bounds__(64) void k_mb_grad_v(const T *__restrict__ logits, 
 #pragma unroll
             for (int e = 0; e < VEC; ++e)
                 gv[e] = fused ? exp2_fast(fmaf(Raw<T>::get(xv[i], e) - rt.m, kLog2e, rt.shift2)) : 0.f;
-            mb_sub_at<VEC>(gv, vi, i, blank, rt.fb);
-            mb_sub_at<VEC>(gv, vi, i, rt.y, rt.fy);
+            mb_sub_at<VEC>(gv, vi, i, blank + lead, rt.fb);
+            mb_sub_at<VEC>(gv, vi, i, rt.y >= 0 ? rt.y + lead : -1, rt.fy);
 #pragma unroll
-            for (int k = 0; k < kMaxBigBlanks; ++k) mb_sub_at<VEC>(gv, vi, i, k < mp.nb ? mp.ids[k] : -1, rt.fg[k]);
+            for (int k = 0; k < kMaxBigBlanks; ++k)
+                mb_sub_at<VEC>(gv, vi, i, k < mp.nb ? mp.ids[k] + lead : -1, rt.fg[k]);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) gv[e] = clamp_to(gv[e], cl, do_clamp);
-            store_raw<T, true>(g + (int64_t)vi * VEC, Raw<T>::put(gv));
+            store_vec(vi, gv);
         }
     }
 }
@@ -3393,46 +3417,60 @@ size_t mb_ring_bytes(int U1p, int max_duration) {
 
 // Vectors per lane of the vector row forms (0: the scalar forms): 16-byte
 // aligned rows of at most 16 KiB.
-static int mb_row_nv(const MbArgs &a) {
-    const bool aligned = ((int64_t)a.V * a.esize) % 16 == 0 && (uintptr_t)a.logits % 16 == 0 &&
-                         (!a.grad || (uintptr_t)a.grad % 16 == 0);
-    if (!aligned) return 0;
-    const int nvec = a.V * a.esize / 16;
+// Vectors per lane of the vector row passes (0: the scalar kernels), and
+// whether rows need the odd forms: rows not all on 16-byte boundaries, which
+// span up to one vector more and need the gradient at the logits' offset
+// from such a boundary when both are read and written; rows of up to 1 KiB
+// keep the scalar kernels there (their results then do not depend on where
+// the rows sit).
+static int mb_row_nv(const MbArgs &a, bool &odd) {
+    const int64_t rb = (int64_t)a.V * a.esize;
+    odd = rb % 16 != 0 || (uintptr_t)a.logits % 16 != 0 || (a.grad && (uintptr_t)a.grad % 16 != 0);
+    if (odd && (rb <= 1024 || (a.grad && a.fused && (((uintptr_t)a.logits ^ (uintptr_t)a.grad) & 15u) != 0)))
+        return 0;
+    const int64_t nvec = odd ? (rb + 32 - 2 * a.esize) / 16 : rb / 16;
     int nv = 1;
     while (nv * 64 < nvec) nv <<= 1;
     return nv <= 16 ? nv : 0;
 }
 
-// full: the row fills all nv vectors of every lane (no tail test).
-template <typename Fn> static hipError_t with_mb_nv(int esize, int nv, bool full, Fn &&fn) {
-    auto go = [&](auto tag, auto fc) -> hipError_t {
+// full: the row fills all nv vectors of every lane (no tail test); odd: the
+// odd forms (never full).
+template <typename Fn> static hipError_t with_mb_nv(int esize, int nv, bool full, bool odd, Fn &&fn) {
+    auto go = [&](auto tag, auto fc, auto oc) -> hipError_t {
         using T = decltype(tag);
         switch (nv) {
-        case 1: return fn(T{}, std::integral_constant<int, 1>{}, fc);
-        case 2: return fn(T{}, std::integral_constant<int, 2>{}, fc);
-        case 4: return fn(T{}, std::integral_constant<int, 4>{}, fc);
-        case 8: return fn(T{}, std::integral_constant<int, 8>{}, fc);
-        default: return fn(T{}, std::integral_constant<int, 16>{}, fc);
+        case 1: return fn(T{}, std::integral_constant<int, 1>{}, fc, oc);
+        case 2: return fn(T{}, std::integral_constant<int, 2>{}, fc, oc);
+        case 4: return fn(T{}, std::integral_constant<int, 4>{}, fc, oc);
+        case 8: return fn(T{}, std::integral_constant<int, 8>{}, fc, oc);
+        default: return fn(T{}, std::integral_constant<int, 16>{}, fc, oc);
         }
     };
+    if (odd)
+        return esize == 4 ? go(float{}, std::false_type{}, std::true_type{})
+                          : go(_Float16{}, std::false_type{}, std::true_type{});
     if (esize == 4)
-        return full ? go(float{}, std::true_type{}) : go(float{}, std::false_type{});
-    return full ? go(_Float16{}, std::true_type{}) : go(_Float16{}, std::false_type{});
+        return full ? go(float{}, std::true_type{}, std::false_type{}) : go(float{}, std::false_type{}, std::false_type{});
+    return full ? go(_Float16{}, std::true_type{}, std::false_type{})
+                : go(_Float16{}, std::false_type{}, std::false_type{});
 }
 
 hipError_t launch_mb_rows(const MbArgs &a, hipStream_t stream) {
     const MbParams mp = mb_params(a);
     constexpr int64_t kMaxBlocks = (int64_t)1 << 24;
-    const int nv = mb_row_nv(a);
+    bool odd = false;
+    const int nv = mb_row_nv(a, odd);
     if (nv > 0)
-        return with_mb_nv(a.esize, nv, a.V * a.esize == nv * 1024, [&](auto tag, auto nvc, auto fc) {
+        return with_mb_nv(a.esize, nv, a.V * a.esize == nv * 1024, odd, [&](auto tag, auto nvc, auto fc, auto oc) {
             using T = decltype(tag);
             constexpr int NV = decltype(nvc)::value;
             constexpr bool FULL = decltype(fc)::value;
+            constexpr bool ODD = decltype(oc)::value;
             for (int64_t b0 = 0; b0 < a.N; b0 += kMaxBlocks) {
                 // a multiple of 8 workgroups, so each XCD takes a contiguous range of rows
                 const unsigned nb = (unsigned)((std::min<int64_t>(kMaxBlocks, a.N - b0) + 7) & ~(int64_t)7);
-                hipLaunchKernelGGL((k_mb_rows_v<T, NV, FULL>), dim3(nb), dim3(64), 0, stream,
+                hipLaunchKernelGGL((k_mb_rows_v<T, NV, FULL, ODD>), dim3(nb), dim3(64), 0, stream,
                                    static_cast<const T *>(a.logits), a.N, a.V, a.blank, a.fused, mp,
                                    MBWS(const SampleDesc *, desc), a.B, a.targets, a.S, MBWS(float2 *, den),
                                    MBWS(double *, wp), a.lay.n_slots, MBWS(uint32_t *, status), b0);
@@ -3497,15 +3535,17 @@ hipError_t launch_mb_sweep(const MbArgs &a, hipStream_t stream) {
 hipError_t launch_mb_grad(const MbArgs &a, hipStream_t stream) {
     const MbParams mp = mb_params(a);
     constexpr int64_t kMaxBlocks = (int64_t)1 << 24;
-    const int nv = mb_row_nv(a);
+    bool odd = false;
+    const int nv = mb_row_nv(a, odd);
     if (nv > 0)
-        return with_mb_nv(a.esize, nv, a.V * a.esize == nv * 1024, [&](auto tag, auto nvc, auto fc) {
+        return with_mb_nv(a.esize, nv, a.V * a.esize == nv * 1024, odd, [&](auto tag, auto nvc, auto fc, auto oc) {
             using T = decltype(tag);
             constexpr int NV = decltype(nvc)::value;
             constexpr bool FULL = decltype(fc)::value;
+            constexpr bool ODD = decltype(oc)::value;
             for (int64_t b0 = 0; b0 < a.N; b0 += kMaxBlocks) {
                 const unsigned nb = (unsigned)std::min<int64_t>(kMaxBlocks, a.N - b0);
-                hipLaunchKernelGGL((k_mb_grad_v<T, NV, FULL>), dim3(nb), dim3(64), 0, stream,
+                hipLaunchKernelGGL((k_mb_grad_v<T, NV, FULL, ODD>), dim3(nb), dim3(64), 0, stream,
                                    static_cast<const T *>(a.logits), static_cast<T *>(a.grad), a.N, a.V, a.blank,
                                    a.fused, mp, a.lay.U1p, MBWS(const SampleDesc *, desc), a.B, a.targets, a.S,
                                    MBWS(const float2 *, den), MBWS(const double *, wp), a.lay.n_slots,

@@ -416,3 +416,46 @@ def test_multiblank_padded_autograd(rl):
     torch.cuda.synchronize()
     assert torch.equal(out.detach(), ref_loss)
     assert torch.allclose(x.grad, ref_grad * up.view(-1, 1, 1, 1), rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("V,dtype,fused", [(1029, torch.float32, True), (2053, torch.float16, True),
+                                           (1029, torch.float32, False), (1537, torch.float16, True)])
+def test_multiblank_rows_off_16_byte_boundaries(rl, V, dtype, fused):
+    """Row lengths that are no multiple of 16 bytes (1024 labels, the blank and four big blanks: 1029 classes):
+    the vector row passes read each row in the 16-byte vectors that cover it and store the row's first and last
+    vectors element by element.  Packed against the oracle (every loss and gradient row), the padded layout
+    against the oracle with zero padding, and logits and gradient at matching and at different offsets from a
+    16-byte boundary (the latter on the scalar kernels) against the oracle."""
+    Ts, Us = [14, 9, 21], [6, 0, 11]
+    ids = [V - 2, V - 3, V - 4, V - 5]
+    w = _mb(Ts, Us, V, ids, [2, 3, 5, 8], 0.05, dtype=dtype, std=2.0 if fused else 1.5, blank=-1, fused=fused,
+            prenormalise=not fused, reduction="sum", seed=V + 11)
+    loss, red, grad, flags = run_mb(rl, w)
+    assert flags == 0
+    check_mb(w, loss, grad, "sum")
+    tg = torch.from_numpy(w.targets).to("cuda")
+    max_T, max_U1 = max(Ts) + 1, max(Us) + 1
+    xp = _padded(w, max_T, max_U1, fill=0.0)
+    loss_p, _, grad_p, _ = rl.rnnt_multiblank_fused(xp, tg, w.logit_lengths, w.target_lengths,
+                                                    big_blank_ids=w.big_blank_ids,
+                                                    big_blank_durations=w.big_blank_durations, blank=w.blank,
+                                                    sigma=w.sigma, reduction="sum", fused_log_softmax=fused)
+    torch.cuda.synchronize()
+    rows, pad = _unpad(w, grad_p, max_T, max_U1)
+    assert pad.numel() > 0 and bool((pad == 0).all())
+    check_mb(w, loss_p, rows, "sum")
+    n = w.logits.numel()
+    for xo, go in ((1, 1), (1, 2)):
+        xs = torch.empty(n + 16, dtype=dtype, device="cuda")
+        gs = torch.empty(n + 16, dtype=dtype, device="cuda")
+        x = xs[xo:xo + n].view(w.N, w.V)
+        x.copy_(w.logits)
+        g = gs[go:go + n].view(w.N, w.V)
+        loss1, _, grad1, _ = rl.rnnt_multiblank_fused(x, tg, w.logit_lengths, w.target_lengths,
+                                                      big_blank_ids=w.big_blank_ids,
+                                                      big_blank_durations=w.big_blank_durations, blank=w.blank,
+                                                      sigma=w.sigma, reduction="sum", fused_log_softmax=fused,
+                                                      grad=g)
+        torch.cuda.synchronize()
+        assert grad1.data_ptr() == g.data_ptr()
+        check_mb(w, loss1, grad1, "sum")
