@@ -563,7 +563,7 @@ template <typename T> __device__ __forceinline__ int lead_of(const T *p) {
 // elements and the sum of exp(x - that maximum), rescaled when it grows; at
 // the end of the row the lanes' sums are rescaled to the row maximum and
 // added.  Every term is formed from x - maximum, as in the other row passes.
-template <typename T, int W, bool ODD, typename Src>
+template <typename T, int W, bool ODD, bool MERGE, typename Src>
 __global__ __launch_bounds__(64 * W) void k_rowstats_stream(const T *__restrict__ logits, int V, int blank, Src src,
                                                          const int32_t *__restrict__ targets, int S,
                                                          float4 *__restrict__ node, float2 *__restrict__ prob) {
@@ -588,30 +588,42 @@ __global__ __launch_bounds__(64 * W) void k_rowstats_stream(const T *__restrict_
         const int lead = ODD ? lead_of(p) : 0;
         const T *pv = p - lead;
         const int nvr = ODD ? (lead + V + VEC - 1) / VEC : nvec;  // vectors covering the row
-        const int nsegr = ODD ? (nvr + 64 * NS - 1) / (64 * NS) : nseg;
-        auto load_seg = [&](int sg, Vec (&x)[NS]) {
+        int nsegr = ODD ? (nvr + 64 * NS - 1) / (64 * NS) : nseg;
+        // MERGE: a last segment of at most one block of 64 vectors is read as
+        // a fifth block of the segment before it (an 8194-byte row in two
+        // steps instead of three)
+        constexpr int NX = NS + (MERGE ? 1 : 0);
+        bool merged = false;
+        if constexpr (MERGE) {
+            merged = nsegr >= 2 && nvr - (nsegr - 1) * 64 * NS <= 64;
+            if (merged) nsegr -= 1;
+        }
+        auto blocks_of = [&](int sg) { return (MERGE && merged && sg == nsegr - 1) ? NX : NS; };
+        auto load_seg = [&](int sg, Vec (&x)[NX]) {
+            const int nb = blocks_of(sg);
 #pragma unroll
-            for (int i = 0; i < NS; ++i) {
+            for (int i = 0; i < NX; ++i) {
                 const int vi = (sg * NS + i) * 64 + lane;
-                if (vi < nvr) x[i] = load_raw<T, true>(pv + (int64_t)vi * VEC);
+                if (i < nb && vi < nvr) x[i] = load_raw<T, true>(pv + (int64_t)vi * VEC);
             }
-            if constexpr (ODD) mask_row_edges<T, NS>(x, sg * NS, lead, nvr, V);
+            if constexpr (ODD) mask_row_edges<T, NX>(x, sg * NS, lead, nvr, V);
         };
         float m = kNegInf, nm = 0.f, s = 0.f;
-        auto take_seg = [&](int sg, const Vec (&x)[NS]) {
-            const float mn = fmaxf(m, row_max<T, NS, false>(x, nvr - sg * NS * 64));
+        auto take_seg = [&](int sg, const Vec (&x)[NX]) {
+            const int cnt = min(nvr - sg * NS * 64, blocks_of(sg) * 64);  // the segment's vectors
+            const float mn = fmaxf(m, row_max<T, NX, false>(x, cnt));
             const float nmn = (mn == kNegInf) ? 0.f : -mn * kLog2e;
             float acc = (m == kNegInf) ? 0.f : s * exp2_fast(nmn - nm);
 #pragma unroll
-            for (int i = 0; i < NS; ++i)
-                if ((sg * NS + i) * 64 + lane < nvr)
+            for (int i = 0; i < NX; ++i)
+                if (i * 64 + lane < cnt)
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) acc += exp2_fast(fmaf(Raw<T>::get(x[i], e), kLog2e, nmn));
             s = acc;
             m = mn;
             nm = nmn;
         };
-        Vec xa[NS], xb[NS];
+        Vec xa[NX], xb[NX];
         load_seg(0, xa);
         for (int sg = 0; sg < nsegr; sg += 2) {
             if (sg + 1 < nsegr) load_seg(sg + 1, xb);
@@ -1829,9 +1841,11 @@ __device__ __forceinline__ void grad_row(typename Raw<T>::vec (&xc)[NV], T *dst,
 
 // The gradient, one wave per workgroup and `split` workgroups per row (SPLIT,
 // when the launch fixes it at compile time), each taking a part of NV 16-byte
-// vectors per lane (4 KiB at NV = 4; NV = 5 makes a row of 4 to 5 KiB one
-// part instead of a whole one and a nearly empty one; the last part may be
-// partial unless FULL): each
+// vectors per lane (4 KiB at NV = 4; the last part may be partial unless
+// FULL).  With NV = 5, parts of part_blocks blocks of 64 vectors and a last
+// part of last_blocks: one part of five blocks for a row of 4 to 5 KiB, or parts of four
+// and a last one of five where a row would end in a part of at most one block
+// (an 8194-byte row: two waves instead of three): each
 // wave loads its part
 // of the row, computes and stores it, and exits.  Many single-wave
 // workgroups of 4 KiB keep enough rows in flight without a prefetch ring
@@ -1847,7 +1861,8 @@ __device__ __forceinline__ void grad_row(typename Raw<T>::vec (&xc)[NV], T *dst,
 // 1.045 masked).
 template <typename T, bool FUSED, bool CLAMP, int SPLIT, bool FULL, int NV>
 __global__ __launch_bounds__(64) void k_grad_rows(const T *logits, T *grad, int blocks_per_chunk,
-                                                  int64_t block_base, int split_rt, RNNT_GRAD_PARAMS) {
+                                                  int64_t block_base, int split_rt, int part_blocks, int last_blocks,
+                                                  RNNT_GRAD_PARAMS) {
     constexpr int VEC = Raw<T>::kVec;
     if (red.on && blockIdx.x == 0)
         reduce_losses(red.loss, log2z, red.B, red.mean, red.out, red.status, red.status_out, red.sflags);
@@ -1858,10 +1873,12 @@ __global__ __launch_bounds__(64) void k_grad_rows(const T *logits, T *grad, int 
     const int split = SPLIT > 0 ? SPLIT : split_rt;
     const int r = part / split;
     if (r >= c.count) return;
-    const int i0 = (part % split) * NV;  // first vector number of this wave's part
+    // the part's 64-vector blocks: NV, or (NV = 5) pb each and pb_last in the last part
+    const int ip = part % split;
+    const int i0 = NV == 4 ? ip * NV : ip * part_blocks;
     const SampleDesc d = desc[c.sample];
     const int lane = threadIdx.x & 63;
-    const int nvec = V / VEC;
+    const int nvec = NV == 4 ? V / VEC : min(V / VEC, (i0 + (ip == split - 1 ? last_blocks : part_blocks)) * 64);
     const int U1 = d.U + 1;
     const int t = (c.row_begin + r) / U1;
     const int u = (c.row_begin + r) - t * U1;
@@ -1903,7 +1920,8 @@ __global__ __launch_bounds__(64) void k_grad_rows(const T *logits, T *grad, int 
 // it, so both give the same bits.
 template <typename T, bool FUSED, bool CLAMP, int NV>
 __global__ __launch_bounds__(64) void k_grad_rows_line(const T *logits, T *grad, int blocks_per_chunk,
-                                                       int64_t block_base, int split, RNNT_GRAD_PARAMS) {
+                                                       int64_t block_base, int split, int part_blocks, int last_blocks,
+                                                       RNNT_GRAD_PARAMS) {
     constexpr int VEC = Raw<T>::kVec;
     if (red.on && blockIdx.x == 0)
         reduce_losses(red.loss, log2z, red.B, red.mean, red.out, red.status, red.status_out, red.sflags);
@@ -1913,7 +1931,10 @@ __global__ __launch_bounds__(64) void k_grad_rows_line(const T *logits, T *grad,
     const int part = (int)(b % bpc);
     const int r = part / split;
     if (r >= c.count) return;
-    const int i0 = (part % split) * NV;  // first vector number of this wave's part
+    // the part's 64-vector blocks (as in k_grad_rows)
+    const int ip = part % split;
+    const int i0 = NV == 4 ? ip * NV : ip * part_blocks;
+    const int iend = NV == 4 ? i0 + NV : i0 + (ip == split - 1 ? last_blocks : part_blocks);
     const SampleDesc d = desc[c.sample];
     const int lane = threadIdx.x & 63;
     const int nvec = V / VEC;
@@ -1932,6 +1953,7 @@ __global__ __launch_bounds__(64) void k_grad_rows_line(const T *logits, T *grad,
     // (a part past nw exists only where some row of the launch takes nvec + kp
     // vectors across one more part than the row alone needs)
     if (i0 * 64 >= nw) return;
+    const int nwp = min(nw, iend * 64);  // this part's end
     const int h = adj_prev ? 0 : (int)(((128u - so) & 127u) >> 4);
     const int64_t e0 = row * (int64_t)V - (int64_t)kp * VEC;  // element offset of position 0
     auto position = [&](int vi) { const int v = vi + h; return v >= nw ? v - nw : v; };
@@ -1941,7 +1963,7 @@ __global__ __launch_bounds__(64) void k_grad_rows_line(const T *logits, T *grad,
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
             const int vi = (i0 + j) * 64 + lane;
-            if (vi < nw) x[j] = load_raw<T, true>(logits + e0 + (int64_t)position(vi) * VEC);
+            if (vi < nwp) x[j] = load_raw<T, true>(logits + e0 + (int64_t)position(vi) * VEC);
         }
     }
     const SampleTerms st{log2z[d.index], mode[d.index] != 0};
@@ -1968,7 +1990,7 @@ __global__ __launch_bounds__(64) void k_grad_rows_line(const T *logits, T *grad,
     for (int j = 0; j < NV; ++j) {
         const int i = i0 + j;
         const int vi = i * 64 + lane;
-        if (vi < nw) {
+        if (vi < nwp) {
             const bool prev = vi < kp;
             const float m = prev ? rp.m : rt.m, shift2 = prev ? rp.shift2 : rt.shift2;
             float gv[VEC];
@@ -2017,7 +2039,8 @@ __global__ __launch_bounds__(64) void k_grad_rows_line(const T *logits, T *grad,
 // k_grad_rows.
 template <typename T, bool FUSED, bool CLAMP, int NV>
 __global__ __launch_bounds__(64) void k_grad_rows_odd(const T *logits, T *grad, int blocks_per_chunk,
-                                                      int64_t block_base, int split, RNNT_GRAD_PARAMS) {
+                                                      int64_t block_base, int split, int part_blocks, int last_blocks,
+                                                      RNNT_GRAD_PARAMS) {
     constexpr int VEC = Raw<T>::kVec;
     constexpr int ES = (int)sizeof(T);
     if (red.on && blockIdx.x == 0)
@@ -2028,7 +2051,10 @@ __global__ __launch_bounds__(64) void k_grad_rows_odd(const T *logits, T *grad, 
     const int part = (int)(b % bpc);
     const int r = part / split;
     if (r >= c.count) return;
-    const int i0 = (part % split) * NV;  // first vector number of this wave's part
+    // the part's 64-vector blocks (as in k_grad_rows)
+    const int ip = part % split;
+    const int i0 = NV == 4 ? ip * NV : ip * part_blocks;
+    const int iend = NV == 4 ? i0 + NV : i0 + (ip == split - 1 ? last_blocks : part_blocks);
     const SampleDesc d = desc[c.sample];
     const int lane = threadIdx.x & 63;
     const int U1 = d.U + 1;
@@ -2047,6 +2073,7 @@ __global__ __launch_bounds__(64) void k_grad_rows_odd(const T *logits, T *grad, 
     const int nw = (int)((((a1 + 15) & ~(uintptr_t)15) - v0) >> 4);  // vectors this row's waves take
     // (a part past nw exists only where some row of the launch needs one more)
     if (i0 * 64 >= nw) return;
+    const int nwp = min(nw, iend * 64);  // this part's end
     const int h = adj_prev ? 0 : (int)(((128u - (uint32_t)(v0 & 127u)) & 127u) >> 4);
     // slots (elements from v0): owned [o0, o1), the row's first element at os
     const int o0 = (int)((a0 - v0) / ES), o1 = (int)((a1 - v0) / ES), os = (int)((rs - v0) / ES);
@@ -2058,7 +2085,7 @@ __global__ __launch_bounds__(64) void k_grad_rows_odd(const T *logits, T *grad, 
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
             const int vi = (i0 + j) * 64 + lane;
-            if (vi < nw) x[j] = load_raw<T, true>(logits + e0 + (int64_t)position(vi) * VEC);
+            if (vi < nwp) x[j] = load_raw<T, true>(logits + e0 + (int64_t)position(vi) * VEC);
         }
     }
     const SampleTerms st{log2z[d.index], mode[d.index] != 0};
@@ -2091,7 +2118,7 @@ __global__ __launch_bounds__(64) void k_grad_rows_odd(const T *logits, T *grad, 
     for (int j = 0; j < NV; ++j) {
         const int i = i0 + j;
         const int vi = i * 64 + lane;
-        if (vi < nw) {
+        if (vi < nwp) {
             const int s0 = position(vi) * VEC;  // the vector's first slot
             float gv[VEC];
             if (i == 0 && has_prev) {
@@ -2353,12 +2380,20 @@ hipError_t launch_rowstats_with(const LaunchArgs &a, const Src &src, hipStream_t
             constexpr int VEC = 16 / (int)sizeof(T);
             const bool odd = !a.aligned16;
             const int nvec = odd ? (a.V + 2 * VEC - 2) / VEC : a.V / VEC;
+            // fp32: a row's last segment of at most one block merges into the
+            // one before (8196-byte rows: 1.218 -> 1.176 ms; on fp16 rows the
+            // same measured 20-40% slower)
+            const int nlo = (a.V + VEC - 1) / VEC;  // the fewest vectors covering a row
+            auto tiny_tail = [](int nv) { return nv > 512 && (nv - 1) % 256 < 64; };
+            const bool merge = sizeof(T) == 4 && (tiny_tail(nvec) || (odd && tiny_tail(nlo)));
             auto kern = odd ? (nvec <= 256   ? k_rowstats_multi<T, 8, 2, 4, true, Src>
                                : nvec <= 320 ? k_rowstats_multi<T, 8, 2, 5, true, Src>
-                                             : k_rowstats_stream<T, 16, true, Src>)
+                               : merge       ? k_rowstats_stream<T, 16, true, true, Src>
+                                             : k_rowstats_stream<T, 16, true, false, Src>)
                             : (nvec <= 256   ? k_rowstats_multi<T, 8, 2, 4, false, Src>
                                : nvec <= 320 ? k_rowstats_multi<T, 8, 2, 5, false, Src>
-                                             : k_rowstats_stream<T, 16, false, Src>);
+                               : merge       ? k_rowstats_stream<T, 16, false, true, Src>
+                                             : k_rowstats_stream<T, 16, false, false, Src>);
             const dim3 wblock(nvec <= 320 ? 512 : 1024);
             hipLaunchKernelGGL(kern, grid, wblock, 0, stream, static_cast<const T *>(a.logits), a.V, a.blank, src,
                                a.targets, a.S, WS(float4 *, node), WS(float2 *, prob));
@@ -2429,6 +2464,25 @@ hipError_t launch_alpha_beta(const LaunchArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// The parts of a row's gradient, `span` the most 16-byte vectors a row's
+// waves take: parts of four blocks of 64 vectors (4 KiB), except one part of
+// five for a row of 4 to 5 KiB (4112-byte fp32 rows: 1.640 -> 1.335 ms against
+// a whole part and one of a single vector; fp16 1.886 -> 1.358) and, for fp32
+// rows, a last part of five where the row would end in a part of at most one
+// block (8196-byte rows: two waves instead of three, 2.590 -> 2.278 ms; fp16
+// rows gain nothing from it).  Parts of five throughout measured 9-10% slower
+// on 8208- and 8704-byte rows.
+struct PartShape {
+    int split, pb, pb_last;
+    bool five;  // the kernels with room for five blocks
+};
+static PartShape part_shape(int span, int esize) {
+    const int p4 = (span + 255) / 256;
+    if (span > 256 && span <= 320) return {1, 5, 5, true};
+    if (esize == 4 && p4 >= 3 && span - (p4 - 1) * 256 <= 64) return {p4 - 1, 4, 5, true};
+    return {p4, 4, 4, false};
+}
+
 // The gradient, and in its first workgroup the loss check and reduction.
 hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
     const dim3 grid(a.lay.n_chunks), block(256);
@@ -2471,16 +2525,16 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
             const T *in = static_cast<const T *>(a.logits);
             T *out = static_cast<T *>(a.grad);
             const bool cl = a.clamp > 0.f;
-            void (*kern)(const T *, T *, int, int64_t, int, int, int, int, int, float, float, float, float, float,
-                         const int32_t *, const SampleDesc *, const ChunkDesc *, const int *, const double *,
-                         const float4 *, const double *, const double *, const int *, const int *, ReduceArgs);
+            void (*kern)(const T *, T *, int, int64_t, int, int, int, int, int, int, int, float, float, float,
+                         float, float, const int32_t *, const SampleDesc *, const ChunkDesc *, const int *,
+                         const double *, const float4 *, const double *, const double *, const int *, const int *,
+                         ReduceArgs);
             // most vectors a row's waves take: the line before the row's
             // start, the row, and the vector holding its end
             const int64_t row_bytes = (int64_t)a.V * a.esize;
-            const int span = (int)((row_bytes + 127 + 15) / 16 + 1);
-            const bool five = span > 256 && span <= 320;
-            const int split = five ? 1 : (span + 255) / 256;
-            if (five)
+            const PartShape ps = part_shape((int)((row_bytes + 127 + 15) / 16 + 1), a.esize);
+            const int split = ps.split;
+            if (ps.five)
                 kern = a.fused ? (cl ? k_grad_rows_odd<T, true, true, 5> : k_grad_rows_odd<T, true, false, 5>)
                                : (cl ? k_grad_rows_odd<T, false, true, 5> : k_grad_rows_odd<T, false, false, 5>);
             else
@@ -2491,7 +2545,8 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
             constexpr int64_t kMaxBlocks = (int64_t)1 << 24;
             for (int64_t base = 0; base < total; base += kMaxBlocks) {
                 const unsigned nb = (unsigned)std::min<int64_t>(kMaxBlocks, total - base);
-                hipLaunchKernelGGL(kern, dim3(nb), dim3(64), 0, stream, in, out, bpc, base, split, RNNT_GRAD_ARGS(g));
+                hipLaunchKernelGGL(kern, dim3(nb), dim3(64), 0, stream, in, out, bpc, base, split, ps.pb, ps.pb_last,
+                                   RNNT_GRAD_ARGS(g));
                 g.red.on = 0;  // the first launch's first workgroup reduces
             }
             return hipGetLastError();
@@ -2504,9 +2559,10 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
             const T *in = static_cast<const T *>(a.logits);
             T *out = static_cast<T *>(a.grad);
             const bool cl = a.clamp > 0.f;
-            void (*kern)(const T *, T *, int, int64_t, int, int, int, int, int, float, float, float, float, float,
-                         const int32_t *, const SampleDesc *, const ChunkDesc *, const int *, const double *,
-                         const float4 *, const double *, const double *, const int *, const int *, ReduceArgs);
+            void (*kern)(const T *, T *, int, int64_t, int, int, int, int, int, int, int, float, float, float,
+                         float, float, const int32_t *, const SampleDesc *, const ChunkDesc *, const int *,
+                         const double *, const float4 *, const double *, const double *, const int *, const int *,
+                         ReduceArgs);
             const uint32_t row_bytes = (uint32_t)a.V * (uint32_t)a.esize;
             const int nvec = (int)(row_bytes / 16);
             const bool full = row_bytes % 4096 == 0;  // every part a whole 4 KiB
@@ -2520,13 +2576,9 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
             uint32_t q = 128;
             while (row_bytes % q != 0) q >>= 1;
             const int span = nvec + (line ? (int)((g0 % q + 128 - q) >> 4) : 0);  // most vectors of a row's waves
-            // One part of five vectors per lane (5 KiB) for a row of 4 to 5 KiB
-            // (4112-byte fp32 rows: 1.640 -> 1.335 ms against a whole part and
-            // one of a single vector); wider rows keep parts of four (two parts
-            // of five instead of three of four measured 9-10% slower on 8208-
-            // and 8704-byte rows)
-            const bool five = span > 256 && span <= 320;
-            const int split = five ? (span + 319) / 320 : (span + 255) / 256;
+            const PartShape ps = part_shape(span, a.esize);
+            const bool five = ps.five;
+            const int split = ps.split;
             if (line && five)
                 kern = a.fused ? (cl ? k_grad_rows_line<T, true, true, 5> : k_grad_rows_line<T, true, false, 5>)
                                : (cl ? k_grad_rows_line<T, false, true, 5> : k_grad_rows_line<T, false, false, 5>);
@@ -2551,7 +2603,8 @@ hipError_t launch_grad(const LaunchArgs &a, hipStream_t stream) {
             constexpr int64_t kMaxBlocks = (int64_t)1 << 24;
             for (int64_t base = 0; base < total; base += kMaxBlocks) {
                 const unsigned nb = (unsigned)std::min<int64_t>(kMaxBlocks, total - base);
-                hipLaunchKernelGGL(kern, dim3(nb), dim3(64), 0, stream, in, out, bpc, base, split, RNNT_GRAD_ARGS(g));
+                hipLaunchKernelGGL(kern, dim3(nb), dim3(64), 0, stream, in, out, bpc, base, split, ps.pb, ps.pb_last,
+                                   RNNT_GRAD_ARGS(g));
                 g.red.on = 0;  // the first launch's first workgroup reduces
             }
             return hipGetLastError();

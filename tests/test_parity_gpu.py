@@ -343,6 +343,22 @@ def test_rows_of_4_to_5_kib(rl, V, dtype, clamp, fused):
     check_against_oracle(w, loss, grad, "mean")
 
 
+@pytest.mark.parametrize("V,dtype,clamp,fused", [
+    (4104, torch.float16, -1.0, True),    # 8208-byte rows: the last block of 64 vectors joins the part before
+    (2056, torch.float32, 0.3, True),     # 8224-byte fp32 rows, clamp
+    (2049, torch.float32, -1.0, False),   # 8196-byte log-prob rows off 16-byte boundaries
+    (6152, torch.float16, -1.0, True),    # 12304-byte rows: three parts, the last of five blocks
+])
+def test_rows_a_block_over_4_kib_parts(rl, V, dtype, clamp, fused):
+    """Rows that would end in a part (gradient) or segment (row pass) of at most one block of 64 vectors: that
+    block is taken as a fifth block of the part or segment before it.  Every gradient row against the oracle."""
+    w = _custom([8, 5], [6, 9], V, dtype=dtype, std=2.0 if fused else 1.5, blank=-1, clamp=clamp, fused=fused,
+                prenormalise=not fused, reduction="mean", seed=V + 2)
+    loss, red, grad, flags = run(rl, w)
+    assert flags == 0
+    check_against_oracle(w, loss, grad, "mean")
+
+
 @pytest.mark.parametrize("V,dtype,clamp,fused,size", [
     (1025, torch.float32, -1.0, True, "small"),   # 4100-byte rows: a BPE vocabulary of 1024 and the blank
     (1025, torch.float32, -1.0, True, "large"),
