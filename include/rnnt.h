@@ -118,8 +118,9 @@ enum {
  *   dtype             RNNT_F32 or RNNT_F16.
  *   logit_lengths     host int32[B]: T_i >= 1.
  *   target_lengths    host int32[B]: 0 <= U_i <= 2047 (U_i+1 is the lattice
- *                     width; the alpha/beta kernel keeps a whole anti-diagonal
- *                     of up to 2048 nodes in one wavefront's registers).
+ *                     width; the alpha/beta kernels keep a whole anti-diagonal
+ *                     of up to 2048 nodes in registers: one wavefront's up to
+ *                     1024 columns, a workgroup of up to eight above).
  *   workspace_bytes   out: required size; the caller allocates it (any
  *                     alignment of 256 bytes or more) and passes it back.
  * Runs every host-side check of rnnt_loss_fused that does not need the
@@ -223,7 +224,9 @@ rnnt_status rnnt_grad_scale(void *grad, rnnt_dtype dtype, int64_t N, int32_t V, 
  *   max_T, max_U1     the padded extents: T_i <= max_T and U_i + 1 <= max_U1
  *                     for every sample, else RNNT_INVALID_VALUE.
  *   logits, grad      device (B*max_T*max_U1, V) of dtype.  Padding rows of
- *                     logits are never read.  Every element of grad is
+ *                     logits never enter a result (where rows are no multiple
+ *                     of 16 bytes, a few of their bytes next to a lattice row
+ *                     are loaded with it and ignored).  Every element of grad is
  *                     written: the rows of each lattice as by rnnt_loss_fused,
  *                     the padding rows with zeros (no zero fill is needed
  *                     beforehand, unlike GPURNNT's grads).  grad may equal
@@ -345,8 +348,8 @@ rnnt_status rnnt_multiblank_loss(const void *logits, rnnt_dtype dtype, int64_t N
  * The multi-blank loss for logits in the padded (B, max_T, max_U1, V) layout
  * (the compute_multiblank_grad_kernel page's activations [B, T, U, V + 1 +
  * num_big_blanks]): node (t, u) of sample i is row (i*max_T + t)*max_U1 + u;
- * padding rows of logits are never read and get a zero gradient (written by
- * the gradient pass itself).  Arguments and limits as for
+ * padding rows of logits never enter a result and get a zero gradient
+ * (written by the gradient pass itself).  Arguments and limits as for
  * rnnt_multiblank_loss, with max_T >= T_i and max_U1 >= U_i + 1 for every
  * sample, and the workspace sized by rnnt_multiblank_padded_workspace_size.
  */

@@ -376,7 +376,7 @@ def _unpad(w, g, max_T, max_U1):
 @pytest.mark.parametrize("V,dtype,fused", [(64, torch.float32, True), (33, torch.float32, True),
                                            (256, torch.float16, False)])
 def test_multiblank_padded_matches_packed(rl, V, dtype, fused):
-    # padded (B, max_T, max_U+1, V) logits (NaN padding, never read): the packed call's losses and, row for row,
+    # padded (B, max_T, max_U+1, V) logits (NaN padding, never used): the packed call's losses and, row for row,
     # its gradient bits; the padding rows get a zero gradient
     Ts, Us = [30, 12, 1, 19], [6, 0, 4, 9]
     w = _mb(Ts, Us, V, [V - 2, V - 3], [2, 5], 0.05, dtype=dtype, std=2.0 if fused else 1.5, blank=-1, fused=fused,

@@ -218,7 +218,7 @@ def _padded_rows(w, g, max_T, max_U1):
 def test_padded_layout_matches_packed(rl, V, dtype, fused, size):
     # padded (B, max_T, max_U+1, V) input: same losses and, row for row, the
     # same gradient bits as the packed call on the same values; the padding
-    # (NaN here, never read) gets a zero gradient.  "large": above the
+    # (NaN here, never used) gets a zero gradient.  "large": above the
     # 64512-row line below which a batch takes three launches
     Ts, Us = ([40, 17, 33, 1, 25], [9, 0, 14, 6, 3]) if size == "small" else \
         ([500, 170, 330, 1, 250], [90, 0, 44, 6, 30])
