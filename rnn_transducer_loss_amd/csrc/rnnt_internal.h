@@ -129,8 +129,10 @@ struct RowGeom {
     int lanes_per_row;  // G: 1..64 lanes cooperate on one row (power of two)
     int vec;            // elements per vector access (1 when rows are not 16-byte aligned)
     int rows_per_block_iter;
-    int stream_parts;   // > 0: rows of more than 1 KiB in 16-byte vectors: the row pass takes one row per wave
-                        // in 4 KiB segments, the gradient pass splits each row over stream_parts waves of 4 KiB
+    int stream_parts;   // > 0: rows of more than 1 KiB in 16-byte vectors (odd forms for rows off 16-byte
+                        // boundaries): the row pass takes one row per wave in segments of 4 or 5 KiB, the
+                        // gradient pass one wave per part of 4 or 5 KiB (the launchers choose the parts);
+                        // this is the number of 4 KiB parts covering the widest row
 };
 
 RowGeom row_geometry(int V, int esize, bool aligned16);
