@@ -1090,7 +1090,7 @@ def _random_case(seed):
     clamp, FastEmit, reduction and logits alignment."""
     rng = np.random.default_rng(seed)
     B = int(rng.integers(1, 12))
-    V = int(rng.choice([1, 2, 7, 16, 29, 64, 100, 257, 512, 1000, 1024, 2048]))
+    V = int(rng.choice([1, 2, 7, 16, 29, 64, 100, 257, 512, 1000, 1024, 1025, 1028, 2048, 2049, 4097]))
     Ts = rng.integers(1, 70, size=B).tolist()
     Us = (rng.integers(0, 30, size=B) if V > 1 else np.zeros(B, np.int64)).tolist()
     dtype = torch.float16 if rng.random() < 0.4 else torch.float32

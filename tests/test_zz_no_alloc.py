@@ -69,8 +69,10 @@ def test_noalloc_matches_the_workspace_call_on_consecutive_calls(rl):
     from test_parity_gpu import check_against_oracle
     big = workloads.make_custom([300, 250, 220, 180], [60, 80, 40, 75], 1024, std=2.0, blank=-1,
                                 reduction="mean", seed=301, device="cuda")
+    odd = workloads.make_custom([70, 45], [25, 31], 1025, std=2.0, blank=-1, reduction="sum", seed=303,
+                                device="cuda")  # 4100-byte rows: the odd row and gradient forms
     small = workloads.make("char", device="cuda")
-    for w, rows in ((big, 300), (small, "all")):
+    for w, rows in ((big, 300), (odd, "all"), (small, "all")):
         out = _noalloc(rl, w)
         ref = _with_workspace(rl, w)
         _same(out, ref)
