@@ -464,6 +464,27 @@ def test_lattice_widths_across_register_tiles(rl, U):
     check_against_oracle(w, loss, grad, "none")
 
 
+@pytest.mark.parametrize("U", [512, 743, 744, 991, 992, 1023, 1500, 1983, 1984])
+@pytest.mark.parametrize("domain", ["prob", "log"])
+def test_wide_sweep_widths_in_a_large_batch(rl, U, domain):
+    """Lattices of 513 to 1985 columns in a batch above 64 K rows, so the recursions run on the six-launch path:
+    the one-wave tiles of two to four column groups up to 1024 columns, the multi-wave sweep above; in the
+    probability domain and in the log domain (log-probs down to -200, as in
+    test_log_domain_across_register_tiles)."""
+    Ts, Us, V = [9, 300], [U, 250], 8
+    log = domain == "log"
+    w = _custom(Ts, Us, V, std=1.0, blank=0, fused=not log, prenormalise=log, reduction="none", seed=U + 7)
+    if log:
+        rng = np.random.default_rng(U)
+        x = np.round(rng.uniform(-200.0, -0.25, size=(w.N, V)) * 4) / 4
+        x[::5, 0] = -0.5
+        w.logits = torch.tensor(x, dtype=torch.float32, device="cuda")
+    assert w.N > 64512
+    loss, red, grad, flags = run(rl, w)
+    assert flags == 0
+    check_against_oracle(w, loss, grad, "none", grad_rows=300)
+
+
 @pytest.mark.parametrize("fused", [True, False])
 def test_wide_lattices_in_a_large_batch(rl, fused):
     """Lattices of 2001 and 1501 columns (eight and six column groups per lane) in a batch above 64 K rows, so
