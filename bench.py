@@ -246,6 +246,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="half", choices=["tiny", "char", "bpe", "half", "skewed", "multiblank", "vocab5k"])
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--vocab", type=int, default=None,
+                    help="the workload's lattices and lengths with another vocabulary size V (any width: rows off "
+                         "16-byte boundaries, rows a little over 4 KiB, ...); not for multiblank")
     ap.add_argument("--fastemit-lambda", type=float, default=0.0,
                     help="FastEmit weight on the label-emission gradient (0: the plain loss)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -273,7 +276,7 @@ def main():
     import workloads
 
     print(f"bench: drawing workload {args.workload}", file=sys.stderr, flush=True)
-    w = workloads.make(args.workload, seed=args.seed, device="cuda")
+    w = workloads.make(args.workload, seed=args.seed, device="cuda", vocab=args.vocab)
     tg = torch.from_numpy(w.targets).cuda()
     T, U = w.logit_lengths, w.target_lengths
     dev = w.logits.device
@@ -393,7 +396,8 @@ def main():
     roofline = None
     if dom_bytes is not None:
         ach = dom_bytes / (per_kernel[dominant] * 1e-3) / 1e9
-        traffic = committed_traffic(symbols[dominant], w.name)
+        # the committed counters are the named workloads' own
+        traffic = committed_traffic(symbols[dominant], w.name) if args.vocab is None else None
         roofline = {"bound": "hbm", "kernel": symbols[dominant], "achieved": round(ach, 1),
                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4),
                     "traffic": traffic, "algorithmic_bytes_per_step": dom_bytes,
@@ -429,7 +433,8 @@ def main():
         "dtype": "f32",   # the arithmetic of the row passes; the recursion accumulates in f64
 
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "V": w.V, "rows": w.N, "elements": w.N * w.V,
+        "config": {"workload": w.name + (f"@V={w.V}" if args.vocab is not None else ""), "B": w.B, "V": w.V,
+                   "rows": w.N, "elements": w.N * w.V,
                    "io_dtype": "fp16" if esize(w.dtype) == 2 else "fp32", "fused_log_softmax": w.fused,
                    "reduction": w.reduction, "clamp": w.clamp, "fastemit_lambda": args.fastemit_lambda,
                    **({"big_blank_durations": list(w.big_blank_durations), "sigma": w.sigma} if multiblank else {}),

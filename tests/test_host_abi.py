@@ -324,3 +324,20 @@ def test_table_span_limit():
             else:
                 with pytest.raises(ValueError):
                     _lib.workspace_size(1, 2, N, _lib.RNNT_F32, Ta, Ua)
+
+
+def test_workload_vocabulary_override():
+    """A named workload at another vocabulary size keeps its lengths and draws its targets over the new
+    non-blank classes; the multi-blank workload (whose big blanks are fixed classes) refuses one."""
+    import workloads
+    T, U, tg, V, blank = workloads.lengths("half")
+    T2, U2, tg2, V2, blank2 = workloads.lengths("half", vocab=4097)
+    assert V == 4096 and V2 == 4097 and blank2 == blank == -1
+    assert (T2 == T).all() and (U2 == U).all()
+    for i, u in enumerate(U2):
+        assert ((tg2[i, :u] >= 0) & (tg2[i, :u] < V2 - 1)).all()
+    _, _, tgc, Vc, bc = workloads.lengths("char", vocab=31)
+    assert Vc == 31 and bc == 0 and all(((tgc[i, :u] >= 1) & (tgc[i, :u] < 31)).all()
+                                         for i, u in enumerate(workloads.lengths("char")[1]))
+    with pytest.raises(ValueError):
+        workloads.lengths("multiblank", vocab=2000)

@@ -133,8 +133,9 @@ def make_custom(T: List[int], U: List[int], V: int, *, dtype=torch.float32, std:
                     tuple(big_blank_ids), tuple(big_blank_durations), float(sigma))
 
 
-def lengths(name: str, seed: Optional[int] = None):
-    """(T, U, targets, V, blank) of a named workload, without drawing logits."""
+def lengths(name: str, seed: Optional[int] = None, vocab: Optional[int] = None):
+    """(T, U, targets, V, blank) of a named workload, without drawing logits; ``vocab`` replaces its V (the
+    same lengths, targets drawn over the new classes)."""
     seed = DEFAULT_SEEDS[name] if seed is None else seed
     rng = np.random.default_rng(seed)
     if name == "tiny":
@@ -163,6 +164,10 @@ def lengths(name: str, seed: Optional[int] = None):
         V, blank = 2048, -1
     else:
         raise KeyError(name)
+    if vocab is not None:
+        if name == "multiblank" or vocab < 2 or (blank >= 0 and blank >= vocab):
+            raise ValueError(f"no vocabulary override {vocab} for workload {name}")
+        V = int(vocab)
     bn = blank + V if blank < 0 else blank
     tg = _draw_targets(rng, U, V, bn, MULTIBLANK["big_blank_ids"] if name == "multiblank" else ())
     return T, U, tg, V, blank
@@ -180,10 +185,10 @@ _PARAMS = {
 }
 
 
-def make(name: str, seed: Optional[int] = None, device="cpu") -> Workload:
-    """One of the five named workloads, fully drawn on ``device``."""
+def make(name: str, seed: Optional[int] = None, device="cpu", vocab: Optional[int] = None) -> Workload:
+    """One of the named workloads, fully drawn on ``device`` (``vocab``: another V, as in :func:`lengths`)."""
     seed = DEFAULT_SEEDS[name] if seed is None else seed
-    T, U, tg, V, blank = lengths(name, seed)
+    T, U, tg, V, blank = lengths(name, seed, vocab)
     dtype, std, clamp, fused, reduction, pre = _PARAMS[name]
     logits = _draw_logits(T, U, V, std, dtype, seed, device, pre)
     w = Workload(name, V, blank, clamp, fused, reduction, T, U, tg, logits, _offsets(T, U))
